@@ -1,0 +1,278 @@
+"""Pins of the CPU oracle against facts other than itself (closed forms, a library's
+autograd, finite differences, invariants, exact FLOP counts).  CPU only."""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decoder_only_gpt_amd import presets, synth
+
+from . import torch_ref
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def small_cfgs():
+    """Shrunk variants that keep each workload's features (bias, tanh GELU,
+    padded vocab, untied head, window) at a size fp64 finishes instantly."""
+    tiny = presets.preset("tiny")
+    gpt2 = presets.preset("gpt2_124m", vocab_size=61, padded_vocab=64, block_size=16, n_layer=2,
+                          n_head=2, n_embd=32, mlp_hidden=128, window_left=[-1, -1], B=2, T=16)
+    chat = presets.preset("nanochat_swa", vocab_size=96, padded_vocab=96, block_size=32, n_layer=2,
+                          n_head=2, n_embd=32, mlp_hidden=64, window_left=[8, -1], B=2, T=32)
+    return {"tiny": tiny, "gpt2_small": gpt2, "chat_small": chat}
+
+
+# ---------------------------------------------------------------- sizes / FLOPs
+@pytest.mark.parametrize("name", presets.ORDER)
+def test_sizes_match_golden(name):
+    cfg = presets.preset(name)
+    g = _gold("model_sizes.json")[name]
+    assert oracle.n_params(cfg) == g["n_params"]
+    assert oracle.n_matmul_params(cfg) == g["n_matmul"]
+    assert oracle.flops_per_token(cfg, g["T"]) == g["flops_per_token"]
+    assert synth.n_params(cfg) == g["n_params"]
+
+
+@pytest.mark.parametrize("name", ["tiny", "gpt2_small"])
+def test_counted_flops_equal_formula_at_full_causal(name):
+    """Counting 2mnk over every product of forward+backward (dense T x T scores)
+    gives exactly 6*N_mm + sum_l 12*C*T per token."""
+    cfg = small_cfgs()[name]
+    p = synth.init_params(cfg, seed=0)
+    idx, tgt = synth.tokens(cfg, seed=1)
+    ctr = oracle.FlopCounter()
+    oracle.loss_and_grads(cfg, p, idx, tgt, ctr=ctr)
+    BT = idx.size
+    assert ctr.flops % BT == 0
+    assert ctr.flops // BT == oracle.flops_per_token(cfg, cfg["T"])
+
+
+# ---------------------------------------------------------------- closed forms
+def _zero_head(cfg, p):
+    P = oracle.unflatten(cfg, p, np.float32)
+    if cfg["tied"]:
+        P["wte"][:] = 0
+    else:
+        P["lm_head.w"][:] = 0
+    return oracle.flatten(cfg, P, np.float32)
+
+
+@pytest.mark.parametrize("name", ["tiny", "gpt2_small", "chat_small"])
+def test_zero_head_loss_is_ln_V(name):
+    cfg = small_cfgs()[name]
+    p = _zero_head(cfg, synth.init_params(cfg, seed=0, perturb=True))
+    idx, tgt = synth.tokens(cfg, seed=1)
+    loss, _ = oracle.loss_and_grads(cfg, p, idx, tgt)
+    assert abs(loss - math.log(cfg["vocab_size"])) < 1e-12
+
+
+def test_zero_head_loss_uses_real_vocab_at_gpt2_vocab():
+    """V = 50257 padded to 50304: the loss must be ln 50257, not ln 50304."""
+    gold = _gold("closed_forms.json")
+    cfg = presets.preset("gpt2_124m", block_size=8, n_layer=1, n_head=1, n_embd=16, mlp_hidden=32,
+                         window_left=[-1], B=1, T=8)
+    p = _zero_head(cfg, synth.init_params(cfg, seed=0))
+    idx, tgt = synth.tokens(cfg, seed=1)
+    loss, _ = oracle.loss_and_grads(cfg, p, idx, tgt)
+    assert abs(loss - gold["ln_V"]["50257"]) < 1e-12
+    assert abs(loss - gold["ln_padded_50304"]) > 1e-4
+
+
+def test_initial_loss_near_ln_V():
+    cfg = presets.preset("tiny")
+    idx, tgt = synth.tokens(cfg, seed=1)
+    for seed in range(3):
+        loss, _ = oracle.loss_and_grads(cfg, synth.init_params(cfg, seed=seed), idx, tgt)
+        assert abs(loss - math.log(65)) < 0.1
+
+
+# ---------------------------------------------------------------- gradients
+@pytest.mark.parametrize("name", ["tiny", "gpt2_small", "chat_small"])
+def test_grads_match_torch_autograd_fp64(name):
+    cfg = small_cfgs()[name]
+    p = synth.init_params(cfg, seed=0, perturb=True).astype(np.float64)
+    idx, tgt = synth.tokens(cfg, seed=1)
+    loss, g = oracle.loss_and_grads(cfg, p, idx, tgt)
+    tl, tg = torch_ref.loss_and_grads(cfg, p, idx, tgt)
+    assert abs(loss - tl) < 1e-12
+    off = 0
+    for name_, shape in oracle.layout(cfg):
+        n = int(np.prod(shape))
+        a, b = g[off:off + n], tg[off:off + n]
+        scale = max(np.abs(b).max(), 1e-30)
+        assert np.abs(a - b).max() / scale < 1e-10, name_
+        off += n
+
+
+@pytest.mark.parametrize("name", ["tiny", "gpt2_small", "chat_small"])
+def test_grads_match_central_differences(name):
+    cfg = small_cfgs()[name]
+    p = synth.init_params(cfg, seed=0, perturb=True).astype(np.float64)
+    idx, tgt = synth.tokens(cfg, seed=1)
+    _, g = oracle.loss_and_grads(cfg, p, idx, tgt)
+    rng = np.random.default_rng(7)
+    h = 1e-5
+    off = 0
+    for name_, shape in oracle.layout(cfg):
+        n = int(np.prod(shape))
+        seg = g[off:off + n]
+        scale = max(np.abs(seg).max(), 1e-12)
+        if name_ in ("wte", "lm_head.w"):   # sample rows that carry gradient
+            cand = np.flatnonzero(np.abs(seg) > 1e-3 * scale)
+        else:
+            cand = np.arange(n)
+        for c in rng.choice(cand, size=min(6, cand.size), replace=False):
+            q = p.copy()
+            q[off + c] += h
+            lp, _ = oracle.loss_and_grads(cfg, q, idx, tgt)
+            q[off + c] -= 2 * h
+            lm, _ = oracle.loss_and_grads(cfg, q, idx, tgt)
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - seg[c]) / scale < 1e-6, (name_, c, fd, seg[c])
+        off += n
+
+
+# ---------------------------------------------------------------- invariants
+def test_attention_special_cases():
+    rng = np.random.default_rng(0)
+    H, T, hd = 2, 9, 4
+    q, k, v = (rng.standard_normal((H, T, hd)) for _ in range(3))
+    y, _ = oracle.attention_fwd(q[:, :1], k[:, :1], v[:, :1], -1)
+    assert np.array_equal(y, v[:, :1])                       # T = 1
+    y0, _ = oracle.attention_fwd(q, k, v, 0)
+    assert np.allclose(y0, v, rtol=0, atol=1e-15)            # window of one key
+    yf, _ = oracle.attention_fwd(q, k, v, -1)
+    yw, _ = oracle.attention_fwd(q, k, v, T - 1)
+    assert np.array_equal(yf, yw)                            # left >= T-1 is full causal
+    assert oracle.visible(T, 3).sum() == sum(min(i, 3) + 1 for i in range(T))
+
+
+def test_causality_and_window_receptive_field():
+    cfg = presets.preset("nanochat_swa", vocab_size=96, padded_vocab=96, block_size=32, n_layer=1,
+                         n_head=2, n_embd=32, mlp_hidden=64, window_left=[4], B=1, T=24)
+    p = synth.init_params(cfg, seed=0, perturb=True)
+    idx, _ = synth.tokens(cfg, seed=1)
+    z0 = oracle.logits(cfg, p, idx)
+    t_change = 10
+    idx2 = idx.copy()
+    idx2[0, t_change] = (idx2[0, t_change] + 1) % cfg["vocab_size"]
+    z1 = oracle.logits(cfg, p, idx2)
+    assert np.array_equal(z0[:t_change], z1[:t_change])          # causal
+    assert not np.allclose(z0[t_change], z1[t_change])
+    assert np.array_equal(z0[t_change + 5:], z1[t_change + 5:])  # beyond the window of 4
+    assert not np.allclose(z0[t_change + 4], z1[t_change + 4])
+
+
+def test_layernorm_and_ce_row_sums():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((5, 16))
+    w = rng.standard_normal(16)
+    b = rng.standard_normal(16)
+    _, xhat, rstd = oracle.layernorm_fwd(x, w, b, 1e-5)
+    dx, _, _ = oracle.layernorm_bwd(rng.standard_normal((5, 16)), xhat, rstd, w)
+    assert np.abs(dx.sum(1)).max() < 1e-12
+    z = rng.standard_normal((6, 12))
+    tgt = rng.integers(0, 10, 6)
+    loss_r, dz = oracle.cross_entropy_fwd_bwd(z, tgt, 10, 6)
+    assert np.abs(dz.sum(1)).max() < 1e-15
+    assert np.all(dz[:, 10:] == 0)
+    ref = torch.nn.functional.cross_entropy(torch.tensor(z[:, :10]), torch.tensor(tgt),
+                                            reduction="none").numpy()
+    assert np.allclose(loss_r, ref, rtol=0, atol=1e-13)
+
+
+def test_gelu_matches_torch():
+    u = np.linspace(-8, 8, 2001)
+    tu = torch.tensor(u, requires_grad=True)
+    for tanh_form, mode in [(False, "none"), (True, "tanh")]:
+        ref = torch.nn.functional.gelu(tu, approximate=mode)
+        (gr,) = torch.autograd.grad(ref.sum(), tu)
+        assert np.allclose(oracle.gelu(u, tanh_form), ref.detach().numpy(), rtol=0, atol=1e-14)
+        assert np.allclose(oracle.gelu_grad(u, tanh_form), gr.numpy(), rtol=0, atol=1e-13)
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(2)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 10,
+                        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -0.0, 1e-40, 3.4e38, np.inf, -np.inf],
+                                 np.float32)])
+    ref = torch.tensor(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.bf16_bits(x), ref)
+    assert oracle.bf16_round(np.float32(1 + 2 ** -8)) == 1.0
+    assert oracle.bf16_round(np.float32(1 + 3 * 2 ** -8)) == np.float32(1 + 2 ** -6)
+
+
+# ---------------------------------------------------------------- AdamW
+def test_adamw_first_step_closed_form():
+    """t = 1 from m = v = 0: p1 = p0 (1 - lr wd) - lr g / (|g| + eps) up to a few ulp."""
+    lr, wd, eps = 1e-3, 0.01, 1e-8
+    rng = np.random.default_rng(3)
+    p = rng.standard_normal(10000).astype(np.float32)
+    g = (rng.standard_normal(10000) * 1e-3).astype(np.float32)
+    s = oracle.adamw_scalars(lr, 0.9, 0.95, eps, wd, 1)
+    p1, m1, v1 = oracle.adamw_update(p, np.zeros_like(p), np.zeros_like(p), g, s)
+    ref = p.astype(np.float64) * (1 - lr * wd) - lr * g / (np.abs(g.astype(np.float64)) + eps)
+    mag = np.maximum(np.abs(p), np.float32(lr))   # rounding is relative to the operands, not the result
+    assert np.all(np.abs(p1 - ref) <= 4 * np.spacing(mag))
+    assert np.allclose(m1, 0.1 * g.astype(np.float64), rtol=1e-6, atol=0)
+    assert np.allclose(v1, 0.05 * g.astype(np.float64) ** 2, rtol=1e-6, atol=0)
+
+
+def test_adamw_constant_gradient_bias_correction():
+    """Constant g, wd = 0: bias-corrected m/sqrt(v) = sign(g) at every t, so p moves by lr per step."""
+    lr = 1e-2
+    p = np.zeros(4, np.float32)
+    m = np.zeros(4, np.float32)
+    v = np.zeros(4, np.float32)
+    g = np.array([0.5, -2.0, 3e-3, -7.0], np.float32)
+    for t in range(1, 21):
+        s = oracle.adamw_scalars(lr, 0.9, 0.95, 0.0, 0.0, t)
+        p, m, v = oracle.adamw_update(p, m, v, g, s)
+        assert np.allclose(p, -lr * t * np.sign(g), rtol=2e-5, atol=0), t
+
+
+def test_adamw_zero_rows_stay_zero_and_scale():
+    s = oracle.adamw_scalars(1e-3, 0.9, 0.95, 1e-8, 0.01, 5, grad_scale=0.25)
+    z = np.zeros(8, np.float32)
+    p1, m1, v1 = oracle.adamw_update(z, z, z, z, s)
+    assert not p1.any() and not m1.any() and not v1.any()
+    g = np.full(8, 4.0, np.float32)
+    _, m2, _ = oracle.adamw_update(z, z, z, g, s)
+    assert np.all(m2 == np.float32(0.1) * np.float32(1.0))   # g * 0.25 = 1 enters the moment
+
+
+def test_clip_scale():
+    assert oracle.clip_scale(0.5, 1.0) == 1.0
+    assert oracle.clip_scale(4.0, 1.0) == 0.25
+    assert oracle.clip_scale(4.0, 0.0) == 1.0
+
+
+def test_loss_falls_toward_unigram_entropy():
+    """A few dozen oracle steps on i.i.d. Zipf tokens move the loss from about ln V down
+    toward (never below, in expectation) the unigram entropy."""
+    gold = _gold("closed_forms.json")
+    cfg = presets.preset("tiny", lr=1e-2)
+    p = synth.init_params(cfg, seed=0)
+    m = np.zeros_like(p)
+    v = np.zeros_like(p)
+    losses = []
+    for t in range(1, 41):
+        idx, tgt = synth.tokens(cfg, seed=100 + t)
+        r = oracle.step(cfg, p, m, v, idx, tgt, t)
+        p, m, v = r["p"], r["m"], r["v"]
+        losses.append(r["loss"])
+    H = gold["unigram_entropy"]["65_s1.1"]
+    assert losses[0] > H + 0.7
+    assert np.mean(losses[-5:]) < losses[0] - 0.5
+    assert np.mean(losses[-5:]) > H - 0.2
