@@ -1,0 +1,160 @@
+"""Training-step benchmark: tokens/s and MFU of one GPT training step on one GPU.
+
+    python bench.py [--steps K] [--warmup W] [--config gpt2_124m] [--no-cpu-baseline]
+
+One step = forward + loss readback + backward + global grad norm + clip +
+AdamW, through the C ABI, on seeded synthetic Zipf tokens already resident in
+HBM and N(0, 0.02) weights.  W untimed warm-up steps, then exactly K timed
+steps between device synchronisations.  MFU uses the per-token FLOP formula
+of the nanochat page ("FLOPs-Berechnung im Detail") against the MI355X dense
+bf16 MFMA peak.  A second, separately run pass brackets every kernel with HIP
+events (gpt_profile_*) to give the dominant kernel's achieved rate against its
+roofline; the CPU oracle is timed on a bounded sample of the same workload.
+Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+METRIC = "training tokens/sec on 1 GPU + MFU vs bf16 MFMA peak, GPT-2 124M shape"
+
+
+def workload_name(cfg, name):
+    return (f"{name}: decoder-only GPT training step, B={cfg['B']} T={cfg['T']} "
+            f"V={cfg['vocab_size']}/{cfg['padded_vocab']} L={cfg['n_layer']} H={cfg['n_head']} "
+            f"C={cfg['n_embd']} F={cfg['mlp_hidden']} {cfg['precision']}")
+
+
+def cpu_baseline(cfg, seconds_budget=30.0):
+    """Time the oracle's full step (fp32 NumPy) on one sequence of the same model."""
+    import numpy as np
+    import oracle
+    from decoder_only_gpt_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    p = synth.init_params(cfg, seed=0)
+    idx, tgt = synth.tokens(cfg, B=1, T=cfg["T"], seed=1)
+    z = np.zeros_like(p)
+    t0 = time.perf_counter()
+    oracle.step(cfg, p, z, z, idx, tgt, 1, dtype=np.float32)
+    dt = time.perf_counter() - t0
+    return {"value": round(cfg["T"] / dt, 2), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"one sequence (B=1, T={cfg['T']}) of the same model, full step "
+                      f"(forward, backward, norm, AdamW) in float32 NumPy; {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="gpt2_124m")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-steps", type=int, default=3)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from decoder_only_gpt_amd import gpt, presets, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    cfg = presets.preset(args.config)
+    B, T = cfg["B"], cfg["T"]
+    model = gpt.Model(cfg)
+    model.set_params(synth.init_params(cfg, seed=0))
+    idx, tgt = synth.tokens(cfg, seed=1)
+    d_idx = torch.from_numpy(idx.reshape(-1)).cuda()
+    d_tgt = torch.from_numpy(tgt.reshape(-1)).cuda()
+    torch.cuda.synchronize()
+
+    losses = []
+    for _ in range(args.warmup):
+        losses.append(model.train_step(d_idx, d_tgt)["loss"])
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for k in range(args.steps):
+        losses.append(model.train_step(d_idx, d_tgt)["loss"])
+        ev[k + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = [ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)]
+    ms_per_step = wall * 1e3 / args.steps
+
+    tokens = B * T
+    value = tokens * args.steps / wall
+    fpt = model.sizes.flops_per_token
+    mfu = fpt * value / (PEAK_BF16_TFLOPS * 1e12)
+
+    # Kernel timing pass (separate steps, same work).
+    model.profile_begin()
+    for _ in range(args.profile_steps):
+        model.train_step(d_idx, d_tgt)
+    kstats = model.profile_end()
+    per_kind = {}
+    for k, s in kstats.items():
+        if s["launches"]:
+            per_kind[k] = {
+                "ms_per_step": round(s["ms"] / args.profile_steps, 4),
+                "launches_per_step": s["launches"] // args.profile_steps,
+                "tflops": round(s["flops"] / (s["ms"] * 1e-3) / 1e12, 2) if s["flops"] else None,
+                "gbs": round(s["bytes"] / (s["ms"] * 1e-3) / 1e9, 1) if s["bytes"] else None,
+            }
+    dom = max((k for k in kstats if kstats[k]["launches"]), key=lambda k: kstats[k]["ms"])
+    ds = kstats[dom]
+    avg_s = ds["ms"] * 1e-3 / ds["launches"]
+    if ds["flops"]:
+        ach = ds["flops"] / ds["launches"] / avg_s / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "avg_launch_us": round(avg_s * 1e6, 2), "launches_per_step":
+                    ds["launches"] // args.profile_steps}
+    else:
+        ach = ds["bytes"] / ds["launches"] / avg_s / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                "avg_launch_us": round(avg_s * 1e6, 2)}
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg["precision"] == "bf16" else "f32",
+        "data": "synthetic (seeded Zipf token ids, N(0,0.02) weights)",
+        "config": {"workload": workload_name(cfg, args.config), "global_batch": B, "seq_len": T,
+                   "parallelism": "none (1 GPU)"},
+        "mfu": round(mfu, 4), "flops_per_token": fpt, "peak_tflops": PEAK_BF16_TFLOPS,
+        "step_ms_median": round(float(np.median(step_ms)), 3),
+        "step_ms_min": round(float(np.min(step_ms)), 3),
+        "loss_first": round(losses[0], 4), "loss_last": round(losses[-1], 4),
+        "kernels": per_kind, "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

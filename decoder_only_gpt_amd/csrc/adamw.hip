@@ -1,0 +1,71 @@
+// AdamW update of the float32 master weights (nanochat "AdamW Fused Step":
+// decay first, then the lerp of the first moment, bias correction, and
+// p -= step_size * m / denom; the second moment and denom, which that listing
+// leaves out, follow the textbook Adam form sqrt(v) / sqrt(1 - beta2^t) + eps).
+//
+// This file is compiled with -ffp-contract=off: every multiply and add below
+// rounds on its own, division and square root are correctly rounded and
+// denormals are kept, so the update is bit-identical to the same sequence of
+// IEEE float operations done anywhere else.  One thread handles four
+// consecutive elements with 16-byte loads; the bf16 copy of p that the matrix
+// products read is written in the same pass.
+
+#include "common.h"
+#include "kernels.h"
+
+namespace gpt {
+
+namespace {
+
+__device__ __forceinline__ void adam_one(float& p, float& m, float& v, float g,
+                                         const AdamScalars& s) {
+  g = g * s.scale;
+  p = p * s.decay;
+  m = m + s.omb1 * (g - m);
+  v = v + s.omb2 * (g * g - v);
+  float d = __fdiv_rn(__fsqrt_rn(v), s.sbc2) + s.eps;
+  p = p - s.step_size * __fdiv_rn(m, d);
+}
+
+__global__ void __launch_bounds__(256) adamw_kernel(int64_t n, float* __restrict__ p,
+                                                    float* __restrict__ m, float* __restrict__ v,
+                                                    const float* __restrict__ g,
+                                                    bf16_t* __restrict__ shadow, AdamScalars s) {
+  const int64_t stride = (int64_t)gridDim.x * 256 * 4;
+  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n; i += stride) {
+    if (i + 3 < n) {
+      float4 pp = *(float4*)(p + i), mm = *(float4*)(m + i), vv = *(float4*)(v + i);
+      float4 gg = *(const float4*)(g + i);
+      adam_one(pp.x, mm.x, vv.x, gg.x, s);
+      adam_one(pp.y, mm.y, vv.y, gg.y, s);
+      adam_one(pp.z, mm.z, vv.z, gg.z, s);
+      adam_one(pp.w, mm.w, vv.w, gg.w, s);
+      *(float4*)(p + i) = pp;
+      *(float4*)(m + i) = mm;
+      *(float4*)(v + i) = vv;
+      if (shadow) *(uint2*)(shadow + i) = make_uint2(pack_bf2(pp.x, pp.y), pack_bf2(pp.z, pp.w));
+    } else {
+      for (int64_t j = i; j < n; ++j) {
+        float pj = p[j], mj = m[j], vj = v[j];
+        adam_one(pj, mj, vj, g[j], s);
+        p[j] = pj;
+        m[j] = mj;
+        v[j] = vj;
+        if (shadow) shadow[j] = f2bf(pj);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t adamw(int64_t n, float* p, float* m, float* v, const float* g, uint16_t* shadow,
+                 AdamScalars sc, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = cdiv(cdiv(n, 4), 256);
+  if (blocks > 8192) blocks = 8192;
+  adamw_kernel<<<(unsigned)blocks, 256, 0, s>>>(n, p, m, v, g, shadow, sc);
+  return hipGetLastError();
+}
+
+}  // namespace gpt

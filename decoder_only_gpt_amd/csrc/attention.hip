@@ -1,0 +1,625 @@
+// Causal multi-head self-attention with an optional left window, forward and
+// backward.
+//
+// What is computed (nanoGPT README: "6-layer Transformer with 6 heads";
+// nanochat "FLOPs-Berechnung im Detail": per-layer (left, right) window, the
+// effective sequence is min(window, T)): for each batch row and head,
+// S = q k^T / sqrt(hd), key j visible to query i iff i - left <= j <= i
+// (left < 0: j <= i), P = softmax_j(S), y = P v.  The log-sum-exp of each
+// query's scores is kept so the backward can rebuild P exactly (the llm.c
+// summary, "Configuración mínima del entorno", names cuDNN FlashAttention for
+// this step; the tiled online-softmax scheme below is written for CDNA4).
+//
+// bf16 path (head_dim 32/64/128), CDNA4 MFMA 32x32x16:
+//   forward: a workgroup owns 128 queries of one (batch, head), one wave per
+//   32 queries.  Each wave computes S^T = K Q^T for 64-key blocks, so every
+//   lane owns ONE query column: the running max / sum are per-lane scalars and
+//   a row reduction is one cross-half swap.  P^T stays in registers and feeds
+//   O^T += V^T P^T directly; V is transposed into LDS on the way in.  Blocks
+//   entirely outside a wave's causal band / window are skipped.
+//   backward: two deterministic kernels (no atomics).  dK/dV: a wave owns 32
+//   keys and walks the query blocks that can see them.  dQ: a wave owns 32
+//   queries and walks their key blocks.  Both rebuild P from the saved LSE.
+// fp32 path: one wave per (query) or (key) row with exact fp32 arithmetic.
+
+#include "common.h"
+#include "kernels.h"
+
+namespace gpt {
+
+namespace {
+
+constexpr float LOG2E = 1.4426950408889634f;
+
+__device__ __forceinline__ bool visible(int i, int j, int left, int T) {
+  return j <= i && j < T && (left < 0 || i - j <= left);
+}
+
+// ---------------------------------------------------------------------------
+// fp32 (generic-type) kernels: one wave per row, lanes split the head dim.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(256) attn_fwd_rows(const T* qkv, T* out, float* lse, int B,
+                                                     int Tn, int H, int hd, int left, float scale) {
+  const int lane = threadIdx.x & 63;
+  const long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= (long)B * H * Tn) return;
+  const int i = (int)(w % Tn);
+  const int h = (int)((w / Tn) % H);
+  const int b = (int)(w / ((long)Tn * H));
+  const long C = (long)H * hd, ld = 3 * C;
+  const T* q = qkv + (long)(b * Tn + i) * ld + h * hd;
+  float q0 = lane < hd ? Act<T>::load(q, lane) : 0.f;
+  float q1 = lane + 64 < hd ? Act<T>::load(q, lane + 64) : 0.f;
+  float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
+  const int j0 = left < 0 ? 0 : max(0, i - left);
+  for (int j = j0; j <= i; ++j) {
+    const T* k = qkv + (long)(b * Tn + j) * ld + C + h * hd;
+    const T* v = k + C;
+    float k0 = lane < hd ? Act<T>::load(k, lane) : 0.f;
+    float k1 = lane + 64 < hd ? Act<T>::load(k, lane + 64) : 0.f;
+    float s = warp_sum(q0 * k0 + q1 * k1) * scale;
+    float mn = fmaxf(m, s);
+    float alpha = expf(m - mn), p = expf(s - mn);
+    float v0 = lane < hd ? Act<T>::load(v, lane) : 0.f;
+    float v1 = lane + 64 < hd ? Act<T>::load(v, lane + 64) : 0.f;
+    l = l * alpha + p;
+    o0 = o0 * alpha + p * v0;
+    o1 = o1 * alpha + p * v1;
+    m = mn;
+  }
+  T* o = out + (long)(b * Tn + i) * C + h * hd;
+  if (lane < hd) Act<T>::store(o, lane, o0 / l);
+  if (lane + 64 < hd) Act<T>::store(o, lane + 64, o1 / l);
+  if (lane == 0) lse[((long)b * H + h) * Tn + i] = m + logf(l);
+}
+
+// D[b,h,i] = sum_d dO[i,d] * O[i,d]  (one thread per (row, head)).
+template <typename T>
+__global__ void __launch_bounds__(256) attn_dvec(const T* out, const T* dout, float* D, int B,
+                                                 int Tn, int H, int hd) {
+  long t = (long)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (long)B * Tn * H) return;
+  int h = (int)(t % H);
+  long row = t / H;
+  int i = (int)(row % Tn), b = (int)(row / Tn);
+  const long C = (long)H * hd;
+  const T* o = out + row * C + h * hd;
+  const T* d = dout + row * C + h * hd;
+  float s = 0.f;
+  for (int e = 0; e < hd; ++e) s += Act<T>::load(o, e) * Act<T>::load(d, e);
+  D[((long)b * H + h) * Tn + i] = s;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) attn_dq_rows(const T* qkv, const float* lse, const T* dout,
+                                                    const float* D, T* dqkv, int B, int Tn, int H,
+                                                    int hd, int left, float scale) {
+  const int lane = threadIdx.x & 63;
+  const long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= (long)B * H * Tn) return;
+  const int i = (int)(w % Tn);
+  const int h = (int)((w / Tn) % H);
+  const int b = (int)(w / ((long)Tn * H));
+  const long C = (long)H * hd, ld = 3 * C;
+  const T* q = qkv + (long)(b * Tn + i) * ld + h * hd;
+  const T* dO = dout + (long)(b * Tn + i) * C + h * hd;
+  float q0 = lane < hd ? Act<T>::load(q, lane) : 0.f;
+  float q1 = lane + 64 < hd ? Act<T>::load(q, lane + 64) : 0.f;
+  float g0 = lane < hd ? Act<T>::load(dO, lane) : 0.f;
+  float g1 = lane + 64 < hd ? Act<T>::load(dO, lane + 64) : 0.f;
+  const long r = ((long)b * H + h) * Tn + i;
+  const float L = lse[r], Di = D[r];
+  float a0 = 0.f, a1 = 0.f;
+  const int j0 = left < 0 ? 0 : max(0, i - left);
+  for (int j = j0; j <= i; ++j) {
+    const T* k = qkv + (long)(b * Tn + j) * ld + C + h * hd;
+    const T* v = k + C;
+    float k0 = lane < hd ? Act<T>::load(k, lane) : 0.f;
+    float k1 = lane + 64 < hd ? Act<T>::load(k, lane + 64) : 0.f;
+    float v0 = lane < hd ? Act<T>::load(v, lane) : 0.f;
+    float v1 = lane + 64 < hd ? Act<T>::load(v, lane + 64) : 0.f;
+    float s = warp_sum(q0 * k0 + q1 * k1) * scale;
+    float dp = warp_sum(g0 * v0 + g1 * v1);
+    float p = expf(s - L);
+    float ds = p * (dp - Di);
+    a0 += ds * k0;
+    a1 += ds * k1;
+  }
+  T* dq = dqkv + (long)(b * Tn + i) * ld + h * hd;
+  if (lane < hd) Act<T>::store(dq, lane, a0 * scale);
+  if (lane + 64 < hd) Act<T>::store(dq, lane + 64, a1 * scale);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) attn_dkv_rows(const T* qkv, const float* lse,
+                                                     const T* dout, const float* D, T* dqkv, int B,
+                                                     int Tn, int H, int hd, int left,
+                                                     float scale) {
+  const int lane = threadIdx.x & 63;
+  const long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= (long)B * H * Tn) return;
+  const int j = (int)(w % Tn);
+  const int h = (int)((w / Tn) % H);
+  const int b = (int)(w / ((long)Tn * H));
+  const long C = (long)H * hd, ld = 3 * C;
+  const T* k = qkv + (long)(b * Tn + j) * ld + C + h * hd;
+  const T* v = k + C;
+  float k0 = lane < hd ? Act<T>::load(k, lane) : 0.f;
+  float k1 = lane + 64 < hd ? Act<T>::load(k, lane + 64) : 0.f;
+  float v0 = lane < hd ? Act<T>::load(v, lane) : 0.f;
+  float v1 = lane + 64 < hd ? Act<T>::load(v, lane + 64) : 0.f;
+  float dk0 = 0.f, dk1 = 0.f, dv0 = 0.f, dv1 = 0.f;
+  const int i1 = left < 0 ? Tn - 1 : min(Tn - 1, j + left);
+  for (int i = j; i <= i1; ++i) {
+    const T* q = qkv + (long)(b * Tn + i) * ld + h * hd;
+    const T* dO = dout + (long)(b * Tn + i) * C + h * hd;
+    float q0 = lane < hd ? Act<T>::load(q, lane) : 0.f;
+    float q1 = lane + 64 < hd ? Act<T>::load(q, lane + 64) : 0.f;
+    float g0 = lane < hd ? Act<T>::load(dO, lane) : 0.f;
+    float g1 = lane + 64 < hd ? Act<T>::load(dO, lane + 64) : 0.f;
+    const long r = ((long)b * H + h) * Tn + i;
+    float s = warp_sum(q0 * k0 + q1 * k1) * scale;
+    float dp = warp_sum(g0 * v0 + g1 * v1);
+    float p = expf(s - lse[r]);
+    float ds = p * (dp - D[r]);
+    dv0 += p * g0;
+    dv1 += p * g1;
+    dk0 += ds * q0;
+    dk1 += ds * q1;
+  }
+  T* dk = dqkv + (long)(b * Tn + j) * ld + C + h * hd;
+  T* dv = dk + C;
+  if (lane < hd) {
+    Act<T>::store(dk, lane, dk0 * scale);
+    Act<T>::store(dv, lane, dv0);
+  }
+  if (lane + 64 < hd) {
+    Act<T>::store(dk, lane + 64, dk1 * scale);
+    Act<T>::store(dv, lane + 64, dv1);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA kernels.
+// ---------------------------------------------------------------------------
+constexpr int KB = 64;  // keys (forward / dQ) or queries (dK/dV) per LDS block
+
+// Rows [row0, row0+64) x HD of a strided bf16 matrix into LDS [64][pitch];
+// rows >= nrows read as zero.
+template <int HD>
+__device__ __forceinline__ void lds_rows(const bf16_t* src, long ld, int row0, int nrows,
+                                         bf16_t* dst, int pitch) {
+  constexpr int VPR = HD / 8;  // 16-byte vectors per row
+  for (int u = threadIdx.x; u < KB * VPR; u += 256) {
+    int r = u / VPR, c = (u % VPR) * 8;
+    u32x4 val = {0, 0, 0, 0};
+    if (row0 + r < nrows) val = *(const u32x4*)(src + (long)(row0 + r) * ld + c);
+    *(u32x4*)(dst + r * pitch + c) = val;
+  }
+}
+
+// The same 64 x HD block stored transposed: dst[d][r] (pitch >= 64 + pad).
+template <int HD>
+__device__ __forceinline__ void lds_rows_t(const bf16_t* src, long ld, int row0, int nrows,
+                                           bf16_t* dst, int pitch) {
+  constexpr int DV = HD / 8;
+  for (int u = threadIdx.x; u < (KB / 4) * DV; u += 256) {
+    int rg = u / DV, dv = u % DV;
+    u32x4 w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int r = row0 + rg * 4 + i;
+      w[i] = u32x4{0, 0, 0, 0};
+      if (r < nrows) w[i] = *(const u32x4*)(src + (long)r * ld + dv * 8);
+    }
+    const uint32_t* w0 = (const uint32_t*)&w[0];
+    const uint32_t* w1 = (const uint32_t*)&w[1];
+    const uint32_t* w2 = (const uint32_t*)&w[2];
+    const uint32_t* w3 = (const uint32_t*)&w[3];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int d = dv * 8 + 2 * j;
+      *(uint2*)(dst + d * pitch + rg * 4) =
+          make_uint2((w0[j] & 0xffffu) | (w1[j] << 16), (w2[j] & 0xffffu) | (w3[j] << 16));
+      *(uint2*)(dst + (d + 1) * pitch + rg * 4) =
+          make_uint2((w0[j] >> 16) | (w1[j] & 0xffff0000u), (w2[j] >> 16) | (w3[j] & 0xffff0000u));
+    }
+  }
+}
+
+// 8 bf16 from two 8-byte LDS reads: elements (base + 4g + 0..3) and (base + 8 + 4g + 0..3)
+// of row `row` — the k-slot order of a 32x32 accumulator handed on as an operand.
+__device__ __forceinline__ bf16x8 lds_slots(const bf16_t* t, int pitch, int row, int base, int g) {
+  uint2 a = *(const uint2*)(t + row * pitch + base + 4 * g);
+  uint2 b = *(const uint2*)(t + row * pitch + base + 8 + 4 * g);
+  u32x4 v{a.x, a.y, b.x, b.y};
+  return *(bf16x8*)&v;
+}
+
+// 8 accumulator values r = 8*s2 .. 8*s2+7 of a 32x32 block as a bf16 operand.
+__device__ __forceinline__ bf16x8 acc_slots(const f32x16& acc, int s2) {
+  u32x4 v{pack_bf2(acc[8 * s2 + 0], acc[8 * s2 + 1]), pack_bf2(acc[8 * s2 + 2], acc[8 * s2 + 3]),
+          pack_bf2(acc[8 * s2 + 4], acc[8 * s2 + 5]), pack_bf2(acc[8 * s2 + 6], acc[8 * s2 + 7])};
+  return *(bf16x8*)&v;
+}
+
+__device__ __forceinline__ int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
+
+template <int HD>
+__global__ void __launch_bounds__(256) attn_fwd_mfma(const bf16_t* qkv, bf16_t* out, float* lse,
+                                                     int Tn, int H, int left, float scale_log2) {
+  constexpr int KP = HD + 8, VP = KB + 8, NS = HD / 16, ND = HD / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[KB * KP];
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[HD * VP];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 5, c = lane & 31;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const long C = (long)H * HD, ld = 3 * C;
+  const bf16_t* base = qkv + (long)b * Tn * ld;
+  const int qblk0 = blockIdx.x * 128;
+  const int qw0 = qblk0 + wave * 32;
+  const int qi = qw0 + c;  // this lane's query
+
+  bf16x8 qf[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    u32x4 v{0, 0, 0, 0};
+    if (qi < Tn) v = *(const u32x4*)(base + (long)qi * ld + h * HD + 16 * s + 8 * g);
+    qf[s] = *(bf16x8*)&v;
+  }
+  f32x16 o[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
+  float mrow = -1e30f, lrow = 0.f;
+
+  const int qlast = min(Tn - 1, qblk0 + 127);
+  const int kfirst = left < 0 ? 0 : max(0, qblk0 - left);
+  for (int kb0 = (kfirst / KB) * KB; kb0 <= qlast; kb0 += KB) {
+    __syncthreads();
+    lds_rows<HD>(base + C + h * HD, ld, kb0, Tn, Ks, KP);
+    lds_rows_t<HD>(base + 2 * C + h * HD, ld, kb0, Tn, Vt, VP);
+    __syncthreads();
+    const bool skip = kb0 > qw0 + 31 || (left >= 0 && kb0 + KB - 1 < qw0 - left);
+    if (skip) continue;
+    f32x16 s[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kk][r] = 0.f;
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        bf16x8 kf = *(const bf16x8*)(Ks + (kk * 32 + c) * KP + 16 * st + 8 * g);
+        s[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], s[kk], 0, 0, 0);
+      }
+    }
+    float mx = -1e30f;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        int j = kb0 + kk * 32 + acc_row(r, g);
+        float v = visible(qi, j, left, Tn) ? s[kk][r] * scale_log2 : -INFINITY;
+        s[kk][r] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mnew = fmaxf(mrow, mx);
+    const float alpha = exp2f(mrow - mnew);
+    float ls = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = exp2f(s[kk][r] - mnew);
+        s[kk][r] = p;
+        ls += p;
+      }
+    ls += __shfl_xor(ls, 32, 64);
+    lrow = lrow * alpha + ls;
+    mrow = mnew;
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        bf16x8 pf = acc_slots(s[kk], s2);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          bf16x8 vf = lds_slots(Vt, VP, d * 32 + c, kk * 32 + 16 * s2, g);
+          o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[d], 0, 0, 0);
+        }
+      }
+  }
+  if (qi < Tn) {
+    const float inv = 1.f / lrow;
+    bf16_t* orow = out + ((long)b * Tn + qi) * C + h * HD;
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        int dd = d * 32 + 8 * r4 + 4 * g;
+        uint2 w = make_uint2(pack_bf2(o[d][4 * r4 + 0] * inv, o[d][4 * r4 + 1] * inv),
+                             pack_bf2(o[d][4 * r4 + 2] * inv, o[d][4 * r4 + 3] * inv));
+        *(uint2*)(orow + dd) = w;
+      }
+    if (g == 0) lse[((long)b * H + h) * Tn + qi] = (mrow + log2f(lrow)) / LOG2E;
+  }
+}
+
+// dK, dV: a wave owns 32 keys; loop over the 64-query blocks that see them.
+template <int HD>
+__global__ void __launch_bounds__(256) attn_dkv_mfma(const bf16_t* qkv, const float* lse,
+                                                     const bf16_t* dout, const float* D,
+                                                     bf16_t* dqkv, int Tn, int H, int left,
+                                                     float scale, float scale_log2) {
+  constexpr int RP = HD + 8, TP = KB + 8, NS = HD / 16, ND = HD / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t Qs[KB * RP];
+  __shared__ __attribute__((aligned(16))) bf16_t Qt[HD * TP];
+  __shared__ __attribute__((aligned(16))) bf16_t Gs[KB * RP];
+  __shared__ __attribute__((aligned(16))) bf16_t Gt[HD * TP];
+  __shared__ float Ls[KB], Ds[KB];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 5, c = lane & 31;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const long C = (long)H * HD, ld = 3 * C;
+  const bf16_t* base = qkv + (long)b * Tn * ld;
+  const bf16_t* gbase = dout + (long)b * Tn * C;
+  const float* lrow = lse + ((long)b * H + h) * Tn;
+  const float* drow = D + ((long)b * H + h) * Tn;
+  const int kblk0 = blockIdx.x * 128;
+  const int kw0 = kblk0 + wave * 32;
+  const int kj = kw0 + c;  // this lane's key (as an operand column)
+
+  bf16x8 kf[NS], vf[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    u32x4 a{0, 0, 0, 0}, v{0, 0, 0, 0};
+    if (kj < Tn) {
+      a = *(const u32x4*)(base + (long)kj * ld + C + h * HD + 16 * s + 8 * g);
+      v = *(const u32x4*)(base + (long)kj * ld + 2 * C + h * HD + 16 * s + 8 * g);
+    }
+    kf[s] = *(bf16x8*)&a;
+    vf[s] = *(bf16x8*)&v;
+  }
+  f32x16 dk[ND], dv[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dk[d][r] = dv[d][r] = 0.f;
+
+  const int klast = min(Tn - 1, kblk0 + 127);
+  const int qend = left < 0 ? Tn - 1 : min(Tn - 1, klast + left);
+  for (int qb0 = (kblk0 / KB) * KB; qb0 <= qend; qb0 += KB) {
+    __syncthreads();
+    lds_rows<HD>(base + h * HD, ld, qb0, Tn, Qs, RP);
+    lds_rows_t<HD>(base + h * HD, ld, qb0, Tn, Qt, TP);
+    lds_rows<HD>(gbase + h * HD, C, qb0, Tn, Gs, RP);
+    lds_rows_t<HD>(gbase + h * HD, C, qb0, Tn, Gt, TP);
+    if (threadIdx.x < KB) {
+      int q = qb0 + threadIdx.x;
+      Ls[threadIdx.x] = q < Tn ? lrow[q] * LOG2E : 0.f;
+      Ds[threadIdx.x] = q < Tn ? drow[q] : 0.f;
+    }
+    __syncthreads();
+    const bool skip = qb0 + KB - 1 < kw0 || (left >= 0 && qb0 > kw0 + 31 + left);
+    if (skip) continue;
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        bf16x8 qa = *(const bf16x8*)(Qs + (qq * 32 + c) * RP + 16 * st + 8 * g);
+        bf16x8 ga = *(const bf16x8*)(Gs + (qq * 32 + c) * RP + 16 * st + 8 * g);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[st], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[st], dp, 0, 0, 0);
+      }
+      // s[r]: query qb0 + qq*32 + acc_row(r, g), key kj.
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        int ql = qq * 32 + acc_row(r, g);
+        int qi = qb0 + ql;
+        float p = (qi < Tn && visible(qi, kj, left, Tn)) ? exp2f(s[r] * scale_log2 - Ls[ql]) : 0.f;
+        s[r] = p;
+        dp[r] = p * (dp[r] - Ds[ql]);
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        bf16x8 pa = acc_slots(s, s2);
+        bf16x8 da = acc_slots(dp, s2);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          bf16x8 gb = lds_slots(Gt, TP, d * 32 + c, qq * 32 + 16 * s2, g);
+          bf16x8 qb = lds_slots(Qt, TP, d * 32 + c, qq * 32 + 16 * s2, g);
+          dv[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, gb, dv[d], 0, 0, 0);
+          dk[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, qb, dk[d], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // dk[d][r]: key kw0 + acc_row(r, g), head dim d*32 + c.
+#pragma unroll
+  for (int d = 0; d < ND; ++d)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      int key = kw0 + acc_row(r, g);
+      if (key < Tn) {
+        bf16_t* row = dqkv + ((long)b * Tn + key) * ld + h * HD + d * 32 + c;
+        row[C] = f2bf(dk[d][r] * scale);
+        row[2 * C] = f2bf(dv[d][r]);
+      }
+    }
+}
+
+// dQ: a wave owns 32 queries; loop over their key blocks.
+template <int HD>
+__global__ void __launch_bounds__(256) attn_dq_mfma(const bf16_t* qkv, const float* lse,
+                                                    const bf16_t* dout, const float* D,
+                                                    bf16_t* dqkv, int Tn, int H, int left,
+                                                    float scale, float scale_log2) {
+  constexpr int RP = HD + 8, TP = KB + 8, NS = HD / 16, ND = HD / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[KB * RP];
+  __shared__ __attribute__((aligned(16))) bf16_t Kt[HD * TP];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[KB * RP];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 5, c = lane & 31;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const long C = (long)H * HD, ld = 3 * C;
+  const bf16_t* base = qkv + (long)b * Tn * ld;
+  const int qblk0 = blockIdx.x * 128;
+  const int qw0 = qblk0 + wave * 32;
+  const int qi = qw0 + c;
+
+  bf16x8 qf[NS], gf[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    u32x4 a{0, 0, 0, 0}, v{0, 0, 0, 0};
+    if (qi < Tn) {
+      a = *(const u32x4*)(base + (long)qi * ld + h * HD + 16 * s + 8 * g);
+      v = *(const u32x4*)(dout + ((long)b * Tn + qi) * C + h * HD + 16 * s + 8 * g);
+    }
+    qf[s] = *(bf16x8*)&a;
+    gf[s] = *(bf16x8*)&v;
+  }
+  const long r0 = ((long)b * H + h) * Tn;
+  const float Lq = qi < Tn ? lse[r0 + qi] * LOG2E : 0.f;
+  const float Dq = qi < Tn ? D[r0 + qi] : 0.f;
+  f32x16 dq[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[d][r] = 0.f;
+
+  const int qlast = min(Tn - 1, qblk0 + 127);
+  const int kfirst = left < 0 ? 0 : max(0, qblk0 - left);
+  for (int kb0 = (kfirst / KB) * KB; kb0 <= qlast; kb0 += KB) {
+    __syncthreads();
+    lds_rows<HD>(base + C + h * HD, ld, kb0, Tn, Ks, RP);
+    lds_rows_t<HD>(base + C + h * HD, ld, kb0, Tn, Kt, TP);
+    lds_rows<HD>(base + 2 * C + h * HD, ld, kb0, Tn, Vs, RP);
+    __syncthreads();
+    const bool skip = kb0 > qw0 + 31 || (left >= 0 && kb0 + KB - 1 < qw0 - left);
+    if (skip) continue;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        bf16x8 ka = *(const bf16x8*)(Ks + (kk * 32 + c) * RP + 16 * st + 8 * g);
+        bf16x8 va = *(const bf16x8*)(Vs + (kk * 32 + c) * RP + 16 * st + 8 * g);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[st], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[st], dp, 0, 0, 0);
+      }
+      // s[r]: key kb0 + kk*32 + acc_row(r, g), query qi.
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        int j = kb0 + kk * 32 + acc_row(r, g);
+        float p = (qi < Tn && visible(qi, j, left, Tn)) ? exp2f(s[r] * scale_log2 - Lq) : 0.f;
+        dp[r] = p * (dp[r] - Dq);
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        bf16x8 da = acc_slots(dp, s2);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          bf16x8 kb = lds_slots(Kt, TP, d * 32 + c, kk * 32 + 16 * s2, g);
+          dq[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, kb, dq[d], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // dq[d][r]: query qw0 + acc_row(r, g), head dim d*32 + c.
+#pragma unroll
+  for (int d = 0; d < ND; ++d)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      int q = qw0 + acc_row(r, g);
+      if (q < Tn) dqkv[((long)b * Tn + q) * ld + h * HD + d * 32 + c] = f2bf(dq[d][r] * scale);
+    }
+}
+
+template <int HD>
+hipError_t launch_fwd(int B, int T, int H, int left, const void* qkv, void* out, float* lse,
+                      hipStream_t s) {
+  dim3 grid((unsigned)cdiv(T, 128), H, B);
+  float sl2 = LOG2E / sqrtf((float)HD);
+  attn_fwd_mfma<HD><<<grid, 256, 0, s>>>((const bf16_t*)qkv, (bf16_t*)out, lse, T, H, left, sl2);
+  return hipGetLastError();
+}
+
+template <int HD>
+hipError_t launch_bwd(int B, int T, int H, int left, const void* qkv, const float* lse,
+                      const void* dout, const float* D, void* dqkv, hipStream_t s) {
+  dim3 grid((unsigned)cdiv(T, 128), H, B);
+  float sc = 1.f / sqrtf((float)HD);
+  float sl2 = sc * LOG2E;
+  attn_dkv_mfma<HD><<<grid, 256, 0, s>>>((const bf16_t*)qkv, lse, (const bf16_t*)dout, D,
+                                         (bf16_t*)dqkv, T, H, left, sc, sl2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  attn_dq_mfma<HD><<<grid, 256, 0, s>>>((const bf16_t*)qkv, lse, (const bf16_t*)dout, D,
+                                        (bf16_t*)dqkv, T, H, left, sc, sl2);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool attention_supported(int prec, int hd) {
+  if (prec == GPT_BF16) return hd == 32 || hd == 64 || hd == 128;
+  return hd >= 1 && hd <= 128;
+}
+
+hipError_t attention_fwd(int prec, int B, int T, int H, int hd, int left, const void* qkv,
+                         void* out, float* lse, hipStream_t s) {
+  if ((long)B * T * H == 0) return hipSuccess;
+  if (!attention_supported(prec, hd)) return hipErrorInvalidValue;
+  if (prec == GPT_BF16) {
+    if (hd == 32) return launch_fwd<32>(B, T, H, left, qkv, out, lse, s);
+    if (hd == 64) return launch_fwd<64>(B, T, H, left, qkv, out, lse, s);
+    return launch_fwd<128>(B, T, H, left, qkv, out, lse, s);
+  }
+  long waves = (long)B * H * T;
+  attn_fwd_rows<float><<<(unsigned)cdiv(waves, 4), 256, 0, s>>>(
+      (const float*)qkv, (float*)out, lse, B, T, H, hd, left, 1.f / sqrtf((float)hd));
+  return hipGetLastError();
+}
+
+hipError_t attention_bwd(int prec, int B, int T, int H, int hd, int left, const void* qkv,
+                         const void* out, const float* lse, const void* dout, void* dqkv,
+                         float* dvec, hipStream_t s) {
+  if ((long)B * T * H == 0) return hipSuccess;
+  if (!attention_supported(prec, hd)) return hipErrorInvalidValue;
+  long rows = (long)B * T * H;
+  if (prec == GPT_BF16) {
+    attn_dvec<bf16_t><<<(unsigned)cdiv(rows, 256), 256, 0, s>>>(
+        (const bf16_t*)out, (const bf16_t*)dout, dvec, B, T, H, hd);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (hd == 32) return launch_bwd<32>(B, T, H, left, qkv, lse, dout, dvec, dqkv, s);
+    if (hd == 64) return launch_bwd<64>(B, T, H, left, qkv, lse, dout, dvec, dqkv, s);
+    return launch_bwd<128>(B, T, H, left, qkv, lse, dout, dvec, dqkv, s);
+  }
+  attn_dvec<float><<<(unsigned)cdiv(rows, 256), 256, 0, s>>>((const float*)out,
+                                                             (const float*)dout, dvec, B, T, H, hd);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  float sc = 1.f / sqrtf((float)hd);
+  attn_dq_rows<float><<<(unsigned)cdiv(rows, 4), 256, 0, s>>>(
+      (const float*)qkv, lse, (const float*)dout, dvec, (float*)dqkv, B, T, H, hd, left, sc);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  attn_dkv_rows<float><<<(unsigned)cdiv(rows, 4), 256, 0, s>>>(
+      (const float*)qkv, lse, (const float*)dout, dvec, (float*)dqkv, B, T, H, hd, left, sc);
+  return hipGetLastError();
+}
+
+}  // namespace gpt

@@ -1,0 +1,82 @@
+// Internal helpers shared by the HIP kernels of the GPT step (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+namespace gpt {
+
+typedef uint16_t bf16_t;  // storage type of bfloat16 values
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+struct alignas(16) u32x4 { uint32_t x, y, z, w; };
+
+// float -> bf16, round to nearest even; NaN -> quiet NaN.
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Type traits for the activation type (float in fp32 mode, bf16 in bf16 mode).
+template <typename T> struct Act;
+template <> struct Act<float> {
+  __device__ __forceinline__ static float load(const float* p, long i) { return p[i]; }
+  __device__ __forceinline__ static void store(float* p, long i, float v) { p[i] = v; }
+};
+template <> struct Act<bf16_t> {
+  __device__ __forceinline__ static float load(const bf16_t* p, long i) { return bf2f(p[i]); }
+  __device__ __forceinline__ static void store(bf16_t* p, long i, float v) { p[i] = f2bf(v); }
+};
+
+// GELU.  Exact form: u * Phi(u) with erff; tanh form: the Hendrycks-Gimpel
+// approximation 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))).
+__device__ __forceinline__ float gelu_f(float u, bool tanh_form) {
+  if (tanh_form) {
+    const float s = 0.7978845608028654f, k = 0.044715f;
+    return 0.5f * u * (1.f + tanhf(s * (u + k * u * u * u)));
+  }
+  return 0.5f * u * (1.f + erff(u * 0.7071067811865476f));
+}
+__device__ __forceinline__ float gelu_grad_f(float u, bool tanh_form) {
+  if (tanh_form) {
+    const float s = 0.7978845608028654f, k = 0.044715f;
+    float t = tanhf(s * (u + k * u * u * u));
+    return 0.5f * (1.f + t) + 0.5f * u * (1.f - t * t) * s * (1.f + 3.f * k * u * u);
+  }
+  return 0.5f * (1.f + erff(u * 0.7071067811865476f)) +
+         u * 0.3989422804014327f * expf(-0.5f * u * u);
+}
+
+__device__ __forceinline__ float warp_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float warp_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ double warp_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+inline long cdiv(long a, long b) { return (a + b - 1) / b; }
+
+}  // namespace gpt

@@ -1,0 +1,766 @@
+// Host side of the GPT step: configuration checks, the device-arena plan, the
+// launch sequences of forward / backward / norm / AdamW, the call-order state
+// machine and the extern "C" entry points declared in include/gpt.h.
+//
+// Call order follows the training loop of the NiNo README ("usage": model
+// output -> cross_entropy -> backward -> step -> zero_grad) and the
+// flattened-parameter model adapter of the Panthalia plugin page
+// ("Components"): one flat float32 vector of parameters, with gradients and
+// both AdamW moments in the same layout.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/gpt.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                     \
+  do {                                                                                    \
+    hipError_t e_ = (expr);                                                               \
+    if (e_ != hipSuccess)                                                                 \
+      return fail(GPT_E_HIP, std::string(#expr) + ": " + hipGetErrorString(e_));         \
+  } while (0)
+
+constexpr int64_t ALIGN = 256;
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+struct LayerOff {  // element offsets into the flat parameter vector (-1 = absent)
+  int64_t ln1w, ln1b, qkvw, qkvb, projw, projb, ln2w, ln2b, fcw, fcb, fcpw, fcpb;
+};
+
+struct ParamLayout {
+  int64_t wte, wpe, lnfw, lnfb, lmw, n;
+  std::vector<LayerOff> layer;
+};
+
+ParamLayout param_layout(const gpt_config& c) {
+  ParamLayout p;
+  const int64_t C = c.n_embd, F = c.mlp_hidden;
+  int64_t o = 0;
+  auto take = [&](int64_t n) { int64_t r = o; o += n; return r; };
+  p.wte = take((int64_t)c.padded_vocab * C);
+  p.wpe = take((int64_t)c.block_size * C);
+  for (int l = 0; l < c.n_layer; ++l) {
+    LayerOff L;
+    L.ln1w = take(C);
+    L.ln1b = c.bias ? take(C) : -1;
+    L.qkvw = take(3 * C * C);
+    L.qkvb = c.bias ? take(3 * C) : -1;
+    L.projw = take(C * C);
+    L.projb = c.bias ? take(C) : -1;
+    L.ln2w = take(C);
+    L.ln2b = c.bias ? take(C) : -1;
+    L.fcw = take(F * C);
+    L.fcb = c.bias ? take(F) : -1;
+    L.fcpw = take(C * F);
+    L.fcpb = c.bias ? take(C) : -1;
+    p.layer.push_back(L);
+  }
+  p.lnfw = take(C);
+  p.lnfb = c.bias ? take(C) : -1;
+  p.lmw = c.tied_lm_head ? p.wte : take((int64_t)c.padded_vocab * C);
+  p.n = o;
+  return p;
+}
+
+int64_t n_matmul(const gpt_config& c) {
+  const int64_t C = c.n_embd, F = c.mlp_hidden;
+  return (int64_t)c.n_layer * (3 * C * C + C * C + 2 * F * C) + (int64_t)c.padded_vocab * C;
+}
+
+double flops_per_token(const gpt_config& c, int T) {
+  const int64_t hd = c.n_embd / c.n_head;
+  double attn = 0;
+  for (int l = 0; l < c.n_layer; ++l) {
+    int w = c.window_left[l];
+    int64_t eff = w < 0 ? T : std::min<int64_t>(w, T);
+    attn += 12.0 * c.n_head * hd * eff;
+  }
+  return 6.0 * (double)n_matmul(c) + attn;
+}
+
+int check_config(const gpt_config* c, int B, int T) {
+  if (!c) return fail(GPT_E_INVALID, "config is NULL");
+  if (c->vocab_size < 1 || c->padded_vocab < c->vocab_size)
+    return fail(GPT_E_INVALID, "need 1 <= vocab_size <= padded_vocab");
+  if (c->block_size < 1) return fail(GPT_E_INVALID, "block_size < 1");
+  if (c->n_layer < 1 || c->n_layer > GPT_MAX_LAYERS) return fail(GPT_E_INVALID, "bad n_layer");
+  if (c->n_head < 1 || c->n_embd < 1 || c->n_embd % c->n_head)
+    return fail(GPT_E_INVALID, "n_embd must be a positive multiple of n_head");
+  if (c->n_embd % 64 || c->mlp_hidden < 64 || c->mlp_hidden % 64)
+    return fail(GPT_E_INVALID, "n_embd and mlp_hidden must be multiples of 64");
+  if (c->precision != GPT_FP32 && c->precision != GPT_BF16)
+    return fail(GPT_E_INVALID, "precision must be 0 (fp32) or 1 (bf16)");
+  if (!(c->ln_eps > 0.f)) return fail(GPT_E_INVALID, "ln_eps must be > 0");
+  if (B < 1 || T < 1 || T > c->block_size)
+    return fail(GPT_E_INVALID, "need B >= 1 and 1 <= T <= block_size");
+  if ((int64_t)B * T > (1 << 26)) return fail(GPT_E_UNSUPPORTED, "B*T too large");
+  if (c->n_embd > 2048) return fail(GPT_E_UNSUPPORTED, "n_embd > 2048");
+  const int hd = c->n_embd / c->n_head;
+  if (!gpt::attention_supported(c->precision, hd))
+    return fail(GPT_E_UNSUPPORTED, "head_dim " + std::to_string(hd) +
+                                       " not supported (bf16: 32/64/128; fp32: <= 128)");
+  const int Vq = (int)align_up(c->padded_vocab, 64);
+  if (!gpt::cross_entropy_supported(c->precision, Vq))
+    return fail(GPT_E_UNSUPPORTED, "padded vocabulary too large for the fused cross-entropy");
+  return GPT_OK;
+}
+
+// Byte offsets of every region of the arena.
+struct Arena {
+  int64_t params, grads, adam_m, adam_v, shadow;
+  int64_t X, ln_mean, ln_rstd;
+  std::vector<int64_t> a1, qkv, att, lse, a2, u, g;
+  int64_t xf, logits, loss_rows, loss, gres[2], gact, dC, dC2, dF, dqkv, dvec;
+  int64_t gemm_ws, gemm_ws_bytes, cs_part, ln_part, e_counts, e_offsets, e_perm, n_part, norm2;
+  int64_t state_end, total;
+};
+
+Arena plan_arena(const gpt_config& c, int B, int T) {
+  Arena a;
+  const int64_t M = (int64_t)B * T, C = c.n_embd, F = c.mlp_hidden, L = c.n_layer;
+  const int64_t H = c.n_head, Vp = c.padded_vocab, Vq = align_up(Vp, 64);
+  const int64_t act = c.precision == GPT_BF16 ? 2 : 4;
+  const int64_t N = param_layout(c).n;
+  int64_t o = 0;
+  auto take = [&](int64_t bytes) { int64_t r = o; o = align_up(o + bytes, ALIGN); return r; };
+  a.params = take(N * 4);
+  a.grads = take(N * 4);
+  a.adam_m = take(N * 4);
+  a.adam_v = take(N * 4);
+  a.shadow = c.precision == GPT_BF16 ? take(N * 2) : -1;
+  a.state_end = o;
+  a.X = take((2 * L + 1) * M * C * 4);
+  a.ln_mean = take((2 * L + 1) * M * 4);
+  a.ln_rstd = take((2 * L + 1) * M * 4);
+  for (int64_t l = 0; l < L; ++l) {
+    a.a1.push_back(take(M * C * act));
+    a.qkv.push_back(take(M * 3 * C * act));
+    a.att.push_back(take(M * C * act));
+    a.lse.push_back(take(M * H * 4));
+    a.a2.push_back(take(M * C * act));
+    a.u.push_back(take(M * F * act));
+    a.g.push_back(c.recompute_gelu ? -1 : take(M * F * act));
+  }
+  a.xf = take(M * C * act);
+  a.logits = take(M * Vq * act);
+  a.loss_rows = take(M * 4);
+  a.loss = take(16);
+  a.gres[0] = take(M * C * 4);
+  a.gres[1] = take(M * C * 4);
+  a.gact = take(M * C * act);
+  a.dC = take(M * C * act);
+  a.dC2 = take(M * C * act);
+  a.dF = take(M * F * act);
+  a.dqkv = take(M * 3 * C * act);
+  a.dvec = take(M * H * 4);
+  int64_t ws = 0;
+  auto ws_need = [&](int64_t m, int64_t n, int64_t k) {
+    ws = std::max<int64_t>(ws, gpt::gemm_workspace_bytes((int)m, (int)n, (int)k, c.precision));
+  };
+  ws_need(3 * C, C, M);
+  ws_need(C, C, M);
+  ws_need(F, C, M);
+  ws_need(C, F, M);
+  ws_need(Vp, C, M);
+  a.gemm_ws_bytes = ws;
+  a.gemm_ws = take(std::max<int64_t>(ws, 16));
+  a.cs_part = take((int64_t)gpt::colsum_partial_rows((int)M) * std::max(3 * C, F) * 4 + 16);
+  a.ln_part = take(2 * (int64_t)gpt::layernorm_bwd_partial_rows((int)M) * C * 4 + 16);
+  a.e_counts = take(Vp * 4);
+  a.e_offsets = take(Vp * 4);
+  a.e_perm = take(M * 4);
+  a.n_part = take(1024 * 8);
+  a.norm2 = take(16);
+  a.total = o;
+  return a;
+}
+
+}  // namespace
+
+struct gpt_model {
+  gpt_config cfg;
+  int B, T;
+  int64_t M, C, F, H, hd, Vp, Vq, N;
+  bool bf16;
+  ParamLayout pl;
+  Arena ar;
+  char* base;
+  int state;  // 0 idle, 1 forward with targets done, 2 backward done
+  // kernel timing (gpt_profile_begin / gpt_profile_end)
+  struct Rec { int kind; double flops, bytes; hipEvent_t a, b; };
+  bool prof_on = false;
+  std::vector<hipEvent_t> ev_pool;
+  size_t ev_used = 0;
+  std::vector<Rec> recs;
+  hipEvent_t next_event() {
+    if (ev_used == ev_pool.size()) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      ev_pool.push_back(e);
+    }
+    return ev_pool[ev_used++];
+  }
+  bool loss_valid;
+  const int32_t* last_idx;
+
+  template <typename T_> T_* at(int64_t off) const { return off < 0 ? nullptr : (T_*)(base + off); }
+  float* P(int64_t e) const { return e < 0 ? nullptr : at<float>(ar.params) + e; }
+  float* G(int64_t e) const { return e < 0 ? nullptr : at<float>(ar.grads) + e; }
+  // Weight operand of a matrix product: bf16 copy in bf16 mode, master otherwise.
+  const void* W(int64_t e) const {
+    return bf16 ? (const void*)(at<uint16_t>(ar.shadow) + e) : (const void*)(P(e));
+  }
+  float* X(int64_t i) const { return at<float>(ar.X) + i * M * C; }
+  float* mean(int64_t i) const { return at<float>(ar.ln_mean) + i * M; }
+  float* rstd(int64_t i) const { return at<float>(ar.ln_rstd) + i * M; }
+  int prec() const { return cfg.precision; }
+};
+
+namespace {
+
+gpt_gemm_desc gemm_desc(const gpt_model* m) {
+  gpt_gemm_desc d;
+  std::memset(&d, 0, sizeof(d));
+  d.precision = m->cfg.precision;
+  d.gelu_tanh = m->cfg.gelu_tanh;
+  d.workspace = m->at<void>(m->ar.gemm_ws);
+  d.workspace_bytes = m->ar.gemm_ws_bytes;
+  return d;
+}
+
+// y[M, N] = x[M, K] . W[N, K]^T  (x row-major, W the [out, in] weight).
+gpt_gemm_desc linear_fwd(const gpt_model* m, const void* x, int64_t K, int64_t w_off, int64_t N,
+                         int64_t w_rows) {
+  gpt_gemm_desc d = gemm_desc(m);
+  d.M = (int)m->M; d.N = (int)N; d.K = (int)K;
+  d.A = x; d.lda = K; d.a_trans = 0; d.a_rows = (int)m->M; d.a_kvalid = (int)K;
+  d.B = m->W(w_off); d.ldb = K; d.b_trans = 0; d.b_rows = (int)w_rows; d.b_kvalid = (int)K;
+  return d;
+}
+
+// dx[M, K] = dy[M, N] . W[N, K]  (reduction over N).
+gpt_gemm_desc linear_dx(const gpt_model* m, const void* dy, int64_t N, int64_t w_off, int64_t K,
+                        int64_t ldy, int64_t w_rows) {
+  gpt_gemm_desc d = gemm_desc(m);
+  d.M = (int)m->M; d.N = (int)K; d.K = (int)N;
+  d.A = dy; d.lda = ldy; d.a_trans = 0; d.a_rows = (int)m->M; d.a_kvalid = (int)N;
+  d.B = m->W(w_off); d.ldb = K; d.b_trans = 1; d.b_rows = (int)K; d.b_kvalid = (int)w_rows;
+  return d;
+}
+
+// dW[N, K] (+)= dy[M, N]^T . x[M, K]  (reduction over the M tokens).
+gpt_gemm_desc linear_dw(const gpt_model* m, const void* dy, int64_t N, int64_t ldy, const void* x,
+                        int64_t K, int64_t w_off, int64_t w_rows, int accumulate) {
+  gpt_gemm_desc d = gemm_desc(m);
+  d.M = (int)w_rows; d.N = (int)K; d.K = (int)m->M;
+  d.A = dy; d.lda = ldy; d.a_trans = 1; d.a_rows = (int)w_rows; d.a_kvalid = (int)m->M;
+  d.B = x; d.ldb = K; d.b_trans = 1; d.b_rows = (int)K; d.b_kvalid = (int)m->M;
+  d.epilogue = accumulate ? GPT_EPI_F32_ACCUM : GPT_EPI_F32;
+  d.out = m->G(w_off); d.ldo = K;
+  (void)N;
+  return d;
+}
+
+// Launch `f` (returns hipError_t); inside a profile window bracket it with events.
+template <typename Fn>
+int launch(gpt_model* m, hipStream_t s, int kind, double flops, double bytes, const char* what,
+           Fn f) {
+  hipEvent_t a = nullptr;
+  if (m->prof_on && (a = m->next_event()) != nullptr) (void)hipEventRecord(a, s);
+  hipError_t e = f();
+  if (e != hipSuccess) return fail(GPT_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  if (a) {
+    hipEvent_t b = m->next_event();
+    if (b) {
+      (void)hipEventRecord(b, s);
+      m->recs.push_back({kind, flops, bytes, a, b});
+    }
+  }
+  return GPT_OK;
+}
+
+#define LAUNCH(kind, flops, bytes, expr)                                          \
+  do {                                                                            \
+    int rc_ = launch(m, s, kind, (double)(flops), (double)(bytes), #expr,         \
+                     [&]() { return (expr); });                                   \
+    if (rc_ != GPT_OK) return rc_;                                                \
+  } while (0)
+
+int run_gemm(gpt_model* m, hipStream_t s, const gpt_gemm_desc& d) {
+  const int kind = gpt::gemm_split_count(d) > 1 ? GPT_K_GEMM_SPLITK : GPT_K_GEMM;
+  LAUNCH(kind, 2.0 * d.M * d.N * d.K, 0, gpt::gemm(d, s));
+  return GPT_OK;
+}
+
+#define GEMM(d)                                   \
+  do {                                            \
+    int rc_ = run_gemm(m, s, (d));                \
+    if (rc_ != GPT_OK) return rc_;                \
+  } while (0)
+
+// Visible (query, key) pairs of one (batch row, head).
+double attn_pairs(int T, int left) {
+  double n = 0;
+  for (int i = 0; i < T; ++i) n += (left < 0 ? i : std::min(i, left)) + 1;
+  return n;
+}
+
+int run_forward(gpt_model* m, const int32_t* idx, const int32_t* tgt, hipStream_t s) {
+  const gpt_config& c = m->cfg;
+  const int prec = m->prec();
+  const int64_t M = m->M, C = m->C, F = m->F;
+  const double act_b = m->bf16 ? 2.0 : 4.0;
+  const double ln_fwd_bytes = M * C * (4.0 + act_b) + 8.0 * M;
+  const double attn_flops = 4.0 * m->hd * m->B * m->H;
+  auto act = [&](int64_t off) { return m->at<char>(off); };
+  LAUNCH(GPT_K_EMBED, 0, 12.0 * M * C,
+         gpt::embed_fwd(prec, idx, m->P(m->pl.wte), m->P(m->pl.wpe), (int)M, m->T, (int)C, m->X(0), s));
+  for (int l = 0; l < c.n_layer; ++l) {
+    const LayerOff& L = m->pl.layer[l];
+    LAUNCH(GPT_K_LAYERNORM, 0, ln_fwd_bytes,
+           gpt::layernorm_fwd(prec, m->X(2 * l), m->P(L.ln1w), m->P(L.ln1b), (int)M, (int)C,
+                              c.ln_eps, act(m->ar.a1[l]), m->mean(2 * l), m->rstd(2 * l), s));
+    gpt_gemm_desc d = linear_fwd(m, act(m->ar.a1[l]), C, L.qkvw, 3 * C, 3 * C);
+    d.epilogue = GPT_EPI_STORE; d.bias = m->P(L.qkvb); d.out = act(m->ar.qkv[l]); d.ldo = 3 * C;
+    GEMM(d);
+    LAUNCH(GPT_K_ATTN_FWD, attn_flops * attn_pairs(m->T, c.window_left[l]), 0,
+           gpt::attention_fwd(prec, m->B, m->T, (int)m->H, (int)m->hd, c.window_left[l],
+                              act(m->ar.qkv[l]), act(m->ar.att[l]), m->at<float>(m->ar.lse[l]), s));
+    d = linear_fwd(m, act(m->ar.att[l]), C, L.projw, C, C);
+    d.epilogue = GPT_EPI_RESIDUAL; d.bias = m->P(L.projb); d.resid = m->X(2 * l);
+    d.out = m->X(2 * l + 1); d.ldo = C;
+    GEMM(d);
+    LAUNCH(GPT_K_LAYERNORM, 0, ln_fwd_bytes,
+           gpt::layernorm_fwd(prec, m->X(2 * l + 1), m->P(L.ln2w), m->P(L.ln2b), (int)M, (int)C,
+                              c.ln_eps, act(m->ar.a2[l]), m->mean(2 * l + 1), m->rstd(2 * l + 1), s));
+    d = linear_fwd(m, act(m->ar.a2[l]), C, L.fcw, F, F);
+    d.epilogue = GPT_EPI_GELU; d.bias = m->P(L.fcb); d.out = act(m->ar.u[l]); d.ldo = F;
+    d.aux = c.recompute_gelu ? nullptr : act(m->ar.g[l]); d.ldaux = F;
+    GEMM(d);
+    if (c.recompute_gelu) {
+      d = linear_fwd(m, act(m->ar.u[l]), F, L.fcpw, C, C);
+      d.a_gelu = 1;
+    } else {
+      d = linear_fwd(m, act(m->ar.g[l]), F, L.fcpw, C, C);
+    }
+    d.epilogue = GPT_EPI_RESIDUAL; d.bias = m->P(L.fcpb); d.resid = m->X(2 * l + 1);
+    d.out = m->X(2 * l + 2); d.ldo = C;
+    GEMM(d);
+  }
+  const int64_t nl = 2 * c.n_layer;
+  LAUNCH(GPT_K_LAYERNORM, 0, ln_fwd_bytes,
+         gpt::layernorm_fwd(prec, m->X(nl), m->P(m->pl.lnfw), m->P(m->pl.lnfb), (int)M, (int)C,
+                            c.ln_eps, act(m->ar.xf), m->mean(nl), m->rstd(nl), s));
+  gpt_gemm_desc d = linear_fwd(m, act(m->ar.xf), C, m->pl.lmw, m->Vq, m->Vp);
+  d.epilogue = GPT_EPI_STORE; d.out = act(m->ar.logits); d.ldo = m->Vq;
+  GEMM(d);
+  if (tgt) {
+    LAUNCH(GPT_K_CROSS_ENTROPY, 0, 2.0 * M * m->Vq * act_b + 8.0 * M,
+           gpt::cross_entropy(prec, act(m->ar.logits), (int)M, c.vocab_size, (int)m->Vq, tgt,
+                              m->at<float>(m->ar.loss_rows), s));
+    LAUNCH(GPT_K_CROSS_ENTROPY, 0, 4.0 * M,
+           gpt::mean_loss(m->at<float>(m->ar.loss_rows), (int)M, m->at<float>(m->ar.loss), s));
+  }
+  return GPT_OK;
+}
+
+int run_backward(gpt_model* m, int acc, hipStream_t s) {
+  const gpt_config& c = m->cfg;
+  const int prec = m->prec();
+  const int64_t M = m->M, C = m->C, F = m->F;
+  const double act_b = m->bf16 ? 2.0 : 4.0;
+  const double ln_bwd_bytes = M * C * (2 * act_b + 12.0) + 8.0 * M;
+  const double attn_flops = 8.0 * m->hd * m->B * m->H;
+  auto act = [&](int64_t off) { return m->at<char>(off); };
+  float* cs_part = m->at<float>(m->ar.cs_part);
+  float* ln_part = m->at<float>(m->ar.ln_part);
+  char* gact = act(m->ar.gact);
+  char* dC = act(m->ar.dC);
+  char* dC2 = act(m->ar.dC2);
+  char* dF = act(m->ar.dF);
+  char* dqkv = act(m->ar.dqkv);
+  int cur = 0;
+  float* gres[2] = {m->at<float>(m->ar.gres[0]), m->at<float>(m->ar.gres[1])};
+  auto bias_grad = [&](const char* x, int64_t n, int64_t off) -> int {
+    if (off < 0) return GPT_OK;
+    LAUNCH(GPT_K_BIAS_GRAD, 0, M * n * act_b,
+           gpt::colsum(prec, x, (int)M, (int)n, m->G(off), acc, cs_part, s));
+    return GPT_OK;
+  };
+#define BIAS_GRAD(x, n, off)                    \
+  do {                                          \
+    int rc_ = bias_grad((x), (n), (off));       \
+    if (rc_ != GPT_OK) return rc_;              \
+  } while (0)
+
+  // lm_head: dxf = dlogits . W ; dW (+)= dlogits^T . xf  (dlogits are in `logits`).
+  const char* dlog = act(m->ar.logits);
+  gpt_gemm_desc d = linear_dx(m, dlog, m->Vq, m->pl.lmw, C, m->Vq, m->Vp);
+  d.epilogue = GPT_EPI_STORE; d.out = dC; d.ldo = C;
+  GEMM(d);
+  d = linear_dw(m, dlog, m->Vq, m->Vq, act(m->ar.xf), C, m->pl.lmw, m->Vp, acc);
+  GEMM(d);
+  const int64_t nl = 2 * c.n_layer;
+  LAUNCH(GPT_K_LAYERNORM, 0, ln_bwd_bytes - 4.0 * M * C,
+         gpt::layernorm_bwd(prec, dC, m->X(nl), m->mean(nl), m->rstd(nl), m->P(m->pl.lnfw), nullptr,
+                            (int)M, (int)C, gres[cur], gact, m->G(m->pl.lnfw), m->G(m->pl.lnfb),
+                            acc, ln_part, s));
+  for (int l = c.n_layer - 1; l >= 0; --l) {
+    const LayerOff& L = m->pl.layer[l];
+    // MLP out: x_out = x_mid + GELU(u) Wfcp^T + b
+    d = linear_dx(m, gact, C, L.fcpw, F, C, C);
+    d.epilogue = GPT_EPI_DGELU; d.aux = act(m->ar.u[l]); d.ldaux = F; d.out = dF; d.ldo = F;
+    GEMM(d);
+    if (c.recompute_gelu) {
+      d = linear_dw(m, gact, C, C, act(m->ar.u[l]), F, L.fcpw, C, acc);
+      d.b_gelu = 1;
+    } else {
+      d = linear_dw(m, gact, C, C, act(m->ar.g[l]), F, L.fcpw, C, acc);
+    }
+    GEMM(d);
+    BIAS_GRAD(gact, C, L.fcpb);
+    // MLP in: u = a2 Wfc^T + b
+    d = linear_dx(m, dF, F, L.fcw, C, F, F);
+    d.epilogue = GPT_EPI_STORE; d.out = dC; d.ldo = C;
+    GEMM(d);
+    d = linear_dw(m, dF, F, F, act(m->ar.a2[l]), C, L.fcw, F, acc);
+    GEMM(d);
+    BIAS_GRAD(dF, F, L.fcb);
+    LAUNCH(GPT_K_LAYERNORM, 0, ln_bwd_bytes,
+           gpt::layernorm_bwd(prec, dC, m->X(2 * l + 1), m->mean(2 * l + 1), m->rstd(2 * l + 1),
+                              m->P(L.ln2w), gres[cur], (int)M, (int)C, gres[cur ^ 1], gact,
+                              m->G(L.ln2w), m->G(L.ln2b), acc, ln_part, s));
+    cur ^= 1;
+    // attention out: x_mid = x_in + y Wproj^T + b
+    d = linear_dx(m, gact, C, L.projw, C, C, C);
+    d.epilogue = GPT_EPI_STORE; d.out = dC2; d.ldo = C;
+    GEMM(d);
+    d = linear_dw(m, gact, C, C, act(m->ar.att[l]), C, L.projw, C, acc);
+    GEMM(d);
+    BIAS_GRAD(gact, C, L.projb);
+    LAUNCH(GPT_K_ATTN_BWD, attn_flops * attn_pairs(m->T, c.window_left[l]), 0,
+           gpt::attention_bwd(prec, m->B, m->T, (int)m->H, (int)m->hd, c.window_left[l],
+                              act(m->ar.qkv[l]), act(m->ar.att[l]), m->at<float>(m->ar.lse[l]),
+                              dC2, dqkv, m->at<float>(m->ar.dvec), s));
+    // qkv = a1 Wqkv^T + b
+    d = linear_dx(m, dqkv, 3 * C, L.qkvw, C, 3 * C, 3 * C);
+    d.epilogue = GPT_EPI_STORE; d.out = dC; d.ldo = C;
+    GEMM(d);
+    d = linear_dw(m, dqkv, 3 * C, 3 * C, act(m->ar.a1[l]), C, L.qkvw, 3 * C, acc);
+    GEMM(d);
+    BIAS_GRAD(dqkv, 3 * C, L.qkvb);
+    LAUNCH(GPT_K_LAYERNORM, 0, ln_bwd_bytes,
+           gpt::layernorm_bwd(prec, dC, m->X(2 * l), m->mean(2 * l), m->rstd(2 * l), m->P(L.ln1w),
+                              gres[cur], (int)M, (int)C, gres[cur ^ 1], gact, m->G(L.ln1w),
+                              m->G(L.ln1b), acc, ln_part, s));
+    cur ^= 1;
+  }
+#undef BIAS_GRAD
+  // x0 = wte[idx] + wpe[t]; with a tied head the lm_head gradient is already in dwte.
+  gpt::EmbedBwdScratch scr{m->at<int32_t>(m->ar.e_counts), m->at<int32_t>(m->ar.e_offsets),
+                           m->at<int32_t>(m->ar.e_perm)};
+  const int wte_acc = (c.tied_lm_head || acc) ? 1 : 0;
+  LAUNCH(GPT_K_EMBED, 0, 4.0 * M * C + 4.0 * (m->Vp + c.block_size) * C,
+         gpt::embed_bwd(m->last_idx, gres[cur], (int)M, m->T, (int)C, (int)m->Vp, c.block_size,
+                        m->G(m->pl.wte), wte_acc, m->G(m->pl.wpe), acc, scr, s));
+  return GPT_OK;
+}
+
+gpt::AdamScalars adam_scalars(const gpt_adamw_hp& hp) {
+  gpt::AdamScalars sc;
+  const double t = (double)hp.step_t;
+  sc.omb1 = (float)(1.0 - hp.beta1);
+  sc.omb2 = (float)(1.0 - hp.beta2);
+  sc.decay = (float)(1.0 - hp.lr * hp.weight_decay);
+  sc.step_size = (float)(hp.lr / (1.0 - std::pow(hp.beta1, t)));
+  sc.sbc2 = (float)std::sqrt(1.0 - std::pow(hp.beta2, t));
+  sc.eps = (float)hp.eps;
+  sc.scale = (float)hp.grad_scale;
+  return sc;
+}
+
+int check_hp(const gpt_adamw_hp* hp) {
+  if (!hp) return fail(GPT_E_INVALID, "hp is NULL");
+  if (hp->step_t < 1) return fail(GPT_E_INVALID, "step_t must be >= 1");
+  if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0 && hp->beta2 >= 0.0 && hp->beta2 < 1.0))
+    return fail(GPT_E_INVALID, "betas must be in [0, 1)");
+  if (!(hp->eps >= 0.0) || !std::isfinite(hp->lr) || !std::isfinite(hp->grad_scale))
+    return fail(GPT_E_INVALID, "bad eps / lr / grad_scale");
+  return GPT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gpt_last_error(void) { return g_err.c_str(); }
+
+double gpt_flops_per_token(const gpt_config* cfg, int32_t T) {
+  if (!cfg || check_config(cfg, 1, T) != GPT_OK) return 0.0;
+  return flops_per_token(*cfg, T);
+}
+
+int gpt_plan(const gpt_config* cfg, int32_t B, int32_t T, gpt_sizes* out) {
+  int rc = check_config(cfg, B, T);
+  if (rc != GPT_OK) return rc;
+  if (!out) return fail(GPT_E_INVALID, "out is NULL");
+  Arena a = plan_arena(*cfg, B, T);
+  out->n_params = param_layout(*cfg).n;
+  out->n_matmul_params = n_matmul(*cfg);
+  out->flops_per_token = flops_per_token(*cfg, T);
+  out->arena_bytes = a.total;
+  out->state_bytes = a.state_end;
+  out->activation_bytes = a.total - a.state_end;
+  g_err.clear();
+  return GPT_OK;
+}
+
+int gpt_init(const gpt_config* cfg, int32_t B, int32_t T, void* d_arena, int64_t arena_bytes,
+             void* stream, gpt_model** out) {
+  int rc = check_config(cfg, B, T);
+  if (rc != GPT_OK) return rc;
+  if (!out || !d_arena) return fail(GPT_E_INVALID, "NULL arena or out");
+  if (((uintptr_t)d_arena) % ALIGN) return fail(GPT_E_INVALID, "arena must be 256-byte aligned");
+  Arena a = plan_arena(*cfg, B, T);
+  if (arena_bytes < a.total)
+    return fail(GPT_E_INVALID, "arena too small: need " + std::to_string(a.total) + " bytes");
+  gpt_model* m = new gpt_model();
+  m->cfg = *cfg;
+  m->B = B;
+  m->T = T;
+  m->M = (int64_t)B * T;
+  m->C = cfg->n_embd;
+  m->F = cfg->mlp_hidden;
+  m->H = cfg->n_head;
+  m->hd = m->C / m->H;
+  m->Vp = cfg->padded_vocab;
+  m->Vq = align_up(m->Vp, 64);
+  m->bf16 = cfg->precision == GPT_BF16;
+  m->pl = param_layout(*cfg);
+  m->N = m->pl.n;
+  m->ar = a;
+  m->base = (char*)d_arena;
+  m->state = 0;
+  m->loss_valid = false;
+  m->last_idx = nullptr;
+  hipStream_t s = (hipStream_t)stream;
+  // Parameters, gradients, moments and the bf16 copy start at zero.  The
+  // activation part is cleared too so padded logit columns read as zero.
+  hipError_t e = hipMemsetAsync(d_arena, 0, (size_t)a.total, s);
+  if (e != hipSuccess) {
+    delete m;
+    return fail(GPT_E_HIP, std::string("hipMemsetAsync: ") + hipGetErrorString(e));
+  }
+  *out = m;
+  g_err.clear();
+  return GPT_OK;
+}
+
+int gpt_destroy(gpt_model* m) {
+  if (m)
+    for (hipEvent_t e : m->ev_pool) (void)hipEventDestroy(e);
+  delete m;
+  return GPT_OK;
+}
+
+int gpt_forward(gpt_model* m, const int32_t* d_idx, const int32_t* d_tgt, void* stream) {
+  if (!m || !d_idx) return fail(GPT_E_INVALID, "NULL model or idx");
+  int rc = run_forward(m, d_idx, d_tgt, (hipStream_t)stream);
+  if (rc != GPT_OK) return rc;
+  m->last_idx = d_idx;
+  if (d_tgt) {
+    m->state = 1;
+    m->loss_valid = true;
+  } else {
+    m->state = 0;
+    m->loss_valid = false;
+  }
+  return GPT_OK;
+}
+
+int gpt_loss(gpt_model* m, void* stream, float* h_mean_loss) {
+  if (!m || !h_mean_loss) return fail(GPT_E_INVALID, "NULL argument");
+  if (!m->loss_valid) return fail(GPT_E_STATE, "no forward with targets since the last update");
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(hipMemcpyAsync(h_mean_loss, m->at<float>(m->ar.loss), 4, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  return GPT_OK;
+}
+
+int gpt_loss_device_ptr(gpt_model* m, const float** d_loss) {
+  if (!m || !d_loss) return fail(GPT_E_INVALID, "NULL argument");
+  *d_loss = m->at<float>(m->ar.loss);
+  return GPT_OK;
+}
+
+int gpt_backward(gpt_model* m, int32_t accumulate, void* stream) {
+  if (!m) return fail(GPT_E_INVALID, "NULL model");
+  if (m->state != 1) return fail(GPT_E_STATE, "backward needs a forward with targets first");
+  if (accumulate != 0 && accumulate != 1) return fail(GPT_E_INVALID, "accumulate must be 0 or 1");
+  int rc = run_backward(m, accumulate, (hipStream_t)stream);
+  if (rc != GPT_OK) return rc;
+  m->state = 2;
+  return GPT_OK;
+}
+
+int gpt_grad_norm(gpt_model* m, void* stream, double* h_norm) {
+  if (!m || !h_norm) return fail(GPT_E_INVALID, "NULL argument");
+  if (m->state != 2) return fail(GPT_E_STATE, "grad_norm needs a backward first");
+  hipStream_t s = (hipStream_t)stream;
+  LAUNCH(GPT_K_NORM, 0, 4.0 * m->N,
+         gpt::sumsq(m->G(0), m->N, m->at<double>(m->ar.n_part), m->at<double>(m->ar.norm2), s));
+  double n2 = 0.0;
+  HIP_TRY(hipMemcpyAsync(&n2, m->at<double>(m->ar.norm2), 8, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  *h_norm = std::sqrt(n2);
+  if (!std::isfinite(*h_norm)) return fail(GPT_E_NONFINITE, "gradient norm is not finite");
+  return GPT_OK;
+}
+
+int gpt_adamw_step(gpt_model* m, const gpt_adamw_hp* hp, void* stream) {
+  if (!m) return fail(GPT_E_INVALID, "NULL model");
+  int rc = check_hp(hp);
+  if (rc != GPT_OK) return rc;
+  if (m->state != 2) return fail(GPT_E_STATE, "adamw_step needs a backward first");
+  hipStream_t s = (hipStream_t)stream;
+  LAUNCH(GPT_K_ADAMW, 0, (m->bf16 ? 30.0 : 28.0) * m->N,
+         gpt::adamw(m->N, m->P(0), m->at<float>(m->ar.adam_m), m->at<float>(m->ar.adam_v), m->G(0),
+                    m->bf16 ? m->at<uint16_t>(m->ar.shadow) : nullptr, adam_scalars(*hp), s));
+  m->state = 0;
+  m->loss_valid = false;
+  return GPT_OK;
+}
+
+static int buffer_region(gpt_model* m, int which, char** ptr, int64_t* bytes) {
+  switch (which) {
+    case GPT_BUF_PARAMS: *ptr = m->at<char>(m->ar.params); *bytes = m->N * 4; return GPT_OK;
+    case GPT_BUF_GRADS: *ptr = m->at<char>(m->ar.grads); *bytes = m->N * 4; return GPT_OK;
+    case GPT_BUF_ADAM_M: *ptr = m->at<char>(m->ar.adam_m); *bytes = m->N * 4; return GPT_OK;
+    case GPT_BUF_ADAM_V: *ptr = m->at<char>(m->ar.adam_v); *bytes = m->N * 4; return GPT_OK;
+    case GPT_BUF_LOSS_ROWS: *ptr = m->at<char>(m->ar.loss_rows); *bytes = m->M * 4; return GPT_OK;
+  }
+  return fail(GPT_E_INVALID, "unknown buffer id");
+}
+
+int gpt_get_buffer(gpt_model* m, int32_t which, void* dst, int32_t dst_on_device, void* stream) {
+  if (!m || !dst) return fail(GPT_E_INVALID, "NULL argument");
+  char* p;
+  int64_t bytes;
+  int rc = buffer_region(m, which, &p, &bytes);
+  if (rc != GPT_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(hipMemcpyAsync(dst, p, (size_t)bytes,
+                         dst_on_device ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToHost, s));
+  if (!dst_on_device) HIP_TRY(hipStreamSynchronize(s));
+  return GPT_OK;
+}
+
+int gpt_set_buffer(gpt_model* m, int32_t which, const void* src, int32_t src_on_device,
+                   void* stream) {
+  if (!m || !src) return fail(GPT_E_INVALID, "NULL argument");
+  if (which == GPT_BUF_LOSS_ROWS) return fail(GPT_E_INVALID, "LOSS_ROWS is read-only");
+  char* p;
+  int64_t bytes;
+  int rc = buffer_region(m, which, &p, &bytes);
+  if (rc != GPT_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(hipMemcpyAsync(p, src, (size_t)bytes,
+                         src_on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, s));
+  if (which == GPT_BUF_PARAMS && m->bf16)
+    HIP_TRY(gpt::to_bf16(m->P(0), m->N, m->at<uint16_t>(m->ar.shadow), s));
+  if (which == GPT_BUF_GRADS) m->state = 2;  // caller-provided gradients may be stepped
+  if (!src_on_device) HIP_TRY(hipStreamSynchronize(s));
+  return GPT_OK;
+}
+
+int gpt_profile_begin(gpt_model* m) {
+  if (!m) return fail(GPT_E_INVALID, "NULL model");
+  m->prof_on = true;
+  m->recs.clear();
+  m->ev_used = 0;
+  return GPT_OK;
+}
+
+int gpt_profile_end(gpt_model* m, void* stream, gpt_kernel_stats* out) {
+  if (!m || !out) return fail(GPT_E_INVALID, "NULL argument");
+  m->prof_on = false;
+  for (int k = 0; k < GPT_NUM_KERNEL_KINDS; ++k) out[k] = gpt_kernel_stats{0, 0.0, 0.0, 0.0};
+  HIP_TRY(hipStreamSynchronize((hipStream_t)stream));
+  for (const auto& r : m->recs) {
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, r.a, r.b));
+    gpt_kernel_stats& o = out[r.kind];
+    o.launches += 1;
+    o.ms += ms;
+    o.flops += r.flops;
+    o.bytes += r.bytes;
+  }
+  m->recs.clear();
+  m->ev_used = 0;
+  return GPT_OK;
+}
+
+int gpt_op_gemm(const gpt_gemm_desc* d, void* stream) {
+  if (!d) return fail(GPT_E_INVALID, "NULL descriptor");
+  if (d->precision != GPT_FP32 && d->precision != GPT_BF16)
+    return fail(GPT_E_INVALID, "bad precision");
+  if (d->epilogue < GPT_EPI_STORE || d->epilogue > GPT_EPI_F32_ACCUM)
+    return fail(GPT_E_INVALID, "bad epilogue");
+  if (d->M < 0 || d->N < 0 || d->K < 0) return fail(GPT_E_INVALID, "negative size");
+  if (!d->out && d->M > 0 && d->N > 0) return fail(GPT_E_INVALID, "NULL out");
+  if (d->epilogue == GPT_EPI_RESIDUAL && !d->resid) return fail(GPT_E_INVALID, "NULL resid");
+  if (d->epilogue == GPT_EPI_DGELU && !d->aux) return fail(GPT_E_INVALID, "NULL aux");
+  hipError_t e = gpt::gemm(*d, (hipStream_t)stream);
+  if (e == hipErrorInvalidValue)
+    return fail(GPT_E_INVALID, "gemm layout rule broken (K, lda, ldb must be multiples of 8)");
+  if (e != hipSuccess) return fail(GPT_E_HIP, std::string("gemm: ") + hipGetErrorString(e));
+  return GPT_OK;
+}
+
+int gpt_op_attention_fwd(int32_t precision, int32_t B, int32_t T, int32_t H, int32_t hd,
+                         int32_t left, const void* qkv, void* out, float* lse, void* stream) {
+  if (B < 0 || T < 0 || H < 0) return fail(GPT_E_INVALID, "negative size");
+  if (!gpt::attention_supported(precision, hd)) return fail(GPT_E_UNSUPPORTED, "head_dim");
+  HIP_TRY(gpt::attention_fwd(precision, B, T, H, hd, left, qkv, out, lse, (hipStream_t)stream));
+  return GPT_OK;
+}
+
+int gpt_op_attention_bwd(int32_t precision, int32_t B, int32_t T, int32_t H, int32_t hd,
+                         int32_t left, const void* qkv, const void* out, const float* lse,
+                         const void* dout, void* dqkv, float* workspace, void* stream) {
+  if (B < 0 || T < 0 || H < 0) return fail(GPT_E_INVALID, "negative size");
+  if (!gpt::attention_supported(precision, hd)) return fail(GPT_E_UNSUPPORTED, "head_dim");
+  HIP_TRY(gpt::attention_bwd(precision, B, T, H, hd, left, qkv, out, lse, dout, dqkv, workspace,
+                             (hipStream_t)stream));
+  return GPT_OK;
+}
+
+int gpt_op_adamw(int64_t n, float* p, float* m, float* v, const float* g, uint16_t* shadow,
+                 const gpt_adamw_hp* hp, void* stream) {
+  int rc = check_hp(hp);
+  if (rc != GPT_OK) return rc;
+  if (n < 0) return fail(GPT_E_INVALID, "negative n");
+  if (n > 0 && (!p || !m || !v || !g)) return fail(GPT_E_INVALID, "NULL array");
+  if ((((uintptr_t)p) | ((uintptr_t)m) | ((uintptr_t)v) | ((uintptr_t)g)) % 16 ||
+      ((uintptr_t)shadow) % 8)
+    return fail(GPT_E_INVALID, "arrays must be 16-byte aligned (shadow 8-byte)");
+  HIP_TRY(gpt::adamw(n, p, m, v, g, shadow, adam_scalars(*hp), (hipStream_t)stream));
+  return GPT_OK;
+}
+
+}  // extern "C"

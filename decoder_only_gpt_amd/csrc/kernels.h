@@ -1,0 +1,63 @@
+// Launchers of the HIP kernels that make up the GPT training step.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/gpt.h"
+
+namespace gpt {
+
+// Matrix products (gemm.hip).  Returns hipSuccess or the launch error;
+// hipErrorInvalidValue when the descriptor breaks the stated layout rules.
+hipError_t gemm(const gpt_gemm_desc& d, hipStream_t s);
+// Bytes of split-K workspace gemm() may use for this shape (0 = never splits).
+int64_t gemm_workspace_bytes(int M, int N, int K, int precision);
+// Number of K splits gemm() will use for this descriptor (1 = single kernel).
+int gemm_split_count(const gpt_gemm_desc& d);
+
+// Attention (attention.hip).
+hipError_t attention_fwd(int prec, int B, int T, int H, int hd, int left, const void* qkv,
+                         void* out, float* lse, hipStream_t s);
+hipError_t attention_bwd(int prec, int B, int T, int H, int hd, int left, const void* qkv,
+                         const void* out, const float* lse, const void* dout, void* dqkv,
+                         float* dvec, hipStream_t s);
+bool attention_supported(int prec, int hd);
+
+// Row-wise kernels (rowwise.hip).
+hipError_t embed_fwd(int prec, const int32_t* idx, const float* wte, const float* wpe, int M, int T,
+                     int C, float* x, hipStream_t s);
+// Deterministic embedding backward: dwte[v] (+)= sum of dx rows whose token is v,
+// in increasing position order; dwpe[t] (+)= sum_b dx[b*T+t].
+struct EmbedBwdScratch { int32_t* counts; int32_t* offsets; int32_t* perm; };
+hipError_t embed_bwd(const int32_t* idx, const float* dx, int M, int T, int C, int Vp, int Tb,
+                     float* dwte, int wte_accumulate, float* dwpe, int wpe_accumulate,
+                     EmbedBwdScratch scr, hipStream_t s);
+hipError_t layernorm_fwd(int prec, const float* x, const float* w, const float* b, int M, int C,
+                         float eps, void* y, float* mean, float* rstd, hipStream_t s);
+// dx = resid_in + LN'(dy); dx_act = act copy of dx; dw/db (+)= column sums.
+hipError_t layernorm_bwd(int prec, const void* dy, const float* x, const float* mean,
+                         const float* rstd, const float* w, const float* resid_in, int M, int C,
+                         float* dx, void* dx_act, float* dw, float* db, int accumulate,
+                         float* partials, hipStream_t s);
+int layernorm_bwd_partial_rows(int M);
+// Column sums of an act-type [M, N] matrix into out[N] (overwrite or add).
+hipError_t colsum(int prec, const void* x, int M, int N, float* out, int accumulate,
+                  float* partials, hipStream_t s);
+int colsum_partial_rows(int M);
+// Fused softmax cross-entropy on logits [M, ldz] (act type): loss_rows[m],
+// logits overwritten by d(mean loss)/dlogits (0 for columns >= V).
+hipError_t cross_entropy(int prec, void* logits, int M, int V, int ldz, const int32_t* tgt,
+                         float* loss_rows, hipStream_t s);
+bool cross_entropy_supported(int prec, int ldz);
+hipError_t mean_loss(const float* loss_rows, int M, float* out, hipStream_t s);
+// Sum of squares of x[n] (float) -> *out (double), fixed order.
+hipError_t sumsq(const float* x, int64_t n, double* partials, double* out, hipStream_t s);
+hipError_t to_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t s);
+
+// AdamW (adamw.hip).
+struct AdamScalars { float omb1, omb2, decay, step_size, sbc2, eps, scale; };
+hipError_t adamw(int64_t n, float* p, float* m, float* v, const float* g, uint16_t* shadow,
+                 AdamScalars sc, hipStream_t s);
+
+}  // namespace gpt

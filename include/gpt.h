@@ -1,0 +1,266 @@
+/*
+ * gpt.h — C ABI of the MI355X (gfx950) decoder-only GPT training step.
+ *
+ * One training step of a GPT of the nanoGPT / llm.c kind: learned token and
+ * position embeddings, pre-LayerNorm blocks of causal (optionally sliding-
+ * window) multi-head self-attention and a GELU MLP, final LayerNorm, a tied or
+ * untied lm_head and the mean cross-entropy loss; then the exact gradient, the
+ * global gradient norm and an AdamW update of float32 master weights.
+ *
+ * Sources (web pages, by title and section):
+ *   - nanoGPT README, "quick start" / "reproducing GPT-2" / "todos": the model
+ *     (6-layer, 6-head, 384-channel character model; GPT-2 124M; absolute
+ *     learned position embeddings, "other embeddings" being a todo);
+ *   - Panthalia "Create a Plugin", "Components of the Example Plugin": the
+ *     GPTConfig fields and the flattened-tensor representation of the model
+ *     that forward/backward/update act on;
+ *   - NiNo README, "usage": the call order model(data) -> cross_entropy ->
+ *     backward -> step -> zero_grad;
+ *   - nanochat "Architektur im Überblick", "FLOPs-Berechnung im Detail" (FLOP
+ *     formula, per-layer (left, right) windows) and "AdamW Fused Step" (the
+ *     update order and host-side hyper-parameters that change without a
+ *     rebuild);
+ *   - llm.c summary "Reimplementando el modelo GPT-2 ...", "Proceso de
+ *     entrenamiento" (gradient clipping) and "Ejecución del entrenamiento"
+ *     (the -r recompute option).
+ *
+ * Conventions (all entry points):
+ *   - Return a gpt_status; no exception crosses the ABI.  On error the
+ *     thread-local message from gpt_last_error() says what failed.
+ *   - "device" pointers are HIP device addresses on the current device;
+ *     "host" pointers are ordinary CPU memory.
+ *   - Every launch is enqueued on the given hipStream_t (passed as void*;
+ *     NULL is the null stream).  Only gpt_loss, gpt_grad_norm and the
+ *     host-side variants of gpt_get_buffer / gpt_set_buffer synchronise.
+ *   - Ownership: the caller allocates the single device arena whose size
+ *     gpt_plan reports, and keeps it alive until gpt_destroy.  The library
+ *     borrows it and owns only the opaque host handle.
+ *   - Token ids outside [0, vocab_size) are undefined behaviour.
+ */
+#ifndef GPT_MI355X_H
+#define GPT_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GPT_MAX_LAYERS 128
+
+typedef enum gpt_status {
+  GPT_OK = 0,
+  GPT_E_INVALID = 1,     /* bad argument or configuration                 */
+  GPT_E_STATE = 2,       /* call out of order (e.g. backward before forward) */
+  GPT_E_HIP = 3,         /* a HIP runtime call failed                      */
+  GPT_E_NONFINITE = 4,   /* gradient norm is NaN or Inf                    */
+  GPT_E_UNSUPPORTED = 5  /* valid but not implemented (e.g. head_dim 48)   */
+} gpt_status;
+
+typedef enum gpt_precision { GPT_FP32 = 0, GPT_BF16 = 1 } gpt_precision;
+
+/* Model hyper-parameters (the GPTConfig of the Panthalia plugin example).
+ * Linear weights are [out, in] row-major.  n_embd % 64 == 0, mlp_hidden % 64
+ * == 0, n_embd % n_head == 0; the bf16 path needs head_dim in {32, 64, 128}. */
+typedef struct gpt_config {
+  int32_t vocab_size;     /* real vocabulary: softmax over [0, vocab_size)          */
+  int32_t padded_vocab;   /* rows of wte / lm_head (>= vocab_size); pad rows are 0  */
+  int32_t block_size;     /* rows of wpe; T <= block_size                           */
+  int32_t n_layer, n_head, n_embd, mlp_hidden;
+  int32_t bias;           /* 1: LayerNorm shifts and Linear biases exist            */
+  int32_t tied_lm_head;   /* 1: lm_head is wte                                      */
+  int32_t gelu_tanh;      /* 1: tanh-approximated GELU, 0: exact erf GELU           */
+  int32_t precision;      /* gpt_precision                                          */
+  int32_t recompute_gelu; /* 1: GELU(u) is recomputed instead of stored             */
+  float ln_eps;           /* LayerNorm epsilon (1e-5)                               */
+  int32_t window_left[GPT_MAX_LAYERS]; /* per layer: key j visible to query i iff
+                                          i - left <= j <= i; < 0 = full causal  */
+} gpt_config;
+
+/* Sizes for one (config, B, T).  All byte counts are for the device arena. */
+typedef struct gpt_sizes {
+  int64_t n_params;         /* float32 entries of the flat parameter vector           */
+  int64_t n_matmul_params;  /* parameters that enter a matmul (the FLOP formula's N)  */
+  double flops_per_token;   /* 6 * n_matmul_params + sum_l 12 * h * q * T_eff          */
+  int64_t arena_bytes;      /* one device allocation, 256-byte aligned base           */
+  int64_t state_bytes;      /* params + grads + m + v (+ bf16 shadow) part of it     */
+  int64_t activation_bytes; /* saved activations + backward scratch                   */
+} gpt_sizes;
+
+/* Which flat float32 buffer gpt_get_buffer / gpt_set_buffer address.  All
+ * are n_params entries in the flat order: wte, wpe, then per layer ln1.w,
+ * [ln1.b], qkv.w, [qkv.b], proj.w, [proj.b], ln2.w, [ln2.b], fc.w, [fc.b],
+ * fcproj.w, [fcproj.b], then lnf.w, [lnf.b], then lm_head.w when untied
+ * (bracketed entries only when bias = 1).  GPT_BUF_LOSS_ROWS is B*T floats
+ * (per-token loss of the last forward with targets). */
+typedef enum gpt_buffer {
+  GPT_BUF_PARAMS = 0, GPT_BUF_GRADS = 1, GPT_BUF_ADAM_M = 2, GPT_BUF_ADAM_V = 3,
+  GPT_BUF_LOSS_ROWS = 4
+} gpt_buffer;
+
+/* AdamW hyper-parameters, host doubles.  Each per-step scalar (1-beta1,
+ * 1-beta2, 1-lr*wd, lr/(1-beta1^t), sqrt(1-beta2^t), eps, grad_scale) is
+ * computed in double and rounded once to float.  Per element, in float32
+ * with no fused multiply-add:
+ *   g *= grad_scale; p *= 1-lr*wd; m += (1-beta1)*(g-m); v += (1-beta2)*(g*g-v);
+ *   p -= step_size * (m / (sqrt(v)/sqrt(1-beta2^t) + eps))
+ * and the bf16 weight copy (bf16 mode) is refreshed from p. */
+typedef struct gpt_adamw_hp {
+  double lr, beta1, beta2, eps, weight_decay;
+  double grad_scale;  /* clipping factor; 1.0 = no clipping                      */
+  int64_t step_t;     /* 1-based step count for the bias corrections            */
+} gpt_adamw_hp;
+
+typedef struct gpt_model gpt_model;
+
+/* Host only.  Validates cfg and (B, T) and fills *out.  INVALID on a bad
+ * config (n_embd % n_head != 0, T > block_size, padded_vocab < vocab_size,
+ * ...), UNSUPPORTED for shapes the kernels do not cover. */
+int gpt_plan(const gpt_config* cfg, int32_t B, int32_t T, gpt_sizes* out);
+
+/* Nanochat FLOP formula per token at sequence length T (host only; 0 on a
+ * bad config). */
+double gpt_flops_per_token(const gpt_config* cfg, int32_t T);
+
+/* Bind a model to a caller-owned device arena of at least arena_bytes
+ * (gpt_plan), 256-byte aligned.  Zeroes parameters, gradients and both
+ * moments on `stream`.  Load weights with gpt_set_buffer(GPT_BUF_PARAMS). */
+int gpt_init(const gpt_config* cfg, int32_t B, int32_t T, void* d_arena, int64_t arena_bytes,
+             void* stream, gpt_model** out);
+
+/* Forward pass on device token ids d_idx [B*T] (int32).  With d_tgt [B*T]
+ * the per-token cross-entropy and its gradient w.r.t. the logits are
+ * computed too (required before gpt_backward); with d_tgt == NULL only the
+ * logits.  Enqueue only. */
+int gpt_forward(gpt_model* m, const int32_t* d_idx, const int32_t* d_tgt, void* stream);
+
+/* Mean loss of the last forward with targets.  Synchronises `stream`. */
+int gpt_loss(gpt_model* m, void* stream, float* h_mean_loss);
+
+/* Device address of that mean loss (one float), valid after gpt_forward
+ * with targets has been enqueued; for callers that avoid a sync. */
+int gpt_loss_device_ptr(gpt_model* m, const float** d_loss);
+
+/* Backward pass of the last forward with targets.  accumulate = 0
+ * overwrites the gradient buffer, 1 adds to it.  Enqueue only. */
+int gpt_backward(gpt_model* m, int32_t accumulate, void* stream);
+
+/* Global L2 norm of the gradient buffer (float32 squares summed per block,
+ * blocks summed in double in a fixed order).  Synchronises.  Returns
+ * GPT_E_NONFINITE (with *h_norm set) if the norm is NaN or Inf. */
+int gpt_grad_norm(gpt_model* m, void* stream, double* h_norm);
+
+/* One AdamW update of all parameters (see gpt_adamw_hp).  Enqueue only. */
+int gpt_adamw_step(gpt_model* m, const gpt_adamw_hp* hp, void* stream);
+
+/* Copy a flat buffer out of (get) or into (set) the model.  `dst`/`src` is
+ * host memory when *_on_device == 0 (the call then synchronises), device
+ * memory otherwise.  Setting PARAMS also refreshes the bf16 weight copy.
+ * LOSS_ROWS is read-only. */
+int gpt_get_buffer(gpt_model* m, int32_t which, void* dst, int32_t dst_on_device, void* stream);
+int gpt_set_buffer(gpt_model* m, int32_t which, const void* src, int32_t src_on_device,
+                   void* stream);
+
+/* ------------------------------------------------------------------------
+ * Kernel timing.  Between gpt_profile_begin and gpt_profile_end every kernel
+ * launch of the step is bracketed by HIP events on its stream, and
+ * gpt_profile_end (which synchronises) sums, per kernel kind, the launches,
+ * the elapsed milliseconds, and the algorithmic FLOPs and HBM bytes of those
+ * launches (FLOPs: 2*M*N*K per matrix product, 4*hd (forward) or 8*hd
+ * (backward) per visible (query, key) pair of attention; bytes: the minimal
+ * reads + writes of the memory-bound kernels).  Calls outside a profile
+ * window launch no events.
+ * ---------------------------------------------------------------------- */
+typedef enum gpt_kernel_kind {
+  GPT_K_GEMM = 0,          /* MFMA / fp32 matrix product, one kernel            */
+  GPT_K_GEMM_SPLITK = 1,   /* split-K matrix product + its fixed-order reduce    */
+  GPT_K_ATTN_FWD = 2,
+  GPT_K_ATTN_BWD = 3,      /* D = rowsum(dO*O), dK/dV kernel, dQ kernel          */
+  GPT_K_LAYERNORM = 4,     /* forward and backward (incl. gain/shift reduce)     */
+  GPT_K_CROSS_ENTROPY = 5, /* fused softmax-CE + dlogits, and the loss mean      */
+  GPT_K_EMBED = 6,         /* embedding forward and backward                     */
+  GPT_K_BIAS_GRAD = 7,     /* column sums for Linear bias gradients              */
+  GPT_K_NORM = 8,          /* gradient sum of squares                            */
+  GPT_K_ADAMW = 9,
+  GPT_NUM_KERNEL_KINDS = 10
+} gpt_kernel_kind;
+
+typedef struct gpt_kernel_stats {
+  int64_t launches;
+  double ms, flops, bytes;
+} gpt_kernel_stats;
+
+int gpt_profile_begin(gpt_model* m);
+/* out: GPT_NUM_KERNEL_KINDS entries. */
+int gpt_profile_end(gpt_model* m, void* stream, gpt_kernel_stats* out);
+
+/* Release the host handle (the arena stays the caller's). */
+int gpt_destroy(gpt_model* m);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* gpt_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Single-operation entry points (the kernels of the step, exposed for
+ * unit parity).  Precision: GPT_FP32 = float operands, GPT_BF16 = bf16
+ * operands with float accumulation.
+ * ---------------------------------------------------------------------- */
+
+/* Epilogues of C = op(A) . op(B)^T (op(A) is M x K, op(B) is N x K). */
+typedef enum gpt_epilogue {
+  GPT_EPI_STORE = 0,      /* out(act)  = acc [+ bias]                               */
+  GPT_EPI_RESIDUAL = 1,   /* out(f32)  = resid + acc [+ bias]                       */
+  GPT_EPI_GELU = 2,       /* out(act)  = u = acc [+ bias]; aux(act) = GELU(u) if aux */
+  GPT_EPI_DGELU = 3,      /* out(act)  = acc * GELU'(aux[m, n])                     */
+  GPT_EPI_F32 = 4,        /* out(f32)  = acc                                        */
+  GPT_EPI_F32_ACCUM = 5   /* out(f32) += acc                                        */
+} gpt_epilogue;
+
+/* One matrix product, nanoGPT Linear convention (y = x W^T).  Operand X (A or
+ * B) is "row-major over K" when x_trans == 0: element (r, k) at X[r*ldx + k];
+ * "K-major" when x_trans == 1: element (r, k) at X[k*ldx + r].  Elements with
+ * r >= x_rows or k >= x_kvalid read as zero (for x_trans == 1 the check on r
+ * is per group of 8, so X must stay finite and allocated up to a multiple of
+ * 8 past x_rows).  Every leading dimension % 8 == 0, and K % 8 == 0 unless both
+ * operands are K-major.
+ * a_gelu / b_gelu = 1 apply GELU to that operand as it is read.  Split-K
+ * partial sums (deterministic, fixed order) use `workspace` when K is long;
+ * workspace_bytes == 0 disables splitting. */
+typedef struct gpt_gemm_desc {
+  int32_t precision, M, N, K;
+  const void* A; int64_t lda; int32_t a_trans, a_rows, a_kvalid, a_gelu;
+  const void* B; int64_t ldb; int32_t b_trans, b_rows, b_kvalid, b_gelu;
+  int32_t epilogue, gelu_tanh;
+  const float* bias;    /* [N] or NULL                                  */
+  const float* resid;   /* [M, ldo] float, RESIDUAL only                 */
+  void* out; int64_t ldo;
+  void* aux; int64_t ldaux;  /* GELU output / DGELU input, act type     */
+  void* workspace; int64_t workspace_bytes;
+} gpt_gemm_desc;
+
+int gpt_op_gemm(const gpt_gemm_desc* d, void* stream);
+
+/* Causal (windowed) attention over a packed qkv [B*T, 3*H*hd] (q | k | v,
+ * head h at columns h*hd of each third).  out [B*T, H*hd] (act type), lse
+ * [B, H, T] float = log-sum-exp of the scaled scores per query.
+ * left < 0: full causal, else key j visible to query i iff i-left <= j <= i. */
+int gpt_op_attention_fwd(int32_t precision, int32_t B, int32_t T, int32_t H, int32_t hd,
+                         int32_t left, const void* qkv, void* out, float* lse, void* stream);
+
+/* Gradient of gpt_op_attention_fwd: dout [B*T, H*hd] -> dqkv [B*T, 3*H*hd].
+ * `workspace` holds B*H*T floats. */
+int gpt_op_attention_bwd(int32_t precision, int32_t B, int32_t T, int32_t H, int32_t hd,
+                         int32_t left, const void* qkv, const void* out, const float* lse,
+                         const void* dout, void* dqkv, float* workspace, void* stream);
+
+/* The AdamW update on raw device float arrays of n entries; `shadow`
+ * (bf16, n entries) is written when non-NULL. */
+int gpt_op_adamw(int64_t n, float* p, float* m, float* v, const float* g, uint16_t* shadow,
+                 const gpt_adamw_hp* hp, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPT_MI355X_H */

@@ -1,0 +1,237 @@
+"""Single-kernel parity on the GPU through the C ABI, against the CPU oracle
+(and plain numpy products as the definition of a matrix product)."""
+
+import numpy as np
+import pytest
+
+import oracle
+from decoder_only_gpt_amd import gpt, synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gpt.lib()
+
+
+def to_dev(a, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+    return t.to(dtype)
+
+
+def rounded(t):
+    """The exact float values a device tensor holds, as float64 numpy."""
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+# ------------------------------------------------------------------ AdamW
+@pytest.mark.parametrize("t,scale", [(1, 1.0), (7, 0.37), (1000, 1.0)])
+def test_adamw_bit_exact(t, scale):
+    n = 1_000_003  # ragged tail
+    rng = np.random.default_rng(t)
+    p = rng.standard_normal(n).astype(np.float32)
+    m, v, g = synth.adam_state(n, seed=t, scale=1e-3)
+    special = np.array([0.0, -0.0, 1e-40, -3e-39, 1e-45, 65504.0, 1e-30], np.float32)
+    p[:7], m[:7], v[:7] = special, special[::-1], np.abs(special)
+    g[:7] = special[[3, 2, 1, 0, 6, 5, 4]]
+    hp = gpt.AdamHP(1e-3, 0.9, 0.95, 1e-8, 0.01, scale, t)
+    s = oracle.adamw_scalars(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, t, scale)
+    pr, mr, vr = oracle.adamw_update(p, m, v, g, s)
+    dp, dm, dv, dg = (torch.from_numpy(x.copy()).cuda() for x in (p, m, v, g))
+    sh = torch.empty(n, dtype=torch.int16, device="cuda")
+    gpt.op_adamw(dp, dm, dv, dg, sh, hp)
+    torch.cuda.synchronize()
+    for got, ref in ((dp, pr), (dm, mr), (dv, vr)):
+        assert np.array_equal(got.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    assert np.array_equal(sh.cpu().numpy().view(np.uint16), oracle.bf16_bits(pr))
+
+
+# ------------------------------------------------------------------ GEMM
+def _operand(rows, K, trans, dtype, seed, gelu=False, tanh_form=False):
+    """Device operand holding op(X) [rows, K]; returns (tensor, ld, exact values as [rows, K])."""
+    ld = -(-rows // 8) * 8 if trans else -(-K // 8) * 8
+    val = synth.normal((rows, K), seed, 1.0)
+    if trans:
+        store = np.zeros((K, ld), np.float32)
+        store[:, :rows] = val.T
+    else:
+        store = np.zeros((rows, ld), np.float32)
+        store[:, :K] = val
+    dev = to_dev(store, dtype)
+    exact = rounded(dev)
+    exact = exact[:, :rows].T if trans else exact[:, :K]
+    if gelu:
+        exact = oracle.gelu(exact, tanh_form)
+    return dev, ld, exact
+
+
+CASES = [
+    # M, N, K, a_trans, b_trans
+    (200, 192, 136, 0, 0),      # forward layout, ragged M
+    (130, 320, 64, 0, 1),       # dX layout (B stored [K, N])
+    (96, 136, 203, 1, 1),       # dW layout, ragged K
+    (256, 256, 4096, 1, 1),     # long K: split-K path
+    (513, 64, 768, 0, 0),
+]
+
+
+@pytest.mark.parametrize("prec", [gpt.FP32, gpt.BF16])
+@pytest.mark.parametrize("M,N,K,at,bt", CASES)
+def test_gemm_layouts(prec, M, N, K, at, bt):
+    dt = torch.bfloat16 if prec == gpt.BF16 else torch.float32
+    A, lda, Ax = _operand(M, K, at, dt, 1)
+    B, ldb, Bx = _operand(N, K, bt, dt, 2)
+    ref = Ax @ Bx.T
+    out = torch.full((M, N), 7.0, dtype=torch.float32, device="cuda")
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    d = gpt.GemmDesc(precision=prec, M=M, N=N, K=K, A=A.data_ptr(), lda=lda, a_trans=at, a_rows=M,
+                     a_kvalid=K, B=B.data_ptr(), ldb=ldb, b_trans=bt, b_rows=N, b_kvalid=K,
+                     epilogue=gpt.EPI_F32, out=out.data_ptr(), ldo=N, workspace=ws.data_ptr(),
+                     workspace_bytes=ws.numel())
+    gpt.op_gemm(d)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    err = np.abs(got - ref).max() / np.abs(ref).max()
+    assert err < 2e-5, err
+
+
+@pytest.mark.parametrize("prec", [gpt.FP32, gpt.BF16])
+@pytest.mark.parametrize("epi", [gpt.EPI_STORE, gpt.EPI_RESIDUAL, gpt.EPI_GELU, gpt.EPI_DGELU,
+                                 gpt.EPI_F32_ACCUM])
+@pytest.mark.parametrize("tanh_form", [0, 1])
+def test_gemm_epilogues(prec, epi, tanh_form):
+    dt = torch.bfloat16 if prec == gpt.BF16 else torch.float32
+    M, N, K = 150, 256, 192
+    A, lda, Ax = _operand(M, K, 0, dt, 3, gelu=(epi == gpt.EPI_RESIDUAL), tanh_form=tanh_form)
+    B, ldb, Bx = _operand(N, K, 0, dt, 4)
+    if epi == gpt.EPI_RESIDUAL and prec == gpt.BF16:
+        Ax = oracle.bf16_round(Ax.astype(np.float32)).astype(np.float64)  # GELU'd operand is bf16
+    acc = Ax @ Bx.T
+    bias = torch.from_numpy(synth.normal(N, 5, 0.5)).cuda()
+    resid = torch.from_numpy(synth.normal((M, N), 6, 1.0)).cuda()
+    aux_in = to_dev(synth.normal((M, N), 7, 1.5), dt)
+    out_t = torch.float32 if epi in (gpt.EPI_RESIDUAL, gpt.EPI_F32_ACCUM) else dt
+    out = torch.zeros((M, N), dtype=out_t, device="cuda")
+    aux = torch.zeros((M, N), dtype=dt, device="cuda")
+    if epi == gpt.EPI_F32_ACCUM:
+        out.copy_(resid)
+    d = gpt.GemmDesc(precision=prec, M=M, N=N, K=K, A=A.data_ptr(), lda=lda, a_trans=0, a_rows=M,
+                     a_kvalid=K, a_gelu=int(epi == gpt.EPI_RESIDUAL), B=B.data_ptr(), ldb=ldb,
+                     b_trans=0, b_rows=N, b_kvalid=K, epilogue=epi, gelu_tanh=tanh_form,
+                     out=out.data_ptr(), ldo=N)
+    bx = bias.cpu().numpy().astype(np.float64)
+    rx = resid.cpu().numpy().astype(np.float64)
+    if epi in (gpt.EPI_STORE, gpt.EPI_GELU, gpt.EPI_RESIDUAL):
+        d.bias = bias.data_ptr()
+    if epi == gpt.EPI_RESIDUAL:
+        d.resid = resid.data_ptr()
+    if epi == gpt.EPI_GELU:
+        d.aux, d.ldaux = aux.data_ptr(), N
+    if epi == gpt.EPI_DGELU:
+        d.aux, d.ldaux = aux_in.data_ptr(), N
+    gpt.op_gemm(d)
+    torch.cuda.synchronize()
+    got = rounded(out)
+    tol = 1e-2 if (prec == gpt.BF16 and out_t != torch.float32) else 2e-5
+    if epi == gpt.EPI_RESIDUAL and prec == gpt.BF16:
+        tol = 1e-3  # a GELU value may round to the neighbouring bf16 on either side
+    if epi == gpt.EPI_STORE:
+        ref = acc + bx
+    elif epi == gpt.EPI_RESIDUAL:
+        ref = rx + acc + bx
+    elif epi == gpt.EPI_GELU:
+        ref = acc + bx
+        g_ref = oracle.gelu(got, tanh_form)   # GELU of the stored pre-activation
+        g_err = np.abs(rounded(aux) - g_ref).max() / np.abs(g_ref).max()
+        assert g_err < (1e-2 if prec == gpt.BF16 else 1e-6)
+    elif epi == gpt.EPI_DGELU:
+        ref = acc * oracle.gelu_grad(rounded(aux_in), tanh_form)
+    else:
+        ref = rx + acc
+    err = np.abs(got - ref).max() / np.abs(ref).max()
+    assert err < tol, err
+
+
+def test_gemm_empty_and_padded_rows():
+    """K = 0 runs the epilogue on zeros; B rows past b_rows read as zero."""
+    M, N, K = 64, 128, 64
+    A = torch.ones((M, K), dtype=torch.bfloat16, device="cuda")
+    B = torch.ones((N, K), dtype=torch.bfloat16, device="cuda")
+    out = torch.full((M, N), 3.0, device="cuda")
+    d = gpt.GemmDesc(precision=gpt.BF16, M=M, N=N, K=K, A=A.data_ptr(), lda=K, a_rows=M, a_kvalid=K,
+                     B=B.data_ptr(), ldb=K, b_rows=65, b_kvalid=K, epilogue=gpt.EPI_F32,
+                     out=out.data_ptr(), ldo=N)
+    gpt.op_gemm(d)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.all(o[:, :65] == K) and np.all(o[:, 65:] == 0)
+    d.K = 0
+    gpt.op_gemm(d)
+    torch.cuda.synchronize()
+    assert np.all(out.cpu().numpy() == 0)
+
+
+# ------------------------------------------------------------------ attention
+ATT = [  # B, T, H, hd, left
+    (2, 1, 2, 64, -1),
+    (2, 77, 2, 64, -1),
+    (1, 300, 2, 64, -1),
+    (1, 300, 2, 64, 100),
+    (2, 200, 1, 32, 0),
+    (1, 260, 2, 128, 64),
+    (1, 129, 3, 128, -1),
+    (1, 190, 2, 32, 17),
+]
+
+
+def _attn_ref(qkv, dout, B, T, H, hd, left):
+    C = H * hd
+    q, k, v = (qkv[:, i * C:(i + 1) * C].reshape(B, T, H, hd).transpose(0, 2, 1, 3) for i in range(3))
+    dy = dout.reshape(B, T, H, hd).transpose(0, 2, 1, 3)
+    y = np.zeros((B, H, T, hd))
+    lse = np.zeros((B, H, T))
+    dq, dk, dv = np.zeros_like(y), np.zeros_like(y), np.zeros_like(y)
+    for b in range(B):
+        y[b], P = oracle.attention_fwd(q[b], k[b], v[b], left)
+        S = (q[b] @ np.swapaxes(k[b], -1, -2)) / np.sqrt(hd)
+        S = np.where(oracle.visible(T, left), S, -np.inf)
+        mx = S.max(-1, keepdims=True)
+        lse[b] = (mx + np.log(np.exp(S - mx).sum(-1, keepdims=True)))[..., 0]
+        dq[b], dk[b], dv[b] = oracle.attention_bwd(dy[b], q[b], k[b], v[b], P)
+    flat = lambda t: t.transpose(0, 2, 1, 3).reshape(B * T, C)
+    return flat(y), lse, np.concatenate([flat(dq), flat(dk), flat(dv)], 1)
+
+
+@pytest.mark.parametrize("prec", [gpt.FP32, gpt.BF16])
+@pytest.mark.parametrize("B,T,H,hd,left", ATT)
+def test_attention_fwd_bwd(prec, B, T, H, hd, left):
+    dt = torch.bfloat16 if prec == gpt.BF16 else torch.float32
+    C = H * hd
+    qkv = to_dev(synth.normal((B * T, 3 * C), 11, 1.0), dt)
+    dout = to_dev(synth.normal((B * T, C), 12, 1.0), dt)
+    out = torch.zeros((B * T, C), dtype=dt, device="cuda")
+    lse = torch.zeros((B, H, T), dtype=torch.float32, device="cuda")
+    dqkv = torch.zeros((B * T, 3 * C), dtype=dt, device="cuda")
+    ws = torch.zeros(B * H * T + 1, dtype=torch.float32, device="cuda")
+    gpt.op_attention_fwd(prec, B, T, H, hd, left, qkv, out, lse)
+    gpt.op_attention_bwd(prec, B, T, H, hd, left, qkv, out, lse, dout, dqkv, ws)
+    torch.cuda.synchronize()
+    y_ref, lse_ref, dqkv_ref = _attn_ref(rounded(qkv), rounded(dout), B, T, H, hd, left)
+    ftol = 1e-2 if prec == gpt.BF16 else 1e-5
+    assert np.abs(rounded(out) - y_ref).max() / np.abs(y_ref).max() < ftol
+    assert np.abs(lse.cpu().numpy() - lse_ref).max() < (2e-3 if prec == gpt.BF16 else 1e-5)
+    g = rounded(dqkv)
+    for i in range(3):
+        a, r = g[:, i * C:(i + 1) * C], dqkv_ref[:, i * C:(i + 1) * C]
+        if not np.abs(r).max():
+            assert not np.abs(a).max()
+            continue
+        err = np.abs(a - r).max() / np.abs(r).max()
+        assert err < (3e-2 if prec == gpt.BF16 else 1e-4), (i, err)
+        cos = (a * r).sum() / np.sqrt((a * a).sum() * (r * r).sum())
+        assert cos > (0.9995 if prec == gpt.BF16 else 1 - 1e-9), (i, cos)

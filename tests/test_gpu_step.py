@@ -1,0 +1,197 @@
+"""Full training-step parity on the GPU (through the C ABI) against the CPU oracle.
+
+fp32 mode: loss within 1e-5 relative, every gradient tensor within 1e-4 of the
+oracle (max-abs normalised).  bf16 mode: loss within 2e-2 relative and a
+per-tensor gradient cosine >= 0.999.  The AdamW update the model applies is
+compared bit for bit with the oracle's float32 schedule run on the gradients
+the model produced.  Shapes are small enough for the fp64 oracle but span
+several tiles with ragged tails.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from decoder_only_gpt_amd import gpt, presets, synth
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gpt.lib()
+
+
+def gpu_cfgs():
+    return {
+        "tiny": presets.preset("tiny"),
+        # GPT-2 features: biases, tanh GELU, padded vocab, clip; T ragged vs the 128 tiles.
+        "gpt2_s": presets.preset("gpt2_124m", vocab_size=500, padded_vocab=512, block_size=128,
+                                 n_layer=2, n_head=2, n_embd=128, mlp_hidden=512,
+                                 window_left=[-1, -1], B=3, T=100, clip=0.05),
+        # GELU recompute (the 350M workload's switch).
+        "gpt2_rc": presets.preset("gpt2_350m", vocab_size=500, padded_vocab=512, block_size=128,
+                                  n_layer=2, n_head=2, n_embd=128, mlp_hidden=256,
+                                  window_left=[-1, -1], B=2, T=96),
+        # nanochat features: head_dim 128, untied head, window on layer 0, vocab not a multiple of 64.
+        "chat_s": presets.preset("nanochat_swa", vocab_size=300, padded_vocab=300, block_size=160,
+                                 n_layer=2, n_head=1, n_embd=128, mlp_hidden=256,
+                                 window_left=[40, -1], B=2, T=150),
+    }
+
+
+def run_gpu(cfg, p, idx, tgt, t=1):
+    m = gpt.Model(cfg)
+    m.set_params(p)
+    di = torch.from_numpy(idx.reshape(-1)).cuda()
+    dt = torch.from_numpy(tgt.reshape(-1)).cuda()
+    m.forward(di, dt)
+    loss = m.loss()
+    m.backward(0)
+    g = m.grads()
+    norm = m.grad_norm()
+    scale = oracle.clip_scale(norm, cfg.get("clip", 0.0))
+    m.adamw_step(t, scale)
+    return dict(loss=loss, grads=g, norm=norm, scale=scale, p=m.params(),
+                m=m.get_buffer(gpt.BUF_ADAM_M), v=m.get_buffer(gpt.BUF_ADAM_V),
+                rows=m.get_buffer(gpt.BUF_LOSS_ROWS))
+
+
+def compare_grads(cfg, g, gref, bf16):
+    off = 0
+    worst = []
+    for name, shape in oracle.layout(cfg):
+        n = int(np.prod(shape))
+        a = g[off:off + n].astype(np.float64)
+        r = gref[off:off + n]
+        off += n
+        na, nr = np.linalg.norm(a), np.linalg.norm(r)
+        if nr == 0:
+            assert na == 0, name
+            continue
+        if bf16:
+            cos = float(a @ r / (na * nr))
+            worst.append((cos, name))
+            assert cos >= 0.999, (name, cos)
+        else:
+            err = np.abs(a - r).max() / np.abs(r).max()
+            worst.append((-err, name))
+            assert err <= 1e-4, (name, err)
+    return min(worst)
+
+
+def check_step(cfg, name, seed=0):
+    bf16 = cfg["precision"] == "bf16"
+    p = synth.init_params(cfg, seed=seed, perturb=True)
+    idx, tgt = synth.tokens(cfg, seed=seed + 1)
+    print(f"[step] {name} {cfg['precision']} B={cfg['B']} T={cfg['T']}", flush=True)
+    got = run_gpu(cfg, p, idx, tgt)
+    ref_loss, ref_g = oracle.loss_and_grads(cfg, p, idx, tgt)
+    tol = 2e-2 if bf16 else 1e-5
+    assert abs(got["loss"] - ref_loss) / ref_loss <= tol, (got["loss"], ref_loss)
+    ref_rows = oracle.loss_rows(cfg, p, idx, tgt)
+    assert np.abs(got["rows"] - ref_rows).max() <= (0.1 if bf16 else 1e-4)
+    compare_grads(cfg, got["grads"], ref_g, bf16)
+    # the norm the device reduced equals the norm of the gradients it wrote
+    n_dev = np.sqrt(np.sum(got["grads"].astype(np.float64) ** 2))
+    assert abs(got["norm"] - n_dev) <= 1e-5 * n_dev
+    # AdamW inside the model == the oracle schedule on the model's own gradients, bit for bit
+    s = oracle.adamw_scalars(cfg["lr"], cfg["beta1"], cfg["beta2"], cfg["eps"],
+                             cfg["weight_decay"], 1, got["scale"])
+    z = np.zeros_like(p)
+    pr, mr, vr = oracle.adamw_update(p, z, z, got["grads"], s)
+    assert np.array_equal(got["p"].view(np.uint32), pr.view(np.uint32))
+    assert np.array_equal(got["m"].view(np.uint32), mr.view(np.uint32))
+    assert np.array_equal(got["v"].view(np.uint32), vr.view(np.uint32))
+    # padded vocabulary rows keep exactly zero gradient and value
+    Vp, V, C = cfg["padded_vocab"], cfg["vocab_size"], cfg["n_embd"]
+    if Vp > V:
+        assert not got["grads"][(V * C):(Vp * C)].any()
+        assert not got["p"][(V * C):(Vp * C)].any()
+    return got
+
+
+@pytest.mark.parametrize("prec", ["fp32", "bf16"])
+@pytest.mark.parametrize("name", ["tiny", "gpt2_s", "gpt2_rc", "chat_s"])
+def test_step_parity(name, prec):
+    cfg = dict(gpu_cfgs()[name], precision=prec)
+    check_step(cfg, name)
+
+
+@pytest.mark.parametrize("prec", ["fp32", "bf16"])
+def test_step_ragged_batch(prec):
+    """B*T not a multiple of any tile, T not a multiple of the attention blocks."""
+    cfg = dict(presets.preset("tiny", B=3, T=27), precision=prec)
+    check_step(cfg, "tiny_ragged", seed=5)
+
+
+@pytest.mark.parametrize("prec", ["fp32", "bf16"])
+def test_step_is_bitwise_deterministic(prec):
+    cfg = dict(gpu_cfgs()["gpt2_s"], precision=prec)
+    p = synth.init_params(cfg, seed=2, perturb=True)
+    idx, tgt = synth.tokens(cfg, seed=3)
+    a = run_gpu(cfg, p, idx, tgt)
+    b = run_gpu(cfg, p, idx, tgt)
+    for k in ("grads", "p", "m", "v", "rows"):
+        assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k
+    assert a["loss"] == b["loss"]
+
+
+def test_call_order_state_machine():
+    cfg = presets.preset("tiny")
+    m = gpt.Model(cfg)
+    with pytest.raises(gpt.GptError) as e:
+        m.backward(0)
+    assert e.value.code == gpt.E_STATE
+    with pytest.raises(gpt.GptError) as e:
+        m.loss()
+    assert e.value.code == gpt.E_STATE
+    idx, tgt = synth.tokens(cfg, seed=1)
+    di = torch.from_numpy(idx.reshape(-1)).cuda()
+    dt = torch.from_numpy(tgt.reshape(-1)).cuda()
+    m.forward(di, None)                    # logits only: no loss, no backward
+    with pytest.raises(gpt.GptError) as e:
+        m.backward(0)
+    assert e.value.code == gpt.E_STATE
+    m.forward(di, dt)
+    m.backward(0)
+    with pytest.raises(gpt.GptError) as e:
+        m.backward(0)                       # a second backward needs a new forward
+    assert e.value.code == gpt.E_STATE
+    m.adamw_step(1)
+    with pytest.raises(gpt.GptError) as e:
+        m.adamw_step(2)
+    assert e.value.code == gpt.E_STATE
+
+
+def test_nonfinite_gradient_is_reported():
+    cfg = presets.preset("tiny")
+    m = gpt.Model(cfg)
+    m.set_params(synth.init_params(cfg))
+    g = np.zeros(m.n_params, np.float32)
+    g[123] = np.inf
+    m.set_buffer(gpt.BUF_GRADS, g)
+    with pytest.raises(gpt.GptError) as e:
+        m.grad_norm()
+    assert e.value.code == gpt.E_NONFINITE
+
+
+def test_gradient_accumulation_adds():
+    """backward(accumulate=1) after backward(0) on the same batch doubles every gradient."""
+    cfg = dict(gpu_cfgs()["gpt2_s"], precision="fp32")
+    p = synth.init_params(cfg, seed=4, perturb=True)
+    idx, tgt = synth.tokens(cfg, seed=5)
+    m = gpt.Model(cfg)
+    m.set_params(p)
+    di = torch.from_numpy(idx.reshape(-1)).cuda()
+    dt = torch.from_numpy(tgt.reshape(-1)).cuda()
+    m.forward(di, dt)
+    m.backward(0)
+    g1 = m.grads()
+    m.forward(di, dt)
+    m.backward(1)
+    g2 = m.grads()
+    assert np.allclose(g2, 2 * g1, rtol=1e-6, atol=1e-12)
