@@ -17,13 +17,20 @@ namespace gpt {
 
 namespace {
 
+// Correctly rounded float square root.  The hardware v_sqrt_f32 is only
+// faithful (1 ulp); the double-precision square root is accurate to well under
+// 2^-53 relative, and rounding it to float is then exact-to-nearest, because a
+// float's square root never lies within 2^-50 (relative) of a float midpoint
+// (53 >= 2*24 + 2 bits).
+__device__ __forceinline__ float sqrt_rn(float x) { return (float)__dsqrt_rn((double)x); }
+
 __device__ __forceinline__ void adam_one(float& p, float& m, float& v, float g,
                                          const AdamScalars& s) {
   g = g * s.scale;
   p = p * s.decay;
   m = m + s.omb1 * (g - m);
   v = v + s.omb2 * (g * g - v);
-  float d = __fdiv_rn(__fsqrt_rn(v), s.sbc2) + s.eps;
+  float d = __fdiv_rn(sqrt_rn(v), s.sbc2) + s.eps;
   p = p - s.step_size * __fdiv_rn(m, d);
 }
 

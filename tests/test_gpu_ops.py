@@ -229,7 +229,9 @@ def test_attention_fwd_bwd(prec, B, T, H, hd, left):
     for i in range(3):
         a, r = g[:, i * C:(i + 1) * C], dqkv_ref[:, i * C:(i + 1) * C]
         if not np.abs(r).max():
-            assert not np.abs(a).max()
+            # exactly zero in real arithmetic (one visible key: dS = P (dP - D) = 0);
+            # the device sees D from the rounded output, so only rounding noise remains
+            assert np.abs(a).max() < 1e-4, (i, np.abs(a).max())
             continue
         err = np.abs(a - r).max() / np.abs(r).max()
         assert err < (3e-2 if prec == gpt.BF16 else 1e-4), (i, err)
