@@ -15,7 +15,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-struct alignas(16) u32x4 { uint32_t x, y, z, w; };
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // float -> bf16, round to nearest even; NaN -> quiet NaN.
 __device__ __forceinline__ bf16_t f2bf(float f) {

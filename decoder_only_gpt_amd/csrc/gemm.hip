@@ -127,166 +127,229 @@ __global__ void __launch_bounds__(256) gemm_simt_kernel(OpArgs A, OpArgs B, int 
 // bf16 MFMA path.
 // ----------------------------------------------------------------------------
 constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int LDS_PITCH = BK + 8;  // bf16 elements per LDS row (16-byte pad)
+constexpr int EPI_PARTIAL = 100;  // split-K: raw float partial tile
 
-__device__ __forceinline__ u32x4 gelu_vec(u32x4 v, int tanh_form) {
-  uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    w[i] = pack_bf2(gelu_f(bf_lo(w[i]), tanh_form), gelu_f(bf_hi(w[i]), tanh_form));
-  return u32x4{w[0], w[1], w[2], w[3]};
+// LDS operand tile: [128 rows][BK] bf16, 128 bytes per row, its eight 16-byte
+// chunks XOR-swizzled by (row & 7).  An MFMA fragment read (32 rows, one
+// chunk each) and both store patterns below then touch 8 distinct chunks per
+// group of 8 lanes, i.e. all banks once.
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  return row * BK + ((chunk ^ (row & 7)) << 3);
+}
+
+__device__ __forceinline__ uint32_t gelu2(uint32_t w, int tanh_form) {
+  return pack_bf2(gelu_f(bf_lo(w), tanh_form), gelu_f(bf_hi(w), tanh_form));
 }
 
 // Global -> registers for one BK-slice of a 128-row operand tile.
-// Non-transposed: 4 vectors of 8 K-contiguous values per thread.
-// Transposed (stored [k][r]): each thread loads 4 k-rows x 8 r-values.
-struct Stage { u32x4 v[4]; };
+//  row-major (K contiguous): thread t loads 4 vectors of 8 K-values,
+//    (row, chunk) = ((t + 256 i) / 8, (t + 256 i) % 8).
+//  K-major (rows contiguous): thread t = 8 * rq + kb loads 8 K-rows
+//    kb*8 .. kb*8+7, each 4 row-values rq*4 .. rq*4+3 (8 bytes).
+template <int TRANS> struct Stage;
+template <> struct Stage<0> { u32x4 v[4]; };
+template <> struct Stage<1> { uint2 w[8]; };
 
+template <int TRANS, bool GELU>
 __device__ __forceinline__ void stage_load(const OpArgs& a, int r0, int k0, int tanh_form,
-                                           Stage& st) {
+                                           Stage<TRANS>& st) {
   const int t = threadIdx.x;
   const bf16_t* X = (const bf16_t*)a.X;
-  if (!a.trans) {
+  if constexpr (TRANS == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int vix = t + 256 * i;
-      int row = vix >> 3, kv = vix & 7;
-      int r = r0 + row, k = k0 + kv * 8;
+      const int vix = t + 256 * i;
+      const int r = r0 + (vix >> 3), k = k0 + (vix & 7) * 8;
       u32x4 val = {0, 0, 0, 0};
       if (r < a.rows && k < a.kvalid) val = *(const u32x4*)(X + (long)r * a.ld + k);
+      if (GELU) val = u32x4{gelu2(val.x, tanh_form), gelu2(val.y, tanh_form),
+                            gelu2(val.z, tanh_form), gelu2(val.w, tanh_form)};
       st.v[i] = val;
     }
   } else {
-    int blk = t >> 1, half = t & 1;
-    int kb = blk >> 4, rb = blk & 15;
-    int r = r0 + rb * 8;
+    const int kb = t & 7, rq = t >> 3;
+    const int r = r0 + rq * 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int k = k0 + kb * 8 + half * 4 + i;
-      u32x4 val = {0, 0, 0, 0};
-      if (r < a.rows && k < a.kvalid) val = *(const u32x4*)(X + (long)k * a.ld + r);
-      st.v[i] = val;
+    for (int i = 0; i < 8; ++i) {
+      const int k = k0 + kb * 8 + i;
+      uint2 val = make_uint2(0, 0);
+      if (r < a.rows && k < a.kvalid) val = *(const uint2*)(X + (long)k * a.ld + r);
+      if (GELU) val = make_uint2(gelu2(val.x, tanh_form), gelu2(val.y, tanh_form));
+      st.w[i] = val;
     }
-  }
-  if (a.gelu) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) st.v[i] = gelu_vec(st.v[i], tanh_form);
   }
 }
 
-__device__ __forceinline__ void stage_store(const OpArgs& a, const Stage& st, bf16_t* lds) {
+template <int TRANS>
+__device__ __forceinline__ void stage_store(const Stage<TRANS>& st, bf16_t* lds) {
   const int t = threadIdx.x;
-  if (!a.trans) {
+  if constexpr (TRANS == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int vix = t + 256 * i;
-      int row = vix >> 3, kv = vix & 7;
-      *(u32x4*)(lds + row * LDS_PITCH + kv * 8) = st.v[i];
+      const int vix = t + 256 * i;
+      *(u32x4*)(lds + lds_off(vix >> 3, vix & 7)) = st.v[i];
     }
   } else {
-    int blk = t >> 1, half = t & 1;
-    int kb = blk >> 4, rb = blk & 15;
-    // st.v[i] holds k = kb*8+half*4+i, r = rb*8 + 0..7.  Row r of the LDS tile
-    // takes the 4 k-values {v[0][r], v[1][r], v[2][r], v[3][r]}.
-    const uint32_t* w0 = (const uint32_t*)&st.v[0];
-    const uint32_t* w1 = (const uint32_t*)&st.v[1];
-    const uint32_t* w2 = (const uint32_t*)&st.v[2];
-    const uint32_t* w3 = (const uint32_t*)&st.v[3];
+    const int kb = t & 7, rq = t >> 3;
+    // Row rq*4+q of the tile takes the 8 K-values {w[i] element q}, i = 0..7.
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {  // r pairs (2j, 2j+1)
-      uint32_t lo01 = (w0[j] & 0xffffu) | (w1[j] << 16);
-      uint32_t lo23 = (w2[j] & 0xffffu) | (w3[j] << 16);
-      uint32_t hi01 = (w0[j] >> 16) | (w1[j] & 0xffff0000u);
-      uint32_t hi23 = (w2[j] >> 16) | (w3[j] & 0xffff0000u);
-      int row = rb * 8 + 2 * j;
-      int col = kb * 8 + half * 4;
-      *(uint2*)(lds + row * LDS_PITCH + col) = make_uint2(lo01, lo23);
-      *(uint2*)(lds + (row + 1) * LDS_PITCH + col) = make_uint2(hi01, hi23);
+    for (int q = 0; q < 4; ++q) {
+      uint32_t d[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t lo = (q >> 1) ? st.w[2 * p].y : st.w[2 * p].x;
+        const uint32_t hi = (q >> 1) ? st.w[2 * p + 1].y : st.w[2 * p + 1].x;
+        d[p] = (q & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+      }
+      *(u32x4*)(lds + lds_off(rq * 4 + q, kb)) = u32x4{d[0], d[1], d[2], d[3]};
     }
   }
 }
 
-template <bool SPLIT>
+// Epilogue on 8 consecutive columns n..n+7 of row m (n + 8 <= N, rows 16-byte aligned).
+template <int EPI>
+__device__ __forceinline__ void epilogue8(const EpiArgs& e, float* partial, int m, int n,
+                                          float4 v0, float4 v1) {
+  const long o = (long)m * e.ldo + n;
+  float x[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  if constexpr (EPI == EPI_PARTIAL) {
+    float* p = partial + ((long)blockIdx.z * e.M + m) * e.N + n;
+    *(float4*)p = v0;
+    *(float4*)(p + 4) = v1;
+    return;
+  }
+  if constexpr (EPI == GPT_EPI_STORE || EPI == GPT_EPI_RESIDUAL || EPI == GPT_EPI_GELU) {
+    if (e.bias) {
+      float4 b0 = *(const float4*)(e.bias + n), b1 = *(const float4*)(e.bias + n + 4);
+      x[0] += b0.x; x[1] += b0.y; x[2] += b0.z; x[3] += b0.w;
+      x[4] += b1.x; x[5] += b1.y; x[6] += b1.z; x[7] += b1.w;
+    }
+  }
+  if constexpr (EPI == GPT_EPI_STORE || EPI == GPT_EPI_GELU) {
+    u32x4 w{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]), pack_bf2(x[4], x[5]),
+            pack_bf2(x[6], x[7])};
+    *(u32x4*)((bf16_t*)e.out + o) = w;
+    if constexpr (EPI == GPT_EPI_GELU) {
+      if (e.aux) {
+        // GELU of the stored (rounded) pre-activation, as a recompute would see it.
+        u32x4 g{gelu2(w.x, e.tanh_form), gelu2(w.y, e.tanh_form), gelu2(w.z, e.tanh_form),
+                gelu2(w.w, e.tanh_form)};
+        *(u32x4*)((bf16_t*)e.aux + (long)m * e.ldaux + n) = g;
+      }
+    }
+  } else if constexpr (EPI == GPT_EPI_DGELU) {
+    u32x4 u = *(const u32x4*)((const bf16_t*)e.aux + (long)m * e.ldaux + n);
+    const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] *= gelu_grad_f(bf_lo(uw[i]), e.tanh_form);
+      x[2 * i + 1] *= gelu_grad_f(bf_hi(uw[i]), e.tanh_form);
+    }
+    *(u32x4*)((bf16_t*)e.out + o) = u32x4{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]),
+                                           pack_bf2(x[4], x[5]), pack_bf2(x[6], x[7])};
+  } else if constexpr (EPI == GPT_EPI_RESIDUAL) {
+    float4 r0 = *(const float4*)(e.resid + o), r1 = *(const float4*)(e.resid + o + 4);
+    *(float4*)((float*)e.out + o) = make_float4(r0.x + x[0], r0.y + x[1], r0.z + x[2], r0.w + x[3]);
+    *(float4*)((float*)e.out + o + 4) =
+        make_float4(r1.x + x[4], r1.y + x[5], r1.z + x[6], r1.w + x[7]);
+  } else if constexpr (EPI == GPT_EPI_F32) {
+    *(float4*)((float*)e.out + o) = v0;
+    *(float4*)((float*)e.out + o + 4) = v1;
+  } else if constexpr (EPI == GPT_EPI_F32_ACCUM) {
+    float4* p = (float4*)((float*)e.out + o);
+    float4 a0 = p[0], a1 = p[1];
+    p[0] = make_float4(a0.x + x[0], a0.y + x[1], a0.z + x[2], a0.w + x[3]);
+    p[1] = make_float4(a1.x + x[4], a1.y + x[5], a1.z + x[6], a1.w + x[7]);
+  }
+}
+
+template <int AT, int BT, int EPI, bool GA, bool GB>
 __global__ void __launch_bounds__(256, 2) gemm_mfma_kernel(OpArgs A, OpArgs B, int K, int kchunk,
                                                            EpiArgs e, float* partial) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * LDS_PITCH];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * LDS_PITCH];
+  // Two stages of A and B tiles (4 x 16 KB); reused as the 128 x 128 float
+  // output tile by the epilogue.
+  __shared__ __attribute__((aligned(16))) char smem[4 * BM * BK * 2];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int kbeg = blockIdx.z * kchunk;
   const int kend = min(K, kbeg + kchunk);
   const int nk = (kend - kbeg + BK - 1) / BK;
+  // Stage s: A tile at smem + s * 32 KB, B tile 16 KB after it.
+  auto a_tile = [&](int st) { return (bf16_t*)(smem + st * 2 * BM * BK * 2); };
+  auto b_tile = [&](int st) { return (bf16_t*)(smem + st * 2 * BM * BK * 2 + BM * BK * 2); };
 
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  f32x16 acc00 = {}, acc01 = {}, acc10 = {}, acc11 = {};
 
   // The K range of this split is [kbeg, kend); clamp operand validity to it.
   OpArgs a = A, b = B;
   a.kvalid = min(a.kvalid, kend);
   b.kvalid = min(b.kvalid, kend);
 
-  Stage sa, sb;
-  stage_load(a, m0, kbeg, e.tanh_form, sa);
-  stage_load(b, n0, kbeg, e.tanh_form, sb);
-  stage_store(a, sa, As[0]);
-  stage_store(b, sb, Bs[0]);
+  Stage<AT> sa;
+  Stage<BT> sb;
+  stage_load<AT, GA>(a, m0, kbeg, e.tanh_form, sa);
+  stage_load<BT, GB>(b, n0, kbeg, e.tanh_form, sb);
+  stage_store<AT>(sa, a_tile(0));
+  stage_store<BT>(sb, b_tile(0));
   __syncthreads();
 
-  const int frow = lane & 31, fk = (lane >> 5) * 8;
+  const int frow = lane & 31, fg = lane >> 5;
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     const bool more = kt + 1 < nk;
     if (more) {
-      stage_load(a, m0, kbeg + (kt + 1) * BK, e.tanh_form, sa);
-      stage_load(b, n0, kbeg + (kt + 1) * BK, e.tanh_form, sb);
+      stage_load<AT, GA>(a, m0, kbeg + (kt + 1) * BK, e.tanh_form, sa);
+      stage_load<BT, GB>(b, n0, kbeg + (kt + 1) * BK, e.tanh_form, sb);
     }
-    const bf16_t* as = As[cur];
-    const bf16_t* bs = Bs[cur];
+    const bf16_t* as = a_tile(cur);
+    const bf16_t* bs = b_tile(cur);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[2], bfr[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = *(const bf16x8*)(as + (wm * 64 + i * 32 + frow) * LDS_PITCH + ks * 16 + fk);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bfr[j] = *(const bf16x8*)(bs + (wn * 64 + j * 32 + frow) * LDS_PITCH + ks * 16 + fk);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      const int ch = ks * 2 + fg;
+      const bf16x8 a0 = *(const bf16x8*)(as + lds_off(wm * 64 + frow, ch));
+      const bf16x8 a1 = *(const bf16x8*)(as + lds_off(wm * 64 + 32 + frow, ch));
+      const bf16x8 b0 = *(const bf16x8*)(bs + lds_off(wn * 64 + frow, ch));
+      const bf16x8 b1 = *(const bf16x8*)(bs + lds_off(wn * 64 + 32 + frow, ch));
+      acc00 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc00, 0, 0, 0);
+      acc01 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc01, 0, 0, 0);
+      acc10 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc10, 0, 0, 0);
+      acc11 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc11, 0, 0, 0);
     }
     if (more) {
-      stage_store(a, sa, As[cur ^ 1]);
-      stage_store(b, sb, Bs[cur ^ 1]);
+      stage_store<AT>(sa, a_tile(cur ^ 1));
+      stage_store<BT>(sb, b_tile(cur ^ 1));
     }
     __syncthreads();
   }
 
-  // Accumulator layout of a 32x32 MFMA block: column = lane % 32,
-  // row = 8 * (r / 4) + 4 * (lane / 32) + r % 4.
-  const int g = lane >> 5, col = lane & 31;
+  // Accumulators -> LDS float tile [128][128].  32x32 block layout:
+  // column = lane % 32, row = 8 * (r / 4) + 4 * (lane / 32) + r % 4.
+  float* Cs = (float*)smem;
+  {
+    const int rb = wm * 64 + 4 * fg, cb = wn * 64 + frow;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        int n = n0 + wn * 64 + j * 32 + col;
-        if (SPLIT) {
-          if (m < e.M && n < e.N) partial[((long)blockIdx.z * e.M + m) * e.N + n] = acc[i][j][r];
-        } else {
-          epilogue<bf16_t>(e, m, n, acc[i][j][r]);
-        }
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int row = rb + 8 * (r >> 2) + (r & 3);
+      Cs[row * BN + cb] = acc00[r];
+      Cs[row * BN + cb + 32] = acc01[r];
+      Cs[(row + 32) * BN + cb] = acc10[r];
+      Cs[(row + 32) * BN + cb + 32] = acc11[r];
+    }
+  }
+  __syncthreads();
+  // Coalesced epilogue: 16 threads per row, 8 consecutive columns each.
+  const int cg = threadIdx.x & 15;
+  const int n = n0 + cg * 8;
+  if (n >= e.N) return;
+  for (int pass = 0; pass < BM / 16; ++pass) {
+    const int row = pass * 16 + (threadIdx.x >> 4);
+    const int m = m0 + row;
+    if (m >= e.M) break;
+    const float4 v0 = *(const float4*)(Cs + row * BN + cg * 8);
+    const float4 v1 = *(const float4*)(Cs + row * BN + cg * 8 + 4);
+    epilogue8<EPI>(e, partial, m, n, v0, v1);
+  }
 }
 
 template <typename ActT>
@@ -297,6 +360,34 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* partial
     for (int z = 0; z < S; ++z) s += partial[(long)z * total + i];
     epilogue<ActT>(e, (int)(i / e.N), (int)(i % e.N), s);
   }
+}
+
+typedef void (*MfmaKernel)(OpArgs, OpArgs, int, int, EpiArgs, float*);
+
+// The specialisations the training step uses; anything else takes the
+// generic kernel.  Key: (a_trans, b_trans, epilogue, a_gelu, b_gelu).
+MfmaKernel mfma_kernel_for(int at, int bt, int epi, int ga, int gb) {
+#define K_(AT, BT, EP, GA, GB)                                        \
+  if (at == AT && bt == BT && epi == EP && ga == GA && gb == GB)      \
+    return gemm_mfma_kernel<AT, BT, EP, GA, GB>;
+  K_(0, 0, GPT_EPI_STORE, 0, 0)
+  K_(0, 0, GPT_EPI_RESIDUAL, 0, 0)
+  K_(0, 0, GPT_EPI_RESIDUAL, 1, 0)
+  K_(0, 0, GPT_EPI_GELU, 0, 0)
+  K_(0, 0, GPT_EPI_DGELU, 0, 0)
+  K_(0, 0, GPT_EPI_F32, 0, 0)
+  K_(0, 0, GPT_EPI_F32_ACCUM, 0, 0)
+  K_(0, 1, GPT_EPI_STORE, 0, 0)
+  K_(0, 1, GPT_EPI_DGELU, 0, 0)
+  K_(0, 1, GPT_EPI_F32, 0, 0)
+  K_(1, 1, GPT_EPI_F32, 0, 0)
+  K_(1, 1, GPT_EPI_F32_ACCUM, 0, 0)
+  K_(1, 1, EPI_PARTIAL, 0, 0)
+  K_(1, 1, GPT_EPI_F32, 0, 1)
+  K_(1, 1, GPT_EPI_F32_ACCUM, 0, 1)
+  K_(1, 1, EPI_PARTIAL, 0, 1)
+#undef K_
+  return nullptr;
 }
 
 int choose_split(int M, int N, int K) {
@@ -313,6 +404,7 @@ int choose_split(int M, int N, int K) {
 
 int gemm_split_count(const gpt_gemm_desc& d) {
   if (d.precision != GPT_BF16 || d.M <= 0 || d.N <= 0 || d.K <= 0) return 1;
+  if (!d.a_trans || !d.b_trans || d.a_gelu) return 1;  // split-K kernels: weight-gradient layout
   int S = choose_split(d.M, d.N, d.K);
   if (S > 1 && (d.workspace == nullptr || d.workspace_bytes < (int64_t)S * d.M * d.N * 4)) S = 1;
   if (S == 1) return 1;
@@ -349,13 +441,23 @@ hipError_t gemm(const gpt_gemm_desc& d, hipStream_t s) {
     return hipGetLastError();
   }
   int S = gemm_split_count(d);
+  const bool vec_ok = d.N % 8 == 0 && d.ldo % 8 == 0 && (d.aux == nullptr || d.ldaux % 8 == 0);
+  MfmaKernel kern = vec_ok ? mfma_kernel_for(d.a_trans, d.b_trans, S > 1 ? EPI_PARTIAL : d.epilogue,
+                                             d.a_gelu, d.b_gelu)
+                           : nullptr;
+  if (kern == nullptr) {
+    // Combinations the step never issues: the generic kernel (bf16 inputs).
+    dim3 grid((unsigned)cdiv(d.N, 64), (unsigned)cdiv(d.M, 64));
+    gemm_simt_kernel<bf16_t, bf16_t><<<grid, 256, 0, s>>>(A, B, d.K, e);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)cdiv(d.N, BN), (unsigned)cdiv(d.M, BM), (unsigned)S);
   if (S == 1) {
-    gemm_mfma_kernel<false><<<grid, 256, 0, s>>>(A, B, d.K, d.K, e, nullptr);
+    kern<<<grid, 256, 0, s>>>(A, B, d.K, d.K, e, nullptr);
     return hipGetLastError();
   }
   const int kchunk = (int)cdiv(cdiv(d.K, S), BK) * BK;
-  gemm_mfma_kernel<true><<<grid, 256, 0, s>>>(A, B, d.K, kchunk, e, (float*)d.workspace);
+  kern<<<grid, 256, 0, s>>>(A, B, d.K, kchunk, e, (float*)d.workspace);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   long total = (long)d.M * d.N;
