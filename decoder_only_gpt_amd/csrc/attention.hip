@@ -75,6 +75,35 @@ __global__ void __launch_bounds__(256) attn_fwd_rows(const T* qkv, T* out, float
 }
 
 // D[b,h,i] = sum_d dO[i,d] * O[i,d]  (one thread per (row, head)).
+// bf16: one wave per token row; a lane takes 8 consecutive head dims (16-byte
+// loads) and the hd/8 lanes of a head combine by butterfly shuffles.
+template <int HD>
+__global__ void __launch_bounds__(256) attn_dvec_bf16(const bf16_t* out, const bf16_t* dout,
+                                                      float* D, int M, int Tn, int H) {
+  constexpr int LPH = HD / 8;  // lanes per head
+  const int lane = threadIdx.x & 63;
+  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const int C = H * HD;
+  const int b = (int)(row / Tn), t = (int)(row % Tn);
+  for (int v0 = 0; v0 < C / 8; v0 += 64) {
+    const int v = v0 + lane;
+    float s = 0.f;
+    if (v < C / 8) {
+      u32x4 a = *(const u32x4*)(out + row * C + v * 8);
+      u32x4 g = *(const u32x4*)(dout + row * C + v * 8);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) s += bf_lo(a[k]) * bf_lo(g[k]) + bf_hi(a[k]) * bf_hi(g[k]);
+    }
+#pragma unroll
+    for (int o = 1; o < LPH; o <<= 1) s += __shfl_xor(s, o, 64);
+    if (v < C / 8 && (lane % LPH) == 0) {
+      const int h = v / LPH;
+      D[((long)b * H + h) * Tn + t] = s;
+    }
+  }
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256) attn_dvec(const T* out, const T* dout, float* D, int B,
                                                  int Tn, int H, int hd) {
@@ -199,40 +228,47 @@ __device__ __forceinline__ void lds_rows(const bf16_t* src, long ld, int row0, i
   }
 }
 
-// The same 64 x HD block stored transposed: dst[d][r] (pitch >= 64 + pad).
+// The same 64 x HD block stored transposed: dst[d][key], 64 keys (128 bytes)
+// per row, 16-byte chunks XOR-swizzled by (d & 7).  A thread moves one 8 x 8
+// block: eight 16-byte row loads, an in-register transpose, eight 16-byte
+// LDS stores; the 8 lanes of a store group hit 8 distinct chunks.
+__device__ __forceinline__ int tswz(int d, int key) {
+  return d * KB + ((((key >> 3) ^ (d & 7))) << 3) + (key & 7);
+}
+
 template <int HD>
 __device__ __forceinline__ void lds_rows_t(const bf16_t* src, long ld, int row0, int nrows,
-                                           bf16_t* dst, int pitch) {
-  constexpr int DV = HD / 8;
-  for (int u = threadIdx.x; u < (KB / 4) * DV; u += 256) {
-    int rg = u / DV, dv = u % DV;
-    u32x4 w[4];
+                                           bf16_t* dst) {
+  constexpr int DB = HD / 8;
+  for (int u = threadIdx.x; u < 8 * DB; u += 256) {
+    const int kb = u & 7, db = u >> 3;
+    u32x4 w[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int r = row0 + rg * 4 + i;
+    for (int i = 0; i < 8; ++i) {
+      const int r = row0 + kb * 8 + i;
       w[i] = u32x4{0, 0, 0, 0};
-      if (r < nrows) w[i] = *(const u32x4*)(src + (long)r * ld + dv * 8);
+      if (r < nrows) w[i] = *(const u32x4*)(src + (long)r * ld + db * 8);
     }
-    const uint32_t* w0 = (const uint32_t*)&w[0];
-    const uint32_t* w1 = (const uint32_t*)&w[1];
-    const uint32_t* w2 = (const uint32_t*)&w[2];
-    const uint32_t* w3 = (const uint32_t*)&w[3];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int d = dv * 8 + 2 * j;
-      *(uint2*)(dst + d * pitch + rg * 4) =
-          make_uint2((w0[j] & 0xffffu) | (w1[j] << 16), (w2[j] & 0xffffu) | (w3[j] << 16));
-      *(uint2*)(dst + (d + 1) * pitch + rg * 4) =
-          make_uint2((w0[j] >> 16) | (w1[j] & 0xffff0000u), (w2[j] >> 16) | (w3[j] & 0xffff0000u));
+    for (int j = 0; j < 8; ++j) {
+      const int d = db * 8 + j;
+      u32x4 o;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t lo = w[2 * p][j >> 1], hi = w[2 * p + 1][j >> 1];
+        o[p] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+      }
+      *(u32x4*)(dst + tswz(d, kb * 8)) = o;
     }
   }
 }
 
-// 8 bf16 from two 8-byte LDS reads: elements (base + 4g + 0..3) and (base + 8 + 4g + 0..3)
-// of row `row` — the k-slot order of a 32x32 accumulator handed on as an operand.
-__device__ __forceinline__ bf16x8 lds_slots(const bf16_t* t, int pitch, int row, int base, int g) {
-  uint2 a = *(const uint2*)(t + row * pitch + base + 4 * g);
-  uint2 b = *(const uint2*)(t + row * pitch + base + 8 + 4 * g);
+// 8 bf16 of row `row` of a transposed tile: keys (base + 4g + 0..3) and
+// (base + 8 + 4g + 0..3) — the k-slot order of a 32x32 accumulator handed on
+// as an operand (base % 16 == 0).
+__device__ __forceinline__ bf16x8 lds_slots(const bf16_t* t, int row, int base, int g) {
+  uint2 a = *(const uint2*)(t + tswz(row, base + 4 * g));
+  uint2 b = *(const uint2*)(t + tswz(row, base + 8 + 4 * g));
   u32x4 v{a.x, a.y, b.x, b.y};
   return *(bf16x8*)&v;
 }
@@ -249,9 +285,9 @@ __device__ __forceinline__ int acc_row(int r, int g) { return 8 * (r >> 2) + 4 *
 template <int HD>
 __global__ void __launch_bounds__(256) attn_fwd_mfma(const bf16_t* qkv, bf16_t* out, float* lse,
                                                      int Tn, int H, int left, float scale_log2) {
-  constexpr int KP = HD + 8, VP = KB + 8, NS = HD / 16, ND = HD / 32;
+  constexpr int KP = HD + 8, NS = HD / 16, ND = HD / 32;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[KB * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[HD * VP];
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[HD * KB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, c = lane & 31;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -280,10 +316,12 @@ __global__ void __launch_bounds__(256) attn_fwd_mfma(const bf16_t* qkv, bf16_t* 
   for (int kb0 = (kfirst / KB) * KB; kb0 <= qlast; kb0 += KB) {
     __syncthreads();
     lds_rows<HD>(base + C + h * HD, ld, kb0, Tn, Ks, KP);
-    lds_rows_t<HD>(base + 2 * C + h * HD, ld, kb0, Tn, Vt, VP);
+    lds_rows_t<HD>(base + 2 * C + h * HD, ld, kb0, Tn, Vt);
     __syncthreads();
     const bool skip = kb0 > qw0 + 31 || (left >= 0 && kb0 + KB - 1 < qw0 - left);
     if (skip) continue;
+    // every (query, key) of this wave and block visible: no per-element mask
+    const bool full = kb0 + KB - 1 <= qw0 && qw0 + 31 < Tn && (left < 0 || qw0 + 31 - kb0 <= left);
     f32x16 s[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -301,7 +339,7 @@ __global__ void __launch_bounds__(256) attn_fwd_mfma(const bf16_t* qkv, bf16_t* 
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         int j = kb0 + kk * 32 + acc_row(r, g);
-        float v = visible(qi, j, left, Tn) ? s[kk][r] * scale_log2 : -INFINITY;
+        float v = (full || visible(qi, j, left, Tn)) ? s[kk][r] * scale_log2 : -INFINITY;
         s[kk][r] = v;
         mx = fmaxf(mx, v);
       }
@@ -331,7 +369,7 @@ __global__ void __launch_bounds__(256) attn_fwd_mfma(const bf16_t* qkv, bf16_t* 
         bf16x8 pf = acc_slots(s[kk], s2);
 #pragma unroll
         for (int d = 0; d < ND; ++d) {
-          bf16x8 vf = lds_slots(Vt, VP, d * 32 + c, kk * 32 + 16 * s2, g);
+          bf16x8 vf = lds_slots(Vt, d * 32 + c, kk * 32 + 16 * s2, g);
           o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[d], 0, 0, 0);
         }
       }
@@ -358,11 +396,11 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma(const bf16_t* qkv, const fl
                                                      const bf16_t* dout, const float* D,
                                                      bf16_t* dqkv, int Tn, int H, int left,
                                                      float scale, float scale_log2) {
-  constexpr int RP = HD + 8, TP = KB + 8, NS = HD / 16, ND = HD / 32;
+  constexpr int RP = HD + 8, NS = HD / 16, ND = HD / 32;
   __shared__ __attribute__((aligned(16))) bf16_t Qs[KB * RP];
-  __shared__ __attribute__((aligned(16))) bf16_t Qt[HD * TP];
+  __shared__ __attribute__((aligned(16))) bf16_t Qt[HD * KB];
   __shared__ __attribute__((aligned(16))) bf16_t Gs[KB * RP];
-  __shared__ __attribute__((aligned(16))) bf16_t Gt[HD * TP];
+  __shared__ __attribute__((aligned(16))) bf16_t Gt[HD * KB];
   __shared__ float Ls[KB], Ds[KB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, c = lane & 31;
@@ -398,9 +436,9 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma(const bf16_t* qkv, const fl
   for (int qb0 = (kblk0 / KB) * KB; qb0 <= qend; qb0 += KB) {
     __syncthreads();
     lds_rows<HD>(base + h * HD, ld, qb0, Tn, Qs, RP);
-    lds_rows_t<HD>(base + h * HD, ld, qb0, Tn, Qt, TP);
+    lds_rows_t<HD>(base + h * HD, ld, qb0, Tn, Qt);
     lds_rows<HD>(gbase + h * HD, C, qb0, Tn, Gs, RP);
-    lds_rows_t<HD>(gbase + h * HD, C, qb0, Tn, Gt, TP);
+    lds_rows_t<HD>(gbase + h * HD, C, qb0, Tn, Gt);
     if (threadIdx.x < KB) {
       int q = qb0 + threadIdx.x;
       Ls[threadIdx.x] = q < Tn ? lrow[q] * LOG2E : 0.f;
@@ -409,6 +447,7 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma(const bf16_t* qkv, const fl
     __syncthreads();
     const bool skip = qb0 + KB - 1 < kw0 || (left >= 0 && qb0 > kw0 + 31 + left);
     if (skip) continue;
+    const bool full = qb0 >= kw0 + 31 && qb0 + KB - 1 < Tn && (left < 0 || qb0 + KB - 1 - kw0 <= left);
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq) {
       f32x16 s, dp;
@@ -426,7 +465,8 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma(const bf16_t* qkv, const fl
       for (int r = 0; r < 16; ++r) {
         int ql = qq * 32 + acc_row(r, g);
         int qi = qb0 + ql;
-        float p = (qi < Tn && visible(qi, kj, left, Tn)) ? exp2f(s[r] * scale_log2 - Ls[ql]) : 0.f;
+        float p = (full || (qi < Tn && visible(qi, kj, left, Tn))) ? exp2f(s[r] * scale_log2 - Ls[ql])
+                                                                   : 0.f;
         s[r] = p;
         dp[r] = p * (dp[r] - Ds[ql]);
       }
@@ -436,8 +476,8 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma(const bf16_t* qkv, const fl
         bf16x8 da = acc_slots(dp, s2);
 #pragma unroll
         for (int d = 0; d < ND; ++d) {
-          bf16x8 gb = lds_slots(Gt, TP, d * 32 + c, qq * 32 + 16 * s2, g);
-          bf16x8 qb = lds_slots(Qt, TP, d * 32 + c, qq * 32 + 16 * s2, g);
+          bf16x8 gb = lds_slots(Gt, d * 32 + c, qq * 32 + 16 * s2, g);
+          bf16x8 qb = lds_slots(Qt, d * 32 + c, qq * 32 + 16 * s2, g);
           dv[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, gb, dv[d], 0, 0, 0);
           dk[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, qb, dk[d], 0, 0, 0);
         }
@@ -464,9 +504,9 @@ __global__ void __launch_bounds__(256) attn_dq_mfma(const bf16_t* qkv, const flo
                                                     const bf16_t* dout, const float* D,
                                                     bf16_t* dqkv, int Tn, int H, int left,
                                                     float scale, float scale_log2) {
-  constexpr int RP = HD + 8, TP = KB + 8, NS = HD / 16, ND = HD / 32;
+  constexpr int RP = HD + 8, NS = HD / 16, ND = HD / 32;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[KB * RP];
-  __shared__ __attribute__((aligned(16))) bf16_t Kt[HD * TP];
+  __shared__ __attribute__((aligned(16))) bf16_t Kt[HD * KB];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[KB * RP];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, c = lane & 31;
@@ -502,11 +542,12 @@ __global__ void __launch_bounds__(256) attn_dq_mfma(const bf16_t* qkv, const flo
   for (int kb0 = (kfirst / KB) * KB; kb0 <= qlast; kb0 += KB) {
     __syncthreads();
     lds_rows<HD>(base + C + h * HD, ld, kb0, Tn, Ks, RP);
-    lds_rows_t<HD>(base + C + h * HD, ld, kb0, Tn, Kt, TP);
+    lds_rows_t<HD>(base + C + h * HD, ld, kb0, Tn, Kt);
     lds_rows<HD>(base + 2 * C + h * HD, ld, kb0, Tn, Vs, RP);
     __syncthreads();
     const bool skip = kb0 > qw0 + 31 || (left >= 0 && kb0 + KB - 1 < qw0 - left);
     if (skip) continue;
+    const bool full = kb0 + KB - 1 <= qw0 && qw0 + 31 < Tn && (left < 0 || qw0 + 31 - kb0 <= left);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       f32x16 s, dp;
@@ -523,7 +564,8 @@ __global__ void __launch_bounds__(256) attn_dq_mfma(const bf16_t* qkv, const flo
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         int j = kb0 + kk * 32 + acc_row(r, g);
-        float p = (qi < Tn && visible(qi, j, left, Tn)) ? exp2f(s[r] * scale_log2 - Lq) : 0.f;
+        float p = (full || (qi < Tn && visible(qi, j, left, Tn))) ? exp2f(s[r] * scale_log2 - Lq)
+                                                                  : 0.f;
         dp[r] = p * (dp[r] - Dq);
       }
 #pragma unroll
@@ -531,7 +573,7 @@ __global__ void __launch_bounds__(256) attn_dq_mfma(const bf16_t* qkv, const flo
         bf16x8 da = acc_slots(dp, s2);
 #pragma unroll
         for (int d = 0; d < ND; ++d) {
-          bf16x8 kb = lds_slots(Kt, TP, d * 32 + c, kk * 32 + 16 * s2, g);
+          bf16x8 kb = lds_slots(Kt, d * 32 + c, kk * 32 + 16 * s2, g);
           dq[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, kb, dq[d], 0, 0, 0);
         }
       }
@@ -600,8 +642,14 @@ hipError_t attention_bwd(int prec, int B, int T, int H, int hd, int left, const 
   if (!attention_supported(prec, hd)) return hipErrorInvalidValue;
   long rows = (long)B * T * H;
   if (prec == GPT_BF16) {
-    attn_dvec<bf16_t><<<(unsigned)cdiv(rows, 256), 256, 0, s>>>(
-        (const bf16_t*)out, (const bf16_t*)dout, dvec, B, T, H, hd);
+    const long M = (long)B * T;
+    const unsigned g = (unsigned)cdiv(M, 4);
+    if (hd == 32)
+      attn_dvec_bf16<32><<<g, 256, 0, s>>>((const bf16_t*)out, (const bf16_t*)dout, dvec, (int)M, T, H);
+    else if (hd == 64)
+      attn_dvec_bf16<64><<<g, 256, 0, s>>>((const bf16_t*)out, (const bf16_t*)dout, dvec, (int)M, T, H);
+    else
+      attn_dvec_bf16<128><<<g, 256, 0, s>>>((const bf16_t*)out, (const bf16_t*)dout, dvec, (int)M, T, H);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (hd == 32) return launch_bwd<32>(B, T, H, left, qkv, lse, dout, dvec, dqkv, s);

@@ -179,8 +179,8 @@ Arena plan_arena(const gpt_config& c, int B, int T) {
   ws_need(Vp, C, M);
   a.gemm_ws_bytes = ws;
   a.gemm_ws = take(std::max<int64_t>(ws, 16));
-  a.cs_part = take((int64_t)gpt::colsum_partial_rows((int)M) * std::max(3 * C, F) * 4 + 16);
-  a.ln_part = take(2 * (int64_t)gpt::layernorm_bwd_partial_rows((int)M) * C * 4 + 16);
+  a.cs_part = take(gpt::colsum_partial_floats((int)M, (int)std::max(3 * C, F)) * 4 + 16);
+  a.ln_part = take(gpt::layernorm_bwd_partial_floats((int)M, (int)C) * 4 + 16);
   a.e_counts = take(Vp * 4);
   a.e_offsets = take(Vp * 4);
   a.e_perm = take(M * 4);

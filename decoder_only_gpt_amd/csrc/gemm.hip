@@ -141,69 +141,78 @@ __device__ __forceinline__ uint32_t gelu2(uint32_t w, int tanh_form) {
   return pack_bf2(gelu_f(bf_lo(w), tanh_form), gelu_f(bf_hi(w), tanh_form));
 }
 
-// Global -> registers for one BK-slice of a 128-row operand tile.
-//  row-major (K contiguous): thread t loads 4 vectors of 8 K-values,
-//    (row, chunk) = ((t + 256 i) / 8, (t + 256 i) % 8).
-//  K-major (rows contiguous): thread t = 8 * rq + kb loads 8 K-rows
-//    kb*8 .. kb*8+7, each 4 row-values rq*4 .. rq*4+3 (8 bytes).
-template <int TRANS> struct Stage;
-template <> struct Stage<0> { u32x4 v[4]; };
-template <> struct Stage<1> { uint2 w[8]; };
+// Global -> registers for one BK-slice of a 128-row operand tile: 4 vectors
+// of 8 bf16 per thread, full 16-byte coalesced loads in both layouts.
+//  row-major (K contiguous): vector (row, chunk) = (v / 8, v % 8), v = t + 256 i.
+//  K-major (rows contiguous): vector (k, rchunk) = (v / 16, v % 16); the tile
+//    lands in LDS untransposed as [BK][128] and the MFMA fragments are read
+//    with the LDS transpose read (see tr_frag).
+struct Stage { u32x4 v[4]; };
 
 template <int TRANS, bool GELU>
 __device__ __forceinline__ void stage_load(const OpArgs& a, int r0, int k0, int tanh_form,
-                                           Stage<TRANS>& st) {
+                                           Stage& st) {
   const int t = threadIdx.x;
   const bf16_t* X = (const bf16_t*)a.X;
-  if constexpr (TRANS == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int vix = t + 256 * i;
+  for (int i = 0; i < 4; ++i) {
+    const int vix = t + 256 * i;
+    u32x4 val = {0, 0, 0, 0};
+    if constexpr (TRANS == 0) {
       const int r = r0 + (vix >> 3), k = k0 + (vix & 7) * 8;
-      u32x4 val = {0, 0, 0, 0};
       if (r < a.rows && k < a.kvalid) val = *(const u32x4*)(X + (long)r * a.ld + k);
-      if (GELU) val = u32x4{gelu2(val.x, tanh_form), gelu2(val.y, tanh_form),
-                            gelu2(val.z, tanh_form), gelu2(val.w, tanh_form)};
-      st.v[i] = val;
+    } else {
+      const int k = k0 + (vix >> 4), r = r0 + (vix & 15) * 8;
+      if (r < a.rows && k < a.kvalid) val = *(const u32x4*)(X + (long)k * a.ld + r);
     }
-  } else {
-    const int kb = t & 7, rq = t >> 3;
-    const int r = r0 + rq * 4;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int k = k0 + kb * 8 + i;
-      uint2 val = make_uint2(0, 0);
-      if (r < a.rows && k < a.kvalid) val = *(const uint2*)(X + (long)k * a.ld + r);
-      if (GELU) val = make_uint2(gelu2(val.x, tanh_form), gelu2(val.y, tanh_form));
-      st.w[i] = val;
-    }
+    if (GELU) val = u32x4{gelu2(val.x, tanh_form), gelu2(val.y, tanh_form),
+                          gelu2(val.z, tanh_form), gelu2(val.w, tanh_form)};
+    st.v[i] = val;
   }
 }
 
+// K-major LDS tile [BK][128]: 256-byte rows whose four 64-byte granules are
+// XOR-swizzled by (k & 3), so the 4 K-rows a transpose read touches at once
+// sit in different banks.
+__device__ __forceinline__ int lds_off_t(int k, int r) { return k * 128 + (r ^ ((k & 3) << 5)); }
+
 template <int TRANS>
-__device__ __forceinline__ void stage_store(const Stage<TRANS>& st, bf16_t* lds) {
+__device__ __forceinline__ void stage_store(const Stage& st, bf16_t* lds) {
   const int t = threadIdx.x;
-  if constexpr (TRANS == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int vix = t + 256 * i;
+  for (int i = 0; i < 4; ++i) {
+    const int vix = t + 256 * i;
+    if constexpr (TRANS == 0)
       *(u32x4*)(lds + lds_off(vix >> 3, vix & 7)) = st.v[i];
-    }
-  } else {
-    const int kb = t & 7, rq = t >> 3;
-    // Row rq*4+q of the tile takes the 8 K-values {w[i] element q}, i = 0..7.
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t d[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t lo = (q >> 1) ? st.w[2 * p].y : st.w[2 * p].x;
-        const uint32_t hi = (q >> 1) ? st.w[2 * p + 1].y : st.w[2 * p + 1].x;
-        d[p] = (q & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-      }
-      *(u32x4*)(lds + lds_off(rq * 4 + q, kb)) = u32x4{d[0], d[1], d[2], d[3]};
-    }
+    else
+      *(u32x4*)(lds + lds_off_t(vix >> 4, (vix & 15) * 8)) = st.v[i];
   }
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// MFMA 32x32x16 operand fragment (row r0 + lane % 32, k-slots 16 ks + 8 (lane / 32)
+// + 0..7) from a K-major tile with two LDS transpose reads.  Within each group
+// of 16 lanes, source lane s = a + 4 b supplies the 4 values at (k = kb + b,
+// rows 4a .. 4a + 3); lane j of the group then receives rows j, k = kb .. kb + 3.
+__device__ __forceinline__ bf16x8 tr_frag(const bf16_t* lds, int r0, int ks, int lane) {
+  const int s = lane & 15, grp = lane >> 4;
+  const int r = r0 + 16 * (grp & 1) + 4 * (s & 3);
+  const int kb = ks * 16 + 8 * (grp >> 1) + (s >> 2);
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds + lds_off_t(kb, r)));
+  v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds + lds_off_t(kb + 4, r)));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return *(bf16x8*)&v;
+}
+
+template <int TRANS>
+__device__ __forceinline__ bf16x8 frag(const bf16_t* lds, int r0, int ks, int lane) {
+  if constexpr (TRANS == 0)
+    return *(const bf16x8*)(lds + lds_off(r0 + (lane & 31), ks * 2 + (lane >> 5)));
+  else
+    return tr_frag(lds, r0, ks, lane);
 }
 
 // Epilogue on 8 consecutive columns n..n+7 of row m (n + 8 <= N, rows 16-byte aligned).
@@ -286,8 +295,7 @@ __global__ void __launch_bounds__(256, 2) gemm_mfma_kernel(OpArgs A, OpArgs B, i
   a.kvalid = min(a.kvalid, kend);
   b.kvalid = min(b.kvalid, kend);
 
-  Stage<AT> sa;
-  Stage<BT> sb;
+  Stage sa, sb;
   stage_load<AT, GA>(a, m0, kbeg, e.tanh_form, sa);
   stage_load<BT, GB>(b, n0, kbeg, e.tanh_form, sb);
   stage_store<AT>(sa, a_tile(0));
@@ -306,11 +314,10 @@ __global__ void __launch_bounds__(256, 2) gemm_mfma_kernel(OpArgs A, OpArgs B, i
     const bf16_t* bs = b_tile(cur);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      const int ch = ks * 2 + fg;
-      const bf16x8 a0 = *(const bf16x8*)(as + lds_off(wm * 64 + frow, ch));
-      const bf16x8 a1 = *(const bf16x8*)(as + lds_off(wm * 64 + 32 + frow, ch));
-      const bf16x8 b0 = *(const bf16x8*)(bs + lds_off(wn * 64 + frow, ch));
-      const bf16x8 b1 = *(const bf16x8*)(bs + lds_off(wn * 64 + 32 + frow, ch));
+      const bf16x8 a0 = frag<AT>(as, wm * 64, ks, lane);
+      const bf16x8 a1 = frag<AT>(as, wm * 64 + 32, ks, lane);
+      const bf16x8 b0 = frag<BT>(bs, wn * 64, ks, lane);
+      const bf16x8 b1 = frag<BT>(bs, wn * 64 + 32, ks, lane);
       acc00 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc00, 0, 0, 0);
       acc01 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc01, 0, 0, 0);
       acc10 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc10, 0, 0, 0);

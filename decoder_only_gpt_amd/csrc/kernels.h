@@ -41,10 +41,14 @@ hipError_t layernorm_bwd(int prec, const void* dy, const float* x, const float* 
                          float* dx, void* dx_act, float* dw, float* db, int accumulate,
                          float* partials, hipStream_t s);
 int layernorm_bwd_partial_rows(int M);
+// Floats of `partials` layernorm_bwd needs.
+int64_t layernorm_bwd_partial_floats(int M, int C);
 // Column sums of an act-type [M, N] matrix into out[N] (overwrite or add).
 hipError_t colsum(int prec, const void* x, int M, int N, float* out, int accumulate,
                   float* partials, hipStream_t s);
 int colsum_partial_rows(int M);
+// Floats of `partials` colsum needs.
+int64_t colsum_partial_floats(int M, int N);
 // Fused softmax cross-entropy on logits [M, ldz] (act type): loss_rows[m],
 // logits overwritten by d(mean loss)/dlogits (0 for columns >= V).
 hipError_t cross_entropy(int prec, void* logits, int M, int V, int ldz, const int32_t* tgt,

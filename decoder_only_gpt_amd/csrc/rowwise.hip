@@ -121,11 +121,22 @@ __global__ void __launch_bounds__(256) embed_wpe_kernel(const float* dx, int M, 
 }
 
 // ------------------------------------------------------------------ LayerNorm
-constexpr int LN_NV = 8;        // float4 vectors per lane -> C <= 2048
-constexpr int LN_BWD_RPW = 8;   // rows per wave in the backward
-constexpr int LN_BWD_RPB = 32;  // rows per workgroup in the backward
+// 4 consecutive act-type values at element offset o (o % 4 == 0).
+__device__ __forceinline__ void store4(float* p, long o, float4 v) { *(float4*)(p + o) = v; }
+__device__ __forceinline__ void store4(bf16_t* p, long o, float4 v) {
+  *(uint2*)(p + o) = make_uint2(pack_bf2(v.x, v.y), pack_bf2(v.z, v.w));
+}
+__device__ __forceinline__ float4 load4(const float* p, long o) { return *(const float4*)(p + o); }
+__device__ __forceinline__ float4 load4(const bf16_t* p, long o) {
+  uint2 u = *(const uint2*)(p + o);
+  return make_float4(bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y));
+}
 
-template <typename ActT>
+constexpr int LN_NV_MAX = 8;    // float4 vectors per lane -> C <= 2048
+constexpr int LN_BWD_RPW = 4;   // rows per wave in the backward
+constexpr int LN_BWD_RPB = 16;  // rows per workgroup in the backward
+
+template <typename ActT, int LN_NV>
 __global__ void __launch_bounds__(256) ln_fwd_kernel(const float* x, const float* w, const float* b,
                                                      int M, int C, float eps, ActT* y, float* mean,
                                                      float* rstd) {
@@ -160,11 +171,9 @@ __global__ void __launch_bounds__(256) ln_fwd_kernel(const float* x, const float
     if (c < C4) {
       float4 ww = ((const float4*)w)[c];
       float4 bb = b ? ((const float4*)b)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-      long o = (long)row * C + 4 * c;
-      Act<ActT>::store(y, o + 0, (v[i].x - mu) * rs * ww.x + bb.x);
-      Act<ActT>::store(y, o + 1, (v[i].y - mu) * rs * ww.y + bb.y);
-      Act<ActT>::store(y, o + 2, (v[i].z - mu) * rs * ww.z + bb.z);
-      Act<ActT>::store(y, o + 3, (v[i].w - mu) * rs * ww.w + bb.w);
+      store4(y, (long)row * C + 4 * c,
+             make_float4((v[i].x - mu) * rs * ww.x + bb.x, (v[i].y - mu) * rs * ww.y + bb.y,
+                         (v[i].z - mu) * rs * ww.z + bb.z, (v[i].w - mu) * rs * ww.w + bb.w));
     }
   }
   if (lane == 0) {
@@ -175,7 +184,7 @@ __global__ void __launch_bounds__(256) ln_fwd_kernel(const float* x, const float
 
 // dx = resid_in + rstd * (dxhat - mean(dxhat) - xhat * mean(dxhat * xhat)), dxhat = dy * w.
 // Per-workgroup partial sums of dy*xhat and dy go to partials[2][nblk][C].
-template <typename ActT>
+template <typename ActT, int LN_NV>
 __global__ void __launch_bounds__(256) ln_bwd_kernel(const ActT* dy, const float* x,
                                                      const float* mean, const float* rstd,
                                                      const float* w, const float* resid_in, int M,
@@ -199,9 +208,7 @@ __global__ void __launch_bounds__(256) ln_bwd_kernel(const ActT* dy, const float
       if (c < C4) {
         float4 xv = ((const float4*)(x + (long)row * C))[c];
         float4 ww = ((const float4*)w)[c];
-        long o = (long)row * C + 4 * c;
-        g[i] = make_float4(Act<ActT>::load(dy, o), Act<ActT>::load(dy, o + 1),
-                           Act<ActT>::load(dy, o + 2), Act<ActT>::load(dy, o + 3));
+        g[i] = load4(dy, (long)row * C + 4 * c);
         xh[i] = make_float4((xv.x - mu) * rs, (xv.y - mu) * rs, (xv.z - mu) * rs, (xv.w - mu) * rs);
         dh[i] = make_float4(g[i].x * ww.x, g[i].y * ww.y, g[i].z * ww.z, g[i].w * ww.w);
         s1 += (dh[i].x + dh[i].y) + (dh[i].z + dh[i].w);
@@ -224,10 +231,7 @@ __global__ void __launch_bounds__(256) ln_bwd_kernel(const ActT* dy, const float
                                r.z + rs * (dh[i].z - c1 - xh[i].z * c2),
                                r.w + rs * (dh[i].w - c1 - xh[i].w * c2));
         ((float4*)(dx + (long)row * C))[c] = d;
-        Act<ActT>::store(dx_act, o + 0, d.x);
-        Act<ActT>::store(dx_act, o + 1, d.y);
-        Act<ActT>::store(dx_act, o + 2, d.z);
-        Act<ActT>::store(dx_act, o + 3, d.w);
+        store4(dx_act, o, d);
       }
     }
   }
@@ -249,30 +253,91 @@ __global__ void __launch_bounds__(256) ln_bwd_kernel(const ActT* dy, const float
   }
 }
 
-// out[c] (+)= sum over rows r of part[r, c], rows in increasing order.
-__global__ void __launch_bounds__(256) reduce_rows_kernel(const float* part, int R, int N,
-                                                          float* out, int accumulate) {
-  int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= N || out == nullptr) return;
+// out[c] (+)= sum over rows r of part[r, c], in two fixed-order stages.
+// Stage 1: workgroup (x, y) owns 64 columns and rows [y*RS, (y+1)*RS); wave w
+// sums rows w, w+4, ... of that slice and the four wave sums are added in wave
+// order -> stage[y][c].  Stage 2 adds the RED_SLICES rows of `stage` in order.
+constexpr int RED_SLICES = 16;
+__global__ void __launch_bounds__(256) reduce_rows_stage1(const float* part, int R, int N,
+                                                          float* stage) {
+  __shared__ float red[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + lane;
+  const int rs = (R + RED_SLICES - 1) / RED_SLICES;
+  const int r0 = blockIdx.y * rs, r1 = min(R, r0 + rs);
   float s = 0.f;
-  for (int r = 0; r < R; ++r) s += part[(long)r * N + c];
-  out[c] = accumulate ? out[c] + s : s;
+  if (c < N) {
+    int r = r0 + wave;
+    for (; r + 12 < r1; r += 16) {  // four independent loads in flight
+      float a = part[(long)r * N + c], b = part[(long)(r + 4) * N + c];
+      float d = part[(long)(r + 8) * N + c], e = part[(long)(r + 12) * N + c];
+      s += ((a + b) + d) + e;
+    }
+    for (; r < r1; r += 4) s += part[(long)r * N + c];
+  }
+  red[wave][lane] = s;
+  __syncthreads();
+  if (wave == 0 && c < N)
+    stage[(long)blockIdx.y * N + c] = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+}
+
+__global__ void __launch_bounds__(256) reduce_rows_stage2(const float* stage, int N, float* out,
+                                                          int accumulate) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= N || out == nullptr) return;
+  float t = 0.f;
+#pragma unroll
+  for (int y = 0; y < RED_SLICES; ++y) t += stage[(long)y * N + c];
+  out[c] = accumulate ? out[c] + t : t;
+}
+
+// `stage` holds RED_SLICES * N floats.
+hipError_t reduce_rows(const float* part, int R, int N, float* out, int accumulate, float* stage,
+                       hipStream_t s) {
+  if (out == nullptr) return hipSuccess;
+  reduce_rows_stage1<<<dim3((unsigned)cdiv(N, 64), RED_SLICES), 256, 0, s>>>(part, R, N, stage);
+  reduce_rows_stage2<<<(unsigned)cdiv(N, 256), 256, 0, s>>>(stage, N, out, accumulate);
+  return hipGetLastError();
 }
 
 // Column sums of an act matrix [M, N]: partial[chunk, n] over 64-row chunks.
+// A wave covers 64 x (16 / sizeof) consecutive columns with 16-byte loads;
+// the four waves of a workgroup take rows w, w+4, ... of the chunk and are
+// added in wave order.
 constexpr int CS_ROWS = 64;
 template <typename ActT>
 __global__ void __launch_bounds__(256) colsum_kernel(const ActT* x, int M, int N, float* partial) {
-  const int n = (blockIdx.x * 256 + threadIdx.x) * 2;
-  if (n >= N) return;
+  constexpr int EPV = 16 / sizeof(ActT);
+  __shared__ float red[4][64 * EPV];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = (blockIdx.x * 64 + lane) * EPV;
   const int r0 = blockIdx.y * CS_ROWS, r1 = min(M, r0 + CS_ROWS);
-  float s0 = 0.f, s1 = 0.f;
-  for (int r = r0; r < r1; ++r) {
-    s0 += Act<ActT>::load(x, (long)r * N + n);
-    s1 += Act<ActT>::load(x, (long)r * N + n + 1);
+  float acc[EPV];
+#pragma unroll
+  for (int k = 0; k < EPV; ++k) acc[k] = 0.f;
+  if (n < N) {
+    for (int r = r0 + wave; r < r1; r += 4) {
+      u32x4 raw = *(const u32x4*)(x + (long)r * N + n);
+      if constexpr (EPV == 8) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          acc[2 * k] += bf_lo(raw[k]);
+          acc[2 * k + 1] += bf_hi(raw[k]);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[k] += __uint_as_float(raw[k]);
+      }
+    }
   }
-  partial[(long)blockIdx.y * N + n] = s0;
-  partial[(long)blockIdx.y * N + n + 1] = s1;
+#pragma unroll
+  for (int k = 0; k < EPV; ++k) red[wave][lane * EPV + k] = acc[k];
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * EPV; i += 256) {
+    const int col = blockIdx.x * 64 * EPV + i;
+    if (col < N)
+      partial[(long)blockIdx.y * N + col] = ((red[0][i] + red[1][i]) + red[2][i]) + red[3][i];
+  }
 }
 
 // ------------------------------------------------------------------ cross-entropy
@@ -446,53 +511,76 @@ hipError_t embed_bwd(const int32_t* idx, const float* dx, int M, int T, int C, i
 hipError_t layernorm_fwd(int prec, const float* x, const float* w, const float* b, int M, int C,
                          float eps, void* y, float* mean, float* rstd, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  if (C % 4 || C > 4 * 64 * LN_NV) return hipErrorInvalidValue;
-  unsigned grid = (unsigned)cdiv(M, 4);
-  if (prec == GPT_BF16)
-    ln_fwd_kernel<bf16_t><<<grid, 256, 0, s>>>(x, w, b, M, C, eps, (bf16_t*)y, mean, rstd);
-  else
-    ln_fwd_kernel<float><<<grid, 256, 0, s>>>(x, w, b, M, C, eps, (float*)y, mean, rstd);
-  return hipGetLastError();
+  if (C % 4 || C > 4 * 64 * LN_NV_MAX) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)cdiv(M, 4);
+  const int nv = (int)cdiv(C / 4, 64);  // float4 vectors per lane
+#define LNF_(NV)                                                                                  \
+  if (nv <= NV) {                                                                                 \
+    if (prec == GPT_BF16)                                                                         \
+      ln_fwd_kernel<bf16_t, NV><<<grid, 256, 0, s>>>(x, w, b, M, C, eps, (bf16_t*)y, mean, rstd); \
+    else                                                                                          \
+      ln_fwd_kernel<float, NV><<<grid, 256, 0, s>>>(x, w, b, M, C, eps, (float*)y, mean, rstd);   \
+    return hipGetLastError();                                                                     \
+  }
+  LNF_(1) LNF_(2) LNF_(3) LNF_(4) LNF_(8)
+#undef LNF_
+  return hipErrorInvalidValue;
 }
 
 int layernorm_bwd_partial_rows(int M) { return (int)cdiv(M, LN_BWD_RPB); }
+int64_t layernorm_bwd_partial_floats(int M, int C) {
+  return (2L * layernorm_bwd_partial_rows(M) + RED_SLICES) * C;
+}
 
 hipError_t layernorm_bwd(int prec, const void* dy, const float* x, const float* mean,
                          const float* rstd, const float* w, const float* resid_in, int M, int C,
                          float* dx, void* dx_act, float* dw, float* db, int accumulate,
                          float* partials, hipStream_t s) {
-  if (C % 4 || C > 4 * 64 * LN_NV) return hipErrorInvalidValue;
+  if (C % 4 || C > 4 * 64 * LN_NV_MAX) return hipErrorInvalidValue;
   const int nblk = layernorm_bwd_partial_rows(M);
+  const int nv = (int)cdiv(C / 4, 64);
   if (nblk > 0) {
-    size_t shmem = (size_t)8 * C * sizeof(float);
-    if (prec == GPT_BF16)
-      ln_bwd_kernel<bf16_t><<<nblk, 256, shmem, s>>>((const bf16_t*)dy, x, mean, rstd, w, resid_in,
-                                                     M, C, dx, (bf16_t*)dx_act, partials);
-    else
-      ln_bwd_kernel<float><<<nblk, 256, shmem, s>>>((const float*)dy, x, mean, rstd, w, resid_in,
-                                                    M, C, dx, (float*)dx_act, partials);
+    const size_t shmem = (size_t)8 * C * sizeof(float);
+    bool done = false;
+#define LNB_(NV)                                                                                 \
+  if (!done && nv <= NV) {                                                                       \
+    if (prec == GPT_BF16)                                                                        \
+      ln_bwd_kernel<bf16_t, NV><<<nblk, 256, shmem, s>>>((const bf16_t*)dy, x, mean, rstd, w,    \
+                                                         resid_in, M, C, dx, (bf16_t*)dx_act,    \
+                                                         partials);                              \
+    else                                                                                         \
+      ln_bwd_kernel<float, NV><<<nblk, 256, shmem, s>>>((const float*)dy, x, mean, rstd, w,      \
+                                                        resid_in, M, C, dx, (float*)dx_act,      \
+                                                        partials);                               \
+    done = true;                                                                                 \
   }
-  unsigned g = (unsigned)cdiv(C, 256);
-  reduce_rows_kernel<<<g, 256, 0, s>>>(partials, nblk, C, dw, accumulate);
-  reduce_rows_kernel<<<g, 256, 0, s>>>(partials + (long)nblk * C, nblk, C, db, accumulate);
-  return hipGetLastError();
+    LNB_(1) LNB_(2) LNB_(3) LNB_(4) LNB_(8)
+#undef LNB_
+  }
+  float* stage = partials + 2L * nblk * C;
+  hipError_t e = reduce_rows(partials, nblk, C, dw, accumulate, stage, s);
+  if (e != hipSuccess) return e;
+  return reduce_rows(partials + (long)nblk * C, nblk, C, db, accumulate, stage, s);
 }
 
 int colsum_partial_rows(int M) { return (int)cdiv(M, CS_ROWS); }
+int64_t colsum_partial_floats(int M, int N) { return ((long)colsum_partial_rows(M) + RED_SLICES) * N; }
 
 hipError_t colsum(int prec, const void* x, int M, int N, float* out, int accumulate,
                   float* partials, hipStream_t s) {
-  if (N % 2) return hipErrorInvalidValue;
+  if (N % 8) return hipErrorInvalidValue;
   const int R = colsum_partial_rows(M);
   if (R > 0) {
-    dim3 g((unsigned)cdiv(N, 512), (unsigned)R);
     if (prec == GPT_BF16)
-      colsum_kernel<bf16_t><<<g, 256, 0, s>>>((const bf16_t*)x, M, N, partials);
+      colsum_kernel<bf16_t><<<dim3((unsigned)cdiv(N, 512), (unsigned)R), 256, 0, s>>>(
+          (const bf16_t*)x, M, N, partials);
     else
-      colsum_kernel<float><<<g, 256, 0, s>>>((const float*)x, M, N, partials);
+      colsum_kernel<float><<<dim3((unsigned)cdiv(N, 256), (unsigned)R), 256, 0, s>>>(
+          (const float*)x, M, N, partials);
   }
-  reduce_rows_kernel<<<(unsigned)cdiv(N, 256), 256, 0, s>>>(partials, R, N, out, accumulate);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return reduce_rows(partials, R, N, out, accumulate, partials + (long)R * N, s);
 }
 
 bool cross_entropy_supported(int prec, int ldz) {
