@@ -15,8 +15,9 @@
 //   32 queries.  Each wave computes S^T = K Q^T for 64-key blocks, so every
 //   lane owns ONE query column: the running max / sum are per-lane scalars and
 //   a row reduction is one cross-half swap.  P^T stays in registers and feeds
-//   O^T += V^T P^T directly; V is transposed into LDS on the way in.  Blocks
-//   entirely outside a wave's causal band / window are skipped.
+//   O^T += V^T P^T directly.  K and V tiles sit in LDS in their natural layout;
+//   operands that need the transposed view are fetched with the LDS transpose
+//   read.  Blocks entirely outside a wave's causal band / window are skipped.
 //   backward: two deterministic kernels (no atomics).  dK/dV: a wave owns 32
 //   keys and walks the query blocks that can see them.  dQ: a wave owns 32
 //   queries and walks their key blocks.  Both rebuild P from the saved LSE.
@@ -214,62 +215,51 @@ __global__ void __launch_bounds__(256) attn_dkv_rows(const T* qkv, const float* 
 // ---------------------------------------------------------------------------
 constexpr int KB = 64;  // keys (forward / dQ) or queries (dK/dV) per LDS block
 
+// LDS row pitch of a [64][HD] tile: 16 bf16 of padding make the four rows a
+// transpose read touches at once (stride HD+16 elements) fall in different
+// banks.
+template <int HD> constexpr int pitch_of() { return HD + 16; }
+
 // Rows [row0, row0+64) x HD of a strided bf16 matrix into LDS [64][pitch];
 // rows >= nrows read as zero.
 template <int HD>
 __device__ __forceinline__ void lds_rows(const bf16_t* src, long ld, int row0, int nrows,
-                                         bf16_t* dst, int pitch) {
-  constexpr int VPR = HD / 8;  // 16-byte vectors per row
+                                         bf16_t* dst) {
+  constexpr int VPR = HD / 8, P = pitch_of<HD>();  // 16-byte vectors per row
   for (int u = threadIdx.x; u < KB * VPR; u += 256) {
     int r = u / VPR, c = (u % VPR) * 8;
     u32x4 val = {0, 0, 0, 0};
     if (row0 + r < nrows) val = *(const u32x4*)(src + (long)(row0 + r) * ld + c);
-    *(u32x4*)(dst + r * pitch + c) = val;
+    *(u32x4*)(dst + r * P + c) = val;
   }
 }
 
-// The same 64 x HD block stored transposed: dst[d][key], 64 keys (128 bytes)
-// per row, 16-byte chunks XOR-swizzled by (d & 7).  A thread moves one 8 x 8
-// block: eight 16-byte row loads, an in-register transpose, eight 16-byte
-// LDS stores; the 8 lanes of a store group hit 8 distinct chunks.
-__device__ __forceinline__ int tswz(int d, int key) {
-  return d * KB + ((((key >> 3) ^ (d & 7))) << 3) + (key & 7);
-}
-
+// MFMA operand fragment whose lane index (lane % 32) runs along the row of a
+// tile: row r0 + lane % 32, head dims 16 st + 8 (lane / 32) + 0..7.
 template <int HD>
-__device__ __forceinline__ void lds_rows_t(const bf16_t* src, long ld, int row0, int nrows,
-                                           bf16_t* dst) {
-  constexpr int DB = HD / 8;
-  for (int u = threadIdx.x; u < 8 * DB; u += 256) {
-    const int kb = u & 7, db = u >> 3;
-    u32x4 w[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = row0 + kb * 8 + i;
-      w[i] = u32x4{0, 0, 0, 0};
-      if (r < nrows) w[i] = *(const u32x4*)(src + (long)r * ld + db * 8);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int d = db * 8 + j;
-      u32x4 o;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t lo = w[2 * p][j >> 1], hi = w[2 * p + 1][j >> 1];
-        o[p] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-      }
-      *(u32x4*)(dst + tswz(d, kb * 8)) = o;
-    }
-  }
+__device__ __forceinline__ bf16x8 row_frag(const bf16_t* t, int r0, int st, int lane) {
+  return *(const bf16x8*)(t + (r0 + (lane & 31)) * pitch_of<HD>() + 16 * st + 8 * (lane >> 5));
 }
 
-// 8 bf16 of row `row` of a transposed tile: keys (base + 4g + 0..3) and
-// (base + 8 + 4g + 0..3) — the k-slot order of a 32x32 accumulator handed on
-// as an operand (base % 16 == 0).
-__device__ __forceinline__ bf16x8 lds_slots(const bf16_t* t, int row, int base, int g) {
-  uint2 a = *(const uint2*)(t + tswz(row, base + 4 * g));
-  uint2 b = *(const uint2*)(t + tswz(row, base + 8 + 4 * g));
-  u32x4 v{a.x, a.y, b.x, b.y};
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+
+// MFMA operand fragment whose lane index runs along the COLUMNS of a tile
+// (head dim c0 + lane % 32) and whose 8 k-slots are tile rows in the order of
+// a 32x32 accumulator handed on as an operand: rows base + 4 g + 0..3 and
+// base + 8 + 4 g + 0..3, g = lane / 32.  Two LDS transpose reads: within each
+// group of 16 lanes, source lane s = a + 4 b supplies (row kb + b, columns
+// 4 a .. 4 a + 3) and lane j receives column j of rows kb .. kb + 3.
+template <int HD>
+__device__ __forceinline__ bf16x8 tr_slots(const bf16_t* t, int c0, int base, int lane) {
+  constexpr int P = pitch_of<HD>();
+  const int s = lane & 15, grp = lane >> 4;
+  const int col = c0 + 16 * (grp & 1) + 4 * (s & 3);
+  const int row = base + 4 * (grp >> 1) + (s >> 2);
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(t + row * P + col));
+  v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(t + (row + 8) * P + col));
+  v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return *(bf16x8*)&v;
 }
 
@@ -285,9 +275,9 @@ __device__ __forceinline__ int acc_row(int r, int g) { return 8 * (r >> 2) + 4 *
 template <int HD>
 __global__ void __launch_bounds__(256) attn_fwd_mfma(const bf16_t* qkv, bf16_t* out, float* lse,
                                                      int Tn, int H, int left, float scale_log2) {
-  constexpr int KP = HD + 8, NS = HD / 16, ND = HD / 32;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[KB * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[HD * KB];
+  constexpr int P = pitch_of<HD>(), NS = HD / 16, ND = HD / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[KB * P];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[KB * P];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, c = lane & 31;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -315,8 +305,8 @@ __global__ void __launch_bounds__(256) attn_fwd_mfma(const bf16_t* qkv, bf16_t* 
   const int kfirst = left < 0 ? 0 : max(0, qblk0 - left);
   for (int kb0 = (kfirst / KB) * KB; kb0 <= qlast; kb0 += KB) {
     __syncthreads();
-    lds_rows<HD>(base + C + h * HD, ld, kb0, Tn, Ks, KP);
-    lds_rows_t<HD>(base + 2 * C + h * HD, ld, kb0, Tn, Vt);
+    lds_rows<HD>(base + C + h * HD, ld, kb0, Tn, Ks);
+    lds_rows<HD>(base + 2 * C + h * HD, ld, kb0, Tn, Vs);
     __syncthreads();
     const bool skip = kb0 > qw0 + 31 || (left >= 0 && kb0 + KB - 1 < qw0 - left);
     if (skip) continue;
@@ -328,11 +318,11 @@ __global__ void __launch_bounds__(256) attn_fwd_mfma(const bf16_t* qkv, bf16_t* 
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kk][r] = 0.f;
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        bf16x8 kf = *(const bf16x8*)(Ks + (kk * 32 + c) * KP + 16 * st + 8 * g);
-        s[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], s[kk], 0, 0, 0);
-      }
+      for (int st = 0; st < NS; ++st)
+        s[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<HD>(Ks, kk * 32, st, lane), qf[st],
+                                                        s[kk], 0, 0, 0);
     }
+    // s[kk][r]: key kb0 + kk*32 + acc_row(r, g), query qi (scaled to log2 units below)
     float mx = -1e30f;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
@@ -362,16 +352,16 @@ __global__ void __launch_bounds__(256) attn_fwd_mfma(const bf16_t* qkv, bf16_t* 
     for (int d = 0; d < ND; ++d)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+    // O^T[d][q] += V^T[d][key] P[key][q]
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         bf16x8 pf = acc_slots(s[kk], s2);
 #pragma unroll
-        for (int d = 0; d < ND; ++d) {
-          bf16x8 vf = lds_slots(Vt, d * 32 + c, kk * 32 + 16 * s2, g);
-          o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[d], 0, 0, 0);
-        }
+        for (int d = 0; d < ND; ++d)
+          o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              tr_slots<HD>(Vs, d * 32, kk * 32 + 16 * s2, lane), pf, o[d], 0, 0, 0);
       }
   }
   if (qi < Tn) {
@@ -396,11 +386,9 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma(const bf16_t* qkv, const fl
                                                      const bf16_t* dout, const float* D,
                                                      bf16_t* dqkv, int Tn, int H, int left,
                                                      float scale, float scale_log2) {
-  constexpr int RP = HD + 8, NS = HD / 16, ND = HD / 32;
-  __shared__ __attribute__((aligned(16))) bf16_t Qs[KB * RP];
-  __shared__ __attribute__((aligned(16))) bf16_t Qt[HD * KB];
-  __shared__ __attribute__((aligned(16))) bf16_t Gs[KB * RP];
-  __shared__ __attribute__((aligned(16))) bf16_t Gt[HD * KB];
+  constexpr int P = pitch_of<HD>(), NS = HD / 16, ND = HD / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t Qs[KB * P];
+  __shared__ __attribute__((aligned(16))) bf16_t Gs[KB * P];
   __shared__ float Ls[KB], Ds[KB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, c = lane & 31;
@@ -435,10 +423,8 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma(const bf16_t* qkv, const fl
   const int qend = left < 0 ? Tn - 1 : min(Tn - 1, klast + left);
   for (int qb0 = (kblk0 / KB) * KB; qb0 <= qend; qb0 += KB) {
     __syncthreads();
-    lds_rows<HD>(base + h * HD, ld, qb0, Tn, Qs, RP);
-    lds_rows_t<HD>(base + h * HD, ld, qb0, Tn, Qt);
-    lds_rows<HD>(gbase + h * HD, C, qb0, Tn, Gs, RP);
-    lds_rows_t<HD>(gbase + h * HD, C, qb0, Tn, Gt);
+    lds_rows<HD>(base + h * HD, ld, qb0, Tn, Qs);
+    lds_rows<HD>(gbase + h * HD, C, qb0, Tn, Gs);
     if (threadIdx.x < KB) {
       int q = qb0 + threadIdx.x;
       Ls[threadIdx.x] = q < Tn ? lrow[q] * LOG2E : 0.f;
@@ -455,10 +441,10 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma(const bf16_t* qkv, const fl
       for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        bf16x8 qa = *(const bf16x8*)(Qs + (qq * 32 + c) * RP + 16 * st + 8 * g);
-        bf16x8 ga = *(const bf16x8*)(Gs + (qq * 32 + c) * RP + 16 * st + 8 * g);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[st], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[st], dp, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<HD>(Qs, qq * 32, st, lane), kf[st], s,
+                                                    0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<HD>(Gs, qq * 32, st, lane), vf[st],
+                                                     dp, 0, 0, 0);
       }
       // s[r]: query qb0 + qq*32 + acc_row(r, g), key kj.
 #pragma unroll
@@ -470,16 +456,17 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma(const bf16_t* qkv, const fl
         s[r] = p;
         dp[r] = p * (dp[r] - Ds[ql]);
       }
+      // dV[key][d] += P^T[key][q] dO[q][d];  dK[key][d] += dS^T[key][q] Q[q][d]
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         bf16x8 pa = acc_slots(s, s2);
         bf16x8 da = acc_slots(dp, s2);
 #pragma unroll
         for (int d = 0; d < ND; ++d) {
-          bf16x8 gb = lds_slots(Gt, d * 32 + c, qq * 32 + 16 * s2, g);
-          bf16x8 qb = lds_slots(Qt, d * 32 + c, qq * 32 + 16 * s2, g);
-          dv[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, gb, dv[d], 0, 0, 0);
-          dk[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, qb, dk[d], 0, 0, 0);
+          dv[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              pa, tr_slots<HD>(Gs, d * 32, qq * 32 + 16 * s2, lane), dv[d], 0, 0, 0);
+          dk[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              da, tr_slots<HD>(Qs, d * 32, qq * 32 + 16 * s2, lane), dk[d], 0, 0, 0);
         }
       }
     }
@@ -504,10 +491,9 @@ __global__ void __launch_bounds__(256) attn_dq_mfma(const bf16_t* qkv, const flo
                                                     const bf16_t* dout, const float* D,
                                                     bf16_t* dqkv, int Tn, int H, int left,
                                                     float scale, float scale_log2) {
-  constexpr int RP = HD + 8, NS = HD / 16, ND = HD / 32;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[KB * RP];
-  __shared__ __attribute__((aligned(16))) bf16_t Kt[HD * KB];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[KB * RP];
+  constexpr int P = pitch_of<HD>(), NS = HD / 16, ND = HD / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[KB * P];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[KB * P];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, c = lane & 31;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -541,9 +527,8 @@ __global__ void __launch_bounds__(256) attn_dq_mfma(const bf16_t* qkv, const flo
   const int kfirst = left < 0 ? 0 : max(0, qblk0 - left);
   for (int kb0 = (kfirst / KB) * KB; kb0 <= qlast; kb0 += KB) {
     __syncthreads();
-    lds_rows<HD>(base + C + h * HD, ld, kb0, Tn, Ks, RP);
-    lds_rows_t<HD>(base + C + h * HD, ld, kb0, Tn, Kt);
-    lds_rows<HD>(base + 2 * C + h * HD, ld, kb0, Tn, Vs, RP);
+    lds_rows<HD>(base + C + h * HD, ld, kb0, Tn, Ks);
+    lds_rows<HD>(base + 2 * C + h * HD, ld, kb0, Tn, Vs);
     __syncthreads();
     const bool skip = kb0 > qw0 + 31 || (left >= 0 && kb0 + KB - 1 < qw0 - left);
     if (skip) continue;
@@ -555,10 +540,10 @@ __global__ void __launch_bounds__(256) attn_dq_mfma(const bf16_t* qkv, const flo
       for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        bf16x8 ka = *(const bf16x8*)(Ks + (kk * 32 + c) * RP + 16 * st + 8 * g);
-        bf16x8 va = *(const bf16x8*)(Vs + (kk * 32 + c) * RP + 16 * st + 8 * g);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[st], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[st], dp, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<HD>(Ks, kk * 32, st, lane), qf[st], s,
+                                                    0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<HD>(Vs, kk * 32, st, lane), gf[st],
+                                                     dp, 0, 0, 0);
       }
       // s[r]: key kb0 + kk*32 + acc_row(r, g), query qi.
 #pragma unroll
@@ -568,14 +553,14 @@ __global__ void __launch_bounds__(256) attn_dq_mfma(const bf16_t* qkv, const flo
                                                                   : 0.f;
         dp[r] = p * (dp[r] - Dq);
       }
+      // dQ[q][d] += dS[q][key] K[key][d]
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         bf16x8 da = acc_slots(dp, s2);
 #pragma unroll
-        for (int d = 0; d < ND; ++d) {
-          bf16x8 kb = lds_slots(Kt, d * 32 + c, kk * 32 + 16 * s2, g);
-          dq[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, kb, dq[d], 0, 0, 0);
-        }
+        for (int d = 0; d < ND; ++d)
+          dq[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              da, tr_slots<HD>(Ks, d * 32, kk * 32 + 16 * s2, lane), dq[d], 0, 0, 0);
       }
     }
   }
