@@ -215,10 +215,10 @@ __global__ void __launch_bounds__(256) attn_dkv_rows(const T* qkv, const float* 
 // ---------------------------------------------------------------------------
 constexpr int KB = 64;  // keys (forward / dQ) or queries (dK/dV) per LDS block
 
-// LDS row pitch of a [64][HD] tile: 16 bf16 of padding make the four rows a
-// transpose read touches at once (stride HD+16 elements) fall in different
-// banks.
-template <int HD> constexpr int pitch_of() { return HD + 16; }
+// LDS row pitch of a [64][HD] tile: HD + 24 bf16 puts any 16 consecutive rows
+// of a 16-byte fragment read on distinct 4-bank groups and the four rows of a
+// transpose read (32 bytes each) on disjoint banks, for 64 (or 32) banks.
+template <int HD> constexpr int pitch_of() { return HD + 24; }
 
 // Rows [row0, row0+64) x HD of a strided bf16 matrix into LDS [64][pitch];
 // rows >= nrows read as zero.
@@ -231,6 +231,35 @@ __device__ __forceinline__ void lds_rows(const bf16_t* src, long ld, int row0, i
     u32x4 val = {0, 0, 0, 0};
     if (row0 + r < nrows) val = *(const u32x4*)(src + (long)(row0 + r) * ld + c);
     *(u32x4*)(dst + r * P + c) = val;
+  }
+}
+
+// Register staging of one [64][HD] tile: vector v = t + 256 i covers row
+// v / (HD/8), head dims (v % (HD/8)) * 8 .. + 7.  Loading the next block into
+// registers while the current one is multiplied hides the global latency.
+template <int HD> struct TileRegs { u32x4 v[(KB * HD / 8 + 255) / 256]; };
+
+template <int HD>
+__device__ __forceinline__ void tile_load(const bf16_t* src, long ld, int row0, int nrows,
+                                          TileRegs<HD>& t) {
+  constexpr int VPR = HD / 8, NV = (KB * HD / 8 + 255) / 256;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int u = threadIdx.x + 256 * i;
+    const int r = u / VPR, c = (u % VPR) * 8;
+    u32x4 val = {0, 0, 0, 0};
+    if (u < KB * VPR && row0 + r < nrows) val = *(const u32x4*)(src + (long)(row0 + r) * ld + c);
+    t.v[i] = val;
+  }
+}
+
+template <int HD>
+__device__ __forceinline__ void tile_store(const TileRegs<HD>& t, bf16_t* dst) {
+  constexpr int VPR = HD / 8, NV = (KB * HD / 8 + 255) / 256, P = pitch_of<HD>();
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int u = threadIdx.x + 256 * i;
+    if (u < KB * VPR) *(u32x4*)(dst + (u / VPR) * P + (u % VPR) * 8) = t.v[i];
   }
 }
 
@@ -276,8 +305,8 @@ template <int HD>
 __global__ void __launch_bounds__(256) attn_fwd_mfma(const bf16_t* qkv, bf16_t* out, float* lse,
                                                      int Tn, int H, int left, float scale_log2) {
   constexpr int P = pitch_of<HD>(), NS = HD / 16, ND = HD / 32;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[KB * P];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[KB * P];
+  __shared__ __attribute__((aligned(16))) bf16_t Kbuf[2][KB * P];
+  __shared__ __attribute__((aligned(16))) bf16_t Vbuf[2][KB * P];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, c = lane & 31;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -303,13 +332,24 @@ __global__ void __launch_bounds__(256) attn_fwd_mfma(const bf16_t* qkv, bf16_t* 
 
   const int qlast = min(Tn - 1, qblk0 + 127);
   const int kfirst = left < 0 ? 0 : max(0, qblk0 - left);
-  for (int kb0 = (kfirst / KB) * KB; kb0 <= qlast; kb0 += KB) {
-    __syncthreads();
-    lds_rows<HD>(base + C + h * HD, ld, kb0, Tn, Ks);
-    lds_rows<HD>(base + 2 * C + h * HD, ld, kb0, Tn, Vs);
-    __syncthreads();
+  const int kstart = (kfirst / KB) * KB;
+  TileRegs<HD> rk, rv;
+  tile_load<HD>(base + C + h * HD, ld, kstart, Tn, rk);
+  tile_load<HD>(base + 2 * C + h * HD, ld, kstart, Tn, rv);
+  tile_store<HD>(rk, Kbuf[0]);
+  tile_store<HD>(rv, Vbuf[0]);
+  __syncthreads();
+  int buf = 0;
+  for (int kb0 = kstart; kb0 <= qlast; kb0 += KB, buf ^= 1) {
+    const bf16_t* Ks = Kbuf[buf];
+    const bf16_t* Vs = Vbuf[buf];
+    const bool more = kb0 + KB <= qlast;
+    if (more) {  // next block's tiles travel while this one is multiplied
+      tile_load<HD>(base + C + h * HD, ld, kb0 + KB, Tn, rk);
+      tile_load<HD>(base + 2 * C + h * HD, ld, kb0 + KB, Tn, rv);
+    }
     const bool skip = kb0 > qw0 + 31 || (left >= 0 && kb0 + KB - 1 < qw0 - left);
-    if (skip) continue;
+    if (!skip) {
     // every (query, key) of this wave and block visible: no per-element mask
     const bool full = kb0 + KB - 1 <= qw0 && qw0 + 31 < Tn && (left < 0 || qw0 + 31 - kb0 <= left);
     f32x16 s[2];
@@ -363,6 +403,12 @@ __global__ void __launch_bounds__(256) attn_fwd_mfma(const bf16_t* qkv, bf16_t* 
           o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               tr_slots<HD>(Vs, d * 32, kk * 32 + 16 * s2, lane), pf, o[d], 0, 0, 0);
       }
+    }  // !skip
+    if (more) {
+      tile_store<HD>(rk, Kbuf[buf ^ 1]);
+      tile_store<HD>(rv, Vbuf[buf ^ 1]);
+    }
+    __syncthreads();
   }
   if (qi < Tn) {
     const float inv = 1.f / lrow;
@@ -387,9 +433,9 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma(const bf16_t* qkv, const fl
                                                      bf16_t* dqkv, int Tn, int H, int left,
                                                      float scale, float scale_log2) {
   constexpr int P = pitch_of<HD>(), NS = HD / 16, ND = HD / 32;
-  __shared__ __attribute__((aligned(16))) bf16_t Qs[KB * P];
-  __shared__ __attribute__((aligned(16))) bf16_t Gs[KB * P];
-  __shared__ float Ls[KB], Ds[KB];
+  __shared__ __attribute__((aligned(16))) bf16_t Qbuf[2][KB * P];
+  __shared__ __attribute__((aligned(16))) bf16_t Gbuf[2][KB * P];
+  __shared__ float Lbuf[2][KB], Dbuf[2][KB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, c = lane & 31;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -421,18 +467,39 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma(const bf16_t* qkv, const fl
 
   const int klast = min(Tn - 1, kblk0 + 127);
   const int qend = left < 0 ? Tn - 1 : min(Tn - 1, klast + left);
-  for (int qb0 = (kblk0 / KB) * KB; qb0 <= qend; qb0 += KB) {
-    __syncthreads();
-    lds_rows<HD>(base + h * HD, ld, qb0, Tn, Qs);
-    lds_rows<HD>(gbase + h * HD, C, qb0, Tn, Gs);
+  const int qstart = (kblk0 / KB) * KB;
+  TileRegs<HD> rq, rg;
+  float rl = 0.f, rd = 0.f;
+  auto load_blk = [&](int q0) {
+    tile_load<HD>(base + h * HD, ld, q0, Tn, rq);
+    tile_load<HD>(gbase + h * HD, C, q0, Tn, rg);
     if (threadIdx.x < KB) {
-      int q = qb0 + threadIdx.x;
-      Ls[threadIdx.x] = q < Tn ? lrow[q] * LOG2E : 0.f;
-      Ds[threadIdx.x] = q < Tn ? drow[q] : 0.f;
+      const int q = q0 + threadIdx.x;
+      rl = q < Tn ? lrow[q] * LOG2E : 0.f;
+      rd = q < Tn ? drow[q] : 0.f;
     }
-    __syncthreads();
+  };
+  auto store_blk = [&](int bb) {
+    tile_store<HD>(rq, Qbuf[bb]);
+    tile_store<HD>(rg, Gbuf[bb]);
+    if (threadIdx.x < KB) {
+      Lbuf[bb][threadIdx.x] = rl;
+      Dbuf[bb][threadIdx.x] = rd;
+    }
+  };
+  load_blk(qstart);
+  store_blk(0);
+  __syncthreads();
+  int buf = 0;
+  for (int qb0 = qstart; qb0 <= qend; qb0 += KB, buf ^= 1) {
+    const bf16_t* Qs = Qbuf[buf];
+    const bf16_t* Gs = Gbuf[buf];
+    const float* Ls = Lbuf[buf];
+    const float* Ds = Dbuf[buf];
+    const bool more = qb0 + KB <= qend;
+    if (more) load_blk(qb0 + KB);
     const bool skip = qb0 + KB - 1 < kw0 || (left >= 0 && qb0 > kw0 + 31 + left);
-    if (skip) continue;
+    if (!skip) {
     const bool full = qb0 >= kw0 + 31 && qb0 + KB - 1 < Tn && (left < 0 || qb0 + KB - 1 - kw0 <= left);
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq) {
@@ -470,6 +537,9 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma(const bf16_t* qkv, const fl
         }
       }
     }
+    }  // !skip
+    if (more) store_blk(buf ^ 1);
+    __syncthreads();
   }
   // dk[d][r]: key kw0 + acc_row(r, g), head dim d*32 + c.
 #pragma unroll
@@ -492,8 +562,8 @@ __global__ void __launch_bounds__(256) attn_dq_mfma(const bf16_t* qkv, const flo
                                                     bf16_t* dqkv, int Tn, int H, int left,
                                                     float scale, float scale_log2) {
   constexpr int P = pitch_of<HD>(), NS = HD / 16, ND = HD / 32;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[KB * P];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[KB * P];
+  __shared__ __attribute__((aligned(16))) bf16_t Kbuf[2][KB * P];
+  __shared__ __attribute__((aligned(16))) bf16_t Vbuf[2][KB * P];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, c = lane & 31;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -525,13 +595,24 @@ __global__ void __launch_bounds__(256) attn_dq_mfma(const bf16_t* qkv, const flo
 
   const int qlast = min(Tn - 1, qblk0 + 127);
   const int kfirst = left < 0 ? 0 : max(0, qblk0 - left);
-  for (int kb0 = (kfirst / KB) * KB; kb0 <= qlast; kb0 += KB) {
-    __syncthreads();
-    lds_rows<HD>(base + C + h * HD, ld, kb0, Tn, Ks);
-    lds_rows<HD>(base + 2 * C + h * HD, ld, kb0, Tn, Vs);
-    __syncthreads();
+  const int kstart = (kfirst / KB) * KB;
+  TileRegs<HD> rk, rv;
+  tile_load<HD>(base + C + h * HD, ld, kstart, Tn, rk);
+  tile_load<HD>(base + 2 * C + h * HD, ld, kstart, Tn, rv);
+  tile_store<HD>(rk, Kbuf[0]);
+  tile_store<HD>(rv, Vbuf[0]);
+  __syncthreads();
+  int buf = 0;
+  for (int kb0 = kstart; kb0 <= qlast; kb0 += KB, buf ^= 1) {
+    const bf16_t* Ks = Kbuf[buf];
+    const bf16_t* Vs = Vbuf[buf];
+    const bool more = kb0 + KB <= qlast;
+    if (more) {
+      tile_load<HD>(base + C + h * HD, ld, kb0 + KB, Tn, rk);
+      tile_load<HD>(base + 2 * C + h * HD, ld, kb0 + KB, Tn, rv);
+    }
     const bool skip = kb0 > qw0 + 31 || (left >= 0 && kb0 + KB - 1 < qw0 - left);
-    if (skip) continue;
+    if (!skip) {
     const bool full = kb0 + KB - 1 <= qw0 && qw0 + 31 < Tn && (left < 0 || qw0 + 31 - kb0 <= left);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -563,6 +644,12 @@ __global__ void __launch_bounds__(256) attn_dq_mfma(const bf16_t* qkv, const flo
               da, tr_slots<HD>(Ks, d * 32, kk * 32 + 16 * s2, lane), dq[d], 0, 0, 0);
       }
     }
+    }  // !skip
+    if (more) {
+      tile_store<HD>(rk, Kbuf[buf ^ 1]);
+      tile_store<HD>(rv, Vbuf[buf ^ 1]);
+    }
+    __syncthreads();
   }
   // dq[d][r]: query qw0 + acc_row(r, g), head dim d*32 + c.
 #pragma unroll

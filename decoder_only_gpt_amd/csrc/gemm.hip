@@ -20,6 +20,8 @@
 #include "kernels.h"
 
 #include <algorithm>
+#include <climits>
+#include <cstdlib>
 
 namespace gpt {
 
@@ -130,11 +132,13 @@ constexpr int BM = 128, BN = 128, BK = 64;
 constexpr int EPI_PARTIAL = 100;  // split-K: raw float partial tile
 
 // LDS operand tile: [128 rows][BK] bf16, 128 bytes per row, its eight 16-byte
-// chunks XOR-swizzled by (row & 7).  An MFMA fragment read (32 rows, one
-// chunk each) and both store patterns below then touch 8 distinct chunks per
-// group of 8 lanes, i.e. all banks once.
+// chunks XOR-swizzled by f(row) = (row & 7) ^ ((row >> 3) & 1).  With 64 banks
+// two consecutive rows share a bank line, so a 16-lane group of a fragment
+// read (rows r..r+15, one logical chunk) needs distinct chunks among the rows
+// of equal parity; f gives that (and distinct chunks for any 8 consecutive
+// rows, the 32-bank case).
 __device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * BK + ((chunk ^ (row & 7)) << 3);
+  return row * BK + ((chunk ^ (row & 7) ^ ((row >> 3) & 1)) << 3);
 }
 
 __device__ __forceinline__ uint32_t gelu2(uint32_t w, int tanh_form) {
@@ -397,6 +401,379 @@ MfmaKernel mfma_kernel_for(int at, int bt, int epi, int ga, int gb) {
   return nullptr;
 }
 
+// Workgroups are dealt round-robin over the 8 XCDs (each with its own L2):
+// renumber them so every XCD walks a contiguous, row-major run of tiles and
+// the tiles sharing an A panel (and reusing B) meet in the same L2.
+__device__ __forceinline__ void xcd_tile(int& tx, int& ty) {
+  const int nx = gridDim.x, total = gridDim.x * gridDim.y;
+  const int L = blockIdx.x + nx * blockIdx.y;
+  int L2 = L;
+  if ((total & 7) == 0) L2 = (L & 7) * (total >> 3) + (L >> 3);
+  tx = L2 % nx;
+  ty = L2 / nx;
+}
+
+// ----------------------------------------------------------------------------
+// bf16 MFMA, 128 x 128 tile, operands fetched straight into LDS with buffer
+// loads (buffer_load_dwordx4 ... lds): no register staging and no LDS store
+// instructions; the loads of tile k+1 run while tile k is multiplied.  One
+// wave instruction fills a contiguous 1 KB LDS block (lane l -> bytes 16 l),
+// so the XOR swizzle of the LDS layouts is applied to the SOURCE address each
+// lane picks.  Lanes outside the valid rows / K range get an offset past the
+// buffer's range and read zeros.
+// ----------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long bytes) {
+  const int n = bytes > 0x7fffffffL ? 0x7fffffff : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, n, 0x00020000);
+}
+
+// Issue this wave's 4 loads of one 128 x BK operand tile into `lds`.
+template <int TRANS>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, const OpArgs& a, int r0,
+                                         int k0, bf16_t* lds, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int blk = wave * 4 + i;  // 1 KB block of the 16 KB tile
+    int r, k;
+    if constexpr (TRANS == 0) {  // [128 rows][64 k]: block = 8 rows x 8 chunks
+      const int row = blk * 8 + (lane >> 3), phys = lane & 7;
+      const int chunk = phys ^ (row & 7) ^ ((row >> 3) & 1);
+      r = r0 + row;
+      k = k0 + chunk * 8;
+    } else {  // [64 k][128 rows]: block = 4 k-rows x 16 chunks
+      const int kk = blk * 4 + (lane >> 4), phys = lane & 15;
+      const int chunk = phys ^ ((kk & 3) << 2);
+      k = k0 + kk;
+      r = r0 + chunk * 8;
+    }
+    const bool ok = r < a.rows && k < a.kvalid;
+    const long e = TRANS ? (long)k * a.ld + r : (long)r * a.ld + k;
+    const unsigned off = ok ? (unsigned)(e * 2) : 0x80000000u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + blk * 512), 16, off, 0, 0, 0);
+  }
+}
+
+template <int AT, int BT, int EPI>
+__global__ void __launch_bounds__(256, 2) gemm_dma_kernel(OpArgs A, OpArgs B, int K, int kchunk,
+                                                          EpiArgs e, float* partial) {
+  __shared__ __attribute__((aligned(16))) bf16_t sA0[BM * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t sB0[BN * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t sA1[BM * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t sB1[BN * BK];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  int tx, ty;
+  xcd_tile(tx, ty);
+  const int m0 = ty * BM, n0 = tx * BN;
+  const int kbeg = blockIdx.z * kchunk;
+  const int kend = min(K, kbeg + kchunk);
+  const int nk = (kend - kbeg + BK - 1) / BK;
+
+  OpArgs a = A, b = B;
+  a.kvalid = min(a.kvalid, kend);
+  b.kvalid = min(b.kvalid, kend);
+  const long a_extent = AT ? (long)a.kvalid * a.ld : (long)a.rows * a.ld;
+  const long b_extent = BT ? (long)b.kvalid * b.ld : (long)b.rows * b.ld;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.X, a_extent * 2);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(b.X, b_extent * 2);
+
+  f32x16 acc00 = {}, acc01 = {}, acc10 = {}, acc11 = {};
+
+  dma_tile<AT>(ra, a, m0, kbeg, sA0, wave, lane);
+  dma_tile<BT>(rb, b, n0, kbeg, sB0, wave, lane);
+  for (int kt = 0; kt < nk; ++kt) {
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's loads of tile kt landed
+    __syncthreads();                     // ... and every other wave's
+    const bool odd = kt & 1;
+    if (kt + 1 < nk) {
+      const int k1 = kbeg + (kt + 1) * BK;
+      dma_tile<AT>(ra, a, m0, k1, odd ? sA0 : sA1, wave, lane);
+      dma_tile<BT>(rb, b, n0, k1, odd ? sB0 : sB1, wave, lane);
+    }
+    const bf16_t* as = odd ? sA1 : sA0;
+    const bf16_t* bs = odd ? sB1 : sB0;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const bf16x8 a0 = frag<AT>(as, wm * 64, ks, lane);
+      const bf16x8 a1 = frag<AT>(as, wm * 64 + 32, ks, lane);
+      const bf16x8 b0 = frag<BT>(bs, wn * 64, ks, lane);
+      const bf16x8 b1 = frag<BT>(bs, wn * 64 + 32, ks, lane);
+      acc00 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc00, 0, 0, 0);
+      acc01 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc01, 0, 0, 0);
+      acc10 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc10, 0, 0, 0);
+      acc11 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc11, 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x3f70);
+  __syncthreads();
+
+  // Accumulators -> LDS float tile [128][128] (all four stage buffers, 64 KB).
+  float* Cs = (float*)sA0;
+  {
+    const int frow = lane & 31, fg = lane >> 5;
+    const int rb = wm * 64 + 4 * fg, cb = wn * 64 + frow;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = rb + 8 * (r >> 2) + (r & 3);
+      Cs[row * BN + cb] = acc00[r];
+      Cs[row * BN + cb + 32] = acc01[r];
+      Cs[(row + 32) * BN + cb] = acc10[r];
+      Cs[(row + 32) * BN + cb + 32] = acc11[r];
+    }
+  }
+  __syncthreads();
+  const int cg = threadIdx.x & 15;
+  const int n = n0 + cg * 8;
+  if (n >= e.N) return;
+  for (int pass = 0; pass < BM / 16; ++pass) {
+    const int row = pass * 16 + (threadIdx.x >> 4);
+    const int m = m0 + row;
+    if (m >= e.M) break;
+    const float4 v0 = *(const float4*)(Cs + row * BN + cg * 8);
+    const float4 v1 = *(const float4*)(Cs + row * BN + cg * 8 + 4);
+    epilogue8<EPI>(e, partial, m, n, v0, v1);
+  }
+}
+
+MfmaKernel dma_kernel_for(int at, int bt, int epi, int ga, int gb) {
+  if (ga || gb) return nullptr;
+#define K_(AT, BT, EP) \
+  if (at == AT && bt == BT && epi == EP) return gemm_dma_kernel<AT, BT, EP>;
+  K_(0, 0, GPT_EPI_STORE)
+  K_(0, 0, GPT_EPI_RESIDUAL)
+  K_(0, 0, GPT_EPI_GELU)
+  K_(0, 0, GPT_EPI_DGELU)
+  K_(0, 0, GPT_EPI_F32)
+  K_(0, 0, GPT_EPI_F32_ACCUM)
+  K_(0, 1, GPT_EPI_STORE)
+  K_(0, 1, GPT_EPI_DGELU)
+  K_(0, 1, GPT_EPI_F32)
+  K_(1, 1, GPT_EPI_F32)
+  K_(1, 1, GPT_EPI_F32_ACCUM)
+  K_(1, 1, EPI_PARTIAL)
+#undef K_
+  return nullptr;
+}
+
+// ----------------------------------------------------------------------------
+// bf16 MFMA, large tile: 256 x 256 per workgroup, 4 waves of 128 x 128 (4 x 4
+// blocks of 32 x 32), BK = 64, two LDS stages of 64 KB filled by direct
+// buffer loads.  Each k-step a wave reads 8 fragments for 16 MFMAs (half the
+// LDS traffic per FLOP of the 128-tile kernel).  The MFMA operands are swapped
+// (D = B-frag x A-frag), so each lane owns one output row and 4 consecutive
+// output columns per 4 accumulator registers: the epilogue stores 8- or
+// 16-byte vectors straight from the accumulators.
+// ----------------------------------------------------------------------------
+constexpr int BIG = 256;
+
+__device__ __forceinline__ int big_off(int row, int chunk) {  // row-major tile [256][BK]
+  return row * BK + ((chunk ^ (row & 7) ^ ((row >> 3) & 1)) << 3);
+}
+__device__ __forceinline__ int big_off_t(int k, int r) {  // K-major tile [BK][256]
+  return k * BIG + (r ^ ((k & 3) << 5));
+}
+
+template <int TRANS>
+__device__ __forceinline__ void dma_tile256(__amdgpu_buffer_rsrc_t rs, const OpArgs& a, int r0,
+                                            int k0, bf16_t* lds, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int blk = wave * 8 + i;  // 1 KB block of the 32 KB tile
+    int r, k;
+    if constexpr (TRANS == 0) {  // block = 8 rows x 8 chunks
+      const int row = blk * 8 + (lane >> 3), phys = lane & 7;
+      const int chunk = phys ^ (row & 7) ^ ((row >> 3) & 1);
+      r = r0 + row;
+      k = k0 + chunk * 8;
+    } else {  // block = 2 k-rows x 32 chunks
+      const int kk = blk * 2 + (lane >> 5), phys = lane & 31;
+      const int chunk = phys ^ ((kk & 3) << 2);
+      k = k0 + kk;
+      r = r0 + chunk * 8;
+    }
+    const bool ok = r < a.rows && k < a.kvalid;
+    const long e = TRANS ? (long)k * a.ld + r : (long)r * a.ld + k;
+    const unsigned off = ok ? (unsigned)(e * 2) : 0x80000000u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + blk * 512), 16, off, 0, 0, 0);
+  }
+}
+
+template <int TRANS>
+__device__ __forceinline__ bf16x8 big_frag(const bf16_t* lds, int r0, int ks, int lane) {
+  if constexpr (TRANS == 0) {
+    return *(const bf16x8*)(lds + big_off(r0 + (lane & 31), ks * 2 + (lane >> 5)));
+  } else {
+    const int s = lane & 15, grp = lane >> 4;
+    const int r = r0 + 16 * (grp & 1) + 4 * (s & 3);
+    const int kb = ks * 16 + 8 * (grp >> 1) + (s >> 2);
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds + big_off_t(kb, r)));
+    v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds + big_off_t(kb + 4, r)));
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return *(bf16x8*)&v;
+  }
+}
+
+// Epilogue on 4 consecutive columns n..n+3 of row m (n + 4 <= N).
+template <int EPI>
+__device__ __forceinline__ void epilogue4(const EpiArgs& e, float* partial, int m, int n, float4 v) {
+  const long o = (long)m * e.ldo + n;
+  if constexpr (EPI == EPI_PARTIAL) {
+    *(float4*)(partial + ((long)blockIdx.z * e.M + m) * e.N + n) = v;
+    return;
+  }
+  if constexpr (EPI == GPT_EPI_STORE || EPI == GPT_EPI_RESIDUAL || EPI == GPT_EPI_GELU) {
+    if (e.bias) {
+      float4 b = *(const float4*)(e.bias + n);
+      v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
+    }
+  }
+  if constexpr (EPI == GPT_EPI_STORE || EPI == GPT_EPI_GELU) {
+    const uint2 w = make_uint2(pack_bf2(v.x, v.y), pack_bf2(v.z, v.w));
+    *(uint2*)((bf16_t*)e.out + o) = w;
+    if constexpr (EPI == GPT_EPI_GELU) {
+      if (e.aux)  // GELU of the stored (rounded) pre-activation
+        *(uint2*)((bf16_t*)e.aux + (long)m * e.ldaux + n) =
+            make_uint2(gelu2(w.x, e.tanh_form), gelu2(w.y, e.tanh_form));
+    }
+  } else if constexpr (EPI == GPT_EPI_DGELU) {
+    const uint2 u = *(const uint2*)((const bf16_t*)e.aux + (long)m * e.ldaux + n);
+    v.x *= gelu_grad_f(bf_lo(u.x), e.tanh_form);
+    v.y *= gelu_grad_f(bf_hi(u.x), e.tanh_form);
+    v.z *= gelu_grad_f(bf_lo(u.y), e.tanh_form);
+    v.w *= gelu_grad_f(bf_hi(u.y), e.tanh_form);
+    *(uint2*)((bf16_t*)e.out + o) = make_uint2(pack_bf2(v.x, v.y), pack_bf2(v.z, v.w));
+  } else if constexpr (EPI == GPT_EPI_RESIDUAL) {
+    const float4 r = *(const float4*)(e.resid + o);
+    *(float4*)((float*)e.out + o) = make_float4(r.x + v.x, r.y + v.y, r.z + v.z, r.w + v.w);
+  } else if constexpr (EPI == GPT_EPI_F32) {
+    *(float4*)((float*)e.out + o) = v;
+  } else if constexpr (EPI == GPT_EPI_F32_ACCUM) {
+    float4* p = (float4*)((float*)e.out + o);
+    const float4 a = *p;
+    *p = make_float4(a.x + v.x, a.y + v.y, a.z + v.z, a.w + v.w);
+  }
+}
+
+
+template <int AT, int BT, int EPI>
+__global__ void __launch_bounds__(256, 1) gemm_big_kernel(OpArgs A, OpArgs B, int K, int kchunk,
+                                                          EpiArgs e, float* partial) {
+  __shared__ __attribute__((aligned(16))) bf16_t sA0[BIG * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t sB0[BIG * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t sA1[BIG * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t sB1[BIG * BK];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  int tx, ty;
+  xcd_tile(tx, ty);
+  const int m0 = ty * BIG, n0 = tx * BIG;
+  const int kbeg = blockIdx.z * kchunk;
+  const int kend = min(K, kbeg + kchunk);
+  const int nk = (kend - kbeg + BK - 1) / BK;
+
+  OpArgs a = A, b = B;
+  a.kvalid = min(a.kvalid, kend);
+  b.kvalid = min(b.kvalid, kend);
+  const long a_extent = AT ? (long)a.kvalid * a.ld : (long)a.rows * a.ld;
+  const long b_extent = BT ? (long)b.kvalid * b.ld : (long)b.rows * b.ld;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.X, a_extent * 2);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(b.X, b_extent * 2);
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  dma_tile256<AT>(ra, a, m0, kbeg, sA0, wave, lane);
+  dma_tile256<BT>(rb, b, n0, kbeg, sB0, wave, lane);
+  for (int kt = 0; kt < nk; ++kt) {
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's loads of tile kt landed
+    __syncthreads();                     // ... and every other wave's
+    const bool odd = kt & 1;
+    if (kt + 1 < nk) {
+      const int k1 = kbeg + (kt + 1) * BK;
+      dma_tile256<AT>(ra, a, m0, k1, odd ? sA0 : sA1, wave, lane);
+      dma_tile256<BT>(rb, b, n0, k1, odd ? sB0 : sB1, wave, lane);
+    }
+    const bf16_t* as = odd ? sA1 : sA0;
+    const bf16_t* bs = odd ? sB1 : sB0;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 af[4], bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = big_frag<AT>(as, wm * 128 + i * 32, ks, lane);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bf[j] = big_frag<BT>(bs, wn * 128 + j * 32, ks, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // Epilogue, one 32-row block of the wave's 128 x 128 tile at a time:
+  // accumulators -> this wave's 16 KB LDS slice as floats [32][CP] (plain
+  // float4 stores), then a rolled loop applies the epilogue to 8 consecutive
+  // columns per lane and stores vectors.  acc[i][j] = D[n][m]: lane column
+  // m = lane % 32, register r holds n = 8 (r / 4) + 4 (lane / 32) + r % 4.
+  constexpr int CP = 132;  // padded row pitch (floats)
+  __syncthreads();         // every wave is done reading the operand tiles
+  float* Cw = (float*)((wave & 2) ? sB0 : sA0) + (wave & 1) * (32 * CP);
+  const int m_l = lane & 31, nq = 4 * (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(float4*)(Cw + m_l * CP + j * 32 + 8 * q + nq) =
+            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                        acc[i][j][4 * q + 3]);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+    const int cg = lane & 15;
+    const int n = n0 + wn * 128 + cg * 8;
+#pragma unroll 1
+    for (int p = 0; p < 8; ++p) {
+      const int row = p * 4 + (lane >> 4);
+      const int m = m0 + wm * 128 + i * 32 + row;
+      if (m < e.M && n < e.N) {
+        const float4 v0 = *(const float4*)(Cw + row * CP + cg * 8);
+        const float4 v1 = *(const float4*)(Cw + row * CP + cg * 8 + 4);
+        epilogue8<EPI>(e, partial, m, n, v0, v1);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next block overwrites
+  }
+}
+
+MfmaKernel big_kernel_for(int at, int bt, int epi, int ga, int gb) {
+  if (ga || gb) return nullptr;
+#define K_(AT, BT, EP) \
+  if (at == AT && bt == BT && epi == EP) return gemm_big_kernel<AT, BT, EP>;
+  K_(0, 0, GPT_EPI_STORE)
+  K_(0, 0, GPT_EPI_RESIDUAL)
+  K_(0, 0, GPT_EPI_GELU)
+  K_(0, 0, GPT_EPI_DGELU)
+  K_(0, 0, GPT_EPI_F32)
+  K_(0, 0, GPT_EPI_F32_ACCUM)
+  K_(0, 1, GPT_EPI_STORE)
+  K_(0, 1, GPT_EPI_DGELU)
+  K_(0, 1, GPT_EPI_F32)
+  K_(1, 1, GPT_EPI_F32)
+  K_(1, 1, GPT_EPI_F32_ACCUM)
+  K_(1, 1, EPI_PARTIAL)
+#undef K_
+  return nullptr;
+}
+
 int choose_split(int M, int N, int K) {
   long tiles = cdiv(M, BM) * cdiv(N, BN);
   if (tiles >= 512 || K < 1024) return 1;
@@ -407,22 +784,91 @@ int choose_split(int M, int N, int K) {
   return s < 1 ? 1 : s;
 }
 
+// Which kernel runs a descriptor and over how many K splits.
+struct GemmPlan {
+  bool big;  // 256 x 256 tiles
+  int S;     // K splits (1 = none)
+};
+
+// Tile override for tuning: GPT_GEMM_TILE=128 or 256 (unset: automatic).
+int tile_override() {
+  static int v = [] {
+    const char* e = getenv("GPT_GEMM_TILE");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
+}
+
+GemmPlan plan_gemm(int M, int N, int K, int precision, bool splittable, int64_t ws_bytes,
+                   bool big_ok) {
+  GemmPlan p{false, 1};
+  if (precision != GPT_BF16 || M <= 0 || N <= 0 || K <= 0) return p;
+  if (!big_ok) {
+    int S = splittable ? choose_split(M, N, K) : 1;
+    if (S > 1 && ws_bytes < (int64_t)S * M * N * 4) S = 1;
+    p.S = S;
+    return p;
+  }
+  const long t256 = cdiv(M, BIG) * cdiv(N, BIG);
+  const int force = tile_override();
+  if (force == 256) {
+    p.big = true;
+    return p;
+  }
+  if (force != 128) {
+    // Weight gradients (short M x N, K = tokens): 256-tiles with K split so the
+    // grid is about one wave of the 256 CUs.
+    if (splittable && K >= 2048 && t256 < 256) {
+      int S = (int)std::min<long>(std::min<long>(256 / t256, K / 1024), 32);
+      if (S >= 2 && ws_bytes >= (int64_t)S * M * N * 4) {
+        p.big = true;
+        p.S = S;
+        return p;
+      }
+    }
+    // Very wide products (the vocabulary projection): 256-tiles.
+    if (!splittable && t256 >= 4096) {
+      p.big = true;
+      return p;
+    }
+  }
+  int S = splittable ? choose_split(M, N, K) : 1;
+  if (S > 1 && ws_bytes < (int64_t)S * M * N * 4) S = 1;
+  p.S = S;
+  return p;
+}
+
+int effective_splits(const GemmPlan& p, int K) {
+  if (p.S <= 1) return 1;
+  const int kchunk = (int)cdiv(cdiv(K, p.S), BK) * BK;
+  return (int)cdiv(K, kchunk);
+}
+
+bool splittable(const gpt_gemm_desc& d) { return d.a_trans && d.b_trans && !d.a_gelu; }
+// Direct-to-LDS loads address each operand through a 31-bit byte offset.
+bool dma_ok(const gpt_gemm_desc& d) {
+  if (getenv("GPT_GEMM_NODMA")) return false;
+  const long ea = d.a_trans ? (long)d.a_kvalid * d.lda : (long)d.a_rows * d.lda;
+  const long eb = d.b_trans ? (long)d.b_kvalid * d.ldb : (long)d.b_rows * d.ldb;
+  return ea * 2 < 0x7fffffffL && eb * 2 < 0x7fffffffL;
+}
+// The large-tile kernel loads straight to LDS, so it cannot apply GELU to an
+// operand on the way in.
+bool big_ok(const gpt_gemm_desc& d) { return !d.a_gelu && !d.b_gelu && dma_ok(d); }
+
 }  // namespace
 
 int gemm_split_count(const gpt_gemm_desc& d) {
-  if (d.precision != GPT_BF16 || d.M <= 0 || d.N <= 0 || d.K <= 0) return 1;
-  if (!d.a_trans || !d.b_trans || d.a_gelu) return 1;  // split-K kernels: weight-gradient layout
-  int S = choose_split(d.M, d.N, d.K);
-  if (S > 1 && (d.workspace == nullptr || d.workspace_bytes < (int64_t)S * d.M * d.N * 4)) S = 1;
-  if (S == 1) return 1;
-  int kchunk = (int)cdiv(cdiv(d.K, S), BK) * BK;
-  return (int)cdiv(d.K, kchunk);
+  GemmPlan p = plan_gemm(d.M, d.N, d.K, d.precision, splittable(d),
+                         d.workspace ? d.workspace_bytes : 0, big_ok(d));
+  return effective_splits(p, d.K);
 }
 
 int64_t gemm_workspace_bytes(int M, int N, int K, int precision) {
-  if (precision != GPT_BF16) return 0;
-  int s = choose_split(M, N, K);
-  return s > 1 ? (int64_t)s * M * N * 4 : 0;
+  GemmPlan p = plan_gemm(M, N, K, precision, true, INT64_MAX, true);
+  GemmPlan q = plan_gemm(M, N, K, precision, true, INT64_MAX, false);
+  const int S = std::max(p.S, q.S);
+  return S > 1 ? (int64_t)S * M * N * 4 : 0;
 }
 
 hipError_t gemm(const gpt_gemm_desc& d, hipStream_t s) {
@@ -447,23 +893,33 @@ hipError_t gemm(const gpt_gemm_desc& d, hipStream_t s) {
     gemm_simt_kernel<float, float><<<grid, 256, 0, s>>>(A, B, d.K, e);
     return hipGetLastError();
   }
-  int S = gemm_split_count(d);
+  const GemmPlan plan = plan_gemm(d.M, d.N, d.K, d.precision, splittable(d),
+                                  d.workspace ? d.workspace_bytes : 0, big_ok(d));
+  const int S = effective_splits(plan, d.K);
   const bool vec_ok = d.N % 8 == 0 && d.ldo % 8 == 0 && (d.aux == nullptr || d.ldaux % 8 == 0);
-  MfmaKernel kern = vec_ok ? mfma_kernel_for(d.a_trans, d.b_trans, S > 1 ? EPI_PARTIAL : d.epilogue,
-                                             d.a_gelu, d.b_gelu)
-                           : nullptr;
+  const int epi = S > 1 ? EPI_PARTIAL : d.epilogue;
+  MfmaKernel kern = nullptr;
+  if (vec_ok) {
+    kern = plan.big ? big_kernel_for(d.a_trans, d.b_trans, epi, d.a_gelu, d.b_gelu)
+                    : mfma_kernel_for(d.a_trans, d.b_trans, epi, d.a_gelu, d.b_gelu);
+    if (!plan.big && dma_ok(d)) {
+      MfmaKernel k2 = dma_kernel_for(d.a_trans, d.b_trans, epi, d.a_gelu, d.b_gelu);
+      if (k2) kern = k2;
+    }
+  }
   if (kern == nullptr) {
     // Combinations the step never issues: the generic kernel (bf16 inputs).
     dim3 grid((unsigned)cdiv(d.N, 64), (unsigned)cdiv(d.M, 64));
     gemm_simt_kernel<bf16_t, bf16_t><<<grid, 256, 0, s>>>(A, B, d.K, e);
     return hipGetLastError();
   }
-  dim3 grid((unsigned)cdiv(d.N, BN), (unsigned)cdiv(d.M, BM), (unsigned)S);
+  const int T = plan.big ? BIG : BM;
+  dim3 grid((unsigned)cdiv(d.N, T), (unsigned)cdiv(d.M, T), (unsigned)S);
   if (S == 1) {
     kern<<<grid, 256, 0, s>>>(A, B, d.K, d.K, e, nullptr);
     return hipGetLastError();
   }
-  const int kchunk = (int)cdiv(cdiv(d.K, S), BK) * BK;
+  const int kchunk = (int)cdiv(cdiv(d.K, plan.S), BK) * BK;
   kern<<<grid, 256, 0, s>>>(A, B, d.K, kchunk, e, (float*)d.workspace);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
