@@ -29,6 +29,26 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 METRIC = "training tokens/sec on 1 GPU + MFU vs bf16 MFMA peak, GPT-2 124M shape"
 
 
+# Call sites that launch exactly one kernel (see gpt_site in include/gpt.h).
+SINGLE_KERNEL_SITES = ["embed_fwd", "ln_fwd", "qkv_fwd", "attn_fwd", "proj_fwd", "fc_fwd",
+                       "fcproj_fwd", "lmhead_fwd", "lmhead_dx", "lmhead_dw", "fcproj_dx", "fc_dx",
+                       "proj_dx", "qkv_dx", "adamw"]
+
+
+def load_traffic(site):
+    """HBM bytes per launch of `site` from the committed PMC summary, if it was
+    taken on the current kernel sources (else None)."""
+    from decoder_only_gpt_amd import profile_run
+    path = os.path.join(ROOT, "profiles", f"traffic_{site}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != profile_run.kernel_source_sha():
+        return None
+    return round(t["hbm_bytes_per_launch"], 1)
+
+
 def workload_name(cfg, name):
     return (f"{name}: decoder-only GPT training step, B={cfg['B']} T={cfg['T']} "
             f"V={cfg['vocab_size']}/{cfg['padded_vocab']} L={cfg['n_layer']} H={cfg['n_head']} "
@@ -108,11 +128,12 @@ def main():
     fpt = model.sizes.flops_per_token
     mfu = fpt * value / (PEAK_BF16_TFLOPS * 1e12)
 
-    # Kernel timing pass (separate steps, same work).
+    # Kernel timing pass (separate steps, same work): HIP events around every
+    # launch, on the stream the kernels run on.
     model.profile_begin()
     for _ in range(args.profile_steps):
         model.train_step(d_idx, d_tgt)
-    kstats = model.profile_end()
+    kstats, sstats = model.profile_end()
     per_kind = {}
     for k, s in kstats.items():
         if s["launches"]:
@@ -122,20 +143,30 @@ def main():
                 "tflops": round(s["flops"] / (s["ms"] * 1e-3) / 1e12, 2) if s["flops"] else None,
                 "gbs": round(s["bytes"] / (s["ms"] * 1e-3) / 1e9, 1) if s["bytes"] else None,
             }
-    dom = max((k for k in kstats if kstats[k]["launches"]), key=lambda k: kstats[k]["ms"])
-    ds = kstats[dom]
+    per_site = {k: {"ms_per_step": round(s["ms"] / args.profile_steps, 4),
+                    "launches_per_step": s["launches"] // args.profile_steps}
+                for k, s in sstats.items() if s["launches"]}
+    # Dominant kernel: the call site with the most time among those that launch a
+    # single kernel (each maps to one kernel specialisation in rocprofv3 traces).
+    single = [k for k in SINGLE_KERNEL_SITES if sstats[k]["launches"]]
+    dom = max(single, key=lambda k: sstats[k]["ms"])
+    ds = sstats[dom]
     avg_s = ds["ms"] * 1e-3 / ds["launches"]
+    traffic = load_traffic(dom)
     if ds["flops"]:
-        ach = ds["flops"] / ds["launches"] / avg_s / 1e12
+        per_launch = ds["flops"] / ds["launches"]
+        ach = per_launch / avg_s / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "avg_launch_us": round(avg_s * 1e6, 2), "launches_per_step":
-                    ds["launches"] // args.profile_steps}
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "algorithmic_per_launch": per_launch, "avg_launch_us": round(avg_s * 1e6, 2),
+                "launches_per_step": ds["launches"] // args.profile_steps}
     else:
-        ach = ds["bytes"] / ds["launches"] / avg_s / 1e9
+        per_launch = ds["bytes"] / ds["launches"]
+        ach = per_launch / avg_s / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
-                "avg_launch_us": round(avg_s * 1e6, 2)}
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "algorithmic_per_launch": per_launch, "avg_launch_us": round(avg_s * 1e6, 2),
+                "launches_per_step": ds["launches"] // args.profile_steps}
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -149,7 +180,7 @@ def main():
         "step_ms_median": round(float(np.median(step_ms)), 3),
         "step_ms_min": round(float(np.min(step_ms)), 3),
         "loss_first": round(losses[0], 4), "loss_last": round(losses[-1], 4),
-        "kernels": per_kind, "roofline": roof,
+        "kernels": per_kind, "sites": per_site, "roofline": roof,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)

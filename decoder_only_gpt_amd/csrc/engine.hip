@@ -202,7 +202,7 @@ struct gpt_model {
   char* base;
   int state;  // 0 idle, 1 forward with targets done, 2 backward done
   // kernel timing (gpt_profile_begin / gpt_profile_end)
-  struct Rec { int kind; double flops, bytes; hipEvent_t a, b; };
+  struct Rec { int kind, site; double flops, bytes; hipEvent_t a, b; };
   bool prof_on = false;
   std::vector<hipEvent_t> ev_pool;
   size_t ev_used = 0;
@@ -278,8 +278,8 @@ gpt_gemm_desc linear_dw(const gpt_model* m, const void* dy, int64_t N, int64_t l
 
 // Launch `f` (returns hipError_t); inside a profile window bracket it with events.
 template <typename Fn>
-int launch(gpt_model* m, hipStream_t s, int kind, double flops, double bytes, const char* what,
-           Fn f) {
+int launch(gpt_model* m, hipStream_t s, int kind, int site, double flops, double bytes,
+           const char* what, Fn f) {
   hipEvent_t a = nullptr;
   if (m->prof_on && (a = m->next_event()) != nullptr) (void)hipEventRecord(a, s);
   hipError_t e = f();
@@ -288,28 +288,28 @@ int launch(gpt_model* m, hipStream_t s, int kind, double flops, double bytes, co
     hipEvent_t b = m->next_event();
     if (b) {
       (void)hipEventRecord(b, s);
-      m->recs.push_back({kind, flops, bytes, a, b});
+      m->recs.push_back({kind, site, flops, bytes, a, b});
     }
   }
   return GPT_OK;
 }
 
-#define LAUNCH(kind, flops, bytes, expr)                                          \
+#define LAUNCH(kind, site, flops, bytes, expr)                                    \
   do {                                                                            \
-    int rc_ = launch(m, s, kind, (double)(flops), (double)(bytes), #expr,         \
+    int rc_ = launch(m, s, kind, site, (double)(flops), (double)(bytes), #expr,   \
                      [&]() { return (expr); });                                   \
     if (rc_ != GPT_OK) return rc_;                                                \
   } while (0)
 
-int run_gemm(gpt_model* m, hipStream_t s, const gpt_gemm_desc& d) {
+int run_gemm(gpt_model* m, hipStream_t s, const gpt_gemm_desc& d, int site) {
   const int kind = gpt::gemm_split_count(d) > 1 ? GPT_K_GEMM_SPLITK : GPT_K_GEMM;
-  LAUNCH(kind, 2.0 * d.M * d.N * d.K, 0, gpt::gemm(d, s));
+  LAUNCH(kind, site, 2.0 * d.M * d.N * d.K, 0, gpt::gemm(d, s));
   return GPT_OK;
 }
 
-#define GEMM(d)                                   \
+#define GEMM(d, site)                             \
   do {                                            \
-    int rc_ = run_gemm(m, s, (d));                \
+    int rc_ = run_gemm(m, s, (d), (site));        \
     if (rc_ != GPT_OK) return rc_;                \
   } while (0)
 
@@ -328,30 +328,30 @@ int run_forward(gpt_model* m, const int32_t* idx, const int32_t* tgt, hipStream_
   const double ln_fwd_bytes = M * C * (4.0 + act_b) + 8.0 * M;
   const double attn_flops = 4.0 * m->hd * m->B * m->H;
   auto act = [&](int64_t off) { return m->at<char>(off); };
-  LAUNCH(GPT_K_EMBED, 0, 12.0 * M * C,
+  LAUNCH(GPT_K_EMBED, GPT_S_EMBED_FWD, 0, 12.0 * M * C,
          gpt::embed_fwd(prec, idx, m->P(m->pl.wte), m->P(m->pl.wpe), (int)M, m->T, (int)C, m->X(0), s));
   for (int l = 0; l < c.n_layer; ++l) {
     const LayerOff& L = m->pl.layer[l];
-    LAUNCH(GPT_K_LAYERNORM, 0, ln_fwd_bytes,
+    LAUNCH(GPT_K_LAYERNORM, GPT_S_LN_FWD, 0, ln_fwd_bytes,
            gpt::layernorm_fwd(prec, m->X(2 * l), m->P(L.ln1w), m->P(L.ln1b), (int)M, (int)C,
                               c.ln_eps, act(m->ar.a1[l]), m->mean(2 * l), m->rstd(2 * l), s));
     gpt_gemm_desc d = linear_fwd(m, act(m->ar.a1[l]), C, L.qkvw, 3 * C, 3 * C);
     d.epilogue = GPT_EPI_STORE; d.bias = m->P(L.qkvb); d.out = act(m->ar.qkv[l]); d.ldo = 3 * C;
-    GEMM(d);
-    LAUNCH(GPT_K_ATTN_FWD, attn_flops * attn_pairs(m->T, c.window_left[l]), 0,
+    GEMM(d, GPT_S_QKV_FWD);
+    LAUNCH(GPT_K_ATTN_FWD, GPT_S_ATTN_FWD, attn_flops * attn_pairs(m->T, c.window_left[l]), 0,
            gpt::attention_fwd(prec, m->B, m->T, (int)m->H, (int)m->hd, c.window_left[l],
                               act(m->ar.qkv[l]), act(m->ar.att[l]), m->at<float>(m->ar.lse[l]), s));
     d = linear_fwd(m, act(m->ar.att[l]), C, L.projw, C, C);
     d.epilogue = GPT_EPI_RESIDUAL; d.bias = m->P(L.projb); d.resid = m->X(2 * l);
     d.out = m->X(2 * l + 1); d.ldo = C;
-    GEMM(d);
-    LAUNCH(GPT_K_LAYERNORM, 0, ln_fwd_bytes,
+    GEMM(d, GPT_S_PROJ_FWD);
+    LAUNCH(GPT_K_LAYERNORM, GPT_S_LN_FWD, 0, ln_fwd_bytes,
            gpt::layernorm_fwd(prec, m->X(2 * l + 1), m->P(L.ln2w), m->P(L.ln2b), (int)M, (int)C,
                               c.ln_eps, act(m->ar.a2[l]), m->mean(2 * l + 1), m->rstd(2 * l + 1), s));
     d = linear_fwd(m, act(m->ar.a2[l]), C, L.fcw, F, F);
     d.epilogue = GPT_EPI_GELU; d.bias = m->P(L.fcb); d.out = act(m->ar.u[l]); d.ldo = F;
     d.aux = c.recompute_gelu ? nullptr : act(m->ar.g[l]); d.ldaux = F;
-    GEMM(d);
+    GEMM(d, GPT_S_FC_FWD);
     if (c.recompute_gelu) {
       d = linear_fwd(m, act(m->ar.u[l]), F, L.fcpw, C, C);
       d.a_gelu = 1;
@@ -360,20 +360,20 @@ int run_forward(gpt_model* m, const int32_t* idx, const int32_t* tgt, hipStream_
     }
     d.epilogue = GPT_EPI_RESIDUAL; d.bias = m->P(L.fcpb); d.resid = m->X(2 * l + 1);
     d.out = m->X(2 * l + 2); d.ldo = C;
-    GEMM(d);
+    GEMM(d, GPT_S_FCPROJ_FWD);
   }
   const int64_t nl = 2 * c.n_layer;
-  LAUNCH(GPT_K_LAYERNORM, 0, ln_fwd_bytes,
+  LAUNCH(GPT_K_LAYERNORM, GPT_S_LN_FWD, 0, ln_fwd_bytes,
          gpt::layernorm_fwd(prec, m->X(nl), m->P(m->pl.lnfw), m->P(m->pl.lnfb), (int)M, (int)C,
                             c.ln_eps, act(m->ar.xf), m->mean(nl), m->rstd(nl), s));
   gpt_gemm_desc d = linear_fwd(m, act(m->ar.xf), C, m->pl.lmw, m->Vq, m->Vp);
   d.epilogue = GPT_EPI_STORE; d.out = act(m->ar.logits); d.ldo = m->Vq;
-  GEMM(d);
+  GEMM(d, GPT_S_LMHEAD_FWD);
   if (tgt) {
-    LAUNCH(GPT_K_CROSS_ENTROPY, 0, 2.0 * M * m->Vq * act_b + 8.0 * M,
+    LAUNCH(GPT_K_CROSS_ENTROPY, GPT_S_CROSS_ENTROPY, 0, 2.0 * M * m->Vq * act_b + 8.0 * M,
            gpt::cross_entropy(prec, act(m->ar.logits), (int)M, c.vocab_size, (int)m->Vq, tgt,
                               m->at<float>(m->ar.loss_rows), s));
-    LAUNCH(GPT_K_CROSS_ENTROPY, 0, 4.0 * M,
+    LAUNCH(GPT_K_CROSS_ENTROPY, GPT_S_CROSS_ENTROPY, 0, 4.0 * M,
            gpt::mean_loss(m->at<float>(m->ar.loss_rows), (int)M, m->at<float>(m->ar.loss), s));
   }
   return GPT_OK;
@@ -398,7 +398,7 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
   float* gres[2] = {m->at<float>(m->ar.gres[0]), m->at<float>(m->ar.gres[1])};
   auto bias_grad = [&](const char* x, int64_t n, int64_t off) -> int {
     if (off < 0) return GPT_OK;
-    LAUNCH(GPT_K_BIAS_GRAD, 0, M * n * act_b,
+    LAUNCH(GPT_K_BIAS_GRAD, GPT_S_BIAS_GRAD, 0, M * n * act_b,
            gpt::colsum(prec, x, (int)M, (int)n, m->G(off), acc, cs_part, s));
     return GPT_OK;
   };
@@ -412,11 +412,11 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
   const char* dlog = act(m->ar.logits);
   gpt_gemm_desc d = linear_dx(m, dlog, m->Vq, m->pl.lmw, C, m->Vq, m->Vp);
   d.epilogue = GPT_EPI_STORE; d.out = dC; d.ldo = C;
-  GEMM(d);
+  GEMM(d, GPT_S_LMHEAD_DX);
   d = linear_dw(m, dlog, m->Vq, m->Vq, act(m->ar.xf), C, m->pl.lmw, m->Vp, acc);
-  GEMM(d);
+  GEMM(d, GPT_S_LMHEAD_DW);
   const int64_t nl = 2 * c.n_layer;
-  LAUNCH(GPT_K_LAYERNORM, 0, ln_bwd_bytes - 4.0 * M * C,
+  LAUNCH(GPT_K_LAYERNORM, GPT_S_LN_BWD, 0, ln_bwd_bytes - 4.0 * M * C,
          gpt::layernorm_bwd(prec, dC, m->X(nl), m->mean(nl), m->rstd(nl), m->P(m->pl.lnfw), nullptr,
                             (int)M, (int)C, gres[cur], gact, m->G(m->pl.lnfw), m->G(m->pl.lnfb),
                             acc, ln_part, s));
@@ -425,23 +425,23 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
     // MLP out: x_out = x_mid + GELU(u) Wfcp^T + b
     d = linear_dx(m, gact, C, L.fcpw, F, C, C);
     d.epilogue = GPT_EPI_DGELU; d.aux = act(m->ar.u[l]); d.ldaux = F; d.out = dF; d.ldo = F;
-    GEMM(d);
+    GEMM(d, GPT_S_FCPROJ_DX);
     if (c.recompute_gelu) {
       d = linear_dw(m, gact, C, C, act(m->ar.u[l]), F, L.fcpw, C, acc);
       d.b_gelu = 1;
     } else {
       d = linear_dw(m, gact, C, C, act(m->ar.g[l]), F, L.fcpw, C, acc);
     }
-    GEMM(d);
+    GEMM(d, GPT_S_FCPROJ_DW);
     BIAS_GRAD(gact, C, L.fcpb);
     // MLP in: u = a2 Wfc^T + b
     d = linear_dx(m, dF, F, L.fcw, C, F, F);
     d.epilogue = GPT_EPI_STORE; d.out = dC; d.ldo = C;
-    GEMM(d);
+    GEMM(d, GPT_S_FC_DX);
     d = linear_dw(m, dF, F, F, act(m->ar.a2[l]), C, L.fcw, F, acc);
-    GEMM(d);
+    GEMM(d, GPT_S_FC_DW);
     BIAS_GRAD(dF, F, L.fcb);
-    LAUNCH(GPT_K_LAYERNORM, 0, ln_bwd_bytes,
+    LAUNCH(GPT_K_LAYERNORM, GPT_S_LN_BWD, 0, ln_bwd_bytes,
            gpt::layernorm_bwd(prec, dC, m->X(2 * l + 1), m->mean(2 * l + 1), m->rstd(2 * l + 1),
                               m->P(L.ln2w), gres[cur], (int)M, (int)C, gres[cur ^ 1], gact,
                               m->G(L.ln2w), m->G(L.ln2b), acc, ln_part, s));
@@ -449,22 +449,22 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
     // attention out: x_mid = x_in + y Wproj^T + b
     d = linear_dx(m, gact, C, L.projw, C, C, C);
     d.epilogue = GPT_EPI_STORE; d.out = dC2; d.ldo = C;
-    GEMM(d);
+    GEMM(d, GPT_S_PROJ_DX);
     d = linear_dw(m, gact, C, C, act(m->ar.att[l]), C, L.projw, C, acc);
-    GEMM(d);
+    GEMM(d, GPT_S_PROJ_DW);
     BIAS_GRAD(gact, C, L.projb);
-    LAUNCH(GPT_K_ATTN_BWD, attn_flops * attn_pairs(m->T, c.window_left[l]), 0,
+    LAUNCH(GPT_K_ATTN_BWD, GPT_S_ATTN_BWD, attn_flops * attn_pairs(m->T, c.window_left[l]), 0,
            gpt::attention_bwd(prec, m->B, m->T, (int)m->H, (int)m->hd, c.window_left[l],
                               act(m->ar.qkv[l]), act(m->ar.att[l]), m->at<float>(m->ar.lse[l]),
                               dC2, dqkv, m->at<float>(m->ar.dvec), s));
     // qkv = a1 Wqkv^T + b
     d = linear_dx(m, dqkv, 3 * C, L.qkvw, C, 3 * C, 3 * C);
     d.epilogue = GPT_EPI_STORE; d.out = dC; d.ldo = C;
-    GEMM(d);
+    GEMM(d, GPT_S_QKV_DX);
     d = linear_dw(m, dqkv, 3 * C, 3 * C, act(m->ar.a1[l]), C, L.qkvw, 3 * C, acc);
-    GEMM(d);
+    GEMM(d, GPT_S_QKV_DW);
     BIAS_GRAD(dqkv, 3 * C, L.qkvb);
-    LAUNCH(GPT_K_LAYERNORM, 0, ln_bwd_bytes,
+    LAUNCH(GPT_K_LAYERNORM, GPT_S_LN_BWD, 0, ln_bwd_bytes,
            gpt::layernorm_bwd(prec, dC, m->X(2 * l), m->mean(2 * l), m->rstd(2 * l), m->P(L.ln1w),
                               gres[cur], (int)M, (int)C, gres[cur ^ 1], gact, m->G(L.ln1w),
                               m->G(L.ln1b), acc, ln_part, s));
@@ -475,7 +475,7 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
   gpt::EmbedBwdScratch scr{m->at<int32_t>(m->ar.e_counts), m->at<int32_t>(m->ar.e_offsets),
                            m->at<int32_t>(m->ar.e_perm)};
   const int wte_acc = (c.tied_lm_head || acc) ? 1 : 0;
-  LAUNCH(GPT_K_EMBED, 0, 4.0 * M * C + 4.0 * (m->Vp + c.block_size) * C,
+  LAUNCH(GPT_K_EMBED, GPT_S_EMBED_BWD, 0, 4.0 * M * C + 4.0 * (m->Vp + c.block_size) * C,
          gpt::embed_bwd(m->last_idx, gres[cur], (int)M, m->T, (int)C, (int)m->Vp, c.block_size,
                         m->G(m->pl.wte), wte_acc, m->G(m->pl.wpe), acc, scr, s));
   return GPT_OK;
@@ -622,7 +622,7 @@ int gpt_grad_norm(gpt_model* m, void* stream, double* h_norm) {
   if (!m || !h_norm) return fail(GPT_E_INVALID, "NULL argument");
   if (m->state != 2) return fail(GPT_E_STATE, "grad_norm needs a backward first");
   hipStream_t s = (hipStream_t)stream;
-  LAUNCH(GPT_K_NORM, 0, 4.0 * m->N,
+  LAUNCH(GPT_K_NORM, GPT_S_GRAD_NORM, 0, 4.0 * m->N,
          gpt::sumsq(m->G(0), m->N, m->at<double>(m->ar.n_part), m->at<double>(m->ar.norm2), s));
   double n2 = 0.0;
   HIP_TRY(hipMemcpyAsync(&n2, m->at<double>(m->ar.norm2), 8, hipMemcpyDeviceToHost, s));
@@ -638,7 +638,7 @@ int gpt_adamw_step(gpt_model* m, const gpt_adamw_hp* hp, void* stream) {
   if (rc != GPT_OK) return rc;
   if (m->state != 2) return fail(GPT_E_STATE, "adamw_step needs a backward first");
   hipStream_t s = (hipStream_t)stream;
-  LAUNCH(GPT_K_ADAMW, 0, (m->bf16 ? 30.0 : 28.0) * m->N,
+  LAUNCH(GPT_K_ADAMW, GPT_S_ADAMW, 0, (m->bf16 ? 30.0 : 28.0) * m->N,
          gpt::adamw(m->N, m->P(0), m->at<float>(m->ar.adam_m), m->at<float>(m->ar.adam_v), m->G(0),
                     m->bf16 ? m->at<uint16_t>(m->ar.shadow) : nullptr, adam_scalars(*hp), s));
   m->state = 0;
@@ -696,19 +696,23 @@ int gpt_profile_begin(gpt_model* m) {
   return GPT_OK;
 }
 
-int gpt_profile_end(gpt_model* m, void* stream, gpt_kernel_stats* out) {
+int gpt_profile_end(gpt_model* m, void* stream, gpt_kernel_stats* out, gpt_kernel_stats* sites) {
   if (!m || !out) return fail(GPT_E_INVALID, "NULL argument");
   m->prof_on = false;
   for (int k = 0; k < GPT_NUM_KERNEL_KINDS; ++k) out[k] = gpt_kernel_stats{0, 0.0, 0.0, 0.0};
+  if (sites)
+    for (int k = 0; k < GPT_NUM_SITES; ++k) sites[k] = gpt_kernel_stats{0, 0.0, 0.0, 0.0};
   HIP_TRY(hipStreamSynchronize((hipStream_t)stream));
   for (const auto& r : m->recs) {
     float ms = 0.f;
     HIP_TRY(hipEventElapsedTime(&ms, r.a, r.b));
-    gpt_kernel_stats& o = out[r.kind];
-    o.launches += 1;
-    o.ms += ms;
-    o.flops += r.flops;
-    o.bytes += r.bytes;
+    for (gpt_kernel_stats* o : {&out[r.kind], sites ? &sites[r.site] : nullptr}) {
+      if (!o) continue;
+      o->launches += 1;
+      o->ms += ms;
+      o->flops += r.flops;
+      o->bytes += r.bytes;
+    }
   }
   m->recs.clear();
   m->ev_used = 0;

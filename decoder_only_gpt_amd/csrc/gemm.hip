@@ -826,8 +826,8 @@ GemmPlan plan_gemm(int M, int N, int K, int precision, bool splittable, int64_t 
         return p;
       }
     }
-    // Very wide products (the vocabulary projection): 256-tiles.
-    if (!splittable && t256 >= 4096) {
+    // The vocabulary projection and its input gradient (N or K = vocabulary): 256-tiles.
+    if (!splittable && (t256 >= 4096 || K >= 16384)) {
       p.big = true;
       return p;
     }

@@ -31,6 +31,10 @@ EXPORTS = [
 ]
 KERNEL_KINDS = ["gemm", "gemm_splitk", "attn_fwd", "attn_bwd", "layernorm", "cross_entropy",
                 "embed", "bias_grad", "norm", "adamw"]
+SITES = ["embed_fwd", "ln_fwd", "qkv_fwd", "attn_fwd", "proj_fwd", "fc_fwd", "fcproj_fwd",
+         "lmhead_fwd", "cross_entropy", "lmhead_dx", "lmhead_dw", "ln_bwd", "fcproj_dx", "fcproj_dw",
+         "fc_dx", "fc_dw", "proj_dx", "proj_dw", "attn_bwd", "qkv_dx", "qkv_dw", "bias_grad",
+         "embed_bwd", "grad_norm", "adamw"]
 
 
 class GptError(RuntimeError):
@@ -118,7 +122,7 @@ def lib():
         "gpt_op_attention_bwd": ([i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp], i32),
         "gpt_op_adamw": ([i64, vp, vp, vp, vp, vp, ctypes.POINTER(AdamHP), vp], i32),
         "gpt_profile_begin": ([vp], i32),
-        "gpt_profile_end": ([vp, vp, ctypes.POINTER(KernelStats)], i32),
+        "gpt_profile_end": ([vp, vp, ctypes.POINTER(KernelStats), ctypes.POINTER(KernelStats)], i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -255,11 +259,14 @@ class Model:
     def profile_begin(self):
         _check(lib().gpt_profile_begin(self.h))
 
-    def profile_end(self) -> dict:
+    def profile_end(self):
+        """(per kernel kind, per call site) dicts of launches / ms / flops / bytes."""
         arr = (KernelStats * len(KERNEL_KINDS))()
-        _check(lib().gpt_profile_end(self.h, _stream(), arr))
-        return {k: dict(launches=int(a.launches), ms=a.ms, flops=a.flops, bytes=a.bytes)
-                for k, a in zip(KERNEL_KINDS, arr)}
+        sites = (KernelStats * len(SITES))()
+        _check(lib().gpt_profile_end(self.h, _stream(), arr, sites))
+        conv = lambda names, a: {k: dict(launches=int(x.launches), ms=x.ms, flops=x.flops,
+                                          bytes=x.bytes) for k, x in zip(names, a)}
+        return conv(KERNEL_KINDS, arr), conv(SITES, sites)
 
     def train_step(self, idx, tgt) -> dict:
         """forward -> loss -> backward -> (norm, clip) -> AdamW; returns loss/norm/scale."""

@@ -1,0 +1,149 @@
+"""Workloads for rocprofv3 runs and the summaries committed from them.
+
+    python -m decoder_only_gpt_amd.profile_run step [--config gpt2_124m] [--steps 3]
+        a few training steps (forward, loss, backward, norm, AdamW) of a preset
+    python -m decoder_only_gpt_amd.profile_run copy [--mib 1024]
+        one plain device-to-device copy of a known size (counter calibration)
+    python -m decoder_only_gpt_amd.profile_run summarize-stats CSV OUT --command "..."
+        rocprofv3 --stats kernel table -> short text summary
+    python -m decoder_only_gpt_amd.profile_run summarize-traffic --kernel SUBSTR
+        --fetch CSV --write CSV --copy-fetch CSV --copy-write CSV --copy-mib N OUT --command "..."
+        per-dispatch FETCH_SIZE / WRITE_SIZE of one kernel, scaled by the same counters
+        on the copy of known size -> JSON used by bench.py
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+
+
+def kernel_source_sha() -> str:
+    """Hash of the HIP sources the measured kernels are built from."""
+    h = hashlib.sha256()
+    csrc = os.path.join(HERE, "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def run_step(config: str, steps: int):
+    import torch
+    from decoder_only_gpt_amd import gpt, presets, synth
+    cfg = presets.preset(config)
+    m = gpt.Model(cfg)
+    m.set_params(synth.init_params(cfg, seed=0))
+    idx, tgt = synth.tokens(cfg, seed=1)
+    di = torch.from_numpy(idx.reshape(-1)).cuda()
+    dt = torch.from_numpy(tgt.reshape(-1)).cuda()
+    for i in range(steps):
+        r = m.train_step(di, dt)
+        print(f"step {i} loss {r['loss']:.4f}", flush=True)
+    torch.cuda.synchronize()
+
+
+def run_copy(mib: int):
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"copied {mib} MiB", flush=True)
+
+
+def summarize_stats(csv_path: str, out_path: str, command: str, top: int = 40):
+    rows = list(csv.DictReader(open(csv_path)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    lines = [f"# rocprofv3 kernel statistics", f"# command: {command}",
+             f"# kernel sources sha: {kernel_source_sha()}",
+             f"# total kernel time {total / 1e6:.3f} ms over the profiled run", "",
+             f"{'calls':>6} {'total_ms':>9} {'avg_us':>9} {'pct':>6}  kernel"]
+    for r in rows[:top]:
+        name = r["Name"]
+        if len(name) > 110:
+            name = name[:107] + "..."
+        lines.append(f"{int(r['Calls']):>6} {float(r['TotalDurationNs']) / 1e6:>9.3f} "
+                     f"{float(r['AverageNs']) / 1e3:>9.2f} {float(r['Percentage']):>6.2f}  {name}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _per_dispatch(csv_path: str, counter: str, substr: str):
+    vals = []
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] == counter and substr in r["Kernel_Name"]:
+            vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} rows for kernels matching {substr!r} in {csv_path}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def summarize_traffic(args):
+    fetch, nf = _per_dispatch(args.fetch, "FETCH_SIZE", args.kernel)
+    write, nw = _per_dispatch(args.write, "WRITE_SIZE", args.kernel)
+    cf, _ = _per_dispatch(args.copy_fetch, "FETCH_SIZE", args.copy_kernel)
+    cw, _ = _per_dispatch(args.copy_write, "WRITE_SIZE", args.copy_kernel)
+    known_kib = args.copy_mib * 1024.0
+    sf, sw = known_kib / cf, known_kib / cw
+    out = {
+        "kernel": args.kernel, "site": args.site, "command": args.command,
+        "kernel_source_sha": kernel_source_sha(),
+        "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
+        "dispatches": [nf, nw],
+        "copy_mib": args.copy_mib, "copy_fetch_kib": cf, "copy_write_kib": cw,
+        "scale_fetch": sf, "scale_write": sw,
+        "hbm_bytes_per_launch": (fetch * sf + write * sw) * 1024.0,
+    }
+    with open(args.out, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    p = sub.add_parser("step")
+    p.add_argument("--config", default="gpt2_124m")
+    p.add_argument("--steps", type=int, default=3)
+    p = sub.add_parser("copy")
+    p.add_argument("--mib", type=int, default=1024)
+    p = sub.add_parser("summarize-stats")
+    p.add_argument("csv")
+    p.add_argument("out")
+    p.add_argument("--command", required=True)
+    p = sub.add_parser("summarize-traffic")
+    p.add_argument("out")
+    p.add_argument("--kernel", required=True)
+    p.add_argument("--site", required=True)
+    p.add_argument("--copy-kernel", default="copy")
+    p.add_argument("--fetch", required=True)
+    p.add_argument("--write", required=True)
+    p.add_argument("--copy-fetch", required=True)
+    p.add_argument("--copy-write", required=True)
+    p.add_argument("--copy-mib", type=int, default=1024)
+    p.add_argument("--command", required=True)
+    a = ap.parse_args()
+    if a.cmd == "step":
+        sys.path.insert(0, ROOT)
+        run_step(a.config, a.steps)
+    elif a.cmd == "copy":
+        run_copy(a.mib)
+    elif a.cmd == "summarize-stats":
+        summarize_stats(a.csv, a.out, a.command)
+    else:
+        summarize_traffic(a)
+
+
+if __name__ == "__main__":
+    main()

@@ -191,9 +191,20 @@ typedef struct gpt_kernel_stats {
   double ms, flops, bytes;
 } gpt_kernel_stats;
 
+/* Call sites of the step (one per distinct launch in the layer loop).  Each
+ * matrix-product site maps to exactly one kernel specialisation. */
+typedef enum gpt_site {
+  GPT_S_EMBED_FWD = 0, GPT_S_LN_FWD, GPT_S_QKV_FWD, GPT_S_ATTN_FWD, GPT_S_PROJ_FWD,
+  GPT_S_FC_FWD, GPT_S_FCPROJ_FWD, GPT_S_LMHEAD_FWD, GPT_S_CROSS_ENTROPY, GPT_S_LMHEAD_DX,
+  GPT_S_LMHEAD_DW, GPT_S_LN_BWD, GPT_S_FCPROJ_DX, GPT_S_FCPROJ_DW, GPT_S_FC_DX, GPT_S_FC_DW,
+  GPT_S_PROJ_DX, GPT_S_PROJ_DW, GPT_S_ATTN_BWD, GPT_S_QKV_DX, GPT_S_QKV_DW, GPT_S_BIAS_GRAD,
+  GPT_S_EMBED_BWD, GPT_S_GRAD_NORM, GPT_S_ADAMW,
+  GPT_NUM_SITES
+} gpt_site;
+
 int gpt_profile_begin(gpt_model* m);
-/* out: GPT_NUM_KERNEL_KINDS entries. */
-int gpt_profile_end(gpt_model* m, void* stream, gpt_kernel_stats* out);
+/* out: GPT_NUM_KERNEL_KINDS entries; sites (may be NULL): GPT_NUM_SITES entries. */
+int gpt_profile_end(gpt_model* m, void* stream, gpt_kernel_stats* out, gpt_kernel_stats* sites);
 
 /* Release the host handle (the arena stays the caller's). */
 int gpt_destroy(gpt_model* m);
