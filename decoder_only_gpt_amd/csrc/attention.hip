@@ -76,11 +76,13 @@ __global__ void __launch_bounds__(256) attn_fwd_rows(const T* qkv, T* out, float
 }
 
 // D[b,h,i] = sum_d dO[i,d] * O[i,d]  (one thread per (row, head)).
-// bf16: one wave per token row; a lane takes 8 consecutive head dims (16-byte
+// bf16: also the log-sum-exp in log2 units, L2 = lse * log2(e), for the
+// MFMA backward kernels.  One wave per token row; a lane takes 8 consecutive head dims (16-byte
 // loads) and the hd/8 lanes of a head combine by butterfly shuffles.
 template <int HD>
 __global__ void __launch_bounds__(256) attn_dvec_bf16(const bf16_t* out, const bf16_t* dout,
-                                                      float* D, int M, int Tn, int H) {
+                                                      const float* lse, float* D, float* L2, int M,
+                                                      int Tn, int H) {
   constexpr int LPH = HD / 8;  // lanes per head
   const int lane = threadIdx.x & 63;
   const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -99,8 +101,9 @@ __global__ void __launch_bounds__(256) attn_dvec_bf16(const bf16_t* out, const b
 #pragma unroll
     for (int o = 1; o < LPH; o <<= 1) s += __shfl_xor(s, o, 64);
     if (v < C / 8 && (lane % LPH) == 0) {
-      const int h = v / LPH;
-      D[((long)b * H + h) * Tn + t] = s;
+      const long o = ((long)b * H + v / LPH) * Tn + t;
+      D[o] = s;
+      L2[o] = lse[o] * LOG2E;
     }
   }
 }
@@ -212,62 +215,59 @@ __global__ void __launch_bounds__(256) attn_dkv_rows(const T* qkv, const float* 
 
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernels.
+//
+// Tiles of 64 rows x HD head dims are fetched straight into LDS with buffer
+// loads (buffer_load_dwordx4 ... lds): one wave instruction fills a contiguous
+// 1 KB block (lane l -> bytes 16 l), so tile rows are stored densely (2 HD
+// bytes each) and the 16-byte chunk index is XOR-swizzled through the source
+// address each lane picks.  Rows at or past the sequence end get an offset
+// outside the buffer and read zeros.  Tile t + 1 is in flight while tile t is
+// multiplied; one barrier per tile.
 // ---------------------------------------------------------------------------
-constexpr int KB = 64;  // keys (forward / dQ) or queries (dK/dV) per LDS block
+constexpr int KB = 64;  // rows per LDS tile: keys (forward, dQ) or queries (dK/dV)
 
-// LDS row pitch of a [64][HD] tile: HD + 24 bf16 puts any 16 consecutive rows
-// of a 16-byte fragment read on distinct 4-bank groups and the four rows of a
-// transpose read (32 bytes each) on disjoint banks, for 64 (or 32) banks.
-template <int HD> constexpr int pitch_of() { return HD + 24; }
+typedef __attribute__((address_space(3))) void lds_void;
 
-// Rows [row0, row0+64) x HD of a strided bf16 matrix into LDS [64][pitch];
-// rows >= nrows read as zero.
-template <int HD>
-__device__ __forceinline__ void lds_rows(const bf16_t* src, long ld, int row0, int nrows,
-                                         bf16_t* dst) {
-  constexpr int VPR = HD / 8, P = pitch_of<HD>();  // 16-byte vectors per row
-  for (int u = threadIdx.x; u < KB * VPR; u += 256) {
-    int r = u / VPR, c = (u % VPR) * 8;
-    u32x4 val = {0, 0, 0, 0};
-    if (row0 + r < nrows) val = *(const u32x4*)(src + (long)(row0 + r) * ld + c);
-    *(u32x4*)(dst + r * P + c) = val;
-  }
+// Chunk swizzle of tile row r: the 16 rows of a 16-byte fragment read and the
+// 4 rows x 64 bytes of a transpose read land on distinct 16-byte bank groups
+// (64 banks of 4 bytes).
+template <int HD> __device__ __forceinline__ int swz(int r) {
+  if constexpr (HD == 32) return (r >> 2) & 3;
+  else if constexpr (HD == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  else return ((r & 3) << 2) | ((r >> 2) & 3);
+}
+// Element offset of (row r, head dim col) in a swizzled tile.
+template <int HD> __device__ __forceinline__ int toff(int r, int col) {
+  return r * HD + (((col >> 3) ^ swz<HD>(r)) << 3) + (col & 7);
 }
 
-// Register staging of one [64][HD] tile: vector v = t + 256 i covers row
-// v / (HD/8), head dims (v % (HD/8)) * 8 .. + 7.  Loading the next block into
-// registers while the current one is multiplied hides the global latency.
-template <int HD> struct TileRegs { u32x4 v[(KB * HD / 8 + 255) / 256]; };
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
 
+// This wave's share of the loads of rows [row0, row0 + 64), columns
+// [col0, col0 + HD) of a bf16 matrix (leading dimension ld) into a tile.
 template <int HD>
-__device__ __forceinline__ void tile_load(const bf16_t* src, long ld, int row0, int nrows,
-                                          TileRegs<HD>& t) {
-  constexpr int VPR = HD / 8, NV = (KB * HD / 8 + 255) / 256;
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, long ld, int col0, int row0,
+                                         int nrows, bf16_t* lds, int wave, int lane) {
+  constexpr int NC = HD / 8, RPB = 64 / NC, NB = KB / RPB;  // chunks / row, rows / block, blocks
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int u = threadIdx.x + 256 * i;
-    const int r = u / VPR, c = (u % VPR) * 8;
-    u32x4 val = {0, 0, 0, 0};
-    if (u < KB * VPR && row0 + r < nrows) val = *(const u32x4*)(src + (long)(row0 + r) * ld + c);
-    t.v[i] = val;
+  for (int i = 0; i < NB / 4; ++i) {
+    const int blk = wave * (NB / 4) + i;
+    const int r = blk * RPB + lane / NC;
+    const int chunk = (lane % NC) ^ swz<HD>(r);
+    const unsigned off = row0 + r < nrows
+                             ? (unsigned)(((long)(row0 + r) * ld + col0 + chunk * 8) * 2)
+                             : 0x80000000u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + blk * 512), 16, off, 0, 0, 0);
   }
 }
 
-template <int HD>
-__device__ __forceinline__ void tile_store(const TileRegs<HD>& t, bf16_t* dst) {
-  constexpr int VPR = HD / 8, NV = (KB * HD / 8 + 255) / 256, P = pitch_of<HD>();
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int u = threadIdx.x + 256 * i;
-    if (u < KB * VPR) *(u32x4*)(dst + (u / VPR) * P + (u % VPR) * 8) = t.v[i];
-  }
-}
-
-// MFMA operand fragment whose lane index (lane % 32) runs along the row of a
-// tile: row r0 + lane % 32, head dims 16 st + 8 (lane / 32) + 0..7.
+// MFMA operand fragment whose lane index (lane % 32) runs along the tile rows:
+// row r0 + lane % 32, head dims 16 st + 8 (lane / 32) + 0..7.
 template <int HD>
 __device__ __forceinline__ bf16x8 row_frag(const bf16_t* t, int r0, int st, int lane) {
-  return *(const bf16x8*)(t + (r0 + (lane & 31)) * pitch_of<HD>() + 16 * st + 8 * (lane >> 5));
+  return *(const bf16x8*)(t + toff<HD>(r0 + (lane & 31), 16 * st + 8 * (lane >> 5)));
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -281,13 +281,12 @@ typedef short v8i16 __attribute__((ext_vector_type(8)));
 // 4 a .. 4 a + 3) and lane j receives column j of rows kb .. kb + 3.
 template <int HD>
 __device__ __forceinline__ bf16x8 tr_slots(const bf16_t* t, int c0, int base, int lane) {
-  constexpr int P = pitch_of<HD>();
   const int s = lane & 15, grp = lane >> 4;
   const int col = c0 + 16 * (grp & 1) + 4 * (s & 3);
   const int row = base + 4 * (grp >> 1) + (s >> 2);
   typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-  v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(t + row * P + col));
-  v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(t + (row + 8) * P + col));
+  v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(t + toff<HD>(row, col)));
+  v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(t + toff<HD>(row + 8, col)));
   v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return *(bf16x8*)&v;
 }
@@ -299,20 +298,36 @@ __device__ __forceinline__ bf16x8 acc_slots(const f32x16& acc, int s2) {
   return *(bf16x8*)&v;
 }
 
+// Row of accumulator register r for lane half g of a 32x32 MFMA block.
 __device__ __forceinline__ int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
 
+// Store a [32 dims][32 columns] accumulator block (lane % 32 = column) as
+// bf16 into row `dst` (this lane's column), head dims d0 + acc_row(r, g).
+__device__ __forceinline__ void store_dims(bf16_t* dst, int d0, const f32x16& a, float mul, int g) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *(uint2*)(dst + d0 + 8 * i + 4 * g) =
+        make_uint2(pack_bf2(a[4 * i] * mul, a[4 * i + 1] * mul),
+                   pack_bf2(a[4 * i + 2] * mul, a[4 * i + 3] * mul));
+}
+
+template <bool B> struct Mask { static constexpr bool value = B; };
+
+// Forward: 128 queries of one (batch, head) per workgroup, 32 per wave.
 template <int HD>
-__global__ void __launch_bounds__(256) attn_fwd_mfma(const bf16_t* qkv, bf16_t* out, float* lse,
-                                                     int Tn, int H, int left, float scale_log2) {
-  constexpr int P = pitch_of<HD>(), NS = HD / 16, ND = HD / 32;
-  __shared__ __attribute__((aligned(16))) bf16_t Kbuf[2][KB * P];
-  __shared__ __attribute__((aligned(16))) bf16_t Vbuf[2][KB * P];
+__global__ void __launch_bounds__(256, HD == 128 ? 1 : 2)
+    attn_fwd_mfma(const bf16_t* qkv, bf16_t* out, float* lse, int Tn, int H, int left,
+                  float scale_log2) {
+  constexpr int NS = HD / 16, ND = HD / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KB * HD];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][KB * HD];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, c = lane & 31;
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int h = blockIdx.x % H, b = blockIdx.x / H;
   const long C = (long)H * HD, ld = 3 * C;
   const bf16_t* base = qkv + (long)b * Tn * ld;
-  const int qblk0 = blockIdx.x * 128;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, (long)Tn * ld * 2);
+  const int qblk0 = (gridDim.y - 1 - blockIdx.y) * 128;  // longest key ranges first
   const int qw0 = qblk0 + wave * 32;
   const int qi = qw0 + c;  // this lane's query
 
@@ -323,65 +338,46 @@ __global__ void __launch_bounds__(256) attn_fwd_mfma(const bf16_t* qkv, bf16_t* 
     if (qi < Tn) v = *(const u32x4*)(base + (long)qi * ld + h * HD + 16 * s + 8 * g);
     qf[s] = *(bf16x8*)&v;
   }
-  f32x16 o[ND];
+  f32x16 o[ND];  // O^T: head dim d * 32 + acc_row(r, g), query qi
 #pragma unroll
-  for (int d = 0; d < ND; ++d)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
-  float mrow = -1e30f, lrow = 0.f;
+  for (int d = 0; d < ND; ++d) o[d] = f32x16{};
+  float mrow = -1e30f, lrow = 0.f;  // running max (log2 units) and sum
 
   const int qlast = min(Tn - 1, qblk0 + 127);
-  const int kfirst = left < 0 ? 0 : max(0, qblk0 - left);
-  const int kstart = (kfirst / KB) * KB;
-  TileRegs<HD> rk, rv;
-  tile_load<HD>(base + C + h * HD, ld, kstart, Tn, rk);
-  tile_load<HD>(base + 2 * C + h * HD, ld, kstart, Tn, rv);
-  tile_store<HD>(rk, Kbuf[0]);
-  tile_store<HD>(rv, Vbuf[0]);
-  __syncthreads();
-  int buf = 0;
-  for (int kb0 = kstart; kb0 <= qlast; kb0 += KB, buf ^= 1) {
-    const bf16_t* Ks = Kbuf[buf];
-    const bf16_t* Vs = Vbuf[buf];
-    const bool more = kb0 + KB <= qlast;
-    if (more) {  // next block's tiles travel while this one is multiplied
-      tile_load<HD>(base + C + h * HD, ld, kb0 + KB, Tn, rk);
-      tile_load<HD>(base + 2 * C + h * HD, ld, kb0 + KB, Tn, rv);
-    }
-    const bool skip = kb0 > qw0 + 31 || (left >= 0 && kb0 + KB - 1 < qw0 - left);
-    if (!skip) {
-    // every (query, key) of this wave and block visible: no per-element mask
-    const bool full = kb0 + KB - 1 <= qw0 && qw0 + 31 < Tn && (left < 0 || qw0 + 31 - kb0 <= left);
+  const int kstart = left < 0 ? 0 : (max(0, qblk0 - left) / KB) * KB;
+
+  auto step = [&](const bf16_t* Kt, const bf16_t* Vt, int kb0, auto mask) {
+    constexpr bool MASK = decltype(mask)::value;
     f32x16 s[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kk][r] = 0.f;
+      s[kk] = f32x16{};
 #pragma unroll
       for (int st = 0; st < NS; ++st)
-        s[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<HD>(Ks, kk * 32, st, lane), qf[st],
+        s[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<HD>(Kt, kk * 32, st, lane), qf[st],
                                                         s[kk], 0, 0, 0);
     }
-    // s[kk][r]: key kb0 + kk*32 + acc_row(r, g), query qi (scaled to log2 units below)
-    float mx = -1e30f;
+    // s[kk][r]: key kb0 + kk * 32 + acc_row(r, g), query qi (raw scores)
+    float mx = -INFINITY;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        int j = kb0 + kk * 32 + acc_row(r, g);
-        float v = (full || visible(qi, j, left, Tn)) ? s[kk][r] * scale_log2 : -INFINITY;
-        s[kk][r] = v;
-        mx = fmaxf(mx, v);
+        if constexpr (MASK) {
+          const int j = kb0 + kk * 32 + acc_row(r, g);
+          if (!visible(qi, j, left, Tn)) s[kk][r] = -INFINITY;
+        }
+        mx = fmaxf(mx, s[kk][r]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mnew = fmaxf(mrow, mx);
-    const float alpha = exp2f(mrow - mnew);
+    const float mnew = fmaxf(mrow, mx * scale_log2);
+    const float alpha = __builtin_amdgcn_exp2f(mrow - mnew);
     float ls = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = exp2f(s[kk][r] - mnew);
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kk][r], scale_log2, -mnew));
         s[kk][r] = p;
         ls += p;
       }
@@ -389,64 +385,71 @@ __global__ void __launch_bounds__(256) attn_fwd_mfma(const bf16_t* qkv, bf16_t* 
     lrow = lrow * alpha + ls;
     mrow = mnew;
 #pragma unroll
-    for (int d = 0; d < ND; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
-    // O^T[d][q] += V^T[d][key] P[key][q]
+    for (int d = 0; d < ND; ++d) o[d] *= alpha;
+    // O^T[d][q] += V^T[d][key] P^T[key][q]
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        bf16x8 pf = acc_slots(s[kk], s2);
+        const bf16x8 pf = acc_slots(s[kk], s2);
 #pragma unroll
         for (int d = 0; d < ND; ++d)
           o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              tr_slots<HD>(Vs, d * 32, kk * 32 + 16 * s2, lane), pf, o[d], 0, 0, 0);
+              tr_slots<HD>(Vt, d * 32, kk * 32 + 16 * s2, lane), pf, o[d], 0, 0, 0);
       }
-    }  // !skip
-    if (more) {
-      tile_store<HD>(rk, Kbuf[buf ^ 1]);
-      tile_store<HD>(rv, Vbuf[buf ^ 1]);
+  };
+
+  dma_tile<HD>(rs, ld, C + h * HD, kstart, Tn, Ks[0], wave, lane);
+  dma_tile<HD>(rs, ld, 2 * C + h * HD, kstart, Tn, Vs[0], wave, lane);
+  int buf = 0;
+  for (int kb0 = kstart; kb0 <= qlast; kb0 += KB, buf ^= 1) {
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's share of tile kb0 landed
+    __syncthreads();                     // ... and every other wave's
+    if (kb0 + KB <= qlast) {
+      dma_tile<HD>(rs, ld, C + h * HD, kb0 + KB, Tn, Ks[buf ^ 1], wave, lane);
+      dma_tile<HD>(rs, ld, 2 * C + h * HD, kb0 + KB, Tn, Vs[buf ^ 1], wave, lane);
     }
-    __syncthreads();
+    const bool skip = kb0 > qw0 + 31 || (left >= 0 && kb0 + KB - 1 < qw0 - left);
+    if (skip) continue;
+    // every (query, key) pair of this wave and block visible: no per-element mask
+    const bool full =
+        kb0 + KB - 1 <= qw0 && qw0 + 31 < Tn && (left < 0 || qw0 + 31 - kb0 <= left);
+    if (full) step(Ks[buf], Vs[buf], kb0, Mask<false>{});
+    else step(Ks[buf], Vs[buf], kb0, Mask<true>{});
   }
   if (qi < Tn) {
     const float inv = 1.f / lrow;
     bf16_t* orow = out + ((long)b * Tn + qi) * C + h * HD;
 #pragma unroll
-    for (int d = 0; d < ND; ++d)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        int dd = d * 32 + 8 * r4 + 4 * g;
-        uint2 w = make_uint2(pack_bf2(o[d][4 * r4 + 0] * inv, o[d][4 * r4 + 1] * inv),
-                             pack_bf2(o[d][4 * r4 + 2] * inv, o[d][4 * r4 + 3] * inv));
-        *(uint2*)(orow + dd) = w;
-      }
+    for (int d = 0; d < ND; ++d) store_dims(orow, d * 32, o[d], inv, g);
     if (g == 0) lse[((long)b * H + h) * Tn + qi] = (mrow + log2f(lrow)) / LOG2E;
   }
 }
 
-// dK, dV: a wave owns 32 keys; loop over the 64-query blocks that see them.
+// dK, dV: 128 keys of one (batch, head) per workgroup, 32 per wave; the
+// workgroup walks the 64-query blocks that can see them.  L2 is the saved
+// log-sum-exp in log2 units, D[q] = sum_d dO[q][d] O[q][d].
 template <int HD>
-__global__ void __launch_bounds__(256) attn_dkv_mfma(const bf16_t* qkv, const float* lse,
-                                                     const bf16_t* dout, const float* D,
-                                                     bf16_t* dqkv, int Tn, int H, int left,
-                                                     float scale, float scale_log2) {
-  constexpr int P = pitch_of<HD>(), NS = HD / 16, ND = HD / 32;
-  __shared__ __attribute__((aligned(16))) bf16_t Qbuf[2][KB * P];
-  __shared__ __attribute__((aligned(16))) bf16_t Gbuf[2][KB * P];
-  __shared__ float Lbuf[2][KB], Dbuf[2][KB];
+__global__ void __launch_bounds__(256, HD == 128 ? 1 : 2)
+    attn_dkv_mfma(const bf16_t* qkv, const float* L2, const bf16_t* dout, const float* D,
+                  bf16_t* dqkv, int Tn, int H, int left, float scale, float scale_log2) {
+  constexpr int NS = HD / 16, ND = HD / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t Qs[2][KB * HD];
+  __shared__ __attribute__((aligned(16))) bf16_t Gs[2][KB * HD];
+  __shared__ __attribute__((aligned(16))) float Ls[2][KB];
+  __shared__ __attribute__((aligned(16))) float Ds[2][KB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, c = lane & 31;
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int h = blockIdx.x % H, b = blockIdx.x / H;
   const long C = (long)H * HD, ld = 3 * C;
   const bf16_t* base = qkv + (long)b * Tn * ld;
-  const bf16_t* gbase = dout + (long)b * Tn * C;
-  const float* lrow = lse + ((long)b * H + h) * Tn;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(base, (long)Tn * ld * 2);
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(dout + (long)b * Tn * C, (long)Tn * C * 2);
+  const float* lrow = L2 + ((long)b * H + h) * Tn;
   const float* drow = D + ((long)b * H + h) * Tn;
-  const int kblk0 = blockIdx.x * 128;
+  const int kblk0 = blockIdx.y * 128;  // earliest keys (most queries) first
   const int kw0 = kblk0 + wave * 32;
-  const int kj = kw0 + c;  // this lane's key (as an operand column)
+  const int kj = kw0 + c;  // this lane's key (operand column)
 
   bf16x8 kf[NS], vf[NS];
 #pragma unroll
@@ -459,117 +462,119 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma(const bf16_t* qkv, const fl
     kf[s] = *(bf16x8*)&a;
     vf[s] = *(bf16x8*)&v;
   }
-  f32x16 dk[ND], dv[ND];
+  f32x16 dk[ND], dv[ND];  // dK^T, dV^T: head dim d * 32 + acc_row(r, g), key kj
 #pragma unroll
-  for (int d = 0; d < ND; ++d)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dk[d][r] = dv[d][r] = 0.f;
+  for (int d = 0; d < ND; ++d) dk[d] = dv[d] = f32x16{};
 
   const int klast = min(Tn - 1, kblk0 + 127);
   const int qend = left < 0 ? Tn - 1 : min(Tn - 1, klast + left);
-  const int qstart = (kblk0 / KB) * KB;
-  TileRegs<HD> rq, rg;
-  float rl = 0.f, rd = 0.f;
-  auto load_blk = [&](int q0) {
-    tile_load<HD>(base + h * HD, ld, q0, Tn, rq);
-    tile_load<HD>(gbase + h * HD, C, q0, Tn, rg);
-    if (threadIdx.x < KB) {
-      const int q = q0 + threadIdx.x;
-      rl = q < Tn ? lrow[q] * LOG2E : 0.f;
-      rd = q < Tn ? drow[q] : 0.f;
-    }
-  };
-  auto store_blk = [&](int bb) {
-    tile_store<HD>(rq, Qbuf[bb]);
-    tile_store<HD>(rg, Gbuf[bb]);
-    if (threadIdx.x < KB) {
-      Lbuf[bb][threadIdx.x] = rl;
-      Dbuf[bb][threadIdx.x] = rd;
-    }
-  };
-  load_blk(qstart);
-  store_blk(0);
-  __syncthreads();
-  int buf = 0;
-  for (int qb0 = qstart; qb0 <= qend; qb0 += KB, buf ^= 1) {
-    const bf16_t* Qs = Qbuf[buf];
-    const bf16_t* Gs = Gbuf[buf];
-    const float* Ls = Lbuf[buf];
-    const float* Ds = Dbuf[buf];
-    const bool more = qb0 + KB <= qend;
-    if (more) load_blk(qb0 + KB);
-    const bool skip = qb0 + KB - 1 < kw0 || (left >= 0 && qb0 > kw0 + 31 + left);
-    if (!skip) {
-    const bool full = qb0 >= kw0 + 31 && qb0 + KB - 1 < Tn && (left < 0 || qb0 + KB - 1 - kw0 <= left);
+
+  auto step = [&](const bf16_t* Qt, const bf16_t* Gt, const float* Lt, const float* Dt, int qb0,
+                  auto mask) {
+    constexpr bool MASK = decltype(mask)::value;
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq) {
-      f32x16 s, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+      f32x16 s{}, dp{};
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<HD>(Qs, qq * 32, st, lane), kf[st], s,
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<HD>(Qt, qq * 32, st, lane), kf[st], s,
                                                     0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<HD>(Gs, qq * 32, st, lane), vf[st],
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<HD>(Gt, qq * 32, st, lane), vf[st],
                                                      dp, 0, 0, 0);
       }
-      // s[r]: query qb0 + qq*32 + acc_row(r, g), key kj.
+      // s[r], dp[r]: query qb0 + qq * 32 + acc_row(r, g), key kj.
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        int ql = qq * 32 + acc_row(r, g);
-        int qi = qb0 + ql;
-        float p = (full || (qi < Tn && visible(qi, kj, left, Tn))) ? exp2f(s[r] * scale_log2 - Ls[ql])
-                                                                   : 0.f;
-        s[r] = p;
-        dp[r] = p * (dp[r] - Ds[ql]);
+      for (int i = 0; i < 4; ++i) {
+        const int ql = qq * 32 + 8 * i + 4 * g;
+        const f32x4 lv = *(const f32x4*)(Lt + ql);
+        const f32x4 dd = *(const f32x4*)(Dt + ql);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float p = __builtin_amdgcn_exp2f(fmaf(s[4 * i + j], scale_log2, -lv[j]));
+          if constexpr (MASK) {
+            const int qi = qb0 + ql + j;
+            if (qi >= Tn || !visible(qi, kj, left, Tn)) p = 0.f;
+          }
+          s[4 * i + j] = p;
+          dp[4 * i + j] = p * (dp[4 * i + j] - dd[j]);
+        }
       }
-      // dV[key][d] += P^T[key][q] dO[q][d];  dK[key][d] += dS^T[key][q] Q[q][d]
+      // dV^T[d][key] += dO^T[d][q] P[q][key];  dK^T[d][key] += Q^T[d][q] dS[q][key]
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        bf16x8 pa = acc_slots(s, s2);
-        bf16x8 da = acc_slots(dp, s2);
+        const bf16x8 pa = acc_slots(s, s2);
+        const bf16x8 da = acc_slots(dp, s2);
 #pragma unroll
         for (int d = 0; d < ND; ++d) {
           dv[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              pa, tr_slots<HD>(Gs, d * 32, qq * 32 + 16 * s2, lane), dv[d], 0, 0, 0);
+              tr_slots<HD>(Gt, d * 32, qq * 32 + 16 * s2, lane), pa, dv[d], 0, 0, 0);
           dk[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              da, tr_slots<HD>(Qs, d * 32, qq * 32 + 16 * s2, lane), dk[d], 0, 0, 0);
+              tr_slots<HD>(Qt, d * 32, qq * 32 + 16 * s2, lane), da, dk[d], 0, 0, 0);
         }
       }
     }
-    }  // !skip
-    if (more) store_blk(buf ^ 1);
-    __syncthreads();
-  }
-  // dk[d][r]: key kw0 + acc_row(r, g), head dim d*32 + c.
-#pragma unroll
-  for (int d = 0; d < ND; ++d)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      int key = kw0 + acc_row(r, g);
-      if (key < Tn) {
-        bf16_t* row = dqkv + ((long)b * Tn + key) * ld + h * HD + d * 32 + c;
-        row[C] = f2bf(dk[d][r] * scale);
-        row[2 * C] = f2bf(dv[d][r]);
-      }
+  };
+
+  // Per-query scalars travel through registers (one per thread of the first wave).
+  float rl = 0.f, rd = 0.f;
+  auto fetch = [&](int q0, int bb) {
+    dma_tile<HD>(rq, ld, h * HD, q0, Tn, Qs[bb], wave, lane);
+    dma_tile<HD>(rg, C, h * HD, q0, Tn, Gs[bb], wave, lane);
+    if (threadIdx.x < KB) {
+      const int q = q0 + threadIdx.x;
+      rl = q < Tn ? lrow[q] : 0.f;
+      rd = q < Tn ? drow[q] : 0.f;
     }
+  };
+  fetch(kblk0, 0);
+  if (threadIdx.x < KB) {
+    Ls[0][threadIdx.x] = rl;
+    Ds[0][threadIdx.x] = rd;
+  }
+  int buf = 0;
+  for (int qb0 = kblk0; qb0 <= qend; qb0 += KB, buf ^= 1) {
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's share of block qb0 landed
+    __syncthreads();                     // ... and every other wave's (tiles and scalars)
+    const bool more = qb0 + KB <= qend;
+    if (more) fetch(qb0 + KB, buf ^ 1);
+    const bool skip = qb0 + KB - 1 < kw0 || (left >= 0 && qb0 > kw0 + 31 + left);
+    if (!skip) {
+      const bool full =
+          qb0 >= kw0 + 31 && qb0 + KB <= Tn && (left < 0 || qb0 + KB - 1 - kw0 <= left);
+      if (full) step(Qs[buf], Gs[buf], Ls[buf], Ds[buf], qb0, Mask<false>{});
+      else step(Qs[buf], Gs[buf], Ls[buf], Ds[buf], qb0, Mask<true>{});
+    }
+    if (more && threadIdx.x < KB) {
+      Ls[buf ^ 1][threadIdx.x] = rl;
+      Ds[buf ^ 1][threadIdx.x] = rd;
+    }
+  }
+  if (kj < Tn) {
+    bf16_t* row = dqkv + ((long)b * Tn + kj) * ld + h * HD;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      store_dims(row + C, d * 32, dk[d], scale, g);
+      store_dims(row + 2 * C, d * 32, dv[d], 1.f, g);
+    }
+  }
 }
 
-// dQ: a wave owns 32 queries; loop over their key blocks.
+// dQ: 128 queries of one (batch, head) per workgroup, 32 per wave; the
+// workgroup walks their key blocks.
 template <int HD>
-__global__ void __launch_bounds__(256) attn_dq_mfma(const bf16_t* qkv, const float* lse,
-                                                    const bf16_t* dout, const float* D,
-                                                    bf16_t* dqkv, int Tn, int H, int left,
-                                                    float scale, float scale_log2) {
-  constexpr int P = pitch_of<HD>(), NS = HD / 16, ND = HD / 32;
-  __shared__ __attribute__((aligned(16))) bf16_t Kbuf[2][KB * P];
-  __shared__ __attribute__((aligned(16))) bf16_t Vbuf[2][KB * P];
+__global__ void __launch_bounds__(256, HD == 128 ? 1 : 2)
+    attn_dq_mfma(const bf16_t* qkv, const float* L2, const bf16_t* dout, const float* D,
+                 bf16_t* dqkv, int Tn, int H, int left, float scale, float scale_log2) {
+  constexpr int NS = HD / 16, ND = HD / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KB * HD];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][KB * HD];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, c = lane & 31;
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int h = blockIdx.x % H, b = blockIdx.x / H;
   const long C = (long)H * HD, ld = 3 * C;
   const bf16_t* base = qkv + (long)b * Tn * ld;
-  const int qblk0 = blockIdx.x * 128;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, (long)Tn * ld * 2);
+  const int qblk0 = (gridDim.y - 1 - blockIdx.y) * 128;  // longest key ranges first
   const int qw0 = qblk0 + wave * 32;
   const int qi = qw0 + c;
 
@@ -585,106 +590,101 @@ __global__ void __launch_bounds__(256) attn_dq_mfma(const bf16_t* qkv, const flo
     gf[s] = *(bf16x8*)&v;
   }
   const long r0 = ((long)b * H + h) * Tn;
-  const float Lq = qi < Tn ? lse[r0 + qi] * LOG2E : 0.f;
+  const float Lq = qi < Tn ? L2[r0 + qi] : 0.f;
   const float Dq = qi < Tn ? D[r0 + qi] : 0.f;
-  f32x16 dq[ND];
+  f32x16 dq[ND];  // dQ^T: head dim d * 32 + acc_row(r, g), query qi
 #pragma unroll
-  for (int d = 0; d < ND; ++d)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dq[d][r] = 0.f;
+  for (int d = 0; d < ND; ++d) dq[d] = f32x16{};
 
   const int qlast = min(Tn - 1, qblk0 + 127);
-  const int kfirst = left < 0 ? 0 : max(0, qblk0 - left);
-  const int kstart = (kfirst / KB) * KB;
-  TileRegs<HD> rk, rv;
-  tile_load<HD>(base + C + h * HD, ld, kstart, Tn, rk);
-  tile_load<HD>(base + 2 * C + h * HD, ld, kstart, Tn, rv);
-  tile_store<HD>(rk, Kbuf[0]);
-  tile_store<HD>(rv, Vbuf[0]);
-  __syncthreads();
-  int buf = 0;
-  for (int kb0 = kstart; kb0 <= qlast; kb0 += KB, buf ^= 1) {
-    const bf16_t* Ks = Kbuf[buf];
-    const bf16_t* Vs = Vbuf[buf];
-    const bool more = kb0 + KB <= qlast;
-    if (more) {
-      tile_load<HD>(base + C + h * HD, ld, kb0 + KB, Tn, rk);
-      tile_load<HD>(base + 2 * C + h * HD, ld, kb0 + KB, Tn, rv);
-    }
-    const bool skip = kb0 > qw0 + 31 || (left >= 0 && kb0 + KB - 1 < qw0 - left);
-    if (!skip) {
-    const bool full = kb0 + KB - 1 <= qw0 && qw0 + 31 < Tn && (left < 0 || qw0 + 31 - kb0 <= left);
+  const int kstart = left < 0 ? 0 : (max(0, qblk0 - left) / KB) * KB;
+
+  auto step = [&](const bf16_t* Kt, const bf16_t* Vt, int kb0, auto mask) {
+    constexpr bool MASK = decltype(mask)::value;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      f32x16 s, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+      f32x16 s{}, dp{};
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<HD>(Ks, kk * 32, st, lane), qf[st], s,
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<HD>(Kt, kk * 32, st, lane), qf[st], s,
                                                     0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<HD>(Vs, kk * 32, st, lane), gf[st],
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<HD>(Vt, kk * 32, st, lane), gf[st],
                                                      dp, 0, 0, 0);
       }
-      // s[r]: key kb0 + kk*32 + acc_row(r, g), query qi.
+      // s[r], dp[r]: key kb0 + kk * 32 + acc_row(r, g), query qi.
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        int j = kb0 + kk * 32 + acc_row(r, g);
-        float p = (full || (qi < Tn && visible(qi, j, left, Tn))) ? exp2f(s[r] * scale_log2 - Lq)
-                                                                  : 0.f;
+        float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -Lq));
+        if constexpr (MASK) {
+          if (!visible(qi, kb0 + kk * 32 + acc_row(r, g), left, Tn)) p = 0.f;
+        }
         dp[r] = p * (dp[r] - Dq);
       }
-      // dQ[q][d] += dS[q][key] K[key][d]
+      // dQ^T[d][q] += K^T[d][key] dS^T[key][q]
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        bf16x8 da = acc_slots(dp, s2);
+        const bf16x8 da = acc_slots(dp, s2);
 #pragma unroll
         for (int d = 0; d < ND; ++d)
           dq[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              da, tr_slots<HD>(Ks, d * 32, kk * 32 + 16 * s2, lane), dq[d], 0, 0, 0);
+              tr_slots<HD>(Kt, d * 32, kk * 32 + 16 * s2, lane), da, dq[d], 0, 0, 0);
       }
     }
-    }  // !skip
-    if (more) {
-      tile_store<HD>(rk, Kbuf[buf ^ 1]);
-      tile_store<HD>(rv, Vbuf[buf ^ 1]);
+  };
+
+  dma_tile<HD>(rs, ld, C + h * HD, kstart, Tn, Ks[0], wave, lane);
+  dma_tile<HD>(rs, ld, 2 * C + h * HD, kstart, Tn, Vs[0], wave, lane);
+  int buf = 0;
+  for (int kb0 = kstart; kb0 <= qlast; kb0 += KB, buf ^= 1) {
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's share of tile kb0 landed
+    __syncthreads();                     // ... and every other wave's
+    if (kb0 + KB <= qlast) {
+      dma_tile<HD>(rs, ld, C + h * HD, kb0 + KB, Tn, Ks[buf ^ 1], wave, lane);
+      dma_tile<HD>(rs, ld, 2 * C + h * HD, kb0 + KB, Tn, Vs[buf ^ 1], wave, lane);
     }
-    __syncthreads();
+    const bool skip = kb0 > qw0 + 31 || (left >= 0 && kb0 + KB - 1 < qw0 - left);
+    if (skip) continue;
+    const bool full =
+        kb0 + KB - 1 <= qw0 && qw0 + 31 < Tn && (left < 0 || qw0 + 31 - kb0 <= left);
+    if (full) step(Ks[buf], Vs[buf], kb0, Mask<false>{});
+    else step(Ks[buf], Vs[buf], kb0, Mask<true>{});
   }
-  // dq[d][r]: query qw0 + acc_row(r, g), head dim d*32 + c.
+  if (qi < Tn) {
+    bf16_t* row = dqkv + ((long)b * Tn + qi) * ld + h * HD;
 #pragma unroll
-  for (int d = 0; d < ND; ++d)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      int q = qw0 + acc_row(r, g);
-      if (q < Tn) dqkv[((long)b * Tn + q) * ld + h * HD + d * 32 + c] = f2bf(dq[d][r] * scale);
-    }
+    for (int d = 0; d < ND; ++d) store_dims(row, d * 32, dq[d], scale, g);
+  }
 }
+
+// Sequences whose packed qkv rows exceed what a 32-bit buffer offset reaches
+// are rejected (T * 3 * H * hd * 2 bytes < 2 GiB).
+inline bool fits_rsrc(int T, int H, int HD) { return (long)T * 3 * H * HD * 2 < 0x7fffffffL; }
 
 template <int HD>
 hipError_t launch_fwd(int B, int T, int H, int left, const void* qkv, void* out, float* lse,
                       hipStream_t s) {
-  dim3 grid((unsigned)cdiv(T, 128), H, B);
+  if (!fits_rsrc(T, H, HD)) return hipErrorInvalidValue;
+  dim3 grid((unsigned)(B * H), (unsigned)cdiv(T, 128));
   float sl2 = LOG2E / sqrtf((float)HD);
   attn_fwd_mfma<HD><<<grid, 256, 0, s>>>((const bf16_t*)qkv, (bf16_t*)out, lse, T, H, left, sl2);
   return hipGetLastError();
 }
 
 template <int HD>
-hipError_t launch_bwd(int B, int T, int H, int left, const void* qkv, const float* lse,
+hipError_t launch_bwd(int B, int T, int H, int left, const void* qkv, const float* L2,
                       const void* dout, const float* D, void* dqkv, hipStream_t s) {
-  dim3 grid((unsigned)cdiv(T, 128), H, B);
+  if (!fits_rsrc(T, H, HD)) return hipErrorInvalidValue;
+  dim3 grid((unsigned)(B * H), (unsigned)cdiv(T, 128));
   float sc = 1.f / sqrtf((float)HD);
   float sl2 = sc * LOG2E;
-  attn_dkv_mfma<HD><<<grid, 256, 0, s>>>((const bf16_t*)qkv, lse, (const bf16_t*)dout, D,
+  attn_dkv_mfma<HD><<<grid, 256, 0, s>>>((const bf16_t*)qkv, L2, (const bf16_t*)dout, D,
                                          (bf16_t*)dqkv, T, H, left, sc, sl2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  attn_dq_mfma<HD><<<grid, 256, 0, s>>>((const bf16_t*)qkv, lse, (const bf16_t*)dout, D,
+  attn_dq_mfma<HD><<<grid, 256, 0, s>>>((const bf16_t*)qkv, L2, (const bf16_t*)dout, D,
                                         (bf16_t*)dqkv, T, H, left, sc, sl2);
   return hipGetLastError();
 }
-
 }  // namespace
 
 bool attention_supported(int prec, int hd) {
@@ -716,17 +716,20 @@ hipError_t attention_bwd(int prec, int B, int T, int H, int hd, int left, const 
   if (prec == GPT_BF16) {
     const long M = (long)B * T;
     const unsigned g = (unsigned)cdiv(M, 4);
+    const bf16_t* o16 = (const bf16_t*)out;
+    const bf16_t* g16 = (const bf16_t*)dout;
+    float* L2 = dvec + rows;  // second half of the workspace
     if (hd == 32)
-      attn_dvec_bf16<32><<<g, 256, 0, s>>>((const bf16_t*)out, (const bf16_t*)dout, dvec, (int)M, T, H);
+      attn_dvec_bf16<32><<<g, 256, 0, s>>>(o16, g16, lse, dvec, L2, (int)M, T, H);
     else if (hd == 64)
-      attn_dvec_bf16<64><<<g, 256, 0, s>>>((const bf16_t*)out, (const bf16_t*)dout, dvec, (int)M, T, H);
+      attn_dvec_bf16<64><<<g, 256, 0, s>>>(o16, g16, lse, dvec, L2, (int)M, T, H);
     else
-      attn_dvec_bf16<128><<<g, 256, 0, s>>>((const bf16_t*)out, (const bf16_t*)dout, dvec, (int)M, T, H);
+      attn_dvec_bf16<128><<<g, 256, 0, s>>>(o16, g16, lse, dvec, L2, (int)M, T, H);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (hd == 32) return launch_bwd<32>(B, T, H, left, qkv, lse, dout, dvec, dqkv, s);
-    if (hd == 64) return launch_bwd<64>(B, T, H, left, qkv, lse, dout, dvec, dqkv, s);
-    return launch_bwd<128>(B, T, H, left, qkv, lse, dout, dvec, dqkv, s);
+    if (hd == 32) return launch_bwd<32>(B, T, H, left, qkv, L2, dout, dvec, dqkv, s);
+    if (hd == 64) return launch_bwd<64>(B, T, H, left, qkv, L2, dout, dvec, dqkv, s);
+    return launch_bwd<128>(B, T, H, left, qkv, L2, dout, dvec, dqkv, s);
   }
   attn_dvec<float><<<(unsigned)cdiv(rows, 256), 256, 0, s>>>((const float*)out,
                                                              (const float*)dout, dvec, B, T, H, hd);

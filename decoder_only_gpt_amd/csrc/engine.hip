@@ -167,7 +167,7 @@ Arena plan_arena(const gpt_config& c, int B, int T) {
   a.dC2 = take(M * C * act);
   a.dF = take(M * F * act);
   a.dqkv = take(M * 3 * C * act);
-  a.dvec = take(M * H * 4);
+  a.dvec = take(2 * M * H * 4);  // D, then the log-sum-exp in log2 units
   int64_t ws = 0;
   auto ws_need = [&](int64_t m, int64_t n, int64_t k) {
     ws = std::max<int64_t>(ws, gpt::gemm_workspace_bytes((int)m, (int)n, (int)k, c.precision));

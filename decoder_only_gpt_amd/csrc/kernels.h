@@ -21,7 +21,7 @@ hipError_t attention_fwd(int prec, int B, int T, int H, int hd, int left, const 
                          void* out, float* lse, hipStream_t s);
 hipError_t attention_bwd(int prec, int B, int T, int H, int hd, int left, const void* qkv,
                          const void* out, const float* lse, const void* dout, void* dqkv,
-                         float* dvec, hipStream_t s);
+                         float* dvec, hipStream_t s);  // dvec: 2 * B * H * T floats
 bool attention_supported(int prec, int hd);
 
 // Row-wise kernels (rowwise.hip).

@@ -260,7 +260,7 @@ int gpt_op_attention_fwd(int32_t precision, int32_t B, int32_t T, int32_t H, int
                          int32_t left, const void* qkv, void* out, float* lse, void* stream);
 
 /* Gradient of gpt_op_attention_fwd: dout [B*T, H*hd] -> dqkv [B*T, 3*H*hd].
- * `workspace` holds B*H*T floats. */
+ * `workspace` holds 2*B*H*T floats (device, caller-owned; overwritten). */
 int gpt_op_attention_bwd(int32_t precision, int32_t B, int32_t T, int32_t H, int32_t hd,
                          int32_t left, const void* qkv, const void* out, const float* lse,
                          const void* dout, void* dqkv, float* workspace, void* stream);

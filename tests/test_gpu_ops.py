@@ -217,7 +217,7 @@ def test_attention_fwd_bwd(prec, B, T, H, hd, left):
     out = torch.zeros((B * T, C), dtype=dt, device="cuda")
     lse = torch.zeros((B, H, T), dtype=torch.float32, device="cuda")
     dqkv = torch.zeros((B * T, 3 * C), dtype=dt, device="cuda")
-    ws = torch.zeros(B * H * T + 1, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(2 * B * H * T + 1, dtype=torch.float32, device="cuda")
     gpt.op_attention_fwd(prec, B, T, H, hd, left, qkv, out, lse)
     gpt.op_attention_bwd(prec, B, T, H, hd, left, qkv, out, lse, dout, dqkv, ws)
     torch.cuda.synchronize()
