@@ -59,6 +59,51 @@ __device__ __forceinline__ float gelu_grad_f(float u, bool tanh_form) {
          u * 0.3989422804014327f * expf(-0.5f * u * u);
 }
 
+// Fast GELU for the bf16 path, whose results are rounded to 8 significant
+// bits: absolute error ~1e-7 relative to the forms above.
+//  tanh form: 0.5 u (1 + tanh z) = u * sigmoid(2 z), z = sqrt(2/pi) (u + 0.044715 u^3),
+//    with the hardware exp2 and reciprocal;
+//  exact form: erf by Abramowitz & Stegun, Handbook of Mathematical Functions,
+//    formula 7.1.26 (|error| <= 1.5e-7), with erf(-x) = -erf(x).
+__device__ __forceinline__ float sigmoid2z(float u, float& z) {
+  const float s = 0.7978845608028654f, k = 0.044715f;
+  z = s * u * fmaf(k, u * u, 1.f);
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-2.8853900817779268f * z));
+}
+// erf(|x|) and exp(-x^2) for the exact form.
+__device__ __forceinline__ float erf_as(float x, float& ex2) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.f));
+  float poly = fmaf(1.061405429f, t, -1.453152027f);
+  poly = fmaf(poly, t, 1.421413741f);
+  poly = fmaf(poly, t, -0.284496736f);
+  poly = fmaf(poly, t, 0.254829592f);
+  poly *= t;
+  ex2 = __builtin_amdgcn_exp2f(-1.4426950408889634f * ax * ax);
+  const float e = 1.f - poly * ex2;
+  return copysignf(e, x);
+}
+__device__ __forceinline__ float gelu_fast(float u, bool tanh_form) {
+  if (tanh_form) {
+    float z;
+    return u * sigmoid2z(u, z);
+  }
+  float ex2;
+  return 0.5f * u * (1.f + erf_as(u * 0.7071067811865476f, ex2));
+}
+__device__ __forceinline__ float gelu_grad_fast(float u, bool tanh_form) {
+  if (tanh_form) {
+    const float s = 0.7978845608028654f, k = 0.044715f;
+    float z;
+    const float sg = sigmoid2z(u, z);
+    // d/du [u sigmoid(2z)] = sg (1 + 2 u (1 - sg) z'(u)),  z' = s (1 + 3 k u^2)
+    return sg * fmaf(2.f * s * u * (1.f - sg), fmaf(3.f * k, u * u, 1.f), 1.f);
+  }
+  float ex2;
+  const float e = erf_as(u * 0.7071067811865476f, ex2);  // ex2 = exp(-u^2 / 2)
+  return fmaf(0.5f, e, 0.5f) + u * 0.3989422804014327f * ex2;
+}
+
 __device__ __forceinline__ float warp_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -126,7 +126,8 @@ struct Arena {
   int64_t X, ln_mean, ln_rstd;
   std::vector<int64_t> a1, qkv, att, lse, a2, u, g;
   int64_t xf, logits, loss_rows, loss, gres[2], gact, dC, dC2, dF, dqkv, dvec;
-  int64_t gemm_ws, gemm_ws_bytes, cs_part, ln_part, e_counts, e_offsets, e_perm, n_part, norm2;
+  int64_t gemm_ws, gemm_ws_bytes, cs_part, ln_part, n_part, norm2;
+  int64_t e_counts, e_offsets, e_rank, e_perm, e_carry_first, e_carry_last, e_flags, e_last_tok;
   int64_t state_end, total;
 };
 
@@ -183,7 +184,13 @@ Arena plan_arena(const gpt_config& c, int B, int T) {
   a.ln_part = take(gpt::layernorm_bwd_partial_floats((int)M, (int)C) * 4 + 16);
   a.e_counts = take(Vp * 4);
   a.e_offsets = take(Vp * 4);
+  a.e_rank = take(M * 4);
   a.e_perm = take(M * 4);
+  const int64_t nch = gpt::embed_bwd_chunks((int)M);
+  a.e_carry_first = take(nch * C * 4);
+  a.e_carry_last = take(nch * C * 4);
+  a.e_flags = take(nch * 4);
+  a.e_last_tok = take(nch * 4);
   a.n_part = take(1024 * 8);
   a.norm2 = take(16);
   a.total = o;
@@ -472,8 +479,10 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
   }
 #undef BIAS_GRAD
   // x0 = wte[idx] + wpe[t]; with a tied head the lm_head gradient is already in dwte.
-  gpt::EmbedBwdScratch scr{m->at<int32_t>(m->ar.e_counts), m->at<int32_t>(m->ar.e_offsets),
-                           m->at<int32_t>(m->ar.e_perm)};
+  gpt::EmbedBwdScratch scr{m->at<int32_t>(m->ar.e_counts),   m->at<int32_t>(m->ar.e_offsets),
+                           m->at<int32_t>(m->ar.e_rank),     m->at<int32_t>(m->ar.e_perm),
+                           m->at<float>(m->ar.e_carry_first), m->at<float>(m->ar.e_carry_last),
+                           m->at<int32_t>(m->ar.e_flags),    m->at<int32_t>(m->ar.e_last_tok)};
   const int wte_acc = (c.tied_lm_head || acc) ? 1 : 0;
   LAUNCH(GPT_K_EMBED, GPT_S_EMBED_BWD, 0, 4.0 * M * C + 4.0 * (m->Vp + c.block_size) * C,
          gpt::embed_bwd(m->last_idx, gres[cur], (int)M, m->T, (int)C, (int)m->Vp, c.block_size,

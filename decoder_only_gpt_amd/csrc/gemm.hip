@@ -141,8 +141,9 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
   return row * BK + ((chunk ^ (row & 7) ^ ((row >> 3) & 1)) << 3);
 }
 
+// GELU of a packed bf16 pair (bf16 path only: fast form).
 __device__ __forceinline__ uint32_t gelu2(uint32_t w, int tanh_form) {
-  return pack_bf2(gelu_f(bf_lo(w), tanh_form), gelu_f(bf_hi(w), tanh_form));
+  return pack_bf2(gelu_fast(bf_lo(w), tanh_form), gelu_fast(bf_hi(w), tanh_form));
 }
 
 // Global -> registers for one BK-slice of a 128-row operand tile: 4 vectors
@@ -255,8 +256,8 @@ __device__ __forceinline__ void epilogue8(const EpiArgs& e, float* partial, int 
     const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      x[2 * i] *= gelu_grad_f(bf_lo(uw[i]), e.tanh_form);
-      x[2 * i + 1] *= gelu_grad_f(bf_hi(uw[i]), e.tanh_form);
+      x[2 * i] *= gelu_grad_fast(bf_lo(uw[i]), e.tanh_form);
+      x[2 * i + 1] *= gelu_grad_fast(bf_hi(uw[i]), e.tanh_form);
     }
     *(u32x4*)((bf16_t*)e.out + o) = u32x4{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]),
                                            pack_bf2(x[4], x[5]), pack_bf2(x[6], x[7])};
@@ -641,10 +642,10 @@ __device__ __forceinline__ void epilogue4(const EpiArgs& e, float* partial, int 
     }
   } else if constexpr (EPI == GPT_EPI_DGELU) {
     const uint2 u = *(const uint2*)((const bf16_t*)e.aux + (long)m * e.ldaux + n);
-    v.x *= gelu_grad_f(bf_lo(u.x), e.tanh_form);
-    v.y *= gelu_grad_f(bf_hi(u.x), e.tanh_form);
-    v.z *= gelu_grad_f(bf_lo(u.y), e.tanh_form);
-    v.w *= gelu_grad_f(bf_hi(u.y), e.tanh_form);
+    v.x *= gelu_grad_fast(bf_lo(u.x), e.tanh_form);
+    v.y *= gelu_grad_fast(bf_hi(u.x), e.tanh_form);
+    v.z *= gelu_grad_fast(bf_lo(u.y), e.tanh_form);
+    v.w *= gelu_grad_fast(bf_hi(u.y), e.tanh_form);
     *(uint2*)((bf16_t*)e.out + o) = make_uint2(pack_bf2(v.x, v.y), pack_bf2(v.z, v.w));
   } else if constexpr (EPI == GPT_EPI_RESIDUAL) {
     const float4 r = *(const float4*)(e.resid + o);

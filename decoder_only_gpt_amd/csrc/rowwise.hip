@@ -41,68 +41,141 @@ __global__ void embed_count_kernel(const int32_t* idx, int M, int32_t* counts) {
   if (i < M) atomicAdd(&counts[idx[i]], 1);  // integer: exact in any order
 }
 
-// Exclusive scan of counts[n] -> offsets[n] (one workgroup, fixed order).
+// Exclusive scan of counts[n] -> offsets[n] (one workgroup): each thread sums
+// a contiguous run, the run totals are scanned with wave shuffles, then each
+// thread writes its run's offsets.
 __global__ void __launch_bounds__(1024) scan_kernel(const int32_t* counts, int n,
                                                     int32_t* offsets) {
-  __shared__ int32_t part[1024];
-  const int t = threadIdx.x;
+  __shared__ int32_t wsum[16];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int per = (n + 1023) / 1024;
   const int b = t * per, e = min(n, b + per);
   int s = 0;
   for (int i = b; i < e; ++i) s += counts[i];
-  part[t] = s;
-  __syncthreads();
-  if (t == 0) {
-    int acc = 0;
-    for (int i = 0; i < 1024; ++i) {
-      int v = part[i];
-      part[i] = acc;
-      acc += v;
-    }
+  int x = s;  // inclusive scan within the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
   }
+  if (lane == 63) wsum[wave] = x;
   __syncthreads();
-  int acc = part[t];
+  int acc = x - s;
+  for (int w = 0; w < wave; ++w) acc += wsum[w];
   for (int i = b; i < e; ++i) {
     offsets[i] = acc;
     acc += counts[i];
   }
 }
 
-// perm[offsets[idx[p]] + rank] = p, rank = #{p' < p : idx[p'] == idx[p]}:
-// positions grouped by token, increasing within a token.
-__global__ void __launch_bounds__(256) embed_rank_kernel(const int32_t* idx, int M,
-                                                         const int32_t* offsets, int32_t* perm) {
+// rank[p] += #{p' < p in block y : idx[p'] == idx[p]} for p in block x (256
+// positions per block, y <= x).  Integer atomics: exact in any order.
+__global__ void __launch_bounds__(256) embed_rank_kernel(const int32_t* __restrict__ idx, int M,
+                                                         int32_t* __restrict__ rank) {
+  const int bx = blockIdx.x, by = blockIdx.y;
+  if (by > bx) return;
   __shared__ int32_t tile[256];
-  const int p = blockIdx.x * 256 + threadIdx.x;
-  const int mine = p < M ? idx[p] : -1;
-  int rank = 0;
-  for (int t0 = 0; t0 <= blockIdx.x * 256; t0 += 256) {
-    __syncthreads();
-    tile[threadIdx.x] = (t0 + (int)threadIdx.x < M) ? idx[t0 + threadIdx.x] : -2;
-    __syncthreads();
-    int lim = min(256, p - t0);
-    for (int k = 0; k < lim; ++k) rank += (tile[k] == mine);
-  }
-  if (p < M) perm[offsets[mine] + rank] = p;
+  const int q = by * 256 + threadIdx.x;
+  tile[threadIdx.x] = q < M ? idx[q] : -1;
+  __syncthreads();
+  const int p = bx * 256 + threadIdx.x;
+  if (p >= M) return;
+  const int mine = idx[p];
+  const int lim = by < bx ? 256 : (int)threadIdx.x;
+  int r = 0;
+  for (int k = 0; k < lim; ++k) r += tile[k] == mine;
+  if (r) atomicAdd(&rank[p], r);
 }
 
-// dwte[v, c] (+)= sum over positions of token v, in position order.
-__global__ void __launch_bounds__(256) embed_wte_kernel(const float* dx, int C, const int32_t* counts,
-                                                        const int32_t* offsets, const int32_t* perm,
-                                                        float* dwte, int accumulate) {
-  const int v = blockIdx.x;
-  const int c = blockIdx.y * 256 + threadIdx.x;
-  if (c >= C) return;
-  const int n = counts[v];
-  float* out = dwte + (long)v * C + c;
-  if (n == 0) {
-    if (!accumulate) *out = 0.f;
-    return;
+// perm[offsets[idx[p]] + rank[p]] = p: positions grouped by token, increasing
+// within a token (a stable counting sort).
+__global__ void embed_place_kernel(const int32_t* idx, int M, const int32_t* offsets,
+                                   const int32_t* rank, int32_t* perm) {
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p < M) perm[offsets[idx[p]] + rank[p]] = p;
+}
+
+// dwte rows from the sorted positions: workgroup ch sums its EB_CHUNK sorted
+// entries segment by segment (a segment = the positions of one token), in
+// position order.  A segment wholly inside the chunk is added to dwte; the
+// fragment of a segment that began in an earlier chunk goes to carry_first[ch]
+// (flag EB_SPAN when it also continues past the chunk), the fragment of one
+// that began here and continues goes to carry_last[ch] (flag EB_LAST).
+constexpr int EB_CHUNK = 64;
+constexpr int EB_LAST = 1, EB_SPAN = 2;
+
+__global__ void __launch_bounds__(256) embed_chunk_kernel(
+    const float* __restrict__ dx, int M, int C, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ perm, float* __restrict__ dwte, float* __restrict__ carry_first,
+    float* __restrict__ carry_last, int32_t* __restrict__ flags, int32_t* __restrict__ last_tok) {
+  __shared__ int32_t pos[EB_CHUNK], tok[EB_CHUNK];
+  __shared__ int32_t nb[2];  // tokens of the entries just before and after the chunk
+  const int ch = blockIdx.x;
+  const int i0 = ch * EB_CHUNK, n = min(M - i0, EB_CHUNK);
+  if (threadIdx.x < n) {
+    const int pp = perm[i0 + threadIdx.x];
+    pos[threadIdx.x] = pp;
+    tok[threadIdx.x] = idx[pp];
   }
-  const int o = offsets[v];
-  float s = 0.f;
-  for (int i = 0; i < n; ++i) s += dx[(long)perm[o + i] * C + c];
-  *out = accumulate ? *out + s : s;
+  if (threadIdx.x == 64) nb[0] = i0 > 0 ? idx[perm[i0 - 1]] : -1;
+  if (threadIdx.x == 65) nb[1] = i0 + n < M ? idx[perm[i0 + n]] : -1;
+  __syncthreads();
+  const bool first_cont = nb[0] == tok[0];     // first segment began in an earlier chunk
+  const bool last_cont = nb[1] == tok[n - 1];  // last segment continues past the chunk
+  if (threadIdx.x == 0) {
+    flags[ch] = (last_cont && !(first_cont && tok[0] == tok[n - 1]) ? EB_LAST : 0) |
+                (first_cont && last_cont && tok[0] == tok[n - 1] ? EB_SPAN : 0);
+    last_tok[ch] = tok[n - 1];
+  }
+  const int C4 = C / 4;
+  for (int c = threadIdx.x; c < C4; c += 256) {
+    float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 0; i < n; ++i) {
+      const float4 v = ((const float4*)(dx + (long)pos[i] * C))[c];
+      run.x += v.x; run.y += v.y; run.z += v.z; run.w += v.w;
+      if (i + 1 < n && tok[i + 1] == tok[i]) continue;  // segment goes on
+      if (first_cont && tok[i] == tok[0]) {
+        ((float4*)(carry_first + (long)ch * C))[c] = run;
+      } else if (i + 1 == n && last_cont) {
+        ((float4*)(carry_last + (long)ch * C))[c] = run;
+      } else {
+        float4* o = (float4*)(dwte + (long)tok[i] * C) + c;
+        const float4 a = *o;
+        *o = make_float4(a.x + run.x, a.y + run.y, a.z + run.z, a.w + run.w);
+      }
+      run = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+}
+
+// Segments that cross chunk boundaries: the chunk where one begins (EB_LAST)
+// adds its fragment, then the fragments of the following chunks in order.
+__global__ void __launch_bounds__(256) embed_carry_kernel(int C, int nch,
+                                                          const float* __restrict__ carry_first,
+                                                          const float* __restrict__ carry_last,
+                                                          const int32_t* __restrict__ flags,
+                                                          const int32_t* __restrict__ last_tok,
+                                                          float* __restrict__ dwte) {
+  const int ch = blockIdx.x;
+  if (!(flags[ch] & EB_LAST)) return;
+  const int v = last_tok[ch];
+  const int C4 = C / 4;
+  for (int c = threadIdx.x; c < C4; c += 256) {
+    float4 s = ((const float4*)(carry_last + (long)ch * C))[c];
+    for (int k = ch + 1; k < nch; ++k) {
+      const float4 f = ((const float4*)(carry_first + (long)k * C))[c];
+      s.x += f.x; s.y += f.y; s.z += f.z; s.w += f.w;
+      if (!(flags[k] & EB_SPAN)) break;
+    }
+    float4* o = (float4*)(dwte + (long)v * C) + c;
+    const float4 a = *o;
+    *o = make_float4(a.x + s.x, a.y + s.y, a.z + s.z, a.w + s.w);
+  }
+}
+
+__global__ void fill_f32(float* p, long n) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0.f;
 }
 
 // dwpe[t, c] (+)= sum_b dx[b*T + t, c]; rows t >= T untouched (accumulate) or zeroed.
@@ -342,10 +415,12 @@ __global__ void __launch_bounds__(256) colsum_kernel(const ActT* x, int M, int N
 
 // ------------------------------------------------------------------ cross-entropy
 // One workgroup per row; the whole row lives in registers, so the logits are
-// read once and the gradient written once.  loss = lse_{v<V} z - z[tgt];
+// read once and the gradient written once (fp32: the generic kernel, bf16:
+// ce_bf16_kernel).  loss = lse_{v<V} z - z[tgt];
 // z is overwritten by (softmax - onehot) / M on [0, V) and 0 on [V, ldz).
 constexpr int CE_THREADS = 1024;
 constexpr int CE_NV = 8;
+constexpr float LOG2E_F = 1.4426950408889634f;
 
 template <typename ActT>
 __global__ void __launch_bounds__(CE_THREADS) ce_kernel(ActT* z, int M, int V, int ldz,
@@ -422,6 +497,99 @@ __global__ void __launch_bounds__(CE_THREADS) ce_kernel(ActT* z, int M, int V, i
   }
 }
 
+// bf16 rows: the logits stay in registers as packed bf16 (4 VGPRs per 8
+// values, so two rows fit per CU), each thread reduces its values to a
+// (max, sum of exp) pair and one block reduction combines the pairs in a fixed
+// order.  exp(x - m) is evaluated as exp2(x log2 e - m log2 e).
+__device__ __forceinline__ void lse_combine(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  const float a = m == -INFINITY ? 0.f : s * __builtin_amdgcn_exp2f((m - mn) * LOG2E_F);
+  const float b = m2 == -INFINITY ? 0.f : s2 * __builtin_amdgcn_exp2f((m2 - mn) * LOG2E_F);
+  m = mn;
+  s = a + b;
+}
+
+__global__ void __launch_bounds__(CE_THREADS, 8) ce_bf16_kernel(bf16_t* z, int V, int ldz,
+                                                             const int32_t* tgt,
+                                                             float* loss_rows, float inv_count) {
+  __shared__ float red_m[CE_THREADS / 64], red_s[CE_THREADS / 64];
+  const int row = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  bf16_t* zr = z + (long)row * ldz;
+  const int target = tgt[row];
+  const int nvec = ldz / 8;
+  u32x4 raw[CE_NV];
+#pragma unroll
+  for (int i = 0; i < CE_NV; ++i) {
+    const int vix = t + i * CE_THREADS;
+    raw[i] = vix < nvec ? *(const u32x4*)(zr + (long)vix * 8) : u32x4{0u, 0u, 0u, 0u};
+  }
+  float zt = 0.f;
+  if (t == 0) zt = bf2f(zr[target]);
+  // running (max, sum) over this thread's vectors, one vector at a time, so
+  // only the packed row stays live
+  // (columns at or past V, the vocabulary padding, count as -inf)
+  float mx = -INFINITY, sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < CE_NV; ++i) {
+    const int lim = V - (t + i * CE_THREADS) * 8;  // valid values in this vector
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float v = (k & 1) ? bf_hi(raw[i][k >> 1]) : bf_lo(raw[i][k >> 1]);
+      x[k] = k < lim ? v : -INFINITY;
+    }
+    float vm = x[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) vm = fmaxf(vm, x[k]);
+    lse_combine(mx, sum, vm, 0.f);
+    if (mx != -INFINITY) {
+      const float ml = mx * LOG2E_F;
+      float vs = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) vs += __builtin_amdgcn_exp2f(fmaf(x[k], LOG2E_F, -ml));
+      sum += vs;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(mx, o, 64), s2 = __shfl_xor(sum, o, 64);
+    lse_combine(mx, sum, m2, s2);
+  }
+  if (lane == 0) {
+    red_m[wave] = mx;
+    red_s[wave] = sum;
+  }
+  __syncthreads();
+  mx = red_m[0];
+  sum = red_s[0];
+  for (int w = 1; w < CE_THREADS / 64; ++w) lse_combine(mx, sum, red_m[w], red_s[w]);
+  if (t == 0) loss_rows[row] = (mx + logf(sum)) - zt;
+  const float inv_s = 1.f / sum, ml = mx * LOG2E_F;
+  // Unpack again below instead of keeping 8 floats per vector alive across
+  // the reduction (the empty asm hides that raw is unchanged).
+#pragma unroll
+  for (int i = 0; i < CE_NV; ++i) asm volatile("" : "+v"(raw[i]));
+  int t2 = t;  // likewise the store addresses are recomputed
+  asm volatile("" : "+v"(t2));
+#pragma unroll
+  for (int i = 0; i < CE_NV; ++i) {
+    const int vix = t2 + i * CE_THREADS;
+    if (vix < nvec) {
+      float d[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int col = vix * 8 + k;
+        const float x = (k & 1) ? bf_hi(raw[i][k >> 1]) : bf_lo(raw[i][k >> 1]);
+        const float p = __builtin_amdgcn_exp2f(fmaf(x, LOG2E_F, -ml)) * inv_s;
+        d[k] = col < V ? (p - (col == target ? 1.f : 0.f)) * inv_count : 0.f;
+      }
+      *(u32x4*)(zr + (long)vix * 8) = u32x4{pack_bf2(d[0], d[1]), pack_bf2(d[2], d[3]),
+                                            pack_bf2(d[4], d[5]), pack_bf2(d[6], d[7])};
+    }
+  }
+}
+
 __global__ void __launch_bounds__(1024) mean_kernel(const float* x, int n, float* out) {
   __shared__ double red[1024];
   double s = 0.0;
@@ -492,17 +660,27 @@ hipError_t embed_fwd(int prec, const int32_t* idx, const float* wte, const float
   return hipGetLastError();
 }
 
+int embed_bwd_chunks(int M) { return (int)cdiv(M, EB_CHUNK); }
+
 hipError_t embed_bwd(const int32_t* idx, const float* dx, int M, int T, int C, int Vp, int Tb,
                      float* dwte, int wte_accumulate, float* dwpe, int wpe_accumulate,
                      EmbedBwdScratch scr, hipStream_t s) {
-  fill_i32<<<(unsigned)cdiv(Vp, 256), 256, 0, s>>>(scr.counts, Vp, 0);
-  if (M > 0) embed_count_kernel<<<(unsigned)cdiv(M, 256), 256, 0, s>>>(idx, M, scr.counts);
-  scan_kernel<<<1, 1024, 0, s>>>(scr.counts, Vp, scr.offsets);
-  if (M > 0)
-    embed_rank_kernel<<<(unsigned)cdiv(M, 256), 256, 0, s>>>(idx, M, scr.offsets, scr.perm);
-  dim3 g((unsigned)Vp, (unsigned)cdiv(C, 256));
-  embed_wte_kernel<<<g, 256, 0, s>>>(dx, C, scr.counts, scr.offsets, scr.perm, dwte,
-                                     wte_accumulate);
+  if (!wte_accumulate)
+    fill_f32<<<(unsigned)cdiv((long)Vp * C, 256), 256, 0, s>>>(dwte, (long)Vp * C);
+  if (M > 0) {
+    const int nb = (int)cdiv(M, 256), nch = embed_bwd_chunks(M);
+    fill_i32<<<(unsigned)cdiv(Vp, 256), 256, 0, s>>>(scr.counts, Vp, 0);
+    fill_i32<<<(unsigned)nb, 256, 0, s>>>(scr.rank, M, 0);
+    embed_count_kernel<<<(unsigned)nb, 256, 0, s>>>(idx, M, scr.counts);
+    scan_kernel<<<1, 1024, 0, s>>>(scr.counts, Vp, scr.offsets);
+    embed_rank_kernel<<<dim3((unsigned)nb, (unsigned)nb), 256, 0, s>>>(idx, M, scr.rank);
+    embed_place_kernel<<<(unsigned)nb, 256, 0, s>>>(idx, M, scr.offsets, scr.rank, scr.perm);
+    embed_chunk_kernel<<<(unsigned)nch, 256, 0, s>>>(dx, M, C, idx, scr.perm, dwte,
+                                                     scr.carry_first, scr.carry_last, scr.flags,
+                                                     scr.last_tok);
+    embed_carry_kernel<<<(unsigned)nch, 256, 0, s>>>(C, nch, scr.carry_first, scr.carry_last,
+                                                     scr.flags, scr.last_tok, dwte);
+  }
   embed_wpe_kernel<<<(unsigned)cdiv((long)Tb * C, 256), 256, 0, s>>>(dx, M, T, C, Tb, dwpe,
                                                                      wpe_accumulate);
   return hipGetLastError();
@@ -594,7 +772,7 @@ hipError_t cross_entropy(int prec, void* logits, int M, int V, int ldz, const in
   if (!cross_entropy_supported(prec, ldz) || V > ldz) return hipErrorInvalidValue;
   float inv = 1.f / (float)M;
   if (prec == GPT_BF16)
-    ce_kernel<bf16_t><<<M, CE_THREADS, 0, s>>>((bf16_t*)logits, M, V, ldz, tgt, loss_rows, inv);
+    ce_bf16_kernel<<<M, CE_THREADS, 0, s>>>((bf16_t*)logits, V, ldz, tgt, loss_rows, inv);
   else
     ce_kernel<float><<<M, CE_THREADS, 0, s>>>((float*)logits, M, V, ldz, tgt, loss_rows, inv);
   return hipGetLastError();

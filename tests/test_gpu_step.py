@@ -129,6 +129,18 @@ def test_step_ragged_batch(prec):
 
 
 @pytest.mark.parametrize("prec", ["fp32", "bf16"])
+@pytest.mark.parametrize("tied", [1, 0])
+def test_step_hot_tokens(prec, tied):
+    """A very skewed token mix: the most frequent ids fill several 64-entry chunks
+    of the sorted positions, so the embedding gradient goes through the
+    cross-chunk carries (and rows of tokens never drawn stay exact)."""
+    cfg = dict(presets.preset("tiny", B=16, T=32, zipf_s=2.5, tied=tied), precision=prec)
+    idx, _ = synth.tokens(cfg, seed=7)
+    assert np.bincount(idx.reshape(-1)).max() > 3 * 64  # at least one token spans whole chunks
+    check_step(cfg, f"tiny_hot_tied{tied}", seed=6)
+
+
+@pytest.mark.parametrize("prec", ["fp32", "bf16"])
 def test_step_is_bitwise_deterministic(prec):
     cfg = dict(gpu_cfgs()["gpt2_s"], precision=prec)
     p = synth.init_params(cfg, seed=2, perturb=True)
