@@ -34,31 +34,58 @@ __device__ __forceinline__ void adam_one(float& p, float& m, float& v, float g,
   p = p - s.step_size * __fdiv_rn(m, d);
 }
 
+// Each thread takes two float4 groups per sweep (all eight loads in flight
+// before any arithmetic); the arrays are streamed once, so the stores are
+// marked non-temporal.
+__device__ __forceinline__ void adam4(float4& pp, float4& mm, float4& vv, const float4& gg,
+                                      const AdamScalars& s) {
+  adam_one(pp.x, mm.x, vv.x, gg.x, s);
+  adam_one(pp.y, mm.y, vv.y, gg.y, s);
+  adam_one(pp.z, mm.z, vv.z, gg.z, s);
+  adam_one(pp.w, mm.w, vv.w, gg.w, s);
+}
+__device__ __forceinline__ void store4_nt(float* q, const float4& v) {
+  __builtin_nontemporal_store(v.x, q);
+  __builtin_nontemporal_store(v.y, q + 1);
+  __builtin_nontemporal_store(v.z, q + 2);
+  __builtin_nontemporal_store(v.w, q + 3);
+}
+
 __global__ void __launch_bounds__(256) adamw_kernel(int64_t n, float* __restrict__ p,
                                                     float* __restrict__ m, float* __restrict__ v,
                                                     const float* __restrict__ g,
                                                     bf16_t* __restrict__ shadow, AdamScalars s) {
-  const int64_t stride = (int64_t)gridDim.x * 256 * 4;
+  const int64_t half = (int64_t)gridDim.x * 256 * 4;  // elements covered by one float4 per thread
+  const int64_t stride = 2 * half;
   for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n; i += stride) {
-    if (i + 3 < n) {
-      float4 pp = *(float4*)(p + i), mm = *(float4*)(m + i), vv = *(float4*)(v + i);
-      float4 gg = *(const float4*)(g + i);
-      adam_one(pp.x, mm.x, vv.x, gg.x, s);
-      adam_one(pp.y, mm.y, vv.y, gg.y, s);
-      adam_one(pp.z, mm.z, vv.z, gg.z, s);
-      adam_one(pp.w, mm.w, vv.w, gg.w, s);
-      *(float4*)(p + i) = pp;
-      *(float4*)(m + i) = mm;
-      *(float4*)(v + i) = vv;
-      if (shadow) *(uint2*)(shadow + i) = make_uint2(pack_bf2(pp.x, pp.y), pack_bf2(pp.z, pp.w));
+    const int64_t i2 = i + half;
+    if (i2 + 3 < n) {
+      float4 p0 = *(float4*)(p + i), m0 = *(float4*)(m + i), v0 = *(float4*)(v + i);
+      float4 g0 = *(const float4*)(g + i);
+      float4 p1 = *(float4*)(p + i2), m1 = *(float4*)(m + i2), v1 = *(float4*)(v + i2);
+      float4 g1 = *(const float4*)(g + i2);
+      adam4(p0, m0, v0, g0, s);
+      adam4(p1, m1, v1, g1, s);
+      store4_nt(p + i, p0);
+      store4_nt(m + i, m0);
+      store4_nt(v + i, v0);
+      store4_nt(p + i2, p1);
+      store4_nt(m + i2, m1);
+      store4_nt(v + i2, v1);
+      if (shadow) {
+        *(uint2*)(shadow + i) = make_uint2(pack_bf2(p0.x, p0.y), pack_bf2(p0.z, p0.w));
+        *(uint2*)(shadow + i2) = make_uint2(pack_bf2(p1.x, p1.y), pack_bf2(p1.z, p1.w));
+      }
     } else {
-      for (int64_t j = i; j < n; ++j) {
-        float pj = p[j], mj = m[j], vj = v[j];
-        adam_one(pj, mj, vj, g[j], s);
-        p[j] = pj;
-        m[j] = mj;
-        v[j] = vj;
-        if (shadow) shadow[j] = f2bf(pj);
+      for (int64_t base : {i, i2}) {
+        for (int64_t j = base; j < min(n, base + 4); ++j) {
+          float pj = p[j], mj = m[j], vj = v[j];
+          adam_one(pj, mj, vj, g[j], s);
+          p[j] = pj;
+          m[j] = mj;
+          v[j] = vj;
+          if (shadow) shadow[j] = f2bf(pj);
+        }
       }
     }
   }
@@ -69,7 +96,7 @@ __global__ void __launch_bounds__(256) adamw_kernel(int64_t n, float* __restrict
 hipError_t adamw(int64_t n, float* p, float* m, float* v, const float* g, uint16_t* shadow,
                  AdamScalars sc, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  int64_t blocks = cdiv(cdiv(n, 4), 256);
+  int64_t blocks = cdiv(cdiv(n, 8), 256);
   if (blocks > 8192) blocks = 8192;
   adamw_kernel<<<(unsigned)blocks, 256, 0, s>>>(n, p, m, v, g, shadow, sc);
   return hipGetLastError();

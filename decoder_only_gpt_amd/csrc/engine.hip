@@ -127,7 +127,8 @@ struct Arena {
   std::vector<int64_t> a1, qkv, att, lse, a2, u, g;
   int64_t xf, logits, loss_rows, loss, gres[2], gact, dC, dC2, dF, dqkv, dvec;
   int64_t gemm_ws, gemm_ws_bytes, cs_part, ln_part, n_part, norm2;
-  int64_t e_counts, e_offsets, e_rank, e_perm, e_carry_first, e_carry_last, e_flags, e_last_tok;
+  int64_t e_counts, e_offsets, e_tile_sums, e_rank, e_perm, e_carry_first, e_carry_last, e_flags,
+      e_last_tok;
   int64_t state_end, total;
 };
 
@@ -184,6 +185,7 @@ Arena plan_arena(const gpt_config& c, int B, int T) {
   a.ln_part = take(gpt::layernorm_bwd_partial_floats((int)M, (int)C) * 4 + 16);
   a.e_counts = take(Vp * 4);
   a.e_offsets = take(Vp * 4);
+  a.e_tile_sums = take((Vp / 1024 + 1) * 4);
   a.e_rank = take(M * 4);
   a.e_perm = take(M * 4);
   const int64_t nch = gpt::embed_bwd_chunks((int)M);
@@ -480,7 +482,8 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
 #undef BIAS_GRAD
   // x0 = wte[idx] + wpe[t]; with a tied head the lm_head gradient is already in dwte.
   gpt::EmbedBwdScratch scr{m->at<int32_t>(m->ar.e_counts),   m->at<int32_t>(m->ar.e_offsets),
-                           m->at<int32_t>(m->ar.e_rank),     m->at<int32_t>(m->ar.e_perm),
+                           m->at<int32_t>(m->ar.e_tile_sums), m->at<int32_t>(m->ar.e_rank),
+                           m->at<int32_t>(m->ar.e_perm),
                            m->at<float>(m->ar.e_carry_first), m->at<float>(m->ar.e_carry_last),
                            m->at<int32_t>(m->ar.e_flags),    m->at<int32_t>(m->ar.e_last_tok)};
   const int wte_acc = (c.tied_lm_head || acc) ? 1 : 0;

@@ -227,7 +227,7 @@ __device__ __forceinline__ void epilogue8(const EpiArgs& e, float* partial, int 
   const long o = (long)m * e.ldo + n;
   float x[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
   if constexpr (EPI == EPI_PARTIAL) {
-    float* p = partial + ((long)blockIdx.z * e.M + m) * e.N + n;
+    float* p = partial + (long)m * e.N + n;  // this split's partial tile
     *(float4*)p = v0;
     *(float4*)(p + 4) = v1;
     return;
@@ -287,6 +287,7 @@ __global__ void __launch_bounds__(256, 2) gemm_mfma_kernel(OpArgs A, OpArgs B, i
   const int wm = wave >> 1, wn = wave & 1;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int kbeg = blockIdx.z * kchunk;
+  if (EPI == EPI_PARTIAL) partial += (long)blockIdx.z * e.M * e.N;
   const int kend = min(K, kbeg + kchunk);
   const int nk = (kend - kbeg + BK - 1) / BK;
   // Stage s: A tile at smem + s * 32 KB, B tile 16 KB after it.
@@ -402,16 +403,27 @@ MfmaKernel mfma_kernel_for(int at, int bt, int epi, int ga, int gb) {
   return nullptr;
 }
 
-// Workgroups are dealt round-robin over the 8 XCDs (each with its own L2):
-// renumber them so every XCD walks a contiguous, row-major run of tiles and
-// the tiles sharing an A panel (and reusing B) meet in the same L2.
-__device__ __forceinline__ void xcd_tile(int& tx, int& ty) {
-  const int nx = gridDim.x, total = gridDim.x * gridDim.y;
-  const int L = blockIdx.x + nx * blockIdx.y;
-  int L2 = L;
-  if ((total & 7) == 0) L2 = (L & 7) * (total >> 3) + (L >> 3);
-  tx = L2 % nx;
-  ty = L2 / nx;
+// Workgroups are dealt round-robin over the 8 XCDs (each with its own 4 MB
+// L2).  Renumber them so every XCD owns a contiguous run of tile ids (all the
+// tiles of a K split stay on one XCD), and order each split's tiles in groups
+// of TILE_GROUP tile-rows walked column by column: the workgroups resident on
+// an XCD at one time then share a few A row panels and B column panels, so
+// each K slice of an operand is fetched into the L2 once and read there by
+// every tile that needs it.
+constexpr int TILE_GROUP = 8;
+__device__ __forceinline__ void xcd_tile(int& tx, int& ty, int& tz) {
+  const int nx = gridDim.x, ny = gridDim.y;
+  const int per_z = nx * ny, total = per_z * gridDim.z;
+  const int L = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+  int id = L;
+  if ((total & 7) == 0) id = (L & 7) * (total >> 3) + (L >> 3);
+  tz = id / per_z;
+  const int r = id - tz * per_z;
+  const int g = r / (TILE_GROUP * nx);
+  const int rows = min(TILE_GROUP, ny - g * TILE_GROUP);
+  const int w = r - g * TILE_GROUP * nx;
+  tx = w / rows;
+  ty = g * TILE_GROUP + w % rows;
 }
 
 // ----------------------------------------------------------------------------
@@ -465,10 +477,11 @@ __global__ void __launch_bounds__(256, 2) gemm_dma_kernel(OpArgs A, OpArgs B, in
   __shared__ __attribute__((aligned(16))) bf16_t sB1[BN * BK];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  int tx, ty;
-  xcd_tile(tx, ty);
+  int tx, ty, tz;
+  xcd_tile(tx, ty, tz);
   const int m0 = ty * BM, n0 = tx * BN;
-  const int kbeg = blockIdx.z * kchunk;
+  const int kbeg = tz * kchunk;
+  if (EPI == EPI_PARTIAL) partial += (long)tz * e.M * e.N;
   const int kend = min(K, kbeg + kchunk);
   const int nk = (kend - kbeg + BK - 1) / BK;
 
@@ -623,7 +636,7 @@ template <int EPI>
 __device__ __forceinline__ void epilogue4(const EpiArgs& e, float* partial, int m, int n, float4 v) {
   const long o = (long)m * e.ldo + n;
   if constexpr (EPI == EPI_PARTIAL) {
-    *(float4*)(partial + ((long)blockIdx.z * e.M + m) * e.N + n) = v;
+    *(float4*)(partial + (long)m * e.N + n) = v;
     return;
   }
   if constexpr (EPI == GPT_EPI_STORE || EPI == GPT_EPI_RESIDUAL || EPI == GPT_EPI_GELU) {
@@ -669,10 +682,11 @@ __global__ void __launch_bounds__(256, 1) gemm_big_kernel(OpArgs A, OpArgs B, in
   __shared__ __attribute__((aligned(16))) bf16_t sB1[BIG * BK];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  int tx, ty;
-  xcd_tile(tx, ty);
+  int tx, ty, tz;
+  xcd_tile(tx, ty, tz);
   const int m0 = ty * BIG, n0 = tx * BIG;
-  const int kbeg = blockIdx.z * kchunk;
+  const int kbeg = tz * kchunk;
+  if (EPI == EPI_PARTIAL) partial += (long)tz * e.M * e.N;
   const int kend = min(K, kbeg + kchunk);
   const int nk = (kend - kbeg + BK - 1) / BK;
 

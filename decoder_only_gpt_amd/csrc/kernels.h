@@ -29,10 +29,11 @@ hipError_t embed_fwd(int prec, const int32_t* idx, const float* wte, const float
                      int C, float* x, hipStream_t s);
 // Deterministic embedding backward: dwte[v] (+)= sum of dx rows whose token is v,
 // in increasing position order; dwpe[t] (+)= sum_b dx[b*T+t].
-// Scratch of embed_bwd: counts/offsets [Vp], rank/perm [M], carry_first /
-// carry_last [embed_bwd_chunks(M)][C] floats, flags/last_tok [chunks].
+// Scratch of embed_bwd: counts/offsets [Vp], tile_sums [Vp / 1024 + 1],
+// rank/perm [M], carry_first / carry_last [embed_bwd_chunks(M)][C] floats,
+// flags/last_tok [chunks].
 struct EmbedBwdScratch {
-  int32_t* counts; int32_t* offsets; int32_t* rank; int32_t* perm;
+  int32_t* counts; int32_t* offsets; int32_t* tile_sums; int32_t* rank; int32_t* perm;
   float* carry_first; float* carry_last; int32_t* flags; int32_t* last_tok;
 };
 int embed_bwd_chunks(int M);

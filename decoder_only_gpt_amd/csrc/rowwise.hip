@@ -41,18 +41,36 @@ __global__ void embed_count_kernel(const int32_t* idx, int M, int32_t* counts) {
   if (i < M) atomicAdd(&counts[idx[i]], 1);  // integer: exact in any order
 }
 
-// Exclusive scan of counts[n] -> offsets[n] (one workgroup): each thread sums
-// a contiguous run, the run totals are scanned with wave shuffles, then each
-// thread writes its run's offsets.
-__global__ void __launch_bounds__(1024) scan_kernel(const int32_t* counts, int n,
-                                                    int32_t* offsets) {
+// Exclusive scan of counts[n] -> offsets[n] over tiles of 1024: scan_tiles
+// writes each tile's total, scan_apply scans a tile (wave shuffles, then the
+// wave totals) and adds the totals of the tiles before it.
+__global__ void __launch_bounds__(1024) scan_tiles(const int32_t* counts, int n, int32_t* tsum) {
   __shared__ int32_t wsum[16];
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int per = (n + 1023) / 1024;
-  const int b = t * per, e = min(n, b + per);
-  int s = 0;
-  for (int i = b; i < e; ++i) s += counts[i];
-  int x = s;  // inclusive scan within the wave
+  const int t = threadIdx.x, i = blockIdx.x * 1024 + t;
+  int v = i < n ? counts[i] : 0;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((t & 63) == 0) wsum[t >> 6] = v;
+  __syncthreads();
+  if (t == 0) {
+    int s = 0;
+    for (int w = 0; w < 16; ++w) s += wsum[w];
+    tsum[blockIdx.x] = s;
+  }
+}
+
+__global__ void __launch_bounds__(1024) scan_apply(const int32_t* counts, int n,
+                                                   const int32_t* tsum, int32_t* offsets) {
+  __shared__ int32_t wsum[16], before[16];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, i = blockIdx.x * 1024 + t;
+  // totals of the earlier tiles
+  int b = 0;
+  for (int k = t; k < (int)blockIdx.x; k += 1024) b += tsum[k];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) b += __shfl_xor(b, o, 64);
+  if (lane == 0) before[wave] = b;
+  const int c = i < n ? counts[i] : 0;
+  int x = c;  // inclusive scan within the wave
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int y = __shfl_up(x, o, 64);
@@ -60,12 +78,9 @@ __global__ void __launch_bounds__(1024) scan_kernel(const int32_t* counts, int n
   }
   if (lane == 63) wsum[wave] = x;
   __syncthreads();
-  int acc = x - s;
-  for (int w = 0; w < wave; ++w) acc += wsum[w];
-  for (int i = b; i < e; ++i) {
-    offsets[i] = acc;
-    acc += counts[i];
-  }
+  int acc = x - c;
+  for (int w = 0; w < 16; ++w) acc += before[w] + (w < wave ? wsum[w] : 0);
+  if (i < n) offsets[i] = acc;
 }
 
 // rank[p] += #{p' < p in block y : idx[p'] == idx[p]} for p in block x (256
@@ -101,7 +116,7 @@ __global__ void embed_place_kernel(const int32_t* idx, int M, const int32_t* off
 // fragment of a segment that began in an earlier chunk goes to carry_first[ch]
 // (flag EB_SPAN when it also continues past the chunk), the fragment of one
 // that began here and continues goes to carry_last[ch] (flag EB_LAST).
-constexpr int EB_CHUNK = 64;
+constexpr int EB_CHUNK = 16;
 constexpr int EB_LAST = 1, EB_SPAN = 2;
 
 __global__ void __launch_bounds__(256) embed_chunk_kernel(
@@ -122,50 +137,71 @@ __global__ void __launch_bounds__(256) embed_chunk_kernel(
   __syncthreads();
   const bool first_cont = nb[0] == tok[0];     // first segment began in an earlier chunk
   const bool last_cont = nb[1] == tok[n - 1];  // last segment continues past the chunk
+  const bool one_token = tok[0] == tok[n - 1];
   if (threadIdx.x == 0) {
-    flags[ch] = (last_cont && !(first_cont && tok[0] == tok[n - 1]) ? EB_LAST : 0) |
-                (first_cont && last_cont && tok[0] == tok[n - 1] ? EB_SPAN : 0);
+    flags[ch] = (last_cont && !(first_cont && one_token) ? EB_LAST : 0) |
+                (first_cont && last_cont && one_token ? EB_SPAN : 0);
     last_tok[ch] = tok[n - 1];
   }
   const int C4 = C / 4;
   for (int c = threadIdx.x; c < C4; c += 256) {
+    float4 v[EB_CHUNK];  // all rows in flight at once
+#pragma unroll
+    for (int i = 0; i < EB_CHUNK; ++i)
+      if (i < n) v[i] = ((const float4*)(dx + (long)pos[i] * C))[c];
     float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int i = 0; i < n; ++i) {
-      const float4 v = ((const float4*)(dx + (long)pos[i] * C))[c];
-      run.x += v.x; run.y += v.y; run.z += v.z; run.w += v.w;
-      if (i + 1 < n && tok[i + 1] == tok[i]) continue;  // segment goes on
-      if (first_cont && tok[i] == tok[0]) {
-        ((float4*)(carry_first + (long)ch * C))[c] = run;
-      } else if (i + 1 == n && last_cont) {
-        ((float4*)(carry_last + (long)ch * C))[c] = run;
-      } else {
-        float4* o = (float4*)(dwte + (long)tok[i] * C) + c;
-        const float4 a = *o;
-        *o = make_float4(a.x + run.x, a.y + run.y, a.z + run.z, a.w + run.w);
+#pragma unroll
+    for (int i = 0; i < EB_CHUNK; ++i) {
+      if (i < n) {
+        run.x += v[i].x; run.y += v[i].y; run.z += v[i].z; run.w += v[i].w;
+        if (i + 1 == n || tok[i + 1] != tok[i]) {  // segment ends at entry i
+          if (first_cont && tok[i] == tok[0]) {
+            ((float4*)(carry_first + (long)ch * C))[c] = run;
+          } else if (i + 1 == n && last_cont) {
+            ((float4*)(carry_last + (long)ch * C))[c] = run;
+          } else {
+            float4* o = (float4*)(dwte + (long)tok[i] * C) + c;
+            const float4 a = *o;
+            *o = make_float4(a.x + run.x, a.y + run.y, a.z + run.z, a.w + run.w);
+          }
+          run = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
       }
-      run = make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
 }
 
 // Segments that cross chunk boundaries: the chunk where one begins (EB_LAST)
-// adds its fragment, then the fragments of the following chunks in order.
+// finds the chunk where it ends (the first later chunk without EB_SPAN), then
+// adds its own fragment and those of the following chunks in order.
 __global__ void __launch_bounds__(256) embed_carry_kernel(int C, int nch,
                                                           const float* __restrict__ carry_first,
                                                           const float* __restrict__ carry_last,
                                                           const int32_t* __restrict__ flags,
                                                           const int32_t* __restrict__ last_tok,
                                                           float* __restrict__ dwte) {
+  __shared__ int end_s;
   const int ch = blockIdx.x;
   if (!(flags[ch] & EB_LAST)) return;
+  if (threadIdx.x == 0) end_s = nch;
+  __syncthreads();
+  for (int base = ch + 1; base < nch; base += 256) {
+    const int k = base + threadIdx.x;
+    if (k < nch && !(flags[k] & EB_SPAN)) atomicMin(&end_s, k);
+    __syncthreads();
+    const bool found = end_s < nch;
+    __syncthreads();  // every thread has read end_s before the next round may lower it
+    if (found) break;
+  }
+  const int e = min(end_s, nch - 1);
   const int v = last_tok[ch];
   const int C4 = C / 4;
   for (int c = threadIdx.x; c < C4; c += 256) {
     float4 s = ((const float4*)(carry_last + (long)ch * C))[c];
-    for (int k = ch + 1; k < nch; ++k) {
+#pragma unroll 8
+    for (int k = ch + 1; k <= e; ++k) {
       const float4 f = ((const float4*)(carry_first + (long)k * C))[c];
       s.x += f.x; s.y += f.y; s.z += f.z; s.w += f.w;
-      if (!(flags[k] & EB_SPAN)) break;
     }
     float4* o = (float4*)(dwte + (long)v * C) + c;
     const float4 a = *o;
@@ -206,8 +242,8 @@ __device__ __forceinline__ float4 load4(const bf16_t* p, long o) {
 }
 
 constexpr int LN_NV_MAX = 8;    // float4 vectors per lane -> C <= 2048
-constexpr int LN_BWD_RPW = 4;   // rows per wave in the backward
-constexpr int LN_BWD_RPB = 16;  // rows per workgroup in the backward
+constexpr int LN_BWD_RPW = 16;  // rows per wave in the backward
+constexpr int LN_BWD_RPB = 64;  // rows per workgroup in the backward
 
 template <typename ActT, int LN_NV>
 __global__ void __launch_bounds__(256) ln_fwd_kernel(const float* x, const float* w, const float* b,
@@ -256,7 +292,23 @@ __global__ void __launch_bounds__(256) ln_fwd_kernel(const float* x, const float
 }
 
 // dx = resid_in + rstd * (dxhat - mean(dxhat) - xhat * mean(dxhat * xhat)), dxhat = dy * w.
-// Per-workgroup partial sums of dy*xhat and dy go to partials[2][nblk][C].
+// A wave walks LN_BWD_RPW consecutive rows, loading row r + 1 while row r is
+// computed.  Per-workgroup partial sums of dy*xhat and dy go to
+// partials[2][nblk][C].
+template <typename ActT> struct Raw4;
+template <> struct Raw4<float> {
+  float4 v;
+  __device__ __forceinline__ void load(const float* p, long o) { v = *(const float4*)(p + o); }
+  __device__ __forceinline__ float4 get() const { return v; }
+};
+template <> struct Raw4<bf16_t> {
+  uint2 v;
+  __device__ __forceinline__ void load(const bf16_t* p, long o) { v = *(const uint2*)(p + o); }
+  __device__ __forceinline__ float4 get() const {
+    return make_float4(bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y));
+  }
+};
+
 template <typename ActT, int LN_NV>
 __global__ void __launch_bounds__(256) ln_bwd_kernel(const ActT* dy, const float* x,
                                                      const float* mean, const float* rstd,
@@ -266,47 +318,71 @@ __global__ void __launch_bounds__(256) ln_bwd_kernel(const ActT* dy, const float
   extern __shared__ float sh[];  // [4 waves][2][C]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int C4 = C / 4;
-  float4 aw[LN_NV], ab[LN_NV];
+  float4 aw[LN_NV], ab[LN_NV], wv[LN_NV];
 #pragma unroll
-  for (int i = 0; i < LN_NV; ++i) aw[i] = ab[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int rr = 0; rr < LN_BWD_RPW; ++rr) {
-    const int row = blockIdx.x * LN_BWD_RPB + wave * LN_BWD_RPW + rr;
-    if (row >= M) break;
-    const float mu = mean[row], rs = rstd[row];
-    float4 xh[LN_NV], dh[LN_NV], g[LN_NV];
+  for (int i = 0; i < LN_NV; ++i) {
+    aw[i] = ab[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int c = lane + 64 * i;
+    wv[i] = c < C4 ? ((const float4*)w)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  struct Row {
+    float4 x[LN_NV], r[LN_NV];
+    Raw4<ActT> g[LN_NV];
+    float mu, rs;
+  };
+  auto load_row = [&](int row, Row& t) {
+    t.mu = mean[row];
+    t.rs = rstd[row];
+#pragma unroll
+    for (int i = 0; i < LN_NV; ++i) {
+      const int c = lane + 64 * i;
+      if (c < C4) {
+        t.x[i] = ((const float4*)(x + (long)row * C))[c];
+        t.g[i].load(dy, (long)row * C + 4 * c);
+        t.r[i] = resid_in ? ((const float4*)(resid_in + (long)row * C))[c]
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  };
+  const int r0 = blockIdx.x * LN_BWD_RPB + wave * LN_BWD_RPW;
+  const int r1 = min(M, r0 + LN_BWD_RPW);
+  Row cur, nxt;
+  if (r0 < r1) load_row(r0, cur);
+  for (int row = r0; row < r1; ++row) {
+    if (row + 1 < r1) load_row(row + 1, nxt);
+    const float mu = cur.mu, rs = cur.rs;
+    float4 xh[LN_NV], dh[LN_NV];
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
     for (int i = 0; i < LN_NV; ++i) {
-      int c = lane + 64 * i;
+      const int c = lane + 64 * i;
       if (c < C4) {
-        float4 xv = ((const float4*)(x + (long)row * C))[c];
-        float4 ww = ((const float4*)w)[c];
-        g[i] = load4(dy, (long)row * C + 4 * c);
+        const float4 xv = cur.x[i], g = cur.g[i].get();
         xh[i] = make_float4((xv.x - mu) * rs, (xv.y - mu) * rs, (xv.z - mu) * rs, (xv.w - mu) * rs);
-        dh[i] = make_float4(g[i].x * ww.x, g[i].y * ww.y, g[i].z * ww.z, g[i].w * ww.w);
+        dh[i] = make_float4(g.x * wv[i].x, g.y * wv[i].y, g.z * wv[i].z, g.w * wv[i].w);
         s1 += (dh[i].x + dh[i].y) + (dh[i].z + dh[i].w);
         s2 += (dh[i].x * xh[i].x + dh[i].y * xh[i].y) + (dh[i].z * xh[i].z + dh[i].w * xh[i].w);
-        aw[i].x += g[i].x * xh[i].x; aw[i].y += g[i].y * xh[i].y;
-        aw[i].z += g[i].z * xh[i].z; aw[i].w += g[i].w * xh[i].w;
-        ab[i].x += g[i].x; ab[i].y += g[i].y; ab[i].z += g[i].z; ab[i].w += g[i].w;
+        aw[i].x += g.x * xh[i].x; aw[i].y += g.y * xh[i].y;
+        aw[i].z += g.z * xh[i].z; aw[i].w += g.w * xh[i].w;
+        ab[i].x += g.x; ab[i].y += g.y; ab[i].z += g.z; ab[i].w += g.w;
       }
     }
     const float c1 = warp_sum(s1) / (float)C, c2 = warp_sum(s2) / (float)C;
 #pragma unroll
     for (int i = 0; i < LN_NV; ++i) {
-      int c = lane + 64 * i;
+      const int c = lane + 64 * i;
       if (c < C4) {
-        long o = (long)row * C + 4 * c;
-        float4 r = resid_in ? ((const float4*)(resid_in + (long)row * C))[c]
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
-        float4 d = make_float4(r.x + rs * (dh[i].x - c1 - xh[i].x * c2),
-                               r.y + rs * (dh[i].y - c1 - xh[i].y * c2),
-                               r.z + rs * (dh[i].z - c1 - xh[i].z * c2),
-                               r.w + rs * (dh[i].w - c1 - xh[i].w * c2));
-        ((float4*)(dx + (long)row * C))[c] = d;
+        const long o = (long)row * C + 4 * c;
+        const float4 r = cur.r[i];
+        const float4 d = make_float4(r.x + rs * (dh[i].x - c1 - xh[i].x * c2),
+                                     r.y + rs * (dh[i].y - c1 - xh[i].y * c2),
+                                     r.z + rs * (dh[i].z - c1 - xh[i].z * c2),
+                                     r.w + rs * (dh[i].w - c1 - xh[i].w * c2));
+        *(float4*)(dx + o) = d;
         store4(dx_act, o, d);
       }
     }
+    cur = nxt;
   }
 #pragma unroll
   for (int i = 0; i < LN_NV; ++i) {
@@ -326,50 +402,45 @@ __global__ void __launch_bounds__(256) ln_bwd_kernel(const ActT* dy, const float
   }
 }
 
-// out[c] (+)= sum over rows r of part[r, c], in two fixed-order stages.
-// Stage 1: workgroup (x, y) owns 64 columns and rows [y*RS, (y+1)*RS); wave w
-// sums rows w, w+4, ... of that slice and the four wave sums are added in wave
-// order -> stage[y][c].  Stage 2 adds the RED_SLICES rows of `stage` in order.
-constexpr int RED_SLICES = 16;
-__global__ void __launch_bounds__(256) reduce_rows_stage1(const float* part, int R, int N,
-                                                          float* stage) {
-  __shared__ float red[4][64];
+// out_p[c] (+)= sum over rows r of part[p * R * N + r * N + c] for parts
+// p = blockIdx.y, in a fixed order: workgroup (x, p) owns 64 columns; wave w
+// of 16 sums rows w, w + 16, ... (four loads in flight) and the 16 wave sums
+// are added in wave order.
+__global__ void __launch_bounds__(1024) colreduce_kernel(const float* __restrict__ part, int R,
+                                                         int N, float* out0, float* out1,
+                                                         int accumulate) {
+  __shared__ float red[16][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = blockIdx.x * 64 + lane;
-  const int rs = (R + RED_SLICES - 1) / RED_SLICES;
-  const int r0 = blockIdx.y * rs, r1 = min(R, r0 + rs);
+  const float* pp = part + (long)blockIdx.y * R * N;
+  float* out = blockIdx.y ? out1 : out0;
   float s = 0.f;
   if (c < N) {
-    int r = r0 + wave;
-    for (; r + 12 < r1; r += 16) {  // four independent loads in flight
-      float a = part[(long)r * N + c], b = part[(long)(r + 4) * N + c];
-      float d = part[(long)(r + 8) * N + c], e = part[(long)(r + 12) * N + c];
+    int r = wave;
+    for (; r + 48 < R; r += 64) {
+      const float a = pp[(long)r * N + c], b = pp[(long)(r + 16) * N + c];
+      const float d = pp[(long)(r + 32) * N + c], e = pp[(long)(r + 48) * N + c];
       s += ((a + b) + d) + e;
     }
-    for (; r < r1; r += 4) s += part[(long)r * N + c];
+    for (; r < R; r += 16) s += pp[(long)r * N + c];
   }
   red[wave][lane] = s;
   __syncthreads();
-  if (wave == 0 && c < N)
-    stage[(long)blockIdx.y * N + c] = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
-}
-
-__global__ void __launch_bounds__(256) reduce_rows_stage2(const float* stage, int N, float* out,
-                                                          int accumulate) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= N || out == nullptr) return;
-  float t = 0.f;
+  if (wave == 0 && c < N && out) {
+    float t = red[0][lane];
 #pragma unroll
-  for (int y = 0; y < RED_SLICES; ++y) t += stage[(long)y * N + c];
-  out[c] = accumulate ? out[c] + t : t;
+    for (int w = 1; w < 16; ++w) t += red[w][lane];
+    out[c] = accumulate ? out[c] + t : t;
+  }
 }
 
-// `stage` holds RED_SLICES * N floats.
-hipError_t reduce_rows(const float* part, int R, int N, float* out, int accumulate, float* stage,
+// One or two column reductions of R x N partial rows (part, then part + R * N).
+hipError_t reduce_rows(const float* part, int R, int N, float* out0, float* out1, int accumulate,
                        hipStream_t s) {
-  if (out == nullptr) return hipSuccess;
-  reduce_rows_stage1<<<dim3((unsigned)cdiv(N, 64), RED_SLICES), 256, 0, s>>>(part, R, N, stage);
-  reduce_rows_stage2<<<(unsigned)cdiv(N, 256), 256, 0, s>>>(stage, N, out, accumulate);
+  if (out0 == nullptr && out1 == nullptr) return hipSuccess;
+  const unsigned parts = out1 ? 2 : 1;
+  colreduce_kernel<<<dim3((unsigned)cdiv(N, 64), parts), 1024, 0, s>>>(part, R, N, out0, out1,
+                                                                       accumulate);
   return hipGetLastError();
 }
 
@@ -672,7 +743,9 @@ hipError_t embed_bwd(const int32_t* idx, const float* dx, int M, int T, int C, i
     fill_i32<<<(unsigned)cdiv(Vp, 256), 256, 0, s>>>(scr.counts, Vp, 0);
     fill_i32<<<(unsigned)nb, 256, 0, s>>>(scr.rank, M, 0);
     embed_count_kernel<<<(unsigned)nb, 256, 0, s>>>(idx, M, scr.counts);
-    scan_kernel<<<1, 1024, 0, s>>>(scr.counts, Vp, scr.offsets);
+    const unsigned ntiles = (unsigned)cdiv(Vp, 1024);
+    scan_tiles<<<ntiles, 1024, 0, s>>>(scr.counts, Vp, scr.tile_sums);
+    scan_apply<<<ntiles, 1024, 0, s>>>(scr.counts, Vp, scr.tile_sums, scr.offsets);
     embed_rank_kernel<<<dim3((unsigned)nb, (unsigned)nb), 256, 0, s>>>(idx, M, scr.rank);
     embed_place_kernel<<<(unsigned)nb, 256, 0, s>>>(idx, M, scr.offsets, scr.rank, scr.perm);
     embed_chunk_kernel<<<(unsigned)nch, 256, 0, s>>>(dx, M, C, idx, scr.perm, dwte,
@@ -707,7 +780,7 @@ hipError_t layernorm_fwd(int prec, const float* x, const float* w, const float* 
 
 int layernorm_bwd_partial_rows(int M) { return (int)cdiv(M, LN_BWD_RPB); }
 int64_t layernorm_bwd_partial_floats(int M, int C) {
-  return (2L * layernorm_bwd_partial_rows(M) + RED_SLICES) * C;
+  return 2L * layernorm_bwd_partial_rows(M) * C;
 }
 
 hipError_t layernorm_bwd(int prec, const void* dy, const float* x, const float* mean,
@@ -735,14 +808,14 @@ hipError_t layernorm_bwd(int prec, const void* dy, const float* x, const float* 
     LNB_(1) LNB_(2) LNB_(3) LNB_(4) LNB_(8)
 #undef LNB_
   }
-  float* stage = partials + 2L * nblk * C;
-  hipError_t e = reduce_rows(partials, nblk, C, dw, accumulate, stage, s);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return reduce_rows(partials + (long)nblk * C, nblk, C, db, accumulate, stage, s);
+  if (dw == nullptr) return hipSuccess;
+  return reduce_rows(partials, nblk, C, dw, db, accumulate, s);
 }
 
 int colsum_partial_rows(int M) { return (int)cdiv(M, CS_ROWS); }
-int64_t colsum_partial_floats(int M, int N) { return ((long)colsum_partial_rows(M) + RED_SLICES) * N; }
+int64_t colsum_partial_floats(int M, int N) { return (long)colsum_partial_rows(M) * N; }
 
 hipError_t colsum(int prec, const void* x, int M, int N, float* out, int accumulate,
                   float* partials, hipStream_t s) {
@@ -758,7 +831,7 @@ hipError_t colsum(int prec, const void* x, int M, int N, float* out, int accumul
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return reduce_rows(partials, R, N, out, accumulate, partials + (long)R * N, s);
+  return reduce_rows(partials, R, N, out, nullptr, accumulate, s);
 }
 
 bool cross_entropy_supported(int prec, int ldz) {
