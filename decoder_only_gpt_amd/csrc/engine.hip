@@ -179,6 +179,7 @@ Arena plan_arena(const gpt_config& c, int B, int T) {
   ws_need(F, C, M);
   ws_need(C, F, M);
   ws_need(Vp, C, M);
+  ws_need(M, C, Vq);  // the vocabulary projection's input gradient
   a.gemm_ws_bytes = ws;
   a.gemm_ws = take(std::max<int64_t>(ws, 16));
   a.cs_part = take(gpt::colsum_partial_floats((int)M, (int)std::max(3 * C, F)) * 4 + 16);

@@ -564,6 +564,7 @@ MfmaKernel dma_kernel_for(int at, int bt, int epi, int ga, int gb) {
   K_(0, 1, GPT_EPI_STORE)
   K_(0, 1, GPT_EPI_DGELU)
   K_(0, 1, GPT_EPI_F32)
+  K_(0, 1, EPI_PARTIAL)
   K_(1, 1, GPT_EPI_F32)
   K_(1, 1, GPT_EPI_F32_ACCUM)
   K_(1, 1, EPI_PARTIAL)
@@ -782,6 +783,7 @@ MfmaKernel big_kernel_for(int at, int bt, int epi, int ga, int gb) {
   K_(0, 1, GPT_EPI_STORE)
   K_(0, 1, GPT_EPI_DGELU)
   K_(0, 1, GPT_EPI_F32)
+  K_(0, 1, EPI_PARTIAL)
   K_(1, 1, GPT_EPI_F32)
   K_(1, 1, GPT_EPI_F32_ACCUM)
   K_(1, 1, EPI_PARTIAL)
@@ -831,10 +833,21 @@ GemmPlan plan_gemm(int M, int N, int K, int precision, bool splittable, int64_t 
     return p;
   }
   if (force != 128) {
-    // Weight gradients (short M x N, K = tokens): 256-tiles with K split so the
-    // grid is about one wave of the 256 CUs.
+    // Long reductions over few output tiles (weight gradients: K = tokens; the
+    // vocabulary projection's input gradient: K = vocabulary): 256-tiles with
+    // K split, the split count the one that needs the fewest rounds of the 256
+    // CUs per unit of work (the smallest such).
     if (splittable && K >= 2048 && t256 < 256) {
-      int S = (int)std::min<long>(std::min<long>(256 / t256, K / 1024), 32);
+      const int maxs = (int)std::min<long>(K / 1024, 32);
+      int S = 1;
+      double best = 1.0;  // rounds per split of the unsplit grid: cdiv(t256, 256) / 1
+      for (int c = 2; c <= maxs; ++c) {
+        const double r = (double)cdiv(t256 * c, 256) / c;
+        if (r < best - 1e-9) {
+          best = r;
+          S = c;
+        }
+      }
       if (S >= 2 && ws_bytes >= (int64_t)S * M * N * 4) {
         p.big = true;
         p.S = S;
@@ -859,7 +872,11 @@ int effective_splits(const GemmPlan& p, int K) {
   return (int)cdiv(K, kchunk);
 }
 
-bool splittable(const gpt_gemm_desc& d) { return d.a_trans && d.b_trans && !d.a_gelu; }
+// K may be split (partials reduced, epilogue applied after) for weight
+// gradients and for very long reductions.
+bool splittable(const gpt_gemm_desc& d) {
+  return !d.a_gelu && !d.b_gelu && ((d.a_trans && d.b_trans) || d.K >= 16384);
+}
 // Direct-to-LDS loads address each operand through a 31-bit byte offset.
 bool dma_ok(const gpt_gemm_desc& d) {
   if (getenv("GPT_GEMM_NODMA")) return false;

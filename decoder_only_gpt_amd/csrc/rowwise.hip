@@ -242,8 +242,8 @@ __device__ __forceinline__ float4 load4(const bf16_t* p, long o) {
 }
 
 constexpr int LN_NV_MAX = 8;    // float4 vectors per lane -> C <= 2048
-constexpr int LN_BWD_RPW = 16;  // rows per wave in the backward
-constexpr int LN_BWD_RPB = 64;  // rows per workgroup in the backward
+constexpr int LN_BWD_RPW = 4;   // rows per wave in the backward
+constexpr int LN_BWD_RPB = 64;  // rows per workgroup in the backward (16 waves)
 
 template <typename ActT, int LN_NV>
 __global__ void __launch_bounds__(256) ln_fwd_kernel(const float* x, const float* w, const float* b,
@@ -292,74 +292,37 @@ __global__ void __launch_bounds__(256) ln_fwd_kernel(const float* x, const float
 }
 
 // dx = resid_in + rstd * (dxhat - mean(dxhat) - xhat * mean(dxhat * xhat)), dxhat = dy * w.
-// A wave walks LN_BWD_RPW consecutive rows, loading row r + 1 while row r is
-// computed.  Per-workgroup partial sums of dy*xhat and dy go to
-// partials[2][nblk][C].
-template <typename ActT> struct Raw4;
-template <> struct Raw4<float> {
-  float4 v;
-  __device__ __forceinline__ void load(const float* p, long o) { v = *(const float4*)(p + o); }
-  __device__ __forceinline__ float4 get() const { return v; }
-};
-template <> struct Raw4<bf16_t> {
-  uint2 v;
-  __device__ __forceinline__ void load(const bf16_t* p, long o) { v = *(const uint2*)(p + o); }
-  __device__ __forceinline__ float4 get() const {
-    return make_float4(bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y));
-  }
-};
-
+// A workgroup of LN_BWD_WAVES waves owns LN_BWD_RPB rows (LN_BWD_RPW per
+// wave).  Its partial sums of dy*xhat and dy go to partials[2][nblk][C]: the
+// wave sums are combined in LDS in four rounds of four waves, in wave order.
+constexpr int LN_BWD_WAVES = 16;
 template <typename ActT, int LN_NV>
-__global__ void __launch_bounds__(256) ln_bwd_kernel(const ActT* dy, const float* x,
-                                                     const float* mean, const float* rstd,
-                                                     const float* w, const float* resid_in, int M,
-                                                     int C, float* dx, ActT* dx_act,
-                                                     float* partials) {
-  extern __shared__ float sh[];  // [4 waves][2][C]
+__global__ void __launch_bounds__(64 * LN_BWD_WAVES) ln_bwd_kernel(
+    const ActT* dy, const float* x, const float* mean, const float* rstd, const float* w,
+    const float* resid_in, int M, int C, float* dx, ActT* dx_act, float* partials) {
+  extern __shared__ float sh[];  // [4 slots][2][C]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int C4 = C / 4;
-  float4 aw[LN_NV], ab[LN_NV], wv[LN_NV];
+  float4 aw[LN_NV], ab[LN_NV];
 #pragma unroll
-  for (int i = 0; i < LN_NV; ++i) {
-    aw[i] = ab[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    const int c = lane + 64 * i;
-    wv[i] = c < C4 ? ((const float4*)w)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  struct Row {
-    float4 x[LN_NV], r[LN_NV];
-    Raw4<ActT> g[LN_NV];
-    float mu, rs;
-  };
-  auto load_row = [&](int row, Row& t) {
-    t.mu = mean[row];
-    t.rs = rstd[row];
-#pragma unroll
-    for (int i = 0; i < LN_NV; ++i) {
-      const int c = lane + 64 * i;
-      if (c < C4) {
-        t.x[i] = ((const float4*)(x + (long)row * C))[c];
-        t.g[i].load(dy, (long)row * C + 4 * c);
-        t.r[i] = resid_in ? ((const float4*)(resid_in + (long)row * C))[c]
-                          : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    }
-  };
-  const int r0 = blockIdx.x * LN_BWD_RPB + wave * LN_BWD_RPW;
-  const int r1 = min(M, r0 + LN_BWD_RPW);
-  Row cur, nxt;
-  if (r0 < r1) load_row(r0, cur);
-  for (int row = r0; row < r1; ++row) {
-    if (row + 1 < r1) load_row(row + 1, nxt);
-    const float mu = cur.mu, rs = cur.rs;
-    float4 xh[LN_NV], dh[LN_NV];
+  for (int i = 0; i < LN_NV; ++i) aw[i] = ab[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int rr = 0; rr < LN_BWD_RPW; ++rr) {
+    const int row = blockIdx.x * LN_BWD_RPB + wave * LN_BWD_RPW + rr;
+    if (row >= M) break;
+    const float mu = mean[row], rs = rstd[row];
+    float4 xh[LN_NV], dh[LN_NV], r[LN_NV];
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
     for (int i = 0; i < LN_NV; ++i) {
       const int c = lane + 64 * i;
       if (c < C4) {
-        const float4 xv = cur.x[i], g = cur.g[i].get();
+        const float4 xv = ((const float4*)(x + (long)row * C))[c];
+        const float4 ww = ((const float4*)w)[c];
+        const float4 g = load4(dy, (long)row * C + 4 * c);
+        r[i] = resid_in ? ((const float4*)(resid_in + (long)row * C))[c]
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
         xh[i] = make_float4((xv.x - mu) * rs, (xv.y - mu) * rs, (xv.z - mu) * rs, (xv.w - mu) * rs);
-        dh[i] = make_float4(g.x * wv[i].x, g.y * wv[i].y, g.z * wv[i].z, g.w * wv[i].w);
+        dh[i] = make_float4(g.x * ww.x, g.y * ww.y, g.z * ww.z, g.w * ww.w);
         s1 += (dh[i].x + dh[i].y) + (dh[i].z + dh[i].w);
         s2 += (dh[i].x * xh[i].x + dh[i].y * xh[i].y) + (dh[i].z * xh[i].z + dh[i].w * xh[i].w);
         aw[i].x += g.x * xh[i].x; aw[i].y += g.y * xh[i].y;
@@ -373,28 +336,40 @@ __global__ void __launch_bounds__(256) ln_bwd_kernel(const ActT* dy, const float
       const int c = lane + 64 * i;
       if (c < C4) {
         const long o = (long)row * C + 4 * c;
-        const float4 r = cur.r[i];
-        const float4 d = make_float4(r.x + rs * (dh[i].x - c1 - xh[i].x * c2),
-                                     r.y + rs * (dh[i].y - c1 - xh[i].y * c2),
-                                     r.z + rs * (dh[i].z - c1 - xh[i].z * c2),
-                                     r.w + rs * (dh[i].w - c1 - xh[i].w * c2));
+        const float4 d = make_float4(r[i].x + rs * (dh[i].x - c1 - xh[i].x * c2),
+                                     r[i].y + rs * (dh[i].y - c1 - xh[i].y * c2),
+                                     r[i].z + rs * (dh[i].z - c1 - xh[i].z * c2),
+                                     r[i].w + rs * (dh[i].w - c1 - xh[i].w * c2));
         *(float4*)(dx + o) = d;
         store4(dx_act, o, d);
       }
     }
-    cur = nxt;
   }
+  // waves 4k .. 4k+3 add into slots 0..3 in round k
+  float* slot = sh + (wave & 3) * 2 * C;
+  for (int round = 0; round < LN_BWD_WAVES / 4; ++round) {
+    if ((wave >> 2) == round) {
 #pragma unroll
-  for (int i = 0; i < LN_NV; ++i) {
-    int c = lane + 64 * i;
-    if (c < C4) {
-      ((float4*)(sh + (wave * 2 + 0) * C))[c] = aw[i];
-      ((float4*)(sh + (wave * 2 + 1) * C))[c] = ab[i];
+      for (int i = 0; i < LN_NV; ++i) {
+        const int c = lane + 64 * i;
+        if (c < C4) {
+          float4* pw = (float4*)slot + c;
+          float4* pb = (float4*)(slot + C) + c;
+          if (round == 0) {
+            *pw = aw[i];
+            *pb = ab[i];
+          } else {
+            const float4 a = *pw, b = *pb;
+            *pw = make_float4(a.x + aw[i].x, a.y + aw[i].y, a.z + aw[i].z, a.w + aw[i].w);
+            *pb = make_float4(b.x + ab[i].x, b.y + ab[i].y, b.z + ab[i].z, b.w + ab[i].w);
+          }
+        }
+      }
     }
+    __syncthreads();
   }
-  __syncthreads();
   const int nblk = gridDim.x;
-  for (int c = threadIdx.x; c < C; c += 256) {
+  for (int c = threadIdx.x; c < C; c += 64 * LN_BWD_WAVES) {
     float sw = ((sh[0 * C + c] + sh[2 * C + c]) + sh[4 * C + c]) + sh[6 * C + c];
     float sb = ((sh[1 * C + c] + sh[3 * C + c]) + sh[5 * C + c]) + sh[7 * C + c];
     partials[(long)blockIdx.x * C + c] = sw;
@@ -796,11 +771,11 @@ hipError_t layernorm_bwd(int prec, const void* dy, const float* x, const float* 
 #define LNB_(NV)                                                                                 \
   if (!done && nv <= NV) {                                                                       \
     if (prec == GPT_BF16)                                                                        \
-      ln_bwd_kernel<bf16_t, NV><<<nblk, 256, shmem, s>>>((const bf16_t*)dy, x, mean, rstd, w,    \
+      ln_bwd_kernel<bf16_t, NV><<<nblk, 1024, shmem, s>>>((const bf16_t*)dy, x, mean, rstd, w,   \
                                                          resid_in, M, C, dx, (bf16_t*)dx_act,    \
                                                          partials);                              \
     else                                                                                         \
-      ln_bwd_kernel<float, NV><<<nblk, 256, shmem, s>>>((const float*)dy, x, mean, rstd, w,      \
+      ln_bwd_kernel<float, NV><<<nblk, 1024, shmem, s>>>((const float*)dy, x, mean, rstd, w,     \
                                                         resid_in, M, C, dx, (float*)dx_act,      \
                                                         partials);                               \
     done = true;                                                                                 \
