@@ -120,12 +120,15 @@ int check_config(const gpt_config* c, int B, int T) {
   return GPT_OK;
 }
 
+// Depth of the rings of gradient buffers shared by the two backward streams.
+constexpr int NGB = 6;
+
 // Byte offsets of every region of the arena.
 struct Arena {
   int64_t params, grads, adam_m, adam_v, shadow;
   int64_t X, ln_mean, ln_rstd;
   std::vector<int64_t> a1, qkv, att, lse, a2, u, g;
-  int64_t xf, logits, loss_rows, loss, gres[2], gact, dC, dC2, dF, dqkv, dvec;
+  int64_t xf, logits, loss_rows, loss, gres[2], gact[NGB], dC, dC2, dF[NGB], dqkv[NGB], dvec;
   int64_t gemm_ws, gemm_ws_bytes, cs_part, ln_part, n_part, norm2;
   int64_t e_counts, e_offsets, e_tile_sums, e_rank, e_perm, e_carry_first, e_carry_last, e_flags,
       e_last_tok;
@@ -164,11 +167,13 @@ Arena plan_arena(const gpt_config& c, int B, int T) {
   a.loss = take(16);
   a.gres[0] = take(M * C * 4);
   a.gres[1] = take(M * C * 4);
-  a.gact = take(M * C * act);
+  // Gradients the weight-gradient branch reads live in rings of NGB buffers,
+  // so the main chain can run ahead of the side stream by a few layers.
+  for (int i = 0; i < NGB; ++i) a.gact[i] = take(M * C * act);
   a.dC = take(M * C * act);
   a.dC2 = take(M * C * act);
-  a.dF = take(M * F * act);
-  a.dqkv = take(M * 3 * C * act);
+  for (int i = 0; i < NGB; ++i) a.dF[i] = take(M * F * act);
+  for (int i = 0; i < NGB; ++i) a.dqkv[i] = take(M * 3 * C * act);
   a.dvec = take(2 * M * H * 4);  // D, then the log-sum-exp in log2 units
   int64_t ws = 0;
   auto ws_need = [&](int64_t m, int64_t n, int64_t k) {
@@ -227,6 +232,11 @@ struct gpt_model {
   }
   bool loss_valid;
   const int32_t* last_idx;
+  // Weight-gradient branch of the backward: a second stream (default
+  // priority) and the events that order it against the main chain.
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  hipEvent_t ev_buf[3 * NGB] = {};  // last side-stream read of gact[], dF[], dqkv[]
 
   template <typename T_> T_* at(int64_t off) const { return off < 0 ? nullptr : (T_*)(base + off); }
   float* P(int64_t e) const { return e < 0 ? nullptr : at<float>(ar.params) + e; }
@@ -399,88 +409,139 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
   auto act = [&](int64_t off) { return m->at<char>(off); };
   float* cs_part = m->at<float>(m->ar.cs_part);
   float* ln_part = m->at<float>(m->ar.ln_part);
-  char* gact = act(m->ar.gact);
   char* dC = act(m->ar.dC);
   char* dC2 = act(m->ar.dC2);
-  char* dF = act(m->ar.dF);
-  char* dqkv = act(m->ar.dqkv);
   int cur = 0;
   float* gres[2] = {m->at<float>(m->ar.gres[0]), m->at<float>(m->ar.gres[1])};
+
+  // Weight and bias gradients only feed the optimizer: they run on the side
+  // stream, overlapping the input-gradient chain on `s`.  While kernels are
+  // being timed everything stays on `s`, so each kernel is timed alone.
+  hipStream_t s2 = m->prof_on ? s : m->side;
+  bool live[3 * NGB] = {};
+  auto hip_ok = [&](hipError_t e, const char* what) -> int {
+    return e == hipSuccess ? GPT_OK : fail(GPT_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  };
+  auto fork = [&]() -> int {  // work enqueued on s so far is visible to s2
+    if (s2 == s) return GPT_OK;
+    int rc = hip_ok(hipEventRecord(m->ev_fork, s), "hipEventRecord");
+    return rc != GPT_OK ? rc : hip_ok(hipStreamWaitEvent(s2, m->ev_fork, 0), "hipStreamWaitEvent");
+  };
+  auto mark = [&](int slot) -> int {  // s2 is done reading buffer `slot` after this point
+    if (s2 == s) return GPT_OK;
+    live[slot] = true;
+    return hip_ok(hipEventRecord(m->ev_buf[slot], s2), "hipEventRecord");
+  };
+  auto before_write = [&](int slot) -> int {  // s may overwrite buffer `slot`
+    if (s2 == s || !live[slot]) return GPT_OK;
+    return hip_ok(hipStreamWaitEvent(s, m->ev_buf[slot], 0), "hipStreamWaitEvent");
+  };
+#define CHECK(x)                    \
+  do {                              \
+    int rc_ = (x);                  \
+    if (rc_ != GPT_OK) return rc_;  \
+  } while (0)
+  auto gemm_on = [&](hipStream_t st, const gpt_gemm_desc& dd, int site) -> int {
+    return run_gemm(m, st, dd, site);
+  };
   auto bias_grad = [&](const char* x, int64_t n, int64_t off) -> int {
     if (off < 0) return GPT_OK;
+    hipStream_t s = s2;
     LAUNCH(GPT_K_BIAS_GRAD, GPT_S_BIAS_GRAD, 0, M * n * act_b,
            gpt::colsum(prec, x, (int)M, (int)n, m->G(off), acc, cs_part, s));
     return GPT_OK;
   };
-#define BIAS_GRAD(x, n, off)                    \
-  do {                                          \
-    int rc_ = bias_grad((x), (n), (off));       \
-    if (rc_ != GPT_OK) return rc_;              \
-  } while (0)
 
   // lm_head: dxf = dlogits . W ; dW (+)= dlogits^T . xf  (dlogits are in `logits`).
   const char* dlog = act(m->ar.logits);
   gpt_gemm_desc d = linear_dx(m, dlog, m->Vq, m->pl.lmw, C, m->Vq, m->Vp);
   d.epilogue = GPT_EPI_STORE; d.out = dC; d.ldo = C;
   GEMM(d, GPT_S_LMHEAD_DX);
+  CHECK(fork());
   d = linear_dw(m, dlog, m->Vq, m->Vq, act(m->ar.xf), C, m->pl.lmw, m->Vp, acc);
-  GEMM(d, GPT_S_LMHEAD_DW);
+  CHECK(gemm_on(s2, d, GPT_S_LMHEAD_DW));
   const int64_t nl = 2 * c.n_layer;
+  int gi = 0;  // gact[gi] holds the current LayerNorm input gradient (bf16); slots 0..NGB-1
+  char* gact = act(m->ar.gact[gi]);
   LAUNCH(GPT_K_LAYERNORM, GPT_S_LN_BWD, 0, ln_bwd_bytes - 4.0 * M * C,
          gpt::layernorm_bwd(prec, dC, m->X(nl), m->mean(nl), m->rstd(nl), m->P(m->pl.lnfw), nullptr,
                             (int)M, (int)C, gres[cur], gact, m->G(m->pl.lnfw), m->G(m->pl.lnfb),
                             acc, ln_part, s));
   for (int l = c.n_layer - 1; l >= 0; --l) {
     const LayerOff& L = m->pl.layer[l];
+    const int di = l % NGB;  // dF / dqkv ring slot: events NGB + di and 2 NGB + di
+    char* dF = act(m->ar.dF[di]);
+    char* dqkv = act(m->ar.dqkv[di]);
     // MLP out: x_out = x_mid + GELU(u) Wfcp^T + b
+    CHECK(before_write(NGB + di));
     d = linear_dx(m, gact, C, L.fcpw, F, C, C);
     d.epilogue = GPT_EPI_DGELU; d.aux = act(m->ar.u[l]); d.ldaux = F; d.out = dF; d.ldo = F;
     GEMM(d, GPT_S_FCPROJ_DX);
+    CHECK(fork());
     if (c.recompute_gelu) {
       d = linear_dw(m, gact, C, C, act(m->ar.u[l]), F, L.fcpw, C, acc);
       d.b_gelu = 1;
     } else {
       d = linear_dw(m, gact, C, C, act(m->ar.g[l]), F, L.fcpw, C, acc);
     }
-    GEMM(d, GPT_S_FCPROJ_DW);
-    BIAS_GRAD(gact, C, L.fcpb);
+    CHECK(gemm_on(s2, d, GPT_S_FCPROJ_DW));
+    CHECK(bias_grad(gact, C, L.fcpb));
+    CHECK(mark(gi));
     // MLP in: u = a2 Wfc^T + b
+    d = linear_dw(m, dF, F, F, act(m->ar.a2[l]), C, L.fcw, F, acc);
+    CHECK(gemm_on(s2, d, GPT_S_FC_DW));
+    CHECK(bias_grad(dF, F, L.fcb));
+    CHECK(mark(NGB + di));
     d = linear_dx(m, dF, F, L.fcw, C, F, F);
     d.epilogue = GPT_EPI_STORE; d.out = dC; d.ldo = C;
     GEMM(d, GPT_S_FC_DX);
-    d = linear_dw(m, dF, F, F, act(m->ar.a2[l]), C, L.fcw, F, acc);
-    GEMM(d, GPT_S_FC_DW);
-    BIAS_GRAD(dF, F, L.fcb);
+    gi = (gi + 1) % NGB;
+    gact = act(m->ar.gact[gi]);
+    CHECK(before_write(gi));
     LAUNCH(GPT_K_LAYERNORM, GPT_S_LN_BWD, 0, ln_bwd_bytes,
            gpt::layernorm_bwd(prec, dC, m->X(2 * l + 1), m->mean(2 * l + 1), m->rstd(2 * l + 1),
                               m->P(L.ln2w), gres[cur], (int)M, (int)C, gres[cur ^ 1], gact,
                               m->G(L.ln2w), m->G(L.ln2b), acc, ln_part, s));
     cur ^= 1;
     // attention out: x_mid = x_in + y Wproj^T + b
+    CHECK(fork());
+    d = linear_dw(m, gact, C, C, act(m->ar.att[l]), C, L.projw, C, acc);
+    CHECK(gemm_on(s2, d, GPT_S_PROJ_DW));
+    CHECK(bias_grad(gact, C, L.projb));
+    CHECK(mark(gi));
     d = linear_dx(m, gact, C, L.projw, C, C, C);
     d.epilogue = GPT_EPI_STORE; d.out = dC2; d.ldo = C;
     GEMM(d, GPT_S_PROJ_DX);
-    d = linear_dw(m, gact, C, C, act(m->ar.att[l]), C, L.projw, C, acc);
-    GEMM(d, GPT_S_PROJ_DW);
-    BIAS_GRAD(gact, C, L.projb);
+    CHECK(before_write(2 * NGB + di));
     LAUNCH(GPT_K_ATTN_BWD, GPT_S_ATTN_BWD, attn_flops * attn_pairs(m->T, c.window_left[l]), 0,
            gpt::attention_bwd(prec, m->B, m->T, (int)m->H, (int)m->hd, c.window_left[l],
                               act(m->ar.qkv[l]), act(m->ar.att[l]), m->at<float>(m->ar.lse[l]),
                               dC2, dqkv, m->at<float>(m->ar.dvec), s));
     // qkv = a1 Wqkv^T + b
+    CHECK(fork());
+    d = linear_dw(m, dqkv, 3 * C, 3 * C, act(m->ar.a1[l]), C, L.qkvw, 3 * C, acc);
+    CHECK(gemm_on(s2, d, GPT_S_QKV_DW));
+    CHECK(bias_grad(dqkv, 3 * C, L.qkvb));
+    CHECK(mark(2 * NGB + di));
     d = linear_dx(m, dqkv, 3 * C, L.qkvw, C, 3 * C, 3 * C);
     d.epilogue = GPT_EPI_STORE; d.out = dC; d.ldo = C;
     GEMM(d, GPT_S_QKV_DX);
-    d = linear_dw(m, dqkv, 3 * C, 3 * C, act(m->ar.a1[l]), C, L.qkvw, 3 * C, acc);
-    GEMM(d, GPT_S_QKV_DW);
-    BIAS_GRAD(dqkv, 3 * C, L.qkvb);
+    gi = (gi + 1) % NGB;
+    gact = act(m->ar.gact[gi]);
+    CHECK(before_write(gi));
     LAUNCH(GPT_K_LAYERNORM, GPT_S_LN_BWD, 0, ln_bwd_bytes,
            gpt::layernorm_bwd(prec, dC, m->X(2 * l), m->mean(2 * l), m->rstd(2 * l), m->P(L.ln1w),
                               gres[cur], (int)M, (int)C, gres[cur ^ 1], gact, m->G(L.ln1w),
                               m->G(L.ln1b), acc, ln_part, s));
     cur ^= 1;
   }
-#undef BIAS_GRAD
+  // The side stream's gradients (dwte among them with a tied head) are
+  // complete before anything below, or anything after the backward, runs.
+  if (s2 != s) {
+    CHECK(hip_ok(hipEventRecord(m->ev_join, s2), "hipEventRecord"));
+    CHECK(hip_ok(hipStreamWaitEvent(s, m->ev_join, 0), "hipStreamWaitEvent"));
+  }
+#undef CHECK
   // x0 = wte[idx] + wpe[t]; with a tied head the lm_head gradient is already in dwte.
   gpt::EmbedBwdScratch scr{m->at<int32_t>(m->ar.e_counts),   m->at<int32_t>(m->ar.e_offsets),
                            m->at<int32_t>(m->ar.e_tile_sums), m->at<int32_t>(m->ar.e_rank),
@@ -572,11 +633,20 @@ int gpt_init(const gpt_config* cfg, int32_t B, int32_t T, void* d_arena, int64_t
   m->loss_valid = false;
   m->last_idx = nullptr;
   hipStream_t s = (hipStream_t)stream;
+  hipError_t se = hipStreamCreateWithFlags(&m->side, hipStreamNonBlocking);
+  if (se == hipSuccess) se = hipEventCreateWithFlags(&m->ev_fork, hipEventDisableTiming);
+  if (se == hipSuccess) se = hipEventCreateWithFlags(&m->ev_join, hipEventDisableTiming);
+  for (int i = 0; i < 3 * NGB && se == hipSuccess; ++i)
+    se = hipEventCreateWithFlags(&m->ev_buf[i], hipEventDisableTiming);
+  if (se != hipSuccess) {
+    gpt_destroy(m);
+    return fail(GPT_E_HIP, std::string("side stream: ") + hipGetErrorString(se));
+  }
   // Parameters, gradients, moments and the bf16 copy start at zero.  The
   // activation part is cleared too so padded logit columns read as zero.
   hipError_t e = hipMemsetAsync(d_arena, 0, (size_t)a.total, s);
   if (e != hipSuccess) {
-    delete m;
+    gpt_destroy(m);
     return fail(GPT_E_HIP, std::string("hipMemsetAsync: ") + hipGetErrorString(e));
   }
   *out = m;
@@ -585,8 +655,14 @@ int gpt_init(const gpt_config* cfg, int32_t B, int32_t T, void* d_arena, int64_t
 }
 
 int gpt_destroy(gpt_model* m) {
-  if (m)
+  if (m) {
     for (hipEvent_t e : m->ev_pool) (void)hipEventDestroy(e);
+    for (hipEvent_t e : {m->ev_fork, m->ev_join})
+      if (e) (void)hipEventDestroy(e);
+    for (hipEvent_t e : m->ev_buf)
+      if (e) (void)hipEventDestroy(e);
+    if (m->side) (void)hipStreamDestroy(m->side);
+  }
   delete m;
   return GPT_OK;
 }
