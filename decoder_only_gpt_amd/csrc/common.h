@@ -104,6 +104,22 @@ __device__ __forceinline__ float gelu_grad_fast(float u, bool tanh_form) {
   return fmaf(0.5f, e, 0.5f) + u * 0.3989422804014327f * ex2;
 }
 
+// GELU(u) and GELU'(u) together (fast forms, shared intermediate values).
+__device__ __forceinline__ void gelu_pair_fast(float u, bool tanh_form, float& g, float& gp) {
+  if (tanh_form) {
+    const float s = 0.7978845608028654f, k = 0.044715f;
+    float z;
+    const float sg = sigmoid2z(u, z);
+    g = u * sg;
+    gp = sg * fmaf(2.f * s * u * (1.f - sg), fmaf(3.f * k, u * u, 1.f), 1.f);
+    return;
+  }
+  float ex2;
+  const float e = erf_as(u * 0.7071067811865476f, ex2);
+  g = 0.5f * u * (1.f + e);
+  gp = fmaf(0.5f, e, 0.5f) + u * 0.3989422804014327f * ex2;
+}
+
 __device__ __forceinline__ float warp_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -369,7 +369,10 @@ int run_forward(gpt_model* m, const int32_t* idx, const int32_t* tgt, hipStream_
            gpt::layernorm_fwd(prec, m->X(2 * l + 1), m->P(L.ln2w), m->P(L.ln2b), (int)M, (int)C,
                               c.ln_eps, act(m->ar.a2[l]), m->mean(2 * l + 1), m->rstd(2 * l + 1), s));
     d = linear_fwd(m, act(m->ar.a2[l]), C, L.fcw, F, F);
-    d.epilogue = GPT_EPI_GELU; d.bias = m->P(L.fcb); d.out = act(m->ar.u[l]); d.ldo = F;
+    // Kept for the backward: u itself when GELU is recomputed there, else
+    // GELU'(u) (in the u buffer) next to GELU(u).
+    d.epilogue = c.recompute_gelu ? GPT_EPI_GELU : GPT_EPI_GELU_PAIR;
+    d.bias = m->P(L.fcb); d.out = act(m->ar.u[l]); d.ldo = F;
     d.aux = c.recompute_gelu ? nullptr : act(m->ar.g[l]); d.ldaux = F;
     GEMM(d, GPT_S_FC_FWD);
     if (c.recompute_gelu) {
@@ -475,7 +478,8 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
     // MLP out: x_out = x_mid + GELU(u) Wfcp^T + b
     CHECK(before_write(NGB + di));
     d = linear_dx(m, gact, C, L.fcpw, F, C, C);
-    d.epilogue = GPT_EPI_DGELU; d.aux = act(m->ar.u[l]); d.ldaux = F; d.out = dF; d.ldo = F;
+    d.epilogue = c.recompute_gelu ? GPT_EPI_DGELU : GPT_EPI_MUL;
+    d.aux = act(m->ar.u[l]); d.ldaux = F; d.out = dF; d.ldo = F;
     GEMM(d, GPT_S_FCPROJ_DX);
     CHECK(fork());
     if (c.recompute_gelu) {
@@ -812,12 +816,14 @@ int gpt_op_gemm(const gpt_gemm_desc* d, void* stream) {
   if (!d) return fail(GPT_E_INVALID, "NULL descriptor");
   if (d->precision != GPT_FP32 && d->precision != GPT_BF16)
     return fail(GPT_E_INVALID, "bad precision");
-  if (d->epilogue < GPT_EPI_STORE || d->epilogue > GPT_EPI_F32_ACCUM)
+  if (d->epilogue < GPT_EPI_STORE || d->epilogue > GPT_EPI_MUL)
     return fail(GPT_E_INVALID, "bad epilogue");
   if (d->M < 0 || d->N < 0 || d->K < 0) return fail(GPT_E_INVALID, "negative size");
   if (!d->out && d->M > 0 && d->N > 0) return fail(GPT_E_INVALID, "NULL out");
   if (d->epilogue == GPT_EPI_RESIDUAL && !d->resid) return fail(GPT_E_INVALID, "NULL resid");
-  if (d->epilogue == GPT_EPI_DGELU && !d->aux) return fail(GPT_E_INVALID, "NULL aux");
+  if ((d->epilogue == GPT_EPI_DGELU || d->epilogue == GPT_EPI_GELU_PAIR ||
+       d->epilogue == GPT_EPI_MUL) && !d->aux)
+    return fail(GPT_E_INVALID, "NULL aux");
   hipError_t e = gpt::gemm(*d, (hipStream_t)stream);
   if (e == hipErrorInvalidValue)
     return fail(GPT_E_INVALID, "gemm layout rule broken (K, lda, ldb must be multiples of 8)");

@@ -64,6 +64,19 @@ __device__ __forceinline__ void epilogue(const EpiArgs& e, int m, int n, float a
       Act<ActT>::store((ActT*)e.out, o, acc * gelu_grad_f(u, e.tanh_form));
       break;
     }
+    case GPT_EPI_GELU_PAIR: {
+      if (e.bias) acc += e.bias[n];
+      ActT r;  // the pre-activation rounded to the activation type
+      Act<ActT>::store(&r, 0, acc);
+      const float u = Act<ActT>::load(&r, 0);
+      Act<ActT>::store((ActT*)e.out, o, gelu_grad_f(u, e.tanh_form));
+      Act<ActT>::store((ActT*)e.aux, (long)m * e.ldaux + n, gelu_f(u, e.tanh_form));
+      break;
+    }
+    case GPT_EPI_MUL:
+      Act<ActT>::store((ActT*)e.out, o,
+                       acc * Act<ActT>::load((const ActT*)e.aux, (long)m * e.ldaux + n));
+      break;
     case GPT_EPI_F32:
       ((float*)e.out)[o] = acc;
       break;
@@ -261,6 +274,29 @@ __device__ __forceinline__ void epilogue8(const EpiArgs& e, float* partial, int 
     }
     *(u32x4*)((bf16_t*)e.out + o) = u32x4{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]),
                                            pack_bf2(x[4], x[5]), pack_bf2(x[6], x[7])};
+  } else if constexpr (EPI == GPT_EPI_MUL) {
+    const u32x4 a = *(const u32x4*)((const bf16_t*)e.aux + (long)m * e.ldaux + n);
+    *(u32x4*)((bf16_t*)e.out + o) = u32x4{
+        pack_bf2(x[0] * bf_lo(a.x), x[1] * bf_hi(a.x)), pack_bf2(x[2] * bf_lo(a.y), x[3] * bf_hi(a.y)),
+        pack_bf2(x[4] * bf_lo(a.z), x[5] * bf_hi(a.z)), pack_bf2(x[6] * bf_lo(a.w), x[7] * bf_hi(a.w))};
+  } else if constexpr (EPI == GPT_EPI_GELU_PAIR) {
+    if (e.bias) {
+      float4 b0 = *(const float4*)(e.bias + n), b1 = *(const float4*)(e.bias + n + 4);
+      x[0] += b0.x; x[1] += b0.y; x[2] += b0.z; x[3] += b0.w;
+      x[4] += b1.x; x[5] += b1.y; x[6] += b1.z; x[7] += b1.w;
+    }
+    const u32x4 w{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]), pack_bf2(x[4], x[5]),
+                  pack_bf2(x[6], x[7])};  // u rounded to bf16
+    float g[8], gp[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      gelu_pair_fast(bf_lo(w[i]), e.tanh_form, g[2 * i], gp[2 * i]);
+      gelu_pair_fast(bf_hi(w[i]), e.tanh_form, g[2 * i + 1], gp[2 * i + 1]);
+    }
+    *(u32x4*)((bf16_t*)e.out + o) = u32x4{pack_bf2(gp[0], gp[1]), pack_bf2(gp[2], gp[3]),
+                                           pack_bf2(gp[4], gp[5]), pack_bf2(gp[6], gp[7])};
+    *(u32x4*)((bf16_t*)e.aux + (long)m * e.ldaux + n) = u32x4{
+        pack_bf2(g[0], g[1]), pack_bf2(g[2], g[3]), pack_bf2(g[4], g[5]), pack_bf2(g[6], g[7])};
   } else if constexpr (EPI == GPT_EPI_RESIDUAL) {
     float4 r0 = *(const float4*)(e.resid + o), r1 = *(const float4*)(e.resid + o + 4);
     *(float4*)((float*)e.out + o) = make_float4(r0.x + x[0], r0.y + x[1], r0.z + x[2], r0.w + x[3]);
@@ -388,10 +424,12 @@ MfmaKernel mfma_kernel_for(int at, int bt, int epi, int ga, int gb) {
   K_(0, 0, GPT_EPI_RESIDUAL, 1, 0)
   K_(0, 0, GPT_EPI_GELU, 0, 0)
   K_(0, 0, GPT_EPI_DGELU, 0, 0)
+  K_(0, 0, GPT_EPI_GELU_PAIR, 0, 0)
   K_(0, 0, GPT_EPI_F32, 0, 0)
   K_(0, 0, GPT_EPI_F32_ACCUM, 0, 0)
   K_(0, 1, GPT_EPI_STORE, 0, 0)
   K_(0, 1, GPT_EPI_DGELU, 0, 0)
+  K_(0, 1, GPT_EPI_MUL, 0, 0)
   K_(0, 1, GPT_EPI_F32, 0, 0)
   K_(1, 1, GPT_EPI_F32, 0, 0)
   K_(1, 1, GPT_EPI_F32_ACCUM, 0, 0)
@@ -559,10 +597,12 @@ MfmaKernel dma_kernel_for(int at, int bt, int epi, int ga, int gb) {
   K_(0, 0, GPT_EPI_RESIDUAL)
   K_(0, 0, GPT_EPI_GELU)
   K_(0, 0, GPT_EPI_DGELU)
+  K_(0, 0, GPT_EPI_GELU_PAIR)
   K_(0, 0, GPT_EPI_F32)
   K_(0, 0, GPT_EPI_F32_ACCUM)
   K_(0, 1, GPT_EPI_STORE)
   K_(0, 1, GPT_EPI_DGELU)
+  K_(0, 1, GPT_EPI_MUL)
   K_(0, 1, GPT_EPI_F32)
   K_(0, 1, EPI_PARTIAL)
   K_(1, 1, GPT_EPI_F32)
@@ -661,6 +701,24 @@ __device__ __forceinline__ void epilogue4(const EpiArgs& e, float* partial, int 
     v.z *= gelu_grad_fast(bf_lo(u.y), e.tanh_form);
     v.w *= gelu_grad_fast(bf_hi(u.y), e.tanh_form);
     *(uint2*)((bf16_t*)e.out + o) = make_uint2(pack_bf2(v.x, v.y), pack_bf2(v.z, v.w));
+  } else if constexpr (EPI == GPT_EPI_MUL) {
+    const uint2 a = *(const uint2*)((const bf16_t*)e.aux + (long)m * e.ldaux + n);
+    *(uint2*)((bf16_t*)e.out + o) = make_uint2(pack_bf2(v.x * bf_lo(a.x), v.y * bf_hi(a.x)),
+                                               pack_bf2(v.z * bf_lo(a.y), v.w * bf_hi(a.y)));
+  } else if constexpr (EPI == GPT_EPI_GELU_PAIR) {
+    if (e.bias) {
+      const float4 b = *(const float4*)(e.bias + n);
+      v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
+    }
+    const uint2 w = make_uint2(pack_bf2(v.x, v.y), pack_bf2(v.z, v.w));
+    float g0, g1, g2, g3, p0, p1, p2, p3;
+    gelu_pair_fast(bf_lo(w.x), e.tanh_form, g0, p0);
+    gelu_pair_fast(bf_hi(w.x), e.tanh_form, g1, p1);
+    gelu_pair_fast(bf_lo(w.y), e.tanh_form, g2, p2);
+    gelu_pair_fast(bf_hi(w.y), e.tanh_form, g3, p3);
+    *(uint2*)((bf16_t*)e.out + o) = make_uint2(pack_bf2(p0, p1), pack_bf2(p2, p3));
+    *(uint2*)((bf16_t*)e.aux + (long)m * e.ldaux + n) =
+        make_uint2(pack_bf2(g0, g1), pack_bf2(g2, g3));
   } else if constexpr (EPI == GPT_EPI_RESIDUAL) {
     const float4 r = *(const float4*)(e.resid + o);
     *(float4*)((float*)e.out + o) = make_float4(r.x + v.x, r.y + v.y, r.z + v.z, r.w + v.w);
@@ -778,10 +836,12 @@ MfmaKernel big_kernel_for(int at, int bt, int epi, int ga, int gb) {
   K_(0, 0, GPT_EPI_RESIDUAL)
   K_(0, 0, GPT_EPI_GELU)
   K_(0, 0, GPT_EPI_DGELU)
+  K_(0, 0, GPT_EPI_GELU_PAIR)
   K_(0, 0, GPT_EPI_F32)
   K_(0, 0, GPT_EPI_F32_ACCUM)
   K_(0, 1, GPT_EPI_STORE)
   K_(0, 1, GPT_EPI_DGELU)
+  K_(0, 1, GPT_EPI_MUL)
   K_(0, 1, GPT_EPI_F32)
   K_(0, 1, EPI_PARTIAL)
   K_(1, 1, GPT_EPI_F32)

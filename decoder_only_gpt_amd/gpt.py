@@ -20,7 +20,7 @@ GPT_MAX_LAYERS = 128
 OK, E_INVALID, E_STATE, E_HIP, E_NONFINITE, E_UNSUPPORTED = range(6)
 FP32, BF16 = 0, 1
 BUF_PARAMS, BUF_GRADS, BUF_ADAM_M, BUF_ADAM_V, BUF_LOSS_ROWS = range(5)
-EPI_STORE, EPI_RESIDUAL, EPI_GELU, EPI_DGELU, EPI_F32, EPI_F32_ACCUM = range(6)
+EPI_STORE, EPI_RESIDUAL, EPI_GELU, EPI_DGELU, EPI_F32, EPI_F32_ACCUM, EPI_GELU_PAIR, EPI_MUL = range(8)
 
 # Every symbol include/gpt.h declares.
 EXPORTS = [

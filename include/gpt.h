@@ -225,7 +225,10 @@ typedef enum gpt_epilogue {
   GPT_EPI_GELU = 2,       /* out(act)  = u = acc [+ bias]; aux(act) = GELU(u) if aux */
   GPT_EPI_DGELU = 3,      /* out(act)  = acc * GELU'(aux[m, n])                     */
   GPT_EPI_F32 = 4,        /* out(f32)  = acc                                        */
-  GPT_EPI_F32_ACCUM = 5   /* out(f32) += acc                                        */
+  GPT_EPI_F32_ACCUM = 5,  /* out(f32) += acc                                        */
+  GPT_EPI_GELU_PAIR = 6,  /* u = acc [+ bias] rounded to act; out(act) = GELU'(u),
+                             aux(act) = GELU(u) (aux required)                       */
+  GPT_EPI_MUL = 7         /* out(act)  = acc * aux[m, n] (aux required)             */
 } gpt_epilogue;
 
 /* One matrix product, nanoGPT Linear convention (y = x W^T).  Operand X (A or

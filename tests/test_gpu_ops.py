@@ -102,7 +102,7 @@ def test_gemm_layouts(prec, M, N, K, at, bt):
 
 @pytest.mark.parametrize("prec", [gpt.FP32, gpt.BF16])
 @pytest.mark.parametrize("epi", [gpt.EPI_STORE, gpt.EPI_RESIDUAL, gpt.EPI_GELU, gpt.EPI_DGELU,
-                                 gpt.EPI_F32_ACCUM])
+                                 gpt.EPI_F32_ACCUM, gpt.EPI_GELU_PAIR, gpt.EPI_MUL])
 @pytest.mark.parametrize("tanh_form", [0, 1])
 def test_gemm_epilogues(prec, epi, tanh_form):
     dt = torch.bfloat16 if prec == gpt.BF16 else torch.float32
@@ -126,13 +126,13 @@ def test_gemm_epilogues(prec, epi, tanh_form):
                      out=out.data_ptr(), ldo=N)
     bx = bias.cpu().numpy().astype(np.float64)
     rx = resid.cpu().numpy().astype(np.float64)
-    if epi in (gpt.EPI_STORE, gpt.EPI_GELU, gpt.EPI_RESIDUAL):
+    if epi in (gpt.EPI_STORE, gpt.EPI_GELU, gpt.EPI_RESIDUAL, gpt.EPI_GELU_PAIR):
         d.bias = bias.data_ptr()
     if epi == gpt.EPI_RESIDUAL:
         d.resid = resid.data_ptr()
-    if epi == gpt.EPI_GELU:
+    if epi in (gpt.EPI_GELU, gpt.EPI_GELU_PAIR):
         d.aux, d.ldaux = aux.data_ptr(), N
-    if epi == gpt.EPI_DGELU:
+    if epi in (gpt.EPI_DGELU, gpt.EPI_MUL):
         d.aux, d.ldaux = aux_in.data_ptr(), N
     gpt.op_gemm(d)
     torch.cuda.synchronize()
@@ -151,6 +151,17 @@ def test_gemm_epilogues(prec, epi, tanh_form):
         assert g_err < (1e-2 if prec == gpt.BF16 else 1e-6)
     elif epi == gpt.EPI_DGELU:
         ref = acc * oracle.gelu_grad(rounded(aux_in), tanh_form)
+    elif epi == gpt.EPI_MUL:
+        ref = acc * rounded(aux_in)
+    elif epi == gpt.EPI_GELU_PAIR:
+        # u = acc + bias rounded to the activation type; out = GELU'(u), aux = GELU(u)
+        u = acc + bx
+        if prec == gpt.BF16:
+            u = oracle.bf16_round(u.astype(np.float32)).astype(np.float64)
+        ref = oracle.gelu_grad(u, tanh_form)
+        g_ref = oracle.gelu(u, tanh_form)
+        g_err = np.abs(rounded(aux) - g_ref).max() / np.abs(g_ref).max()
+        assert g_err < (1e-2 if prec == gpt.BF16 else 1e-5), g_err
     else:
         ref = rx + acc
     err = np.abs(got - ref).max() / np.abs(ref).max()
