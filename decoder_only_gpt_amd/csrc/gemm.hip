@@ -509,10 +509,12 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, const OpArgs
 template <int AT, int BT, int EPI>
 __global__ void __launch_bounds__(256, 2) gemm_dma_kernel(OpArgs A, OpArgs B, int K, int kchunk,
                                                           EpiArgs e, float* partial) {
-  __shared__ __attribute__((aligned(16))) bf16_t sA0[BM * BK];
-  __shared__ __attribute__((aligned(16))) bf16_t sB0[BN * BK];
-  __shared__ __attribute__((aligned(16))) bf16_t sA1[BM * BK];
-  __shared__ __attribute__((aligned(16))) bf16_t sB1[BN * BK];
+  // One 64 KB block: two stages of A and B tiles, later the float output tile.
+  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * (BM + BN) * BK];
+  bf16_t* const sA0 = smem;
+  bf16_t* const sB0 = smem + BM * BK;
+  bf16_t* const sA1 = smem + (BM + BN) * BK;
+  bf16_t* const sB1 = smem + (2 * BM + BN) * BK;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   int tx, ty, tz;
@@ -561,8 +563,8 @@ __global__ void __launch_bounds__(256, 2) gemm_dma_kernel(OpArgs A, OpArgs B, in
   __builtin_amdgcn_s_waitcnt(0x3f70);
   __syncthreads();
 
-  // Accumulators -> LDS float tile [128][128] (all four stage buffers, 64 KB).
-  float* Cs = (float*)sA0;
+  // Accumulators -> LDS float tile [128][128] (the whole 64 KB block).
+  float* Cs = (float*)smem;
   {
     const int frow = lane & 31, fg = lane >> 5;
     const int rb = wm * 64 + 4 * fg, cb = wn * 64 + frow;
@@ -735,10 +737,12 @@ __device__ __forceinline__ void epilogue4(const EpiArgs& e, float* partial, int 
 template <int AT, int BT, int EPI>
 __global__ void __launch_bounds__(256, 1) gemm_big_kernel(OpArgs A, OpArgs B, int K, int kchunk,
                                                           EpiArgs e, float* partial) {
-  __shared__ __attribute__((aligned(16))) bf16_t sA0[BIG * BK];
-  __shared__ __attribute__((aligned(16))) bf16_t sB0[BIG * BK];
-  __shared__ __attribute__((aligned(16))) bf16_t sA1[BIG * BK];
-  __shared__ __attribute__((aligned(16))) bf16_t sB1[BIG * BK];
+  // One 128 KB block: two stages of A and B tiles, later the epilogue slices.
+  __shared__ __attribute__((aligned(16))) bf16_t smem[4 * BIG * BK];
+  bf16_t* const sA0 = smem;
+  bf16_t* const sB0 = smem + BIG * BK;
+  bf16_t* const sA1 = smem + 2 * BIG * BK;
+  bf16_t* const sB1 = smem + 3 * BIG * BK;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   int tx, ty, tz;
@@ -800,7 +804,7 @@ __global__ void __launch_bounds__(256, 1) gemm_big_kernel(OpArgs A, OpArgs B, in
   // m = lane % 32, register r holds n = 8 (r / 4) + 4 (lane / 32) + r % 4.
   constexpr int CP = 132;  // padded row pitch (floats)
   __syncthreads();         // every wave is done reading the operand tiles
-  float* Cw = (float*)((wave & 2) ? sB0 : sA0) + (wave & 1) * (32 * CP);
+  float* Cw = (float*)smem + wave * (32 * CP);  // 4 slices of 16.5 KB (66 KB of the 128 KB)
   const int m_l = lane & 31, nq = 4 * (lane >> 5);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -826,6 +830,154 @@ __global__ void __launch_bounds__(256, 1) gemm_big_kernel(OpArgs A, OpArgs B, in
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next block overwrites
   }
+}
+
+// ----------------------------------------------------------------------------
+// bf16 MFMA, 256 x 256 tile with 8 waves (2 along M x 4 along N, 128 x 64
+// each): two waves per SIMD, so one wave's LDS reads and load waits hide
+// behind the other's MFMAs, at 1.5x the LDS reads per FLOP of the 4-wave
+// layout.  BK = 64, two 64 KB LDS stages filled by direct buffer loads (four
+// 1 KB blocks per wave and operand per stage); the epilogue stages each
+// wave's 32-row slices through LDS for 16-byte vector stores.
+// ----------------------------------------------------------------------------
+template <int TRANS>
+__device__ __forceinline__ void dma_tile256_w8(__amdgpu_buffer_rsrc_t rs, const OpArgs& a, int r0,
+                                               int k0, bf16_t* lds, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int blk = wave * 4 + i;  // 1 KB block of the 32 KB tile
+    int r, k;
+    if constexpr (TRANS == 0) {  // block = 8 rows x 8 chunks
+      const int row = blk * 8 + (lane >> 3), phys = lane & 7;
+      const int chunk = phys ^ (row & 7) ^ ((row >> 3) & 1);
+      r = r0 + row;
+      k = k0 + chunk * 8;
+    } else {  // block = 2 k-rows x 32 chunks
+      const int kk = blk * 2 + (lane >> 5), phys = lane & 31;
+      const int chunk = phys ^ ((kk & 3) << 2);
+      k = k0 + kk;
+      r = r0 + chunk * 8;
+    }
+    const bool ok = r < a.rows && k < a.kvalid;
+    const long e = TRANS ? (long)k * a.ld + r : (long)r * a.ld + k;
+    const unsigned off = ok ? (unsigned)(e * 2) : 0x80000000u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + blk * 512), 16, off, 0, 0, 0);
+  }
+}
+
+template <int AT, int BT, int EPI>
+__global__ void __launch_bounds__(512, 1) gemm_big8_kernel(OpArgs A, OpArgs B, int K, int kchunk,
+                                                           EpiArgs e, float* partial) {
+  // One 128 KB block: two stages of A and B tiles, later the epilogue slices.
+  __shared__ __attribute__((aligned(16))) bf16_t smem[4 * BIG * BK];
+  bf16_t* const sA0 = smem;
+  bf16_t* const sB0 = smem + BIG * BK;
+  bf16_t* const sA1 = smem + 2 * BIG * BK;
+  bf16_t* const sB1 = smem + 3 * BIG * BK;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 2, wn = wave & 3;  // rows wm * 128 .., columns wn * 64 ..
+  int tx, ty, tz;
+  xcd_tile(tx, ty, tz);
+  const int m0 = ty * BIG, n0 = tx * BIG;
+  const int kbeg = tz * kchunk;
+  if (EPI == EPI_PARTIAL) partial += (long)tz * e.M * e.N;
+  const int kend = min(K, kbeg + kchunk);
+  const int nk = (kend - kbeg + BK - 1) / BK;
+
+  OpArgs a = A, b = B;
+  a.kvalid = min(a.kvalid, kend);
+  b.kvalid = min(b.kvalid, kend);
+  const long a_extent = AT ? (long)a.kvalid * a.ld : (long)a.rows * a.ld;
+  const long b_extent = BT ? (long)b.kvalid * b.ld : (long)b.rows * b.ld;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.X, a_extent * 2);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(b.X, b_extent * 2);
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  dma_tile256_w8<AT>(ra, a, m0, kbeg, sA0, wave, lane);
+  dma_tile256_w8<BT>(rb, b, n0, kbeg, sB0, wave, lane);
+  for (int kt = 0; kt < nk; ++kt) {
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's loads of tile kt landed
+    __syncthreads();                     // ... and every other wave's
+    const bool odd = kt & 1;
+    if (kt + 1 < nk) {
+      const int k1 = kbeg + (kt + 1) * BK;
+      dma_tile256_w8<AT>(ra, a, m0, k1, odd ? sA0 : sA1, wave, lane);
+      dma_tile256_w8<BT>(rb, b, n0, k1, odd ? sB0 : sB1, wave, lane);
+    }
+    const bf16_t* as = odd ? sA1 : sA0;
+    const bf16_t* bs = odd ? sB1 : sB0;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 af[4], bf[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = big_frag<AT>(as, wm * 128 + i * 32, ks, lane);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bf[j] = big_frag<BT>(bs, wn * 64 + j * 32, ks, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // Epilogue, one 32-row block of the wave's 128 x 64 tile at a time:
+  // accumulators -> this wave's LDS slice as floats [32][CP], then each lane
+  // applies the epilogue to 8 consecutive columns.  acc[i][j] = D[n][m]: lane
+  // column m = lane % 32, register r holds n = 8 (r / 4) + 4 (lane / 32) + r % 4.
+  constexpr int CP = 68;  // padded row pitch (floats)
+  __syncthreads();        // every wave is done reading the operand tiles
+  float* Cw = (float*)smem + wave * (32 * CP);  // 8 slices of 8.5 KB (68 KB of the 128 KB)
+  const int m_l = lane & 31, nq = 4 * (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(float4*)(Cw + m_l * CP + j * 32 + 8 * q + nq) =
+            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                        acc[i][j][4 * q + 3]);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+    const int cg = lane & 7;
+    const int n = n0 + wn * 64 + cg * 8;
+#pragma unroll 1
+    for (int p = 0; p < 4; ++p) {
+      const int row = p * 8 + (lane >> 3);
+      const int m = m0 + wm * 128 + i * 32 + row;
+      if (m < e.M && n < e.N) {
+        const float4 v0 = *(const float4*)(Cw + row * CP + cg * 8);
+        const float4 v1 = *(const float4*)(Cw + row * CP + cg * 8 + 4);
+        epilogue8<EPI>(e, partial, m, n, v0, v1);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next block overwrites
+  }
+}
+
+MfmaKernel big8_kernel_for(int at, int bt, int epi, int ga, int gb) {
+  if (ga || gb) return nullptr;
+#define K_(AT, BT, EP) \
+  if (at == AT && bt == BT && epi == EP) return gemm_big8_kernel<AT, BT, EP>;
+  K_(0, 0, GPT_EPI_STORE)
+  K_(0, 0, GPT_EPI_RESIDUAL)
+  K_(0, 0, GPT_EPI_GELU)
+  K_(0, 0, GPT_EPI_GELU_PAIR)
+  K_(0, 0, GPT_EPI_F32)
+  K_(0, 1, GPT_EPI_STORE)
+  K_(0, 1, GPT_EPI_DGELU)
+  K_(0, 1, GPT_EPI_MUL)
+  K_(0, 1, EPI_PARTIAL)
+  K_(1, 1, GPT_EPI_F32)
+  K_(1, 1, GPT_EPI_F32_ACCUM)
+  K_(1, 1, EPI_PARTIAL)
+#undef K_
+  return nullptr;
 }
 
 MfmaKernel big_kernel_for(int at, int bt, int epi, int ga, int gb) {
@@ -866,6 +1018,12 @@ struct GemmPlan {
   bool big;  // 256 x 256 tiles
   int S;     // K splits (1 = none)
 };
+
+// Tuning switch: GPT_GEMM_BIG4=1 runs the 4-wave large-tile kernel instead.
+bool big8_disabled() {
+  static bool v = getenv("GPT_GEMM_BIG4") != nullptr;
+  return v;
+}
 
 // Tile override for tuning: GPT_GEMM_TILE=128 or 256 (unset: automatic).
 int tile_override() {
@@ -1005,14 +1163,22 @@ hipError_t gemm(const gpt_gemm_desc& d, hipStream_t s) {
     gemm_simt_kernel<bf16_t, bf16_t><<<grid, 256, 0, s>>>(A, B, d.K, e);
     return hipGetLastError();
   }
+  int threads = 256;
+  if (plan.big && vec_ok) {  // the 8-wave large-tile kernel where it has the combination
+    MfmaKernel k8 = big8_kernel_for(d.a_trans, d.b_trans, epi, d.a_gelu, d.b_gelu);
+    if (k8 && !big8_disabled()) {
+      kern = k8;
+      threads = 512;
+    }
+  }
   const int T = plan.big ? BIG : BM;
   dim3 grid((unsigned)cdiv(d.N, T), (unsigned)cdiv(d.M, T), (unsigned)S);
   if (S == 1) {
-    kern<<<grid, 256, 0, s>>>(A, B, d.K, d.K, e, nullptr);
+    kern<<<grid, threads, 0, s>>>(A, B, d.K, d.K, e, nullptr);
     return hipGetLastError();
   }
   const int kchunk = (int)cdiv(cdiv(d.K, plan.S), BK) * BK;
-  kern<<<grid, 256, 0, s>>>(A, B, d.K, kchunk, e, (float*)d.workspace);
+  kern<<<grid, threads, 0, s>>>(A, B, d.K, kchunk, e, (float*)d.workspace);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   long total = (long)d.M * d.N;
