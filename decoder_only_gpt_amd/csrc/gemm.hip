@@ -1077,6 +1077,17 @@ GemmPlan plan_gemm(int M, int N, int K, int precision, bool splittable, int64_t 
       p.big = true;
       return p;
     }
+    // Otherwise 256-tiles (one workgroup per CU) when they fill the rounds of
+    // the 256 CUs at least as evenly as 128-tiles (two workgroups per CU) do.
+    if (!splittable && t256 >= 128) {
+      const long t128 = cdiv(M, BM) * cdiv(N, BN);
+      const double f256 = (double)t256 / (256.0 * cdiv(t256, 256));
+      const double f128 = (double)t128 / (512.0 * cdiv(t128, 512));
+      if (f256 + 1e-9 >= f128) {
+        p.big = true;
+        return p;
+      }
+    }
   }
   int S = splittable ? choose_split(M, N, K) : 1;
   if (S > 1 && ws_bytes < (int64_t)S * M * N * 4) S = 1;
