@@ -30,8 +30,9 @@ METRIC = "training tokens/sec on 1 GPU + MFU vs bf16 MFMA peak, GPT-2 124M shape
 
 
 # Call sites that launch exactly one kernel (see gpt_site in include/gpt.h).
+# (lmhead_dx is split over K: a GEMM plus the fixed-order reduction.)
 SINGLE_KERNEL_SITES = ["embed_fwd", "ln_fwd", "qkv_fwd", "attn_fwd", "proj_fwd", "fc_fwd",
-                       "fcproj_fwd", "lmhead_fwd", "lmhead_dx", "lmhead_dw", "fcproj_dx", "fc_dx",
+                       "fcproj_fwd", "lmhead_fwd", "lmhead_dw", "fcproj_dx", "fc_dx",
                        "proj_dx", "qkv_dx", "adamw"]
 
 

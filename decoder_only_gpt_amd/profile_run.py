@@ -36,7 +36,10 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def run_step(config: str, steps: int):
+def run_step(config: str, steps: int, concurrent: bool = False):
+    """A few training steps.  Unless `concurrent`, inside a kernel-timing window,
+    which keeps every kernel on one stream (as the benchmark's per-kernel pass
+    does), so a trace times each kernel alone."""
     import torch
     from decoder_only_gpt_amd import gpt, presets, synth
     cfg = presets.preset(config)
@@ -45,9 +48,13 @@ def run_step(config: str, steps: int):
     idx, tgt = synth.tokens(cfg, seed=1)
     di = torch.from_numpy(idx.reshape(-1)).cuda()
     dt = torch.from_numpy(tgt.reshape(-1)).cuda()
+    if not concurrent:
+        m.profile_begin()
     for i in range(steps):
         r = m.train_step(di, dt)
         print(f"step {i} loss {r['loss']:.4f}", flush=True)
+    if not concurrent:
+        m.profile_end()
     torch.cuda.synchronize()
 
 
@@ -116,6 +123,8 @@ def main():
     p = sub.add_parser("step")
     p.add_argument("--config", default="gpt2_124m")
     p.add_argument("--steps", type=int, default=3)
+    p.add_argument("--concurrent", action="store_true",
+                   help="weight gradients on their side stream, as in training")
     p = sub.add_parser("copy")
     p.add_argument("--mib", type=int, default=1024)
     p = sub.add_parser("summarize-stats")
@@ -136,7 +145,7 @@ def main():
     a = ap.parse_args()
     if a.cmd == "step":
         sys.path.insert(0, ROOT)
-        run_step(a.config, a.steps)
+        run_step(a.config, a.steps, a.concurrent)
     elif a.cmd == "copy":
         run_copy(a.mib)
     elif a.cmd == "summarize-stats":
