@@ -411,6 +411,26 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* partial
   }
 }
 
+// Split-K reduction, 8 consecutive columns per thread (N % 8 == 0, 16-byte
+// aligned rows): partials summed in z order, then the vector epilogue.
+template <int EPI>
+__global__ void __launch_bounds__(256) splitk_reduce8_kernel(const float* __restrict__ partial,
+                                                             int S, EpiArgs e) {
+  const long per_row = e.N / 8, total = (long)e.M * per_row;
+  const long plane = (long)e.M * e.N;
+  for (long i = blockIdx.x * 256L + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
+    const int m = (int)(i / per_row), n = (int)(i % per_row) * 8;
+    const float* p = partial + (long)m * e.N + n;
+    float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+    for (int z = 1; z < S; ++z) {
+      const float4 c = *(const float4*)(p + z * plane), d = *(const float4*)(p + z * plane + 4);
+      a.x += c.x; a.y += c.y; a.z += c.z; a.w += c.w;
+      b.x += d.x; b.y += d.y; b.z += d.z; b.w += d.w;
+    }
+    epilogue8<EPI>(e, nullptr, m, n, a, b);
+  }
+}
+
 typedef void (*MfmaKernel)(OpArgs, OpArgs, int, int, EpiArgs, float*);
 
 // The specialisations the training step uses; anything else takes the
@@ -1193,8 +1213,20 @@ hipError_t gemm(const gpt_gemm_desc& d, hipStream_t s) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   long total = (long)d.M * d.N;
+  const float* ws = (const float*)d.workspace;
+  if (vec_ok && (d.epilogue == GPT_EPI_F32 || d.epilogue == GPT_EPI_F32_ACCUM ||
+                 d.epilogue == GPT_EPI_STORE)) {
+    const unsigned blocks = (unsigned)std::min<long>(cdiv(total / 8, 256), 4096);
+    if (d.epilogue == GPT_EPI_F32)
+      splitk_reduce8_kernel<GPT_EPI_F32><<<blocks, 256, 0, s>>>(ws, S, e);
+    else if (d.epilogue == GPT_EPI_F32_ACCUM)
+      splitk_reduce8_kernel<GPT_EPI_F32_ACCUM><<<blocks, 256, 0, s>>>(ws, S, e);
+    else
+      splitk_reduce8_kernel<GPT_EPI_STORE><<<blocks, 256, 0, s>>>(ws, S, e);
+    return hipGetLastError();
+  }
   unsigned blocks = (unsigned)std::min<long>(cdiv(total, 256), 4096);
-  splitk_reduce_kernel<bf16_t><<<blocks, 256, 0, s>>>((const float*)d.workspace, S, e);
+  splitk_reduce_kernel<bf16_t><<<blocks, 256, 0, s>>>(ws, S, e);
   return hipGetLastError();
 }
 
