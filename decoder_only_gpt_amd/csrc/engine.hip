@@ -237,6 +237,10 @@ struct gpt_model {
   hipStream_t side = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   hipEvent_t ev_buf[3 * NGB] = {};  // last side-stream read of gact[], dF[], dqkv[]
+  // AdamW runs on the side stream in parameter groups (embeddings, each layer,
+  // the final LayerNorm and untied head); the next forward waits per group.
+  std::vector<hipEvent_t> ev_adam;
+  bool adam_pending = false;
 
   template <typename T_> T_* at(int64_t off) const { return off < 0 ? nullptr : (T_*)(base + off); }
   float* P(int64_t e) const { return e < 0 ? nullptr : at<float>(ar.params) + e; }
@@ -340,6 +344,30 @@ double attn_pairs(int T, int left) {
   return n;
 }
 
+// Parameter group g of the flat vector: 0 = embeddings, 1..L = layers,
+// L + 1 = final LayerNorm and untied head.  Returns [begin, end).
+void adam_group(const gpt_model* m, int g, int64_t* b, int64_t* e) {
+  const int L = m->cfg.n_layer;
+  auto start = [&](int k) -> int64_t {
+    if (k == 0) return 0;
+    if (k <= L) return m->pl.layer[k - 1].ln1w;
+    if (k == L + 1) return m->pl.lnfw;
+    return m->N;
+  };
+  *b = start(g);
+  *e = start(g + 1);
+}
+
+// Make stream s wait for the side-stream AdamW of group g (all groups: g < 0).
+int wait_adam(gpt_model* m, hipStream_t s, int g) {
+  if (!m->adam_pending) return GPT_OK;
+  const int idx = g < 0 ? (int)m->ev_adam.size() - 1 : g;
+  hipError_t e = hipStreamWaitEvent(s, m->ev_adam[idx], 0);
+  if (e != hipSuccess) return fail(GPT_E_HIP, std::string("hipStreamWaitEvent: ") + hipGetErrorString(e));
+  if (g < 0) m->adam_pending = false;
+  return GPT_OK;
+}
+
 int run_forward(gpt_model* m, const int32_t* idx, const int32_t* tgt, hipStream_t s) {
   const gpt_config& c = m->cfg;
   const int prec = m->prec();
@@ -348,10 +376,13 @@ int run_forward(gpt_model* m, const int32_t* idx, const int32_t* tgt, hipStream_
   const double ln_fwd_bytes = M * C * (4.0 + act_b) + 8.0 * M;
   const double attn_flops = 4.0 * m->hd * m->B * m->H;
   auto act = [&](int64_t off) { return m->at<char>(off); };
+  int rc = wait_adam(m, s, 0);
+  if (rc != GPT_OK) return rc;
   LAUNCH(GPT_K_EMBED, GPT_S_EMBED_FWD, 0, 12.0 * M * C,
          gpt::embed_fwd(prec, idx, m->P(m->pl.wte), m->P(m->pl.wpe), (int)M, m->T, (int)C, m->X(0), s));
   for (int l = 0; l < c.n_layer; ++l) {
     const LayerOff& L = m->pl.layer[l];
+    if ((rc = wait_adam(m, s, 1 + l)) != GPT_OK) return rc;
     LAUNCH(GPT_K_LAYERNORM, GPT_S_LN_FWD, 0, ln_fwd_bytes,
            gpt::layernorm_fwd(prec, m->X(2 * l), m->P(L.ln1w), m->P(L.ln1b), (int)M, (int)C,
                               c.ln_eps, act(m->ar.a1[l]), m->mean(2 * l), m->rstd(2 * l), s));
@@ -386,6 +417,7 @@ int run_forward(gpt_model* m, const int32_t* idx, const int32_t* tgt, hipStream_
     GEMM(d, GPT_S_FCPROJ_FWD);
   }
   const int64_t nl = 2 * c.n_layer;
+  if ((rc = wait_adam(m, s, -1)) != GPT_OK) return rc;  // the last group: all are done
   LAUNCH(GPT_K_LAYERNORM, GPT_S_LN_FWD, 0, ln_fwd_bytes,
          gpt::layernorm_fwd(prec, m->X(nl), m->P(m->pl.lnfw), m->P(m->pl.lnfb), (int)M, (int)C,
                             c.ln_eps, act(m->ar.xf), m->mean(nl), m->rstd(nl), s));
@@ -642,6 +674,11 @@ int gpt_init(const gpt_config* cfg, int32_t B, int32_t T, void* d_arena, int64_t
   if (se == hipSuccess) se = hipEventCreateWithFlags(&m->ev_join, hipEventDisableTiming);
   for (int i = 0; i < 3 * NGB && se == hipSuccess; ++i)
     se = hipEventCreateWithFlags(&m->ev_buf[i], hipEventDisableTiming);
+  for (int i = 0; i < cfg->n_layer + 2 && se == hipSuccess; ++i) {
+    hipEvent_t ev = nullptr;
+    se = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (se == hipSuccess) m->ev_adam.push_back(ev);
+  }
   if (se != hipSuccess) {
     gpt_destroy(m);
     return fail(GPT_E_HIP, std::string("side stream: ") + hipGetErrorString(se));
@@ -665,6 +702,8 @@ int gpt_destroy(gpt_model* m) {
       if (e) (void)hipEventDestroy(e);
     for (hipEvent_t e : m->ev_buf)
       if (e) (void)hipEventDestroy(e);
+    if (m->side) (void)hipStreamSynchronize(m->side);
+    for (hipEvent_t e : m->ev_adam) (void)hipEventDestroy(e);
     if (m->side) (void)hipStreamDestroy(m->side);
   }
   delete m;
@@ -731,9 +770,27 @@ int gpt_adamw_step(gpt_model* m, const gpt_adamw_hp* hp, void* stream) {
   if (rc != GPT_OK) return rc;
   if (m->state != 2) return fail(GPT_E_STATE, "adamw_step needs a backward first");
   hipStream_t s = (hipStream_t)stream;
-  LAUNCH(GPT_K_ADAMW, GPT_S_ADAMW, 0, (m->bf16 ? 30.0 : 28.0) * m->N,
-         gpt::adamw(m->N, m->P(0), m->at<float>(m->ar.adam_m), m->at<float>(m->ar.adam_v), m->G(0),
-                    m->bf16 ? m->at<uint16_t>(m->ar.shadow) : nullptr, adam_scalars(*hp), s));
+  float* pm = m->at<float>(m->ar.adam_m);
+  float* pv = m->at<float>(m->ar.adam_v);
+  uint16_t* sh = m->bf16 ? m->at<uint16_t>(m->ar.shadow) : nullptr;
+  const gpt::AdamScalars sc = adam_scalars(*hp);
+  if (m->prof_on) {  // timed alone, in one launch
+    LAUNCH(GPT_K_ADAMW, GPT_S_ADAMW, 0, (m->bf16 ? 30.0 : 28.0) * m->N,
+           gpt::adamw(m->N, m->P(0), pm, pv, m->G(0), sh, sc, s));
+  } else {
+    // On the side stream, group by group; the next forward waits for each
+    // group just before it uses those parameters.
+    HIP_TRY(hipEventRecord(m->ev_fork, s));
+    HIP_TRY(hipStreamWaitEvent(m->side, m->ev_fork, 0));
+    for (int g = 0; g < (int)m->ev_adam.size(); ++g) {
+      int64_t b, e;
+      adam_group(m, g, &b, &e);
+      HIP_TRY(gpt::adamw(e - b, m->P(b), pm + b, pv + b, m->G(b), sh ? sh + b : nullptr, sc,
+                         m->side));
+      HIP_TRY(hipEventRecord(m->ev_adam[g], m->side));
+    }
+    m->adam_pending = true;
+  }
   m->state = 0;
   m->loss_valid = false;
   return GPT_OK;
@@ -757,6 +814,7 @@ int gpt_get_buffer(gpt_model* m, int32_t which, void* dst, int32_t dst_on_device
   int rc = buffer_region(m, which, &p, &bytes);
   if (rc != GPT_OK) return rc;
   hipStream_t s = (hipStream_t)stream;
+  if ((rc = wait_adam(m, s, -1)) != GPT_OK) return rc;
   HIP_TRY(hipMemcpyAsync(dst, p, (size_t)bytes,
                          dst_on_device ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToHost, s));
   if (!dst_on_device) HIP_TRY(hipStreamSynchronize(s));
@@ -772,6 +830,7 @@ int gpt_set_buffer(gpt_model* m, int32_t which, const void* src, int32_t src_on_
   int rc = buffer_region(m, which, &p, &bytes);
   if (rc != GPT_OK) return rc;
   hipStream_t s = (hipStream_t)stream;
+  if ((rc = wait_adam(m, s, -1)) != GPT_OK) return rc;
   HIP_TRY(hipMemcpyAsync(p, src, (size_t)bytes,
                          src_on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, s));
   if (which == GPT_BUF_PARAMS && m->bf16)
