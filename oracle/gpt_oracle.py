@@ -43,7 +43,7 @@ __all__ = [
     "clip_scale", "adamw_scalars", "adamw_update", "bf16_round", "bf16_bits",
     "layernorm_fwd", "layernorm_bwd", "gelu", "gelu_grad", "attention_fwd",
     "attention_bwd", "cross_entropy_fwd_bwd", "visible", "step", "logits",
-    "loss_rows",
+    "loss_rows", "cosine_lr", "train_steps",
 ]
 
 
@@ -443,6 +443,50 @@ def bf16_bits(x) -> np.ndarray:
 def bf16_round(x) -> np.ndarray:
     """float32 values rounded to the nearest bfloat16 (returned as float32)."""
     return (bf16_bits(x).astype(np.uint32) << 16).view(np.float32)
+
+
+def cosine_lr(t: int, max_lr: float, min_lr: float, warmup: int, decay_steps: int) -> float:
+    """Learning rate of step t (1-based): a linear ramp to max_lr over `warmup`
+    steps, then half a cosine period down to min_lr at `decay_steps`, then
+    min_lr.  (Panthalia "Create a Plugin": helpers for cosine-annealed learning
+    rates; nanoGPT README, "quick start": the rate decays until lr_decay_iters.
+    The ramp and the half period are the plainest reading of "cosine annealing".)"""
+    if warmup > 0 and t <= warmup:
+        return max_lr * t / warmup
+    if t >= decay_steps:
+        return min_lr
+    r = (t - warmup) / (decay_steps - warmup)
+    return min_lr + 0.5 * (max_lr - min_lr) * (1.0 + math.cos(math.pi * r))
+
+
+def train_steps(cfg, flat_params, batches, lrs, dtype=np.float64):
+    """Several training steps with gradient accumulation (Panthalia "Create a
+    Plugin": accumulations per step x examples per accumulation).
+    batches[k] = list of (idx, tgt) micro-batches of step k + 1; lrs[k] its rate.
+    Per step: the micro-batch gradients (each of a mean loss) are summed; the
+    step's gradient is their mean, so AdamW gets grad_scale = clip / n where
+    clip is the global-norm factor of that mean.  Returns dict(losses =
+    per-step mean of the micro-batch losses, norms, p, m, v)."""
+    p = np.asarray(flat_params, np.float32)
+    m = np.zeros_like(p)
+    v = np.zeros_like(p)
+    losses, norms = [], []
+    for k, micro in enumerate(batches):
+        gsum = None
+        lsum = 0.0
+        for idx, tgt in micro:
+            loss, g = loss_and_grads(cfg, p, idx, tgt, dtype)
+            gsum = g if gsum is None else gsum + g
+            lsum += loss
+        n = len(micro)
+        norm = grad_norm(gsum) / n
+        scale = clip_scale(norm, cfg.get("clip", 0.0)) / n
+        s = adamw_scalars(lrs[k], cfg["beta1"], cfg["beta2"], cfg["eps"], cfg["weight_decay"],
+                          k + 1, scale)
+        p, m, v = adamw_update(p, m, v, gsum.astype(np.float32), s)
+        losses.append(lsum / n)
+        norms.append(norm)
+    return dict(losses=losses, norms=norms, p=p, m=m, v=v)
 
 
 def step(cfg, flat_params, m, v, idx, tgt, t: int, dtype=np.float64):

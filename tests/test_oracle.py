@@ -276,3 +276,67 @@ def test_loss_falls_toward_unigram_entropy():
     assert losses[0] > H + 0.7
     assert np.mean(losses[-5:]) < losses[0] - 0.5
     assert np.mean(losses[-5:]) > H - 0.2
+
+
+def test_cosine_lr_closed_form_points():
+    """Linear warm-up to the peak, half a cosine down to the floor, then the floor
+    (Panthalia "Create a Plugin": cosine-annealed rate; nanoGPT README, quick start:
+    decay until lr_decay_iters)."""
+    c = oracle.cosine_lr
+    assert c(1, 1e-3, 1e-4, 4, 12) == pytest.approx(2.5e-4, rel=1e-15)
+    assert c(4, 1e-3, 1e-4, 4, 12) == pytest.approx(1e-3, rel=1e-15)
+    assert c(8, 1e-3, 1e-4, 4, 12) == pytest.approx(5.5e-4, rel=1e-15)   # midpoint: mean
+    assert c(6, 1e-3, 1e-4, 4, 12) == pytest.approx(1e-4 + 9e-4 * (2 + 2 ** 0.5) / 4, rel=1e-14)
+    assert c(12, 1e-3, 1e-4, 4, 12) == pytest.approx(1e-4, rel=1e-15)
+    assert c(50, 1e-3, 1e-4, 4, 12) == 1e-4
+    assert c(1, 1e-3, 0.0, 0, 10) == pytest.approx(1e-3 * (1 + math.cos(math.pi / 10)) / 2)
+    lrs = [c(t, 1e-3, 1e-4, 4, 12) for t in range(1, 20)]
+    assert all(a < b for a, b in zip(lrs[:3], lrs[1:4]))           # rising during warm-up
+    assert all(a > b for a, b in zip(lrs[3:11], lrs[4:12]))        # strictly falling after
+
+
+def _split_rows(idx, tgt, n):
+    B = idx.shape[0]
+    k = B // n
+    return [(idx[i * k:(i + 1) * k], tgt[i * k:(i + 1) * k]) for i in range(n)]
+
+
+@pytest.mark.parametrize("clip", [0.0, 0.05])
+def test_accumulated_step_equals_one_big_batch(clip):
+    """Accumulating n equal micro-batches is one step on their concatenation: the
+    loss is a mean over equally many tokens, so the mean of the micro losses and
+    gradients is the big batch's loss and gradient, and clipping sees the same
+    norm (Panthalia "Create a Plugin": accumulations x examples per accumulation)."""
+    cfg = presets.preset("tiny", B=4, T=16, clip=clip)
+    p0 = synth.init_params(cfg, seed=11, perturb=True)
+    steps = []
+    p, m, v = p0, np.zeros_like(p0), np.zeros_like(p0)
+    for t in (1, 2):
+        idx, tgt = synth.tokens(cfg, seed=40 + t)
+        r = oracle.step(cfg, p, m, v, idx, tgt, t)
+        p, m, v = r["p"], r["m"], r["v"]
+        steps.append((r, idx, tgt))
+    acc = oracle.train_steps(cfg, p0, [_split_rows(i, g, 2) for _, i, g in steps],
+                             [cfg["lr"], cfg["lr"]])
+    for k, (r, _, _) in enumerate(steps):
+        assert acc["losses"][k] == pytest.approx(r["loss"], rel=1e-12)
+        assert acc["norms"][k] == pytest.approx(r["norm"], rel=1e-12)
+    if clip:
+        assert steps[0][0]["scale"] < 1.0  # the clipping branch really ran
+    assert np.abs(acc["p"] - p).max() <= 1e-7
+    assert np.abs(acc["m"] - m).max() <= 1e-9
+    assert np.abs(acc["v"] - v).max() <= 1e-12
+
+
+def test_train_steps_uses_each_steps_rate():
+    """A zero rate leaves parameters untouched (and leaves weight decay inert);
+    the moments still advance."""
+    cfg = presets.preset("tiny", B=2, T=16)
+    p0 = synth.init_params(cfg, seed=12, perturb=True)
+    batches = [[synth.tokens(cfg, seed=60 + j)] for j in range(2)]
+    r = oracle.train_steps(cfg, p0, batches, [0.0, 0.0])
+    assert np.array_equal(r["p"], p0)
+    assert np.abs(r["m"]).max() > 0
+    r1 = oracle.train_steps(cfg, p0, batches[:1], [cfg["lr"]])
+    ref = oracle.step(cfg, p0, np.zeros_like(p0), np.zeros_like(p0), *batches[0][0], 1)
+    assert np.array_equal(r1["p"], ref["p"])
