@@ -175,9 +175,9 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def adam_hp(cfg: dict, t: int, grad_scale: float = 1.0) -> AdamHP:
-    return AdamHP(cfg["lr"], cfg["beta1"], cfg["beta2"], cfg["eps"], cfg["weight_decay"],
-                  grad_scale, t)
+def adam_hp(cfg: dict, t: int, grad_scale: float = 1.0, lr: float | None = None) -> AdamHP:
+    return AdamHP(cfg["lr"] if lr is None else lr, cfg["beta1"], cfg["beta2"], cfg["eps"],
+                  cfg["weight_decay"], grad_scale, t)
 
 
 class Model:
@@ -252,8 +252,8 @@ class Model:
         _check(lib().gpt_grad_norm(self.h, _stream(), ctypes.byref(out)))
         return float(out.value)
 
-    def adamw_step(self, t: int, grad_scale: float = 1.0):
-        hp = adam_hp(self.cfg, t, grad_scale)
+    def adamw_step(self, t: int, grad_scale: float = 1.0, lr: float | None = None):
+        hp = adam_hp(self.cfg, t, grad_scale, lr)
         _check(lib().gpt_adamw_step(self.h, ctypes.byref(hp), _stream()))
 
     def profile_begin(self):
