@@ -43,7 +43,9 @@ __all__ = [
     "clip_scale", "adamw_scalars", "adamw_update", "bf16_round", "bf16_bits",
     "layernorm_fwd", "layernorm_bwd", "gelu", "gelu_grad", "attention_fwd",
     "attention_bwd", "cross_entropy_fwd_bwd", "visible", "step", "logits",
-    "loss_rows", "cosine_lr", "train_steps",
+    "loss_rows", "cosine_lr", "train_steps", "NS_COEFFS", "muon_matrices",
+    "orthogonalize", "muon_momentum", "muon_second_moment", "cautious_update",
+    "muon_matrix_update", "MuonHP", "muon_hybrid_step",
 ]
 
 
@@ -499,3 +501,151 @@ def step(cfg, flat_params, m, v, idx, tgt, t: int, dtype=np.float64):
                       t, scale)
     p1, m1, v1 = adamw_update(flat_params, m, v, g.astype(np.float32), s)
     return dict(loss=loss, grads=g, norm=norm, scale=scale, p=p1, m=m1, v=v1)
+
+
+# --------------------------------------------------------------------------
+# Muon for the 2-D block matrices, AdamW for the rest (nanochat
+# "Optimierungsstrategien Muon und AdamW")
+# --------------------------------------------------------------------------
+# The page's "Polar Express" listing iterates over a coefficient table that the
+# page does not print.  The plainest stand-in is the fixed quintic
+# Newton-Schulz polynomial of the original Muon optimizer (K. Jordan et al.,
+# "Muon: An optimizer for hidden layers in neural networks", 2024):
+# p(s) = a s + b s^3 + c s^5 with these (a, b, c) at every iteration.
+NS_COEFFS = (3.4445, -4.7750, 2.0315)
+
+
+def muon_matrices(cfg):
+    """Names of the tensors Muon updates: every per-layer Linear weight (attention
+    and MLP matrices).  Embeddings, the lm_head and 0-D/1-D tensors go to AdamW
+    (nanochat, "Verantwortlichkeiten und Design-Philosophie")."""
+    return [n for n, s in layout(cfg) if len(s) == 2 and n not in ("wte", "wpe", "lm_head.w")]
+
+
+def _r(x, bf16: bool):
+    """Round to bfloat16 when computing in bfloat16 (PyTorch semantics: every
+    op's result is stored in the tensor's dtype)."""
+    return bf16_round(np.asarray(x, np.float64)).astype(np.float64) if bf16 else x
+
+
+def orthogonalize(G, steps: int = 5, coeffs=NS_COEFFS, bf16: bool = True):
+    """The page's orthogonalization listing ("Polar Express Details"):
+    X = G in bf16; X /= ||X||_F * 1.01 + 1e-6; then `steps` times
+      tall (rows > cols): A = X^T X, B = b A + c A A, X = a X + X B;
+      otherwise (wide or square): A = X X^T, B = b A + c A A, X = a X + B X.
+    (The wide branch of the listing uses B without defining it; it is the same
+    polynomial in A as in the tall branch, which makes both branches apply
+    p(s) = a s + b s^3 + c s^5 to every singular value.)
+    With bf16=True every intermediate is rounded to bf16 as the listing's
+    bf16 tensors would be; with bf16=False the iteration runs in float64."""
+    X = _r(np.asarray(G, np.float64), bf16)
+    n = _r(np.sqrt(np.sum(X * X)), bf16)
+    den = _r(_r(n * 1.01, bf16) + 1e-6, bf16)
+    X = _r(X / den, bf16)
+    a, b, c = coeffs
+    tall = X.shape[0] > X.shape[1]
+    for _ in range(steps):
+        A = _r(X.T @ X if tall else X @ X.T, bf16)
+        AA = _r(A @ A, bf16)
+        B = _r(_r(b * A, bf16) + _r(c * AA, bf16), bf16)
+        XB = _r(X @ B if tall else B @ X, bf16)
+        X = _r(_r(a * X, bf16) + XB, bf16)
+    return X
+
+
+def muon_momentum(g, buf, mu: float):
+    """Momentum with the Nesterov look-ahead, in the lerp form the AdamW listing
+    uses for its first moment: buf <- lerp(buf, g, 1 - mu); u = lerp(g, buf, mu).
+    (The Muon pipeline diagram is missing from the page; this is the standard
+    Muon momentum.)  float32, one rounded op at a time.  Returns (u, buf)."""
+    f32 = np.float32
+    g = np.asarray(g, f32)
+    buf = np.asarray(buf, f32)
+    buf = (buf + f32(1.0 - mu) * (g - buf)).astype(f32)
+    u = (g + f32(mu) * (buf - g)).astype(f32)
+    return u, buf
+
+
+def muon_second_moment(X, v, beta2: float, eps: float = 1e-10):
+    """The factored second moment (page: reduced row-wise for tall matrices,
+    column-wise for wide ones).  Reading: one entry per index of the longer
+    dimension (per row when rows > cols, else per column), the mean of X^2
+    over the shorter dimension; v <- v + (1 - beta2) (s - v); each row (column)
+    of X is divided by sqrt(v) + eps and the result rescaled to the Frobenius
+    norm of X, so only the relative row (column) scales change.
+    Returns (Y, v) in float64."""
+    X = np.asarray(X, np.float64)
+    tall = X.shape[0] > X.shape[1]
+    s = np.mean(X * X, axis=1 if tall else 0)
+    v = np.asarray(v, np.float64)
+    v = v + (1.0 - beta2) * (s - v)
+    d = np.sqrt(v) + eps
+    Y = X / d[:, None] if tall else X / d[None, :]
+    ny = np.sqrt(np.sum(Y * Y))
+    if ny > 0:
+        Y = Y * (np.sqrt(np.sum(X * X)) / ny)
+    return Y, v
+
+
+def cautious_update(p, Y, lr: float, wd: float):
+    """The page's cautious update: mask = (Y * p >= 0); p -= lr * Y + lr * wd * p * mask
+    (weight decay only where the update already pulls the parameter toward zero).
+    float64."""
+    p = np.asarray(p, np.float64)
+    Y = np.asarray(Y, np.float64)
+    mask = (Y * p) >= 0
+    return p - (lr * Y + lr * wd * p * mask)
+
+
+@dataclass(frozen=True)
+class MuonHP:
+    lr: float = 0.02
+    momentum: float = 0.95
+    beta2: float = 0.95
+    weight_decay: float = 0.0
+    ns_steps: int = 5
+    eps: float = 1e-10
+
+
+def muon_matrix_update(p, g, buf, v, hp: MuonHP, bf16: bool = True):
+    """One Muon step of one matrix: momentum -> orthogonalization -> second
+    moment -> cautious update (the page's four stages).  p, g, buf float32
+    [rows, cols]; v float32 [max(rows, cols)].  Returns (p, buf, v) as float32."""
+    u, buf = muon_momentum(g, buf, hp.momentum)
+    X = orthogonalize(u, hp.ns_steps, NS_COEFFS, bf16)
+    Y, v = muon_second_moment(X, v, hp.beta2, hp.eps)
+    p = cautious_update(p, Y, hp.lr, hp.weight_decay)
+    return p.astype(np.float32), buf, v.astype(np.float32)
+
+
+def muon_hybrid_step(cfg, flat_params, m, v, flat_grads, adam_hp: dict, muon_hp: MuonHP,
+                     t: int, grad_scale: float = 1.0, bf16: bool = True):
+    """One optimizer step of the hybrid: Muon for `muon_matrices(cfg)`, AdamW
+    (adamw_update) for every other tensor.  The gradients are multiplied by
+    grad_scale first (float32).  For a Muon matrix the flat m slot holds its
+    momentum buffer and the first max(rows, cols) entries of its v slot its
+    second moment (the rest of that slot stays zero).  Returns (p, m, v) float32."""
+    f32 = np.float32
+    p = np.array(flat_params, f32)
+    m = np.array(m, f32)
+    v = np.array(v, f32)
+    g = np.asarray(flat_grads, f32)
+    muon = set(muon_matrices(cfg))
+    s = adamw_scalars(adam_hp["lr"], adam_hp["beta1"], adam_hp["beta2"], adam_hp["eps"],
+                      adam_hp["weight_decay"], t, grad_scale)
+    off = 0
+    for name, shape in layout(cfg):
+        n = int(np.prod(shape))
+        sl = slice(off, off + n)
+        off += n
+        if name in muon:
+            L = max(shape)
+            gs = (g[sl] * f32(grad_scale)).astype(f32).reshape(shape)
+            pn, bn, vn = muon_matrix_update(p[sl].reshape(shape), gs, m[sl].reshape(shape),
+                                            v[off - n:off - n + L], muon_hp, bf16)
+            p[sl] = pn.reshape(-1)
+            m[sl] = bn.reshape(-1)
+            v[off - n:off - n + L] = vn
+        else:
+            p[sl], m[sl], v[sl] = adamw_update(p[sl], m[sl], v[sl], g[sl], s)
+    return p, m, v

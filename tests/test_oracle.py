@@ -340,3 +340,117 @@ def test_train_steps_uses_each_steps_rate():
     r1 = oracle.train_steps(cfg, p0, batches[:1], [cfg["lr"]])
     ref = oracle.step(cfg, p0, np.zeros_like(p0), np.zeros_like(p0), *batches[0][0], 1)
     assert np.array_equal(r1["p"], ref["p"])
+
+
+# ---------------------------------------------------------------- Muon (nanochat)
+def _quintic_closed_form(G, steps=5):
+    """U p^steps(S / den) V^T from the SVD of G: the orthogonalization acts on
+    singular values only."""
+    U, S, Vt = np.linalg.svd(G, full_matrices=False)
+    den = np.sqrt(np.sum(G * G)) * 1.01 + 1e-6
+    s = S / den
+    a, b, c = oracle.NS_COEFFS
+    for _ in range(steps):
+        s = a * s + b * s ** 3 + c * s ** 5
+    return (U * s) @ Vt
+
+
+@pytest.mark.parametrize("shape", [(48, 16), (16, 16), (16, 40)])
+def test_orthogonalize_acts_on_singular_values(shape):
+    """tall, square and wide branches == the SVD closed form (float64)."""
+    rng = np.random.default_rng(sum(shape))
+    G = rng.standard_normal(shape) * 0.03
+    X = oracle.orthogonalize(G, 5, bf16=False)
+    ref = _quintic_closed_form(G, 5)
+    assert np.abs(X - ref).max() <= 1e-10 * np.abs(ref).max()
+    for k in (1, 2):  # every iteration count, not just the default
+        assert np.allclose(oracle.orthogonalize(G, k, bf16=False), _quintic_closed_form(G, k),
+                           rtol=0, atol=1e-12)
+    # five quintic steps leave every singular value in the polynomial's band around 1
+    sv = np.linalg.svd(X, compute_uv=False)
+    assert sv.max() < 1.25 and sv.min() > 0.55
+
+
+def test_orthogonalize_bf16_stays_near_exact_and_representable():
+    rng = np.random.default_rng(3)
+    G = rng.standard_normal((64, 24)) * 0.01
+    Xb = oracle.orthogonalize(G, 5, bf16=True)
+    Xe = oracle.orthogonalize(G, 5, bf16=False)
+    assert np.linalg.norm(Xb - Xe) <= 0.06 * np.linalg.norm(Xe)
+    assert np.array_equal(Xb.astype(np.float32), oracle.bf16_round(Xb.astype(np.float32)))
+
+
+def test_muon_momentum_constant_gradient_closed_form():
+    """Constant g from a zero buffer: buf_t = (1 - mu^t) g and the Nesterov
+    look-ahead u_t = (1 - mu^(t+1)) g."""
+    g = np.array([1.0, -2.0, 0.5, 3.0], np.float32)
+    buf = np.zeros(4, np.float32)
+    mu = 0.95
+    for t in range(1, 9):
+        u, buf = oracle.muon_momentum(g, buf, mu)
+        assert np.allclose(buf, (1 - mu ** t) * g, rtol=1e-5, atol=0)
+        assert np.allclose(u, (1 - mu ** (t + 1)) * g, rtol=1e-5, atol=0)
+
+
+def test_muon_second_moment_properties():
+    rng = np.random.default_rng(4)
+    # equal row scales: nothing to correct, Y == X
+    X = np.tile(rng.choice([-1.0, 1.0], size=(1, 8)), (20, 1)) * 0.3
+    Y, v = oracle.muon_second_moment(X, np.zeros(20), 0.95)
+    assert np.allclose(Y, X, rtol=1e-12, atol=0)
+    assert np.allclose(v, 0.05 * 0.09, rtol=1e-12)
+    # tall: after the first step every row has the same RMS, the norm is kept
+    X = rng.standard_normal((30, 6)) * rng.uniform(0.1, 3.0, size=(30, 1))
+    Y, v = oracle.muon_second_moment(X, np.zeros(30), 0.9)
+    rms = np.sqrt(np.mean(Y * Y, axis=1))
+    assert np.allclose(rms, rms[0], rtol=1e-9)
+    assert np.isclose(np.linalg.norm(Y), np.linalg.norm(X), rtol=1e-12)
+    assert np.allclose(v, 0.1 * np.mean(X * X, axis=1), rtol=1e-12)
+    # wide: per column
+    X = rng.standard_normal((5, 40)) * rng.uniform(0.1, 3.0, size=(1, 40))
+    Y, v = oracle.muon_second_moment(X, np.zeros(40), 0.9)
+    rms = np.sqrt(np.mean(Y * Y, axis=0))
+    assert np.allclose(rms, rms[0], rtol=1e-9)
+    assert v.shape == (40,)
+    # an existing second moment: the row scale follows the running average, not the new stats
+    X = np.ones((4, 2))
+    Y, v = oracle.muon_second_moment(X, np.array([4.0, 1.0, 1.0, 1.0]), 0.5)
+    assert np.allclose(v, [2.5, 1.0, 1.0, 1.0])
+    assert Y[0, 0] < Y[1, 0]
+
+
+def test_cautious_update_hand_example():
+    p = np.array([1.0, 1.0, -1.0, -1.0, 0.0])
+    Y = np.array([0.5, -0.5, 0.5, -0.5, 0.3])
+    out = oracle.cautious_update(p, Y, lr=0.1, wd=0.2)
+    # same sign (or p = 0): decay applies; opposite sign: no decay
+    assert np.allclose(out, [1 - 0.05 - 0.02, 1 + 0.05, -1 - 0.05, -1 + 0.05 + 0.02, -0.03])
+
+
+def test_muon_hybrid_step_routes_tensors():
+    """AdamW slices equal adamw_update on the same slice; Muon slices with lr = 0
+    keep their values while the momentum and second moment advance; the unused
+    tail of each Muon v slot stays zero."""
+    cfg = presets.preset("tiny", bias=1)
+    p0 = synth.init_params(cfg, seed=21, perturb=True)
+    g = synth.normal(p0.size, seed=22, scale=1e-2)
+    z = np.zeros_like(p0)
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+    mh = oracle.MuonHP(lr=0.0, weight_decay=0.1)
+    p, m, v = oracle.muon_hybrid_step(cfg, p0, z, z, g, hp, mh, t=1, grad_scale=0.5)
+    s = oracle.adamw_scalars(1e-3, 0.9, 0.95, 1e-8, 0.1, 1, 0.5)
+    muon = set(oracle.muon_matrices(cfg))
+    assert len(muon) == 4 * cfg["n_layer"]
+    off = 0
+    for name, shape in oracle.layout(cfg):
+        n = int(np.prod(shape))
+        sl = slice(off, off + n)
+        if name in muon:
+            assert np.array_equal(p[sl], p0[sl])
+            assert np.allclose(m[sl], 0.05 * 0.5 * g[sl], rtol=1e-6)
+            L = max(shape)
+            assert (v[off:off + L] > 0).all() and not v[off + L:off + n].any()
+        else:
+            pr, mr, vr = oracle.adamw_update(p0[sl], z[sl], z[sl], g[sl], s)
+            assert np.array_equal(p[sl], pr) and np.array_equal(m[sl], mr)
+        off += n
