@@ -78,6 +78,39 @@ def cpu_baseline(cfg, seconds_budget=30.0):
                       f"(forward, backward, norm, AdamW) in float32 NumPy; {dt:.1f} s"}
 
 
+def muon_ns_flops(cfg, steps=5):
+    """Matrix-product FLOPs of the Newton-Schulz iterations of one Muon step:
+    per matrix [r, c] with s = min(r, c), l = max(r, c) and per iteration,
+    the Gram product 2 s^2 l, A A 2 s^3 and the update product 2 s^2 l."""
+    C, F = cfg["n_embd"], cfg["mlp_hidden"]
+    total = 0
+    for r, c in ((3 * C, C), (C, C), (F, C), (C, F)):
+        s_, l_ = min(r, c), max(r, c)
+        total += 4 * s_ * s_ * l_ + 2 * s_ ** 3
+    return total * steps * cfg["n_layer"]
+
+
+def time_muon(model, cfg, torch, gpt, reps=5):
+    """The hybrid optimizer step (Muon on the block matrices, AdamW on the rest)
+    in place of AdamW: HIP events on the stream it runs on, after one untimed
+    call, on fixed synthetic gradients."""
+    g = torch.randn(model.n_params, generator=torch.Generator().manual_seed(5)) * 1e-3
+    g = g.cuda()
+    ms = []
+    for r in range(reps + 1):
+        model.set_buffer(gpt.BUF_GRADS, g)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        model.muon_step(1000 + r, 1.0)
+        e1.record()
+        torch.cuda.synchronize()
+        if r:
+            ms.append(e0.elapsed_time(e1))
+    t = sorted(ms)[len(ms) // 2]
+    fl = muon_ns_flops(cfg)
+    return {"ms": round(t, 3), "ns_flop": fl, "ns_tflops_over_step": round(fl / (t * 1e-3) / 1e12, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,6 +202,8 @@ def main():
                 "algorithmic_per_launch": per_launch, "avg_launch_us": round(avg_s * 1e6, 2),
                 "launches_per_step": ds["launches"] // args.profile_steps}
 
+    muon = time_muon(model, cfg, torch, gpt)
+
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
@@ -181,7 +216,7 @@ def main():
         "step_ms_median": round(float(np.median(step_ms)), 3),
         "step_ms_min": round(float(np.min(step_ms)), 3),
         "loss_first": round(losses[0], 4), "loss_last": round(losses[-1], 4),
-        "kernels": per_kind, "sites": per_site, "roofline": roof,
+        "kernels": per_kind, "sites": per_site, "roofline": roof, "muon_step": muon,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)

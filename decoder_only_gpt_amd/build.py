@@ -20,9 +20,10 @@ OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgptmi.so")
 ARCH = "gfx950"
 
-SOURCES = ["engine.hip", "gemm.hip", "attention.hip", "rowwise.hip", "adamw.hip"]
-# Per-file extra flags.  The AdamW update must round every operation on its own.
-EXTRA = {"adamw.hip": ["-ffp-contract=off"]}
+SOURCES = ["engine.hip", "gemm.hip", "attention.hip", "rowwise.hip", "adamw.hip", "muon.hip"]
+# Per-file extra flags.  The AdamW update and the Muon momentum must round every
+# operation on their own.
+EXTRA = {"adamw.hip": ["-ffp-contract=off"], "muon.hip": ["-ffp-contract=off"]}
 
 BASE_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",

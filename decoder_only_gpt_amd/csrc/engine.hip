@@ -10,10 +10,12 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "../../include/gpt.h"
@@ -129,7 +131,7 @@ struct Arena {
   int64_t X, ln_mean, ln_rstd;
   std::vector<int64_t> a1, qkv, att, lse, a2, u, g;
   int64_t xf, logits, loss_rows, loss, gres[2], gact[NGB], dC, dC2, dF[NGB], dqkv[NGB], dvec;
-  int64_t gemm_ws, gemm_ws_bytes, cs_part, ln_part, n_part, norm2;
+  int64_t gemm_ws, gemm_ws_bytes, cs_part, ln_part, n_part, norm2, muon_ws;
   int64_t e_counts, e_offsets, e_tile_sums, e_rank, e_perm, e_carry_first, e_carry_last, e_flags,
       e_last_tok;
   int64_t state_end, total;
@@ -201,6 +203,12 @@ Arena plan_arena(const gpt_config& c, int B, int T) {
   a.e_last_tok = take(nch * 4);
   a.n_part = take(1024 * 8);
   a.norm2 = take(16);
+  // Muon working set, sized for the largest kind of block matrix (one kind at a time).
+  int64_t mw = 0;
+  for (auto rc : {std::pair<int64_t, int64_t>{3 * C, C}, {C, C}, {F, C}, {C, F}})
+    mw = std::max<int64_t>(mw, gpt::muon_workspace_bytes((int)rc.first, (int)rc.second, (int)L,
+                                                         c.precision));
+  a.muon_ws = take(mw);
   a.total = o;
   return a;
 }
@@ -604,6 +612,21 @@ gpt::AdamScalars adam_scalars(const gpt_adamw_hp& hp) {
   return sc;
 }
 
+// The kinds of per-layer block matrix Muon updates: (offset in layer 0, rows, cols).
+struct MuonKind { int64_t off0, off1; int rows, cols; };
+std::vector<MuonKind> muon_kinds(const gpt_model* m) {
+  const auto& L0 = m->pl.layer[0];
+  const bool two = m->cfg.n_layer > 1;
+  const auto* L1 = two ? &m->pl.layer[1] : nullptr;
+  const int C = (int)m->C, F = (int)m->F;
+  return {
+      {L0.qkvw, two ? L1->qkvw : L0.qkvw, 3 * C, C},
+      {L0.projw, two ? L1->projw : L0.projw, C, C},
+      {L0.fcw, two ? L1->fcw : L0.fcw, F, C},
+      {L0.fcpw, two ? L1->fcpw : L0.fcpw, C, F},
+  };
+}
+
 int check_hp(const gpt_adamw_hp* hp) {
   if (!hp) return fail(GPT_E_INVALID, "hp is NULL");
   if (hp->step_t < 1) return fail(GPT_E_INVALID, "step_t must be >= 1");
@@ -796,6 +819,71 @@ int gpt_adamw_step(gpt_model* m, const gpt_adamw_hp* hp, void* stream) {
   return GPT_OK;
 }
 
+int gpt_muon_step(gpt_model* m, const gpt_adamw_hp* adam, const gpt_muon_hp* muon,
+                  void* stream) {
+  if (!m) return fail(GPT_E_INVALID, "NULL model");
+  int rc = check_hp(adam);
+  if (rc != GPT_OK) return rc;
+  if (!muon) return fail(GPT_E_INVALID, "muon hp is NULL");
+  if (!(muon->momentum >= 0.0 && muon->momentum < 1.0 && muon->beta2 >= 0.0 &&
+        muon->beta2 < 1.0) ||
+      !(muon->eps >= 0.0) || !std::isfinite(muon->lr) || !std::isfinite(muon->weight_decay) ||
+      muon->ns_steps < 0 || muon->ns_steps > 16)
+    return fail(GPT_E_INVALID, "bad muon hyper-parameters");
+  if (m->state != 2) return fail(GPT_E_STATE, "muon_step needs a backward first");
+  hipStream_t s = (hipStream_t)stream;
+  if ((rc = wait_adam(m, s, -1)) != GPT_OK) return rc;
+  float* pm = m->at<float>(m->ar.adam_m);
+  float* pv = m->at<float>(m->ar.adam_v);
+  uint16_t* sh = m->bf16 ? m->at<uint16_t>(m->ar.shadow) : nullptr;
+  const std::vector<MuonKind> kinds = muon_kinds(m);
+  // AdamW on the runs of the flat vector between the Muon matrices.
+  std::vector<std::pair<int64_t, int64_t>> muon_ranges;
+  for (int l = 0; l < m->cfg.n_layer; ++l)
+    for (const MuonKind& k : kinds) {
+      const int64_t b = k.off0 + l * (k.off1 - k.off0);
+      muon_ranges.push_back({b, b + (int64_t)k.rows * k.cols});
+    }
+  std::sort(muon_ranges.begin(), muon_ranges.end());
+  const gpt::AdamScalars sc = adam_scalars(*adam);
+  int64_t pos = 0;
+  for (size_t i = 0; i <= muon_ranges.size(); ++i) {
+    const int64_t end = i < muon_ranges.size() ? muon_ranges[i].first : m->N;
+    if (end > pos)
+      HIP_TRY(gpt::adamw(end - pos, m->P(pos), pm + pos, pv + pos, m->G(pos),
+                         sh ? sh + pos : nullptr, sc, s));
+    if (i < muon_ranges.size()) pos = muon_ranges[i].second;
+  }
+  gpt::MuonScalars ms;
+  ms.grad_scale = (float)adam->grad_scale;
+  ms.mu = (float)muon->momentum;
+  ms.omm = (float)(1.0 - muon->momentum);
+  ms.omb2 = (float)(1.0 - muon->beta2);
+  ms.eps = (float)muon->eps;
+  ms.lr = (float)muon->lr;
+  ms.lrwd = (float)(muon->lr * muon->weight_decay);
+  ms.a = 3.4445f;
+  ms.b = -4.7750f;
+  ms.c = 2.0315f;
+  ms.ns_steps = muon->ns_steps;
+  for (const MuonKind& k : kinds) {
+    gpt::MuonGroup g;
+    g.g = m->G(k.off0);
+    g.buf = pm + k.off0;
+    g.v = pv + k.off0;
+    g.p = m->P(k.off0);
+    g.shadow = sh ? sh + k.off0 : nullptr;
+    g.ls = (long)(k.off1 - k.off0);
+    g.rows = k.rows;
+    g.cols = k.cols;
+    g.count = m->cfg.n_layer;
+    HIP_TRY(gpt::muon_matrices(g, ms, m->prec(), m->at<void>(m->ar.muon_ws), s));
+  }
+  m->state = 0;
+  m->loss_valid = false;
+  return GPT_OK;
+}
+
 static int buffer_region(gpt_model* m, int which, char** ptr, int64_t* bytes) {
   switch (which) {
     case GPT_BUF_PARAMS: *ptr = m->at<char>(m->ar.params); *bytes = m->N * 4; return GPT_OK;
@@ -875,13 +963,16 @@ int gpt_op_gemm(const gpt_gemm_desc* d, void* stream) {
   if (!d) return fail(GPT_E_INVALID, "NULL descriptor");
   if (d->precision != GPT_FP32 && d->precision != GPT_BF16)
     return fail(GPT_E_INVALID, "bad precision");
-  if (d->epilogue < GPT_EPI_STORE || d->epilogue > GPT_EPI_MUL)
+  if (d->epilogue < GPT_EPI_STORE || d->epilogue > GPT_EPI_AXPBY)
     return fail(GPT_E_INVALID, "bad epilogue");
+  if (d->batch < 0) return fail(GPT_E_INVALID, "negative batch");
+  if (d->batch > 1 && (d->bias || d->resid))
+    return fail(GPT_E_INVALID, "batched products take no bias or resid");
   if (d->M < 0 || d->N < 0 || d->K < 0) return fail(GPT_E_INVALID, "negative size");
   if (!d->out && d->M > 0 && d->N > 0) return fail(GPT_E_INVALID, "NULL out");
   if (d->epilogue == GPT_EPI_RESIDUAL && !d->resid) return fail(GPT_E_INVALID, "NULL resid");
   if ((d->epilogue == GPT_EPI_DGELU || d->epilogue == GPT_EPI_GELU_PAIR ||
-       d->epilogue == GPT_EPI_MUL) && !d->aux)
+       d->epilogue == GPT_EPI_MUL || d->epilogue == GPT_EPI_AXPBY) && !d->aux)
     return fail(GPT_E_INVALID, "NULL aux");
   hipError_t e = gpt::gemm(*d, (hipStream_t)stream);
   if (e == hipErrorInvalidValue)

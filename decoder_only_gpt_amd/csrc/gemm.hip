@@ -35,6 +35,9 @@ struct EpiArgs {
   long ldo;
   void* aux;
   long ldaux;
+  float alpha, beta;           // AXPBY
+  int batch;                   // > 1: grid z indexes the matrix of a batch
+  long sa, sb, so, saux;       // byte strides between the matrices of a batch
 };
 
 template <typename ActT>
@@ -77,6 +80,11 @@ __device__ __forceinline__ void epilogue(const EpiArgs& e, int m, int n, float a
       Act<ActT>::store((ActT*)e.out, o,
                        acc * Act<ActT>::load((const ActT*)e.aux, (long)m * e.ldaux + n));
       break;
+    case GPT_EPI_AXPBY:
+      Act<ActT>::store((ActT*)e.out, o,
+                       e.alpha * acc +
+                           e.beta * Act<ActT>::load((const ActT*)e.aux, (long)m * e.ldaux + n));
+      break;
     case GPT_EPI_F32:
       ((float*)e.out)[o] = acc;
       break;
@@ -91,6 +99,15 @@ struct OpArgs {
   long ld;
   int trans, rows, kvalid, gelu;
 };
+
+// Matrix z of a batched product: operand and output bases moved by the
+// batch strides.
+__device__ __forceinline__ void batch_select(int z, OpArgs& a, OpArgs& b, EpiArgs& e) {
+  a.X = (const char*)a.X + z * e.sa;
+  b.X = (const char*)b.X + z * e.sb;
+  e.out = (char*)e.out + z * e.so;
+  if (e.aux) e.aux = (char*)e.aux + z * e.saux;
+}
 
 // ----------------------------------------------------------------------------
 // fp32 / generic path: 64x64 tile, 16x16 threads, 4x4 outputs per thread.
@@ -108,6 +125,7 @@ template <typename InT, typename ActT>
 __global__ void __launch_bounds__(256) gemm_simt_kernel(OpArgs A, OpArgs B, int K, EpiArgs e) {
   __shared__ float As[16][64 + 1];
   __shared__ float Bs[16][64 + 1];
+  if (e.batch > 1) batch_select(blockIdx.z, A, B, e);
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
   float acc[4][4] = {};
@@ -279,6 +297,14 @@ __device__ __forceinline__ void epilogue8(const EpiArgs& e, float* partial, int 
     *(u32x4*)((bf16_t*)e.out + o) = u32x4{
         pack_bf2(x[0] * bf_lo(a.x), x[1] * bf_hi(a.x)), pack_bf2(x[2] * bf_lo(a.y), x[3] * bf_hi(a.y)),
         pack_bf2(x[4] * bf_lo(a.z), x[5] * bf_hi(a.z)), pack_bf2(x[6] * bf_lo(a.w), x[7] * bf_hi(a.w))};
+  } else if constexpr (EPI == GPT_EPI_AXPBY) {
+    const u32x4 a = *(const u32x4*)((const bf16_t*)e.aux + (long)m * e.ldaux + n);
+    const float al = e.alpha, be = e.beta;
+    *(u32x4*)((bf16_t*)e.out + o) = u32x4{
+        pack_bf2(al * x[0] + be * bf_lo(a.x), al * x[1] + be * bf_hi(a.x)),
+        pack_bf2(al * x[2] + be * bf_lo(a.y), al * x[3] + be * bf_hi(a.y)),
+        pack_bf2(al * x[4] + be * bf_lo(a.z), al * x[5] + be * bf_hi(a.z)),
+        pack_bf2(al * x[6] + be * bf_lo(a.w), al * x[7] + be * bf_hi(a.w))};
   } else if constexpr (EPI == GPT_EPI_GELU_PAIR) {
     if (e.bias) {
       float4 b0 = *(const float4*)(e.bias + n), b1 = *(const float4*)(e.bias + n + 4);
@@ -322,8 +348,13 @@ __global__ void __launch_bounds__(256, 2) gemm_mfma_kernel(OpArgs A, OpArgs B, i
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-  const int kbeg = blockIdx.z * kchunk;
-  if (EPI == EPI_PARTIAL) partial += (long)blockIdx.z * e.M * e.N;
+  int zs = blockIdx.z;  // K split, or the matrix of a batch
+  if (e.batch > 1) {
+    batch_select(zs, A, B, e);
+    zs = 0;
+  }
+  const int kbeg = zs * kchunk;
+  if (EPI == EPI_PARTIAL) partial += (long)zs * e.M * e.N;
   const int kend = min(K, kbeg + kchunk);
   const int nk = (kend - kbeg + BK - 1) / BK;
   // Stage s: A tile at smem + s * 32 KB, B tile 16 KB after it.
@@ -451,6 +482,9 @@ MfmaKernel mfma_kernel_for(int at, int bt, int epi, int ga, int gb) {
   K_(0, 1, GPT_EPI_DGELU, 0, 0)
   K_(0, 1, GPT_EPI_MUL, 0, 0)
   K_(0, 1, GPT_EPI_F32, 0, 0)
+  K_(0, 0, GPT_EPI_AXPBY, 0, 0)
+  K_(0, 1, GPT_EPI_AXPBY, 0, 0)
+  K_(1, 1, GPT_EPI_STORE, 0, 0)
   K_(1, 1, GPT_EPI_F32, 0, 0)
   K_(1, 1, GPT_EPI_F32_ACCUM, 0, 0)
   K_(1, 1, EPI_PARTIAL, 0, 0)
@@ -539,6 +573,10 @@ __global__ void __launch_bounds__(256, 2) gemm_dma_kernel(OpArgs A, OpArgs B, in
   const int wm = wave >> 1, wn = wave & 1;
   int tx, ty, tz;
   xcd_tile(tx, ty, tz);
+  if (e.batch > 1) {  // tz indexes the matrix of a batch (never split over K)
+    batch_select(tz, A, B, e);
+    tz = 0;
+  }
   const int m0 = ty * BM, n0 = tx * BN;
   const int kbeg = tz * kchunk;
   if (EPI == EPI_PARTIAL) partial += (long)tz * e.M * e.N;
@@ -627,6 +665,9 @@ MfmaKernel dma_kernel_for(int at, int bt, int epi, int ga, int gb) {
   K_(0, 1, GPT_EPI_MUL)
   K_(0, 1, GPT_EPI_F32)
   K_(0, 1, EPI_PARTIAL)
+  K_(0, 0, GPT_EPI_AXPBY)
+  K_(0, 1, GPT_EPI_AXPBY)
+  K_(1, 1, GPT_EPI_STORE)
   K_(1, 1, GPT_EPI_F32)
   K_(1, 1, GPT_EPI_F32_ACCUM)
   K_(1, 1, EPI_PARTIAL)
@@ -727,6 +768,12 @@ __device__ __forceinline__ void epilogue4(const EpiArgs& e, float* partial, int 
     const uint2 a = *(const uint2*)((const bf16_t*)e.aux + (long)m * e.ldaux + n);
     *(uint2*)((bf16_t*)e.out + o) = make_uint2(pack_bf2(v.x * bf_lo(a.x), v.y * bf_hi(a.x)),
                                                pack_bf2(v.z * bf_lo(a.y), v.w * bf_hi(a.y)));
+  } else if constexpr (EPI == GPT_EPI_AXPBY) {
+    const uint2 a = *(const uint2*)((const bf16_t*)e.aux + (long)m * e.ldaux + n);
+    const float al = e.alpha, be = e.beta;
+    *(uint2*)((bf16_t*)e.out + o) =
+        make_uint2(pack_bf2(al * v.x + be * bf_lo(a.x), al * v.y + be * bf_hi(a.x)),
+                   pack_bf2(al * v.z + be * bf_lo(a.y), al * v.w + be * bf_hi(a.y)));
   } else if constexpr (EPI == GPT_EPI_GELU_PAIR) {
     if (e.bias) {
       const float4 b = *(const float4*)(e.bias + n);
@@ -767,6 +814,10 @@ __global__ void __launch_bounds__(256, 1) gemm_big_kernel(OpArgs A, OpArgs B, in
   const int wm = wave >> 1, wn = wave & 1;
   int tx, ty, tz;
   xcd_tile(tx, ty, tz);
+  if (e.batch > 1) {  // tz indexes the matrix of a batch (never split over K)
+    batch_select(tz, A, B, e);
+    tz = 0;
+  }
   const int m0 = ty * BIG, n0 = tx * BIG;
   const int kbeg = tz * kchunk;
   if (EPI == EPI_PARTIAL) partial += (long)tz * e.M * e.N;
@@ -898,6 +949,10 @@ __global__ void __launch_bounds__(512, 1) gemm_big8_kernel(OpArgs A, OpArgs B, i
   const int wm = wave >> 2, wn = wave & 3;  // rows wm * 128 .., columns wn * 64 ..
   int tx, ty, tz;
   xcd_tile(tx, ty, tz);
+  if (e.batch > 1) {  // tz indexes the matrix of a batch (never split over K)
+    batch_select(tz, A, B, e);
+    tz = 0;
+  }
   const int m0 = ty * BIG, n0 = tx * BIG;
   const int kbeg = tz * kchunk;
   if (EPI == EPI_PARTIAL) partial += (long)tz * e.M * e.N;
@@ -993,6 +1048,9 @@ MfmaKernel big8_kernel_for(int at, int bt, int epi, int ga, int gb) {
   K_(0, 1, GPT_EPI_DGELU)
   K_(0, 1, GPT_EPI_MUL)
   K_(0, 1, EPI_PARTIAL)
+  K_(0, 0, GPT_EPI_AXPBY)
+  K_(0, 1, GPT_EPI_AXPBY)
+  K_(1, 1, GPT_EPI_STORE)
   K_(1, 1, GPT_EPI_F32)
   K_(1, 1, GPT_EPI_F32_ACCUM)
   K_(1, 1, EPI_PARTIAL)
@@ -1016,6 +1074,9 @@ MfmaKernel big_kernel_for(int at, int bt, int epi, int ga, int gb) {
   K_(0, 1, GPT_EPI_MUL)
   K_(0, 1, GPT_EPI_F32)
   K_(0, 1, EPI_PARTIAL)
+  K_(0, 0, GPT_EPI_AXPBY)
+  K_(0, 1, GPT_EPI_AXPBY)
+  K_(1, 1, GPT_EPI_STORE)
   K_(1, 1, GPT_EPI_F32)
   K_(1, 1, GPT_EPI_F32_ACCUM)
   K_(1, 1, EPI_PARTIAL)
@@ -1055,7 +1116,7 @@ int tile_override() {
 }
 
 GemmPlan plan_gemm(int M, int N, int K, int precision, bool splittable, int64_t ws_bytes,
-                   bool big_ok) {
+                   bool big_ok, int batch = 1) {
   GemmPlan p{false, 1};
   if (precision != GPT_BF16 || M <= 0 || N <= 0 || K <= 0) return p;
   if (!big_ok) {
@@ -1064,7 +1125,7 @@ GemmPlan plan_gemm(int M, int N, int K, int precision, bool splittable, int64_t 
     p.S = S;
     return p;
   }
-  const long t256 = cdiv(M, BIG) * cdiv(N, BIG);
+  const long t256 = cdiv(M, BIG) * cdiv(N, BIG) * batch;
   const int force = tile_override();
   if (force == 256) {
     p.big = true;
@@ -1100,7 +1161,7 @@ GemmPlan plan_gemm(int M, int N, int K, int precision, bool splittable, int64_t 
     // Otherwise 256-tiles (one workgroup per CU) when they fill the rounds of
     // the 256 CUs at least as evenly as 128-tiles (two workgroups per CU) do.
     if (!splittable && t256 >= 128) {
-      const long t128 = cdiv(M, BM) * cdiv(N, BN);
+      const long t128 = cdiv(M, BM) * cdiv(N, BN) * batch;
       const double f256 = (double)t256 / (256.0 * cdiv(t256, 256));
       const double f128 = (double)t128 / (512.0 * cdiv(t128, 512));
       if (f256 + 1e-9 >= f128) {
@@ -1157,12 +1218,16 @@ hipError_t gemm(const gpt_gemm_desc& d, hipStream_t s) {
   // Vector loads: 8 K-values (row-major operand) or 8 rows (K-major operand).
   const bool k_vectors = !d.a_trans || !d.b_trans;
   if (d.K < 0 || (k_vectors && d.K % 8) || (d.lda % 8) || (d.ldb % 8)) return hipErrorInvalidValue;
-  EpiArgs e{d.epilogue, d.gelu_tanh, d.M, d.N, d.bias, d.resid, d.out, d.ldo, d.aux, d.ldaux};
+  const int batch = d.batch > 1 ? d.batch : 1;
+  if (batch > 1 && (d.bias || d.resid)) return hipErrorInvalidValue;
+  EpiArgs e{d.epilogue, d.gelu_tanh, d.M,      d.N,        d.bias,       d.resid,
+            d.out,      d.ldo,       d.aux,    d.ldaux,    d.alpha,      d.beta,
+            batch,      d.stride_a,  d.stride_b, d.stride_out, d.stride_aux};
   OpArgs A{d.A, d.lda, d.a_trans, d.a_rows, d.a_kvalid, d.a_gelu};
   OpArgs B{d.B, d.ldb, d.b_trans, d.b_rows, d.b_kvalid, d.b_gelu};
   if (d.K == 0) {
     // Empty reduction: the epilogue still runs on a zero accumulator.
-    dim3 grid((unsigned)cdiv(d.N, 64), (unsigned)cdiv(d.M, 64));
+    dim3 grid((unsigned)cdiv(d.N, 64), (unsigned)cdiv(d.M, 64), (unsigned)batch);
     if (d.precision == GPT_BF16)
       gemm_simt_kernel<bf16_t, bf16_t><<<grid, 256, 0, s>>>(A, B, 0, e);
     else
@@ -1170,12 +1235,12 @@ hipError_t gemm(const gpt_gemm_desc& d, hipStream_t s) {
     return hipGetLastError();
   }
   if (d.precision != GPT_BF16) {
-    dim3 grid((unsigned)cdiv(d.N, 64), (unsigned)cdiv(d.M, 64));
+    dim3 grid((unsigned)cdiv(d.N, 64), (unsigned)cdiv(d.M, 64), (unsigned)batch);
     gemm_simt_kernel<float, float><<<grid, 256, 0, s>>>(A, B, d.K, e);
     return hipGetLastError();
   }
-  const GemmPlan plan = plan_gemm(d.M, d.N, d.K, d.precision, splittable(d),
-                                  d.workspace ? d.workspace_bytes : 0, big_ok(d));
+  const GemmPlan plan = plan_gemm(d.M, d.N, d.K, d.precision, batch == 1 && splittable(d),
+                                  d.workspace ? d.workspace_bytes : 0, big_ok(d), batch);
   const int S = effective_splits(plan, d.K);
   const bool vec_ok = d.N % 8 == 0 && d.ldo % 8 == 0 && (d.aux == nullptr || d.ldaux % 8 == 0);
   const int epi = S > 1 ? EPI_PARTIAL : d.epilogue;
@@ -1190,7 +1255,7 @@ hipError_t gemm(const gpt_gemm_desc& d, hipStream_t s) {
   }
   if (kern == nullptr) {
     // Combinations the step never issues: the generic kernel (bf16 inputs).
-    dim3 grid((unsigned)cdiv(d.N, 64), (unsigned)cdiv(d.M, 64));
+    dim3 grid((unsigned)cdiv(d.N, 64), (unsigned)cdiv(d.M, 64), (unsigned)batch);
     gemm_simt_kernel<bf16_t, bf16_t><<<grid, 256, 0, s>>>(A, B, d.K, e);
     return hipGetLastError();
   }
@@ -1203,7 +1268,7 @@ hipError_t gemm(const gpt_gemm_desc& d, hipStream_t s) {
     }
   }
   const int T = plan.big ? BIG : BM;
-  dim3 grid((unsigned)cdiv(d.N, T), (unsigned)cdiv(d.M, T), (unsigned)S);
+  dim3 grid((unsigned)cdiv(d.N, T), (unsigned)cdiv(d.M, T), (unsigned)(S * batch));
   if (S == 1) {
     kern<<<grid, threads, 0, s>>>(A, B, d.K, d.K, e, nullptr);
     return hipGetLastError();

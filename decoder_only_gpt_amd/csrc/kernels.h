@@ -71,4 +71,24 @@ struct AdamScalars { float omb1, omb2, decay, step_size, sbc2, eps, scale; };
 hipError_t adamw(int64_t n, float* p, float* m, float* v, const float* g, uint16_t* shadow,
                  AdamScalars sc, hipStream_t s);
 
+// Muon for one kind of block matrix across the layers (muon.hip).  Matrix l
+// (l < count) of shape [rows, cols] sits at element offset l * ls of the
+// parameter, gradient, momentum (buf) and second-moment (v, first max(rows,
+// cols) entries used) arrays, all given at layer 0.  `shadow` (bf16 copy of
+// p, bf16 mode) may be NULL.
+struct MuonGroup {
+  const float* g; float* buf; float* v; float* p; uint16_t* shadow;
+  long ls; int rows, cols, count;
+};
+struct MuonScalars {
+  float grad_scale, omm, mu, omb2, eps, lr, lrwd;  // omm = 1 - mu, omb2 = 1 - beta2, lrwd = lr * wd
+  float a, b, c;                                  // Newton-Schulz polynomial
+  int ns_steps;
+};
+constexpr int MUON_PREP_BLOCKS = 64;  // sum-of-squares partials per matrix
+// Workspace bytes muon_matrices needs for `count` matrices of [rows, cols].
+int64_t muon_workspace_bytes(int rows, int cols, int count, int prec);
+hipError_t muon_matrices(const MuonGroup& g, const MuonScalars& sc, int prec, void* workspace,
+                         hipStream_t s);
+
 }  // namespace gpt

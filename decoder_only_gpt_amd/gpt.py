@@ -20,12 +20,14 @@ GPT_MAX_LAYERS = 128
 OK, E_INVALID, E_STATE, E_HIP, E_NONFINITE, E_UNSUPPORTED = range(6)
 FP32, BF16 = 0, 1
 BUF_PARAMS, BUF_GRADS, BUF_ADAM_M, BUF_ADAM_V, BUF_LOSS_ROWS = range(5)
-EPI_STORE, EPI_RESIDUAL, EPI_GELU, EPI_DGELU, EPI_F32, EPI_F32_ACCUM, EPI_GELU_PAIR, EPI_MUL = range(8)
+(EPI_STORE, EPI_RESIDUAL, EPI_GELU, EPI_DGELU, EPI_F32, EPI_F32_ACCUM, EPI_GELU_PAIR, EPI_MUL,
+ EPI_AXPBY) = range(9)
 
 # Every symbol include/gpt.h declares.
 EXPORTS = [
     "gpt_plan", "gpt_flops_per_token", "gpt_init", "gpt_forward", "gpt_loss",
-    "gpt_loss_device_ptr", "gpt_backward", "gpt_grad_norm", "gpt_adamw_step", "gpt_get_buffer",
+    "gpt_loss_device_ptr", "gpt_backward", "gpt_grad_norm", "gpt_adamw_step", "gpt_muon_step",
+    "gpt_get_buffer",
     "gpt_set_buffer", "gpt_destroy", "gpt_last_error", "gpt_op_gemm", "gpt_op_attention_fwd",
     "gpt_op_attention_bwd", "gpt_op_adamw", "gpt_profile_begin", "gpt_profile_end",
 ]
@@ -75,6 +77,16 @@ class KernelStats(ctypes.Structure):
                 ("bytes", ctypes.c_double)]
 
 
+class MuonHP(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("momentum", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("weight_decay", ctypes.c_double), ("eps", ctypes.c_double),
+                ("ns_steps", ctypes.c_int32)]
+
+
+def muon_hp(lr=0.02, momentum=0.95, beta2=0.95, weight_decay=0.0, eps=1e-10, ns_steps=5) -> MuonHP:
+    return MuonHP(lr, momentum, beta2, weight_decay, eps, ns_steps)
+
+
 class GemmDesc(ctypes.Structure):
     _fields_ = [
         ("precision", ctypes.c_int32), ("M", ctypes.c_int32), ("N", ctypes.c_int32),
@@ -88,6 +100,9 @@ class GemmDesc(ctypes.Structure):
         ("out", ctypes.c_void_p), ("ldo", ctypes.c_int64),
         ("aux", ctypes.c_void_p), ("ldaux", ctypes.c_int64),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
+        ("alpha", ctypes.c_float), ("beta", ctypes.c_float), ("batch", ctypes.c_int32),
+        ("stride_a", ctypes.c_int64), ("stride_b", ctypes.c_int64),
+        ("stride_out", ctypes.c_int64), ("stride_aux", ctypes.c_int64),
     ]
 
 
@@ -113,6 +128,7 @@ def lib():
         "gpt_backward": ([vp, i32, vp], i32),
         "gpt_grad_norm": ([vp, vp, ctypes.POINTER(ctypes.c_double)], i32),
         "gpt_adamw_step": ([vp, ctypes.POINTER(AdamHP), vp], i32),
+        "gpt_muon_step": ([vp, ctypes.POINTER(AdamHP), ctypes.POINTER(MuonHP), vp], i32),
         "gpt_get_buffer": ([vp, i32, vp, i32, vp], i32),
         "gpt_set_buffer": ([vp, i32, vp, i32, vp], i32),
         "gpt_destroy": ([vp], i32),
@@ -255,6 +271,13 @@ class Model:
     def adamw_step(self, t: int, grad_scale: float = 1.0, lr: float | None = None):
         hp = adam_hp(self.cfg, t, grad_scale, lr)
         _check(lib().gpt_adamw_step(self.h, ctypes.byref(hp), _stream()))
+
+    def muon_step(self, t: int, grad_scale: float = 1.0, muon: MuonHP | None = None,
+                  lr: float | None = None):
+        """Muon on the per-layer Linear weights, AdamW (lr, t, grad_scale) on the rest."""
+        hp = adam_hp(self.cfg, t, grad_scale, lr)
+        mh = muon if muon is not None else muon_hp()
+        _check(lib().gpt_muon_step(self.h, ctypes.byref(hp), ctypes.byref(mh), _stream()))
 
     def profile_begin(self):
         _check(lib().gpt_profile_begin(self.h))

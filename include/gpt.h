@@ -112,6 +112,24 @@ typedef struct gpt_adamw_hp {
   int64_t step_t;     /* 1-based step count for the bias corrections            */
 } gpt_adamw_hp;
 
+/* Muon hyper-parameters (nanochat "Optimierungsstrategien Muon und AdamW").
+ * For each per-layer Linear weight W [rows, cols] with gradient G:
+ *   g = G * grad_scale; buf += (1-momentum)(g - buf); u = g + momentum (buf - g)
+ *   X = act(u) / (||X||_F * 1.01 + 1e-6); then ns_steps times, with
+ *   (a, b, c) = (3.4445, -4.7750, 2.0315):
+ *     rows > cols: A = X^T X, B = b A + c A A, X = a X + X B
+ *     otherwise:   A = X X^T, B = b A + c A A, X = a X + B X
+ *   s_i = mean of X^2 over the shorter dimension (i along the longer one);
+ *   v_i += (1-beta2)(s_i - v_i); Y = X / (sqrt(v_i) + eps), rescaled to ||X||_F;
+ *   W -= lr Y + lr weight_decay W [Y W >= 0]   (cautious decay).
+ * The momentum buffer is the matrix's ADAM_M slot and v the first
+ * max(rows, cols) entries of its ADAM_V slot.  bf16 mode: X, A and B are bf16
+ * (the page's iteration runs in bf16); fp32 mode: float. */
+typedef struct gpt_muon_hp {
+  double lr, momentum, beta2, weight_decay, eps;
+  int32_t ns_steps;   /* 0..16 */
+} gpt_muon_hp;
+
 typedef struct gpt_model gpt_model;
 
 /* Host only.  Validates cfg and (B, T) and fills *out.  INVALID on a bad
@@ -153,6 +171,13 @@ int gpt_grad_norm(gpt_model* m, void* stream, double* h_norm);
 
 /* One AdamW update of all parameters (see gpt_adamw_hp).  Enqueue only. */
 int gpt_adamw_step(gpt_model* m, const gpt_adamw_hp* hp, void* stream);
+
+/* The hybrid optimizer step (after gpt_backward, in place of gpt_adamw_step):
+ * Muon (hp `muon`, above) on every per-layer Linear weight, AdamW (hp
+ * `adam`, including its grad_scale and step_t) on every other tensor
+ * (embeddings, LayerNorm and bias vectors, the untied lm_head).  Runs on
+ * `stream`; uses a Muon region of the arena.  Errors as gpt_adamw_step. */
+int gpt_muon_step(gpt_model* m, const gpt_adamw_hp* adam, const gpt_muon_hp* muon, void* stream);
 
 /* Copy a flat buffer out of (get) or into (set) the model.  `dst`/`src` is
  * host memory when *_on_device == 0 (the call then synchronises), device
@@ -228,7 +253,8 @@ typedef enum gpt_epilogue {
   GPT_EPI_F32_ACCUM = 5,  /* out(f32) += acc                                        */
   GPT_EPI_GELU_PAIR = 6,  /* u = acc [+ bias] rounded to act; out(act) = GELU'(u),
                              aux(act) = GELU(u) (aux required)                       */
-  GPT_EPI_MUL = 7         /* out(act)  = acc * aux[m, n] (aux required)             */
+  GPT_EPI_MUL = 7,        /* out(act)  = acc * aux[m, n] (aux required)             */
+  GPT_EPI_AXPBY = 8       /* out(act)  = alpha * acc + beta * aux[m, n] (aux required) */
 } gpt_epilogue;
 
 /* One matrix product, nanoGPT Linear convention (y = x W^T).  Operand X (A or
@@ -251,6 +277,13 @@ typedef struct gpt_gemm_desc {
   void* out; int64_t ldo;
   void* aux; int64_t ldaux;  /* GELU output / DGELU input, act type     */
   void* workspace; int64_t workspace_bytes;
+  float alpha, beta;    /* AXPBY scalars (ignored by the other epilogues)        */
+  /* batch > 1: `batch` independent products of the same shape; matrix z reads
+   * A + z*stride_a, B + z*stride_b, aux + z*stride_aux and writes
+   * out + z*stride_out (byte strides).  Batched products are never split
+   * over K and take no bias or resid.  batch 0 or 1: one product. */
+  int32_t batch;
+  int64_t stride_a, stride_b, stride_out, stride_aux;
 } gpt_gemm_desc;
 
 int gpt_op_gemm(const gpt_gemm_desc* d, void* stream);

@@ -124,3 +124,58 @@ def test_full_size_step_reproducible(name):
     assert outs[0][0] == outs[1][0] and outs[0][1] == outs[1][1]
     assert np.array_equal(outs[0][2].view(np.uint32), outs[1][2].view(np.uint32))
     assert abs(outs[0][0] - np.log(cfg["vocab_size"])) < 0.5
+
+
+@pytest.mark.parametrize("name", ["gpt2_124m", "nanochat_swa"])
+def test_full_size_muon_step(name):
+    """The hybrid Muon step at full model size on the gradients of a full
+    batch: every Muon momentum buffer bit for bit; layer 0's four matrices no
+    farther from the float64 Muon than 1.5x the oracle's bf16 Muon (+1e-3),
+    cosine >= 0.99; AdamW slices (embeddings, final LayerNorm) bit for bit."""
+    cfg = presets.preset(name)
+    print(f"[full muon] {name}", flush=True)
+    p = synth.init_params(cfg, seed=0, perturb=True)
+    idx, tgt = synth.tokens(cfg, seed=1)
+    m = gpt.Model(cfg)
+    m.set_params(p)
+    g, _ = _grads_of(m, idx, tgt)
+    hp = oracle.MuonHP(lr=0.02, momentum=0.95, beta2=0.95, weight_decay=0.1)
+    m.muon_step(1, 0.7, gpt.muon_hp(hp.lr, hp.momentum, hp.beta2, hp.weight_decay, hp.eps, 5))
+    gp, gm, gv = m.params(), m.get_buffer(gpt.BUF_ADAM_M), m.get_buffer(gpt.BUF_ADAM_V)
+    lay = {n: s for n, s in oracle.layout(cfg)}
+    offs, off = {}, 0
+    for n, s in oracle.layout(cfg):
+        offs[n] = off
+        off += int(np.prod(s))
+    f32 = np.float32
+    s_ad = oracle.adamw_scalars(cfg["lr"], cfg["beta1"], cfg["beta2"], cfg["eps"],
+                                cfg["weight_decay"], 1, 0.7)
+    for n in oracle.muon_matrices(cfg):
+        k = int(np.prod(lay[n]))
+        sl = slice(offs[n], offs[n] + k)
+        gs = (g[sl] * f32(0.7)).astype(f32)
+        _, buf = oracle.muon_momentum(gs, np.zeros(k, f32), hp.momentum)
+        assert np.array_equal(gm[sl].view(np.uint32), buf.view(np.uint32)), n
+        if n.startswith("h0."):
+            shape = lay[n]
+            d = {}
+            for bf in (True, False):
+                pr, _, _ = oracle.muon_matrix_update(p[sl].reshape(shape), gs.reshape(shape),
+                                                    np.zeros(shape, f32),
+                                                    np.zeros(max(shape), f32), hp, bf)
+                d[bf] = pr.reshape(-1).astype(np.float64) - p[sl]
+            d_got = gp[sl].astype(np.float64) - p[sl]
+            nx = np.linalg.norm(d[False])
+            e_dev = np.linalg.norm(d_got - d[False]) / nx
+            e_or = np.linalg.norm(d[True] - d[False]) / nx
+            c = float(d_got @ d[False] / (np.linalg.norm(d_got) * nx))
+            print(f"[full muon] {n} {shape} vs float64: device {e_dev:.4f} (cos {c:.5f}), "
+                  f"oracle bf16 {e_or:.4f}", flush=True)
+            assert e_dev <= 1.5 * e_or + 1e-3 and c >= 0.99, (n, e_dev, e_or, c)
+    for n in ("wte", "lnf.w"):
+        k = int(np.prod(lay[n]))
+        sl = slice(offs[n], offs[n] + k)
+        z = np.zeros(k, f32)
+        pr, mr, vr = oracle.adamw_update(p[sl], z, z, g[sl], s_ad)
+        assert np.array_equal(gp[sl].view(np.uint32), pr.view(np.uint32)), n
+        assert np.array_equal(gv[sl].view(np.uint32), vr.view(np.uint32)), n

@@ -248,3 +248,65 @@ def test_attention_fwd_bwd(prec, B, T, H, hd, left):
         assert err < (3e-2 if prec == gpt.BF16 else 1e-4), (i, err)
         cos = (a * r).sum() / np.sqrt((a * a).sum() * (r * r).sum())
         assert cos > (0.9995 if prec == gpt.BF16 else 1 - 1e-9), (i, cos)
+
+
+# ------------------------------------------------------------------ batched GEMM
+BATCH_CASES = [
+    # batch, M, N, K, a_trans, b_trans, epilogue
+    (3, 200, 136, 192, 0, 0, gpt.EPI_AXPBY),
+    (3, 130, 256, 64, 0, 1, gpt.EPI_AXPBY),
+    (3, 96, 136, 200, 1, 1, gpt.EPI_STORE),     # Gram layout, ragged K
+    (4, 3072, 1024, 256, 0, 0, gpt.EPI_AXPBY),  # 256-tiles
+    (4, 768, 768, 3072, 1, 1, gpt.EPI_STORE),   # the Gram product of a tall 3072 x 768 matrix
+]
+
+
+def _stacked(batch, rows, K, trans, dt, seed):
+    """`batch` operands op(X_z) [rows, K] stored one after another; returns the
+    device tensor, ld, byte stride and the exact values [batch, rows, K]."""
+    ld = -(-rows // 8) * 8 if trans else -(-K // 8) * 8
+    vals = np.stack([synth.normal((rows, K), seed + z, 1.0) for z in range(batch)])
+    if trans:
+        store = np.zeros((batch, K, ld), np.float32)
+        store[:, :, :rows] = vals.transpose(0, 2, 1)
+    else:
+        store = np.zeros((batch, rows, ld), np.float32)
+        store[:, :, :K] = vals
+    dev = to_dev(store, dt)
+    ex = rounded(dev)
+    ex = ex[:, :, :rows].transpose(0, 2, 1) if trans else ex[:, :, :K]
+    return dev, ld, dev[0].numel() * dev.element_size(), ex
+
+
+@pytest.mark.parametrize("prec", [gpt.FP32, gpt.BF16])
+@pytest.mark.parametrize("batch,M,N,K,at,bt,epi", BATCH_CASES)
+def test_gemm_batched(prec, batch, M, N, K, at, bt, epi):
+    """Batched products (the Newton-Schulz iteration's launches): every matrix
+    of the batch against its own product, with the AXPBY epilogue
+    out = alpha * acc + beta * aux."""
+    if prec == gpt.FP32 and M * N * K * batch > 1e9:
+        pytest.skip("the generic fp32 kernel is a correctness path; large shapes run in bf16")
+    dt = torch.bfloat16 if prec == gpt.BF16 else torch.float32
+    A, lda, sa, Ax = _stacked(batch, M, K, at, dt, 10)
+    B, ldb, sb, Bx = _stacked(batch, N, K, bt, dt, 20)
+    aux = to_dev(np.stack([synth.normal((M, N), 30 + z, 1.0) for z in range(batch)]), dt)
+    out = torch.zeros((batch, M, N), dtype=dt, device="cuda")
+    alpha, beta = 2.0315, -4.775
+    d = gpt.GemmDesc(precision=prec, M=M, N=N, K=K, A=A.data_ptr(), lda=lda, a_trans=at,
+                     a_rows=M, a_kvalid=K, B=B.data_ptr(), ldb=ldb, b_trans=bt, b_rows=N,
+                     b_kvalid=K, epilogue=epi, out=out.data_ptr(), ldo=N, alpha=alpha, beta=beta,
+                     batch=batch, stride_a=sa, stride_b=sb, stride_out=M * N * out.element_size())
+    if epi == gpt.EPI_AXPBY:
+        d.aux, d.ldaux, d.stride_aux = aux.data_ptr(), N, M * N * aux.element_size()
+    print(f"[gemm batched] prec={prec} batch={batch} {M}x{N}x{K} at={at} bt={bt} epi={epi}",
+          flush=True)
+    gpt.op_gemm(d)
+    torch.cuda.synchronize()
+    got = rounded(out)
+    ref = np.matmul(Ax, Bx.transpose(0, 2, 1))
+    if epi == gpt.EPI_AXPBY:
+        ref = alpha * ref + beta * rounded(aux)
+    tol = 1e-2 if prec == gpt.BF16 else 2e-5
+    for z in range(batch):
+        err = np.abs(got[z] - ref[z]).max() / np.abs(ref[z]).max()
+        assert err < tol, (z, err)
