@@ -91,7 +91,48 @@ __global__ void __launch_bounds__(256) adamw_kernel(int64_t n, float* __restrict
   }
 }
 
+// AdamW over a list of segments of the flat vectors in one launch.  seg holds
+// (begin, length, first block) per segment, lengths multiples of 4, each
+// segment covered by consecutive blocks of ADAM_SEG_CHUNK elements.
+constexpr int ADAM_SEG_CHUNK = 256 * 8;
+
+__global__ void __launch_bounds__(256) adamw_segments_kernel(
+    const int64_t* __restrict__ seg, int nseg, float* __restrict__ p, float* __restrict__ m,
+    float* __restrict__ v, const float* __restrict__ g, bf16_t* __restrict__ shadow,
+    AdamScalars s) {
+  int lo = 0, hi = nseg - 1;  // the last segment whose first block <= this block
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (seg[3 * mid + 2] <= (int64_t)blockIdx.x) lo = mid; else hi = mid - 1;
+  }
+  const int64_t b = seg[3 * lo], end = b + seg[3 * lo + 1];
+  const int64_t base = b + ((int64_t)blockIdx.x - seg[3 * lo + 2]) * ADAM_SEG_CHUNK;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t i = base + h * (ADAM_SEG_CHUNK / 2) + threadIdx.x * 4;
+    if (i + 3 < end) {
+      float4 p0 = *(float4*)(p + i), m0 = *(float4*)(m + i), v0 = *(float4*)(v + i);
+      const float4 g0 = *(const float4*)(g + i);
+      adam4(p0, m0, v0, g0, s);
+      store4_nt(p + i, p0);
+      store4_nt(m + i, m0);
+      store4_nt(v + i, v0);
+      if (shadow) *(uint2*)(shadow + i) = make_uint2(pack_bf2(p0.x, p0.y), pack_bf2(p0.z, p0.w));
+    }
+  }
+}
+
 }  // namespace
+
+int adamw_segment_blocks(int64_t len) { return (int)cdiv(len, ADAM_SEG_CHUNK); }
+
+hipError_t adamw_segments(const int64_t* d_seg, int nseg, int blocks, float* p, float* m,
+                          float* v, const float* g, uint16_t* shadow, AdamScalars sc,
+                          hipStream_t s) {
+  if (nseg <= 0 || blocks <= 0) return hipSuccess;
+  adamw_segments_kernel<<<(unsigned)blocks, 256, 0, s>>>(d_seg, nseg, p, m, v, g, shadow, sc);
+  return hipGetLastError();
+}
 
 hipError_t adamw(int64_t n, float* p, float* m, float* v, const float* g, uint16_t* shadow,
                  AdamScalars sc, hipStream_t s) {

@@ -131,7 +131,7 @@ struct Arena {
   int64_t X, ln_mean, ln_rstd;
   std::vector<int64_t> a1, qkv, att, lse, a2, u, g;
   int64_t xf, logits, loss_rows, loss, gres[2], gact[NGB], dC, dC2, dF[NGB], dqkv[NGB], dvec;
-  int64_t gemm_ws, gemm_ws_bytes, cs_part, ln_part, n_part, norm2, muon_ws;
+  int64_t gemm_ws, gemm_ws_bytes, cs_part, ln_part, n_part, norm2, muon_ws, adam_seg;
   int64_t e_counts, e_offsets, e_tile_sums, e_rank, e_perm, e_carry_first, e_carry_last, e_flags,
       e_last_tok;
   int64_t state_end, total;
@@ -209,6 +209,7 @@ Arena plan_arena(const gpt_config& c, int B, int T) {
     mw = std::max<int64_t>(mw, gpt::muon_workspace_bytes((int)rc.first, (int)rc.second, (int)L,
                                                          c.precision));
   a.muon_ws = take(mw);
+  a.adam_seg = take((4 * L + 4) * 3 * 8);  // AdamW segments of the Muon step
   a.total = o;
   return a;
 }
@@ -249,6 +250,10 @@ struct gpt_model {
   // the final LayerNorm and untied head); the next forward waits per group.
   std::vector<hipEvent_t> ev_adam;
   bool adam_pending = false;
+  // The runs of the flat vector outside the Muon matrices (AdamW in the
+  // Muon step): (begin, length, first block) triples, also on the device.
+  std::vector<int64_t> adam_seg;
+  int adam_seg_blocks = 0;
 
   template <typename T_> T_* at(int64_t off) const { return off < 0 ? nullptr : (T_*)(base + off); }
   float* P(int64_t e) const { return e < 0 ? nullptr : at<float>(ar.params) + e; }
@@ -713,6 +718,32 @@ int gpt_init(const gpt_config* cfg, int32_t B, int32_t T, void* d_arena, int64_t
     gpt_destroy(m);
     return fail(GPT_E_HIP, std::string("hipMemsetAsync: ") + hipGetErrorString(e));
   }
+  {
+    std::vector<std::pair<int64_t, int64_t>> mr;
+    for (int l = 0; l < cfg->n_layer; ++l)
+      for (const MuonKind& k : muon_kinds(m)) {
+        const int64_t b = k.off0 + l * (k.off1 - k.off0);
+        mr.push_back({b, b + (int64_t)k.rows * k.cols});
+      }
+    std::sort(mr.begin(), mr.end());
+    int64_t pos = 0;
+    for (size_t i = 0; i <= mr.size(); ++i) {
+      const int64_t end = i < mr.size() ? mr[i].first : m->N;
+      if (end > pos) {
+        m->adam_seg.insert(m->adam_seg.end(), {pos, end - pos, (int64_t)m->adam_seg_blocks});
+        m->adam_seg_blocks += gpt::adamw_segment_blocks(end - pos);
+      }
+      if (i < mr.size()) pos = mr[i].second;
+    }
+    // After the clear on the same stream; the host vector lives as long as the model.
+    e = hipMemcpyAsync(m->at<int64_t>(a.adam_seg), m->adam_seg.data(), m->adam_seg.size() * 8,
+                       hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+      gpt_destroy(m);
+      return fail(GPT_E_HIP, std::string("hipMemcpy: ") + hipGetErrorString(e));
+    }
+  }
   *out = m;
   g_err.clear();
   return GPT_OK;
@@ -837,23 +868,10 @@ int gpt_muon_step(gpt_model* m, const gpt_adamw_hp* adam, const gpt_muon_hp* muo
   float* pv = m->at<float>(m->ar.adam_v);
   uint16_t* sh = m->bf16 ? m->at<uint16_t>(m->ar.shadow) : nullptr;
   const std::vector<MuonKind> kinds = muon_kinds(m);
-  // AdamW on the runs of the flat vector between the Muon matrices.
-  std::vector<std::pair<int64_t, int64_t>> muon_ranges;
-  for (int l = 0; l < m->cfg.n_layer; ++l)
-    for (const MuonKind& k : kinds) {
-      const int64_t b = k.off0 + l * (k.off1 - k.off0);
-      muon_ranges.push_back({b, b + (int64_t)k.rows * k.cols});
-    }
-  std::sort(muon_ranges.begin(), muon_ranges.end());
-  const gpt::AdamScalars sc = adam_scalars(*adam);
-  int64_t pos = 0;
-  for (size_t i = 0; i <= muon_ranges.size(); ++i) {
-    const int64_t end = i < muon_ranges.size() ? muon_ranges[i].first : m->N;
-    if (end > pos)
-      HIP_TRY(gpt::adamw(end - pos, m->P(pos), pm + pos, pv + pos, m->G(pos),
-                         sh ? sh + pos : nullptr, sc, s));
-    if (i < muon_ranges.size()) pos = muon_ranges[i].second;
-  }
+  // AdamW on the runs of the flat vector between the Muon matrices, one launch.
+  HIP_TRY(gpt::adamw_segments(m->at<int64_t>(m->ar.adam_seg), (int)(m->adam_seg.size() / 3),
+                              m->adam_seg_blocks, m->P(0), pm, pv, m->G(0), sh,
+                              adam_scalars(*adam), s));
   gpt::MuonScalars ms;
   ms.grad_scale = (float)adam->grad_scale;
   ms.mu = (float)muon->momentum;

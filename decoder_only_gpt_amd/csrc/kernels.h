@@ -70,6 +70,13 @@ hipError_t to_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t s);
 struct AdamScalars { float omb1, omb2, decay, step_size, sbc2, eps, scale; };
 hipError_t adamw(int64_t n, float* p, float* m, float* v, const float* g, uint16_t* shadow,
                  AdamScalars sc, hipStream_t s);
+// AdamW over segments of the flat vectors in one launch.  d_seg (device):
+// (begin, length, first block) per segment; lengths multiples of 4; the
+// first blocks are the running sum of adamw_segment_blocks(length).
+int adamw_segment_blocks(int64_t len);
+hipError_t adamw_segments(const int64_t* d_seg, int nseg, int blocks, float* p, float* m,
+                          float* v, const float* g, uint16_t* shadow, AdamScalars sc,
+                          hipStream_t s);
 
 // Muon for one kind of block matrix across the layers (muon.hip).  Matrix l
 // (l < count) of shape [rows, cols] sits at element offset l * ls of the

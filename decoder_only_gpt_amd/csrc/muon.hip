@@ -124,21 +124,32 @@ __global__ void __launch_bounds__(MU_THREADS) muon_row_stats_kernel(const ActT* 
   if (lane == 0) s[(long)l * r + row] = a / (float)c;
 }
 
-// Wide and square matrices (r <= c): one thread per column, s_j over the r rows.
+// Wide and square matrices (r <= c): a block takes 64 columns; its 4 waves
+// sum every 4th row (one 64-column row segment per wave and step), then the
+// four partial sums are added in a fixed order.
 template <typename ActT>
 __global__ void __launch_bounds__(MU_THREADS) muon_col_stats_kernel(const ActT* __restrict__ X,
                                                                    int r, int c,
                                                                    float* __restrict__ s) {
+  __shared__ float part[MU_THREADS / 64][64];
   const int l = blockIdx.y;
-  const int col = blockIdx.x * MU_THREADS + threadIdx.x;
-  if (col >= c) return;
-  const ActT* x = X + (long)l * r * c + col;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = blockIdx.x * 64 + lane;
   float a = 0.f;
-  for (int i = 0; i < r; ++i) {
-    const float v = Act<ActT>::load(x, (long)i * c);
-    a += v * v;
+  if (col < c) {
+    const ActT* x = X + (long)l * r * c + col;
+    for (int i = wave; i < r; i += MU_THREADS / 64) {
+      const float v = Act<ActT>::load(x, (long)i * c);
+      a += v * v;
+    }
   }
-  s[(long)l * c + col] = a / (float)r;
+  part[wave][lane] = a;
+  __syncthreads();
+  if (wave == 0 && col < c) {
+    float t = part[0][lane];
+    for (int w = 1; w < MU_THREADS / 64; ++w) t += part[w][lane];
+    s[(long)l * c + col] = t / (float)r;
+  }
 }
 
 // One block per matrix: the running second moment (first n_long entries of
@@ -180,15 +191,20 @@ __global__ void __launch_bounds__(MU_THREADS) muon_update_kernel(
   bf16_t* sh = shadow ? shadow + l * ls : nullptr;
   const ActT* xl = X + l * rc;
   const float* rl = rfac + (long)l * (tall ? r : c);
-  for (long i = (long)blockIdx.x * MU_THREADS + threadIdx.x; i < rc;
-       i += (long)gridDim.x * MU_THREADS) {
+  // 4 consecutive elements of one row per thread (c % 4 == 0).
+  for (long i = ((long)blockIdx.x * MU_THREADS + threadIdx.x) * 4; i < rc;
+       i += (long)gridDim.x * MU_THREADS * 4) {
     const int row = (int)(i / c), col = (int)(i - (long)row * c);
-    const float y = Act<ActT>::load(xl, i) * rl[tall ? row : col];
-    const float pv = pl[i];
-    const float dec = (y * pv >= 0.f) ? lrwd * pv : 0.f;
-    const float pn = pv - (lr * y + dec);
-    pl[i] = pn;
-    if (sh) sh[i] = f2bf(pn);
+    float4 p4 = *(const float4*)(pl + i);
+    float pv[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float y = Act<ActT>::load(xl, i + k) * rl[tall ? row : col + k];
+      const float dec = (y * pv[k] >= 0.f) ? lrwd * pv[k] : 0.f;
+      pv[k] = pv[k] - (lr * y + dec);
+    }
+    *(float4*)(pl + i) = make_float4(pv[0], pv[1], pv[2], pv[3]);
+    if (sh) *(uint2*)(sh + i) = make_uint2(pack_bf2(pv[0], pv[1]), pack_bf2(pv[2], pv[3]));
   }
 }
 
@@ -307,7 +323,7 @@ hipError_t muon_matrices(const MuonGroup& gp, const MuonScalars& sc, int prec, v
     else
       muon_row_stats_kernel<float><<<gs, MU_THREADS, 0, s>>>((const float*)X, r, c, st);
   } else {
-    dim3 gs((unsigned)((c + MU_THREADS - 1) / MU_THREADS), (unsigned)L);
+    dim3 gs((unsigned)((c + 63) / 64), (unsigned)L);
     if (bf16)
       muon_col_stats_kernel<bf16_t><<<gs, MU_THREADS, 0, s>>>((const bf16_t*)X, r, c, st);
     else

@@ -2,6 +2,8 @@
 
     python -m decoder_only_gpt_amd.profile_run step [--config gpt2_124m] [--steps 3]
         a few training steps (forward, loss, backward, norm, AdamW) of a preset
+    python -m decoder_only_gpt_amd.profile_run muon [--config gpt2_124m] [--steps 3]
+        a few hybrid Muon + AdamW optimizer steps on fixed synthetic gradients
     python -m decoder_only_gpt_amd.profile_run copy [--mib 1024]
         one plain device-to-device copy of a known size (counter calibration)
     python -m decoder_only_gpt_amd.profile_run summarize-stats CSV OUT --command "..."
@@ -56,6 +58,21 @@ def run_step(config: str, steps: int, concurrent: bool = False):
     if not concurrent:
         m.profile_end()
     torch.cuda.synchronize()
+
+
+def run_muon(config: str, steps: int):
+    """A few hybrid optimizer steps (Muon on the block matrices, AdamW on the rest)."""
+    import torch
+    from decoder_only_gpt_amd import gpt, presets, synth
+    cfg = presets.preset(config)
+    m = gpt.Model(cfg)
+    m.set_params(synth.init_params(cfg, seed=0))
+    g = torch.from_numpy(synth.normal(m.n_params, seed=5, scale=1e-3)).cuda()
+    for i in range(steps):
+        m.set_buffer(gpt.BUF_GRADS, g)
+        m.muon_step(i + 1, 1.0)
+        torch.cuda.synchronize()
+        print(f"muon step {i}", flush=True)
 
 
 def run_copy(mib: int):
@@ -125,6 +142,9 @@ def main():
     p.add_argument("--steps", type=int, default=3)
     p.add_argument("--concurrent", action="store_true",
                    help="weight gradients on their side stream, as in training")
+    p = sub.add_parser("muon")
+    p.add_argument("--config", default="gpt2_124m")
+    p.add_argument("--steps", type=int, default=3)
     p = sub.add_parser("copy")
     p.add_argument("--mib", type=int, default=1024)
     p = sub.add_parser("summarize-stats")
@@ -146,6 +166,9 @@ def main():
     if a.cmd == "step":
         sys.path.insert(0, ROOT)
         run_step(a.config, a.steps, a.concurrent)
+    elif a.cmd == "muon":
+        sys.path.insert(0, ROOT)
+        run_muon(a.config, a.steps)
     elif a.cmd == "copy":
         run_copy(a.mib)
     elif a.cmd == "summarize-stats":
