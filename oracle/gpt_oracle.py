@@ -45,7 +45,8 @@ __all__ = [
     "attention_bwd", "cross_entropy_fwd_bwd", "visible", "step", "logits",
     "loss_rows", "cosine_lr", "train_steps", "NS_COEFFS", "muon_matrices",
     "orthogonalize", "muon_momentum", "muon_second_moment", "cautious_update",
-    "muon_matrix_update", "MuonHP", "muon_hybrid_step",
+    "muon_matrix_update", "MuonHP", "muon_hybrid_step", "sample_token", "next_token_logits",
+    "generate",
 ]
 
 
@@ -649,3 +650,62 @@ def muon_hybrid_step(cfg, flat_params, m, v, flat_grads, adam_hp: dict, muon_hp:
         else:
             p[sl], m[sl], v[sl] = adamw_update(p[sl], m[sl], v[sl], g[sl], s)
     return p, m, v
+
+
+# --------------------------------------------------------------------------
+# sampling (nanoGPT README, "sampling / inference": sample.py draws
+# --num_samples continuations of --max_new_tokens tokens after a --start
+# prompt; llm.c summary, "Sampling": unconditional / conditional sampling)
+# --------------------------------------------------------------------------
+def sample_token(z, V: int, temperature: float, top_k: int, u: float) -> int:
+    """One draw from the logits z (entries >= V are padding and never drawn).
+    temperature == 0: the argmax (the lowest index among equal maxima).
+    Otherwise w = z[:V] / temperature; when 0 < top_k < V only entries >= the
+    top_k-th largest w are kept (ties at the threshold kept);
+    p_i = exp(w_i - max w) over the kept entries; the token is the smallest
+    i with p_0 + ... + p_i > u * sum(p) (inverse CDF, u in [0, 1)).
+    Readings: the pages name temperature-free "sampling"; temperature and
+    top-k are the usual knobs of sample.py-style sampling and reduce to
+    plain softmax sampling at temperature 1, top_k 0."""
+    z = np.asarray(z, np.float64)[:V]
+    if temperature == 0.0:
+        return int(np.argmax(z))
+    w = z / temperature
+    keep = np.ones(V, bool)
+    if 0 < top_k < V:
+        thr = np.sort(w)[::-1][top_k - 1]
+        keep = w >= thr
+    m = w[keep].max()
+    p = np.where(keep, np.exp(w - m), 0.0)
+    c = np.cumsum(p)
+    target = u * c[-1]
+    i = int(np.searchsorted(c, target, side="right"))
+    return min(i, int(np.flatnonzero(keep)[-1]))
+
+
+def next_token_logits(cfg, flat_params, tokens, dtype=np.float64):
+    """Logits of the last position of each row of tokens [B, T] from a full
+    forward of the sequence so far (no cache: the definition a cached
+    decoder must reproduce)."""
+    tokens = np.asarray(tokens)
+    B, T = tokens.shape
+    z = logits(cfg, flat_params, tokens, dtype)
+    return z.reshape(B, T, -1)[:, -1, :]
+
+
+def generate(cfg, flat_params, prompt, n_new: int, temperature: float, top_k: int, uniforms,
+             dtype=np.float64):
+    """Autoregressive continuation of prompt [B, T0] by n_new tokens; draw s of
+    row b uses uniforms[b, s].  Reading: the sequence never exceeds
+    block_size (no cropping of the context).  Returns [B, T0 + n_new]."""
+    tokens = np.array(prompt, np.int32)
+    B, T0 = tokens.shape
+    if T0 + n_new > cfg["block_size"]:
+        raise ValueError("prompt + new tokens exceed block_size")
+    u = np.asarray(uniforms, np.float64).reshape(B, n_new)
+    for s_ in range(n_new):
+        z = next_token_logits(cfg, flat_params, tokens, dtype)
+        nxt = np.array([sample_token(z[b], cfg["vocab_size"], temperature, top_k, u[b, s_])
+                        for b in range(B)], np.int32)
+        tokens = np.concatenate([tokens, nxt[:, None]], axis=1)
+    return tokens

@@ -454,3 +454,66 @@ def test_muon_hybrid_step_routes_tensors():
             pr, mr, vr = oracle.adamw_update(p0[sl], z[sl], z[sl], g[sl], s)
             assert np.array_equal(p[sl], pr) and np.array_equal(m[sl], mr)
         off += n
+
+
+# ---------------------------------------------------------------- sampling
+def test_sample_token_uniform_logits_is_floor_uV():
+    """Equal logits: the inverse CDF of the uniform distribution, token = floor(u V)."""
+    V = 37
+    z = np.zeros(40)
+    z[V:] = 50.0  # padding never drawn
+    for u in (np.arange(200) + 0.5) / 200:
+        assert oracle.sample_token(z, V, 1.0, 0, u) == int(np.floor(u * V))
+    # ties at the top-k threshold are kept: top_k = 5 of equal values keeps all of them
+    assert oracle.sample_token(z, V, 0.7, 5, 0.999) == V - 1
+
+
+def test_sample_token_greedy_cases():
+    rng = np.random.default_rng(0)
+    z = rng.standard_normal(50)
+    z[17] = z.max() + 0.1
+    z[30] = z[17]  # equal maxima: the lower index wins
+    for u in (0.0, 0.3, 0.999):
+        assert oracle.sample_token(z, 50, 0.0, 0, u) == 17
+        assert oracle.sample_token(z, 50, 1.3, 1, u) in (17, 30)   # top-1 keeps both tied maxima
+    z[30] -= 1e-3
+    for u in (0.0, 0.5, 0.999):
+        assert oracle.sample_token(z, 50, 1.0, 1, u) == 17
+        assert oracle.sample_token(z, 50, 1e-4, 0, u) == 17      # temperature -> 0: the argmax
+
+
+@pytest.mark.parametrize("temperature,top_k", [(1.0, 0), (0.6, 0), (1.0, 3)])
+def test_sample_token_frequencies_follow_softmax(temperature, top_k):
+    """u on an even grid of N points: each token's share differs from its
+    (top-k renormalized) softmax probability by at most 1/N."""
+    rng = np.random.default_rng(1)
+    V, N = 12, 20000
+    z = rng.standard_normal(V) * 2
+    w = z / temperature
+    keep = np.ones(V, bool)
+    if top_k:
+        keep = w >= np.sort(w)[::-1][top_k - 1]
+    p = np.where(keep, np.exp(w - w.max()), 0)
+    p /= p.sum()
+    counts = np.bincount([oracle.sample_token(z, V, temperature, top_k, (i + 0.5) / N)
+                          for i in range(N)], minlength=V)
+    assert np.abs(counts / N - p).max() <= 1.0 / N + 1e-12
+    if top_k:
+        assert counts[~keep].sum() == 0
+
+
+def test_generate_composes_forward_and_sampler():
+    cfg = presets.preset("tiny", B=2, T=8)
+    p = synth.init_params(cfg, seed=3, perturb=True)
+    prompt, _ = synth.tokens(cfg, B=2, T=5, seed=4)
+    u = np.random.default_rng(5).random((2, 6))
+    out = oracle.generate(cfg, p, prompt, 6, 0.9, 10, u)
+    assert out.shape == (2, 11) and np.array_equal(out[:, :5], prompt)
+    assert np.array_equal(oracle.generate(cfg, p, prompt, 3, 0.9, 10, u[:, :3]), out[:, :8])
+    for s_ in range(6):
+        z = oracle.next_token_logits(cfg, p, out[:, :5 + s_])
+        for b in range(2):
+            assert out[b, 5 + s_] == oracle.sample_token(z[b], cfg["vocab_size"], 0.9, 10, u[b, s_])
+    # the last position's logits do not depend on anything after it (causality)
+    z_full = oracle.logits(cfg, p, out).reshape(2, 11, -1)
+    assert np.allclose(oracle.next_token_logits(cfg, p, out[:, :7]), z_full[:, 6], atol=1e-12)
