@@ -20,7 +20,7 @@ OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgptmi.so")
 ARCH = "gfx950"
 
-SOURCES = ["engine.hip", "gemm.hip", "attention.hip", "rowwise.hip", "adamw.hip", "muon.hip"]
+SOURCES = ["engine.hip", "gemm.hip", "attention.hip", "rowwise.hip", "adamw.hip", "muon.hip", "decode.hip"]
 # Per-file extra flags.  The AdamW update and the Muon momentum must round every
 # operation on their own.
 EXTRA = {"adamw.hip": ["-ffp-contract=off"], "muon.hip": ["-ffp-contract=off"]}

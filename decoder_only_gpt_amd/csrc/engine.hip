@@ -749,6 +749,215 @@ int gpt_init(const gpt_config* cfg, int32_t B, int32_t T, void* d_arena, int64_t
   return GPT_OK;
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------- generation
+struct gpt_gen {
+  gpt_model* m;
+  int B, Tmax, pos;
+  char* base;
+  int64_t kc, vc, x, a, qkv, att, u, gact, mean, rstd, logits, tok, total;
+};
+
+namespace {
+
+int64_t gen_layout(const gpt_model* m, int B, int Tmax, gpt_gen* g) {
+  const int64_t act = m->bf16 ? 2 : 4, C = m->C, F = m->F, L = m->cfg.n_layer;
+  int64_t o = 0;
+  auto take = [&](int64_t bytes) { int64_t r = o; o = align_up(o + bytes, ALIGN); return r; };
+  g->kc = take(L * B * m->H * Tmax * m->hd * act);
+  g->vc = take(L * B * m->H * Tmax * m->hd * act);
+  g->x = take(B * C * 4);
+  g->a = take(B * C * act);
+  g->qkv = take(B * 3 * C * act);
+  g->att = take(B * C * act);
+  g->u = take(B * F * act);
+  g->gact = take(B * F * act);
+  g->mean = take(B * 4);
+  g->rstd = take(B * 4);
+  g->logits = take(B * m->Vq * act);
+  g->tok = take(B * 4);
+  g->total = o;
+  return o;
+}
+
+int gen_check(const gpt_model* m, int B, int Tmax) {
+  if (!m) return fail(GPT_E_INVALID, "NULL model");
+  if (B < 1 || Tmax < 1 || Tmax > m->cfg.block_size)
+    return fail(GPT_E_INVALID, "need B >= 1 and 1 <= Tmax <= block_size");
+  if (!gpt::attn_decode_supported((int)m->hd))
+    return fail(GPT_E_UNSUPPORTED, "head_dim must be 32, 64 or 128 for generation");
+  return GPT_OK;
+}
+
+// out[B, N] = a[B, K] . W[N, K]^T with the given epilogue (rows of the decode step).
+hipError_t gen_linear(const gpt_gen* g, const void* a, int64_t K, int64_t w_off, int64_t N,
+                      int64_t b_off, int epi, void* out, int64_t ldo, const float* resid,
+                      void* aux, hipStream_t s) {
+  const gpt_model* m = g->m;
+  gpt_gemm_desc d;
+  std::memset(&d, 0, sizeof(d));
+  d.precision = m->cfg.precision;
+  d.gelu_tanh = m->cfg.gelu_tanh;
+  d.M = g->B; d.N = (int)N; d.K = (int)K;
+  d.A = a; d.lda = K; d.a_rows = g->B; d.a_kvalid = (int)K;
+  d.B = m->W(w_off); d.ldb = K; d.b_rows = (int)N; d.b_kvalid = (int)K;
+  d.epilogue = epi;
+  d.bias = b_off >= 0 ? m->P(b_off) : nullptr;
+  d.resid = resid;
+  d.out = out; d.ldo = ldo;
+  d.aux = aux; d.ldaux = aux ? ldo : 0;
+  return gpt::gemm(d, s);
+}
+
+int gen_step(gpt_gen* g, const int32_t* d_tok, hipStream_t s) {
+  gpt_model* m = g->m;
+  if (g->pos >= g->Tmax) return fail(GPT_E_INVALID, "the cache is full (Tmax tokens)");
+  int rc = wait_adam(m, s, -1);
+  if (rc != GPT_OK) return rc;
+  const gpt_config& c = m->cfg;
+  const int prec = m->prec();
+  const int B = g->B;
+  const int64_t C = m->C, F = m->F, act = m->bf16 ? 2 : 4;
+  char* base = g->base;
+  float* x = (float*)(base + g->x);
+  void* a = base + g->a;
+  float* mean = (float*)(base + g->mean);
+  float* rstd = (float*)(base + g->rstd);
+  const int64_t cache_layer = (int64_t)B * m->H * g->Tmax * m->hd * act;
+  HIP_TRY(gpt::gen_embed(d_tok, m->P(m->pl.wte), m->P(m->pl.wpe), g->pos, B, (int)C, x, s));
+  for (int l = 0; l < c.n_layer; ++l) {
+    const LayerOff& L = m->pl.layer[l];
+    HIP_TRY(gpt::layernorm_fwd(prec, x, m->P(L.ln1w), m->P(L.ln1b), B, (int)C, c.ln_eps, a, mean,
+                               rstd, s));
+    HIP_TRY(gen_linear(g, a, C, L.qkvw, 3 * C, L.qkvb, GPT_EPI_STORE, base + g->qkv, 3 * C,
+                       nullptr, nullptr, s));
+    HIP_TRY(gpt::attn_decode(prec, (int)m->hd, base + g->qkv, base + g->kc + l * cache_layer,
+                             base + g->vc + l * cache_layer, g->pos, g->Tmax, B, (int)m->H,
+                             c.window_left[l], base + g->att, s));
+    HIP_TRY(gen_linear(g, base + g->att, C, L.projw, C, L.projb, GPT_EPI_RESIDUAL, x, C, x,
+                       nullptr, s));
+    HIP_TRY(gpt::layernorm_fwd(prec, x, m->P(L.ln2w), m->P(L.ln2b), B, (int)C, c.ln_eps, a, mean,
+                               rstd, s));
+    HIP_TRY(gen_linear(g, a, C, L.fcw, F, L.fcb, GPT_EPI_GELU, base + g->u, F, nullptr,
+                       base + g->gact, s));
+    HIP_TRY(gen_linear(g, base + g->gact, F, L.fcpw, C, L.fcpb, GPT_EPI_RESIDUAL, x, C, x,
+                       nullptr, s));
+  }
+  HIP_TRY(gpt::layernorm_fwd(prec, x, m->P(m->pl.lnfw), m->P(m->pl.lnfb), B, (int)C, c.ln_eps, a,
+                             mean, rstd, s));
+  HIP_TRY(gen_linear(g, a, C, m->pl.lmw, m->Vp, -1, GPT_EPI_STORE, base + g->logits, m->Vq,
+                     nullptr, nullptr, s));
+  g->pos += 1;
+  return GPT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gpt_gen_plan(const gpt_model* m, int32_t B, int32_t Tmax, int64_t* bytes) {
+  int rc = gen_check(m, B, Tmax);
+  if (rc != GPT_OK) return rc;
+  if (!bytes) return fail(GPT_E_INVALID, "NULL bytes");
+  gpt_gen g;
+  *bytes = gen_layout(m, B, Tmax, &g);
+  return GPT_OK;
+}
+
+int gpt_gen_init(gpt_model* m, int32_t B, int32_t Tmax, void* d_arena, int64_t arena_bytes,
+                 void* stream, gpt_gen** out) {
+  int rc = gen_check(m, B, Tmax);
+  if (rc != GPT_OK) return rc;
+  if (!d_arena || !out) return fail(GPT_E_INVALID, "NULL arena or out");
+  if (((uintptr_t)d_arena) % ALIGN) return fail(GPT_E_INVALID, "arena must be 256-byte aligned");
+  gpt_gen* g = new gpt_gen();
+  g->m = m;
+  g->B = B;
+  g->Tmax = Tmax;
+  g->pos = 0;
+  g->base = (char*)d_arena;
+  if (arena_bytes < gen_layout(m, B, Tmax, g)) {
+    delete g;
+    return fail(GPT_E_INVALID, "generation arena too small");
+  }
+  hipError_t e = hipMemsetAsync(d_arena, 0, (size_t)g->total, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    delete g;
+    return fail(GPT_E_HIP, std::string("hipMemsetAsync: ") + hipGetErrorString(e));
+  }
+  *out = g;
+  return GPT_OK;
+}
+
+int gpt_gen_reset(gpt_gen* g) {
+  if (!g) return fail(GPT_E_INVALID, "NULL context");
+  g->pos = 0;
+  return GPT_OK;
+}
+
+int gpt_gen_step(gpt_gen* g, const int32_t* d_tokens, void* stream) {
+  if (!g || !d_tokens) return fail(GPT_E_INVALID, "NULL argument");
+  return gen_step(g, d_tokens, (hipStream_t)stream);
+}
+
+int gpt_gen_logits(gpt_gen* g, void* h_dst, int64_t* ld, void* stream) {
+  if (!g || !h_dst || !ld) return fail(GPT_E_INVALID, "NULL argument");
+  const int64_t act = g->m->bf16 ? 2 : 4;
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(hipMemcpyAsync(h_dst, g->base + g->logits, (size_t)(g->B * g->m->Vq * act),
+                         hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  *ld = g->m->Vq;
+  return GPT_OK;
+}
+
+int gpt_gen_sample(gpt_gen* g, float temperature, int32_t top_k, const float* d_u,
+                   int64_t u_stride, int32_t* d_tokens, void* stream) {
+  if (!g || !d_tokens || (!d_u && temperature != 0.f)) return fail(GPT_E_INVALID, "NULL argument");
+  if (!(temperature >= 0.f) || top_k < 0) return fail(GPT_E_INVALID, "bad temperature / top_k");
+  if (g->pos == 0) return fail(GPT_E_STATE, "sample needs a step first");
+  HIP_TRY(gpt::sample(g->m->prec(), g->base + g->logits, g->m->Vq, g->B, g->m->cfg.vocab_size,
+                      temperature, top_k, d_u, u_stride, d_tokens, nullptr, 0, 0,
+                      (hipStream_t)stream));
+  return GPT_OK;
+}
+
+int gpt_generate(gpt_gen* g, const int32_t* d_prompt, int32_t T0, int32_t n_new,
+                 float temperature, int32_t top_k, const float* d_uniforms, int32_t* d_out,
+                 void* stream) {
+  if (!g || !d_prompt || !d_out || (!d_uniforms && n_new > 0 && temperature != 0.f))
+    return fail(GPT_E_INVALID, "NULL argument");
+  if (T0 < 1 || n_new < 0 || T0 + n_new > g->Tmax)
+    return fail(GPT_E_INVALID, "need T0 >= 1 and T0 + n_new <= Tmax");
+  if (!(temperature >= 0.f) || top_k < 0) return fail(GPT_E_INVALID, "bad temperature / top_k");
+  hipStream_t s = (hipStream_t)stream;
+  const int Ltot = T0 + n_new;
+  int32_t* tok = (int32_t*)(g->base + g->tok);
+  g->pos = 0;
+  HIP_TRY(gpt::copy_prompt(d_prompt, T0, Ltot, g->B, d_out, s));
+  for (int t = 0; t < T0; ++t) {
+    HIP_TRY(gpt::gather_column(d_out, Ltot, t, g->B, tok, s));
+    int rc = gen_step(g, tok, s);
+    if (rc != GPT_OK) return rc;
+  }
+  for (int k = 0; k < n_new; ++k) {
+    HIP_TRY(gpt::sample(g->m->prec(), g->base + g->logits, g->m->Vq, g->B,
+                        g->m->cfg.vocab_size, temperature, top_k,
+                        d_uniforms ? d_uniforms + k : nullptr, n_new, tok, d_out, Ltot, T0 + k, s));
+    if (k + 1 < n_new) {
+      int rc = gen_step(g, tok, s);
+      if (rc != GPT_OK) return rc;
+    }
+  }
+  return GPT_OK;
+}
+
+int gpt_gen_destroy(gpt_gen* g) {
+  delete g;
+  return GPT_OK;
+}
+
 int gpt_destroy(gpt_model* m) {
   if (m) {
     for (hipEvent_t e : m->ev_pool) (void)hipEventDestroy(e);

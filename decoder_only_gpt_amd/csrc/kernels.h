@@ -78,6 +78,25 @@ hipError_t adamw_segments(const int64_t* d_seg, int nseg, int blocks, float* p, 
                           float* v, const float* g, uint16_t* shadow, AdamScalars sc,
                           hipStream_t s);
 
+// Generation (decode.hip).  x[b] = wte[tok[b]] + wpe[pos].
+hipError_t gen_embed(const int32_t* tok, const float* wte, const float* wpe, int pos, int B, int C,
+                     float* x, hipStream_t s);
+// One query per (sequence b, head h) at position pos: qkv [B, 3*H*hd] (act);
+// caches [B, H, Tmax, hd] (act) of this layer; row pos of both caches is
+// written from qkv; out [B, H*hd] (act).
+bool attn_decode_supported(int hd);
+hipError_t attn_decode(int prec, int hd, const void* qkv, void* kc, void* vc, int pos, int Tmax,
+                       int B, int H, int left, void* out, hipStream_t s);
+// Per row b of logits [B, ldz] (act): token from the first V entries with
+// u[b * u_stride]; written to tok[b] and, if seq, seq[b * seq_stride + seq_col].
+hipError_t sample(int prec, const void* logits, long ldz, int B, int V, float temperature,
+                  int top_k, const float* u, long u_stride, int32_t* tok, int32_t* seq,
+                  long seq_stride, int seq_col, hipStream_t s);
+hipError_t gather_column(const int32_t* seq, long stride, int col, int B, int32_t* tok,
+                         hipStream_t s);
+hipError_t copy_prompt(const int32_t* prompt, int T0, int Ltot, int B, int32_t* out,
+                       hipStream_t s);
+
 // Muon for one kind of block matrix across the layers (muon.hip).  Matrix l
 // (l < count) of shape [rows, cols] sits at element offset l * ls of the
 // parameter, gradient, momentum (buf) and second-moment (v, first max(rows,

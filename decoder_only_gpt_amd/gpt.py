@@ -28,7 +28,8 @@ EXPORTS = [
     "gpt_plan", "gpt_flops_per_token", "gpt_init", "gpt_forward", "gpt_loss",
     "gpt_loss_device_ptr", "gpt_backward", "gpt_grad_norm", "gpt_adamw_step", "gpt_muon_step",
     "gpt_get_buffer",
-    "gpt_set_buffer", "gpt_destroy", "gpt_last_error", "gpt_op_gemm", "gpt_op_attention_fwd",
+    "gpt_set_buffer", "gpt_destroy", "gpt_gen_plan", "gpt_gen_init", "gpt_gen_reset",
+    "gpt_gen_step", "gpt_gen_logits", "gpt_gen_sample", "gpt_generate", "gpt_gen_destroy", "gpt_last_error", "gpt_op_gemm", "gpt_op_attention_fwd",
     "gpt_op_attention_bwd", "gpt_op_adamw", "gpt_profile_begin", "gpt_profile_end",
 ]
 KERNEL_KINDS = ["gemm", "gemm_splitk", "attn_fwd", "attn_bwd", "layernorm", "cross_entropy",
@@ -129,6 +130,14 @@ def lib():
         "gpt_grad_norm": ([vp, vp, ctypes.POINTER(ctypes.c_double)], i32),
         "gpt_adamw_step": ([vp, ctypes.POINTER(AdamHP), vp], i32),
         "gpt_muon_step": ([vp, ctypes.POINTER(AdamHP), ctypes.POINTER(MuonHP), vp], i32),
+        "gpt_gen_plan": ([vp, i32, i32, ctypes.POINTER(i64)], i32),
+        "gpt_gen_init": ([vp, i32, i32, vp, i64, vp, ctypes.POINTER(vp)], i32),
+        "gpt_gen_reset": ([vp], i32),
+        "gpt_gen_step": ([vp, vp, vp], i32),
+        "gpt_gen_logits": ([vp, vp, ctypes.POINTER(i64), vp], i32),
+        "gpt_gen_sample": ([vp, ctypes.c_float, i32, vp, i64, vp, vp], i32),
+        "gpt_generate": ([vp, vp, i32, i32, ctypes.c_float, i32, vp, vp, vp], i32),
+        "gpt_gen_destroy": ([vp], i32),
         "gpt_get_buffer": ([vp, i32, vp, i32, vp], i32),
         "gpt_set_buffer": ([vp, i32, vp, i32, vp], i32),
         "gpt_destroy": ([vp], i32),
@@ -305,6 +314,69 @@ class Model:
                 scale = clip / norm
         self.adamw_step(self.step_t, scale)
         return dict(loss=loss, norm=norm, scale=scale)
+
+
+class Generator:
+    """Key/value-cache generation on a model's weights (B sequences of up to
+    Tmax tokens); methods map 1:1 onto the gpt_gen_* entry points."""
+
+    def __init__(self, model: Model, B: int, Tmax: int):
+        import torch
+        self.model, self.B, self.Tmax = model, B, Tmax
+        n = ctypes.c_int64()
+        _check(lib().gpt_gen_plan(model.h, B, Tmax, ctypes.byref(n)))
+        self.arena = torch.empty(int(n.value), dtype=torch.uint8, device="cuda")
+        h = ctypes.c_void_p()
+        _check(lib().gpt_gen_init(model.h, B, Tmax, ctypes.c_void_p(self.arena.data_ptr()),
+                                  int(n.value), _stream(), ctypes.byref(h)))
+        self.h = h
+        self._keep = []
+
+    def __del__(self):
+        h = getattr(self, "h", None)
+        if h is not None and _LIB is not None:
+            _LIB.gpt_gen_destroy(h)
+            self.h = None
+
+    def reset(self):
+        _check(lib().gpt_gen_reset(self.h))
+
+    def step(self, tokens):
+        """tokens: device int32 tensor [B]."""
+        self._keep = [tokens]
+        _check(lib().gpt_gen_step(self.h, ctypes.c_void_p(tokens.data_ptr()), _stream()))
+
+    def logits(self) -> np.ndarray:
+        """Last step's logits as float32 [B, vocab_size]."""
+        bf16 = self.model.cfg["precision"] == "bf16"
+        Vq = -(-self.model.cfg["padded_vocab"] // 64) * 64
+        raw = np.empty(self.B * Vq, np.uint16 if bf16 else np.float32)
+        ld = ctypes.c_int64()
+        _check(lib().gpt_gen_logits(self.h, raw.ctypes.data_as(ctypes.c_void_p), ctypes.byref(ld),
+                                    _stream()))
+        z = (raw.astype(np.uint32) << 16).view(np.float32) if bf16 else raw
+        return z.reshape(self.B, int(ld.value))[:, :self.model.cfg["vocab_size"]]
+
+    def sample(self, temperature: float, top_k: int, u=None, u_stride: int = 1):
+        """Device int32 tensor [B] of drawn tokens; u: device float tensor (or None for greedy)."""
+        import torch
+        out = torch.empty(self.B, dtype=torch.int32, device="cuda")
+        _check(lib().gpt_gen_sample(self.h, float(temperature), int(top_k),
+                                    None if u is None else ctypes.c_void_p(u.data_ptr()),
+                                    int(u_stride), ctypes.c_void_p(out.data_ptr()), _stream()))
+        return out
+
+    def generate(self, prompt, n_new: int, temperature: float, top_k: int, uniforms=None):
+        """prompt: device int32 [B, T0]; uniforms: device float [B, n_new] (or None for
+        greedy).  Returns the device int32 tensor [B, T0 + n_new]."""
+        import torch
+        B, T0 = prompt.shape
+        out = torch.empty((B, T0 + n_new), dtype=torch.int32, device="cuda")
+        _check(lib().gpt_generate(self.h, ctypes.c_void_p(prompt.data_ptr()), int(T0), int(n_new),
+                                  float(temperature), int(top_k),
+                                  None if uniforms is None else ctypes.c_void_p(uniforms.data_ptr()),
+                                  ctypes.c_void_p(out.data_ptr()), _stream()))
+        return out
 
 
 # ---------------------------------------------------------------- single ops

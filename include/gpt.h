@@ -234,6 +234,48 @@ int gpt_profile_end(gpt_model* m, void* stream, gpt_kernel_stats* out, gpt_kerne
 /* Release the host handle (the arena stays the caller's). */
 int gpt_destroy(gpt_model* m);
 
+/* ---- Generation with a key/value cache (nanoGPT README, "sampling /
+ * inference"; llm.c summary, "Sampling").  A generation context reads the
+ * weights of a model (bf16 copy in bf16 mode, float32 in fp32 mode; they must
+ * not change while it is used) and owns a caller-provided device arena with
+ * the caches [n_layer][B][n_head][Tmax][head_dim] (act type) of B sequences
+ * and the activations of one decode step.  Every call is enqueued on
+ * `stream`; none synchronises unless stated. */
+typedef struct gpt_gen gpt_gen;
+
+/* Device bytes of a generation arena for B sequences of up to Tmax tokens
+ * (1 <= Tmax <= block_size).  GPT_E_UNSUPPORTED if head_dim is not 32/64/128. */
+int gpt_gen_plan(const gpt_model* m, int32_t B, int32_t Tmax, int64_t* bytes);
+/* Create a context on `d_arena` (256-byte aligned, >= gpt_gen_plan bytes,
+ * caller-owned).  The host handle is freed by gpt_gen_destroy. */
+int gpt_gen_init(gpt_model* m, int32_t B, int32_t Tmax, void* d_arena, int64_t arena_bytes,
+                 void* stream, gpt_gen** out);
+/* Forget the cached tokens (next gpt_gen_step is position 0). */
+int gpt_gen_reset(gpt_gen* g);
+/* Append one token per sequence (d_tokens: device int32 [B], ids < vocab)
+ * at the current position: its keys / values join the cache and the logits
+ * of the next token are computed.  GPT_E_INVALID once Tmax tokens are cached. */
+int gpt_gen_step(gpt_gen* g, const int32_t* d_tokens, void* stream);
+/* Copy the last step's logits [B][ld] to host memory (synchronous): element
+ * type is the act type (bf16 bits in bf16 mode, float in fp32 mode); *ld
+ * receives the row pitch in elements (>= vocab_size; entries >= vocab_size
+ * are padding). */
+int gpt_gen_logits(gpt_gen* g, void* h_dst, int64_t* ld, void* stream);
+/* Draw one token per sequence from the last step's logits: temperature 0 =
+ * argmax (lowest index on ties); otherwise softmax of logits/temperature over
+ * the top_k largest (0 = all; ties at the threshold kept), token = the
+ * smallest i whose cumulative probability exceeds d_u[b*u_stride] (device
+ * float in [0, 1)).  Writes d_tokens[b] (device int32 [B]). */
+int gpt_gen_sample(gpt_gen* g, float temperature, int32_t top_k, const float* d_u,
+                   int64_t u_stride, int32_t* d_tokens, void* stream);
+/* Reset, feed the prompt d_prompt [B][T0] one position at a time, then draw
+ * n_new tokens (draw s of row b uses d_uniforms[b*n_new + s]); d_out [B][T0 +
+ * n_new] receives the prompt and the continuation.  T0 >= 1, T0 + n_new <= Tmax. */
+int gpt_generate(gpt_gen* g, const int32_t* d_prompt, int32_t T0, int32_t n_new,
+                 float temperature, int32_t top_k, const float* d_uniforms, int32_t* d_out,
+                 void* stream);
+int gpt_gen_destroy(gpt_gen* g);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* gpt_last_error(void);
 
