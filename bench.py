@@ -111,6 +111,47 @@ def time_muon(model, cfg, torch, gpt, reps=5):
     return {"ms": round(t, 3), "ns_flop": fl, "ns_tflops_over_step": round(fl / (t * 1e-3) / 1e12, 1)}
 
 
+def decode_bytes(cfg, B, pos):
+    """HBM bytes one decode step must read at context length pos: every
+    weight matrix once (the tied lm_head is wte), the LayerNorm and bias
+    vectors, the B embedding rows, and the cached keys and values of all
+    layers (positions 0..pos-1), plus the new cache rows and the logits written."""
+    C, F, L, H = cfg["n_embd"], cfg["mlp_hidden"], cfg["n_layer"], cfg["n_head"]
+    act = 2 if cfg["precision"] == "bf16" else 4
+    Vp = cfg["padded_vocab"]
+    mats = L * (3 * C * C + C * C + 2 * F * C) + Vp * C
+    vecs = L * (4 * C + (3 * C + C + F + C + 2 * C if cfg["bias"] else 0)) + 2 * C
+    kv_read = 2 * L * B * pos * C * act
+    writes = 2 * L * B * C * act + B * Vp * act
+    return mats * act + vecs * 4 + 2 * B * C * 4 + kv_read + writes
+
+
+def time_decode(model, cfg, torch, gpt, np, B=16, prefill=512, steps=64):
+    """Decode throughput with the key/value cache: B sequences, a prompt of
+    `prefill` tokens fed one position at a time (untimed), then `steps`
+    timed decode steps (one token per sequence each), HIP events on the
+    stream they run on."""
+    g = gpt.Generator(model, B, prefill + steps)
+    rng = np.random.default_rng(9)
+    toks = torch.from_numpy(rng.integers(0, cfg["vocab_size"], (prefill + steps, B),
+                                         dtype=np.int32)).cuda()
+    for t in range(prefill):
+        g.step(toks[t])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for t in range(prefill, prefill + steps):
+        g.step(toks[t])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    byts = np.mean([decode_bytes(cfg, B, pos) for pos in range(prefill, prefill + steps)])
+    return {"batch": B, "context": [prefill, prefill + steps], "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(B / (ms * 1e-3), 1),
+            "hbm_bytes_per_step": int(byts), "achieved_gbs": round(byts / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -203,6 +244,7 @@ def main():
                 "launches_per_step": ds["launches"] // args.profile_steps}
 
     muon = time_muon(model, cfg, torch, gpt)
+    decode = time_decode(model, cfg, torch, gpt, np=np)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -217,6 +259,7 @@ def main():
         "step_ms_min": round(float(np.min(step_ms)), 3),
         "loss_first": round(losses[0], 4), "loss_last": round(losses[-1], 4),
         "kernels": per_kind, "sites": per_site, "roofline": roof, "muon_step": muon,
+        "decode": decode,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)

@@ -297,6 +297,11 @@ gpt_gemm_desc linear_dx(const gpt_model* m, const void* dy, int64_t N, int64_t w
   d.M = (int)m->M; d.N = (int)K; d.K = (int)N;
   d.A = dy; d.lda = ldy; d.a_trans = 0; d.a_rows = (int)m->M; d.a_kvalid = (int)N;
   d.B = m->W(w_off); d.ldb = K; d.b_trans = 1; d.b_rows = (int)K; d.b_kvalid = (int)w_rows;
+  // Input gradients run on the main stream while the side stream's weight
+  // gradients own the split-K workspace: they never split (the vocabulary
+  // projection's, issued before the side stream starts, gets it back).
+  d.workspace = nullptr;
+  d.workspace_bytes = 0;
   return d;
 }
 
@@ -504,6 +509,8 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
   const char* dlog = act(m->ar.logits);
   gpt_gemm_desc d = linear_dx(m, dlog, m->Vq, m->pl.lmw, C, m->Vq, m->Vp);
   d.epilogue = GPT_EPI_STORE; d.out = dC; d.ldo = C;
+  d.workspace = m->at<void>(m->ar.gemm_ws);
+  d.workspace_bytes = m->ar.gemm_ws_bytes;
   GEMM(d, GPT_S_LMHEAD_DX);
   CHECK(fork());
   d = linear_dw(m, dlog, m->Vq, m->Vq, act(m->ar.xf), C, m->pl.lmw, m->Vp, acc);
@@ -756,7 +763,7 @@ struct gpt_gen {
   gpt_model* m;
   int B, Tmax, pos;
   char* base;
-  int64_t kc, vc, x, a, qkv, att, u, gact, mean, rstd, logits, tok, total;
+  int64_t kc, vc, x, a, qkv, att, u, gact, mean, rstd, logits, tok, ws, ws_bytes, total;
 };
 
 namespace {
@@ -777,6 +784,9 @@ int64_t gen_layout(const gpt_model* m, int B, int Tmax, gpt_gen* g) {
   g->rstd = take(B * 4);
   g->logits = take(B * m->Vq * act);
   g->tok = take(B * 4);
+  // split-K partials of the decode products (at most 32 splits of B x max(3C, F) floats)
+  g->ws_bytes = 32 * (int64_t)B * std::max(3 * C, F) * 4;
+  g->ws = take(g->ws_bytes);
   g->total = o;
   return o;
 }
@@ -807,6 +817,8 @@ hipError_t gen_linear(const gpt_gen* g, const void* a, int64_t K, int64_t w_off,
   d.resid = resid;
   d.out = out; d.ldo = ldo;
   d.aux = aux; d.ldaux = aux ? ldo : 0;
+  d.workspace = g->base + g->ws;
+  d.workspace_bytes = g->ws_bytes;
   return gpt::gemm(d, s);
 }
 

@@ -483,6 +483,7 @@ MfmaKernel mfma_kernel_for(int at, int bt, int epi, int ga, int gb) {
   K_(0, 1, GPT_EPI_MUL, 0, 0)
   K_(0, 1, GPT_EPI_F32, 0, 0)
   K_(0, 0, GPT_EPI_AXPBY, 0, 0)
+  K_(0, 0, EPI_PARTIAL, 0, 0)
   K_(0, 1, GPT_EPI_AXPBY, 0, 0)
   K_(1, 1, GPT_EPI_STORE, 0, 0)
   K_(1, 1, GPT_EPI_F32, 0, 0)
@@ -666,6 +667,7 @@ MfmaKernel dma_kernel_for(int at, int bt, int epi, int ga, int gb) {
   K_(0, 1, GPT_EPI_F32)
   K_(0, 1, EPI_PARTIAL)
   K_(0, 0, GPT_EPI_AXPBY)
+  K_(0, 0, EPI_PARTIAL)
   K_(0, 1, GPT_EPI_AXPBY)
   K_(1, 1, GPT_EPI_STORE)
   K_(1, 1, GPT_EPI_F32)
@@ -1125,6 +1127,18 @@ GemmPlan plan_gemm(int M, int N, int K, int precision, bool splittable, int64_t 
     p.S = S;
     return p;
   }
+  // Few rows (decode steps: one row per sequence): one row of 128-tiles, so the
+  // weight matrix is streamed by as many workgroups as K splits allow.
+  if (splittable && batch == 1 && M <= BM) {
+    const long t128 = cdiv(N, BN);
+    if (t128 < 256) {
+      int S = (int)std::min<long>(std::min<long>(32, K / BK), cdiv(512, t128));
+      if (S > 1 && ws_bytes >= (int64_t)S * M * N * 4) {
+        p.S = S;
+        return p;
+      }
+    }
+  }
   const long t256 = cdiv(M, BIG) * cdiv(N, BIG) * batch;
   const int force = tile_override();
   if (force == 256) {
@@ -1183,9 +1197,9 @@ int effective_splits(const GemmPlan& p, int K) {
 }
 
 // K may be split (partials reduced, epilogue applied after) for weight
-// gradients and for very long reductions.
+// gradients, for very long reductions and for products of at most 128 rows.
 bool splittable(const gpt_gemm_desc& d) {
-  return !d.a_gelu && !d.b_gelu && ((d.a_trans && d.b_trans) || d.K >= 16384);
+  return !d.a_gelu && !d.b_gelu && ((d.a_trans && d.b_trans) || d.K >= 16384 || d.M <= BM);
 }
 // Direct-to-LDS loads address each operand through a 31-bit byte offset.
 bool dma_ok(const gpt_gemm_desc& d) {

@@ -4,6 +4,9 @@
         a few training steps (forward, loss, backward, norm, AdamW) of a preset
     python -m decoder_only_gpt_amd.profile_run muon [--config gpt2_124m] [--steps 3]
         a few hybrid Muon + AdamW optimizer steps on fixed synthetic gradients
+    python -m decoder_only_gpt_amd.profile_run decode [--config gpt2_124m] [--batch 16]
+        [--prefill 512] [--steps 64]
+        key/value-cache decode steps after a prompt fed one position at a time
     python -m decoder_only_gpt_amd.profile_run copy [--mib 1024]
         one plain device-to-device copy of a known size (counter calibration)
     python -m decoder_only_gpt_amd.profile_run summarize-stats CSV OUT --command "..."
@@ -73,6 +76,24 @@ def run_muon(config: str, steps: int):
         m.muon_step(i + 1, 1.0)
         torch.cuda.synchronize()
         print(f"muon step {i}", flush=True)
+
+
+def run_decode(config: str, batch: int, prefill: int, steps: int):
+    import numpy as np
+    import torch
+    from decoder_only_gpt_amd import gpt, presets, synth
+    cfg = presets.preset(config)
+    m = gpt.Model(cfg, B=1, T=8)
+    m.set_params(synth.init_params(cfg, seed=0))
+    g = gpt.Generator(m, batch, prefill + steps)
+    rng = np.random.default_rng(9)
+    toks = torch.from_numpy(rng.integers(0, cfg["vocab_size"], (prefill + steps, batch),
+                                         dtype=np.int32)).cuda()
+    for t in range(prefill + steps):
+        g.step(toks[t])
+        if t % 128 == 0 or t == prefill + steps - 1:
+            torch.cuda.synchronize()
+            print(f"decode position {t}", flush=True)
 
 
 def run_copy(mib: int):
@@ -145,6 +166,11 @@ def main():
     p = sub.add_parser("muon")
     p.add_argument("--config", default="gpt2_124m")
     p.add_argument("--steps", type=int, default=3)
+    p = sub.add_parser("decode")
+    p.add_argument("--config", default="gpt2_124m")
+    p.add_argument("--batch", type=int, default=16)
+    p.add_argument("--prefill", type=int, default=512)
+    p.add_argument("--steps", type=int, default=64)
     p = sub.add_parser("copy")
     p.add_argument("--mib", type=int, default=1024)
     p = sub.add_parser("summarize-stats")
@@ -169,6 +195,9 @@ def main():
     elif a.cmd == "muon":
         sys.path.insert(0, ROOT)
         run_muon(a.config, a.steps)
+    elif a.cmd == "decode":
+        sys.path.insert(0, ROOT)
+        run_decode(a.config, a.batch, a.prefill, a.steps)
     elif a.cmd == "copy":
         run_copy(a.mib)
     elif a.cmd == "summarize-stats":

@@ -104,9 +104,12 @@ def test_gemm_layouts(prec, M, N, K, at, bt):
 @pytest.mark.parametrize("epi", [gpt.EPI_STORE, gpt.EPI_RESIDUAL, gpt.EPI_GELU, gpt.EPI_DGELU,
                                  gpt.EPI_F32_ACCUM, gpt.EPI_GELU_PAIR, gpt.EPI_MUL])
 @pytest.mark.parametrize("tanh_form", [0, 1])
-def test_gemm_epilogues(prec, epi, tanh_form):
+@pytest.mark.parametrize("M,split", [(150, False), (16, True)])
+def test_gemm_epilogues(prec, epi, tanh_form, M, split):
+    """Every epilogue; M = 16 with a workspace is the few-row path (decode
+    steps), split over K with the epilogue applied by the reduction."""
     dt = torch.bfloat16 if prec == gpt.BF16 else torch.float32
-    M, N, K = 150, 256, 192
+    N, K = 256, 192
     A, lda, Ax = _operand(M, K, 0, dt, 3, gelu=(epi == gpt.EPI_RESIDUAL), tanh_form=tanh_form)
     B, ldb, Bx = _operand(N, K, 0, dt, 4)
     if epi == gpt.EPI_RESIDUAL and prec == gpt.BF16:
@@ -124,6 +127,9 @@ def test_gemm_epilogues(prec, epi, tanh_form):
                      a_kvalid=K, a_gelu=int(epi == gpt.EPI_RESIDUAL), B=B.data_ptr(), ldb=ldb,
                      b_trans=0, b_rows=N, b_kvalid=K, epilogue=epi, gelu_tanh=tanh_form,
                      out=out.data_ptr(), ldo=N)
+    if split:
+        ws = torch.empty(32 * M * N * 4, dtype=torch.uint8, device="cuda")
+        d.workspace, d.workspace_bytes = ws.data_ptr(), ws.numel()
     bx = bias.cpu().numpy().astype(np.float64)
     rx = resid.cpu().numpy().astype(np.float64)
     if epi in (gpt.EPI_STORE, gpt.EPI_GELU, gpt.EPI_RESIDUAL, gpt.EPI_GELU_PAIR):
