@@ -252,6 +252,13 @@ __device__ __forceinline__ bf16x8 frag(const bf16_t* lds, int r0, int ks, int la
 }
 
 // Epilogue on 8 consecutive columns n..n+7 of row m (n + 8 <= N, rows 16-byte aligned).
+// 16-byte output stores.  The non-temporal form (plain STORE / GELU outputs:
+// the vocabulary projection's 1.6 GB of logits above all) does not allocate
+// in the L2, so the operand panels keep the cache; measured neutral to worse
+// for the epilogues that also read an auxiliary input, which keep plain stores.
+__device__ __forceinline__ void st16nt(void* p, u32x4 v) { __builtin_nontemporal_store(v, (u32x4*)p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
+
 template <int EPI>
 __device__ __forceinline__ void epilogue8(const EpiArgs& e, float* partial, int m, int n,
                                           float4 v0, float4 v1) {
@@ -273,13 +280,13 @@ __device__ __forceinline__ void epilogue8(const EpiArgs& e, float* partial, int 
   if constexpr (EPI == GPT_EPI_STORE || EPI == GPT_EPI_GELU) {
     u32x4 w{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]), pack_bf2(x[4], x[5]),
             pack_bf2(x[6], x[7])};
-    *(u32x4*)((bf16_t*)e.out + o) = w;
+    st16nt((bf16_t*)e.out + o, w);
     if constexpr (EPI == GPT_EPI_GELU) {
       if (e.aux) {
         // GELU of the stored (rounded) pre-activation, as a recompute would see it.
         u32x4 g{gelu2(w.x, e.tanh_form), gelu2(w.y, e.tanh_form), gelu2(w.z, e.tanh_form),
                 gelu2(w.w, e.tanh_form)};
-        *(u32x4*)((bf16_t*)e.aux + (long)m * e.ldaux + n) = g;
+        st16nt((bf16_t*)e.aux + (long)m * e.ldaux + n, g);
       }
     }
   } else if constexpr (EPI == GPT_EPI_DGELU) {
@@ -290,21 +297,21 @@ __device__ __forceinline__ void epilogue8(const EpiArgs& e, float* partial, int 
       x[2 * i] *= gelu_grad_fast(bf_lo(uw[i]), e.tanh_form);
       x[2 * i + 1] *= gelu_grad_fast(bf_hi(uw[i]), e.tanh_form);
     }
-    *(u32x4*)((bf16_t*)e.out + o) = u32x4{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]),
-                                           pack_bf2(x[4], x[5]), pack_bf2(x[6], x[7])};
+    st16((bf16_t*)e.out + o, u32x4{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]),
+                                           pack_bf2(x[4], x[5]), pack_bf2(x[6], x[7])});
   } else if constexpr (EPI == GPT_EPI_MUL) {
     const u32x4 a = *(const u32x4*)((const bf16_t*)e.aux + (long)m * e.ldaux + n);
-    *(u32x4*)((bf16_t*)e.out + o) = u32x4{
+    st16((bf16_t*)e.out + o, u32x4{
         pack_bf2(x[0] * bf_lo(a.x), x[1] * bf_hi(a.x)), pack_bf2(x[2] * bf_lo(a.y), x[3] * bf_hi(a.y)),
-        pack_bf2(x[4] * bf_lo(a.z), x[5] * bf_hi(a.z)), pack_bf2(x[6] * bf_lo(a.w), x[7] * bf_hi(a.w))};
+        pack_bf2(x[4] * bf_lo(a.z), x[5] * bf_hi(a.z)), pack_bf2(x[6] * bf_lo(a.w), x[7] * bf_hi(a.w))});
   } else if constexpr (EPI == GPT_EPI_AXPBY) {
     const u32x4 a = *(const u32x4*)((const bf16_t*)e.aux + (long)m * e.ldaux + n);
     const float al = e.alpha, be = e.beta;
-    *(u32x4*)((bf16_t*)e.out + o) = u32x4{
+    st16((bf16_t*)e.out + o, u32x4{
         pack_bf2(al * x[0] + be * bf_lo(a.x), al * x[1] + be * bf_hi(a.x)),
         pack_bf2(al * x[2] + be * bf_lo(a.y), al * x[3] + be * bf_hi(a.y)),
         pack_bf2(al * x[4] + be * bf_lo(a.z), al * x[5] + be * bf_hi(a.z)),
-        pack_bf2(al * x[6] + be * bf_lo(a.w), al * x[7] + be * bf_hi(a.w))};
+        pack_bf2(al * x[6] + be * bf_lo(a.w), al * x[7] + be * bf_hi(a.w))});
   } else if constexpr (EPI == GPT_EPI_GELU_PAIR) {
     if (e.bias) {
       float4 b0 = *(const float4*)(e.bias + n), b1 = *(const float4*)(e.bias + n + 4);
@@ -319,10 +326,10 @@ __device__ __forceinline__ void epilogue8(const EpiArgs& e, float* partial, int 
       gelu_pair_fast(bf_lo(w[i]), e.tanh_form, g[2 * i], gp[2 * i]);
       gelu_pair_fast(bf_hi(w[i]), e.tanh_form, g[2 * i + 1], gp[2 * i + 1]);
     }
-    *(u32x4*)((bf16_t*)e.out + o) = u32x4{pack_bf2(gp[0], gp[1]), pack_bf2(gp[2], gp[3]),
-                                           pack_bf2(gp[4], gp[5]), pack_bf2(gp[6], gp[7])};
-    *(u32x4*)((bf16_t*)e.aux + (long)m * e.ldaux + n) = u32x4{
-        pack_bf2(g[0], g[1]), pack_bf2(g[2], g[3]), pack_bf2(g[4], g[5]), pack_bf2(g[6], g[7])};
+    st16((bf16_t*)e.out + o, u32x4{pack_bf2(gp[0], gp[1]), pack_bf2(gp[2], gp[3]),
+                                           pack_bf2(gp[4], gp[5]), pack_bf2(gp[6], gp[7])});
+    st16((bf16_t*)e.aux + (long)m * e.ldaux + n, u32x4{
+        pack_bf2(g[0], g[1]), pack_bf2(g[2], g[3]), pack_bf2(g[4], g[5]), pack_bf2(g[6], g[7])});
   } else if constexpr (EPI == GPT_EPI_RESIDUAL) {
     float4 r0 = *(const float4*)(e.resid + o), r1 = *(const float4*)(e.resid + o + 4);
     *(float4*)((float*)e.out + o) = make_float4(r0.x + x[0], r0.y + x[1], r0.z + x[2], r0.w + x[3]);
