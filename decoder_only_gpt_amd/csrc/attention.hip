@@ -259,7 +259,16 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, long ld, int
     const unsigned off = row0 + r < nrows
                              ? (unsigned)(((long)(row0 + r) * ld + col0 + chunk * 8) * 2)
                              : 0x80000000u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + blk * 512), 16, off, 0, 0, 0);
+    // Issued from inline asm (M0 = the block's LDS address): the compiler's
+    // wait insertion would otherwise put a vmcnt(0) after these loads, ahead
+    // of the current stage's fragment reads, and the next tile would never
+    // load while this one is multiplied.  Every loop waits vmcnt(0) and
+    // synchronises before it reads a stage or refills the other one.
+    const unsigned m0v = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds + blk * 512));
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0v), "v"(off), "s"(rs)
+                 : "memory", "m0");
   }
 }
 

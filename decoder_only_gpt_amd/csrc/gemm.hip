@@ -542,8 +542,30 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, lo
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, n, 0x00020000);
 }
 
+// One 16-byte direct-to-LDS load per lane into the wave's 1 KB block at
+// `lds` (lane l -> bytes 16 l).  With ASM the load is issued from inline asm
+// (M0 = the block's LDS address, set in the same statement; no register
+// result): the compiler's wait insertion then does not treat it as a pending
+// write of the LDS the fragment reads of the current stage use.  Without it,
+// the compiler places a vmcnt(0) right after the next stage's loads wherever
+// fragments are read with the LDS transpose builtin, so those loads never
+// overlap the MFMAs.  Kernels using ASM order their loads themselves: every
+// stage ends with vmcnt(0) and a barrier before its buffer is read or refilled.
+template <bool ASM>
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, bf16_t* lds, unsigned off) {
+  if constexpr (ASM) {
+    const unsigned m0v = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds);
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0v), "v"(off), "s"(rs)
+                 : "memory", "m0");
+  } else {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, off, 0, 0, 0);
+  }
+}
+
 // Issue this wave's 4 loads of one 128 x BK operand tile into `lds`.
-template <int TRANS>
+template <int TRANS, bool ASM = false>
 __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, const OpArgs& a, int r0,
                                          int k0, bf16_t* lds, int wave, int lane) {
 #pragma unroll
@@ -564,7 +586,7 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, const OpArgs
     const bool ok = r < a.rows && k < a.kvalid;
     const long e = TRANS ? (long)k * a.ld + r : (long)r * a.ld + k;
     const unsigned off = ok ? (unsigned)(e * 2) : 0x80000000u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + blk * 512), 16, off, 0, 0, 0);
+    dma16<ASM>(rs, lds + blk * 512, off);
   }
 }
 
@@ -601,16 +623,16 @@ __global__ void __launch_bounds__(256, 2) gemm_dma_kernel(OpArgs A, OpArgs B, in
 
   f32x16 acc00 = {}, acc01 = {}, acc10 = {}, acc11 = {};
 
-  dma_tile<AT>(ra, a, m0, kbeg, sA0, wave, lane);
-  dma_tile<BT>(rb, b, n0, kbeg, sB0, wave, lane);
+  dma_tile<AT, (AT || BT)>(ra, a, m0, kbeg, sA0, wave, lane);
+  dma_tile<BT, (AT || BT)>(rb, b, n0, kbeg, sB0, wave, lane);
   for (int kt = 0; kt < nk; ++kt) {
     __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's loads of tile kt landed
     __syncthreads();                     // ... and every other wave's
     const bool odd = kt & 1;
     if (kt + 1 < nk) {
       const int k1 = kbeg + (kt + 1) * BK;
-      dma_tile<AT>(ra, a, m0, k1, odd ? sA0 : sA1, wave, lane);
-      dma_tile<BT>(rb, b, n0, k1, odd ? sB0 : sB1, wave, lane);
+      dma_tile<AT, (AT || BT)>(ra, a, m0, k1, odd ? sA0 : sA1, wave, lane);
+      dma_tile<BT, (AT || BT)>(rb, b, n0, k1, odd ? sB0 : sB1, wave, lane);
     }
     const bf16_t* as = odd ? sA1 : sA0;
     const bf16_t* bs = odd ? sB1 : sB0;
@@ -702,7 +724,7 @@ __device__ __forceinline__ int big_off_t(int k, int r) {  // K-major tile [BK][2
   return k * BIG + (r ^ ((k & 3) << 5));
 }
 
-template <int TRANS>
+template <int TRANS, bool ASM = false>
 __device__ __forceinline__ void dma_tile256(__amdgpu_buffer_rsrc_t rs, const OpArgs& a, int r0,
                                             int k0, bf16_t* lds, int wave, int lane) {
 #pragma unroll
@@ -723,7 +745,7 @@ __device__ __forceinline__ void dma_tile256(__amdgpu_buffer_rsrc_t rs, const OpA
     const bool ok = r < a.rows && k < a.kvalid;
     const long e = TRANS ? (long)k * a.ld + r : (long)r * a.ld + k;
     const unsigned off = ok ? (unsigned)(e * 2) : 0x80000000u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + blk * 512), 16, off, 0, 0, 0);
+    dma16<ASM>(rs, lds + blk * 512, off);
   }
 }
 
@@ -849,16 +871,16 @@ __global__ void __launch_bounds__(256, 1) gemm_big_kernel(OpArgs A, OpArgs B, in
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  dma_tile256<AT>(ra, a, m0, kbeg, sA0, wave, lane);
-  dma_tile256<BT>(rb, b, n0, kbeg, sB0, wave, lane);
+  dma_tile256<AT, (AT || BT)>(ra, a, m0, kbeg, sA0, wave, lane);
+  dma_tile256<BT, (AT || BT)>(rb, b, n0, kbeg, sB0, wave, lane);
   for (int kt = 0; kt < nk; ++kt) {
     __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's loads of tile kt landed
     __syncthreads();                     // ... and every other wave's
     const bool odd = kt & 1;
     if (kt + 1 < nk) {
       const int k1 = kbeg + (kt + 1) * BK;
-      dma_tile256<AT>(ra, a, m0, k1, odd ? sA0 : sA1, wave, lane);
-      dma_tile256<BT>(rb, b, n0, k1, odd ? sB0 : sB1, wave, lane);
+      dma_tile256<AT, (AT || BT)>(ra, a, m0, k1, odd ? sA0 : sA1, wave, lane);
+      dma_tile256<BT, (AT || BT)>(rb, b, n0, k1, odd ? sB0 : sB1, wave, lane);
     }
     const bf16_t* as = odd ? sA1 : sA0;
     const bf16_t* bs = odd ? sB1 : sB0;
@@ -920,7 +942,7 @@ __global__ void __launch_bounds__(256, 1) gemm_big_kernel(OpArgs A, OpArgs B, in
 // 1 KB blocks per wave and operand per stage); the epilogue stages each
 // wave's 32-row slices through LDS for 16-byte vector stores.
 // ----------------------------------------------------------------------------
-template <int TRANS>
+template <int TRANS, bool ASM = false>
 __device__ __forceinline__ void dma_tile256_w8(__amdgpu_buffer_rsrc_t rs, const OpArgs& a, int r0,
                                                int k0, bf16_t* lds, int wave, int lane) {
 #pragma unroll
@@ -941,7 +963,7 @@ __device__ __forceinline__ void dma_tile256_w8(__amdgpu_buffer_rsrc_t rs, const 
     const bool ok = r < a.rows && k < a.kvalid;
     const long e = TRANS ? (long)k * a.ld + r : (long)r * a.ld + k;
     const unsigned off = ok ? (unsigned)(e * 2) : 0x80000000u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + blk * 512), 16, off, 0, 0, 0);
+    dma16<ASM>(rs, lds + blk * 512, off);
   }
 }
 
@@ -982,16 +1004,16 @@ __global__ void __launch_bounds__(512, 1) gemm_big8_kernel(OpArgs A, OpArgs B, i
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  dma_tile256_w8<AT>(ra, a, m0, kbeg, sA0, wave, lane);
-  dma_tile256_w8<BT>(rb, b, n0, kbeg, sB0, wave, lane);
+  dma_tile256_w8<AT, (AT || BT)>(ra, a, m0, kbeg, sA0, wave, lane);
+  dma_tile256_w8<BT, (AT || BT)>(rb, b, n0, kbeg, sB0, wave, lane);
   for (int kt = 0; kt < nk; ++kt) {
     __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's loads of tile kt landed
     __syncthreads();                     // ... and every other wave's
     const bool odd = kt & 1;
     if (kt + 1 < nk) {
       const int k1 = kbeg + (kt + 1) * BK;
-      dma_tile256_w8<AT>(ra, a, m0, k1, odd ? sA0 : sA1, wave, lane);
-      dma_tile256_w8<BT>(rb, b, n0, k1, odd ? sB0 : sB1, wave, lane);
+      dma_tile256_w8<AT, (AT || BT)>(ra, a, m0, k1, odd ? sA0 : sA1, wave, lane);
+      dma_tile256_w8<BT, (AT || BT)>(rb, b, n0, k1, odd ? sB0 : sB1, wave, lane);
     }
     const bf16_t* as = odd ? sA1 : sA0;
     const bf16_t* bs = odd ? sB1 : sB0;
