@@ -1052,7 +1052,9 @@ __global__ void __launch_bounds__(512, 1) gemm_big8_kernel(OpArgs A, OpArgs B, i
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
     const int cg = lane & 7;
     const int n = n0 + wn * 64 + cg * 8;
-#pragma unroll 1
+    // Unrolled: the four passes' auxiliary reads (GELU', residual) are
+    // independent, so they are in flight together rather than one at a time.
+#pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int row = p * 8 + (lane >> 3);
       const int m = m0 + wm * 128 + i * 32 + row;
