@@ -245,6 +245,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, lo
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
 }
 
+// max / sum of a value and its partner 32 lanes away (v_permlane32_swap: one
+// VALU op, where a shuffle would go through the LDS crossbar); both halves of
+// the wave get the identical result.
+__device__ __forceinline__ float swap32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // This wave's share of the loads of rows [row0, row0 + 64), columns
 // [col0, col0 + HD) of a bf16 matrix (leading dimension ld) into a tile.
 template <int HD>
@@ -378,23 +392,32 @@ __global__ void __launch_bounds__(256, HD == 128 ? 1 : 2)
         }
         mx = fmaxf(mx, s[kk][r]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mnew = fmaxf(mrow, mx * scale_log2);
-    const float alpha = __builtin_amdgcn_exp2f(mrow - mnew);
+    // The two halves of the wave hold the two 16-key halves of each 32-key
+    // block for the same query: combined by one lane swap.
+    mx = swap32_max(mx);
+    // Lazy rescaling: the running maximum (log2 units) is raised, and O and
+    // the sum rescaled, only when some query's block maximum exceeds it by
+    // more than 8; otherwise the exponents use the stale maximum, so every
+    // p <= 2^8 and O / sum is unchanged mathematically.
+    const float mcand = mx * scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mcand > mrow + 8.f) != 0) {
+      const float mnew = fmaxf(mrow, mcand);
+      const float alpha = __builtin_amdgcn_exp2f(mrow - mnew);
+      lrow *= alpha;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) o[d] *= alpha;
+      mrow = mnew;
+    }
     float ls = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kk][r], scale_log2, -mnew));
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kk][r], scale_log2, -mrow));
         s[kk][r] = p;
         ls += p;
       }
-    ls += __shfl_xor(ls, 32, 64);
-    lrow = lrow * alpha + ls;
-    mrow = mnew;
-#pragma unroll
-    for (int d = 0; d < ND; ++d) o[d] *= alpha;
+    lrow += swap32_sum(ls);
     // O^T[d][q] += V^T[d][key] P^T[key][q]
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
