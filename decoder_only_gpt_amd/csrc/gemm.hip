@@ -1205,14 +1205,15 @@ GemmPlan plan_gemm(int M, int N, int K, int precision, bool splittable, int64_t 
     }
     // Otherwise 256-tiles (one workgroup per CU) when they fill the rounds of
     // the 256 CUs at least as evenly as 128-tiles (two workgroups per CU) do;
-    // on a tie with a short reduction (K <= 1024) the 128-tiles, whose two
-    // workgroups per CU hide each other's epilogue (measured on the 768 x 768
-    // projections).
+    // on a tie below full rounds with a short reduction (K <= 1024) the
+    // 128-tiles, whose two workgroups per CU hide each other's epilogue
+    // (measured on the 768 x 768 projections; at full rounds, e.g. the
+    // 3072-wide FC products, the 256-tiles stay faster).
     if (!splittable && t256 >= 128) {
       const long t128 = cdiv(M, BM) * cdiv(N, BN) * batch;
       const double f256 = (double)t256 / (256.0 * cdiv(t256, 256));
       const double f128 = (double)t128 / (512.0 * cdiv(t128, 512));
-      const bool tie = f256 < f128 + 1e-9;
+      const bool tie = f256 < f128 + 1e-9 && f256 < 1.0 - 1e-9;
       if (f256 + 1e-9 >= f128 && !(tie && K <= 1024)) {
         p.big = true;
         return p;
