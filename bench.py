@@ -56,8 +56,10 @@ def workload_name(cfg, name):
             f"C={cfg['n_embd']} F={cfg['mlp_hidden']} {cfg['precision']}")
 
 
-def cpu_baseline(cfg, seconds_budget=30.0):
-    """Time the oracle's full step (fp32 NumPy) on one sequence of the same model."""
+def cpu_baseline(cfg, min_seconds=10.0, max_steps=6):
+    """Time the oracle's full step (fp32 NumPy) on one sequence of the same
+    model, repeated on successive sequences until at least `min_seconds` of
+    CPU work (at most `max_steps` steps) so the sample is not one short run."""
     import numpy as np
     import oracle
     from decoder_only_gpt_amd import synth
@@ -67,15 +69,20 @@ def cpu_baseline(cfg, seconds_budget=30.0):
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
     p = synth.init_params(cfg, seed=0)
-    idx, tgt = synth.tokens(cfg, B=1, T=cfg["T"], seed=1)
-    z = np.zeros_like(p)
+    m = np.zeros_like(p)
+    v = np.zeros_like(p)
+    steps = 0
     t0 = time.perf_counter()
-    oracle.step(cfg, p, z, z, idx, tgt, 1, dtype=np.float32)
+    while steps < max_steps and (steps == 0 or time.perf_counter() - t0 < min_seconds):
+        idx, tgt = synth.tokens(cfg, B=1, T=cfg["T"], seed=1 + steps)
+        r = oracle.step(cfg, p, m, v, idx, tgt, steps + 1, dtype=np.float32)
+        p, m, v = r["p"], r["m"], r["v"]
+        steps += 1
     dt = time.perf_counter() - t0
-    return {"value": round(cfg["T"] / dt, 2), "unit": "tokens/s", "cores": int(threads),
+    return {"value": round(steps * cfg["T"] / dt, 2), "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"one sequence (B=1, T={cfg['T']}) of the same model, full step "
-                      f"(forward, backward, norm, AdamW) in float32 NumPy; {dt:.1f} s"}
+            "sample": f"{steps} steps of one sequence each (B=1, T={cfg['T']}) of the same model, "
+                      f"full step (forward, backward, norm, AdamW) in float32 NumPy; {dt:.1f} s"}
 
 
 def muon_ns_flops(cfg, steps=5):
