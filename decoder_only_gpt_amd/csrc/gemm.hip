@@ -590,6 +590,19 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, const OpArgs
   }
 }
 
+// Scheduling groups for one 16-deep step of NM MFMAs (4 or 8) with the NDS
+// LDS reads of the next step spread evenly after them.
+template <int N> __device__ __forceinline__ void sched_ds() {
+  if constexpr (N > 0) __builtin_amdgcn_sched_group_barrier(0x100, N, 0);
+}
+template <int NM, int NDS, int Q = 0> __device__ __forceinline__ void sched_mfma_ds() {
+  if constexpr (Q < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    sched_ds<NDS / NM + (Q < NDS % NM ? 1 : 0)>();
+    sched_mfma_ds<NM, NDS, Q + 1>();
+  }
+}
+
 template <int AT, int BT, int EPI>
 __global__ void __launch_bounds__(256, 2) gemm_dma_kernel(OpArgs A, OpArgs B, int K, int kchunk,
                                                           EpiArgs e, float* partial) {
@@ -636,17 +649,37 @@ __global__ void __launch_bounds__(256, 2) gemm_dma_kernel(OpArgs A, OpArgs B, in
     }
     const bf16_t* as = odd ? sA1 : sA0;
     const bf16_t* bs = odd ? sB1 : sB0;
+    // Fragments double-buffered across the 16-deep steps (see the 8-wave kernel).
+    constexpr int NDS = (AT ? 4 : 2) + (BT ? 4 : 2);
+    bf16x8 fa[2][2], fb[2][2];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      fa[0][h] = frag<AT>(as, wm * 64 + 32 * h, 0, lane);
+      fb[0][h] = frag<BT>(bs, wn * 64 + 32 * h, 0, lane);
+    }
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      const bf16x8 a0 = frag<AT>(as, wm * 64, ks, lane);
-      const bf16x8 a1 = frag<AT>(as, wm * 64 + 32, ks, lane);
-      const bf16x8 b0 = frag<BT>(bs, wn * 64, ks, lane);
-      const bf16x8 b1 = frag<BT>(bs, wn * 64 + 32, ks, lane);
-      acc00 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc00, 0, 0, 0);
-      acc01 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc01, 0, 0, 0);
-      acc10 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc10, 0, 0, 0);
-      acc11 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc11, 0, 0, 0);
+      const int cur = ks & 1;
+      if (ks + 1 < BK / 16) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          fa[cur ^ 1][h] = frag<AT>(as, wm * 64 + 32 * h, ks + 1, lane);
+          fb[cur ^ 1][h] = frag<BT>(bs, wn * 64 + 32 * h, ks + 1, lane);
+        }
+      }
+      acc00 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][0], fb[cur][0], acc00, 0, 0, 0);
+      acc01 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][0], fb[cur][1], acc01, 0, 0, 0);
+      acc10 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][1], fb[cur][0], acc10, 0, 0, 0);
+      acc11 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][1], fb[cur][1], acc11, 0, 0, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      if (ks + 1 < BK / 16) sched_mfma_ds<4, NDS>();
+      else __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
   __builtin_amdgcn_s_waitcnt(0x3f70);
   __syncthreads();
@@ -1017,19 +1050,44 @@ __global__ void __launch_bounds__(512, 1) gemm_big8_kernel(OpArgs A, OpArgs B, i
     }
     const bf16_t* as = odd ? sA1 : sA0;
     const bf16_t* bs = odd ? sB1 : sB0;
+    // Fragments double-buffered across the 16-deep steps: the reads of step
+    // ks + 1 are issued between the MFMAs of step ks (the scheduling groups
+    // pin that interleave), so no MFMA waits on an LDS read it could have had
+    // one step earlier.
+    constexpr int NDS = (AT ? 8 : 4) + (BT ? 4 : 2);  // LDS read instructions per step
+    bf16x8 af[2][4], bf[2][2];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[0][i] = big_frag<AT>(as, wm * 128 + i * 32, 0, lane);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) bf[0][j] = big_frag<BT>(bs, wn * 64 + j * 32, 0, lane);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[4], bf[2];
+      const int cur = ks & 1;
+      if (ks + 1 < BK / 16) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = big_frag<AT>(as, wm * 128 + i * 32, ks, lane);
+        for (int i = 0; i < 4; ++i)
+          af[cur ^ 1][i] = big_frag<AT>(as, wm * 128 + i * 32, ks + 1, lane);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bf[j] = big_frag<BT>(bs, wn * 64 + j * 32, ks, lane);
+        for (int j = 0; j < 2; ++j)
+          bf[cur ^ 1][j] = big_frag<BT>(bs, wn * 64 + j * 32, ks + 1, lane);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+          acc[i][j] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[cur][j], af[cur][i], acc[i][j], 0, 0, 0);
     }
+    // schedule: step 0's reads, then per step its 8 MFMAs with the next
+    // step's reads spread between them
+    __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      if (ks + 1 < BK / 16) sched_mfma_ds<8, NDS>();
+      else __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // Epilogue, one 32-row block of the wave's 128 x 64 tile at a time:
