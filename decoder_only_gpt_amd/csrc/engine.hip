@@ -187,6 +187,10 @@ Arena plan_arena(const gpt_config& c, int B, int T) {
   ws_need(C, F, M);
   ws_need(Vp, C, M);
   ws_need(M, C, Vq);  // the vocabulary projection's input gradient
+  {  // a block's four weight gradients as one grouped launch
+    const int gm[4] = {(int)C, (int)F, (int)C, (int)(3 * C)}, gn[4] = {(int)F, (int)C, (int)C, (int)C};
+    ws = std::max<int64_t>(ws, gpt::gemm_group_workspace_bytes(gm, gn, 4, (int)M));
+  }
   a.gemm_ws_bytes = ws;
   a.gemm_ws = take(std::max<int64_t>(ws, 16));
   a.cs_part = take(gpt::colsum_partial_floats((int)M, (int)std::max(3 * C, F)) * 4 + 16);
@@ -497,6 +501,13 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
   auto gemm_on = [&](hipStream_t st, const gpt_gemm_desc& dd, int site) -> int {
     return run_gemm(m, st, dd, site);
   };
+  auto gemm_group_on = [&](hipStream_t st, const gpt_gemm_desc* dd, int n, int site) -> int {
+    double fl = 0;
+    for (int i = 0; i < n; ++i) fl += 2.0 * dd[i].M * dd[i].N * dd[i].K;
+    hipStream_t s = st;
+    LAUNCH(GPT_K_GEMM_SPLITK, site, fl, 0, gpt::gemm_group(dd, n, s));
+    return GPT_OK;
+  };
   auto bias_grad = [&](const char* x, int64_t n, int64_t off) -> int {
     if (off < 0) return GPT_OK;
     hipStream_t s = s2;
@@ -534,20 +545,25 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
     d.aux = act(m->ar.u[l]); d.ldaux = F; d.out = dF; d.ldo = F;
     GEMM(d, GPT_S_FCPROJ_DX);
     CHECK(fork());
+    // The block's weight gradients share K (the tokens): they are collected
+    // and issued as one grouped launch once dqkv exists, and the buffers they
+    // read are released after it.  With GELU recompute the FC-projection
+    // weight gradient applies GELU to its operand and runs alone.
+    gpt_gemm_desc dw[4];
+    int ndw = 0, held[4], nheld = 0;
     if (c.recompute_gelu) {
       d = linear_dw(m, gact, C, C, act(m->ar.u[l]), F, L.fcpw, C, acc);
       d.b_gelu = 1;
+      CHECK(gemm_on(s2, d, GPT_S_FCPROJ_DW));
     } else {
-      d = linear_dw(m, gact, C, C, act(m->ar.g[l]), F, L.fcpw, C, acc);
+      dw[ndw++] = linear_dw(m, gact, C, C, act(m->ar.g[l]), F, L.fcpw, C, acc);
     }
-    CHECK(gemm_on(s2, d, GPT_S_FCPROJ_DW));
     CHECK(bias_grad(gact, C, L.fcpb));
-    CHECK(mark(gi));
+    held[nheld++] = gi;
     // MLP in: u = a2 Wfc^T + b
-    d = linear_dw(m, dF, F, F, act(m->ar.a2[l]), C, L.fcw, F, acc);
-    CHECK(gemm_on(s2, d, GPT_S_FC_DW));
+    dw[ndw++] = linear_dw(m, dF, F, F, act(m->ar.a2[l]), C, L.fcw, F, acc);
     CHECK(bias_grad(dF, F, L.fcb));
-    CHECK(mark(NGB + di));
+    held[nheld++] = NGB + di;
     d = linear_dx(m, dF, F, L.fcw, C, F, F);
     d.epilogue = GPT_EPI_STORE; d.out = dC; d.ldo = C;
     GEMM(d, GPT_S_FC_DX);
@@ -561,10 +577,9 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
     cur ^= 1;
     // attention out: x_mid = x_in + y Wproj^T + b
     CHECK(fork());
-    d = linear_dw(m, gact, C, C, act(m->ar.att[l]), C, L.projw, C, acc);
-    CHECK(gemm_on(s2, d, GPT_S_PROJ_DW));
+    dw[ndw++] = linear_dw(m, gact, C, C, act(m->ar.att[l]), C, L.projw, C, acc);
     CHECK(bias_grad(gact, C, L.projb));
-    CHECK(mark(gi));
+    held[nheld++] = gi;
     d = linear_dx(m, gact, C, L.projw, C, C, C);
     d.epilogue = GPT_EPI_STORE; d.out = dC2; d.ldo = C;
     GEMM(d, GPT_S_PROJ_DX);
@@ -575,10 +590,11 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
                               dC2, dqkv, m->at<float>(m->ar.dvec), s));
     // qkv = a1 Wqkv^T + b
     CHECK(fork());
-    d = linear_dw(m, dqkv, 3 * C, 3 * C, act(m->ar.a1[l]), C, L.qkvw, 3 * C, acc);
-    CHECK(gemm_on(s2, d, GPT_S_QKV_DW));
+    dw[ndw++] = linear_dw(m, dqkv, 3 * C, 3 * C, act(m->ar.a1[l]), C, L.qkvw, 3 * C, acc);
     CHECK(bias_grad(dqkv, 3 * C, L.qkvb));
-    CHECK(mark(2 * NGB + di));
+    held[nheld++] = 2 * NGB + di;
+    CHECK(gemm_group_on(s2, dw, ndw, GPT_S_BLOCK_DW));
+    for (int i = 0; i < nheld; ++i) CHECK(mark(held[i]));
     d = linear_dx(m, dqkv, 3 * C, L.qkvw, C, 3 * C, 3 * C);
     d.epilogue = GPT_EPI_STORE; d.out = dC; d.ldo = C;
     GEMM(d, GPT_S_QKV_DX);
@@ -1198,7 +1214,8 @@ int gpt_profile_end(gpt_model* m, void* stream, gpt_kernel_stats* out, gpt_kerne
   return GPT_OK;
 }
 
-int gpt_op_gemm(const gpt_gemm_desc* d, void* stream) {
+namespace {
+int check_gemm_desc(const gpt_gemm_desc* d) {
   if (!d) return fail(GPT_E_INVALID, "NULL descriptor");
   if (d->precision != GPT_FP32 && d->precision != GPT_BF16)
     return fail(GPT_E_INVALID, "bad precision");
@@ -1213,11 +1230,37 @@ int gpt_op_gemm(const gpt_gemm_desc* d, void* stream) {
   if ((d->epilogue == GPT_EPI_DGELU || d->epilogue == GPT_EPI_GELU_PAIR ||
        d->epilogue == GPT_EPI_MUL || d->epilogue == GPT_EPI_AXPBY) && !d->aux)
     return fail(GPT_E_INVALID, "NULL aux");
+  return GPT_OK;
+}
+}  // namespace
+
+int gpt_op_gemm(const gpt_gemm_desc* d, void* stream) {
+  int rc = check_gemm_desc(d);
+  if (rc != GPT_OK) return rc;
   hipError_t e = gpt::gemm(*d, (hipStream_t)stream);
   if (e == hipErrorInvalidValue)
     return fail(GPT_E_INVALID, "gemm layout rule broken (K, lda, ldb must be multiples of 8)");
   if (e != hipSuccess) return fail(GPT_E_HIP, std::string("gemm: ") + hipGetErrorString(e));
   return GPT_OK;
+}
+
+int gpt_op_gemm_group(const gpt_gemm_desc* descs, int32_t n, void* stream) {
+  if (n < 1 || n > 4) return fail(GPT_E_INVALID, "group of 1..4 products");
+  if (!descs) return fail(GPT_E_INVALID, "NULL descriptors");
+  for (int i = 0; i < n; ++i) {
+    int rc = check_gemm_desc(&descs[i]);
+    if (rc != GPT_OK) return rc;
+  }
+  hipError_t e = gpt::gemm_group(descs, n, (hipStream_t)stream);
+  if (e == hipErrorInvalidValue)
+    return fail(GPT_E_INVALID, "gemm layout rule broken (K, lda, ldb must be multiples of 8)");
+  if (e != hipSuccess) return fail(GPT_E_HIP, std::string("gemm group: ") + hipGetErrorString(e));
+  return GPT_OK;
+}
+
+int64_t gpt_op_gemm_group_workspace(const int32_t* M, const int32_t* N, int32_t n, int32_t K) {
+  if (!M || !N || n < 1 || n > 4) return 0;
+  return gpt::gemm_group_workspace_bytes(M, N, n, K);
 }
 
 int gpt_op_attention_fwd(int32_t precision, int32_t B, int32_t T, int32_t H, int32_t hd,

@@ -1000,23 +1000,19 @@ __device__ __forceinline__ void dma_tile256_w8(__amdgpu_buffer_rsrc_t rs, const 
   }
 }
 
+// One 256 x 256 output tile (tx, ty) over the K range of split tz; `smem` is
+// the kernel's 128 KB LDS block (two stages of A and B tiles, later the
+// epilogue slices).
 template <int AT, int BT, int EPI>
-__global__ void __launch_bounds__(512, 1) gemm_big8_kernel(OpArgs A, OpArgs B, int K, int kchunk,
-                                                           EpiArgs e, float* partial) {
-  // One 128 KB block: two stages of A and B tiles, later the epilogue slices.
-  __shared__ __attribute__((aligned(16))) bf16_t smem[4 * BIG * BK];
+__device__ __forceinline__ void big8_tile(const OpArgs& A, const OpArgs& B, int K, int kchunk,
+                                          const EpiArgs& e, float* partial, int tx, int ty, int tz,
+                                          bf16_t* smem) {
   bf16_t* const sA0 = smem;
   bf16_t* const sB0 = smem + BIG * BK;
   bf16_t* const sA1 = smem + 2 * BIG * BK;
   bf16_t* const sB1 = smem + 3 * BIG * BK;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 2, wn = wave & 3;  // rows wm * 128 .., columns wn * 64 ..
-  int tx, ty, tz;
-  xcd_tile(tx, ty, tz);
-  if (e.batch > 1) {  // tz indexes the matrix of a batch (never split over K)
-    batch_select(tz, A, B, e);
-    tz = 0;
-  }
   const int m0 = ty * BIG, n0 = tx * BIG;
   const int kbeg = tz * kchunk;
   if (EPI == EPI_PARTIAL) partial += (long)tz * e.M * e.N;
@@ -1124,6 +1120,56 @@ __global__ void __launch_bounds__(512, 1) gemm_big8_kernel(OpArgs A, OpArgs B, i
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next block overwrites
   }
+}
+
+template <int AT, int BT, int EPI>
+__global__ void __launch_bounds__(512, 1) gemm_big8_kernel(OpArgs A, OpArgs B, int K, int kchunk,
+                                                           EpiArgs e, float* partial) {
+  __shared__ __attribute__((aligned(16))) bf16_t smem[4 * BIG * BK];
+  int tx, ty, tz;
+  xcd_tile(tx, ty, tz);
+  if (e.batch > 1) {  // tz indexes the matrix of a batch (never split over K)
+    batch_select(tz, A, B, e);
+    tz = 0;
+  }
+  big8_tile<AT, BT, EPI>(A, B, K, kchunk, e, partial, tx, ty, tz, smem);
+}
+
+// Up to GROUP_MAX products with the same K (a transformer block's weight
+// gradients: K = tokens) in one launch over their concatenated 256-tiles, each
+// split S ways over K.  Workgroups walk the flat (split, tile) space in the
+// XCD-contiguous order of `xcd_tile`; within a product, tiles go in groups of
+// TILE_GROUP tile rows, column by column.
+constexpr int GROUP_MAX = 4;
+struct GroupArgs {
+  OpArgs A[GROUP_MAX], B[GROUP_MAX];
+  int M[GROUP_MAX], N[GROUP_MAX], nx[GROUP_MAX], ny[GROUP_MAX];
+  int tile0[GROUP_MAX + 1];  // first flat tile of each product; tile0[n] = all tiles
+  long part[GROUP_MAX];      // float offset of each product's S partial tiles
+  int n;
+};
+
+template <int AT, int BT>
+__global__ void __launch_bounds__(512, 1) gemm_big8_group_kernel(GroupArgs g, int K, int kchunk,
+                                                                 float* partial) {
+  __shared__ __attribute__((aligned(16))) bf16_t smem[4 * BIG * BK];
+  const int T = g.tile0[g.n];
+  const int total = gridDim.x, L = blockIdx.x;
+  const int id = (total & 7) == 0 ? (L & 7) * (total >> 3) + (L >> 3) : L;
+  const int tz = id / T, t = id - tz * T;
+  int p = 0;
+  while (p + 1 < g.n && t >= g.tile0[p + 1]) ++p;
+  const int r = t - g.tile0[p], nx = g.nx[p], ny = g.ny[p];
+  const int grp = r / (TILE_GROUP * nx);
+  const int rows = min(TILE_GROUP, ny - grp * TILE_GROUP);
+  const int w = r - grp * TILE_GROUP * nx;
+  EpiArgs e{};
+  e.epi = EPI_PARTIAL;
+  e.M = g.M[p];
+  e.N = g.N[p];
+  e.batch = 1;
+  big8_tile<AT, BT, EPI_PARTIAL>(g.A[p], g.B[p], K, kchunk, e, partial + g.part[p], w / rows,
+                                 grp * TILE_GROUP + w % rows, tz, smem);
 }
 
 MfmaKernel big8_kernel_for(int at, int bt, int epi, int ga, int gb) {
@@ -1401,6 +1447,105 @@ hipError_t gemm(const gpt_gemm_desc& d, hipStream_t s) {
   unsigned blocks = (unsigned)std::min<long>(cdiv(total, 256), 4096);
   splitk_reduce_kernel<bf16_t><<<blocks, 256, 0, s>>>(ws, S, e);
   return hipGetLastError();
+}
+
+namespace {
+// Split count of a grouped launch over T 256-tiles: at most one (split, tile)
+// workgroup per CU, each split at least 1024 deep.
+int group_splits(long T, int K) {
+  int S = (int)std::max<long>(1, 256 / std::max<long>(T, 1));
+  return std::min(S, std::max(1, K / 1024));
+}
+
+long group_tiles(const int* M, const int* N, int n) {
+  long T = 0;
+  for (int i = 0; i < n; ++i) T += cdiv(M[i], BIG) * cdiv(N[i], BIG);
+  return T;
+}
+
+// The grouped kernel's conditions: bf16, both operands K-major, fp32 output
+// (store or accumulate, the same for all), one K, vector-width leading
+// dimensions, operands within the 31-bit buffer offsets.
+bool group_ok(const gpt_gemm_desc* d, int n) {
+  if (n < 1 || n > GROUP_MAX) return false;
+  for (int i = 0; i < n; ++i) {
+    const gpt_gemm_desc& x = d[i];
+    if (x.precision != GPT_BF16 || !x.a_trans || !x.b_trans || x.a_gelu || x.b_gelu) return false;
+    if (x.batch > 1 || x.bias || x.resid || x.K != d[0].K || x.epilogue != d[0].epilogue) return false;
+    if (x.epilogue != GPT_EPI_F32 && x.epilogue != GPT_EPI_F32_ACCUM) return false;
+    if (x.M <= 0 || x.N <= 0 || x.K <= 0 || x.N % 8 || x.ldo % 8 || x.lda % 8 || x.ldb % 8) return false;
+    if (!dma_ok(x)) return false;
+  }
+  return true;
+}
+}  // namespace
+
+int64_t gemm_group_workspace_bytes(const int* M, const int* N, int n, int K) {
+  if (n < 1 || n > GROUP_MAX) return 0;
+  const int S = group_splits(group_tiles(M, N, n), K);
+  int64_t mn = 0;
+  for (int i = 0; i < n; ++i) mn += (int64_t)M[i] * N[i];
+  return (int64_t)S * mn * 4;
+}
+
+hipError_t gemm_group(const gpt_gemm_desc* d, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int Ms[GROUP_MAX], Ns[GROUP_MAX];
+  bool grouped = group_ok(d, n);
+  if (grouped) {
+    for (int i = 0; i < n; ++i) {
+      Ms[i] = d[i].M;
+      Ns[i] = d[i].N;
+    }
+    grouped = d[0].workspace &&
+              d[0].workspace_bytes >= gemm_group_workspace_bytes(Ms, Ns, n, d[0].K);
+  }
+  if (!grouped) {  // one launch per product, each with its own plan
+    for (int i = 0; i < n; ++i) {
+      hipError_t e = gemm(d[i], s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  const int K = d[0].K;
+  const long T = group_tiles(Ms, Ns, n);
+  const int S0 = group_splits(T, K);
+  const int kchunk = (int)cdiv(cdiv(K, S0), BK) * BK;
+  const int S = (int)cdiv(K, kchunk);
+  GroupArgs g{};
+  g.n = n;
+  long tile = 0, part = 0;
+  for (int i = 0; i < n; ++i) {
+    const gpt_gemm_desc& x = d[i];
+    g.A[i] = OpArgs{x.A, x.lda, 1, x.a_rows, x.a_kvalid, 0};
+    g.B[i] = OpArgs{x.B, x.ldb, 1, x.b_rows, x.b_kvalid, 0};
+    g.M[i] = x.M;
+    g.N[i] = x.N;
+    g.nx[i] = (int)cdiv(x.N, BIG);
+    g.ny[i] = (int)cdiv(x.M, BIG);
+    g.tile0[i] = (int)tile;
+    g.part[i] = part;
+    tile += (long)g.nx[i] * g.ny[i];
+    part += (long)S * x.M * x.N;
+  }
+  g.tile0[n] = (int)tile;
+  float* ws = (float*)d[0].workspace;
+  gemm_big8_group_kernel<1, 1><<<(unsigned)(T * S), 512, 0, s>>>(g, K, kchunk, ws);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  for (int i = 0; i < n; ++i) {  // each product's partials summed in split order
+    const gpt_gemm_desc& x = d[i];
+    EpiArgs e{x.epilogue, x.gelu_tanh, x.M, x.N, nullptr, nullptr, x.out, x.ldo, nullptr, 0,
+              1.f,        0.f,         1,   0,   0,       0,       0};
+    const unsigned blocks = (unsigned)std::min<long>(cdiv((long)x.M * x.N / 8, 256), 4096);
+    if (x.epilogue == GPT_EPI_F32)
+      splitk_reduce8_kernel<GPT_EPI_F32><<<blocks, 256, 0, s>>>(ws + g.part[i], S, e);
+    else
+      splitk_reduce8_kernel<GPT_EPI_F32_ACCUM><<<blocks, 256, 0, s>>>(ws + g.part[i], S, e);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 }  // namespace gpt

@@ -13,6 +13,11 @@ namespace gpt {
 hipError_t gemm(const gpt_gemm_desc& d, hipStream_t s);
 // Bytes of split-K workspace gemm() may use for this shape (0 = never splits).
 int64_t gemm_workspace_bytes(int M, int N, int K, int precision);
+// n (<= 4) weight-gradient products with the same K in one launch (split-K
+// partials in d[0].workspace, reduced per product in split order); products
+// the grouped kernel cannot take, or a short workspace, run one by one.
+hipError_t gemm_group(const gpt_gemm_desc* d, int n, hipStream_t s);
+int64_t gemm_group_workspace_bytes(const int* M, const int* N, int n, int K);
 // Number of K splits gemm() will use for this descriptor (1 = single kernel).
 int gemm_split_count(const gpt_gemm_desc& d);
 

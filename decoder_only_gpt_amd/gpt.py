@@ -29,15 +29,17 @@ EXPORTS = [
     "gpt_loss_device_ptr", "gpt_backward", "gpt_grad_norm", "gpt_adamw_step", "gpt_muon_step",
     "gpt_get_buffer",
     "gpt_set_buffer", "gpt_destroy", "gpt_gen_plan", "gpt_gen_init", "gpt_gen_reset",
-    "gpt_gen_step", "gpt_gen_logits", "gpt_gen_sample", "gpt_generate", "gpt_gen_destroy", "gpt_last_error", "gpt_op_gemm", "gpt_op_attention_fwd",
-    "gpt_op_attention_bwd", "gpt_op_adamw", "gpt_profile_begin", "gpt_profile_end",
+    "gpt_gen_step", "gpt_gen_logits", "gpt_gen_sample", "gpt_generate", "gpt_gen_destroy",
+    "gpt_last_error", "gpt_op_gemm", "gpt_op_gemm_group", "gpt_op_gemm_group_workspace",
+    "gpt_op_attention_fwd", "gpt_op_attention_bwd", "gpt_op_adamw", "gpt_profile_begin",
+    "gpt_profile_end",
 ]
 KERNEL_KINDS = ["gemm", "gemm_splitk", "attn_fwd", "attn_bwd", "layernorm", "cross_entropy",
                 "embed", "bias_grad", "norm", "adamw"]
 SITES = ["embed_fwd", "ln_fwd", "qkv_fwd", "attn_fwd", "proj_fwd", "fc_fwd", "fcproj_fwd",
          "lmhead_fwd", "cross_entropy", "lmhead_dx", "lmhead_dw", "ln_bwd", "fcproj_dx", "fcproj_dw",
          "fc_dx", "fc_dw", "proj_dx", "proj_dw", "attn_bwd", "qkv_dx", "qkv_dw", "bias_grad",
-         "embed_bwd", "grad_norm", "adamw"]
+         "embed_bwd", "grad_norm", "adamw", "block_dw"]
 
 
 class GptError(RuntimeError):
@@ -143,6 +145,9 @@ def lib():
         "gpt_destroy": ([vp], i32),
         "gpt_last_error": ([], ctypes.c_char_p),
         "gpt_op_gemm": ([ctypes.POINTER(GemmDesc), vp], i32),
+        "gpt_op_gemm_group": ([ctypes.POINTER(GemmDesc), i32, vp], i32),
+        "gpt_op_gemm_group_workspace": ([ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
+                                         i32, i32], i64),
         "gpt_op_attention_fwd": ([i32, i32, i32, i32, i32, i32, vp, vp, vp, vp], i32),
         "gpt_op_attention_bwd": ([i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp], i32),
         "gpt_op_adamw": ([i64, vp, vp, vp, vp, vp, ctypes.POINTER(AdamHP), vp], i32),
@@ -386,6 +391,18 @@ def _ptr(t):
 
 def op_gemm(desc: GemmDesc):
     _check(lib().gpt_op_gemm(ctypes.byref(desc), _stream()))
+
+
+def op_gemm_group(descs):
+    """gpt_op_gemm_group over a list of GemmDesc (1..4)."""
+    arr = (GemmDesc * len(descs))(*descs)
+    _check(lib().gpt_op_gemm_group(arr, len(descs), _stream()))
+
+
+def op_gemm_group_workspace(Ms, Ns, K: int) -> int:
+    n = len(Ms)
+    return int(lib().gpt_op_gemm_group_workspace((ctypes.c_int32 * n)(*Ms), (ctypes.c_int32 * n)(*Ns),
+                                                 n, int(K)))
 
 
 def op_attention_fwd(precision, B, T, H, hd, left, qkv, out, lse):

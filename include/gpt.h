@@ -224,6 +224,7 @@ typedef enum gpt_site {
   GPT_S_LMHEAD_DW, GPT_S_LN_BWD, GPT_S_FCPROJ_DX, GPT_S_FCPROJ_DW, GPT_S_FC_DX, GPT_S_FC_DW,
   GPT_S_PROJ_DX, GPT_S_PROJ_DW, GPT_S_ATTN_BWD, GPT_S_QKV_DX, GPT_S_QKV_DW, GPT_S_BIAS_GRAD,
   GPT_S_EMBED_BWD, GPT_S_GRAD_NORM, GPT_S_ADAMW,
+  GPT_S_BLOCK_DW,  /* a block's four weight gradients as one grouped launch (+ reductions) */
   GPT_NUM_SITES
 } gpt_site;
 
@@ -329,6 +330,23 @@ typedef struct gpt_gemm_desc {
 } gpt_gemm_desc;
 
 int gpt_op_gemm(const gpt_gemm_desc* d, void* stream);
+
+/* n (1..4) products sharing K in one launch, as a transformer block's weight
+ * gradients dW (+)= dY^T X are (the backward of the step's Linear layers,
+ * nanoGPT "model.py" CausalSelfAttention / MLP; K = the batch's tokens).  Each
+ * descriptor is validated as in gpt_op_gemm.  Grouped when every product is
+ * bf16 with both operands K-major (a_trans = b_trans = 1), epilogue F32 or
+ * F32_ACCUM (the same for all), no bias / resid / GELU operand / batch, and
+ * descs[0].workspace holds the split partials (gpt_op_gemm_group_workspace);
+ * the 256-tiles of all products are split over K together and each product's
+ * partial sums are reduced in fixed split order, so results are reproducible
+ * (not bitwise equal to gpt_op_gemm, whose split count differs).  Otherwise
+ * the products run one by one through gpt_op_gemm.  descs is host memory,
+ * read during the call only. */
+int gpt_op_gemm_group(const gpt_gemm_desc* descs, int32_t n, void* stream);
+/* Workspace bytes the grouped launch of products [M_i, N_i] with reduction
+ * length K needs (0 if n is out of range). */
+int64_t gpt_op_gemm_group_workspace(const int32_t* M, const int32_t* N, int32_t n, int32_t K);
 
 /* Causal (windowed) attention over a packed qkv [B*T, 3*H*hd] (q | k | v,
  * head h at columns h*hd of each third).  out [B*T, H*hd] (act type), lse

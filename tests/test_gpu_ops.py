@@ -256,6 +256,72 @@ def test_attention_fwd_bwd(prec, B, T, H, hd, left):
         assert cos > (0.9995 if prec == gpt.BF16 else 1 - 1e-9), (i, cos)
 
 
+# ------------------------------------------------------------------ grouped GEMM
+GROUP_CASES = [
+    # reduction length K, products [(M, N)], epilogue
+    (2048, [(64, 256), (256, 64), (64, 64), (192, 64)], gpt.EPI_F32),        # a small block's dW
+    (3000, [(200, 136), (72, 512)], gpt.EPI_F32_ACCUM),                      # ragged tiles and K
+    (2048, [(768, 3072), (3072, 768), (768, 768), (2304, 768)], gpt.EPI_F32),  # GPT-2 124M's block
+    (1024, [(130, 72)], gpt.EPI_F32),                                         # a group of one
+]
+
+
+def _group_descs(K, shapes, epi, seed, trans_a=1):
+    """Descriptors dW_i (+)= A_i^T-layout products for gpt_op_gemm_group, with
+    the exact expected results."""
+    ds, keep, refs = [], [], []
+    for i, (M, N) in enumerate(shapes):
+        A, lda, Ax = _operand(M, K, trans_a if i == 0 else 1, torch.bfloat16, seed + 2 * i)
+        B, ldb, Bx = _operand(N, K, 1, torch.bfloat16, seed + 2 * i + 1)
+        init = synth.normal((M, N), seed + 50 + i, 1.0).astype(np.float32)
+        out = torch.from_numpy(init.copy()).cuda()
+        ref = Ax @ Bx.T + (init if epi == gpt.EPI_F32_ACCUM else 0.0)
+        ds.append(gpt.GemmDesc(precision=gpt.BF16, M=M, N=N, K=K, A=A.data_ptr(), lda=lda,
+                               a_trans=trans_a if i == 0 else 1, a_rows=M, a_kvalid=K,
+                               B=B.data_ptr(), ldb=ldb, b_trans=1, b_rows=N, b_kvalid=K,
+                               epilogue=epi, out=out.data_ptr(), ldo=N))
+        keep += [A, B, out]
+        refs.append((out, ref))
+    return ds, keep, refs
+
+
+@pytest.mark.parametrize("K,shapes,epi", GROUP_CASES)
+def test_gemm_group(K, shapes, epi):
+    """A block's weight gradients in one grouped launch: every product matches
+    its exact value (bf16 inputs, fp32 accumulation), for fresh and
+    accumulated outputs."""
+    ds, keep, refs = _group_descs(K, shapes, epi, seed=300)
+    need = gpt.op_gemm_group_workspace([m for m, _ in shapes], [n for _, n in shapes], K)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    for d in ds:
+        d.workspace, d.workspace_bytes = ws.data_ptr(), ws.numel()
+    gpt.op_gemm_group(ds)
+    torch.cuda.synchronize()
+    for out, ref in refs:
+        err = np.abs(out.cpu().numpy() - ref).max() / np.abs(ref).max()
+        assert err < 2e-5, err
+
+
+def test_gemm_group_fallbacks():
+    """A member the grouped kernel cannot take (row-major A) and a workspace
+    too small for the partials both run product by product, with the same
+    results; the group size is checked."""
+    K, shapes = 1024, [(96, 128), (64, 256)]
+    for trans_a, ws_bytes in ((0, 1 << 24), (1, 16)):
+        ds, keep, refs = _group_descs(K, shapes, gpt.EPI_F32, seed=400, trans_a=trans_a)
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+        for d in ds:
+            d.workspace, d.workspace_bytes = ws.data_ptr(), ws_bytes
+        gpt.op_gemm_group(ds)
+        torch.cuda.synchronize()
+        for out, ref in refs:
+            err = np.abs(out.cpu().numpy() - ref).max() / np.abs(ref).max()
+            assert err < 2e-5, (trans_a, ws_bytes, err)
+    with pytest.raises(gpt.GptError):
+        gpt.op_gemm_group([])
+
+
 # ------------------------------------------------------------------ batched GEMM
 BATCH_CASES = [
     # batch, M, N, K, a_trans, b_trans, epilogue
