@@ -54,7 +54,13 @@ __device__ __forceinline__ void store4_nt(float* q, const float4& v) {
 __global__ void __launch_bounds__(256) adamw_kernel(int64_t n, float* __restrict__ p,
                                                     float* __restrict__ m, float* __restrict__ v,
                                                     const float* __restrict__ g,
-                                                    bf16_t* __restrict__ shadow, AdamScalars s) {
+                                                    bf16_t* __restrict__ shadow, AdamScalars s,
+                                                    const float* __restrict__ d_scale) {
+  if (d_scale) {  // gradient scale from the device clip; NaN: non-finite norm, no update
+    const float sc = *d_scale;
+    if (sc != sc) return;
+    s.scale = sc;
+  }
   const int64_t half = (int64_t)gridDim.x * 256 * 4;  // elements covered by one float4 per thread
   const int64_t stride = 2 * half;
   for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n; i += stride) {
@@ -122,7 +128,30 @@ __global__ void __launch_bounds__(256) adamw_segments_kernel(
   }
 }
 
+// The global-norm clip of a step on the device, in the host rule's double
+// arithmetic: norm = sqrt(sum g^2) / n_micro, c = max_norm / norm if
+// max_norm > 0 and norm > max_norm (else 1), grad_scale = c / n_micro.
+// out = {norm, grad_scale}; scale = (float) grad_scale, NaN if the norm is not
+// finite.
+__global__ void clip_scale_kernel(const double* __restrict__ norm2, int n_micro, double max_norm,
+                                  double* __restrict__ out, float* __restrict__ scale) {
+  if (blockIdx.x != 0 || threadIdx.x != 0) return;
+  const double norm = sqrt(*norm2) / (double)n_micro;
+  const double c = (max_norm > 0.0 && norm > max_norm) ? max_norm / norm : 1.0;
+  const double sc = c / (double)n_micro;
+  const bool finite = norm - norm == 0.0;
+  out[0] = norm;
+  out[1] = finite ? sc : __builtin_nan("");
+  *scale = finite ? (float)sc : __builtin_nanf("");
+}
+
 }  // namespace
+
+hipError_t clip_scale(const double* norm2, int n_micro, double max_norm, double* out, float* scale,
+                      hipStream_t s) {
+  clip_scale_kernel<<<1, 64, 0, s>>>(norm2, n_micro, max_norm, out, scale);
+  return hipGetLastError();
+}
 
 int adamw_segment_blocks(int64_t len) { return (int)cdiv(len, ADAM_SEG_CHUNK); }
 
@@ -135,11 +164,11 @@ hipError_t adamw_segments(const int64_t* d_seg, int nseg, int blocks, float* p, 
 }
 
 hipError_t adamw(int64_t n, float* p, float* m, float* v, const float* g, uint16_t* shadow,
-                 AdamScalars sc, hipStream_t s) {
+                 AdamScalars sc, hipStream_t s, const float* d_scale) {
   if (n <= 0) return hipSuccess;
   int64_t blocks = cdiv(cdiv(n, 8), 256);
   if (blocks > 8192) blocks = 8192;
-  adamw_kernel<<<(unsigned)blocks, 256, 0, s>>>(n, p, m, v, g, shadow, sc);
+  adamw_kernel<<<(unsigned)blocks, 256, 0, s>>>(n, p, m, v, g, shadow, sc, d_scale);
   return hipGetLastError();
 }
 

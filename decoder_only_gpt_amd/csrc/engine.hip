@@ -131,7 +131,7 @@ struct Arena {
   int64_t X, ln_mean, ln_rstd;
   std::vector<int64_t> a1, qkv, att, lse, a2, u, g;
   int64_t xf, logits, loss_rows, loss, gres[2], gact[NGB], dC, dC2, dF[NGB], dqkv[NGB], dvec;
-  int64_t gemm_ws, gemm_ws_bytes, cs_part, ln_part, n_part, norm2, muon_ws, adam_seg;
+  int64_t gemm_ws, gemm_ws_bytes, cs_part, ln_part, n_part, norm2, clip, muon_ws, adam_seg;
   int64_t e_counts, e_offsets, e_tile_sums, e_rank, e_perm, e_carry_first, e_carry_last, e_flags,
       e_last_tok;
   int64_t state_end, total;
@@ -207,6 +207,7 @@ Arena plan_arena(const gpt_config& c, int B, int T) {
   a.e_last_tok = take(nch * 4);
   a.n_part = take(1024 * 8);
   a.norm2 = take(16);
+  a.clip = take(32);  // device clip: {norm, grad_scale} doubles, then grad_scale as float
   // Muon working set, sized for the largest kind of block matrix (one kind at a time).
   int64_t mw = 0;
   for (auto rc : {std::pair<int64_t, int64_t>{3 * C, C}, {C, C}, {F, C}, {C, F}})
@@ -248,7 +249,7 @@ struct gpt_model {
   // Weight-gradient branch of the backward: a second stream (default
   // priority) and the events that order it against the main chain.
   hipStream_t side = nullptr;
-  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr, ev_lmdw = nullptr;
   hipEvent_t ev_buf[3 * NGB] = {};  // last side-stream read of gact[], dF[], dqkv[]
   // AdamW runs on the side stream in parameter groups (embeddings, each layer,
   // the final LayerNorm and untied head); the next forward waits per group.
@@ -526,6 +527,7 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
   CHECK(fork());
   d = linear_dw(m, dlog, m->Vq, m->Vq, act(m->ar.xf), C, m->pl.lmw, m->Vp, acc);
   CHECK(gemm_on(s2, d, GPT_S_LMHEAD_DW));
+  if (s2 != s) CHECK(hip_ok(hipEventRecord(m->ev_lmdw, s2), "hipEventRecord"));
   const int64_t nl = 2 * c.n_layer;
   int gi = 0;  // gact[gi] holds the current LayerNorm input gradient (bf16); slots 0..NGB-1
   char* gact = act(m->ar.gact[gi]);
@@ -607,14 +609,10 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
                               m->G(L.ln1b), acc, ln_part, s));
     cur ^= 1;
   }
-  // The side stream's gradients (dwte among them with a tied head) are
-  // complete before anything below, or anything after the backward, runs.
-  if (s2 != s) {
-    CHECK(hip_ok(hipEventRecord(m->ev_join, s2), "hipEventRecord"));
-    CHECK(hip_ok(hipStreamWaitEvent(s, m->ev_join, 0), "hipStreamWaitEvent"));
-  }
-#undef CHECK
-  // x0 = wte[idx] + wpe[t]; with a tied head the lm_head gradient is already in dwte.
+  // x0 = wte[idx] + wpe[t]; with a tied head the lm_head gradient is already
+  // in dwte: the embedding backward waits for that side-stream launch only,
+  // and the rest of the side stream joins after it.
+  if (s2 != s) CHECK(hip_ok(hipStreamWaitEvent(s, m->ev_lmdw, 0), "hipStreamWaitEvent"));
   gpt::EmbedBwdScratch scr{m->at<int32_t>(m->ar.e_counts),   m->at<int32_t>(m->ar.e_offsets),
                            m->at<int32_t>(m->ar.e_tile_sums), m->at<int32_t>(m->ar.e_rank),
                            m->at<int32_t>(m->ar.e_perm),
@@ -624,6 +622,12 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
   LAUNCH(GPT_K_EMBED, GPT_S_EMBED_BWD, 0, 4.0 * M * C + 4.0 * (m->Vp + c.block_size) * C,
          gpt::embed_bwd(m->last_idx, gres[cur], (int)M, m->T, (int)C, (int)m->Vp, c.block_size,
                         m->G(m->pl.wte), wte_acc, m->G(m->pl.wpe), acc, scr, s));
+  // Every gradient is complete before anything after the backward runs.
+  if (s2 != s) {
+    CHECK(hip_ok(hipEventRecord(m->ev_join, s2), "hipEventRecord"));
+    CHECK(hip_ok(hipStreamWaitEvent(s, m->ev_join, 0), "hipStreamWaitEvent"));
+  }
+#undef CHECK
   return GPT_OK;
 }
 
@@ -723,6 +727,7 @@ int gpt_init(const gpt_config* cfg, int32_t B, int32_t T, void* d_arena, int64_t
   hipError_t se = hipStreamCreateWithFlags(&m->side, hipStreamNonBlocking);
   if (se == hipSuccess) se = hipEventCreateWithFlags(&m->ev_fork, hipEventDisableTiming);
   if (se == hipSuccess) se = hipEventCreateWithFlags(&m->ev_join, hipEventDisableTiming);
+  if (se == hipSuccess) se = hipEventCreateWithFlags(&m->ev_lmdw, hipEventDisableTiming);
   for (int i = 0; i < 3 * NGB && se == hipSuccess; ++i)
     se = hipEventCreateWithFlags(&m->ev_buf[i], hipEventDisableTiming);
   for (int i = 0; i < cfg->n_layer + 2 && se == hipSuccess; ++i) {
@@ -989,7 +994,7 @@ int gpt_gen_destroy(gpt_gen* g) {
 int gpt_destroy(gpt_model* m) {
   if (m) {
     for (hipEvent_t e : m->ev_pool) (void)hipEventDestroy(e);
-    for (hipEvent_t e : {m->ev_fork, m->ev_join})
+    for (hipEvent_t e : {m->ev_fork, m->ev_join, m->ev_lmdw})
       if (e) (void)hipEventDestroy(e);
     for (hipEvent_t e : m->ev_buf)
       if (e) (void)hipEventDestroy(e);
@@ -1084,6 +1089,54 @@ int gpt_adamw_step(gpt_model* m, const gpt_adamw_hp* hp, void* stream) {
   }
   m->state = 0;
   m->loss_valid = false;
+  return GPT_OK;
+}
+
+int gpt_adamw_step_clipped(gpt_model* m, const gpt_adamw_hp* hp, int32_t n_micro, double max_norm,
+                           double* h_norm_scale, void* stream) {
+  if (!m) return fail(GPT_E_INVALID, "NULL model");
+  int rc = check_hp(hp);
+  if (rc != GPT_OK) return rc;
+  if (n_micro < 1) return fail(GPT_E_INVALID, "n_micro must be >= 1");
+  if (!(max_norm >= 0.0) || !std::isfinite(max_norm)) return fail(GPT_E_INVALID, "bad max_norm");
+  if (m->state != 2) return fail(GPT_E_STATE, "adamw_step needs a backward first");
+  hipStream_t s = (hipStream_t)stream;
+  double* clip = m->at<double>(m->ar.clip);
+  float* d_scale = (float*)(clip + 2);
+  LAUNCH(GPT_K_NORM, GPT_S_GRAD_NORM, 0, 4.0 * m->N,
+         gpt::sumsq(m->G(0), m->N, m->at<double>(m->ar.n_part), m->at<double>(m->ar.norm2), s));
+  HIP_TRY(gpt::clip_scale(m->at<double>(m->ar.norm2), n_micro, max_norm, clip, d_scale, s));
+  if (h_norm_scale)
+    HIP_TRY(hipMemcpyAsync(h_norm_scale, clip, 16, hipMemcpyDeviceToHost, s));
+  float* pm = m->at<float>(m->ar.adam_m);
+  float* pv = m->at<float>(m->ar.adam_v);
+  uint16_t* sh = m->bf16 ? m->at<uint16_t>(m->ar.shadow) : nullptr;
+  const gpt::AdamScalars sc = adam_scalars(*hp);
+  if (m->prof_on) {
+    LAUNCH(GPT_K_ADAMW, GPT_S_ADAMW, 0, (m->bf16 ? 30.0 : 28.0) * m->N,
+           gpt::adamw(m->N, m->P(0), pm, pv, m->G(0), sh, sc, s, d_scale));
+  } else {
+    HIP_TRY(hipEventRecord(m->ev_fork, s));
+    HIP_TRY(hipStreamWaitEvent(m->side, m->ev_fork, 0));
+    for (int g = 0; g < (int)m->ev_adam.size(); ++g) {
+      int64_t b, e;
+      adam_group(m, g, &b, &e);
+      HIP_TRY(gpt::adamw(e - b, m->P(b), pm + b, pv + b, m->G(b), sh ? sh + b : nullptr, sc,
+                         m->side, d_scale));
+      HIP_TRY(hipEventRecord(m->ev_adam[g], m->side));
+    }
+    m->adam_pending = true;
+  }
+  m->state = 0;
+  m->loss_valid = false;
+  return GPT_OK;
+}
+
+int gpt_loss_async(gpt_model* m, float* h_loss, void* stream) {
+  if (!m || !h_loss) return fail(GPT_E_INVALID, "NULL argument");
+  if (!m->loss_valid) return fail(GPT_E_STATE, "no forward with targets since the last update");
+  HIP_TRY(hipMemcpyAsync(h_loss, m->at<float>(m->ar.loss), 4, hipMemcpyDeviceToHost,
+                         (hipStream_t)stream));
   return GPT_OK;
 }
 

@@ -73,8 +73,14 @@ hipError_t to_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t s);
 
 // AdamW (adamw.hip).
 struct AdamScalars { float omb1, omb2, decay, step_size, sbc2, eps, scale; };
+// d_scale (device, may be NULL): the gradient scale in place of sc.scale; a
+// NaN there leaves p, m, v and the shadow unchanged.
 hipError_t adamw(int64_t n, float* p, float* m, float* v, const float* g, uint16_t* shadow,
-                 AdamScalars sc, hipStream_t s);
+                 AdamScalars sc, hipStream_t s, const float* d_scale = nullptr);
+// Device global-norm clip from the sum of squares at norm2: out = {norm,
+// grad_scale} (doubles), scale = grad_scale as float (NaN: non-finite norm).
+hipError_t clip_scale(const double* norm2, int n_micro, double max_norm, double* out, float* scale,
+                      hipStream_t s);
 // AdamW over segments of the flat vectors in one launch.  d_seg (device):
 // (begin, length, first block) per segment; lengths multiples of 4; the
 // first blocks are the running sum of adamw_segment_blocks(length).

@@ -9,6 +9,7 @@ is no fallback path.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 
 import numpy as np
@@ -26,7 +27,8 @@ BUF_PARAMS, BUF_GRADS, BUF_ADAM_M, BUF_ADAM_V, BUF_LOSS_ROWS = range(5)
 # Every symbol include/gpt.h declares.
 EXPORTS = [
     "gpt_plan", "gpt_flops_per_token", "gpt_init", "gpt_forward", "gpt_loss",
-    "gpt_loss_device_ptr", "gpt_backward", "gpt_grad_norm", "gpt_adamw_step", "gpt_muon_step",
+    "gpt_loss_device_ptr", "gpt_loss_async", "gpt_backward", "gpt_grad_norm", "gpt_adamw_step",
+    "gpt_adamw_step_clipped", "gpt_muon_step",
     "gpt_get_buffer",
     "gpt_set_buffer", "gpt_destroy", "gpt_gen_plan", "gpt_gen_init", "gpt_gen_reset",
     "gpt_gen_step", "gpt_gen_logits", "gpt_gen_sample", "gpt_generate", "gpt_gen_destroy",
@@ -40,6 +42,9 @@ SITES = ["embed_fwd", "ln_fwd", "qkv_fwd", "attn_fwd", "proj_fwd", "fc_fwd", "fc
          "lmhead_fwd", "cross_entropy", "lmhead_dx", "lmhead_dw", "ln_bwd", "fcproj_dx", "fcproj_dw",
          "fc_dx", "fc_dw", "proj_dx", "proj_dw", "attn_bwd", "qkv_dx", "qkv_dw", "bias_grad",
          "embed_bwd", "grad_norm", "adamw", "block_dw"]
+
+
+GPT_E_NONFINITE = 4  # gpt_status: gradient norm is NaN or Inf
 
 
 class GptError(RuntimeError):
@@ -131,6 +136,8 @@ def lib():
         "gpt_backward": ([vp, i32, vp], i32),
         "gpt_grad_norm": ([vp, vp, ctypes.POINTER(ctypes.c_double)], i32),
         "gpt_adamw_step": ([vp, ctypes.POINTER(AdamHP), vp], i32),
+        "gpt_adamw_step_clipped": ([vp, ctypes.POINTER(AdamHP), i32, ctypes.c_double, vp, vp], i32),
+        "gpt_loss_async": ([vp, vp, vp], i32),
         "gpt_muon_step": ([vp, ctypes.POINTER(AdamHP), ctypes.POINTER(MuonHP), vp], i32),
         "gpt_gen_plan": ([vp, i32, i32, ctypes.POINTER(i64)], i32),
         "gpt_gen_init": ([vp, i32, i32, vp, i64, vp, ctypes.POINTER(vp)], i32),
@@ -286,6 +293,29 @@ class Model:
         hp = adam_hp(self.cfg, t, grad_scale, lr)
         _check(lib().gpt_adamw_step(self.h, ctypes.byref(hp), _stream()))
 
+    def _pinned(self):
+        """Page-locked host slots for the asynchronous read-backs: loss (float32)
+        and {norm, grad_scale} (float64)."""
+        if getattr(self, "_pin", None) is None:
+            import torch
+            self._pin = (torch.zeros(1, dtype=torch.float32, pin_memory=True),
+                         torch.zeros(2, dtype=torch.float64, pin_memory=True))
+        return self._pin
+
+    def loss_async(self):
+        """Enqueue the loss copy into the page-locked slot (read it after a sync)."""
+        pl, _ = self._pinned()
+        _check(lib().gpt_loss_async(self.h, ctypes.c_void_p(pl.data_ptr()), _stream()))
+
+    def adamw_step_clipped(self, t: int, max_norm: float, n_micro: int = 1,
+                           lr: float | None = None):
+        """Device-side norm, clip and AdamW; {norm, grad_scale} land in the
+        page-locked slot (read them after a sync)."""
+        _, pn = self._pinned()
+        hp = adam_hp(self.cfg, t, 1.0, lr)
+        _check(lib().gpt_adamw_step_clipped(self.h, ctypes.byref(hp), int(n_micro), float(max_norm),
+                                            ctypes.c_void_p(pn.data_ptr()), _stream()))
+
     def muon_step(self, t: int, grad_scale: float = 1.0, muon: MuonHP | None = None,
                   lr: float | None = None):
         """Muon on the per-layer Linear weights, AdamW (lr, t, grad_scale) on the rest."""
@@ -306,18 +336,26 @@ class Model:
         return conv(KERNEL_KINDS, arr), conv(SITES, sites)
 
     def train_step(self, idx, tgt) -> dict:
-        """forward -> loss -> backward -> (norm, clip) -> AdamW; returns loss/norm/scale."""
+        """forward -> loss -> backward -> (norm, clip) -> AdamW; returns loss/norm/scale.
+        Everything is enqueued before any host wait: the loss and the norm /
+        clip scale come back through asynchronous copies, read after one sync
+        at the end (while AdamW still runs on the model's side stream)."""
+        import torch
         self.forward(idx, tgt)
-        loss = self.loss()
+        self.loss_async()
         self.backward(0)
         self.step_t += 1
-        norm, scale = None, 1.0
         clip = float(self.cfg.get("clip", 0.0) or 0.0)
         if clip > 0.0:
-            norm = self.grad_norm()
-            if norm > clip:
-                scale = clip / norm
-        self.adamw_step(self.step_t, scale)
+            self.adamw_step_clipped(self.step_t, clip)
+        else:
+            self.adamw_step(self.step_t, 1.0)
+        torch.cuda.current_stream().synchronize()
+        pl, pn = self._pinned()
+        loss = float(pl[0])
+        norm, scale = (float(pn[0]), float(pn[1])) if clip > 0.0 else (None, 1.0)
+        if norm is not None and not math.isfinite(norm):
+            raise GptError(GPT_E_NONFINITE, f"gradient norm is not finite ({norm}); no update")
         return dict(loss=loss, norm=norm, scale=scale)
 
 

@@ -160,6 +160,11 @@ int gpt_loss(gpt_model* m, void* stream, float* h_mean_loss);
  * with targets has been enqueued; for callers that avoid a sync. */
 int gpt_loss_device_ptr(gpt_model* m, const float** d_loss);
 
+/* The mean loss of the last forward with targets, copied to host memory
+ * h_loss asynchronously on `stream` (valid once the stream has passed this
+ * point; page-locked memory keeps the call asynchronous). */
+int gpt_loss_async(gpt_model* m, float* h_loss, void* stream);
+
 /* Backward pass of the last forward with targets.  accumulate = 0
  * overwrites the gradient buffer, 1 adds to it.  Enqueue only. */
 int gpt_backward(gpt_model* m, int32_t accumulate, void* stream);
@@ -171,6 +176,21 @@ int gpt_grad_norm(gpt_model* m, void* stream, double* h_norm);
 
 /* One AdamW update of all parameters (see gpt_adamw_hp).  Enqueue only. */
 int gpt_adamw_step(gpt_model* m, const gpt_adamw_hp* hp, void* stream);
+
+/* Gradient-norm clipping and the AdamW update with no host round trip
+ * (llm.c / nanoGPT "train_gpt2": clip the global gradient norm at
+ * max_norm before the optimizer step).  Enqueue only.  On the device: norm =
+ * sqrt(sum g^2) / n_micro (the norm of the mean of n_micro accumulated
+ * micro-batch gradients), c = max_norm / norm if max_norm > 0 and
+ * norm > max_norm, else 1, grad_scale = c / n_micro; hp->grad_scale is
+ * ignored.  The arithmetic is gpt_grad_norm followed by that host rule in
+ * double, so the update is bit-identical to gpt_adamw_step with the
+ * host-computed grad_scale.  A non-finite norm leaves parameters, moments and
+ * the bf16 copy unchanged.  h_norm_scale: NULL or host memory for {norm,
+ * grad_scale} (NaN scale: non-finite norm), copied asynchronously on
+ * `stream`; page-locked memory keeps the call asynchronous. */
+int gpt_adamw_step_clipped(gpt_model* m, const gpt_adamw_hp* hp, int32_t n_micro, double max_norm,
+                           double* h_norm_scale, void* stream);
 
 /* The hybrid optimizer step (after gpt_backward, in place of gpt_adamw_step):
  * Muon (hp `muon`, above) on every per-layer Linear weight, AdamW (hp

@@ -213,3 +213,77 @@ def test_gradient_accumulation_adds():
         off += n
         scale = np.abs(b).max()
         assert np.abs(a - b).max() <= 1e-6 * scale, name
+
+
+def _two_models(cfg, seed):
+    p = synth.init_params(cfg, seed=seed, perturb=True)
+    ms = []
+    for _ in range(2):
+        m = gpt.Model(cfg)
+        m.set_params(p)
+        ms.append(m)
+    return ms
+
+
+@pytest.mark.parametrize("prec", ["fp32", "bf16"])
+@pytest.mark.parametrize("max_norm", [0.0, 1e-3, 1e9])   # no clip, clip active, clip inactive
+@pytest.mark.parametrize("n_micro", [1, 2])
+def test_device_clip_matches_host_rule(prec, max_norm, n_micro):
+    """gpt_adamw_step_clipped (norm, clip and AdamW on the device, no host
+    round trip) against gpt_grad_norm + the host clip rule + gpt_adamw_step:
+    the same norm and grad_scale doubles, parameters and moments bit for bit."""
+    cfg = dict(gpu_cfgs()["gpt2_s"], precision=prec)
+    host, dev = _two_models(cfg, seed=6)
+    batches = [synth.tokens(cfg, seed=20 + k) for k in range(n_micro)]
+    for m in (host, dev):
+        for k, (idx, tgt) in enumerate(batches):
+            m.forward(torch.from_numpy(idx.reshape(-1)).cuda(), torch.from_numpy(tgt.reshape(-1)).cuda())
+            m.backward(1 if k else 0)
+    norm = host.grad_norm() / n_micro
+    clip = max_norm / norm if (max_norm > 0.0 and norm > max_norm) else 1.0
+    scale = clip / n_micro
+    host.adamw_step(1, scale)
+    dev.adamw_step_clipped(1, max_norm, n_micro)
+    torch.cuda.synchronize()
+    _, pn = dev._pinned()
+    assert float(pn[0]) == norm and float(pn[1]) == scale
+    for which in (gpt.BUF_PARAMS, gpt.BUF_ADAM_M, gpt.BUF_ADAM_V):
+        a, b = host.get_buffer(which), dev.get_buffer(which)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), which
+
+
+def test_device_clip_nonfinite_skips_update():
+    """A non-finite gradient norm: no parameter or moment changes, NaN scale
+    reported, and Model.train_step raises."""
+    cfg = presets.preset("tiny")
+    m = gpt.Model(cfg)
+    m.set_params(synth.init_params(cfg))
+    p0 = m.params().copy()
+    g = np.zeros(m.n_params, np.float32)
+    g[77] = np.nan
+    m.set_buffer(gpt.BUF_GRADS, g)
+    m.adamw_step_clipped(1, 1.0)
+    torch.cuda.synchronize()
+    _, pn = m._pinned()
+    assert not np.isfinite(float(pn[0])) and np.isnan(float(pn[1]))
+    assert np.array_equal(m.params().view(np.uint32), p0.view(np.uint32))
+    assert not np.any(m.get_buffer(gpt.BUF_ADAM_M)) and not np.any(m.get_buffer(gpt.BUF_ADAM_V))
+
+
+def test_train_step_async_readback_matches_sync_path():
+    """Model.train_step (asynchronous loss / norm read-back, device clip)
+    returns the same loss, norm and scale and leaves the same parameters as the
+    synchronous call sequence."""
+    cfg = gpu_cfgs()["gpt2_s"]
+    a, b = _two_models(cfg, seed=8)
+    idx, tgt = synth.tokens(cfg, seed=9)
+    di, dt = torch.from_numpy(idx.reshape(-1)).cuda(), torch.from_numpy(tgt.reshape(-1)).cuda()
+    r = a.train_step(di, dt)
+    b.forward(di, dt)
+    loss = b.loss()
+    b.backward(0)
+    norm = b.grad_norm()
+    scale = cfg["clip"] / norm if norm > cfg["clip"] else 1.0
+    b.adamw_step(1, scale)
+    assert r["loss"] == loss and r["norm"] == norm and r["scale"] == scale
+    assert np.array_equal(a.params().view(np.uint32), b.params().view(np.uint32))
