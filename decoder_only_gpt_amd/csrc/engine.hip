@@ -502,11 +502,12 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
   auto gemm_on = [&](hipStream_t st, const gpt_gemm_desc& dd, int site) -> int {
     return run_gemm(m, st, dd, site);
   };
-  auto gemm_group_on = [&](hipStream_t st, const gpt_gemm_desc* dd, int n, int site) -> int {
+  auto gemm_group_on = [&](hipStream_t st, const gpt_gemm_desc* dd, float* const* db, int n,
+                           int site) -> int {
     double fl = 0;
     for (int i = 0; i < n; ++i) fl += 2.0 * dd[i].M * dd[i].N * dd[i].K;
     hipStream_t s = st;
-    LAUNCH(GPT_K_GEMM_SPLITK, site, fl, 0, gpt::gemm_group(dd, n, s));
+    LAUNCH(GPT_K_GEMM_SPLITK, site, fl, 0, gpt::gemm_group(dd, n, s, db));
     return GPT_OK;
   };
   auto bias_grad = [&](const char* x, int64_t n, int64_t off) -> int {
@@ -551,20 +552,28 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
     // and issued as one grouped launch once dqkv exists, and the buffers they
     // read are released after it.  With GELU recompute the FC-projection
     // weight gradient applies GELU to its operand and runs alone.
+    // In bf16 the bias gradients (column sums of each dY) come out of the same
+    // launch, summed from the dY tiles it stages in LDS.
     gpt_gemm_desc dw[4];
+    float* db[4];
     int ndw = 0, held[4], nheld = 0;
+    auto add_dw = [&](const gpt_gemm_desc& dd, const char* dy, int64_t n, int64_t b_off) -> int {
+      dw[ndw] = dd;
+      db[ndw] = (m->bf16 && b_off >= 0) ? m->G(b_off) : nullptr;
+      ++ndw;
+      return m->bf16 ? GPT_OK : bias_grad(dy, n, b_off);
+    };
     if (c.recompute_gelu) {
       d = linear_dw(m, gact, C, C, act(m->ar.u[l]), F, L.fcpw, C, acc);
       d.b_gelu = 1;
       CHECK(gemm_on(s2, d, GPT_S_FCPROJ_DW));
+      CHECK(bias_grad(gact, C, L.fcpb));
     } else {
-      dw[ndw++] = linear_dw(m, gact, C, C, act(m->ar.g[l]), F, L.fcpw, C, acc);
+      CHECK(add_dw(linear_dw(m, gact, C, C, act(m->ar.g[l]), F, L.fcpw, C, acc), gact, C, L.fcpb));
     }
-    CHECK(bias_grad(gact, C, L.fcpb));
     held[nheld++] = gi;
     // MLP in: u = a2 Wfc^T + b
-    dw[ndw++] = linear_dw(m, dF, F, F, act(m->ar.a2[l]), C, L.fcw, F, acc);
-    CHECK(bias_grad(dF, F, L.fcb));
+    CHECK(add_dw(linear_dw(m, dF, F, F, act(m->ar.a2[l]), C, L.fcw, F, acc), dF, F, L.fcb));
     held[nheld++] = NGB + di;
     d = linear_dx(m, dF, F, L.fcw, C, F, F);
     d.epilogue = GPT_EPI_STORE; d.out = dC; d.ldo = C;
@@ -579,8 +588,8 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
     cur ^= 1;
     // attention out: x_mid = x_in + y Wproj^T + b
     CHECK(fork());
-    dw[ndw++] = linear_dw(m, gact, C, C, act(m->ar.att[l]), C, L.projw, C, acc);
-    CHECK(bias_grad(gact, C, L.projb));
+    CHECK(add_dw(linear_dw(m, gact, C, C, act(m->ar.att[l]), C, L.projw, C, acc), gact, C,
+                 L.projb));
     held[nheld++] = gi;
     d = linear_dx(m, gact, C, L.projw, C, C, C);
     d.epilogue = GPT_EPI_STORE; d.out = dC2; d.ldo = C;
@@ -592,10 +601,10 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
                               dC2, dqkv, m->at<float>(m->ar.dvec), s));
     // qkv = a1 Wqkv^T + b
     CHECK(fork());
-    dw[ndw++] = linear_dw(m, dqkv, 3 * C, 3 * C, act(m->ar.a1[l]), C, L.qkvw, 3 * C, acc);
-    CHECK(bias_grad(dqkv, 3 * C, L.qkvb));
+    CHECK(add_dw(linear_dw(m, dqkv, 3 * C, 3 * C, act(m->ar.a1[l]), C, L.qkvw, 3 * C, acc), dqkv,
+                 3 * C, L.qkvb));
     held[nheld++] = 2 * NGB + di;
-    CHECK(gemm_group_on(s2, dw, ndw, GPT_S_BLOCK_DW));
+    CHECK(gemm_group_on(s2, dw, db, ndw, GPT_S_BLOCK_DW));
     for (int i = 0; i < nheld; ++i) CHECK(mark(held[i]));
     d = linear_dx(m, dqkv, 3 * C, L.qkvw, C, 3 * C, 3 * C);
     d.epilogue = GPT_EPI_STORE; d.out = dC; d.ldo = C;
@@ -1297,16 +1306,18 @@ int gpt_op_gemm(const gpt_gemm_desc* d, void* stream) {
   return GPT_OK;
 }
 
-int gpt_op_gemm_group(const gpt_gemm_desc* descs, int32_t n, void* stream) {
+int gpt_op_gemm_group(const gpt_gemm_desc* descs, float* const* bias_grads, int32_t n,
+                      void* stream) {
   if (n < 1 || n > 4) return fail(GPT_E_INVALID, "group of 1..4 products");
   if (!descs) return fail(GPT_E_INVALID, "NULL descriptors");
   for (int i = 0; i < n; ++i) {
     int rc = check_gemm_desc(&descs[i]);
     if (rc != GPT_OK) return rc;
   }
-  hipError_t e = gpt::gemm_group(descs, n, (hipStream_t)stream);
+  hipError_t e = gpt::gemm_group(descs, n, (hipStream_t)stream, bias_grads);
   if (e == hipErrorInvalidValue)
-    return fail(GPT_E_INVALID, "gemm layout rule broken (K, lda, ldb must be multiples of 8)");
+    return fail(GPT_E_INVALID, "gemm layout rule broken (K, lda, ldb multiples of 8; bias "
+                               "gradients need a bf16 K-major A)");
   if (e != hipSuccess) return fail(GPT_E_HIP, std::string("gemm group: ") + hipGetErrorString(e));
   return GPT_OK;
 }

@@ -1003,10 +1003,15 @@ __device__ __forceinline__ void dma_tile256_w8(__amdgpu_buffer_rsrc_t rs, const 
 // One 256 x 256 output tile (tx, ty) over the K range of split tz; `smem` is
 // the kernel's 128 KB LDS block (two stages of A and B tiles, later the
 // epilogue slices).
-template <int AT, int BT, int EPI>
+// CSUM (K-major A only): when `csum` is set, the tile's column sums of A over
+// its K range (sum_k A(m, k) for its 256 rows m: a Linear layer's bias
+// gradient when A = dY) are written to csum[m], in a fixed order (per thread
+// over the k-slices, then over 16 thread groups).
+template <int AT, int BT, int EPI, bool CSUM = false>
 __device__ __forceinline__ void big8_tile(const OpArgs& A, const OpArgs& B, int K, int kchunk,
                                           const EpiArgs& e, float* partial, int tx, int ty, int tz,
-                                          bf16_t* smem) {
+                                          bf16_t* smem, float* csum = nullptr) {
+  static_assert(!CSUM || AT == 1, "column sums of a K-major A tile");
   bf16_t* const sA0 = smem;
   bf16_t* const sB0 = smem + BIG * BK;
   bf16_t* const sA1 = smem + 2 * BIG * BK;
@@ -1027,6 +1032,8 @@ __device__ __forceinline__ void big8_tile(const OpArgs& A, const OpArgs& B, int 
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.X, a_extent * 2);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(b.X, b_extent * 2);
 
+  float cs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const bool do_cs = CSUM && csum != nullptr;
   f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -1084,6 +1091,21 @@ __device__ __forceinline__ void big8_tile(const OpArgs& A, const OpArgs& B, int 
       else __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (CSUM) {
+      if (do_cs) {  // thread: 8 rows (chunk c), k-rows kg + 16 j of this slice
+        const int c = threadIdx.x & 31, kg = threadIdx.x >> 5;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int k = kg + 16 * j;
+          const u32x4 v = *(const u32x4*)(as + k * BIG + ((c ^ ((k & 3) << 2)) << 3));
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            cs[2 * q] += bf_lo(v[q]);
+            cs[2 * q + 1] += bf_hi(v[q]);
+          }
+        }
+      }
+    }
   }
 
   // Epilogue, one 32-row block of the wave's 128 x 64 tile at a time:
@@ -1092,6 +1114,21 @@ __device__ __forceinline__ void big8_tile(const OpArgs& A, const OpArgs& B, int 
   // column m = lane % 32, register r holds n = 8 (r / 4) + 4 (lane / 32) + r % 4.
   constexpr int CP = 68;  // padded row pitch (floats)
   __syncthreads();        // every wave is done reading the operand tiles
+  if constexpr (CSUM) {
+    if (do_cs) {  // combine the 16 k-groups per row in LDS past the epilogue slices
+      float* red = (float*)smem + 24576;
+      const int c = threadIdx.x & 31, kg = threadIdx.x >> 5;
+      *(float4*)(red + kg * 256 + 8 * c) = make_float4(cs[0], cs[1], cs[2], cs[3]);
+      *(float4*)(red + kg * 256 + 8 * c + 4) = make_float4(cs[4], cs[5], cs[6], cs[7]);
+      __syncthreads();
+      if (threadIdx.x < 256) {
+        float t = 0.f;
+#pragma unroll
+        for (int g = 0; g < 16; ++g) t += red[g * 256 + threadIdx.x];
+        if (m0 + (int)threadIdx.x < e.M) csum[m0 + threadIdx.x] = t;
+      }
+    }
+  }
   float* Cw = (float*)smem + wave * (32 * CP);  // 8 slices of 8.5 KB (68 KB of the 128 KB)
   const int m_l = lane & 31, nq = 4 * (lane >> 5);
 #pragma unroll
@@ -1146,6 +1183,7 @@ struct GroupArgs {
   int M[GROUP_MAX], N[GROUP_MAX], nx[GROUP_MAX], ny[GROUP_MAX];
   int tile0[GROUP_MAX + 1];  // first flat tile of each product; tile0[n] = all tiles
   long part[GROUP_MAX];      // float offset of each product's S partial tiles
+  float* csum[GROUP_MAX];    // NULL, or [S][M] partial column sums of A (bias gradient)
   int n;
 };
 
@@ -1168,8 +1206,10 @@ __global__ void __launch_bounds__(512, 1) gemm_big8_group_kernel(GroupArgs g, in
   e.M = g.M[p];
   e.N = g.N[p];
   e.batch = 1;
-  big8_tile<AT, BT, EPI_PARTIAL>(g.A[p], g.B[p], K, kchunk, e, partial + g.part[p], w / rows,
-                                 grp * TILE_GROUP + w % rows, tz, smem);
+  const int tx = w / rows;
+  float* cs = (AT == 1 && tx == 0 && g.csum[p]) ? g.csum[p] + (long)tz * e.M : nullptr;
+  big8_tile<AT, BT, EPI_PARTIAL, AT == 1>(g.A[p], g.B[p], K, kchunk, e, partial + g.part[p], tx,
+                                          grp * TILE_GROUP + w % rows, tz, smem, cs);
 }
 
 MfmaKernel big8_kernel_for(int at, int bt, int epi, int ga, int gb) {
@@ -1450,6 +1490,32 @@ hipError_t gemm(const gpt_gemm_desc& d, hipStream_t s) {
 }
 
 namespace {
+// out[m] (+)= sum over z of part[z][m], z in order (the grouped launch's
+// partial column sums).
+__global__ void __launch_bounds__(256) csum_reduce_kernel(const float* __restrict__ part, int S,
+                                                          int M, float* __restrict__ out,
+                                                          int accumulate) {
+  const int m = blockIdx.x * 256 + threadIdx.x;
+  if (m >= M) return;
+  float t = part[m];
+  for (int z = 1; z < S; ++z) t += part[(long)z * M + m];
+  out[m] = accumulate ? out[m] + t : t;
+}
+
+// out[m] (+)= sum_k A(m, k) of a K-major bf16 operand, k in order (the
+// bias gradients of products the grouped kernel does not take).
+__global__ void __launch_bounds__(256) csum_kmajor_kernel(const bf16_t* __restrict__ A, long lda,
+                                                          int M, int K, float* __restrict__ out,
+                                                          int accumulate) {
+  const int m = blockIdx.x * 256 + threadIdx.x;
+  if (m >= M) return;
+  float t = 0.f;
+  for (int k = 0; k < K; ++k) t += bf2f(A[(long)k * lda + m]);
+  out[m] = accumulate ? out[m] + t : t;
+}
+}  // namespace
+
+namespace {
 // Split count of a grouped launch over T 256-tiles: at most one (split, tile)
 // workgroup per CU, each split at least 1024 deep.
 int group_splits(long T, int K) {
@@ -1484,12 +1550,17 @@ int64_t gemm_group_workspace_bytes(const int* M, const int* N, int n, int K) {
   if (n < 1 || n > GROUP_MAX) return 0;
   const int S = group_splits(group_tiles(M, N, n), K);
   int64_t mn = 0;
-  for (int i = 0; i < n; ++i) mn += (int64_t)M[i] * N[i];
+  for (int i = 0; i < n; ++i) mn += (int64_t)M[i] * N[i] + M[i];  // product + column-sum partials
   return (int64_t)S * mn * 4;
 }
 
-hipError_t gemm_group(const gpt_gemm_desc* d, int n, hipStream_t s) {
+hipError_t gemm_group(const gpt_gemm_desc* d, int n, hipStream_t s, float* const* db) {
   if (n <= 0) return hipSuccess;
+  if (db) {  // column sums need a bf16 K-major A
+    for (int i = 0; i < n; ++i)
+      if (db[i] && (d[i].precision != GPT_BF16 || !d[i].a_trans || d[i].a_gelu))
+        return hipErrorInvalidValue;
+  }
   int Ms[GROUP_MAX], Ns[GROUP_MAX];
   bool grouped = group_ok(d, n);
   if (grouped) {
@@ -1504,6 +1575,13 @@ hipError_t gemm_group(const gpt_gemm_desc* d, int n, hipStream_t s) {
     for (int i = 0; i < n; ++i) {
       hipError_t e = gemm(d[i], s);
       if (e != hipSuccess) return e;
+      if (db && db[i] && d[i].M > 0) {
+        csum_kmajor_kernel<<<(unsigned)cdiv(d[i].M, 256), 256, 0, s>>>(
+            (const bf16_t*)d[i].A, d[i].lda, d[i].M, d[i].K, db[i],
+            d[i].epilogue == GPT_EPI_F32_ACCUM);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
     }
     return hipSuccess;
   }
@@ -1530,6 +1608,10 @@ hipError_t gemm_group(const gpt_gemm_desc* d, int n, hipStream_t s) {
   }
   g.tile0[n] = (int)tile;
   float* ws = (float*)d[0].workspace;
+  for (int i = 0; i < n; ++i) {  // column-sum partials after the product partials
+    g.csum[i] = (db && db[i]) ? ws + part : nullptr;
+    part += (long)S * d[i].M;
+  }
   gemm_big8_group_kernel<1, 1><<<(unsigned)(T * S), 512, 0, s>>>(g, K, kchunk, ws);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -1544,6 +1626,12 @@ hipError_t gemm_group(const gpt_gemm_desc* d, int n, hipStream_t s) {
       splitk_reduce8_kernel<GPT_EPI_F32_ACCUM><<<blocks, 256, 0, s>>>(ws + g.part[i], S, e);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
+    if (g.csum[i]) {
+      csum_reduce_kernel<<<(unsigned)cdiv(x.M, 256), 256, 0, s>>>(
+          g.csum[i], S, x.M, db[i], x.epilogue == GPT_EPI_F32_ACCUM);
+      err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
   }
   return hipSuccess;
 }

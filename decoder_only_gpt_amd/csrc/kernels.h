@@ -16,7 +16,9 @@ int64_t gemm_workspace_bytes(int M, int N, int K, int precision);
 // n (<= 4) weight-gradient products with the same K in one launch (split-K
 // partials in d[0].workspace, reduced per product in split order); products
 // the grouped kernel cannot take, or a short workspace, run one by one.
-hipError_t gemm_group(const gpt_gemm_desc* d, int n, hipStream_t s);
+// db (may be NULL; entries may be NULL): db[i] (+)= the column sums of the
+// bf16 K-major A_i (sum over K), stored or added as the product's epilogue.
+hipError_t gemm_group(const gpt_gemm_desc* d, int n, hipStream_t s, float* const* db = nullptr);
 int64_t gemm_group_workspace_bytes(const int* M, const int* N, int n, int K);
 // Number of K splits gemm() will use for this descriptor (1 = single kernel).
 int gemm_split_count(const gpt_gemm_desc& d);

@@ -152,7 +152,7 @@ def lib():
         "gpt_destroy": ([vp], i32),
         "gpt_last_error": ([], ctypes.c_char_p),
         "gpt_op_gemm": ([ctypes.POINTER(GemmDesc), vp], i32),
-        "gpt_op_gemm_group": ([ctypes.POINTER(GemmDesc), i32, vp], i32),
+        "gpt_op_gemm_group": ([ctypes.POINTER(GemmDesc), vp, i32, vp], i32),
         "gpt_op_gemm_group_workspace": ([ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
                                          i32, i32], i64),
         "gpt_op_attention_fwd": ([i32, i32, i32, i32, i32, i32, vp, vp, vp, vp], i32),
@@ -431,10 +431,14 @@ def op_gemm(desc: GemmDesc):
     _check(lib().gpt_op_gemm(ctypes.byref(desc), _stream()))
 
 
-def op_gemm_group(descs):
-    """gpt_op_gemm_group over a list of GemmDesc (1..4)."""
+def op_gemm_group(descs, bias_grads=None):
+    """gpt_op_gemm_group over a list of GemmDesc (1..4); bias_grads: None or a
+    list of float32 device tensors (or None) receiving the column sums of A."""
     arr = (GemmDesc * len(descs))(*descs)
-    _check(lib().gpt_op_gemm_group(arr, len(descs), _stream()))
+    db = None
+    if bias_grads is not None:
+        db = (ctypes.c_void_p * len(descs))(*[None if t is None else t.data_ptr() for t in bias_grads])
+    _check(lib().gpt_op_gemm_group(arr, db, len(descs), _stream()))
 
 
 def op_gemm_group_workspace(Ms, Ns, K: int) -> int:

@@ -361,11 +361,16 @@ int gpt_op_gemm(const gpt_gemm_desc* d, void* stream);
  * the 256-tiles of all products are split over K together and each product's
  * partial sums are reduced in fixed split order, so results are reproducible
  * (not bitwise equal to gpt_op_gemm, whose split count differs).  Otherwise
- * the products run one by one through gpt_op_gemm.  descs is host memory,
- * read during the call only. */
-int gpt_op_gemm_group(const gpt_gemm_desc* descs, int32_t n, void* stream);
+ * the products run one by one through gpt_op_gemm.  bias_grads: NULL, or n
+ * device pointers (entries may be NULL): bias_grads[i][m] (+)= sum over k of
+ * A_i(m, k), the Linear bias gradient when A_i = dY, stored or added as
+ * product i's epilogue; taken from the operand tiles the grouped kernel has
+ * in LDS (requires a bf16 K-major A_i, else GPT_E_INVALID).  descs and
+ * bias_grads are host memory, read during the call only. */
+int gpt_op_gemm_group(const gpt_gemm_desc* descs, float* const* bias_grads, int32_t n,
+                      void* stream);
 /* Workspace bytes the grouped launch of products [M_i, N_i] with reduction
- * length K needs (0 if n is out of range). */
+ * length K needs, bias-gradient partials included (0 if n is out of range). */
 int64_t gpt_op_gemm_group_workspace(const int32_t* M, const int32_t* N, int32_t n, int32_t K);
 
 /* Causal (windowed) attention over a packed qkv [B*T, 3*H*hd] (q | k | v,

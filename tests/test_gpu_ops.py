@@ -268,56 +268,76 @@ GROUP_CASES = [
 
 def _group_descs(K, shapes, epi, seed, trans_a=1):
     """Descriptors dW_i (+)= A_i^T-layout products for gpt_op_gemm_group, with
-    the exact expected results."""
-    ds, keep, refs = [], [], []
+    the exact expected results; bias-gradient buffers (column sums of A_i,
+    on every second product) with theirs."""
+    ds, keep, refs, dbs, db_refs = [], [], [], [], []
+    acc = epi == gpt.EPI_F32_ACCUM
     for i, (M, N) in enumerate(shapes):
         A, lda, Ax = _operand(M, K, trans_a if i == 0 else 1, torch.bfloat16, seed + 2 * i)
         B, ldb, Bx = _operand(N, K, 1, torch.bfloat16, seed + 2 * i + 1)
         init = synth.normal((M, N), seed + 50 + i, 1.0).astype(np.float32)
         out = torch.from_numpy(init.copy()).cuda()
-        ref = Ax @ Bx.T + (init if epi == gpt.EPI_F32_ACCUM else 0.0)
+        ref = Ax @ Bx.T + (init if acc else 0.0)
         ds.append(gpt.GemmDesc(precision=gpt.BF16, M=M, N=N, K=K, A=A.data_ptr(), lda=lda,
                                a_trans=trans_a if i == 0 else 1, a_rows=M, a_kvalid=K,
                                B=B.data_ptr(), ldb=ldb, b_trans=1, b_rows=N, b_kvalid=K,
                                epilogue=epi, out=out.data_ptr(), ldo=N))
         keep += [A, B, out]
         refs.append((out, ref))
-    return ds, keep, refs
+        if i % 2 == 0:
+            b0 = synth.normal((M,), seed + 80 + i, 1.0).astype(np.float32)
+            db = torch.from_numpy(b0.copy()).cuda()
+            dbs.append(db)
+            db_refs.append((db, Ax.sum(axis=1) + (b0 if acc else 0.0)))
+        else:
+            dbs.append(None)
+    return ds, keep, refs, dbs, db_refs
+
+
+def _check_group(refs, db_refs, what):
+    for out, ref in refs:
+        err = np.abs(out.cpu().numpy() - ref).max() / np.abs(ref).max()
+        assert err < 2e-5, (what, err)
+    for db, ref in db_refs:  # fp32 sums of up to a few thousand bf16 values
+        err = np.abs(db.cpu().numpy() - ref).max() / max(np.abs(ref).max(), 1.0)
+        assert err < 2e-5, (what, "bias", err)
 
 
 @pytest.mark.parametrize("K,shapes,epi", GROUP_CASES)
 def test_gemm_group(K, shapes, epi):
     """A block's weight gradients in one grouped launch: every product matches
     its exact value (bf16 inputs, fp32 accumulation), for fresh and
-    accumulated outputs."""
-    ds, keep, refs = _group_descs(K, shapes, epi, seed=300)
+    accumulated outputs, and so do the bias gradients the launch sums from
+    its A tiles."""
+    ds, keep, refs, dbs, db_refs = _group_descs(K, shapes, epi, seed=300)
     need = gpt.op_gemm_group_workspace([m for m, _ in shapes], [n for _, n in shapes], K)
     assert need > 0
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     for d in ds:
         d.workspace, d.workspace_bytes = ws.data_ptr(), ws.numel()
-    gpt.op_gemm_group(ds)
+    gpt.op_gemm_group(ds, dbs)
     torch.cuda.synchronize()
-    for out, ref in refs:
-        err = np.abs(out.cpu().numpy() - ref).max() / np.abs(ref).max()
-        assert err < 2e-5, err
+    _check_group(refs, db_refs, "grouped")
 
 
 def test_gemm_group_fallbacks():
     """A member the grouped kernel cannot take (row-major A) and a workspace
     too small for the partials both run product by product, with the same
     results; the group size is checked."""
-    K, shapes = 1024, [(96, 128), (64, 256)]
+    K, shapes = 1024, [(96, 128), (64, 256), (72, 64)]
     for trans_a, ws_bytes in ((0, 1 << 24), (1, 16)):
-        ds, keep, refs = _group_descs(K, shapes, gpt.EPI_F32, seed=400, trans_a=trans_a)
+        ds, keep, refs, dbs, db_refs = _group_descs(K, shapes, gpt.EPI_F32, seed=400,
+                                                    trans_a=trans_a)
         ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
         for d in ds:
             d.workspace, d.workspace_bytes = ws.data_ptr(), ws_bytes
-        gpt.op_gemm_group(ds)
+        if trans_a == 0:  # a bias gradient needs a K-major A
+            with pytest.raises(gpt.GptError):
+                gpt.op_gemm_group(ds, dbs)
+            dbs[0], db_refs = None, db_refs[1:]
+        gpt.op_gemm_group(ds, dbs)
         torch.cuda.synchronize()
-        for out, ref in refs:
-            err = np.abs(out.cpu().numpy() - ref).max() / np.abs(ref).max()
-            assert err < 2e-5, (trans_a, ws_bytes, err)
+        _check_group(refs, db_refs, (trans_a, ws_bytes))
     with pytest.raises(gpt.GptError):
         gpt.op_gemm_group([])
 
