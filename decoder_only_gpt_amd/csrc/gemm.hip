@@ -1342,6 +1342,14 @@ GemmPlan plan_gemm(int M, int N, int K, int precision, bool splittable, int64_t 
         return p;
       }
     }
+    // Long reductions over many output tiles (the vocabulary weight gradient:
+    // K = tokens, 591 tiles): unsplit 256-tiles.  Alone this is 3% slower than
+    // 128-tiles (the last of three rounds is a third full), but it runs beside
+    // the input-gradient chain, which fills those CUs: +1.1% on the step.
+    if (splittable && K >= 2048 && t256 >= 256) {
+      p.big = true;
+      return p;
+    }
     // The vocabulary projection and its input gradient (N or K = vocabulary): 256-tiles.
     if (!splittable && (t256 >= 4096 || K >= 16384)) {
       p.big = true;

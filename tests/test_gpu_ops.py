@@ -100,6 +100,32 @@ def test_gemm_layouts(prec, M, N, K, at, bt):
     assert err < 2e-5, err
 
 
+@pytest.mark.parametrize("epi", [gpt.EPI_F32, gpt.EPI_F32_ACCUM])
+def test_gemm_long_reduction_many_tiles(epi):
+    """Weight-gradient layout with a long reduction over >= 256 output tiles of
+    256 (the vocabulary weight gradient's plan: unsplit 256-tiles), ragged in
+    M, N and K; sampled rows and columns against their exact values."""
+    M, N, K = 4224, 3880, 2056
+    A, lda, Ax = _operand(M, K, 1, torch.bfloat16, 31)
+    B, ldb, Bx = _operand(N, K, 1, torch.bfloat16, 32)
+    init = synth.normal((M, N), 33, 1.0).astype(np.float32)
+    out = torch.from_numpy(init.copy()).cuda()
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    d = gpt.GemmDesc(precision=gpt.BF16, M=M, N=N, K=K, A=A.data_ptr(), lda=lda, a_trans=1, a_rows=M,
+                     a_kvalid=K, B=B.data_ptr(), ldb=ldb, b_trans=1, b_rows=N, b_kvalid=K,
+                     epilogue=epi, out=out.data_ptr(), ldo=N, workspace=ws.data_ptr(),
+                     workspace_bytes=ws.numel())
+    gpt.op_gemm(d)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    rng = np.random.default_rng(34)
+    rows = np.concatenate([rng.choice(M, 48, replace=False), [0, 255, 256, M - 1]])
+    cols = np.concatenate([rng.choice(N, 48, replace=False), [0, 255, 256, N - 1]])
+    ref = Ax[rows] @ Bx[cols].T + (init[np.ix_(rows, cols)] if epi == gpt.EPI_F32_ACCUM else 0.0)
+    err = np.abs(got[np.ix_(rows, cols)] - ref).max() / np.abs(ref).max()
+    assert err < 2e-5, err
+
+
 @pytest.mark.parametrize("prec", [gpt.FP32, gpt.BF16])
 @pytest.mark.parametrize("epi", [gpt.EPI_STORE, gpt.EPI_RESIDUAL, gpt.EPI_GELU, gpt.EPI_DGELU,
                                  gpt.EPI_F32_ACCUM, gpt.EPI_GELU_PAIR, gpt.EPI_MUL])
