@@ -1172,6 +1172,145 @@ __global__ void __launch_bounds__(512, 1) gemm_big8_kernel(OpArgs A, OpArgs B, i
   big8_tile<AT, BT, EPI>(A, B, K, kchunk, e, partial, tx, ty, tz, smem);
 }
 
+// ----------------------------------------------------------------------------
+// bf16 MFMA, 256 x 192 tile, 8 waves of 64 x 96 (2 x 3 MFMA blocks): for
+// N = 768 products (the residual-width outputs: M = tokens), whose 256 x 256
+// grid is 192 tiles (three quarters of the CUs) and whose 128-tile grid is 1.5
+// rounds, this grid is 256 tiles: one full round.  Stages, loaders and LDS
+// layouts are the 256-tile kernel's (B rows past the tile are masked, so they
+// are not fetched); the epilogue stages each wave's two 32 x 96 slices.
+// ----------------------------------------------------------------------------
+constexpr int BW = 192;
+
+template <int AT, int BT, int EPI>
+__global__ void __launch_bounds__(512, 1) gemm_big8w_kernel(OpArgs A, OpArgs B, int K, int kchunk,
+                                                            EpiArgs e, float* partial) {
+  __shared__ __attribute__((aligned(16))) bf16_t smem[4 * BIG * BK];
+  bf16_t* const sA0 = smem;
+  bf16_t* const sB0 = smem + BIG * BK;
+  bf16_t* const sA1 = smem + 2 * BIG * BK;
+  bf16_t* const sB1 = smem + 3 * BIG * BK;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;  // rows wm * 64 .., columns wn * 96 ..
+  int tx, ty, tz;
+  xcd_tile(tx, ty, tz);
+  if (e.batch > 1) {  // tz indexes the matrix of a batch (never split over K)
+    batch_select(tz, A, B, e);
+    tz = 0;
+  }
+  const int m0 = ty * BIG, n0 = tx * BW;
+  const int kbeg = tz * kchunk;
+  if (EPI == EPI_PARTIAL) partial += (long)tz * e.M * e.N;
+  const int kend = min(K, kbeg + kchunk);
+  const int nk = (kend - kbeg + BK - 1) / BK;
+
+  OpArgs a = A, b = B;
+  a.kvalid = min(a.kvalid, kend);
+  b.kvalid = min(b.kvalid, kend);
+  const long a_extent = AT ? (long)a.kvalid * a.ld : (long)a.rows * a.ld;
+  const long b_extent = BT ? (long)b.kvalid * b.ld : (long)b.rows * b.ld;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.X, a_extent * 2);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(b.X, b_extent * 2);
+  b.rows = min(b.rows, n0 + BW);  // the 256-row loader skips rows past this tile
+
+  f32x16 acc[2][3];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 3; ++j) acc[i][j] = f32x16{};
+
+  dma_tile256_w8<AT, (AT || BT)>(ra, a, m0, kbeg, sA0, wave, lane);
+  dma_tile256_w8<BT, (AT || BT)>(rb, b, n0, kbeg, sB0, wave, lane);
+  for (int kt = 0; kt < nk; ++kt) {
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's loads of tile kt landed
+    __syncthreads();                     // ... and every other wave's
+    const bool odd = kt & 1;
+    if (kt + 1 < nk) {
+      const int k1 = kbeg + (kt + 1) * BK;
+      dma_tile256_w8<AT, (AT || BT)>(ra, a, m0, k1, odd ? sA0 : sA1, wave, lane);
+      dma_tile256_w8<BT, (AT || BT)>(rb, b, n0, k1, odd ? sB0 : sB1, wave, lane);
+    }
+    const bf16_t* as = odd ? sA1 : sA0;
+    const bf16_t* bs = odd ? sB1 : sB0;
+    // Fragments double-buffered across the 16-deep steps, as in the 256-tile kernel.
+    constexpr int NDS = (AT ? 4 : 2) + (BT ? 6 : 3);
+    bf16x8 af[2][2], bf[2][3];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) af[0][i] = big_frag<AT>(as, wm * 64 + i * 32, 0, lane);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) bf[0][j] = big_frag<BT>(bs, wn * 96 + j * 32, 0, lane);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < BK / 16) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          af[cur ^ 1][i] = big_frag<AT>(as, wm * 64 + i * 32, ks + 1, lane);
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+          bf[cur ^ 1][j] = big_frag<BT>(bs, wn * 96 + j * 32, ks + 1, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+          acc[i][j] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[cur][j], af[cur][i], acc[i][j], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      if (ks + 1 < BK / 16) sched_mfma_ds<6, NDS>();
+      else __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // Epilogue, one 32-row block of the wave's 64 x 96 tile at a time (see the
+  // 256-tile kernel): acc[i][j] = D[n][m], lane column m = lane % 32, register
+  // r holds n = 8 (r / 4) + 4 (lane / 32) + r % 4; 12 groups of 8 columns per row.
+  constexpr int CP = 100;  // padded row pitch (floats)
+  __syncthreads();         // every wave is done reading the operand tiles
+  float* Cw = (float*)smem + wave * (32 * CP);  // 8 slices of 12.5 KB (100 KB of the 128 KB)
+  const int m_l = lane & 31, nq = 4 * (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(float4*)(Cw + m_l * CP + j * 32 + 8 * q + nq) =
+            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                        acc[i][j][4 * q + 3]);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+#pragma unroll
+    for (int p = 0; p < 6; ++p) {  // 32 rows x 12 column groups = 6 passes of 64 lanes
+      const int item = p * 64 + lane, row = item / 12, cg = item - row * 12;
+      const int m = m0 + wm * 64 + i * 32 + row, n = n0 + wn * 96 + cg * 8;
+      if (m < e.M && n < e.N) {
+        const float4 v0 = *(const float4*)(Cw + row * CP + cg * 8);
+        const float4 v1 = *(const float4*)(Cw + row * CP + cg * 8 + 4);
+        epilogue8<EPI>(e, partial, m, n, v0, v1);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next block overwrites
+  }
+}
+
+MfmaKernel big8w_kernel_for(int at, int bt, int epi, int ga, int gb) {
+  if (ga || gb) return nullptr;
+#define K_(AT, BT, EP) \
+  if (at == AT && bt == BT && epi == EP) return gemm_big8w_kernel<AT, BT, EP>;
+  K_(0, 0, GPT_EPI_STORE)
+  K_(0, 0, GPT_EPI_RESIDUAL)
+  K_(0, 1, GPT_EPI_STORE)
+  K_(0, 1, GPT_EPI_MUL)
+  K_(0, 1, GPT_EPI_DGELU)
+#undef K_
+  return nullptr;
+}
+
 // Up to GROUP_MAX products with the same K (a transformer block's weight
 // gradients: K = tokens) in one launch over their concatenated 256-tiles, each
 // split S ways over K.  Workgroups walk the flat (split, tile) space in the
@@ -1273,8 +1412,9 @@ int choose_split(int M, int N, int K) {
 
 // Which kernel runs a descriptor and over how many K splits.
 struct GemmPlan {
-  bool big;  // 256 x 256 tiles
-  int S;     // K splits (1 = none)
+  bool big;   // 256 x 256 tiles
+  int S;      // K splits (1 = none)
+  bool wide;  // 256 x 192 tiles (unsplit)
 };
 
 // Tuning switch: GPT_GEMM_BIG4=1 runs the 4-wave large-tile kernel instead.
@@ -1293,8 +1433,8 @@ int tile_override() {
 }
 
 GemmPlan plan_gemm(int M, int N, int K, int precision, bool splittable, int64_t ws_bytes,
-                   bool big_ok, int batch = 1) {
-  GemmPlan p{false, 1};
+                   bool big_ok, int batch = 1, bool wide_ok = false) {
+  GemmPlan p{false, 1, false};
   if (precision != GPT_BF16 || M <= 0 || N <= 0 || K <= 0) return p;
   if (!big_ok) {
     int S = splittable ? choose_split(M, N, K) : 1;
@@ -1316,6 +1456,20 @@ GemmPlan plan_gemm(int M, int N, int K, int precision, bool splittable, int64_t 
   }
   const long t256 = cdiv(M, BIG) * cdiv(N, BIG) * batch;
   const int force = tile_override();
+  // 256 x 192 tiles where that grid fills whole rounds of the 256 CUs and the
+  // square grids do not (N = 768: 256 tiles against 192 of 256 x 256 and 1.5
+  // rounds of 128 x 128; QKV forward: 3 rounds).  Not for products that may be
+  // split over K (the vocabulary input gradient is 4% faster split 4 ways on
+  // 256-tiles than unsplit here).
+  if (wide_ok && !splittable && batch == 1 && force == 0) {
+    auto fill = [](long t, long slots) { return (double)t / (double)(cdiv(t, slots) * slots); };
+    const long t192 = cdiv(M, BIG) * cdiv(N, BW), t128 = cdiv(M, BM) * cdiv(N, BN);
+    const double f192 = fill(t192, 256);
+    if (t192 >= 256 && f192 >= 0.95 && f192 > std::max(fill(t256, 256), fill(t128, 512)) + 0.05) {
+      p.wide = true;
+      return p;
+    }
+  }
   if (force == 256) {
     p.big = true;
     return p;
@@ -1399,12 +1553,18 @@ bool dma_ok(const gpt_gemm_desc& d) {
 // The large-tile kernel loads straight to LDS, so it cannot apply GELU to an
 // operand on the way in.
 bool big_ok(const gpt_gemm_desc& d) { return !d.a_gelu && !d.b_gelu && dma_ok(d); }
+// The 256 x 192 kernel has the layout / epilogue combination and vector stores apply.
+bool wide_ok(const gpt_gemm_desc& d) {
+  const bool vec = d.N % 8 == 0 && d.ldo % 8 == 0 && (d.aux == nullptr || d.ldaux % 8 == 0);
+  return vec && d.batch <= 1 && big_ok(d) &&
+         big8w_kernel_for(d.a_trans, d.b_trans, d.epilogue, d.a_gelu, d.b_gelu) != nullptr;
+}
 
 }  // namespace
 
 int gemm_split_count(const gpt_gemm_desc& d) {
   GemmPlan p = plan_gemm(d.M, d.N, d.K, d.precision, splittable(d),
-                         d.workspace ? d.workspace_bytes : 0, big_ok(d));
+                         d.workspace ? d.workspace_bytes : 0, big_ok(d), 1, wide_ok(d));
   return effective_splits(p, d.K);
 }
 
@@ -1442,7 +1602,14 @@ hipError_t gemm(const gpt_gemm_desc& d, hipStream_t s) {
     return hipGetLastError();
   }
   const GemmPlan plan = plan_gemm(d.M, d.N, d.K, d.precision, batch == 1 && splittable(d),
-                                  d.workspace ? d.workspace_bytes : 0, big_ok(d), batch);
+                                  d.workspace ? d.workspace_bytes : 0, big_ok(d), batch,
+                                  wide_ok(d));
+  if (plan.wide) {  // wide_ok: the kernel exists for this combination
+    dim3 grid((unsigned)cdiv(d.N, BW), (unsigned)cdiv(d.M, BIG), 1);
+    big8w_kernel_for(d.a_trans, d.b_trans, d.epilogue, 0, 0)<<<grid, 512, 0, s>>>(A, B, d.K, d.K,
+                                                                                  e, nullptr);
+    return hipGetLastError();
+  }
   const int S = effective_splits(plan, d.K);
   const bool vec_ok = d.N % 8 == 0 && d.ldo % 8 == 0 && (d.aux == nullptr || d.ldaux % 8 == 0);
   const int epi = S > 1 ? EPI_PARTIAL : d.epilogue;

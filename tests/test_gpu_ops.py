@@ -100,6 +100,55 @@ def test_gemm_layouts(prec, M, N, K, at, bt):
     assert err < 2e-5, err
 
 
+WIDE_CASES = [
+    # M, N, K, b_trans, epilogue: products whose 256 x 192 grid fills whole CU rounds
+    (16344, 768, 520, 0, gpt.EPI_RESIDUAL),   # FC-projection / attention-projection forward
+    (16344, 768, 1040, 1, gpt.EPI_STORE),     # FC / QKV input gradients
+    (16344, 768, 264, 1, gpt.EPI_MUL),
+    (16344, 768, 264, 1, gpt.EPI_DGELU),
+    (16384, 2304, 136, 0, gpt.EPI_STORE),     # QKV forward (with bias)
+]
+
+
+@pytest.mark.parametrize("M,N,K,bt,epi", WIDE_CASES)
+def test_gemm_wide_tiles(M, N, K, bt, epi):
+    """The 256 x 192 tile plan (taken only at token-count M): ragged M and K;
+    sampled rows, all columns, against exact values."""
+    A, lda, Ax = _operand(M, K, 0, torch.bfloat16, 41)
+    B, ldb, Bx = _operand(N, K, bt, torch.bfloat16, 42)
+    bias = torch.from_numpy(synth.normal(N, 43, 0.5)).cuda()
+    resid = torch.from_numpy(synth.normal((M, N), 44, 1.0)).cuda()
+    aux = to_dev(synth.normal((M, N), 45, 1.5), torch.bfloat16)
+    f32 = epi == gpt.EPI_RESIDUAL
+    out = torch.zeros((M, N), dtype=torch.float32 if f32 else torch.bfloat16, device="cuda")
+    d = gpt.GemmDesc(precision=gpt.BF16, M=M, N=N, K=K, A=A.data_ptr(), lda=lda, a_trans=0, a_rows=M,
+                     a_kvalid=K, B=B.data_ptr(), ldb=ldb, b_trans=bt, b_rows=N, b_kvalid=K,
+                     epilogue=epi, gelu_tanh=1, out=out.data_ptr(), ldo=N)
+    if epi in (gpt.EPI_STORE, gpt.EPI_RESIDUAL):
+        d.bias = bias.data_ptr()
+    if epi == gpt.EPI_RESIDUAL:
+        d.resid = resid.data_ptr()
+    if epi in (gpt.EPI_MUL, gpt.EPI_DGELU):
+        d.aux, d.ldaux = aux.data_ptr(), N
+    gpt.op_gemm(d)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(46)
+    rows = np.concatenate([rng.choice(M, 40, replace=False), [0, 255, 256, M - 1]])
+    got = rounded(out)[rows]
+    acc = Ax[rows] @ Bx.T
+    bx = bias.cpu().numpy().astype(np.float64)
+    if epi == gpt.EPI_RESIDUAL:
+        ref = resid.cpu().numpy()[rows].astype(np.float64) + acc + bx
+    elif epi == gpt.EPI_STORE:
+        ref = acc + bx
+    elif epi == gpt.EPI_MUL:
+        ref = acc * rounded(aux)[rows]
+    else:
+        ref = acc * oracle.gelu_grad(rounded(aux)[rows], 1)
+    err = np.abs(got - ref).max() / np.abs(ref).max()
+    assert err < (2e-5 if f32 else 1e-2), err
+
+
 @pytest.mark.parametrize("epi", [gpt.EPI_F32, gpt.EPI_F32_ACCUM])
 def test_gemm_long_reduction_many_tiles(epi):
     """Weight-gradient layout with a long reduction over >= 256 output tiles of
