@@ -1665,18 +1665,6 @@ hipError_t gemm(const gpt_gemm_desc& d, hipStream_t s) {
 }
 
 namespace {
-// out[m] (+)= sum over z of part[z][m], z in order (the grouped launch's
-// partial column sums).
-__global__ void __launch_bounds__(256) csum_reduce_kernel(const float* __restrict__ part, int S,
-                                                          int M, float* __restrict__ out,
-                                                          int accumulate) {
-  const int m = blockIdx.x * 256 + threadIdx.x;
-  if (m >= M) return;
-  float t = part[m];
-  for (int z = 1; z < S; ++z) t += part[(long)z * M + m];
-  out[m] = accumulate ? out[m] + t : t;
-}
-
 // out[m] (+)= sum_k A(m, k) of a K-major bf16 operand, k in order (the
 // bias gradients of products the grouped kernel does not take).
 __global__ void __launch_bounds__(256) csum_kmajor_kernel(const bf16_t* __restrict__ A, long lda,
@@ -1687,6 +1675,57 @@ __global__ void __launch_bounds__(256) csum_kmajor_kernel(const bf16_t* __restri
   float t = 0.f;
   for (int k = 0; k < K; ++k) t += bf2f(A[(long)k * lda + m]);
   out[m] = accumulate ? out[m] + t : t;
+}
+
+// Every reduction of a grouped launch in one kernel: work item i < vec_end
+// sums 8 consecutive outputs of product p over the S splits (split order) and
+// stores or adds them; items past vec_end do the same for one bias-gradient
+// element.  Same sums, in the same order, as one reduction per product.
+struct GroupReduceArgs {
+  const float* part[GROUP_MAX];
+  float* out[GROUP_MAX];
+  long ldo[GROUP_MAX];
+  int M[GROUP_MAX], N[GROUP_MAX];
+  long vec0[GROUP_MAX + 1];  // first vector item of each product; vec0[n]: all
+  const float* cpart[GROUP_MAX];  // the nc bias gradients: partials [S][M] and outputs
+  float* db[GROUP_MAX];
+  int cM[GROUP_MAX];
+  long c0[GROUP_MAX + 1];  // first item of each bias gradient (c0[0] = vec0[n]); c0[nc]: all
+  int n, nc, S, accumulate;
+};
+
+__global__ void __launch_bounds__(256) group_reduce_kernel(GroupReduceArgs r) {
+  const long total = r.c0[r.nc];
+  for (long i = blockIdx.x * 256L + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
+    if (i < r.vec0[r.n]) {
+      int p = 0;
+      while (p + 1 < r.n && i >= r.vec0[p + 1]) ++p;
+      const long j = i - r.vec0[p], per_row = r.N[p] / 8, plane = (long)r.M[p] * r.N[p];
+      const int m = (int)(j / per_row), n = (int)(j % per_row) * 8;
+      const float* q = r.part[p] + (long)m * r.N[p] + n;
+      float4 a = *(const float4*)q, b = *(const float4*)(q + 4);
+      for (int z = 1; z < r.S; ++z) {
+        const float4 c = *(const float4*)(q + z * plane), d = *(const float4*)(q + z * plane + 4);
+        a.x += c.x; a.y += c.y; a.z += c.z; a.w += c.w;
+        b.x += d.x; b.y += d.y; b.z += d.z; b.w += d.w;
+      }
+      float4* o = (float4*)(r.out[p] + (long)m * r.ldo[p] + n);
+      if (r.accumulate) {
+        const float4 u = o[0], v = o[1];
+        a = make_float4(u.x + a.x, u.y + a.y, u.z + a.z, u.w + a.w);
+        b = make_float4(v.x + b.x, v.y + b.y, v.z + b.z, v.w + b.w);
+      }
+      o[0] = a;
+      o[1] = b;
+    } else {
+      int p = 0;
+      while (p + 1 < r.nc && i >= r.c0[p + 1]) ++p;
+      const int m = (int)(i - r.c0[p]);
+      float t = r.cpart[p][m];
+      for (int z = 1; z < r.S; ++z) t += r.cpart[p][(long)z * r.cM[p] + m];
+      r.db[p][m] = r.accumulate ? r.db[p][m] + t : t;
+    }
+  }
 }
 }  // namespace
 
@@ -1790,24 +1829,37 @@ hipError_t gemm_group(const gpt_gemm_desc* d, int n, hipStream_t s, float* const
   gemm_big8_group_kernel<1, 1><<<(unsigned)(T * S), 512, 0, s>>>(g, K, kchunk, ws);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  for (int i = 0; i < n; ++i) {  // each product's partials summed in split order
-    const gpt_gemm_desc& x = d[i];
-    EpiArgs e{x.epilogue, x.gelu_tanh, x.M, x.N, nullptr, nullptr, x.out, x.ldo, nullptr, 0,
-              1.f,        0.f,         1,   0,   0,       0,       0};
-    const unsigned blocks = (unsigned)std::min<long>(cdiv((long)x.M * x.N / 8, 256), 4096);
-    if (x.epilogue == GPT_EPI_F32)
-      splitk_reduce8_kernel<GPT_EPI_F32><<<blocks, 256, 0, s>>>(ws + g.part[i], S, e);
-    else
-      splitk_reduce8_kernel<GPT_EPI_F32_ACCUM><<<blocks, 256, 0, s>>>(ws + g.part[i], S, e);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    if (g.csum[i]) {
-      csum_reduce_kernel<<<(unsigned)cdiv(x.M, 256), 256, 0, s>>>(
-          g.csum[i], S, x.M, db[i], x.epilogue == GPT_EPI_F32_ACCUM);
-      err = hipGetLastError();
-      if (err != hipSuccess) return err;
-    }
+  // Each product's partials (and bias partials) summed in split order, one launch.
+  GroupReduceArgs r{};
+  r.n = n;
+  r.S = S;
+  r.accumulate = d[0].epilogue == GPT_EPI_F32_ACCUM;
+  long items = 0;
+  for (int i = 0; i < n; ++i) {
+    r.part[i] = ws + g.part[i];
+    r.out[i] = (float*)d[i].out;
+    r.ldo[i] = d[i].ldo;
+    r.M[i] = d[i].M;
+    r.N[i] = d[i].N;
+    r.vec0[i] = items;
+    items += (long)d[i].M * d[i].N / 8;
   }
+  r.vec0[n] = items;
+  r.nc = 0;
+  for (int i = 0; i < n; ++i) {  // the products with a bias gradient, in product order
+    if (!g.csum[i]) continue;
+    r.cpart[r.nc] = g.csum[i];
+    r.db[r.nc] = db[i];
+    r.cM[r.nc] = d[i].M;
+    r.c0[r.nc] = items;
+    items += d[i].M;
+    ++r.nc;
+  }
+  r.c0[r.nc] = items;
+  const unsigned blocks = (unsigned)std::min<long>(cdiv(items, 256), 8192);
+  group_reduce_kernel<<<blocks, 256, 0, s>>>(r);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
   return hipSuccess;
 }
 
