@@ -1545,7 +1545,8 @@ bool splittable(const gpt_gemm_desc& d) {
 }
 // Direct-to-LDS loads address each operand through a 31-bit byte offset.
 bool dma_ok(const gpt_gemm_desc& d) {
-  if (getenv("GPT_GEMM_NODMA")) return false;
+  static const bool nodma = getenv("GPT_GEMM_NODMA") != nullptr;  // tuning switch
+  if (nodma) return false;
   const long ea = d.a_trans ? (long)d.a_kvalid * d.lda : (long)d.a_rows * d.lda;
   const long eb = d.b_trans ? (long)d.b_kvalid * d.ldb : (long)d.b_rows * d.ldb;
   return ea * 2 < 0x7fffffffL && eb * 2 < 0x7fffffffL;
