@@ -4,16 +4,16 @@
 //
 //   gen_embed      x[b] = wte[token[b]] + wpe[pos]
 //   attn_decode    one query per (sequence, head) against the cached keys and
-//                  values 0..pos-1 plus its own (written to the cache here);
-//                  each thread takes every 256th key with a running softmax,
-//                  the block combines in a fixed order
+//                  values 0..pos-1 plus its own (written to the cache here),
+//                  running softmax per lane, merged in a fixed order (fp32:
+//                  one key per thread; bf16: HD / 8 lanes per key, 16 waves)
 //   sample         temperature / top-k / inverse-CDF draw per sequence (one
 //                  1024-thread block per row): the top-k threshold by a 4-pass
 //                  radix select on order-preserving keys, the cumulative sum by
 //                  a fixed-order scan of per-thread chunks, so the same logits
 //                  and u always give the same token
-// The matrix products and LayerNorms of the step are the training kernels
-// run on B rows.
+//   rows_linear    the bf16 matrix products of the step on MFMA 16x16x32, all
+//                  of K in one workgroup (fp32 runs the training GEMM on B rows)
 
 #include "common.h"
 #include "kernels.h"
@@ -106,6 +106,268 @@ __global__ void __launch_bounds__(AD_THREADS) attn_decode_kernel(
       Act<ActT>::store(out, (long)b * C + h * HD + d0 + tid, acc / L);
     }
     __syncthreads();
+  }
+}
+
+// bf16 decode attention, one 1024-thread workgroup per (sequence, head).
+// HD / 8 lanes share a key, each holding 8 of its dimensions (one 16-byte
+// load of the key row and one of the value row), so a wave reads 64 / (HD / 8)
+// whole rows per load; wave w takes key blocks w, w + 16, ... and issues the
+// loads of AW_DEPTH blocks before using them.  A lane keeps a running softmax
+// over its keys; the lanes of a wave merge by a fixed xor butterfly (every
+// lane ends with the same total), the 16 waves in wave order through LDS.
+constexpr int AW_WAVES = 16, AW_DEPTH = 4;
+
+template <int HD>
+__global__ void __launch_bounds__(AW_WAVES * 64) attn_decode_wide_kernel(
+    const bf16_t* __restrict__ qkv, bf16_t* __restrict__ kc, bf16_t* __restrict__ vc, int pos,
+    int Tmax, int H, int left, float scale, bf16_t* __restrict__ out) {
+  constexpr int LPK = HD / 8, KPB = 64 / LPK;
+  __shared__ float wmax[AW_WAVES], wsum[AW_WAVES];
+  __shared__ float wo[AW_WAVES][HD];
+  const int bh = blockIdx.x, b = bh / H, h = bh - b * H;
+  const int C = H * HD, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kk = lane / LPK, dp = lane % LPK;
+  const bf16_t* row = qkv + (long)b * 3 * C;
+  bf16_t* kb = kc + (long)bh * Tmax * HD;
+  bf16_t* vb = vc + (long)bh * Tmax * HD;
+  if (tid < LPK) {  // this position's key and value join the cache
+    *(u32x4*)(kb + (long)pos * HD + tid * 8) = *(const u32x4*)(row + C + h * HD + tid * 8);
+    *(u32x4*)(vb + (long)pos * HD + tid * 8) = *(const u32x4*)(row + 2 * C + h * HD + tid * 8);
+  }
+  const u32x4 qv = *(const u32x4*)(row + h * HD + dp * 8);
+  const float q[8] = {bf_lo(qv.x) * scale, bf_hi(qv.x) * scale, bf_lo(qv.y) * scale,
+                      bf_hi(qv.y) * scale, bf_lo(qv.z) * scale, bf_hi(qv.z) * scale,
+                      bf_lo(qv.w) * scale, bf_hi(qv.w) * scale};
+  const int j0 = left < 0 ? 0 : max(0, pos - left);
+  float m = -FLT_MAX, l = 0.f, o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = 0.f;
+  constexpr int STRIDE = AW_WAVES * KPB;
+  for (int jr = j0 + wave * KPB; jr <= pos; jr += AW_DEPTH * STRIDE) {
+    u32x4 kv[AW_DEPTH], vv[AW_DEPTH];
+#pragma unroll
+    for (int i = 0; i < AW_DEPTH; ++i) {
+      const int j = jr + i * STRIDE + kk;
+      kv[i] = u32x4{0, 0, 0, 0};
+      vv[i] = kv[i];
+      if (j <= pos) {
+        // the current position reads its own key / value from qkv (the cache
+        // row is written above by other lanes; reading qkv avoids relying on it)
+        const bf16_t* kr = j == pos ? row + C + h * HD : kb + (long)j * HD;
+        const bf16_t* vr = j == pos ? row + 2 * C + h * HD : vb + (long)j * HD;
+        kv[i] = *(const u32x4*)(kr + dp * 8);
+        vv[i] = *(const u32x4*)(vr + dp * 8);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < AW_DEPTH; ++i) {
+      const int j = jr + i * STRIDE + kk;
+      const u32x4 k = kv[i];
+      float s = q[0] * bf_lo(k.x);
+      s = fmaf(q[1], bf_hi(k.x), s);
+      s = fmaf(q[2], bf_lo(k.y), s);
+      s = fmaf(q[3], bf_hi(k.y), s);
+      s = fmaf(q[4], bf_lo(k.z), s);
+      s = fmaf(q[5], bf_hi(k.z), s);
+      s = fmaf(q[6], bf_lo(k.w), s);
+      s = fmaf(q[7], bf_hi(k.w), s);
+#pragma unroll
+      for (int off = LPK / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+      if (j <= pos) {
+        const u32x4 v = vv[i];
+        const float vf[8] = {bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y),
+                             bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w)};
+        const float mn = fmaxf(m, s);
+        const float corr = __expf(m - mn), p = __expf(s - mn);
+        l = l * corr + p;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) o[d] = o[d] * corr + p * vf[d];
+        m = mn;
+      }
+    }
+  }
+  // merge the key slots of the wave (lanes that differ in kk)
+  float M = m;
+#pragma unroll
+  for (int off = LPK; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+  const float f = l > 0.f ? __expf(m - M) : 0.f;
+  float L = l * f;
+#pragma unroll
+  for (int d = 0; d < 8; ++d) o[d] *= f;
+#pragma unroll
+  for (int off = LPK; off < 64; off <<= 1) {
+    L += __shfl_xor(L, off);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) o[d] += __shfl_xor(o[d], off);
+  }
+  if (kk == 0) {
+#pragma unroll
+    for (int d = 0; d < 8; ++d) wo[wave][dp * 8 + d] = o[d];
+    if (dp == 0) {
+      wmax[wave] = M;
+      wsum[wave] = L;
+    }
+  }
+  __syncthreads();
+  if (tid < HD) {
+    float Mx = -FLT_MAX;
+#pragma unroll
+    for (int w = 0; w < AW_WAVES; ++w) Mx = fmaxf(Mx, wmax[w]);
+    float Ls = 0.f, acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < AW_WAVES; ++w) {
+      const float g = wsum[w] > 0.f ? __expf(wmax[w] - Mx) : 0.f;
+      Ls += wsum[w] * g;
+      acc += wo[w][tid] * g;
+    }
+    out[(long)b * C + h * HD + tid] = f2bf(acc / Ls);
+  }
+}
+
+// Few-row product of the decode step (bf16): out[b, n] = epilogue(sum_k
+// a[b, k] W[n, k]) for the B rows (one per sequence) against a [N, K] weight,
+// on MFMA 16x16x32: the first operand is 16 weight rows (output columns), the
+// second 16 activation rows, so weight and activation loads go 1:1.
+//
+// Grid (column tiles of 16, row groups of 16); 4 waves per workgroup take
+// interleaved 64-wide k blocks (lane quarter q holds k = 16q..16q+15 of a
+// block, the same k for both operands, fed as two 8-deep halves), RL_DEPTH
+// blocks of loads at a time with the next weights in flight behind the
+// MFMAs, then sum in wave order through LDS and apply the epilogue.  All of K
+// stays in one workgroup: a product is one launch with no partials to reduce.
+// (Splitting k over workgroups with a last-arriver reduction measured several
+// times slower: each writer's device-scope release writes back its XCD's L2.)
+//
+// With LNV > 0 the activation rows are LayerNorm(x) of the fp32 residual
+// stream, computed by each workgroup into LDS first (one wave per row, all
+// rows' loads issued together, the same arithmetic as the LayerNorm kernel, so
+// the operand is bit-identical to the unfused one).
+constexpr int RL_DEPTH = 4;
+
+template <int WAVES>
+__device__ __forceinline__ void rl_load(u32x4 (&v)[RL_DEPTH][2], const bf16_t* p, int kb0,
+                                        int kend) {
+#pragma unroll
+  for (int i = 0; i < RL_DEPTH; ++i) {
+    const int kb = kb0 + i * WAVES;  // wave-uniform
+    if (kb < kend) {
+      v[i][0] = *(const u32x4*)(p + kb * 64);
+      v[i][1] = *(const u32x4*)(p + kb * 64 + 8);
+    }
+  }
+}
+
+template <int EPI, int WAVES, int LNV>
+__global__ void __launch_bounds__(WAVES * 64) rows_linear_kernel(
+    const bf16_t* __restrict__ a, const float* __restrict__ x, const float* __restrict__ lnw,
+    const float* __restrict__ lnb, float eps, int B, int K, const bf16_t* __restrict__ W, int N,
+    const float* __restrict__ bias, void* out, long ldo, const float* resid, bf16_t* aux,
+    int tanh_form) {
+  static_assert(WAVES >= 4 && (LNV == 0 || WAVES == 4), "256-thread epilogue, 4-row prologue");
+  constexpr int STEP = RL_DEPTH * WAVES;
+  __shared__ float part[WAVES * 64 * 4];
+  extern __shared__ __align__(16) bf16_t xs[];  // LNV > 0: 16 rows, stride K + 8
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * 16, b0 = blockIdx.y * 16;
+  const int li = lane & 15, kq = lane >> 4;
+  const int KB = K / 64, LDX = K + 8;  // K % 64 == 0
+  // Rows past N (or B) read a valid row instead: MFMA output (n, b) depends
+  // on weight row n and activation row b alone, and such outputs are dropped.
+  const bf16_t* wrow = W + (long)min(n0 + li, N - 1) * K + kq * 16;
+  u32x4 wv[RL_DEPTH][2], xv[RL_DEPTH][2];
+  rl_load<WAVES>(wv, wrow, wave, KB);
+  const bf16_t* xrow;
+  if constexpr (LNV > 0) {
+    constexpr int RPW = 16 / WAVES;
+    const int C4 = K / 4;
+    float4 v[RPW][LNV], g[LNV], be[LNV];
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+      const float4* xr = (const float4*)(x + (long)min(b0 + wave + rr * WAVES, B - 1) * K);
+#pragma unroll
+      for (int i = 0; i < LNV; ++i) {
+        const int c = lane + 64 * i;
+        v[rr][i] = c < C4 ? xr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < LNV; ++i) {
+      const int c = lane + 64 * i;
+      g[i] = c < C4 ? ((const float4*)lnw)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+      be[i] = lnb && c < C4 ? ((const float4*)lnb)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < LNV; ++i) s += (v[rr][i].x + v[rr][i].y) + (v[rr][i].z + v[rr][i].w);
+      const float mu = warp_sum(s) / (float)K;
+      float q = 0.f;
+#pragma unroll
+      for (int i = 0; i < LNV; ++i) {
+        if (lane + 64 * i < C4) {
+          const float e0 = v[rr][i].x - mu, e1 = v[rr][i].y - mu, e2 = v[rr][i].z - mu,
+                      e3 = v[rr][i].w - mu;
+          q += (e0 * e0 + e1 * e1) + (e2 * e2 + e3 * e3);
+        }
+      }
+      const float rs = 1.f / sqrtf(warp_sum(q) / (float)K + eps);
+      const int r = wave + rr * WAVES;
+#pragma unroll
+      for (int i = 0; i < LNV; ++i) {
+        const int c = lane + 64 * i;
+        if (c < C4)
+          *(uint2*)(xs + r * LDX + 4 * c) =
+              make_uint2(pack_bf2((v[rr][i].x - mu) * rs * g[i].x + be[i].x,
+                                  (v[rr][i].y - mu) * rs * g[i].y + be[i].y),
+                         pack_bf2((v[rr][i].z - mu) * rs * g[i].z + be[i].z,
+                                  (v[rr][i].w - mu) * rs * g[i].w + be[i].w));
+      }
+    }
+    __syncthreads();
+    xrow = xs + li * LDX + kq * 16;
+  } else {
+    xrow = a + (long)min(b0 + li, B - 1) * K + kq * 16;
+  }
+  rl_load<WAVES>(xv, xrow, wave, KB);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int kb0 = wave; kb0 < KB; kb0 += STEP) {
+#pragma unroll
+    for (int i = 0; i < RL_DEPTH; ++i) {
+      if (kb0 + i * WAVES < KB) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wv[i][0]),
+                                                      __builtin_bit_cast(bf16x8, xv[i][0]), acc,
+                                                      0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wv[i][1]),
+                                                      __builtin_bit_cast(bf16x8, xv[i][1]), acc,
+                                                      0, 0, 0);
+      }
+    }
+    rl_load<WAVES>(wv, wrow, kb0 + STEP, KB);  // both operands of the next batch
+    rl_load<WAVES>(xv, xrow, kb0 + STEP, KB);
+  }
+  // acc item r of lane l: output column n0 + 4 (l / 16) + r, row b0 + l % 16.
+  *(f32x4*)(part + (wave * 64 + lane) * 4) = acc;
+  __syncthreads();
+  const int t = threadIdx.x, l = t >> 2, r = t & 3;  // one (column, row) per thread
+  if (t >= 256) return;
+  float v = 0.f;
+#pragma unroll
+  for (int w = 0; w < WAVES; ++w) v += part[(w * 64 + l) * 4 + r];
+  const int n = n0 + 4 * (l >> 4) + r, b = b0 + (l & 15);
+  if (n < N && b < B) {
+    if (bias) v += bias[n];
+    const long o = (long)b * ldo + n;
+    if constexpr (EPI == GPT_EPI_RESIDUAL) {
+      ((float*)out)[o] = resid[o] + v;
+    } else {
+      const bf16_t u = f2bf(v);
+      ((bf16_t*)out)[o] = u;
+      if constexpr (EPI == GPT_EPI_GELU) {  // GELU of the stored (rounded) pre-activation
+        if (aux) aux[o] = f2bf(gelu_fast(bf2f(u), tanh_form));
+      }
+    }
   }
 }
 
@@ -280,6 +542,43 @@ hipError_t gen_embed(const int32_t* tok, const float* wte, const float* wpe, int
   return hipGetLastError();
 }
 
+template <int EPI, int WAVES, int LNV>
+hipError_t rows_linear_go(const RowsLinear& p, hipStream_t s) {
+  const dim3 grid((unsigned)((p.N + 15) / 16), (unsigned)((p.B + 15) / 16));
+  const size_t lds = LNV > 0 ? (size_t)16 * (p.K + 8) * sizeof(bf16_t) : 0;
+  rows_linear_kernel<EPI, WAVES, LNV><<<grid, WAVES * 64, lds, s>>>(
+      (const bf16_t*)p.a, p.x, p.ln_w, p.ln_b, p.eps, p.B, p.K, (const bf16_t*)p.W, p.N, p.bias,
+      p.out, p.ldo, p.resid, (bf16_t*)p.aux, p.tanh_form);
+  return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t rows_linear_epi(const RowsLinear& p, hipStream_t s) {
+  if constexpr (EPI != GPT_EPI_RESIDUAL) {
+    if (p.x) {  // LayerNorm prologue: one float4 per lane per 256 columns
+      const int nv = (p.K / 4 + 63) / 64;
+      if (nv <= 1) return rows_linear_go<EPI, 4, 1>(p, s);
+      if (nv <= 2) return rows_linear_go<EPI, 4, 2>(p, s);
+      if (nv <= 3) return rows_linear_go<EPI, 4, 3>(p, s);
+      return rows_linear_go<EPI, 4, 4>(p, s);  // K <= 1024
+    }
+  }
+  // 16 waves when 4 would need more than one batch of loads per wave
+  if (p.K / 64 > 4 * RL_DEPTH) return rows_linear_go<EPI, 16, 0>(p, s);
+  return rows_linear_go<EPI, 4, 0>(p, s);
+}
+
+hipError_t rows_linear(const RowsLinear& p, hipStream_t s) {
+  if (p.B <= 0 || p.N <= 0) return hipSuccess;
+  if (p.K % 64 || (!p.a && !p.x) || (p.x && (!p.ln_w || p.K > ROWS_LINEAR_MAX_LN_K)) ||
+      (p.B + 15) / 16 > 65535)
+    return hipErrorInvalidValue;
+  if (p.epi == GPT_EPI_STORE) return rows_linear_epi<GPT_EPI_STORE>(p, s);
+  if (p.epi == GPT_EPI_GELU) return rows_linear_epi<GPT_EPI_GELU>(p, s);
+  if (p.epi == GPT_EPI_RESIDUAL && !p.x) return rows_linear_epi<GPT_EPI_RESIDUAL>(p, s);
+  return hipErrorInvalidValue;
+}
+
 bool attn_decode_supported(int hd) { return hd == 32 || hd == 64 || hd == 128; }
 
 hipError_t attn_decode(int prec, int hd, const void* qkv, void* kc, void* vc, int pos, int Tmax,
@@ -288,10 +587,13 @@ hipError_t attn_decode(int prec, int hd, const void* qkv, void* kc, void* vc, in
 #define AD_(T, D)                                                                            \
   attn_decode_kernel<T, D><<<B * H, AD_THREADS, 0, s>>>((const T*)qkv, (T*)kc, (T*)vc, pos, \
                                                         Tmax, H, left, scale, (T*)out)
+#define AW_(D)                                                                           \
+  attn_decode_wide_kernel<D><<<B * H, AW_WAVES * 64, 0, s>>>(                          \
+      (const bf16_t*)qkv, (bf16_t*)kc, (bf16_t*)vc, pos, Tmax, H, left, scale, (bf16_t*)out)
   if (prec == GPT_BF16) {
-    if (hd == 32) AD_(bf16_t, 32);
-    else if (hd == 64) AD_(bf16_t, 64);
-    else if (hd == 128) AD_(bf16_t, 128);
+    if (hd == 32) AW_(32);
+    else if (hd == 64) AW_(64);
+    else if (hd == 128) AW_(128);
     else return hipErrorInvalidValue;
   } else {
     if (hd == 32) AD_(float, 32);
@@ -300,6 +602,7 @@ hipError_t attn_decode(int prec, int hd, const void* qkv, void* kc, void* vc, in
     else return hipErrorInvalidValue;
   }
 #undef AD_
+#undef AW_
   return hipGetLastError();
 }
 

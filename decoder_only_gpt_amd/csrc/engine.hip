@@ -814,7 +814,7 @@ int64_t gen_layout(const gpt_model* m, int B, int Tmax, gpt_gen* g) {
   g->rstd = take(B * 4);
   g->logits = take(B * m->Vq * act);
   g->tok = take(B * 4);
-  // split-K partials of the decode products (at most 32 splits of B x max(3C, F) floats)
+  // split-K partials of the fp32 decode products (at most 32 splits of B x max(3C, F) floats)
   g->ws_bytes = 32 * (int64_t)B * std::max(3 * C, F) * 4;
   g->ws = take(g->ws_bytes);
   g->total = o;
@@ -831,10 +831,42 @@ int gen_check(const gpt_model* m, int B, int Tmax) {
 }
 
 // out[B, N] = a[B, K] . W[N, K]^T with the given epilogue (rows of the decode step).
+// One product of a decode step, optionally after a LayerNorm of the fp32 rows
+// ln_x (ln_w set): bf16 runs the few-row MFMA kernel, which folds the
+// LayerNorm in for K up to ROWS_LINEAR_MAX_LN_K; fp32 (and wider bf16 rows)
+// run the LayerNorm kernel into a first.
 hipError_t gen_linear(const gpt_gen* g, const void* a, int64_t K, int64_t w_off, int64_t N,
                       int64_t b_off, int epi, void* out, int64_t ldo, const float* resid,
-                      void* aux, hipStream_t s) {
+                      void* aux, hipStream_t s, const float* ln_x = nullptr,
+                      int64_t ln_w = -1, int64_t ln_b = -1) {
   const gpt_model* m = g->m;
+  const bool fold_ln = ln_w >= 0 && m->bf16 && K <= gpt::ROWS_LINEAR_MAX_LN_K;
+  if (ln_w >= 0 && !fold_ln) {
+    const hipError_t e = gpt::layernorm_fwd(m->prec(), ln_x, m->P(ln_w), m->P(ln_b), g->B, (int)K,
+                                            m->cfg.ln_eps, (void*)a, (float*)(g->base + g->mean),
+                                            (float*)(g->base + g->rstd), s);
+    if (e != hipSuccess) return e;
+  }
+  if (m->bf16) {
+    gpt::RowsLinear p;
+    if (fold_ln) {
+      p.x = ln_x;
+      p.ln_w = m->P(ln_w);
+      p.ln_b = m->P(ln_b);
+      p.eps = m->cfg.ln_eps;
+    } else {
+      p.a = a;
+    }
+    p.B = g->B; p.K = (int)K; p.N = (int)N;
+    p.W = m->W(w_off);
+    p.bias = b_off >= 0 ? m->P(b_off) : nullptr;
+    p.epi = epi;
+    p.out = out; p.ldo = ldo;
+    p.resid = resid;
+    p.aux = aux;
+    p.tanh_form = m->cfg.gelu_tanh;
+    return gpt::rows_linear(p, s);
+  }
   gpt_gemm_desc d;
   std::memset(&d, 0, sizeof(d));
   d.precision = m->cfg.precision;
@@ -870,19 +902,15 @@ int gen_step(gpt_gen* g, const int32_t* d_tok, hipStream_t s) {
   HIP_TRY(gpt::gen_embed(d_tok, m->P(m->pl.wte), m->P(m->pl.wpe), g->pos, B, (int)C, x, s));
   for (int l = 0; l < c.n_layer; ++l) {
     const LayerOff& L = m->pl.layer[l];
-    HIP_TRY(gpt::layernorm_fwd(prec, x, m->P(L.ln1w), m->P(L.ln1b), B, (int)C, c.ln_eps, a, mean,
-                               rstd, s));
     HIP_TRY(gen_linear(g, a, C, L.qkvw, 3 * C, L.qkvb, GPT_EPI_STORE, base + g->qkv, 3 * C,
-                       nullptr, nullptr, s));
+                       nullptr, nullptr, s, x, L.ln1w, L.ln1b));
     HIP_TRY(gpt::attn_decode(prec, (int)m->hd, base + g->qkv, base + g->kc + l * cache_layer,
                              base + g->vc + l * cache_layer, g->pos, g->Tmax, B, (int)m->H,
                              c.window_left[l], base + g->att, s));
     HIP_TRY(gen_linear(g, base + g->att, C, L.projw, C, L.projb, GPT_EPI_RESIDUAL, x, C, x,
                        nullptr, s));
-    HIP_TRY(gpt::layernorm_fwd(prec, x, m->P(L.ln2w), m->P(L.ln2b), B, (int)C, c.ln_eps, a, mean,
-                               rstd, s));
     HIP_TRY(gen_linear(g, a, C, L.fcw, F, L.fcb, GPT_EPI_GELU, base + g->u, F, nullptr,
-                       base + g->gact, s));
+                       base + g->gact, s, x, L.ln2w, L.ln2b));
     HIP_TRY(gen_linear(g, base + g->gact, F, L.fcpw, C, L.fcpb, GPT_EPI_RESIDUAL, x, C, x,
                        nullptr, s));
   }

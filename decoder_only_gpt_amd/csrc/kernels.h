@@ -98,6 +98,29 @@ hipError_t gen_embed(const int32_t* tok, const float* wte, const float* wpe, int
 // caches [B, H, Tmax, hd] (act) of this layer; row pos of both caches is
 // written from qkv; out [B, H*hd] (act).
 bool attn_decode_supported(int hd);
+// Few-row bf16 product of a decode step: out[b, n] = epilogue(sum_k a[b, k] W[n, k]),
+// W [N, K] bf16 (K % 64 == 0).  The activation rows are a [B, K] bf16, or with x set
+// LayerNorm(x) of the fp32 rows x [B, K] with ln_w / ln_b (ln_b optional) and eps.
+// Epilogue STORE / RESIDUAL (out and resid float, no LayerNorm) / GELU (aux = GELU of
+// the stored pre-activation), bias optional.
+struct RowsLinear {
+  const void* a = nullptr;
+  const float* x = nullptr;
+  const float* ln_w = nullptr;
+  const float* ln_b = nullptr;
+  float eps = 0.f;
+  int B = 0, K = 0, N = 0;
+  const void* W = nullptr;
+  const float* bias = nullptr;
+  int epi = 0;
+  void* out = nullptr;
+  long ldo = 0;
+  const float* resid = nullptr;
+  void* aux = nullptr;
+  int tanh_form = 0;
+};
+constexpr int ROWS_LINEAR_MAX_LN_K = 1024;  // LayerNorm rows staged in LDS
+hipError_t rows_linear(const RowsLinear& p, hipStream_t s);
 hipError_t attn_decode(int prec, int hd, const void* qkv, void* kc, void* vc, int pos, int Tmax,
                        int B, int H, int left, void* out, hipStream_t s);
 // Per row b of logits [B, ldz] (act): token from the first V entries with

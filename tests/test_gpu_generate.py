@@ -74,6 +74,24 @@ def test_decode_logits_match_full_forward(name, prec):
     print(f"[gen] {name} {prec} worst logit error {worst:.2e}", flush=True)
 
 
+@pytest.mark.parametrize("prec", ["fp32", "bf16"])
+def test_decode_logits_more_rows_than_one_tile(prec):
+    """20 sequences: the bf16 decode products take rows in groups of 16, so
+    the second group (rows 16..19) runs with a ragged tail."""
+    cfg, p, m = _setup("chat_s", prec, seed=3)
+    B, T = 20, 24
+    seq, _ = synth.tokens(cfg, B=B, T=T, seed=15)
+    g = gpt.Generator(m, B, T)
+    tol = 3e-2 if prec == "bf16" else 1e-4
+    print(f"[gen] logits chat_s {prec} B={B} T={T}", flush=True)
+    for t in range(T):
+        g.step(_dev(seq[:, t]))
+        z = g.logits()
+        ref = oracle.next_token_logits(cfg, p, seq[:, :t + 1])[:, :cfg["vocab_size"]]
+        err = np.abs(z - ref).max(axis=1) / np.abs(ref).max(axis=1)
+        assert err.max() <= tol, (t, int(err.argmax()), float(err.max()))
+
+
 def _valid_draw(z, V, temperature, top_k, u, tok):
     w = np.asarray(z, np.float64)[:V] / temperature
     keep = np.ones(V, bool)
