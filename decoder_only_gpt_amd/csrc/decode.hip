@@ -268,7 +268,11 @@ __global__ void __launch_bounds__(WAVES * 64) rows_linear_kernel(
   constexpr int STEP = RL_DEPTH * WAVES;
   __shared__ float part[WAVES * 64 * 4];
   extern __shared__ __align__(16) bf16_t xs[];  // LNV > 0: 16 rows, stride K + 8
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // The wave index in a scalar register: the block conditions below are then
+  // scalar branches.  Derived per lane they compile to EXEC-masked regions,
+  // and an MFMA in such a region still runs when EXEC is zero, accumulating
+  // whatever its operand registers hold.
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = blockIdx.x * 16, b0 = blockIdx.y * 16;
   const int li = lane & 15, kq = lane >> 4;
   const int KB = K / 64, LDX = K + 8;  // K % 64 == 0

@@ -8,7 +8,9 @@ checked through properties that hold at any size:
     (loss rows bitwise equal to a B = 1 run of that sequence);
   * the whole-batch gradient equals the mean of the per-sequence gradients;
   * the gradient of one sequence matches the oracle's (full model size);
-  * padded vocabulary rows stay exactly zero; the step is bitwise reproducible.
+  * padded vocabulary rows stay exactly zero; the step is bitwise reproducible;
+  * decode at the benchmark's 16 sequences: logits of sampled rows equal the
+    oracle's full forward of that row's prefix.
 """
 
 import numpy as np
@@ -179,3 +181,27 @@ def test_full_size_muon_step(name):
         pr, mr, vr = oracle.adamw_update(p[sl], z, z, g[sl], s_ad)
         assert np.array_equal(gp[sl].view(np.uint32), pr.view(np.uint32)), n
         assert np.array_equal(gv[sl].view(np.uint32), vr.view(np.uint32)), n
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_decode_logits(name):
+    """Key/value-cache decode of 16 sequences at full model size (the decode
+    products at their real shapes: LayerNorm folded in for n_embd <= 1024, 16
+    waves per workgroup for the FC projection), sampled rows against the oracle."""
+    cfg = presets.preset(name)
+    B, T = 16, 4
+    print(f"[full] decode {name} B={B} T={T}", flush=True)
+    p = synth.init_params(cfg, seed=2, perturb=True)
+    seq, _ = synth.tokens(cfg, B=B, T=T, seed=3)
+    m = gpt.Model(cfg, B=1, T=8)
+    m.set_params(p)
+    g = gpt.Generator(m, B, T)
+    rows = [0, B - 1]
+    V = cfg["vocab_size"]
+    for t in range(T):
+        g.step(torch.from_numpy(np.ascontiguousarray(seq[:, t], np.int32)).cuda())
+        z = g.logits()
+        assert np.all(np.isfinite(z[:, :V]))
+        ref = oracle.next_token_logits(cfg, p, seq[rows, :t + 1], dtype=np.float32)[:, :V]
+        err = np.abs(z[rows, :V] - ref).max(axis=1) / np.abs(ref).max(axis=1)
+        assert err.max() <= 3e-2, (t, err)

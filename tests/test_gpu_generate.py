@@ -39,6 +39,11 @@ CFGS = {
     "chat_s": presets.preset("nanochat_swa", vocab_size=300, padded_vocab=300, block_size=160,
                              n_layer=2, n_head=1, n_embd=128, mlp_hidden=256,
                              window_left=[20, -1], B=2, T=64),
+    # wider than the bf16 decode products fold the LayerNorm into (1024), and an
+    # FC projection long enough (K = 2048) for 16 waves per workgroup
+    "wide_s": presets.preset("gpt2_124m", vocab_size=200, padded_vocab=208, block_size=64,
+                             n_layer=1, n_head=9, n_embd=1152, mlp_hidden=2048,
+                             window_left=[-1], B=2, T=16),
 }
 
 
@@ -55,10 +60,10 @@ def _dev(a):
 
 
 @pytest.mark.parametrize("prec", ["fp32", "bf16"])
-@pytest.mark.parametrize("name", ["tiny", "gpt2_s", "chat_s"])
+@pytest.mark.parametrize("name", ["tiny", "gpt2_s", "chat_s", "wide_s"])
 def test_decode_logits_match_full_forward(name, prec):
     cfg, p, m = _setup(name, prec)
-    B, T = 3, 48 if name != "tiny" else 32
+    B, T = 3, {"tiny": 32, "wide_s": 16}.get(name, 48)
     seq, _ = synth.tokens(cfg, B=B, T=T, seed=11)
     g = gpt.Generator(m, B, T)
     tol = 3e-2 if prec == "bf16" else 1e-4
