@@ -344,7 +344,7 @@ __global__ void __launch_bounds__(256, HD == 128 ? 1 : 2)
   constexpr int NS = HD / 16, ND = HD / 32;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KB * HD];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[2][KB * HD];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5, c = lane & 31;
   const int h = blockIdx.x % H, b = blockIdx.x / H;
   const long C = (long)H * HD, ld = 3 * C;
@@ -470,7 +470,7 @@ __global__ void __launch_bounds__(256, HD == 128 ? 1 : 2)
   __shared__ __attribute__((aligned(16))) bf16_t Gs[2][KB * HD];
   __shared__ __attribute__((aligned(16))) float Ls[2][KB];
   __shared__ __attribute__((aligned(16))) float Ds[2][KB];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5, c = lane & 31;
   const int h = blockIdx.x % H, b = blockIdx.x / H;
   const long C = (long)H * HD, ld = 3 * C;
@@ -600,7 +600,7 @@ __global__ void __launch_bounds__(256, HD == 128 ? 1 : 2)
   constexpr int NS = HD / 16, ND = HD / 32;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KB * HD];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[2][KB * HD];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5, c = lane & 31;
   const int h = blockIdx.x % H, b = blockIdx.x / H;
   const long C = (long)H * HD, ld = 3 * C;
