@@ -80,11 +80,13 @@ def test_decode_logits_match_full_forward(name, prec):
 
 
 @pytest.mark.parametrize("prec", ["fp32", "bf16"])
-def test_decode_logits_more_rows_than_one_tile(prec):
-    """20 sequences: the bf16 decode products take rows in groups of 16, so
-    the second group (rows 16..19) runs with a ragged tail."""
+@pytest.mark.parametrize("B", [1, 20])
+def test_decode_logits_row_groups(prec, B):
+    """The bf16 decode products take rows in groups of 16: one sequence (15
+    rows of the group stand in for row 0), and 20 (the second group, rows
+    16..19, runs with a ragged tail)."""
     cfg, p, m = _setup("chat_s", prec, seed=3)
-    B, T = 20, 24
+    T = 24
     seq, _ = synth.tokens(cfg, B=B, T=T, seed=15)
     g = gpt.Generator(m, B, T)
     tol = 3e-2 if prec == "bf16" else 1e-4
@@ -94,7 +96,7 @@ def test_decode_logits_more_rows_than_one_tile(prec):
         z = g.logits()
         ref = oracle.next_token_logits(cfg, p, seq[:, :t + 1])[:, :cfg["vocab_size"]]
         err = np.abs(z - ref).max(axis=1) / np.abs(ref).max(axis=1)
-        assert err.max() <= tol, (t, int(err.argmax()), float(err.max()))
+        assert err.max() <= tol, (B, t, int(err.argmax()), float(err.max()))
 
 
 def _valid_draw(z, V, temperature, top_k, u, tok):
