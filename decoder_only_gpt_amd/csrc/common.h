@@ -65,10 +65,13 @@ __device__ __forceinline__ float gelu_grad_f(float u, bool tanh_form) {
 //    with the hardware exp2 and reciprocal;
 //  exact form: erf by Abramowitz & Stegun, Handbook of Mathematical Functions,
 //    formula 7.1.26 (|error| <= 1.5e-7), with erf(-x) = -erf(x).
-__device__ __forceinline__ float sigmoid2z(float u, float& z) {
-  const float s = 0.7978845608028654f, k = 0.044715f;
-  z = s * u * fmaf(k, u * u, 1.f);
-  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-2.8853900817779268f * z));
+__device__ __forceinline__ float sigmoid2z(float u, float u2) {
+  // sigmoid(2 z) of the tanh form, z = s (u + k u^3), s = sqrt(2 / pi),
+  // k = 0.044715: the exp2 argument -2 log2(e) z is one polynomial in u
+  // (u2 = u * u, shared with the derivative).
+  constexpr float c0 = -2.8853900817779268f * 0.7978845608028654f;
+  constexpr float c1 = c0 * 0.044715f;
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(u * fmaf(c1, u2, c0)));
 }
 // erf(|x|) and exp(-x^2) for the exact form.
 __device__ __forceinline__ float erf_as(float x, float& ex2) {
@@ -84,20 +87,17 @@ __device__ __forceinline__ float erf_as(float x, float& ex2) {
   return copysignf(e, x);
 }
 __device__ __forceinline__ float gelu_fast(float u, bool tanh_form) {
-  if (tanh_form) {
-    float z;
-    return u * sigmoid2z(u, z);
-  }
+  if (tanh_form) return u * sigmoid2z(u, u * u);
   float ex2;
   return 0.5f * u * (1.f + erf_as(u * 0.7071067811865476f, ex2));
 }
 __device__ __forceinline__ float gelu_grad_fast(float u, bool tanh_form) {
   if (tanh_form) {
-    const float s = 0.7978845608028654f, k = 0.044715f;
-    float z;
-    const float sg = sigmoid2z(u, z);
-    // d/du [u sigmoid(2z)] = sg (1 + 2 u (1 - sg) z'(u)),  z' = s (1 + 3 k u^2)
-    return sg * fmaf(2.f * s * u * (1.f - sg), fmaf(3.f * k, u * u, 1.f), 1.f);
+    // d/du [u sigmoid(2z)] = sg (1 + u (1 - sg) 2 z'(u)),  2 z' = 2 s + 6 s k u^2
+    constexpr float s2 = 2.f * 0.7978845608028654f, s6k = 6.f * 0.7978845608028654f * 0.044715f;
+    const float u2 = u * u;
+    const float sg = sigmoid2z(u, u2);
+    return sg * fmaf(u * (1.f - sg), fmaf(s6k, u2, s2), 1.f);
   }
   float ex2;
   const float e = erf_as(u * 0.7071067811865476f, ex2);  // ex2 = exp(-u^2 / 2)
@@ -107,11 +107,11 @@ __device__ __forceinline__ float gelu_grad_fast(float u, bool tanh_form) {
 // GELU(u) and GELU'(u) together (fast forms, shared intermediate values).
 __device__ __forceinline__ void gelu_pair_fast(float u, bool tanh_form, float& g, float& gp) {
   if (tanh_form) {
-    const float s = 0.7978845608028654f, k = 0.044715f;
-    float z;
-    const float sg = sigmoid2z(u, z);
+    constexpr float s2 = 2.f * 0.7978845608028654f, s6k = 6.f * 0.7978845608028654f * 0.044715f;
+    const float u2 = u * u;
+    const float sg = sigmoid2z(u, u2);
     g = u * sg;
-    gp = sg * fmaf(2.f * s * u * (1.f - sg), fmaf(3.f * k, u * u, 1.f), 1.f);
+    gp = sg * fmaf(u * (1.f - sg), fmaf(s6k, u2, s2), 1.f);
     return;
   }
   float ex2;
