@@ -259,6 +259,16 @@ __device__ __forceinline__ bf16x8 frag(const bf16_t* lds, int r0, int ks, int la
 __device__ __forceinline__ void st16nt(void* p, u32x4 v) { __builtin_nontemporal_store(v, (u32x4*)p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
 
+// The MUL epilogue (out = acc * aux) with its 8 auxiliary values already loaded.
+__device__ __forceinline__ void mul8_store(const EpiArgs& e, int m, int n, float4 v0, float4 v1,
+                                           u32x4 a) {
+  st16((bf16_t*)e.out + (long)m * e.ldo + n,
+       u32x4{pack_bf2(v0.x * bf_lo(a.x), v0.y * bf_hi(a.x)),
+             pack_bf2(v0.z * bf_lo(a.y), v0.w * bf_hi(a.y)),
+             pack_bf2(v1.x * bf_lo(a.z), v1.y * bf_hi(a.z)),
+             pack_bf2(v1.z * bf_lo(a.w), v1.w * bf_hi(a.w))});
+}
+
 template <int EPI>
 __device__ __forceinline__ void epilogue8(const EpiArgs& e, float* partial, int m, int n,
                                           float4 v0, float4 v1) {
@@ -1131,6 +1141,20 @@ __device__ __forceinline__ void big8_tile(const OpArgs& A, const OpArgs& B, int 
   }
   float* Cw = (float*)smem + wave * (32 * CP);  // 8 slices of 8.5 KB (68 KB of the 128 KB)
   const int m_l = lane & 31, nq = 4 * (lane >> 5);
+  // MUL: the 16 auxiliary vectors this lane multiplies by are loaded before
+  // the blocks, so one memory round trip covers all of them.
+  u32x4 pre[4][4];
+  if constexpr (EPI == GPT_EPI_MUL) {
+    const int n = n0 + wn * 64 + (lane & 7) * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int m = m0 + wm * 128 + i * 32 + p * 8 + (lane >> 3);
+        if (m < e.M && n < e.N)
+          pre[i][p] = *(const u32x4*)((const bf16_t*)e.aux + (long)m * e.ldaux + n);
+      }
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -1152,7 +1176,8 @@ __device__ __forceinline__ void big8_tile(const OpArgs& A, const OpArgs& B, int 
       if (m < e.M && n < e.N) {
         const float4 v0 = *(const float4*)(Cw + row * CP + cg * 8);
         const float4 v1 = *(const float4*)(Cw + row * CP + cg * 8 + 4);
-        epilogue8<EPI>(e, partial, m, n, v0, v1);
+        if constexpr (EPI == GPT_EPI_MUL) mul8_store(e, m, n, v0, v1, pre[i][p]);
+        else epilogue8<EPI>(e, partial, m, n, v0, v1);
       }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next block overwrites
