@@ -1141,6 +1141,22 @@ __device__ __forceinline__ void big8_tile(const OpArgs& A, const OpArgs& B, int 
   }
   float* Cw = (float*)smem + wave * (32 * CP);  // 8 slices of 8.5 KB (68 KB of the 128 KB)
   const int m_l = lane & 31, nq = 4 * (lane >> 5);
+  // The bias of this lane's 8 columns, loaded once for the tile (the
+  // epilogue would reload it for every row block) and added here.
+  constexpr bool BIAS_EPI = EPI == GPT_EPI_STORE || EPI == GPT_EPI_RESIDUAL ||
+                            EPI == GPT_EPI_GELU || EPI == GPT_EPI_GELU_PAIR;
+  float4 bias0 = make_float4(0.f, 0.f, 0.f, 0.f), bias1 = bias0;
+  EpiArgs eb = e;
+  bool has_bias = false;
+  if constexpr (BIAS_EPI) {
+    const int n = n0 + wn * 64 + (lane & 7) * 8;
+    has_bias = e.bias != nullptr;
+    if (has_bias && n < e.N) {
+      bias0 = *(const float4*)(e.bias + n);
+      bias1 = *(const float4*)(e.bias + n + 4);
+    }
+    eb.bias = nullptr;
+  }
   // MUL: the 16 auxiliary vectors this lane multiplies by are loaded before
   // the blocks, so one memory round trip covers all of them.
   u32x4 pre[4][4];
@@ -1174,10 +1190,19 @@ __device__ __forceinline__ void big8_tile(const OpArgs& A, const OpArgs& B, int 
       const int row = p * 8 + (lane >> 3);
       const int m = m0 + wm * 128 + i * 32 + row;
       if (m < e.M && n < e.N) {
-        const float4 v0 = *(const float4*)(Cw + row * CP + cg * 8);
-        const float4 v1 = *(const float4*)(Cw + row * CP + cg * 8 + 4);
-        if constexpr (EPI == GPT_EPI_MUL) mul8_store(e, m, n, v0, v1, pre[i][p]);
-        else epilogue8<EPI>(e, partial, m, n, v0, v1);
+        float4 v0 = *(const float4*)(Cw + row * CP + cg * 8);
+        float4 v1 = *(const float4*)(Cw + row * CP + cg * 8 + 4);
+        if constexpr (EPI == GPT_EPI_MUL) {
+          mul8_store(e, m, n, v0, v1, pre[i][p]);
+        } else if constexpr (BIAS_EPI) {
+          if (has_bias) {
+            v0 = make_float4(v0.x + bias0.x, v0.y + bias0.y, v0.z + bias0.z, v0.w + bias0.w);
+            v1 = make_float4(v1.x + bias1.x, v1.y + bias1.y, v1.z + bias1.z, v1.w + bias1.w);
+          }
+          epilogue8<EPI>(eb, partial, m, n, v0, v1);
+        } else {
+          epilogue8<EPI>(e, partial, m, n, v0, v1);
+        }
       }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next block overwrites
