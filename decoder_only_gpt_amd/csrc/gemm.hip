@@ -336,7 +336,9 @@ __device__ __forceinline__ void epilogue8(const EpiArgs& e, float* partial, int 
       gelu_pair_fast(bf_lo(w[i]), e.tanh_form, g[2 * i], gp[2 * i]);
       gelu_pair_fast(bf_hi(w[i]), e.tanh_form, g[2 * i + 1], gp[2 * i + 1]);
     }
-    st16((bf16_t*)e.out + o, u32x4{pack_bf2(gp[0], gp[1]), pack_bf2(gp[2], gp[3]),
+    // GELU'(u) is read only by the backward pass: streamed past the caches
+    // (GELU(u), the next product's operand, is stored normally).
+    st16nt((bf16_t*)e.out + o, u32x4{pack_bf2(gp[0], gp[1]), pack_bf2(gp[2], gp[3]),
                                            pack_bf2(gp[4], gp[5]), pack_bf2(gp[6], gp[7])});
     st16((bf16_t*)e.aux + (long)m * e.ldaux + n, u32x4{
         pack_bf2(g[0], g[1]), pack_bf2(g[2], g[3]), pack_bf2(g[4], g[5]), pack_bf2(g[6], g[7])});
