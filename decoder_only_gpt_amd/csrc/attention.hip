@@ -79,39 +79,8 @@ __global__ void __launch_bounds__(256) attn_fwd_rows(const T* qkv, T* out, float
   if (lane == 0) lse[((long)b * H + h) * Tn + i] = m + logf(l);
 }
 
-// D[b,h,i] = sum_d dO[i,d] * O[i,d]  (one thread per (row, head)).
-// bf16: also the log-sum-exp in log2 units, L2 = lse * log2(e), for the
-// MFMA backward kernels.  One wave per token row; a lane takes 8 consecutive head dims (16-byte
-// loads) and the hd/8 lanes of a head combine by butterfly shuffles.
-template <int HD>
-__global__ void __launch_bounds__(256) attn_dvec_bf16(const bf16_t* out, const bf16_t* dout,
-                                                      const float* lse, float* D, float* L2, int M,
-                                                      int Tn, int H) {
-  constexpr int LPH = HD / 8;  // lanes per head
-  const int lane = threadIdx.x & 63;
-  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= M) return;
-  const int C = H * HD;
-  const int b = (int)(row / Tn), t = (int)(row % Tn);
-  for (int v0 = 0; v0 < C / 8; v0 += 64) {
-    const int v = v0 + lane;
-    float s = 0.f;
-    if (v < C / 8) {
-      u32x4 a = *(const u32x4*)(out + row * C + v * 8);
-      u32x4 g = *(const u32x4*)(dout + row * C + v * 8);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) s += bf_lo(a[k]) * bf_lo(g[k]) + bf_hi(a[k]) * bf_hi(g[k]);
-    }
-#pragma unroll
-    for (int o = 1; o < LPH; o <<= 1) s += __shfl_xor(s, o, 64);
-    if (v < C / 8 && (lane % LPH) == 0) {
-      const long o = ((long)b * H + v / LPH) * Tn + t;
-      D[o] = s;
-      L2[o] = lse[o] * LOG2E;
-    }
-  }
-}
-
+// D[b,h,i] = sum_d dO[i,d] * O[i,d]  (one thread per (row, head)); the bf16
+// path computes it inside the dQ kernel.
 template <typename T>
 __global__ void __launch_bounds__(256) attn_dvec(const T* out, const T* dout, float* D, int B,
                                                  int Tn, int H, int hd) {
@@ -603,8 +572,9 @@ __global__ void __launch_bounds__(256, HD == 128 ? 1 : 2)
 // workgroup walks their key blocks.
 template <int HD>
 __global__ void __launch_bounds__(256, HD == 128 ? 1 : 2)
-    attn_dq_mfma(const bf16_t* qkv, const float* L2, const bf16_t* dout, const float* D,
-                 bf16_t* dqkv, int Tn, int H, int left, float scale, float scale_log2) {
+    attn_dq_mfma(const bf16_t* qkv, const float* lse, const bf16_t* out, const bf16_t* dout,
+                 float* D, float* L2, bf16_t* dqkv, int Tn, int H, int left, float scale,
+                 float scale_log2) {
   constexpr int NS = HD / 16, ND = HD / 32;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KB * HD];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[2][KB * HD];
@@ -619,19 +589,30 @@ __global__ void __launch_bounds__(256, HD == 128 ? 1 : 2)
   const int qi = qw0 + c;
 
   bf16x8 qf[NS], gf[NS];
+  float dpart = 0.f;  // this lane's share of D = sum_d dO O for its query
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    u32x4 a{0, 0, 0, 0}, v{0, 0, 0, 0};
+    u32x4 a{0, 0, 0, 0}, v{0, 0, 0, 0}, o{0, 0, 0, 0};
     if (qi < Tn) {
+      const long row = ((long)b * Tn + qi) * C + h * HD + 16 * s + 8 * g;
       a = *(const u32x4*)(base + (long)qi * ld + h * HD + 16 * s + 8 * g);
-      v = *(const u32x4*)(dout + ((long)b * Tn + qi) * C + h * HD + 16 * s + 8 * g);
+      v = *(const u32x4*)(dout + row);
+      o = *(const u32x4*)(out + row);
     }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dpart += bf_lo(o[k]) * bf_lo(v[k]) + bf_hi(o[k]) * bf_hi(v[k]);
     qf[s] = *(bf16x8*)&a;
     gf[s] = *(bf16x8*)&v;
   }
+  // Lanes c and c + 32 hold the two halves of query qi's head dims; the sum
+  // and the log-sum-exp in log2 units also go to D and L2 for the dK/dV kernel.
   const long r0 = ((long)b * H + h) * Tn;
-  const float Lq = qi < Tn ? L2[r0 + qi] : 0.f;
-  const float Dq = qi < Tn ? D[r0 + qi] : 0.f;
+  const float Dq = dpart + __shfl_xor(dpart, 32, 64);
+  const float Lq = qi < Tn ? lse[r0 + qi] * LOG2E : 0.f;
+  if (g == 0 && qi < Tn) {
+    D[r0 + qi] = Dq;
+    L2[r0 + qi] = Lq;
+  }
   f32x16 dq[ND];  // dQ^T: head dim d * 32 + acc_row(r, g), query qi
 #pragma unroll
   for (int d = 0; d < ND; ++d) dq[d] = f32x16{};
@@ -715,18 +696,21 @@ hipError_t launch_fwd(int B, int T, int H, int left, const void* qkv, void* out,
 }
 
 template <int HD>
-hipError_t launch_bwd(int B, int T, int H, int left, const void* qkv, const float* L2,
-                      const void* dout, const float* D, void* dqkv, hipStream_t s) {
+// dQ first: it also writes D and L2 (per query), which dK/dV then reads.
+hipError_t launch_bwd(int B, int T, int H, int left, const void* qkv, const void* out,
+                      const float* lse, const void* dout, float* D, float* L2, void* dqkv,
+                      hipStream_t s) {
   if (!fits_rsrc(T, H, HD)) return hipErrorInvalidValue;
   dim3 grid((unsigned)(B * H), (unsigned)cdiv(T, 128));
   float sc = 1.f / sqrtf((float)HD);
   float sl2 = sc * LOG2E;
-  attn_dkv_mfma<HD><<<grid, 256, 0, s>>>((const bf16_t*)qkv, L2, (const bf16_t*)dout, D,
-                                         (bf16_t*)dqkv, T, H, left, sc, sl2);
+  attn_dq_mfma<HD><<<grid, 256, 0, s>>>((const bf16_t*)qkv, lse, (const bf16_t*)out,
+                                        (const bf16_t*)dout, D, L2, (bf16_t*)dqkv, T, H, left,
+                                        sc, sl2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  attn_dq_mfma<HD><<<grid, 256, 0, s>>>((const bf16_t*)qkv, L2, (const bf16_t*)dout, D,
-                                        (bf16_t*)dqkv, T, H, left, sc, sl2);
+  attn_dkv_mfma<HD><<<grid, 256, 0, s>>>((const bf16_t*)qkv, L2, (const bf16_t*)dout, D,
+                                         (bf16_t*)dqkv, T, H, left, sc, sl2);
   return hipGetLastError();
 }
 }  // namespace
@@ -758,22 +742,10 @@ hipError_t attention_bwd(int prec, int B, int T, int H, int hd, int left, const 
   if (!attention_supported(prec, hd)) return hipErrorInvalidValue;
   long rows = (long)B * T * H;
   if (prec == GPT_BF16) {
-    const long M = (long)B * T;
-    const unsigned g = (unsigned)cdiv(M, 4);
-    const bf16_t* o16 = (const bf16_t*)out;
-    const bf16_t* g16 = (const bf16_t*)dout;
     float* L2 = dvec + rows;  // second half of the workspace
-    if (hd == 32)
-      attn_dvec_bf16<32><<<g, 256, 0, s>>>(o16, g16, lse, dvec, L2, (int)M, T, H);
-    else if (hd == 64)
-      attn_dvec_bf16<64><<<g, 256, 0, s>>>(o16, g16, lse, dvec, L2, (int)M, T, H);
-    else
-      attn_dvec_bf16<128><<<g, 256, 0, s>>>(o16, g16, lse, dvec, L2, (int)M, T, H);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (hd == 32) return launch_bwd<32>(B, T, H, left, qkv, L2, dout, dvec, dqkv, s);
-    if (hd == 64) return launch_bwd<64>(B, T, H, left, qkv, L2, dout, dvec, dqkv, s);
-    return launch_bwd<128>(B, T, H, left, qkv, L2, dout, dvec, dqkv, s);
+    if (hd == 32) return launch_bwd<32>(B, T, H, left, qkv, out, lse, dout, dvec, L2, dqkv, s);
+    if (hd == 64) return launch_bwd<64>(B, T, H, left, qkv, out, lse, dout, dvec, L2, dqkv, s);
+    return launch_bwd<128>(B, T, H, left, qkv, out, lse, dout, dvec, L2, dqkv, s);
   }
   attn_dvec<float><<<(unsigned)cdiv(rows, 256), 256, 0, s>>>((const float*)out,
                                                              (const float*)dout, dvec, B, T, H, hd);
