@@ -46,7 +46,7 @@ __all__ = [
     "loss_rows", "cosine_lr", "train_steps", "NS_COEFFS", "muon_matrices",
     "orthogonalize", "muon_momentum", "muon_second_moment", "cautious_update",
     "muon_matrix_update", "MuonHP", "muon_hybrid_step", "sample_token", "next_token_logits",
-    "generate",
+    "generate", "philox4x32_10", "philox_normals", "init_params",
 ]
 
 
@@ -709,3 +709,80 @@ def generate(cfg, flat_params, prompt, n_new: int, temperature: float, top_k: in
                         for b in range(B)], np.int32)
         tokens = np.concatenate([tokens, nxt[:, None]], axis=1)
     return tokens
+
+
+# --------------------------------------------------------------------------
+# seeded initialisation (the weights N(0, 0.02) of the workload configs; gains
+# 1, shifts and biases 0, padded vocabulary rows 0)
+# --------------------------------------------------------------------------
+_PHILOX_M = (0xD2511F53, 0xCD9E8D57)  # round multipliers
+_PHILOX_W = (0x9E3779B9, 0xBB67AE85)  # key increments (golden ratio, sqrt(3) - 1)
+
+
+def philox4x32_10(ctr, key):
+    """Philox4x32 with 10 rounds (Salmon, Moraes, Dror and Shaw, "Parallel random
+    numbers: as easy as 1, 2, 3", SC 2011).  ctr: [n, 4] counters, key: 2 words
+    (uint32).  Each round multiplies words 0 and 2 by the two constants, and
+    the new block is (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1,
+    lo(M0 c0)); the key grows by the two increments before every round after
+    the first.  Returns [n, 4] uint32."""
+    mask = np.uint64(0xFFFFFFFF)
+    c = np.asarray(ctr, dtype=np.uint64).reshape(-1, 4) & mask
+    k0, k1 = (np.uint64(int(key[0]) & 0xFFFFFFFF), np.uint64(int(key[1]) & 0xFFFFFFFF))
+    c0, c1, c2, c3 = c[:, 0], c[:, 1], c[:, 2], c[:, 3]
+    for r in range(10):
+        if r:
+            k0 = (k0 + np.uint64(_PHILOX_W[0])) & mask
+            k1 = (k1 + np.uint64(_PHILOX_W[1])) & mask
+        p0 = np.uint64(_PHILOX_M[0]) * c0
+        p1 = np.uint64(_PHILOX_M[1]) * c2
+        c0, c1, c2, c3 = ((p1 >> np.uint64(32)) ^ c1 ^ k0, p1 & mask,
+                          (p0 >> np.uint64(32)) ^ c3 ^ k1, p0 & mask)
+    return np.stack([c0, c1, c2, c3], axis=1).astype(np.uint32)
+
+
+def philox_normals(begin: int, n: int, seed: int) -> np.ndarray:
+    """Standard normals z[i] for flat indices i in [begin, begin + n), float64.
+    Index i uses Philox block j = i // 4 (counter (j mod 2^32, j div 2^32, 0, 0),
+    key (seed mod 2^32, seed div 2^32)); its words (x0, x1) give z[4j], z[4j+1]
+    and (x2, x3) give z[4j+2], z[4j+3] by the Box-Muller transform (Box and
+    Muller, 1958): u1 = (x + 1) / 2^32, u2 = x' / 2^32, r = sqrt(-2 ln u1),
+    (r cos 2 pi u2, r sin 2 pi u2)."""
+    if n <= 0:
+        return np.zeros(0)
+    j0, j1 = begin // 4, (begin + n - 1) // 4
+    j = np.arange(j0, j1 + 1, dtype=np.uint64)
+    ctr = np.stack([j & np.uint64(0xFFFFFFFF), j >> np.uint64(32),
+                    np.zeros_like(j), np.zeros_like(j)], axis=1)
+    x = philox4x32_10(ctr, (seed & 0xFFFFFFFF, seed >> 32)).astype(np.float64)
+    z = np.empty((len(j), 4))
+    for a, b in ((0, 1), (2, 3)):
+        r = np.sqrt(-2.0 * np.log((x[:, a] + 1.0) / 4294967296.0))
+        th = 2.0 * np.pi * (x[:, b] / 4294967296.0)
+        z[:, a] = r * np.cos(th)
+        z[:, b] = r * np.sin(th)
+    z = z.reshape(-1)
+    off = begin - 4 * j0
+    return z[off:off + n]
+
+
+def init_params(cfg, seed: int, std: float = 0.02) -> np.ndarray:
+    """The flat float32 parameter vector of a seeded initialisation: every matrix
+    and embedding entry is (float) (std * z[i]) with z the standard normal of
+    its flat index i (philox_normals), except the padded vocabulary rows
+    (>= vocab_size) of wte / lm_head, which are 0; LayerNorm gains are 1 and
+    LayerNorm shifts and Linear biases 0."""
+    V, out, off = cfg["vocab_size"], [], 0
+    for name, shape in layout(cfg):
+        n = int(np.prod(shape))
+        if len(shape) == 2:
+            a = (std * philox_normals(off, n, seed)).astype(np.float32)
+            if name in ("wte", "lm_head.w"):
+                a.reshape(shape)[V:] = 0.0
+        elif name.endswith("ln1.w") or name.endswith("ln2.w") or name == "lnf.w":
+            a = np.ones(n, np.float32)
+        else:
+            a = np.zeros(n, np.float32)
+        out.append(a)
+        off += n
+    return np.concatenate(out)

@@ -517,3 +517,67 @@ def test_generate_composes_forward_and_sampler():
     # the last position's logits do not depend on anything after it (causality)
     z_full = oracle.logits(cfg, p, out).reshape(2, 11, -1)
     assert np.allclose(oracle.next_token_logits(cfg, p, out[:, :7]), z_full[:, 6], atol=1e-12)
+
+
+# ---------------------------------------------------------------- seeded initialisation
+def test_philox_known_answers():
+    """The generator behind the seeded init against the published Philox4x32-10
+    known-answer vectors (a wrong multiplier, key increment, word order or
+    round count fails one of them)."""
+    for kat in _gold("philox_kat.json")["philox4x32_10"]:
+        ctr = [[int(x, 16) for x in kat["ctr"]]]
+        key = [int(x, 16) for x in kat["key"]]
+        got = oracle.philox4x32_10(ctr, key)[0]
+        assert [f"{int(x):08x}" for x in got] == kat["out"]
+
+
+def test_philox_normals_distribution():
+    """Box-Muller output is standard normal: moments, tail mass and the
+    normal CDF at a few points (a missing 2 pi, a wrong log argument or sqrt
+    factor moves one of them far outside the sampling error); independent
+    of the offset at which a range starts; the seed changes every value."""
+    from scipy.stats import norm
+    n = 2_000_000
+    z = oracle.philox_normals(0, n, seed=11)
+    assert abs(z.mean()) < 5 / math.sqrt(n)
+    assert abs(z.var() - 1.0) < 5 * math.sqrt(2.0 / n)
+    assert abs((z ** 4).mean() - 3.0) < 5 * math.sqrt(96.0 / n)
+    assert abs((z ** 3).mean()) < 5 * math.sqrt(15.0 / n)
+    for x in (-2.0, -0.5, 0.0, 0.7, 1.5):
+        frac = (z <= x).mean()
+        p = norm.cdf(x)
+        assert abs(frac - p) < 5 * math.sqrt(p * (1 - p) / n)
+    # pairs from one Box-Muller draw are uncorrelated
+    assert abs(np.corrcoef(z[0::4], z[1::4])[0, 1]) < 5 / math.sqrt(n / 4)
+    assert np.array_equal(oracle.philox_normals(13, 1000, 11), z[13:1013])
+    assert not np.any(oracle.philox_normals(0, 1000, 12) == z[:1000])
+    # 64-bit counters: the high word of the block index takes part
+    hi = oracle.philox_normals(4 << 32, 8, 11)
+    assert not np.allclose(hi, z[:8])
+
+
+@pytest.mark.parametrize("name", ["tiny", "gpt2_small", "chat_small"])
+def test_init_params_structure(name):
+    """N(0, 0.02) matrices and embeddings, padded vocabulary rows exactly 0,
+    gains 1, shifts and biases 0; the initial loss is near ln V."""
+    cfg = small_cfgs()[name]
+    p = oracle.init_params(cfg, seed=5)
+    P = oracle.unflatten(cfg, p, np.float32)
+    V = cfg["vocab_size"]
+    mats = []
+    for key, t in P.items():
+        if t.ndim == 2:
+            if key in ("wte", "lm_head.w"):
+                assert np.all(t[V:] == 0)
+                t = t[:V]
+            mats.append(t.reshape(-1))
+        elif key.endswith(("ln1.w", "ln2.w")) or key == "lnf.w":
+            assert np.all(t == 1)
+        else:
+            assert np.all(t == 0)
+    w = np.concatenate(mats).astype(np.float64)
+    assert abs(w.mean()) < 5 * 0.02 / math.sqrt(w.size)
+    assert abs(w.std() / 0.02 - 1) < 5 / math.sqrt(2 * w.size)
+    idx, tgt = synth.tokens(cfg, seed=1)
+    loss, _ = oracle.loss_and_grads(cfg, p, idx, tgt)
+    assert 0 <= loss - math.log(V) < 0.1
