@@ -29,11 +29,13 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 METRIC = "training tokens/sec on 1 GPU + MFU vs bf16 MFMA peak, GPT-2 124M shape"
 
 
-# Call sites that launch exactly one kernel (see gpt_site in include/gpt.h).
-# (lmhead_dx is split over K: a GEMM plus the fixed-order reduction.)
+# Call sites that launch exactly one kernel (see gpt_site in include/gpt.h):
+# each maps to one kernel specialisation in rocprofv3 traces.  (lmhead_dx is
+# split over K: a GEMM plus the fixed-order reduction; attn_bwd is two kernels;
+# ln_bwd, cross_entropy, embed_bwd and grad_norm include their reductions.)
 SINGLE_KERNEL_SITES = ["embed_fwd", "ln_fwd", "qkv_fwd", "attn_fwd", "proj_fwd", "fc_fwd",
                        "fcproj_fwd", "lmhead_fwd", "lmhead_dw", "fcproj_dx", "fc_dx",
-                       "proj_dx", "qkv_dx", "adamw"]
+                       "proj_dx", "qkv_dx", "adamw", "block_dw", "block_dw_reduce"]
 
 
 def load_traffic(site):
@@ -61,25 +63,23 @@ def cpu_baseline(cfg, min_seconds=10.0, max_steps=6):
     model, repeated on successive sequences until at least `min_seconds` of
     CPU work (at most `max_steps` steps) so the sample is not one short run."""
     import numpy as np
+    from threadpoolctl import threadpool_limits
     import oracle
     from decoder_only_gpt_amd import synth
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+    cores = len(os.sched_getaffinity(0))  # the host cores this process may use
     p = synth.init_params(cfg, seed=0)
     m = np.zeros_like(p)
     v = np.zeros_like(p)
     steps = 0
-    t0 = time.perf_counter()
-    while steps < max_steps and (steps == 0 or time.perf_counter() - t0 < min_seconds):
-        idx, tgt = synth.tokens(cfg, B=1, T=cfg["T"], seed=1 + steps)
-        r = oracle.step(cfg, p, m, v, idx, tgt, steps + 1, dtype=np.float32)
-        p, m, v = r["p"], r["m"], r["v"]
-        steps += 1
-    dt = time.perf_counter() - t0
-    return {"value": round(steps * cfg["T"] / dt, 2), "unit": "tokens/s", "cores": int(threads),
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        while steps < max_steps and (steps == 0 or time.perf_counter() - t0 < min_seconds):
+            idx, tgt = synth.tokens(cfg, B=1, T=cfg["T"], seed=1 + steps)
+            r = oracle.step(cfg, p, m, v, idx, tgt, steps + 1, dtype=np.float32)
+            p, m, v = r["p"], r["m"], r["v"]
+            steps += 1
+        dt = time.perf_counter() - t0
+    return {"value": round(steps * cfg["T"] / dt, 2), "unit": "tokens/s", "cores": int(cores),
             "kind": "oracle",
             "sample": f"{steps} steps of one sequence each (B=1, T={cfg['T']}) of the same model, "
                       f"full step (forward, backward, norm, AdamW) in float32 NumPy; {dt:.1f} s"}
@@ -228,8 +228,8 @@ def main():
     per_site = {k: {"ms_per_step": round(s["ms"] / args.profile_steps, 4),
                     "launches_per_step": s["launches"] // args.profile_steps}
                 for k, s in sstats.items() if s["launches"]}
-    # Dominant kernel: the call site with the most time among those that launch a
-    # single kernel (each maps to one kernel specialisation in rocprofv3 traces).
+    # Dominant kernel: the call site with the most time per step among those that
+    # launch a single kernel (rocprofv3's top kernel: the grouped weight gradients).
     single = [k for k in SINGLE_KERNEL_SITES if sstats[k]["launches"]]
     dom = max(single, key=lambda k: sstats[k]["ms"])
     ds = sstats[dom]

@@ -55,7 +55,9 @@ __global__ void __launch_bounds__(256) adamw_kernel(int64_t n, float* __restrict
                                                     float* __restrict__ m, float* __restrict__ v,
                                                     const float* __restrict__ g,
                                                     bf16_t* __restrict__ shadow, AdamScalars s,
-                                                    const float* __restrict__ d_scale) {
+                                                    const float* __restrict__ d_scale,
+                                                    Guard guard) {
+  if (guard_tripped(guard)) return;
   if (d_scale) {  // gradient scale from the device clip; NaN: non-finite norm, no update
     const float sc = *d_scale;
     if (sc != sc) return;
@@ -105,7 +107,8 @@ constexpr int ADAM_SEG_CHUNK = 256 * 8;
 __global__ void __launch_bounds__(256) adamw_segments_kernel(
     const int64_t* __restrict__ seg, int nseg, float* __restrict__ p, float* __restrict__ m,
     float* __restrict__ v, const float* __restrict__ g, bf16_t* __restrict__ shadow,
-    AdamScalars s) {
+    AdamScalars s, Guard guard) {
+  if (guard_tripped(guard)) return;
   int lo = 0, hi = nseg - 1;  // the last segment whose first block <= this block
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -132,14 +135,15 @@ __global__ void __launch_bounds__(256) adamw_segments_kernel(
 // arithmetic: norm = sqrt(sum g^2) / n_micro, c = max_norm / norm if
 // max_norm > 0 and norm > max_norm (else 1), grad_scale = c / n_micro.
 // out = {norm, grad_scale}; scale = (float) grad_scale, NaN if the norm is not
-// finite.
+// finite or the guard is tripped.
 __global__ void clip_scale_kernel(const double* __restrict__ norm2, int n_micro, double max_norm,
-                                  double* __restrict__ out, float* __restrict__ scale) {
+                                  double* __restrict__ out, float* __restrict__ scale,
+                                  Guard guard) {
   if (blockIdx.x != 0 || threadIdx.x != 0) return;
   const double norm = sqrt(*norm2) / (double)n_micro;
   const double c = (max_norm > 0.0 && norm > max_norm) ? max_norm / norm : 1.0;
   const double sc = c / (double)n_micro;
-  const bool finite = norm - norm == 0.0;
+  const bool finite = norm - norm == 0.0 && !guard_tripped(guard);
   out[0] = norm;
   out[1] = finite ? sc : __builtin_nan("");
   *scale = finite ? (float)sc : __builtin_nanf("");
@@ -148,8 +152,8 @@ __global__ void clip_scale_kernel(const double* __restrict__ norm2, int n_micro,
 }  // namespace
 
 hipError_t clip_scale(const double* norm2, int n_micro, double max_norm, double* out, float* scale,
-                      hipStream_t s) {
-  clip_scale_kernel<<<1, 64, 0, s>>>(norm2, n_micro, max_norm, out, scale);
+                      Guard guard, hipStream_t s) {
+  clip_scale_kernel<<<1, 64, 0, s>>>(norm2, n_micro, max_norm, out, scale, guard);
   return hipGetLastError();
 }
 
@@ -157,18 +161,19 @@ int adamw_segment_blocks(int64_t len) { return (int)cdiv(len, ADAM_SEG_CHUNK); }
 
 hipError_t adamw_segments(const int64_t* d_seg, int nseg, int blocks, float* p, float* m,
                           float* v, const float* g, uint16_t* shadow, AdamScalars sc,
-                          hipStream_t s) {
+                          Guard guard, hipStream_t s) {
   if (nseg <= 0 || blocks <= 0) return hipSuccess;
-  adamw_segments_kernel<<<(unsigned)blocks, 256, 0, s>>>(d_seg, nseg, p, m, v, g, shadow, sc);
+  adamw_segments_kernel<<<(unsigned)blocks, 256, 0, s>>>(d_seg, nseg, p, m, v, g, shadow, sc,
+                                                         guard);
   return hipGetLastError();
 }
 
 hipError_t adamw(int64_t n, float* p, float* m, float* v, const float* g, uint16_t* shadow,
-                 AdamScalars sc, hipStream_t s, const float* d_scale) {
+                 AdamScalars sc, hipStream_t s, const float* d_scale, Guard guard) {
   if (n <= 0) return hipSuccess;
   int64_t blocks = cdiv(cdiv(n, 8), 256);
   if (blocks > 8192) blocks = 8192;
-  adamw_kernel<<<(unsigned)blocks, 256, 0, s>>>(n, p, m, v, g, shadow, sc, d_scale);
+  adamw_kernel<<<(unsigned)blocks, 256, 0, s>>>(n, p, m, v, g, shadow, sc, d_scale, guard);
   return hipGetLastError();
 }
 

@@ -138,4 +138,23 @@ __device__ __forceinline__ double warp_sum_d(double v) {
 
 inline long cdiv(long a, long b) { return (a + b - 1) / b; }
 
+// Token-id guard.  A forward that meets a token id or target outside
+// [0, vocab_size) reads a clamped id (0) instead, so no kernel indexes out of
+// bounds, and stores its forward count (gen >= 1) at *flag.  Update kernels
+// given a Guard skip their writes when the flag holds a forward count >=
+// gen_lo (a forward since the last update saw a bad id).  flag == NULL: off.
+struct Guard {
+  const int32_t* flag;
+  int32_t gen_lo;
+};
+__device__ __forceinline__ bool guard_tripped(const Guard& g) {
+  return g.flag != nullptr && *(volatile const int32_t*)g.flag >= g.gen_lo;
+}
+// id if 0 <= id < n, else 0 with *flag = gen (flag may be NULL).
+__device__ __forceinline__ int checked_id(int id, int n, int32_t* flag, int32_t gen) {
+  if ((unsigned)id < (unsigned)n) return id;
+  if (flag) *(volatile int32_t*)flag = gen;
+  return 0;
+}
+
 }  // namespace gpt

@@ -27,9 +27,9 @@ namespace {
 __global__ void __launch_bounds__(256) gen_embed_kernel(const int32_t* __restrict__ tok,
                                                         const float* __restrict__ wte,
                                                         const float* __restrict__ wpe, int pos,
-                                                        int C, float* __restrict__ x) {
+                                                        int C, int V, float* __restrict__ x) {
   const int b = blockIdx.x;
-  const long t = tok[b];
+  const long t = checked_id(tok[b], V, nullptr, 0);  // out-of-range ids read row 0
   for (int c = threadIdx.x * 4; c < C; c += 256 * 4) {  // C % 64 == 0
     const float4 e = *(const float4*)(wte + t * C + c);
     const float4 p = *(const float4*)(wpe + (long)pos * C + c);
@@ -541,8 +541,8 @@ __global__ void copy_prompt_kernel(const int32_t* __restrict__ prompt, int T0, i
 }  // namespace
 
 hipError_t gen_embed(const int32_t* tok, const float* wte, const float* wpe, int pos, int B, int C,
-                     float* x, hipStream_t s) {
-  gen_embed_kernel<<<B, 256, 0, s>>>(tok, wte, wpe, pos, C, x);
+                     int V, float* x, hipStream_t s) {
+  gen_embed_kernel<<<B, 256, 0, s>>>(tok, wte, wpe, pos, C, V, x);
   return hipGetLastError();
 }
 

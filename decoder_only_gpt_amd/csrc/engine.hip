@@ -134,6 +134,7 @@ struct Arena {
   int64_t gemm_ws, gemm_ws_bytes, cs_part, ln_part, n_part, norm2, clip, muon_ws, adam_seg;
   int64_t e_counts, e_offsets, e_tile_sums, e_rank, e_perm, e_carry_first, e_carry_last, e_flags,
       e_last_tok;
+  int64_t ids, id_flag;  // token ids the forward used; forward count of the last bad id
   int64_t state_end, total;
 };
 
@@ -205,6 +206,8 @@ Arena plan_arena(const gpt_config& c, int B, int T) {
   a.e_carry_last = take(nch * C * 4);
   a.e_flags = take(nch * 4);
   a.e_last_tok = take(nch * 4);
+  a.ids = take(M * 4);
+  a.id_flag = take(16);
   a.n_part = take(1024 * 8);
   a.norm2 = take(16);
   a.clip = take(32);  // device clip: {norm, grad_scale} doubles, then grad_scale as float
@@ -245,7 +248,13 @@ struct gpt_model {
     return ev_pool[ev_used++];
   }
   bool loss_valid;
-  const int32_t* last_idx;
+  // Token-id guard: forwards are counted from 1 (gen); a forward that meets an
+  // id or target outside [0, vocab_size) writes its count to the id flag.
+  // upd_gen is the count at the last parameter update, so a flag > upd_gen
+  // means a bad id since then.
+  int32_t gen = 0, upd_gen = 0;
+  int32_t* id_flag() const { return at<int32_t>(ar.id_flag); }
+  gpt::Guard guard() const { return gpt::Guard{id_flag(), upd_gen + 1}; }
   // Weight-gradient branch of the backward: a second stream (default
   // priority) and the events that order it against the main chain.
   hipStream_t side = nullptr;
@@ -401,8 +410,10 @@ int run_forward(gpt_model* m, const int32_t* idx, const int32_t* tgt, hipStream_
   auto act = [&](int64_t off) { return m->at<char>(off); };
   int rc = wait_adam(m, s, 0);
   if (rc != GPT_OK) return rc;
+  const int32_t gen = ++m->gen;
   LAUNCH(GPT_K_EMBED, GPT_S_EMBED_FWD, 0, 12.0 * M * C,
-         gpt::embed_fwd(prec, idx, m->P(m->pl.wte), m->P(m->pl.wpe), (int)M, m->T, (int)C, m->X(0), s));
+         gpt::embed_fwd(prec, idx, m->P(m->pl.wte), m->P(m->pl.wpe), (int)M, m->T, (int)C,
+                        c.vocab_size, m->X(0), m->at<int32_t>(m->ar.ids), m->id_flag(), gen, s));
   for (int l = 0; l < c.n_layer; ++l) {
     const LayerOff& L = m->pl.layer[l];
     if ((rc = wait_adam(m, s, 1 + l)) != GPT_OK) return rc;
@@ -450,9 +461,10 @@ int run_forward(gpt_model* m, const int32_t* idx, const int32_t* tgt, hipStream_
   if (tgt) {
     LAUNCH(GPT_K_CROSS_ENTROPY, GPT_S_CROSS_ENTROPY, 0, 2.0 * M * m->Vq * act_b + 8.0 * M,
            gpt::cross_entropy(prec, act(m->ar.logits), (int)M, c.vocab_size, (int)m->Vq, tgt,
-                              m->at<float>(m->ar.loss_rows), s));
+                              m->at<float>(m->ar.loss_rows), m->id_flag(), gen, s));
     LAUNCH(GPT_K_CROSS_ENTROPY, GPT_S_CROSS_ENTROPY, 0, 4.0 * M,
-           gpt::mean_loss(m->at<float>(m->ar.loss_rows), (int)M, m->at<float>(m->ar.loss), s));
+           gpt::mean_loss(m->at<float>(m->ar.loss_rows), (int)M, m->at<float>(m->ar.loss),
+                          m->id_flag(), gen, s));
   }
   return GPT_OK;
 }
@@ -507,7 +519,9 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
     double fl = 0;
     for (int i = 0; i < n; ++i) fl += 2.0 * dd[i].M * dd[i].N * dd[i].K;
     hipStream_t s = st;
-    LAUNCH(GPT_K_GEMM_SPLITK, site, fl, 0, gpt::gemm_group(dd, n, s, db));
+    // The products and their fixed-order reduction are timed as separate sites.
+    LAUNCH(GPT_K_GEMM_SPLITK, site, fl, 0, gpt::gemm_group(dd, n, s, db, 1));
+    LAUNCH(GPT_K_GEMM_SPLITK, GPT_S_BLOCK_DW_REDUCE, 0, 0, gpt::gemm_group(dd, n, s, db, 2));
     return GPT_OK;
   };
   auto bias_grad = [&](const char* x, int64_t n, int64_t off) -> int {
@@ -629,7 +643,8 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
                            m->at<int32_t>(m->ar.e_flags),    m->at<int32_t>(m->ar.e_last_tok)};
   const int wte_acc = (c.tied_lm_head || acc) ? 1 : 0;
   LAUNCH(GPT_K_EMBED, GPT_S_EMBED_BWD, 0, 4.0 * M * C + 4.0 * (m->Vp + c.block_size) * C,
-         gpt::embed_bwd(m->last_idx, gres[cur], (int)M, m->T, (int)C, (int)m->Vp, c.block_size,
+         gpt::embed_bwd(m->at<int32_t>(m->ar.ids), gres[cur], (int)M, m->T, (int)C, (int)m->Vp,
+                        c.block_size,
                         m->G(m->pl.wte), wte_acc, m->G(m->pl.wpe), acc, scr, s));
   // Every gradient is complete before anything after the backward runs.
   if (s2 != s) {
@@ -705,7 +720,7 @@ int gpt_plan(const gpt_config* cfg, int32_t B, int32_t T, gpt_sizes* out) {
 }
 
 int gpt_init(const gpt_config* cfg, int32_t B, int32_t T, void* d_arena, int64_t arena_bytes,
-             void* stream, gpt_model** out) {
+             uint64_t seed, void* stream, gpt_model** out) {
   int rc = check_config(cfg, B, T);
   if (rc != GPT_OK) return rc;
   if (!out || !d_arena) return fail(GPT_E_INVALID, "NULL arena or out");
@@ -731,7 +746,6 @@ int gpt_init(const gpt_config* cfg, int32_t B, int32_t T, void* d_arena, int64_t
   m->base = (char*)d_arena;
   m->state = 0;
   m->loss_valid = false;
-  m->last_idx = nullptr;
   hipStream_t s = (hipStream_t)stream;
   hipError_t se = hipStreamCreateWithFlags(&m->side, hipStreamNonBlocking);
   if (se == hipSuccess) se = hipEventCreateWithFlags(&m->ev_fork, hipEventDisableTiming);
@@ -754,6 +768,35 @@ int gpt_init(const gpt_config* cfg, int32_t B, int32_t T, void* d_arena, int64_t
   if (e != hipSuccess) {
     gpt_destroy(m);
     return fail(GPT_E_HIP, std::string("hipMemsetAsync: ") + hipGetErrorString(e));
+  }
+  // Seeded weights: matrices and embeddings N(0, 0.02) with the padded
+  // vocabulary rows 0, LayerNorm gains 1 (shifts and biases stay 0).
+  {
+    const ParamLayout& pl = m->pl;
+    const int64_t C = m->C, V = cfg->vocab_size;
+    float* P0 = m->P(0);
+    auto normal = [&](int64_t off, int64_t n, int64_t n_normal) {
+      return gpt::init_normal(P0 + off, off, n, n_normal, 0.02, seed, s);
+    };
+    std::vector<std::pair<int64_t, int64_t>> gains = {{pl.lnfw, C}};
+    e = normal(pl.wte, m->Vp * C, V * C);
+    if (e == hipSuccess) e = normal(pl.wpe, (int64_t)cfg->block_size * C, (int64_t)cfg->block_size * C);
+    for (int l = 0; l < cfg->n_layer && e == hipSuccess; ++l) {
+      const LayerOff& L = pl.layer[l];
+      gains.push_back({L.ln1w, C});
+      gains.push_back({L.ln2w, C});
+      for (auto w : {std::pair<int64_t, int64_t>{L.qkvw, 3 * C * C}, {L.projw, C * C},
+                     {L.fcw, m->F * C}, {L.fcpw, C * m->F}})
+        if (e == hipSuccess) e = normal(w.first, w.second, w.second);
+    }
+    if (e == hipSuccess && !cfg->tied_lm_head) e = normal(pl.lmw, m->Vp * C, V * C);
+    for (auto gn : gains)
+      if (e == hipSuccess) e = gpt::fill_value(P0 + gn.first, gn.second, 1.f, s);
+    if (e == hipSuccess && m->bf16) e = gpt::to_bf16(P0, m->N, m->at<uint16_t>(a.shadow), s);
+    if (e != hipSuccess) {
+      gpt_destroy(m);
+      return fail(GPT_E_HIP, std::string("parameter init: ") + hipGetErrorString(e));
+    }
   }
   {
     std::vector<std::pair<int64_t, int64_t>> mr;
@@ -899,7 +942,8 @@ int gen_step(gpt_gen* g, const int32_t* d_tok, hipStream_t s) {
   float* mean = (float*)(base + g->mean);
   float* rstd = (float*)(base + g->rstd);
   const int64_t cache_layer = (int64_t)B * m->H * g->Tmax * m->hd * act;
-  HIP_TRY(gpt::gen_embed(d_tok, m->P(m->pl.wte), m->P(m->pl.wpe), g->pos, B, (int)C, x, s));
+  HIP_TRY(gpt::gen_embed(d_tok, m->P(m->pl.wte), m->P(m->pl.wpe), g->pos, B, (int)C,
+                         m->cfg.vocab_size, x, s));
   for (int l = 0; l < c.n_layer; ++l) {
     const LayerOff& L = m->pl.layer[l];
     HIP_TRY(gen_linear(g, a, C, L.qkvw, 3 * C, L.qkvb, GPT_EPI_STORE, base + g->qkv, 3 * C,
@@ -1047,7 +1091,6 @@ int gpt_forward(gpt_model* m, const int32_t* d_idx, const int32_t* d_tgt, void* 
   if (!m || !d_idx) return fail(GPT_E_INVALID, "NULL model or idx");
   int rc = run_forward(m, d_idx, d_tgt, (hipStream_t)stream);
   if (rc != GPT_OK) return rc;
-  m->last_idx = d_idx;
   if (d_tgt) {
     m->state = 1;
     m->loss_valid = true;
@@ -1062,8 +1105,12 @@ int gpt_loss(gpt_model* m, void* stream, float* h_mean_loss) {
   if (!m || !h_mean_loss) return fail(GPT_E_INVALID, "NULL argument");
   if (!m->loss_valid) return fail(GPT_E_STATE, "no forward with targets since the last update");
   hipStream_t s = (hipStream_t)stream;
+  int32_t flag = 0;
   HIP_TRY(hipMemcpyAsync(h_mean_loss, m->at<float>(m->ar.loss), 4, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipMemcpyAsync(&flag, m->id_flag(), 4, hipMemcpyDeviceToHost, s));
   HIP_TRY(hipStreamSynchronize(s));
+  if (flag == m->gen)
+    return fail(GPT_E_INVALID, "a token id or target of the last forward is outside [0, vocab_size)");
   return GPT_OK;
 }
 
@@ -1090,9 +1137,13 @@ int gpt_grad_norm(gpt_model* m, void* stream, double* h_norm) {
   LAUNCH(GPT_K_NORM, GPT_S_GRAD_NORM, 0, 4.0 * m->N,
          gpt::sumsq(m->G(0), m->N, m->at<double>(m->ar.n_part), m->at<double>(m->ar.norm2), s));
   double n2 = 0.0;
+  int32_t flag = 0;
   HIP_TRY(hipMemcpyAsync(&n2, m->at<double>(m->ar.norm2), 8, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipMemcpyAsync(&flag, m->id_flag(), 4, hipMemcpyDeviceToHost, s));
   HIP_TRY(hipStreamSynchronize(s));
   *h_norm = std::sqrt(n2);
+  if (flag > m->upd_gen)
+    return fail(GPT_E_INVALID, "a forward since the last update met a token id outside [0, vocab_size)");
   if (!std::isfinite(*h_norm)) return fail(GPT_E_NONFINITE, "gradient norm is not finite");
   return GPT_OK;
 }
@@ -1109,7 +1160,7 @@ int gpt_adamw_step(gpt_model* m, const gpt_adamw_hp* hp, void* stream) {
   const gpt::AdamScalars sc = adam_scalars(*hp);
   if (m->prof_on) {  // timed alone, in one launch
     LAUNCH(GPT_K_ADAMW, GPT_S_ADAMW, 0, (m->bf16 ? 30.0 : 28.0) * m->N,
-           gpt::adamw(m->N, m->P(0), pm, pv, m->G(0), sh, sc, s));
+           gpt::adamw(m->N, m->P(0), pm, pv, m->G(0), sh, sc, s, nullptr, m->guard()));
   } else {
     // On the side stream, group by group; the next forward waits for each
     // group just before it uses those parameters.
@@ -1119,13 +1170,14 @@ int gpt_adamw_step(gpt_model* m, const gpt_adamw_hp* hp, void* stream) {
       int64_t b, e;
       adam_group(m, g, &b, &e);
       HIP_TRY(gpt::adamw(e - b, m->P(b), pm + b, pv + b, m->G(b), sh ? sh + b : nullptr, sc,
-                         m->side));
+                         m->side, nullptr, m->guard()));
       HIP_TRY(hipEventRecord(m->ev_adam[g], m->side));
     }
     m->adam_pending = true;
   }
   m->state = 0;
   m->loss_valid = false;
+  m->upd_gen = m->gen;
   return GPT_OK;
 }
 
@@ -1142,7 +1194,8 @@ int gpt_adamw_step_clipped(gpt_model* m, const gpt_adamw_hp* hp, int32_t n_micro
   float* d_scale = (float*)(clip + 2);
   LAUNCH(GPT_K_NORM, GPT_S_GRAD_NORM, 0, 4.0 * m->N,
          gpt::sumsq(m->G(0), m->N, m->at<double>(m->ar.n_part), m->at<double>(m->ar.norm2), s));
-  HIP_TRY(gpt::clip_scale(m->at<double>(m->ar.norm2), n_micro, max_norm, clip, d_scale, s));
+  HIP_TRY(gpt::clip_scale(m->at<double>(m->ar.norm2), n_micro, max_norm, clip, d_scale,
+                          m->guard(), s));
   if (h_norm_scale)
     HIP_TRY(hipMemcpyAsync(h_norm_scale, clip, 16, hipMemcpyDeviceToHost, s));
   float* pm = m->at<float>(m->ar.adam_m);
@@ -1166,6 +1219,7 @@ int gpt_adamw_step_clipped(gpt_model* m, const gpt_adamw_hp* hp, int32_t n_micro
   }
   m->state = 0;
   m->loss_valid = false;
+  m->upd_gen = m->gen;
   return GPT_OK;
 }
 
@@ -1198,7 +1252,7 @@ int gpt_muon_step(gpt_model* m, const gpt_adamw_hp* adam, const gpt_muon_hp* muo
   // AdamW on the runs of the flat vector between the Muon matrices, one launch.
   HIP_TRY(gpt::adamw_segments(m->at<int64_t>(m->ar.adam_seg), (int)(m->adam_seg.size() / 3),
                               m->adam_seg_blocks, m->P(0), pm, pv, m->G(0), sh,
-                              adam_scalars(*adam), s));
+                              adam_scalars(*adam), m->guard(), s));
   gpt::MuonScalars ms;
   ms.grad_scale = (float)adam->grad_scale;
   ms.mu = (float)muon->momentum;
@@ -1222,10 +1276,11 @@ int gpt_muon_step(gpt_model* m, const gpt_adamw_hp* adam, const gpt_muon_hp* muo
     g.rows = k.rows;
     g.cols = k.cols;
     g.count = m->cfg.n_layer;
-    HIP_TRY(gpt::muon_matrices(g, ms, m->prec(), m->at<void>(m->ar.muon_ws), s));
+    HIP_TRY(gpt::muon_matrices(g, ms, m->prec(), m->at<void>(m->ar.muon_ws), m->guard(), s));
   }
   m->state = 0;
   m->loss_valid = false;
+  m->upd_gen = m->gen;
   return GPT_OK;
 }
 

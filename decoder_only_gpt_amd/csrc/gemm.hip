@@ -7,13 +7,18 @@
 //   backward dx = dy W             A = dy [M,K]            B = W stored [K,N]
 //   backward dW = dy^T x           A = dy stored [K,M]     B = x stored [K,N]
 //
-// bf16 path: CDNA4 MFMA (v_mfma_f32_32x32x16_bf16), 128x128 output tile per
-// 256-thread workgroup (2x2 waves of 64x64), K staged through LDS in 64-wide
-// slices with double buffering.  Operands stored K-major are transposed in
-// registers (4x8 blocks) on their way into LDS so every MFMA fragment is one
-// 16-byte LDS read.  Long-K products (the weight gradients, K = B*T) are split
-// over K into float partial tiles that a second kernel sums in a fixed order,
-// so results are bitwise reproducible.
+// bf16 path: CDNA4 MFMA (v_mfma_f32_32x32x16_bf16) with float accumulation.
+// Output tiles of 256 x 256 (8 waves of 128 x 64, one workgroup per CU),
+// 256 x 192 (8 waves of 64 x 96; N = 768 products) or 128 x 128 (4 waves of
+// 64 x 64, two workgroups per CU).  K is staged through LDS in 64-deep slices,
+// two stages, fetched straight from memory into LDS by buffer_load ... lds
+// (no register staging): row-major tiles land with their 16-byte chunks XOR-
+// swizzled per row, K-major tiles land untransposed and their MFMA fragments
+// are read with the LDS transpose read (ds_read_b64_tr_b16).  An operand that
+// takes GELU as it is read goes through registers instead (gemm_mfma_kernel).
+// Long-K products (the weight gradients, K = B*T) are split over K into float
+// partial tiles that a second kernel sums in a fixed order, so results are
+// bitwise reproducible.
 // fp32 path: a plain LDS-tiled FMA kernel (correctness path; small shapes).
 
 #include "common.h"
@@ -752,13 +757,8 @@ MfmaKernel dma_kernel_for(int at, int bt, int epi, int ga, int gb) {
 }
 
 // ----------------------------------------------------------------------------
-// bf16 MFMA, large tile: 256 x 256 per workgroup, 4 waves of 128 x 128 (4 x 4
-// blocks of 32 x 32), BK = 64, two LDS stages of 64 KB filled by direct
-// buffer loads.  Each k-step a wave reads 8 fragments for 16 MFMAs (half the
-// LDS traffic per FLOP of the 128-tile kernel).  The MFMA operands are swapped
-// (D = B-frag x A-frag), so each lane owns one output row and 4 consecutive
-// output columns per 4 accumulator registers: the epilogue stores 8- or
-// 16-byte vectors straight from the accumulators.
+// bf16 MFMA, large tiles (256 rows): LDS layouts and fragment reads shared by
+// the 256 x 256 and 256 x 192 kernels below.
 // ----------------------------------------------------------------------------
 constexpr int BIG = 256;
 
@@ -767,31 +767,6 @@ __device__ __forceinline__ int big_off(int row, int chunk) {  // row-major tile 
 }
 __device__ __forceinline__ int big_off_t(int k, int r) {  // K-major tile [BK][256]
   return k * BIG + (r ^ ((k & 3) << 5));
-}
-
-template <int TRANS, bool ASM = false>
-__device__ __forceinline__ void dma_tile256(__amdgpu_buffer_rsrc_t rs, const OpArgs& a, int r0,
-                                            int k0, bf16_t* lds, int wave, int lane) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int blk = wave * 8 + i;  // 1 KB block of the 32 KB tile
-    int r, k;
-    if constexpr (TRANS == 0) {  // block = 8 rows x 8 chunks
-      const int row = blk * 8 + (lane >> 3), phys = lane & 7;
-      const int chunk = phys ^ (row & 7) ^ ((row >> 3) & 1);
-      r = r0 + row;
-      k = k0 + chunk * 8;
-    } else {  // block = 2 k-rows x 32 chunks
-      const int kk = blk * 2 + (lane >> 5), phys = lane & 31;
-      const int chunk = phys ^ ((kk & 3) << 2);
-      k = k0 + kk;
-      r = r0 + chunk * 8;
-    }
-    const bool ok = r < a.rows && k < a.kvalid;
-    const long e = TRANS ? (long)k * a.ld + r : (long)r * a.ld + k;
-    const unsigned off = ok ? (unsigned)(e * 2) : 0x80000000u;
-    dma16<ASM>(rs, lds + blk * 512, off);
-  }
 }
 
 template <int TRANS>
@@ -808,174 +783,6 @@ __device__ __forceinline__ bf16x8 big_frag(const bf16_t* lds, int r0, int ks, in
     typedef short v8i16 __attribute__((ext_vector_type(8)));
     v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     return *(bf16x8*)&v;
-  }
-}
-
-// Epilogue on 4 consecutive columns n..n+3 of row m (n + 4 <= N).
-template <int EPI>
-__device__ __forceinline__ void epilogue4(const EpiArgs& e, float* partial, int m, int n, float4 v) {
-  const long o = (long)m * e.ldo + n;
-  if constexpr (EPI == EPI_PARTIAL) {
-    *(float4*)(partial + (long)m * e.N + n) = v;
-    return;
-  }
-  if constexpr (EPI == GPT_EPI_STORE || EPI == GPT_EPI_RESIDUAL || EPI == GPT_EPI_GELU) {
-    if (e.bias) {
-      float4 b = *(const float4*)(e.bias + n);
-      v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
-    }
-  }
-  if constexpr (EPI == GPT_EPI_STORE || EPI == GPT_EPI_GELU) {
-    const uint2 w = make_uint2(pack_bf2(v.x, v.y), pack_bf2(v.z, v.w));
-    *(uint2*)((bf16_t*)e.out + o) = w;
-    if constexpr (EPI == GPT_EPI_GELU) {
-      if (e.aux)  // GELU of the stored (rounded) pre-activation
-        *(uint2*)((bf16_t*)e.aux + (long)m * e.ldaux + n) =
-            make_uint2(gelu2(w.x, e.tanh_form), gelu2(w.y, e.tanh_form));
-    }
-  } else if constexpr (EPI == GPT_EPI_DGELU) {
-    const uint2 u = *(const uint2*)((const bf16_t*)e.aux + (long)m * e.ldaux + n);
-    v.x *= gelu_grad_fast(bf_lo(u.x), e.tanh_form);
-    v.y *= gelu_grad_fast(bf_hi(u.x), e.tanh_form);
-    v.z *= gelu_grad_fast(bf_lo(u.y), e.tanh_form);
-    v.w *= gelu_grad_fast(bf_hi(u.y), e.tanh_form);
-    *(uint2*)((bf16_t*)e.out + o) = make_uint2(pack_bf2(v.x, v.y), pack_bf2(v.z, v.w));
-  } else if constexpr (EPI == GPT_EPI_MUL) {
-    const uint2 a = *(const uint2*)((const bf16_t*)e.aux + (long)m * e.ldaux + n);
-    *(uint2*)((bf16_t*)e.out + o) = make_uint2(pack_bf2(v.x * bf_lo(a.x), v.y * bf_hi(a.x)),
-                                               pack_bf2(v.z * bf_lo(a.y), v.w * bf_hi(a.y)));
-  } else if constexpr (EPI == GPT_EPI_AXPBY) {
-    const uint2 a = *(const uint2*)((const bf16_t*)e.aux + (long)m * e.ldaux + n);
-    const float al = e.alpha, be = e.beta;
-    *(uint2*)((bf16_t*)e.out + o) =
-        make_uint2(pack_bf2(al * v.x + be * bf_lo(a.x), al * v.y + be * bf_hi(a.x)),
-                   pack_bf2(al * v.z + be * bf_lo(a.y), al * v.w + be * bf_hi(a.y)));
-  } else if constexpr (EPI == GPT_EPI_GELU_PAIR) {
-    if (e.bias) {
-      const float4 b = *(const float4*)(e.bias + n);
-      v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
-    }
-    const uint2 w = make_uint2(pack_bf2(v.x, v.y), pack_bf2(v.z, v.w));
-    float g0, g1, g2, g3, p0, p1, p2, p3;
-    gelu_pair_fast(bf_lo(w.x), e.tanh_form, g0, p0);
-    gelu_pair_fast(bf_hi(w.x), e.tanh_form, g1, p1);
-    gelu_pair_fast(bf_lo(w.y), e.tanh_form, g2, p2);
-    gelu_pair_fast(bf_hi(w.y), e.tanh_form, g3, p3);
-    *(uint2*)((bf16_t*)e.out + o) = make_uint2(pack_bf2(p0, p1), pack_bf2(p2, p3));
-    *(uint2*)((bf16_t*)e.aux + (long)m * e.ldaux + n) =
-        make_uint2(pack_bf2(g0, g1), pack_bf2(g2, g3));
-  } else if constexpr (EPI == GPT_EPI_RESIDUAL) {
-    const float4 r = *(const float4*)(e.resid + o);
-    *(float4*)((float*)e.out + o) = make_float4(r.x + v.x, r.y + v.y, r.z + v.z, r.w + v.w);
-  } else if constexpr (EPI == GPT_EPI_F32) {
-    *(float4*)((float*)e.out + o) = v;
-  } else if constexpr (EPI == GPT_EPI_F32_ACCUM) {
-    float4* p = (float4*)((float*)e.out + o);
-    const float4 a = *p;
-    *p = make_float4(a.x + v.x, a.y + v.y, a.z + v.z, a.w + v.w);
-  }
-}
-
-
-template <int AT, int BT, int EPI>
-__global__ void __launch_bounds__(256, 1) gemm_big_kernel(OpArgs A, OpArgs B, int K, int kchunk,
-                                                          EpiArgs e, float* partial) {
-  // One 128 KB block: two stages of A and B tiles, later the epilogue slices.
-  __shared__ __attribute__((aligned(16))) bf16_t smem[4 * BIG * BK];
-  bf16_t* const sA0 = smem;
-  bf16_t* const sB0 = smem + BIG * BK;
-  bf16_t* const sA1 = smem + 2 * BIG * BK;
-  bf16_t* const sB1 = smem + 3 * BIG * BK;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  int tx, ty, tz;
-  xcd_tile(tx, ty, tz);
-  if (e.batch > 1) {  // tz indexes the matrix of a batch (never split over K)
-    batch_select(tz, A, B, e);
-    tz = 0;
-  }
-  const int m0 = ty * BIG, n0 = tx * BIG;
-  const int kbeg = tz * kchunk;
-  if (EPI == EPI_PARTIAL) partial += (long)tz * e.M * e.N;
-  const int kend = min(K, kbeg + kchunk);
-  const int nk = (kend - kbeg + BK - 1) / BK;
-
-  OpArgs a = A, b = B;
-  a.kvalid = min(a.kvalid, kend);
-  b.kvalid = min(b.kvalid, kend);
-  const long a_extent = AT ? (long)a.kvalid * a.ld : (long)a.rows * a.ld;
-  const long b_extent = BT ? (long)b.kvalid * b.ld : (long)b.rows * b.ld;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.X, a_extent * 2);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(b.X, b_extent * 2);
-
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  dma_tile256<AT, (AT || BT)>(ra, a, m0, kbeg, sA0, wave, lane);
-  dma_tile256<BT, (AT || BT)>(rb, b, n0, kbeg, sB0, wave, lane);
-  for (int kt = 0; kt < nk; ++kt) {
-    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's loads of tile kt landed
-    __syncthreads();                     // ... and every other wave's
-    const bool odd = kt & 1;
-    if (kt + 1 < nk) {
-      const int k1 = kbeg + (kt + 1) * BK;
-      dma_tile256<AT, (AT || BT)>(ra, a, m0, k1, odd ? sA0 : sA1, wave, lane);
-      dma_tile256<BT, (AT || BT)>(rb, b, n0, k1, odd ? sB0 : sB1, wave, lane);
-    }
-    const bf16_t* as = odd ? sA1 : sA0;
-    const bf16_t* bs = odd ? sB1 : sB0;
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[4], bf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = big_frag<AT>(as, wm * 128 + i * 32, ks, lane);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bf[j] = big_frag<BT>(bs, wn * 128 + j * 32, ks, lane);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
-    }
-  }
-
-  // Epilogue, one 32-row block of the wave's 128 x 128 tile at a time:
-  // accumulators -> this wave's 16 KB LDS slice as floats [32][CP] (plain
-  // float4 stores), then a rolled loop applies the epilogue to 8 consecutive
-  // columns per lane and stores vectors.  acc[i][j] = D[n][m]: lane column
-  // m = lane % 32, register r holds n = 8 (r / 4) + 4 (lane / 32) + r % 4.
-  constexpr int CP = 132;  // padded row pitch (floats)
-  __syncthreads();         // every wave is done reading the operand tiles
-  float* Cw = (float*)smem + wave * (32 * CP);  // 4 slices of 16.5 KB (66 KB of the 128 KB)
-  const int m_l = lane & 31, nq = 4 * (lane >> 5);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *(float4*)(Cw + m_l * CP + j * 32 + 8 * q + nq) =
-            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                        acc[i][j][4 * q + 3]);
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
-    const int cg = lane & 15;
-    const int n = n0 + wn * 128 + cg * 8;
-#pragma unroll 1
-    for (int p = 0; p < 8; ++p) {
-      const int row = p * 4 + (lane >> 4);
-      const int m = m0 + wm * 128 + i * 32 + row;
-      if (m < e.M && n < e.N) {
-        const float4 v0 = *(const float4*)(Cw + row * CP + cg * 8);
-        const float4 v1 = *(const float4*)(Cw + row * CP + cg * 8 + 4);
-        epilogue8<EPI>(e, partial, m, n, v0, v1);
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next block overwrites
   }
 }
 
@@ -1412,31 +1219,8 @@ MfmaKernel big8_kernel_for(int at, int bt, int epi, int ga, int gb) {
   K_(0, 0, GPT_EPI_GELU)
   K_(0, 0, GPT_EPI_GELU_PAIR)
   K_(0, 0, GPT_EPI_F32)
-  K_(0, 1, GPT_EPI_STORE)
-  K_(0, 1, GPT_EPI_DGELU)
-  K_(0, 1, GPT_EPI_MUL)
-  K_(0, 1, EPI_PARTIAL)
-  K_(0, 0, GPT_EPI_AXPBY)
-  K_(0, 1, GPT_EPI_AXPBY)
-  K_(1, 1, GPT_EPI_STORE)
-  K_(1, 1, GPT_EPI_F32)
-  K_(1, 1, GPT_EPI_F32_ACCUM)
-  K_(1, 1, EPI_PARTIAL)
-#undef K_
-  return nullptr;
-}
-
-MfmaKernel big_kernel_for(int at, int bt, int epi, int ga, int gb) {
-  if (ga || gb) return nullptr;
-#define K_(AT, BT, EP) \
-  if (at == AT && bt == BT && epi == EP) return gemm_big_kernel<AT, BT, EP>;
-  K_(0, 0, GPT_EPI_STORE)
-  K_(0, 0, GPT_EPI_RESIDUAL)
-  K_(0, 0, GPT_EPI_GELU)
-  K_(0, 0, GPT_EPI_DGELU)
-  K_(0, 0, GPT_EPI_GELU_PAIR)
-  K_(0, 0, GPT_EPI_F32)
   K_(0, 0, GPT_EPI_F32_ACCUM)
+  K_(0, 0, GPT_EPI_DGELU)
   K_(0, 1, GPT_EPI_STORE)
   K_(0, 1, GPT_EPI_DGELU)
   K_(0, 1, GPT_EPI_MUL)
@@ -1469,21 +1253,6 @@ struct GemmPlan {
   bool wide;  // 256 x 192 tiles (unsplit)
 };
 
-// Tuning switch: GPT_GEMM_BIG4=1 runs the 4-wave large-tile kernel instead.
-bool big8_disabled() {
-  static bool v = getenv("GPT_GEMM_BIG4") != nullptr;
-  return v;
-}
-
-// Tile override for tuning: GPT_GEMM_TILE=128 or 256 (unset: automatic).
-int tile_override() {
-  static int v = [] {
-    const char* e = getenv("GPT_GEMM_TILE");
-    return e ? atoi(e) : 0;
-  }();
-  return v;
-}
-
 GemmPlan plan_gemm(int M, int N, int K, int precision, bool splittable, int64_t ws_bytes,
                    bool big_ok, int batch = 1, bool wide_ok = false) {
   GemmPlan p{false, 1, false};
@@ -1507,13 +1276,12 @@ GemmPlan plan_gemm(int M, int N, int K, int precision, bool splittable, int64_t 
     }
   }
   const long t256 = cdiv(M, BIG) * cdiv(N, BIG) * batch;
-  const int force = tile_override();
   // 256 x 192 tiles where that grid fills whole rounds of the 256 CUs and the
   // square grids do not (N = 768: 256 tiles against 192 of 256 x 256 and 1.5
   // rounds of 128 x 128; QKV forward: 3 rounds).  Not for products that may be
   // split over K (the vocabulary input gradient is 4% faster split 4 ways on
   // 256-tiles than unsplit here).
-  if (wide_ok && !splittable && batch == 1 && force == 0) {
+  if (wide_ok && !splittable && batch == 1) {
     auto fill = [](long t, long slots) { return (double)t / (double)(cdiv(t, slots) * slots); };
     const long t192 = cdiv(M, BIG) * cdiv(N, BW), t128 = cdiv(M, BM) * cdiv(N, BN);
     const double f192 = fill(t192, 256);
@@ -1522,11 +1290,7 @@ GemmPlan plan_gemm(int M, int N, int K, int precision, bool splittable, int64_t 
       return p;
     }
   }
-  if (force == 256) {
-    p.big = true;
-    return p;
-  }
-  if (force != 128) {
+  {
     // Long reductions over few output tiles (weight gradients: K = tokens; the
     // vocabulary projection's input gradient: K = vocabulary): 256-tiles with
     // K split, the split count the one that needs the fewest rounds of the 256
@@ -1597,8 +1361,6 @@ bool splittable(const gpt_gemm_desc& d) {
 }
 // Direct-to-LDS loads address each operand through a 31-bit byte offset.
 bool dma_ok(const gpt_gemm_desc& d) {
-  static const bool nodma = getenv("GPT_GEMM_NODMA") != nullptr;  // tuning switch
-  if (nodma) return false;
   const long ea = d.a_trans ? (long)d.a_kvalid * d.lda : (long)d.a_rows * d.lda;
   const long eb = d.b_trans ? (long)d.b_kvalid * d.ldb : (long)d.b_rows * d.ldb;
   return ea * 2 < 0x7fffffffL && eb * 2 < 0x7fffffffL;
@@ -1666,13 +1428,26 @@ hipError_t gemm(const gpt_gemm_desc& d, hipStream_t s) {
   const int S = effective_splits(plan, d.K);
   const bool vec_ok = d.N % 8 == 0 && d.ldo % 8 == 0 && (d.aux == nullptr || d.ldaux % 8 == 0);
   const int epi = S > 1 ? EPI_PARTIAL : d.epilogue;
+  // 256-tiles run the 8-wave kernel; a combination it lacks drops to the
+  // 128-tile kernels (the split plan and its partials do not depend on the tile).
   MfmaKernel kern = nullptr;
+  int threads = 256;
+  bool big = plan.big;
   if (vec_ok) {
-    kern = plan.big ? big_kernel_for(d.a_trans, d.b_trans, epi, d.a_gelu, d.b_gelu)
-                    : mfma_kernel_for(d.a_trans, d.b_trans, epi, d.a_gelu, d.b_gelu);
-    if (!plan.big && dma_ok(d)) {
-      MfmaKernel k2 = dma_kernel_for(d.a_trans, d.b_trans, epi, d.a_gelu, d.b_gelu);
-      if (k2) kern = k2;
+    if (big) {
+      kern = big8_kernel_for(d.a_trans, d.b_trans, epi, d.a_gelu, d.b_gelu);
+      threads = 512;
+      if (kern == nullptr) {
+        big = false;
+        threads = 256;
+      }
+    }
+    if (!big) {
+      kern = mfma_kernel_for(d.a_trans, d.b_trans, epi, d.a_gelu, d.b_gelu);
+      if (dma_ok(d)) {
+        MfmaKernel k2 = dma_kernel_for(d.a_trans, d.b_trans, epi, d.a_gelu, d.b_gelu);
+        if (k2) kern = k2;
+      }
     }
   }
   if (kern == nullptr) {
@@ -1681,15 +1456,7 @@ hipError_t gemm(const gpt_gemm_desc& d, hipStream_t s) {
     gemm_simt_kernel<bf16_t, bf16_t><<<grid, 256, 0, s>>>(A, B, d.K, e);
     return hipGetLastError();
   }
-  int threads = 256;
-  if (plan.big && vec_ok) {  // the 8-wave large-tile kernel where it has the combination
-    MfmaKernel k8 = big8_kernel_for(d.a_trans, d.b_trans, epi, d.a_gelu, d.b_gelu);
-    if (k8 && !big8_disabled()) {
-      kern = k8;
-      threads = 512;
-    }
-  }
-  const int T = plan.big ? BIG : BM;
+  const int T = big ? BIG : BM;
   dim3 grid((unsigned)cdiv(d.N, T), (unsigned)cdiv(d.M, T), (unsigned)(S * batch));
   if (S == 1) {
     kern<<<grid, threads, 0, s>>>(A, B, d.K, d.K, e, nullptr);
@@ -1821,8 +1588,9 @@ int64_t gemm_group_workspace_bytes(const int* M, const int* N, int n, int K) {
   return (int64_t)S * mn * 4;
 }
 
-hipError_t gemm_group(const gpt_gemm_desc* d, int n, hipStream_t s, float* const* db) {
+hipError_t gemm_group(const gpt_gemm_desc* d, int n, hipStream_t s, float* const* db, int phase) {
   if (n <= 0) return hipSuccess;
+  const bool run_products = phase != 2, run_reduce = phase != 1;
   if (db) {  // column sums need a bf16 K-major A
     for (int i = 0; i < n; ++i)
       if (db[i] && (d[i].precision != GPT_BF16 || !d[i].a_trans || d[i].a_gelu))
@@ -1839,6 +1607,7 @@ hipError_t gemm_group(const gpt_gemm_desc* d, int n, hipStream_t s, float* const
               d[0].workspace_bytes >= gemm_group_workspace_bytes(Ms, Ns, n, d[0].K);
   }
   if (!grouped) {  // one launch per product, each with its own plan
+    if (!run_products) return hipSuccess;
     for (int i = 0; i < n; ++i) {
       hipError_t e = gemm(d[i], s);
       if (e != hipSuccess) return e;
@@ -1879,9 +1648,11 @@ hipError_t gemm_group(const gpt_gemm_desc* d, int n, hipStream_t s, float* const
     g.csum[i] = (db && db[i]) ? ws + part : nullptr;
     part += (long)S * d[i].M;
   }
-  gemm_big8_group_kernel<1, 1><<<(unsigned)(T * S), 512, 0, s>>>(g, K, kchunk, ws);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (run_products) {
+    gemm_big8_group_kernel<1, 1><<<(unsigned)(T * S), 512, 0, s>>>(g, K, kchunk, ws);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || !run_reduce) return err;
+  }
   // Each product's partials (and bias partials) summed in split order, one launch.
   GroupReduceArgs r{};
   r.n = n;
@@ -1911,9 +1682,7 @@ hipError_t gemm_group(const gpt_gemm_desc* d, int n, hipStream_t s, float* const
   r.c0[r.nc] = items;
   const unsigned blocks = (unsigned)std::min<long>(cdiv(items, 256), 8192);
   group_reduce_kernel<<<blocks, 256, 0, s>>>(r);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  return hipSuccess;
+  return hipGetLastError();
 }
 
 }  // namespace gpt

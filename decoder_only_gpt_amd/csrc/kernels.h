@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "../../include/gpt.h"
+#include "common.h"
 
 namespace gpt {
 
@@ -18,7 +19,10 @@ int64_t gemm_workspace_bytes(int M, int N, int K, int precision);
 // the grouped kernel cannot take, or a short workspace, run one by one.
 // db (may be NULL; entries may be NULL): db[i] (+)= the column sums of the
 // bf16 K-major A_i (sum over K), stored or added as the product's epilogue.
-hipError_t gemm_group(const gpt_gemm_desc* d, int n, hipStream_t s, float* const* db = nullptr);
+// phase: 0 = everything; 1 = the products (partials) only; 2 = the reduction
+// only (after phase 1 with the same arguments; nothing when not grouped).
+hipError_t gemm_group(const gpt_gemm_desc* d, int n, hipStream_t s, float* const* db = nullptr,
+                      int phase = 0);
 int64_t gemm_group_workspace_bytes(const int* M, const int* N, int n, int K);
 // Number of K splits gemm() will use for this descriptor (1 = single kernel).
 int gemm_split_count(const gpt_gemm_desc& d);
@@ -32,8 +36,11 @@ hipError_t attention_bwd(int prec, int B, int T, int H, int hd, int left, const 
 bool attention_supported(int prec, int hd);
 
 // Row-wise kernels (rowwise.hip).
+// Ids outside [0, V) are read as 0 and mark *flag = gen; ids_out (may be
+// NULL) receives the ids used.
 hipError_t embed_fwd(int prec, const int32_t* idx, const float* wte, const float* wpe, int M, int T,
-                     int C, float* x, hipStream_t s);
+                     int C, int V, float* x, int32_t* ids_out, int32_t* flag, int32_t gen,
+                     hipStream_t s);
 // Deterministic embedding backward: dwte[v] (+)= sum of dx rows whose token is v,
 // in increasing position order; dwpe[t] (+)= sum_b dx[b*T+t].
 // Scratch of embed_bwd: counts/offsets [Vp], tile_sums [Vp / 1024 + 1],
@@ -64,36 +71,49 @@ int colsum_partial_rows(int M);
 // Floats of `partials` colsum needs.
 int64_t colsum_partial_floats(int M, int N);
 // Fused softmax cross-entropy on logits [M, ldz] (act type): loss_rows[m],
-// logits overwritten by d(mean loss)/dlogits (0 for columns >= V).
+// logits overwritten by d(mean loss)/dlogits (0 for columns >= V).  Targets
+// outside [0, V) are read as 0 and mark *flag = gen.
 hipError_t cross_entropy(int prec, void* logits, int M, int V, int ldz, const int32_t* tgt,
-                         float* loss_rows, hipStream_t s);
+                         float* loss_rows, int32_t* flag, int32_t gen, hipStream_t s);
 bool cross_entropy_supported(int prec, int ldz);
-hipError_t mean_loss(const float* loss_rows, int M, float* out, hipStream_t s);
+// out = mean of loss_rows (double, fixed order); NaN when *flag == gen.
+hipError_t mean_loss(const float* loss_rows, int M, float* out, const int32_t* flag, int32_t gen,
+                     hipStream_t s);
 // Sum of squares of x[n] (float) -> *out (double), fixed order.
 hipError_t sumsq(const float* x, int64_t n, double* partials, double* out, hipStream_t s);
 hipError_t to_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t s);
+// Seeded initialisation: p[0 .. n) holds flat indices begin .. begin + n; the
+// first n_normal get (float)(stdv * z(i)), z the Philox4x32-10 / Box-Muller
+// standard normal of flat index i under `seed`, the rest 0.
+hipError_t init_normal(float* p, int64_t begin, int64_t n, int64_t n_normal, double stdv,
+                       uint64_t seed, hipStream_t s);
+hipError_t fill_value(float* p, int64_t n, float v, hipStream_t s);
 
 // AdamW (adamw.hip).
 struct AdamScalars { float omb1, omb2, decay, step_size, sbc2, eps, scale; };
 // d_scale (device, may be NULL): the gradient scale in place of sc.scale; a
 // NaN there leaves p, m, v and the shadow unchanged.
+// A tripped guard (common.h) leaves them unchanged too.
 hipError_t adamw(int64_t n, float* p, float* m, float* v, const float* g, uint16_t* shadow,
-                 AdamScalars sc, hipStream_t s, const float* d_scale = nullptr);
+                 AdamScalars sc, hipStream_t s, const float* d_scale = nullptr,
+                 Guard guard = Guard{nullptr, 0});
 // Device global-norm clip from the sum of squares at norm2: out = {norm,
-// grad_scale} (doubles), scale = grad_scale as float (NaN: non-finite norm).
+// grad_scale} (doubles), scale = grad_scale as float (NaN: non-finite norm or
+// a tripped guard).
 hipError_t clip_scale(const double* norm2, int n_micro, double max_norm, double* out, float* scale,
-                      hipStream_t s);
+                      Guard guard, hipStream_t s);
 // AdamW over segments of the flat vectors in one launch.  d_seg (device):
 // (begin, length, first block) per segment; lengths multiples of 4; the
 // first blocks are the running sum of adamw_segment_blocks(length).
 int adamw_segment_blocks(int64_t len);
 hipError_t adamw_segments(const int64_t* d_seg, int nseg, int blocks, float* p, float* m,
                           float* v, const float* g, uint16_t* shadow, AdamScalars sc,
-                          hipStream_t s);
+                          Guard guard, hipStream_t s);
 
-// Generation (decode.hip).  x[b] = wte[tok[b]] + wpe[pos].
+// Generation (decode.hip).  x[b] = wte[tok[b]] + wpe[pos]; ids outside [0, V)
+// read row 0.
 hipError_t gen_embed(const int32_t* tok, const float* wte, const float* wpe, int pos, int B, int C,
-                     float* x, hipStream_t s);
+                     int V, float* x, hipStream_t s);
 // One query per (sequence b, head h) at position pos: qkv [B, 3*H*hd] (act);
 // caches [B, H, Tmax, hd] (act) of this layer; row pos of both caches is
 // written from qkv; out [B, H*hd] (act).
@@ -150,7 +170,8 @@ struct MuonScalars {
 constexpr int MUON_PREP_BLOCKS = 64;  // sum-of-squares partials per matrix
 // Workspace bytes muon_matrices needs for `count` matrices of [rows, cols].
 int64_t muon_workspace_bytes(int rows, int cols, int count, int prec);
+// A tripped guard leaves the parameters, momentum and second moment unchanged.
 hipError_t muon_matrices(const MuonGroup& g, const MuonScalars& sc, int prec, void* workspace,
-                         hipStream_t s);
+                         Guard guard, hipStream_t s);
 
 }  // namespace gpt

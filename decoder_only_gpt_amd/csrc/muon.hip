@@ -48,8 +48,9 @@ __device__ __forceinline__ double block_sum_d(double v, double* red) {
 template <typename ActT>
 __global__ void __launch_bounds__(MU_THREADS) muon_prep_kernel(
     const float* __restrict__ g, float* __restrict__ buf, long ls, long rc, float scale,
-    float omm, float mu, ActT* __restrict__ X, int chunk, double* __restrict__ part) {
+    float omm, float mu, ActT* __restrict__ X, int chunk, double* __restrict__ part, Guard guard) {
   __shared__ double red[MU_THREADS];
+  const bool frozen = guard_tripped(guard);  // momentum left unchanged
   const int l = blockIdx.y;
   const float* gl = g + l * ls;
   float* bl = buf + l * ls;
@@ -69,7 +70,7 @@ __global__ void __launch_bounds__(MU_THREADS) muon_prep_kernel(
       const float x = Act<ActT>::load(xl, i + k);
       ss += x * x;
     }
-    *(float4*)(bl + i) = make_float4(mv[0], mv[1], mv[2], mv[3]);
+    if (!frozen) *(float4*)(bl + i) = make_float4(mv[0], mv[1], mv[2], mv[3]);
   }
   const double t = block_sum_d((double)ss, red);
   if (threadIdx.x == 0) part[(long)l * gridDim.x + blockIdx.x] = t;
@@ -156,8 +157,9 @@ __global__ void __launch_bounds__(MU_THREADS) muon_col_stats_kernel(const ActT* 
 // the matrix's v slot) and the per-row (per-column) factors r_i.
 __global__ void __launch_bounds__(MU_THREADS) muon_second_kernel(
     const float* __restrict__ s, float* __restrict__ v, long ls, int n_long, int n_short,
-    float omb2, float eps, float* __restrict__ rfac) {
+    float omb2, float eps, float* __restrict__ rfac, Guard guard) {
   __shared__ double red[MU_THREADS];
+  if (guard_tripped(guard)) return;  // second moment left unchanged (no update follows)
   const int l = blockIdx.x;
   const float* sl = s + (long)l * n_long;
   float* vl = v + l * ls;
@@ -184,7 +186,9 @@ __global__ void __launch_bounds__(MU_THREADS) muon_second_kernel(
 template <typename ActT>
 __global__ void __launch_bounds__(MU_THREADS) muon_update_kernel(
     float* __restrict__ p, long ls, const ActT* __restrict__ X, int r, int c, int tall,
-    const float* __restrict__ rfac, float lr, float lrwd, bf16_t* __restrict__ shadow) {
+    const float* __restrict__ rfac, float lr, float lrwd, bf16_t* __restrict__ shadow,
+    Guard guard) {
+  if (guard_tripped(guard)) return;
   const int l = blockIdx.y;
   const long rc = (long)r * c;
   float* pl = p + l * ls;
@@ -220,7 +224,7 @@ int64_t muon_workspace_bytes(int r, int c, int L, int prec) {
 }
 
 hipError_t muon_matrices(const MuonGroup& gp, const MuonScalars& sc, int prec, void* ws,
-                         hipStream_t s) {
+                         Guard guard, hipStream_t s) {
   const int r = gp.rows, c = gp.cols, L = gp.count;
   if (L <= 0) return hipSuccess;
   const bool bf16 = prec == GPT_BF16;
@@ -245,10 +249,12 @@ hipError_t muon_matrices(const MuonGroup& gp, const MuonScalars& sc, int prec, v
   dim3 gprep((unsigned)nb, (unsigned)L);
   if (bf16)
     muon_prep_kernel<bf16_t><<<gprep, MU_THREADS, 0, s>>>(gp.g, gp.buf, gp.ls, rc, sc.grad_scale,
-                                                          sc.omm, sc.mu, (bf16_t*)X0, chunk, part);
+                                                          sc.omm, sc.mu, (bf16_t*)X0, chunk, part,
+                                                          guard);
   else
     muon_prep_kernel<float><<<gprep, MU_THREADS, 0, s>>>(gp.g, gp.buf, gp.ls, rc, sc.grad_scale,
-                                                         sc.omm, sc.mu, (float*)X0, chunk, part);
+                                                         sc.omm, sc.mu, (float*)X0, chunk, part,
+                                                         guard);
   if (bf16)
     muon_norm_kernel<true><<<L, MU_THREADS, 0, s>>>(part, nb, den);
   else
@@ -329,13 +335,16 @@ hipError_t muon_matrices(const MuonGroup& gp, const MuonScalars& sc, int prec, v
     else
       muon_col_stats_kernel<float><<<gs, MU_THREADS, 0, s>>>((const float*)X, r, c, st);
   }
-  muon_second_kernel<<<L, MU_THREADS, 0, s>>>(st, gp.v, gp.ls, nl, sdim, sc.omb2, sc.eps, rfac);
+  muon_second_kernel<<<L, MU_THREADS, 0, s>>>(st, gp.v, gp.ls, nl, sdim, sc.omb2, sc.eps, rfac,
+                                              guard);
   if (bf16)
     muon_update_kernel<bf16_t><<<dim3(eb, L), MU_THREADS, 0, s>>>(
-        gp.p, gp.ls, (const bf16_t*)X, r, c, tall, rfac, sc.lr, sc.lrwd, (bf16_t*)gp.shadow);
+        gp.p, gp.ls, (const bf16_t*)X, r, c, tall, rfac, sc.lr, sc.lrwd, (bf16_t*)gp.shadow,
+        guard);
   else
     muon_update_kernel<float><<<dim3(eb, L), MU_THREADS, 0, s>>>(
-        gp.p, gp.ls, (const float*)X, r, c, tall, rfac, sc.lr, sc.lrwd, (bf16_t*)gp.shadow);
+        gp.p, gp.ls, (const float*)X, r, c, tall, rfac, sc.lr, sc.lrwd, (bf16_t*)gp.shadow,
+        guard);
   return hipGetLastError();
 }
 

@@ -18,14 +18,18 @@ namespace {
 // ------------------------------------------------------------------ embeddings
 // x[m, :] = wte[idx[m], :] + wpe[m % T, :]   (nanoGPT README: learned token and
 // position embeddings; "todos" lists other position schemes as future work).
+// Ids outside [0, V) read row 0 and mark *flag = gen; ids_out[m] receives the
+// id used (the backward's copy).
 __global__ void __launch_bounds__(256) embed_fwd_kernel(const int32_t* idx, const float* wte,
                                                         const float* wpe, int M, int T, int C,
-                                                        float* x) {
+                                                        int V, float* x, int32_t* ids_out,
+                                                        int32_t* flag, int32_t gen) {
   const int C4 = C / 4;
   long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= (long)M * C4) return;
   int m = (int)(i / C4), c = (int)(i % C4);
-  int tok = idx[m];
+  const int tok = checked_id(idx[m], V, flag, gen);
+  if (c == 0 && ids_out) ids_out[m] = tok;
   float4 a = ((const float4*)(wte + (long)tok * C))[c];
   float4 b = ((const float4*)(wpe + (long)(m % T) * C))[c];
   ((float4*)(x + (long)m * C))[c] = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
@@ -227,6 +231,60 @@ __global__ void __launch_bounds__(256) embed_wpe_kernel(const float* dx, int M, 
   float s = 0.f;
   for (int m = t; m < M; m += T) s += dx[(long)m * C + c];
   dwpe[i] = accumulate ? dwpe[i] + s : s;
+}
+
+// ------------------------------------------------------------------ seeded init
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011): ten rounds of two 32x32 -> 64-bit products on
+// words 0 and 2, the new block (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^
+// k1, lo(M0 c0)), the key bumped by the Weyl increments between rounds.
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c.x, p1 = (uint64_t)0xCD9E8D57u * c.z;
+    c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c.w ^ k1,
+                   (uint32_t)p0);
+  }
+  return c;
+}
+
+// p[i - begin] for flat indices i in [begin, begin + n): std * z(i) for the
+// first n_normal of them, 0 after.  z(i): block j = i / 4 of Philox (counter
+// (j lo, j hi, 0, 0), key (seed lo, seed hi)); words (x0, x1) -> z(4j), z(4j+1)
+// and (x2, x3) -> z(4j+2), z(4j+3) by Box-Muller (Box and Muller, 1958) in
+// double: r = sqrt(-2 ln((x + 1) / 2^32)), angle 2 pi x' / 2^32.
+__global__ void __launch_bounds__(256) init_normal_kernel(float* __restrict__ p, int64_t begin,
+                                                          int64_t n, int64_t n_normal, double stdv,
+                                                          uint64_t seed) {
+  const int64_t j = begin / 4 + (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (4 * j >= begin + n) return;
+  const uint4 x = philox4x32_10(make_uint4((uint32_t)j, (uint32_t)((uint64_t)j >> 32), 0u, 0u),
+                                (uint32_t)seed, (uint32_t)(seed >> 32));
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  double z[4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const double r = sqrt(-2.0 * log(((double)w[2 * h] + 1.0) * 0x1p-32));
+    double sn, cs;
+    sincos(6.283185307179586 * ((double)w[2 * h + 1] * 0x1p-32), &sn, &cs);
+    z[2 * h] = r * cs;
+    z[2 * h + 1] = r * sn;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t i = 4 * j + q;
+    if (i < begin || i >= begin + n) continue;
+    p[i - begin] = i - begin < n_normal ? (float)(stdv * z[q]) : 0.f;
+  }
+}
+
+__global__ void __launch_bounds__(256) fill_value_kernel(float* __restrict__ p, int64_t n, float v) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
 }
 
 // ------------------------------------------------------------------ LayerNorm
@@ -471,14 +529,15 @@ constexpr float LOG2E_F = 1.4426950408889634f;
 template <typename ActT>
 __global__ void __launch_bounds__(CE_THREADS) ce_kernel(ActT* z, int M, int V, int ldz,
                                                         const int32_t* tgt, float* loss_rows,
-                                                        float inv_count) {
+                                                        float inv_count, int32_t* flag,
+                                                        int32_t gen) {
   constexpr int EPV = 16 / sizeof(ActT);
   __shared__ float red[CE_THREADS / 64];
   __shared__ float zt_s;
   const int row = blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   ActT* zr = z + (long)row * ldz;
-  const int target = tgt[row];
+  const int target = checked_id(tgt[row], V, t == 0 ? flag : nullptr, gen);
   const int nvec = ldz / EPV;
   float v[CE_NV][EPV];
 #pragma unroll
@@ -557,12 +616,13 @@ __device__ __forceinline__ void lse_combine(float& m, float& s, float m2, float 
 
 __global__ void __launch_bounds__(CE_THREADS, 8) ce_bf16_kernel(bf16_t* z, int V, int ldz,
                                                              const int32_t* tgt,
-                                                             float* loss_rows, float inv_count) {
+                                                             float* loss_rows, float inv_count,
+                                                             int32_t* flag, int32_t gen) {
   __shared__ float red_m[CE_THREADS / 64], red_s[CE_THREADS / 64];
   const int row = blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   bf16_t* zr = z + (long)row * ldz;
-  const int target = tgt[row];
+  const int target = checked_id(tgt[row], V, t == 0 ? flag : nullptr, gen);
   const int nvec = ldz / 8;
   u32x4 raw[CE_NV];
 #pragma unroll
@@ -636,7 +696,10 @@ __global__ void __launch_bounds__(CE_THREADS, 8) ce_bf16_kernel(bf16_t* z, int V
   }
 }
 
-__global__ void __launch_bounds__(1024) mean_kernel(const float* x, int n, float* out) {
+// The mean of x[n] in double, fixed order; NaN when *flag == gen (a token id
+// of this forward was out of range).
+__global__ void __launch_bounds__(1024) mean_kernel(const float* x, int n, float* out,
+                                                    const int32_t* flag, int32_t gen) {
   __shared__ double red[1024];
   double s = 0.0;
   for (int i = threadIdx.x; i < n; i += 1024) s += (double)x[i];
@@ -646,7 +709,10 @@ __global__ void __launch_bounds__(1024) mean_kernel(const float* x, int n, float
     if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
-  if (threadIdx.x == 0) out[0] = (float)(red[0] / (double)n);
+  if (threadIdx.x == 0) {
+    const bool bad = flag != nullptr && *(volatile const int32_t*)flag == gen;
+    out[0] = bad ? __builtin_nanf("") : (float)(red[0] / (double)n);
+  }
 }
 
 // ------------------------------------------------------------------ sum of squares
@@ -698,11 +764,13 @@ __global__ void __launch_bounds__(256) to_bf16_kernel(const float* x, int64_t n,
 }  // namespace
 
 hipError_t embed_fwd(int prec, const int32_t* idx, const float* wte, const float* wpe, int M, int T,
-                     int C, float* x, hipStream_t s) {
+                     int C, int V, float* x, int32_t* ids_out, int32_t* flag, int32_t gen,
+                     hipStream_t s) {
   (void)prec;
   long n = (long)M * (C / 4);
   if (n == 0) return hipSuccess;
-  embed_fwd_kernel<<<(unsigned)cdiv(n, 256), 256, 0, s>>>(idx, wte, wpe, M, T, C, x);
+  embed_fwd_kernel<<<(unsigned)cdiv(n, 256), 256, 0, s>>>(idx, wte, wpe, M, T, C, V, x, ids_out,
+                                                          flag, gen);
   return hipGetLastError();
 }
 
@@ -731,6 +799,20 @@ hipError_t embed_bwd(const int32_t* idx, const float* dx, int M, int T, int C, i
   }
   embed_wpe_kernel<<<(unsigned)cdiv((long)Tb * C, 256), 256, 0, s>>>(dx, M, T, C, Tb, dwpe,
                                                                      wpe_accumulate);
+  return hipGetLastError();
+}
+
+hipError_t init_normal(float* p, int64_t begin, int64_t n, int64_t n_normal, double stdv,
+                       uint64_t seed, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = cdiv((begin + n + 3) / 4 - begin / 4, 256);
+  init_normal_kernel<<<(unsigned)blocks, 256, 0, s>>>(p, begin, n, n_normal, stdv, seed);
+  return hipGetLastError();
+}
+
+hipError_t fill_value(float* p, int64_t n, float v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  fill_value_kernel<<<(unsigned)cdiv(n, 256), 256, 0, s>>>(p, n, v);
   return hipGetLastError();
 }
 
@@ -815,19 +897,22 @@ bool cross_entropy_supported(int prec, int ldz) {
 }
 
 hipError_t cross_entropy(int prec, void* logits, int M, int V, int ldz, const int32_t* tgt,
-                         float* loss_rows, hipStream_t s) {
+                         float* loss_rows, int32_t* flag, int32_t gen, hipStream_t s) {
   if (M == 0) return hipSuccess;
   if (!cross_entropy_supported(prec, ldz) || V > ldz) return hipErrorInvalidValue;
   float inv = 1.f / (float)M;
   if (prec == GPT_BF16)
-    ce_bf16_kernel<<<M, CE_THREADS, 0, s>>>((bf16_t*)logits, V, ldz, tgt, loss_rows, inv);
+    ce_bf16_kernel<<<M, CE_THREADS, 0, s>>>((bf16_t*)logits, V, ldz, tgt, loss_rows, inv, flag,
+                                            gen);
   else
-    ce_kernel<float><<<M, CE_THREADS, 0, s>>>((float*)logits, M, V, ldz, tgt, loss_rows, inv);
+    ce_kernel<float><<<M, CE_THREADS, 0, s>>>((float*)logits, M, V, ldz, tgt, loss_rows, inv,
+                                              flag, gen);
   return hipGetLastError();
 }
 
-hipError_t mean_loss(const float* loss_rows, int M, float* out, hipStream_t s) {
-  mean_kernel<<<1, 1024, 0, s>>>(loss_rows, M, out);
+hipError_t mean_loss(const float* loss_rows, int M, float* out, const int32_t* flag, int32_t gen,
+                     hipStream_t s) {
+  mean_kernel<<<1, 1024, 0, s>>>(loss_rows, M, out, flag, gen);
   return hipGetLastError();
 }
 

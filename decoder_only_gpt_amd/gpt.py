@@ -33,7 +33,8 @@ EXPORTS = [
     "gpt_set_buffer", "gpt_destroy", "gpt_gen_plan", "gpt_gen_init", "gpt_gen_reset",
     "gpt_gen_step", "gpt_gen_logits", "gpt_gen_sample", "gpt_generate", "gpt_gen_destroy",
     "gpt_last_error", "gpt_op_gemm", "gpt_op_gemm_group", "gpt_op_gemm_group_workspace",
-    "gpt_op_attention_fwd", "gpt_op_attention_bwd", "gpt_op_adamw", "gpt_profile_begin",
+    "gpt_op_attention_fwd", "gpt_op_attention_bwd",
+    "gpt_op_adamw", "gpt_profile_begin",
     "gpt_profile_end",
 ]
 KERNEL_KINDS = ["gemm", "gemm_splitk", "attn_fwd", "attn_bwd", "layernorm", "cross_entropy",
@@ -41,7 +42,7 @@ KERNEL_KINDS = ["gemm", "gemm_splitk", "attn_fwd", "attn_bwd", "layernorm", "cro
 SITES = ["embed_fwd", "ln_fwd", "qkv_fwd", "attn_fwd", "proj_fwd", "fc_fwd", "fcproj_fwd",
          "lmhead_fwd", "cross_entropy", "lmhead_dx", "lmhead_dw", "ln_bwd", "fcproj_dx", "fcproj_dw",
          "fc_dx", "fc_dw", "proj_dx", "proj_dw", "attn_bwd", "qkv_dx", "qkv_dw", "bias_grad",
-         "embed_bwd", "grad_norm", "adamw", "block_dw"]
+         "embed_bwd", "grad_norm", "adamw", "block_dw", "block_dw_reduce"]
 
 
 GPT_E_NONFINITE = 4  # gpt_status: gradient norm is NaN or Inf
@@ -129,7 +130,8 @@ def lib():
     sig = {
         "gpt_plan": ([ctypes.POINTER(Config), i32, i32, ctypes.POINTER(Sizes)], i32),
         "gpt_flops_per_token": ([ctypes.POINTER(Config), i32], ctypes.c_double),
-        "gpt_init": ([ctypes.POINTER(Config), i32, i32, vp, i64, vp, ctypes.POINTER(vp)], i32),
+        "gpt_init": ([ctypes.POINTER(Config), i32, i32, vp, i64, ctypes.c_uint64, vp,
+                      ctypes.POINTER(vp)], i32),
         "gpt_forward": ([vp, vp, vp, vp], i32),
         "gpt_loss": ([vp, vp, ctypes.POINTER(ctypes.c_float)], i32),
         "gpt_loss_device_ptr": ([vp, ctypes.POINTER(vp)], i32),
@@ -212,6 +214,22 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+def check_ids(t, n: int, what: str = "idx"):
+    """Token ids handed to the library must be a contiguous int32 CUDA tensor
+    of n entries (the kernels read n int32 values at its address)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch tensor")
+    if t.dtype != torch.int32:
+        raise TypeError(f"{what} must be int32, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a CUDA tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if t.numel() != n:
+        raise ValueError(f"{what} must have {n} entries, got {t.numel()}")
+
+
 def adam_hp(cfg: dict, t: int, grad_scale: float = 1.0, lr: float | None = None) -> AdamHP:
     return AdamHP(cfg["lr"] if lr is None else lr, cfg["beta1"], cfg["beta2"], cfg["eps"],
                   cfg["weight_decay"], grad_scale, t)
@@ -220,7 +238,7 @@ def adam_hp(cfg: dict, t: int, grad_scale: float = 1.0, lr: float | None = None)
 class Model:
     """One model bound to a device arena; methods map 1:1 onto the C ABI."""
 
-    def __init__(self, cfg: dict, B: int | None = None, T: int | None = None):
+    def __init__(self, cfg: dict, B: int | None = None, T: int | None = None, seed: int = 0):
         import torch
         self.cfg = dict(cfg)
         self.B = cfg["B"] if B is None else B
@@ -232,7 +250,7 @@ class Model:
         self._c = make_config(cfg)
         _check(lib().gpt_init(ctypes.byref(self._c), self.B, self.T,
                               ctypes.c_void_p(self.arena.data_ptr()), int(self.sizes.arena_bytes),
-                              _stream(), ctypes.byref(h)))
+                              ctypes.c_uint64(int(seed)), _stream(), ctypes.byref(h)))
         self.h = h
         self.step_t = 0
 
@@ -272,6 +290,10 @@ class Model:
 
     # ---- the step
     def forward(self, idx, tgt=None):
+        n = self.B * self.T
+        check_ids(idx, n, "idx")
+        if tgt is not None:
+            check_ids(tgt, n, "tgt")
         self._idx, self._tgt = idx, tgt  # keep the device tensors alive
         _check(lib().gpt_forward(self.h, ctypes.c_void_p(idx.data_ptr()),
                                  None if tgt is None else ctypes.c_void_p(tgt.data_ptr()), _stream()))
@@ -344,18 +366,23 @@ class Model:
         self.forward(idx, tgt)
         self.loss_async()
         self.backward(0)
-        self.step_t += 1
+        t = self.step_t + 1
         clip = float(self.cfg.get("clip", 0.0) or 0.0)
         if clip > 0.0:
-            self.adamw_step_clipped(self.step_t, clip)
+            self.adamw_step_clipped(t, clip)
         else:
-            self.adamw_step(self.step_t, 1.0)
+            self.adamw_step(t, 1.0)
         torch.cuda.current_stream().synchronize()
         pl, pn = self._pinned()
         loss = float(pl[0])
         norm, scale = (float(pn[0]), float(pn[1])) if clip > 0.0 else (None, 1.0)
+        # An update the device skipped does not count as an optimizer step.
+        if math.isnan(loss):  # the library's mark for an out-of-range token id
+            raise GptError(E_INVALID, "loss is NaN: a token id or target is outside [0, vocab_size) "
+                                      "(the update was skipped) or the loss diverged")
         if norm is not None and not math.isfinite(norm):
             raise GptError(GPT_E_NONFINITE, f"gradient norm is not finite ({norm}); no update")
+        self.step_t = t
         return dict(loss=loss, norm=norm, scale=scale)
 
 

@@ -11,6 +11,9 @@
         one plain device-to-device copy of a known size (counter calibration)
     python -m decoder_only_gpt_amd.profile_run summarize-stats CSV OUT --command "..."
         rocprofv3 --stats kernel table -> short text summary
+    python -m decoder_only_gpt_amd.profile_run summarize-mfma CSV OUT --command "..."
+        rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE counter rows -> per-kernel
+        fraction of SIMD cycles the matrix units were busy
     python -m decoder_only_gpt_amd.profile_run summarize-traffic --kernel SUBSTR
         --fetch CSV --write CSV --copy-fetch CSV --copy-write CSV --copy-mib N OUT --command "..."
         per-dispatch FETCH_SIZE / WRITE_SIZE of one kernel, scaled by the same counters
@@ -124,6 +127,50 @@ def summarize_stats(csv_path: str, out_path: str, command: str, top: int = 40):
         f.write("\n".join(lines) + "\n")
 
 
+# MI355X: 8 XCDs of 32 CUs, 4 SIMDs per CU.  rocprofv3 sums a counter over
+# its hardware instances: GRBM_GUI_ACTIVE over the 8 XCDs (so the sum is 8x
+# the elapsed GPU cycles) and SQ_VALU_MFMA_BUSY_CYCLES over the 1024 SIMDs.
+N_XCD, N_SIMD = 8, 1024
+
+
+def summarize_mfma(csv_path: str, out_path: str, command: str, top: int = 40):
+    """Per kernel: mean over dispatches of MFMA-busy cycles / (elapsed cycles x
+    SIMDs), elapsed cycles = GRBM_GUI_ACTIVE / XCDs."""
+    disp = {}
+    for r in csv.DictReader(open(csv_path)):
+        key = (r["Dispatch_Id"], r["Kernel_Name"])
+        d = disp.setdefault(key, {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        if "Start_Timestamp" in r and "End_Timestamp" in r:
+            d["_ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    per = {}
+    for (_, name), d in disp.items():
+        if "SQ_VALU_MFMA_BUSY_CYCLES" not in d or not d.get("GRBM_GUI_ACTIVE"):
+            continue
+        cyc = d["GRBM_GUI_ACTIVE"] / N_XCD
+        frac = d["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * N_SIMD)
+        e = per.setdefault(name, {"n": 0, "frac": 0.0, "cyc": 0.0, "busy": 0.0})
+        e["n"] += 1
+        e["frac"] += frac
+        e["cyc"] += cyc
+        e["busy"] += d["SQ_VALU_MFMA_BUSY_CYCLES"]
+    rows = sorted(per.items(), key=lambda kv: -kv[1]["cyc"])
+    lines = ["# rocprofv3 MFMA utilisation per kernel",
+             f"# command: {command}",
+             f"# kernel sources sha: {kernel_source_sha()}",
+             f"# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {N_XCD} XCDs x {N_SIMD} SIMDs),",
+             "#   averaged over a kernel's dispatches (counters summed over their hardware instances);",
+             "#   cyc = elapsed GPU cycles per dispatch (GRBM_GUI_ACTIVE / 8)", "",
+             f"{'calls':>6} {'mfma_busy':>9} {'kcyc':>9}  kernel"]
+    for name, e in rows[:top]:
+        if len(name) > 110:
+            name = name[:107] + "..."
+        lines.append(f"{e['n']:>6} {e['frac'] / e['n']:>9.3f} {e['cyc'] / e['n'] / 1e3:>9.1f}  {name}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def _per_dispatch(csv_path: str, counter: str, substr: str):
     vals = []
     for r in csv.DictReader(open(csv_path)):
@@ -177,6 +224,10 @@ def main():
     p.add_argument("csv")
     p.add_argument("out")
     p.add_argument("--command", required=True)
+    p = sub.add_parser("summarize-mfma")
+    p.add_argument("csv")
+    p.add_argument("out")
+    p.add_argument("--command", required=True)
     p = sub.add_parser("summarize-traffic")
     p.add_argument("out")
     p.add_argument("--kernel", required=True)
@@ -202,6 +253,8 @@ def main():
         run_copy(a.mib)
     elif a.cmd == "summarize-stats":
         summarize_stats(a.csv, a.out, a.command)
+    elif a.cmd == "summarize-mfma":
+        summarize_mfma(a.csv, a.out, a.command)
     else:
         summarize_traffic(a)
 

@@ -35,7 +35,12 @@
  *   - Ownership: the caller allocates the single device arena whose size
  *     gpt_plan reports, and keeps it alive until gpt_destroy.  The library
  *     borrows it and owns only the opaque host handle.
- *   - Token ids outside [0, vocab_size) are undefined behaviour.
+ *   - Token ids and targets must lie in [0, vocab_size).  The kernels never
+ *     index out of bounds with others: they read id 0 in their place, the
+ *     forward is flagged, its mean loss reads NaN, gpt_loss / gpt_grad_norm
+ *     return GPT_E_INVALID, and the next optimizer step (gpt_adamw_step,
+ *     gpt_adamw_step_clipped, gpt_muon_step) leaves parameters and moments
+ *     unchanged.  A later update after clean forwards proceeds normally.
  */
 #ifndef GPT_MI355X_H
 #define GPT_MI355X_H
@@ -142,18 +147,38 @@ int gpt_plan(const gpt_config* cfg, int32_t B, int32_t T, gpt_sizes* out);
 double gpt_flops_per_token(const gpt_config* cfg, int32_t T);
 
 /* Bind a model to a caller-owned device arena of at least arena_bytes
- * (gpt_plan), 256-byte aligned.  Zeroes parameters, gradients and both
- * moments on `stream`.  Load weights with gpt_set_buffer(GPT_BUF_PARAMS). */
+ * (gpt_plan), 256-byte aligned, and initialise it on `stream` (BASELINE
+ * workloads: "weights N(0,0.02)"; nanoGPT README "quick start": a GPT trained
+ * from scratch): every matrix and embedding entry at flat index i is
+ * (float)(0.02 * z(i)), z(i) a standard normal drawn from `seed` by
+ * Philox4x32-10 (Salmon et al., SC 2011; block i / 4, counter (i/4 lo, i/4 hi,
+ * 0, 0), key (seed lo, seed hi)) and the Box-Muller transform in double (words
+ * 0, 1 -> entries 4j, 4j+1 as r cos, r sin; words 2, 3 -> 4j+2, 4j+3); the
+ * padded vocabulary rows (>= vocab_size) of wte / lm_head are 0, LayerNorm
+ * gains 1, LayerNorm shifts and Linear biases 0.  Gradients and both moments
+ * start at 0.  The same seed gives the same bits.  Other weights can be
+ * loaded with gpt_set_buffer(GPT_BUF_PARAMS).  Synchronises `stream`.
+ * INVALID for a bad config, a NULL or misaligned arena or one too small;
+ * HIP on a failed launch. */
 int gpt_init(const gpt_config* cfg, int32_t B, int32_t T, void* d_arena, int64_t arena_bytes,
-             void* stream, gpt_model** out);
+             uint64_t seed, void* stream, gpt_model** out);
 
-/* Forward pass on device token ids d_idx [B*T] (int32).  With d_tgt [B*T]
- * the per-token cross-entropy and its gradient w.r.t. the logits are
- * computed too (required before gpt_backward); with d_tgt == NULL only the
- * logits.  Enqueue only. */
+/* Forward pass (NiNo README "usage": output = model(data); nanoGPT README
+ * "quick start": the GPT of model.py) on device token ids d_idx [B*T]
+ * (int32, row-major [B][T], caller-owned and read during the enqueued work
+ * only).  With d_tgt [B*T] (int32, the next-token targets: Panthalia "Create
+ * a Plugin", input-target pairs) the per-token cross-entropy (NiNo "usage":
+ * loss = F.cross_entropy(output, target), mean) and its gradient w.r.t. the
+ * logits are computed too (required before gpt_backward); with d_tgt == NULL
+ * only the logits.  Ids outside [0, vocab_size): see the conventions above.
+ * Enqueue only.  INVALID on NULL model / d_idx. */
 int gpt_forward(gpt_model* m, const int32_t* d_idx, const int32_t* d_tgt, void* stream);
 
-/* Mean loss of the last forward with targets.  Synchronises `stream`. */
+/* Mean loss of the last forward with targets (NiNo README "usage": the mean
+ * cross-entropy; llm.c summary "Proceso de entrenamiento": the loss printed
+ * per iteration), summed in double in a fixed order.  Synchronises `stream`.
+ * STATE if there is no forward with targets since the last update; INVALID
+ * (with *h_mean_loss = NaN) if that forward met an id outside [0, vocab_size). */
 int gpt_loss(gpt_model* m, void* stream, float* h_mean_loss);
 
 /* Device address of that mean loss (one float), valid after gpt_forward
@@ -165,13 +190,21 @@ int gpt_loss_device_ptr(gpt_model* m, const float** d_loss);
  * point; page-locked memory keeps the call asynchronous). */
 int gpt_loss_async(gpt_model* m, float* h_loss, void* stream);
 
-/* Backward pass of the last forward with targets.  accumulate = 0
- * overwrites the gradient buffer, 1 adds to it.  Enqueue only. */
+/* Backward pass of the last forward with targets (NiNo README "usage":
+ * loss.backward(); Panthalia "Create a Plugin": gradient computation on the
+ * flattened representation): the exact gradient of the mean loss w.r.t. every
+ * parameter, into the flat gradient buffer.  accumulate = 0 overwrites it,
+ * 1 adds to it (gradient accumulation over micro-batches, Panthalia
+ * "accumulations").  Enqueue only.  STATE without a preceding forward with
+ * targets; INVALID for accumulate not in {0, 1}. */
 int gpt_backward(gpt_model* m, int32_t accumulate, void* stream);
 
-/* Global L2 norm of the gradient buffer (float32 squares summed per block,
- * blocks summed in double in a fixed order).  Synchronises.  Returns
- * GPT_E_NONFINITE (with *h_norm set) if the norm is NaN or Inf. */
+/* Global L2 norm of the gradient buffer (llm.c summary "Proceso de
+ * entrenamiento": the gradient norm that clipping acts on), float32 squares
+ * summed per block, blocks summed in double in a fixed order.  Synchronises.
+ * Returns GPT_E_NONFINITE (with *h_norm set) if the norm is NaN or Inf;
+ * STATE without a backward; INVALID (with *h_norm set) if a forward since
+ * the last update met an id outside [0, vocab_size). */
 int gpt_grad_norm(gpt_model* m, void* stream, double* h_norm);
 
 /* One AdamW update of all parameters (see gpt_adamw_hp).  Enqueue only. */
@@ -244,7 +277,8 @@ typedef enum gpt_site {
   GPT_S_LMHEAD_DW, GPT_S_LN_BWD, GPT_S_FCPROJ_DX, GPT_S_FCPROJ_DW, GPT_S_FC_DX, GPT_S_FC_DW,
   GPT_S_PROJ_DX, GPT_S_PROJ_DW, GPT_S_ATTN_BWD, GPT_S_QKV_DX, GPT_S_QKV_DW, GPT_S_BIAS_GRAD,
   GPT_S_EMBED_BWD, GPT_S_GRAD_NORM, GPT_S_ADAMW,
-  GPT_S_BLOCK_DW,  /* a block's four weight gradients as one grouped launch (+ reductions) */
+  GPT_S_BLOCK_DW,  /* a block's four weight gradients as one grouped launch (split partials) */
+  GPT_S_BLOCK_DW_REDUCE,  /* ... and the fixed-order reduction of its partials and bias sums */
   GPT_NUM_SITES
 } gpt_site;
 

@@ -119,3 +119,28 @@ def test_window_changes_only_attention_flops(L):
     full = dict(cfg, window_left=[-1] * 12)
     d = gpt.flops_per_token(full, 2048) - gpt.flops_per_token(cfg, 2048)
     assert d == 6 * 12 * 6 * 128 * (2048 - 512)
+
+
+def test_binding_rejects_bad_token_tensors():
+    """The binding hands the library only contiguous int32 CUDA tensors of B*T
+    entries; anything else is refused before any device call (CPU only)."""
+    import torch
+    good = torch.zeros(8, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        gpt.check_ids(torch.zeros(8, dtype=torch.int64), 8)
+    with pytest.raises(TypeError):
+        gpt.check_ids([0] * 8, 8)
+    with pytest.raises(ValueError):
+        gpt.check_ids(good, 8)  # not a CUDA tensor
+    if torch.cuda.is_available():  # pragma: no cover - CPU suite
+        return
+    # shape / contiguity checks run after the device check; exercise them on
+    # a tensor that claims to be on the device
+    t = torch.zeros(16, dtype=torch.int32)
+    import unittest.mock as um
+    with um.patch.object(torch.Tensor, "is_cuda", new_callable=um.PropertyMock, return_value=True):
+        gpt.check_ids(t[:8], 8)
+        with pytest.raises(ValueError):
+            gpt.check_ids(t, 8)
+        with pytest.raises(ValueError):
+            gpt.check_ids(t[::2], 8)

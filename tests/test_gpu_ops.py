@@ -450,9 +450,8 @@ def _stacked(batch, rows, K, trans, dt, seed):
 def test_gemm_batched(prec, batch, M, N, K, at, bt, epi):
     """Batched products (the Newton-Schulz iteration's launches): every matrix
     of the batch against its own product, with the AXPBY epilogue
-    out = alpha * acc + beta * aux."""
-    if prec == gpt.FP32 and M * N * K * batch > 1e9:
-        pytest.skip("the generic fp32 kernel is a correctness path; large shapes run in bf16")
+    out = alpha * acc + beta * aux.  At the GPT-2 124M Muon shapes the
+    reference takes sampled rows of every matrix (all columns)."""
     dt = torch.bfloat16 if prec == gpt.BF16 else torch.float32
     A, lda, sa, Ax = _stacked(batch, M, K, at, dt, 10)
     B, ldb, sb, Bx = _stacked(batch, N, K, bt, dt, 20)
@@ -469,10 +468,14 @@ def test_gemm_batched(prec, batch, M, N, K, at, bt, epi):
           flush=True)
     gpt.op_gemm(d)
     torch.cuda.synchronize()
-    got = rounded(out)
-    ref = np.matmul(Ax, Bx.transpose(0, 2, 1))
+    rows = np.arange(M)
+    if M * N * K * batch > 1e9:
+        rng = np.random.default_rng(M + N + K)
+        rows = np.unique(np.concatenate([rng.choice(M, 40, replace=False), [0, M - 1]]))
+    got = rounded(out)[:, rows]
+    ref = np.matmul(Ax[:, rows], Bx.transpose(0, 2, 1))
     if epi == gpt.EPI_AXPBY:
-        ref = alpha * ref + beta * rounded(aux)
+        ref = alpha * ref + beta * rounded(aux)[:, rows]
     tol = 1e-2 if prec == gpt.BF16 else 2e-5
     for z in range(batch):
         err = np.abs(got[z] - ref[z]).max() / np.abs(ref[z]).max()

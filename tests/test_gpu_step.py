@@ -287,3 +287,58 @@ def test_train_step_async_readback_matches_sync_path():
     b.adamw_step(1, scale)
     assert r["loss"] == loss and r["norm"] == norm and r["scale"] == scale
     assert np.array_equal(a.params().view(np.uint32), b.params().view(np.uint32))
+
+
+def test_out_of_range_ids_are_flagged_and_skip_the_update():
+    """Token ids / targets outside [0, vocab_size) are read as 0 (no
+    out-of-bounds access), the forward is flagged: its mean loss is NaN,
+    gpt_loss and gpt_grad_norm report INVALID, the next update leaves
+    parameters and moments untouched, and Model.train_step raises without
+    counting a step.  Clean forwards afterwards train normally."""
+    cfg = gpu_cfgs()["gpt2_s"]
+    V = cfg["vocab_size"]
+    m = gpt.Model(cfg)
+    m.set_params(synth.init_params(cfg, seed=2, perturb=True))
+    idx, tgt = synth.tokens(cfg, seed=3)
+    p0 = m.params().copy()
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32).reshape(-1)).cuda()
+    bad_idx = idx.copy()
+    bad_idx[0, 5] = V  # one past the real vocabulary (a padded row)
+    bad_tgt = tgt.copy()
+    bad_tgt[1, 7] = -1
+    with pytest.raises(gpt.GptError) as e:
+        m.train_step(dev(bad_idx), dev(tgt))
+    assert e.value.code == gpt.E_INVALID and m.step_t == 0
+    assert np.array_equal(m.params().view(np.uint32), p0.view(np.uint32))
+    assert not np.any(m.get_buffer(gpt.BUF_ADAM_M)) and not np.any(m.get_buffer(gpt.BUF_ADAM_V))
+    # synchronous calls: a bad target
+    m.forward(dev(idx), dev(bad_tgt))
+    with pytest.raises(gpt.GptError) as e:
+        m.loss()
+    assert e.value.code == gpt.E_INVALID
+    m.backward(0)
+    with pytest.raises(gpt.GptError) as e:
+        m.grad_norm()
+    assert e.value.code == gpt.E_INVALID
+    m.adamw_step(1, 1.0)
+    assert np.array_equal(m.params().view(np.uint32), p0.view(np.uint32))
+    # clean data: the step goes through and changes the weights
+    r = m.train_step(dev(idx), dev(tgt))
+    assert np.isfinite(r["loss"]) and m.step_t == 1
+    assert not np.array_equal(m.params().view(np.uint32), p0.view(np.uint32))
+
+
+def test_train_step_nonfinite_does_not_count_a_step():
+    """A non-finite gradient inside Model.train_step: the device skips the
+    update, the call raises and the AdamW step count is not advanced."""
+    cfg = gpu_cfgs()["gpt2_s"]
+    m = gpt.Model(cfg)
+    p = synth.init_params(cfg, seed=2)
+    p[oracle.n_params(cfg) // 2] = np.inf  # a weight inside a block matrix
+    m.set_params(p)
+    idx, tgt = synth.tokens(cfg, seed=3)
+    di, dt = torch.from_numpy(idx.reshape(-1)).cuda(), torch.from_numpy(tgt.reshape(-1)).cuda()
+    with pytest.raises(gpt.GptError):
+        m.train_step(di, dt)
+    assert m.step_t == 0
+    assert np.array_equal(m.params().view(np.uint32), p.view(np.uint32))
