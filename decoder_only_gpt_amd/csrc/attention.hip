@@ -30,7 +30,16 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <mutex>
+#include <vector>
+
 namespace gpt {
+
+// Device scratch of the allocation-free backward entry point: D and the
+// log-sum-exp in log2 units, 2 * B*H*T floats.  Every GPU the library runs on
+// holds its own copy until the process ends; host code reaches it only
+// through the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) float scratch[ATTN_SCRATCH_FLOATS];
 
 namespace {
 
@@ -733,6 +742,25 @@ hipError_t attention_fwd(int prec, int B, int T, int H, int hd, int left, const 
   attn_fwd_rows<float><<<(unsigned)cdiv(waves, 4), 256, 0, s>>>(
       (const float*)qkv, (float*)out, lse, B, T, H, hd, left, 1.f / sqrtf((float)hd));
   return hipGetLastError();
+}
+
+hipError_t attention_scratch(long floats, float** out) {
+  if (floats < 0 || floats > ATTN_SCRATCH_FLOATS) return hipErrorInvalidValue;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::vector<float*> addr;  // per device, filled on the first call there
+  std::lock_guard<std::mutex> lock(mu);
+  if ((size_t)dev >= addr.size()) addr.resize((size_t)dev + 1, nullptr);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = (float*)p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t attention_bwd(int prec, int B, int T, int H, int hd, int left, const void* qkv,

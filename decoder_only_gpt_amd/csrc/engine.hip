@@ -1428,6 +1428,23 @@ int gpt_op_attention_bwd(int32_t precision, int32_t B, int32_t T, int32_t H, int
   return GPT_OK;
 }
 
+int gpt_op_attention_bwd_noalloc(int32_t precision, int32_t B, int32_t T, int32_t H, int32_t hd,
+                                 int32_t left, const void* qkv, const void* out, const float* lse,
+                                 const void* dout, void* dqkv, void* stream) {
+  if (B < 0 || T < 0 || H < 0) return fail(GPT_E_INVALID, "negative size");
+  if (!gpt::attention_supported(precision, hd)) return fail(GPT_E_UNSUPPORTED, "head_dim");
+  const long need = 2L * B * H * T;
+  if (need > gpt::ATTN_SCRATCH_FLOATS)
+    return fail(GPT_E_INVALID, "B*H*T = " + std::to_string((long)B * H * T) +
+                                   " exceeds the static scratch (at most " +
+                                   std::to_string(gpt::ATTN_SCRATCH_FLOATS / 2) + " rows)");
+  float* ws = nullptr;
+  HIP_TRY(gpt::attention_scratch(need, &ws));
+  HIP_TRY(gpt::attention_bwd(precision, B, T, H, hd, left, qkv, out, lse, dout, dqkv, ws,
+                             (hipStream_t)stream));
+  return GPT_OK;
+}
+
 int gpt_op_adamw(int64_t n, float* p, float* m, float* v, const float* g, uint16_t* shadow,
                  const gpt_adamw_hp* hp, void* stream) {
   int rc = check_hp(hp);

@@ -34,6 +34,10 @@ hipError_t attention_bwd(int prec, int B, int T, int H, int hd, int left, const 
                          const void* out, const float* lse, const void* dout, void* dqkv,
                          float* dvec, hipStream_t s);  // dvec: 2 * B * H * T floats
 bool attention_supported(int prec, int hd);
+// The device address of this GPU's static attention scratch (floats) for a
+// caller that needs `floats` of it; hipErrorInvalidValue beyond the maximum.
+constexpr long ATTN_SCRATCH_FLOATS = 2L << 20;  // 8 MiB: B*H*T <= 1,048,576
+hipError_t attention_scratch(long floats, float** out);
 
 // Row-wise kernels (rowwise.hip).
 // Ids outside [0, V) are read as 0 and mark *flag = gen; ids_out (may be

@@ -33,7 +33,7 @@ EXPORTS = [
     "gpt_set_buffer", "gpt_destroy", "gpt_gen_plan", "gpt_gen_init", "gpt_gen_reset",
     "gpt_gen_step", "gpt_gen_logits", "gpt_gen_sample", "gpt_generate", "gpt_gen_destroy",
     "gpt_last_error", "gpt_op_gemm", "gpt_op_gemm_group", "gpt_op_gemm_group_workspace",
-    "gpt_op_attention_fwd", "gpt_op_attention_bwd",
+    "gpt_op_attention_fwd", "gpt_op_attention_bwd", "gpt_op_attention_bwd_noalloc",
     "gpt_op_adamw", "gpt_profile_begin",
     "gpt_profile_end",
 ]
@@ -159,6 +159,8 @@ def lib():
                                          i32, i32], i64),
         "gpt_op_attention_fwd": ([i32, i32, i32, i32, i32, i32, vp, vp, vp, vp], i32),
         "gpt_op_attention_bwd": ([i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp], i32),
+        "gpt_op_attention_bwd_noalloc": ([i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp],
+                                         i32),
         "gpt_op_adamw": ([i64, vp, vp, vp, vp, vp, ctypes.POINTER(AdamHP), vp], i32),
         "gpt_profile_begin": ([vp], i32),
         "gpt_profile_end": ([vp, vp, ctypes.POINTER(KernelStats), ctypes.POINTER(KernelStats)], i32),
@@ -482,6 +484,11 @@ def op_attention_fwd(precision, B, T, H, hd, left, qkv, out, lse):
 def op_attention_bwd(precision, B, T, H, hd, left, qkv, out, lse, dout, dqkv, workspace):
     _check(lib().gpt_op_attention_bwd(precision, B, T, H, hd, left, _ptr(qkv), _ptr(out), _ptr(lse),
                                       _ptr(dout), _ptr(dqkv), _ptr(workspace), _stream()))
+
+
+def op_attention_bwd_noalloc(precision, B, T, H, hd, left, qkv, out, lse, dout, dqkv):
+    _check(lib().gpt_op_attention_bwd_noalloc(precision, B, T, H, hd, left, _ptr(qkv), _ptr(out),
+                                              _ptr(lse), _ptr(dout), _ptr(dqkv), _stream()))
 
 
 def op_adamw(p, m, v, g, shadow, hp: AdamHP):

@@ -420,6 +420,20 @@ int gpt_op_attention_bwd(int32_t precision, int32_t B, int32_t T, int32_t H, int
                          int32_t left, const void* qkv, const void* out, const float* lse,
                          const void* dout, void* dqkv, float* workspace, void* stream);
 
+/* gpt_op_attention_bwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and the same result, bit for bit, with no
+ * workspace argument.  D and the log2-unit log-sum-exp live in a static
+ * device array of 2^21 floats (8 MiB) per GPU, held until the process ends,
+ * so B*H*T <= 1,048,576; larger sizes return GPT_E_INVALID before any launch.
+ * The call allocates nothing (no hipMalloc / hipFree / allocating library
+ * call).  Every call on one GPU shares that array: calls that overlap on one
+ * GPU (concurrent streams, threads) race; calls ordered on one stream are
+ * safe.  Nothing in the array needs to start at zero. */
+int gpt_op_attention_bwd_noalloc(int32_t precision, int32_t B, int32_t T, int32_t H, int32_t hd,
+                                 int32_t left, const void* qkv, const void* out, const float* lse,
+                                 const void* dout, void* dqkv, void* stream);
+
 /* The AdamW update on raw device float arrays of n entries; `shadow`
  * (bf16, n entries) is written when non-NULL. */
 int gpt_op_adamw(int64_t n, float* p, float* m, float* v, const float* g, uint16_t* shadow,
