@@ -32,6 +32,12 @@ BASE_FLAGS = [
 ]
 
 
+# Host-code sanitizers for the checked build of the C-ABI host logic (GPU code
+# is never built with them).
+SAN_FLAGS = "-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined".split()
+SAN_LIB = os.path.join(OUT_DIR, "libgptmi_san.so")
+
+
 def hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
         if c and (os.path.sep not in c or os.path.exists(c)):
@@ -63,6 +69,46 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_sanitized(verbose: bool = False) -> str:
+    """libgptmi_san.so: the library with the host side of engine.hip (config
+    checks, arena plan, parameter layout, call-order state machine, ABI
+    entry points) built with AddressSanitizer and UBSan.  Load it with the
+    sanitizer runtime preloaded (sanitizer_runtime())."""
+    os.makedirs(OUT_DIR, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        if src == "engine.hip":
+            obj = os.path.join(OUT_DIR, "engine_san.o")
+            cmd = [hipcc(), *BASE_FLAGS, *SAN_FLAGS, "-Xarch_host", "-fno-omit-frame-pointer", "-c",
+                   os.path.join(CSRC, src), "-o", obj]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"sanitized compile failed:\n{' '.join(cmd)}\n{r.stderr}")
+            objs.append(obj)
+        else:
+            obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
+            if not os.path.exists(obj):
+                obj = _compile(src)
+            objs.append(obj)
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", SAN_LIB, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized link failed:\n{' '.join(cmd)}\n{r.stderr}")
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
+def sanitizer_runtime() -> str:
+    """Path of the AddressSanitizer runtime shared library of this hipcc."""
+    r = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                       text=True, check=True)
+    return r.stdout.strip()
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if len(sys.argv) > 1 and sys.argv[1] == "--sanitized":
+        build_sanitized(verbose=True)
+    else:
+        build(verbose=True)
     sys.exit(0)
