@@ -31,6 +31,7 @@
 #include "kernels.h"
 
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 namespace gpt {
@@ -440,18 +441,39 @@ __global__ void __launch_bounds__(256, HD == 128 ? 1 : 2)
   }
 }
 
+// Scheduling of one phase of a software-pipelined tile: MFMA i of the phase,
+// then its share of the LDS reads (of the next phase's fragments) and of the
+// VALU work, for i = 0 .. NM - 1.
+template <int NM, int NDS, int NV, int I = 0> __device__ __forceinline__ void phase_pattern() {
+  if constexpr (I < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    constexpr int ds = NDS / NM + (I < NDS % NM ? 1 : 0);
+    constexpr int nv = NV / NM + (I < NV % NM ? 1 : 0);
+    if constexpr (ds > 0) __builtin_amdgcn_sched_group_barrier(0x100, ds, 0);
+    if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(0x002, nv, 0);
+    phase_pattern<NM, NDS, NV, I + 1>();
+  }
+}
+
 // dK, dV: 128 keys of one (batch, head) per workgroup, 32 per wave; the
-// workgroup walks the 64-query blocks that can see them.  L2 is the saved
-// log-sum-exp in log2 units, D[q] = sum_d dO[q][d] O[q][d].
+// workgroup walks 128-query tiles of Q and dO (QT rows each, two LDS stages,
+// with the per-query L2 and D).  L2 is the saved log-sum-exp in log2 units,
+// D[q] = sum_d dO[q][d] O[q][d].  A tile whose (query, key) pairs are all
+// visible runs its four 32-query sub-blocks without masks or per-sub-block
+// branches; other tiles (diagonal, window edge, sequence end) take a
+// per-sub-block masked path.  (A software pipeline like the dQ kernel's needs
+// more registers than two waves per SIMD leave here: it spills.)
+constexpr int QT = 128;  // queries per LDS tile of the dK/dV kernel
+
 template <int HD>
 __global__ void __launch_bounds__(256, HD == 128 ? 1 : 2)
     attn_dkv_mfma(const bf16_t* qkv, const float* L2, const bf16_t* dout, const float* D,
                   bf16_t* dqkv, int Tn, int H, int left, float scale, float scale_log2) {
   constexpr int NS = HD / 16, ND = HD / 32;
-  __shared__ __attribute__((aligned(16))) bf16_t Qs[2][KB * HD];
-  __shared__ __attribute__((aligned(16))) bf16_t Gs[2][KB * HD];
-  __shared__ __attribute__((aligned(16))) float Ls[2][KB];
-  __shared__ __attribute__((aligned(16))) float Ds[2][KB];
+  __shared__ __attribute__((aligned(16))) bf16_t Qs[2][QT * HD];
+  __shared__ __attribute__((aligned(16))) bf16_t Gs[2][QT * HD];
+  __shared__ __attribute__((aligned(16))) float Ls[2][QT];
+  __shared__ __attribute__((aligned(16))) float Ds[2][QT];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5, c = lane & 31;
   const int h = blockIdx.x % H, b = blockIdx.x / H;
@@ -483,86 +505,127 @@ __global__ void __launch_bounds__(256, HD == 128 ? 1 : 2)
   const int klast = min(Tn - 1, kblk0 + 127);
   const int qend = left < 0 ? Tn - 1 : min(Tn - 1, klast + left);
 
-  auto step = [&](const bf16_t* Qt, const bf16_t* Gt, const float* Lt, const float* Dt, int qb0,
-                  auto mask) {
+  // S and dP of the 32 queries at tile row r0 (s[r], dp[r]: query r0 +
+  // acc_row(r, g), key kj), from fragments qr / gr.
+  auto sdp = [&](f32x16& s, f32x16& dp, const bf16x8* qr, const bf16x8* gr) {
+    s = f32x16{};
+    dp = f32x16{};
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qr[st], kf[st], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gr[st], vf[st], dp, 0, 0, 0);
+    }
+  };
+  auto rows = [&](bf16x8* qr, bf16x8* gr, const bf16_t* Qt, const bf16_t* Gt, int r0) {
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      qr[st] = row_frag<HD>(Qt, r0, st, lane);
+      gr[st] = row_frag<HD>(Gt, r0, st, lane);
+    }
+  };
+  // P = exp2(S log2e / sqrt(hd) - L2), dS = P (dP - D) as bf16 operands; MASK
+  // zeroes P outside the visible band (qb = the sub-block's first query).
+  auto soft = [&](f32x16& s, f32x16& dp, const float* Lt, const float* Dt, int r0, bf16x8* pa,
+                  bf16x8* da, auto mask, int qb) {
     constexpr bool MASK = decltype(mask)::value;
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-      f32x16 s{}, dp{};
-      __builtin_amdgcn_s_setprio(1);
+    for (int i = 0; i < 4; ++i) {
+      const int ql = r0 + 8 * i + 4 * g;
+      const f32x4 lv = *(const f32x4*)(Lt + ql);
+      const f32x4 dd = *(const f32x4*)(Dt + ql);
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<HD>(Qt, qq * 32, st, lane), kf[st], s,
-                                                    0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<HD>(Gt, qq * 32, st, lane), vf[st],
-                                                     dp, 0, 0, 0);
-      }
-      __builtin_amdgcn_s_setprio(0);
-      // s[r], dp[r]: query qb0 + qq * 32 + acc_row(r, g), key kj.
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ql = qq * 32 + 8 * i + 4 * g;
-        const f32x4 lv = *(const f32x4*)(Lt + ql);
-        const f32x4 dd = *(const f32x4*)(Dt + ql);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float p = __builtin_amdgcn_exp2f(fmaf(s[4 * i + j], scale_log2, -lv[j]));
-          if constexpr (MASK) {
-            const int qi = qb0 + ql + j;
-            if (qi >= Tn || !visible(qi, kj, left, Tn)) p = 0.f;
-          }
-          s[4 * i + j] = p;
-          dp[4 * i + j] = p * (dp[4 * i + j] - dd[j]);
+      for (int j = 0; j < 4; ++j) {
+        float p = __builtin_amdgcn_exp2f(fmaf(s[4 * i + j], scale_log2, -lv[j]));
+        if constexpr (MASK) {
+          const int qi = qb + 8 * i + 4 * g + j;
+          if (qi >= Tn || !visible(qi, kj, left, Tn)) p = 0.f;
         }
+        s[4 * i + j] = p;
+        dp[4 * i + j] = p * (dp[4 * i + j] - dd[j]);
       }
-      __builtin_amdgcn_s_setprio(1);
-      // dV^T[d][key] += dO^T[d][q] P[q][key];  dK^T[d][key] += Q^T[d][q] dS[q][key]
+    }
+    pa[0] = acc_slots(s, 0);
+    pa[1] = acc_slots(s, 1);
+    da[0] = acc_slots(dp, 0);
+    da[1] = acc_slots(dp, 1);
+  };
+  // dV^T[d][key] += dO^T[d][q] P[q][key];  dK^T[d][key] += Q^T[d][q] dS[q][key]
+  // over the 32 queries at tile row r0; the transposed fragments of each
+  // 16-query half are read just before its MFMAs.
+  auto dvk = [&](const bf16_t* Qt, const bf16_t* Gt, int r0, const bf16x8* pa, const bf16x8* da) {
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const bf16x8 pa = acc_slots(s, s2);
-        const bf16x8 da = acc_slots(dp, s2);
+    for (int s2 = 0; s2 < 2; ++s2) {
+      bf16x8 tg[ND], tq[ND];
 #pragma unroll
-        for (int d = 0; d < ND; ++d) {
-          dv[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              tr_slots<HD>(Gt, d * 32, qq * 32 + 16 * s2, lane), pa, dv[d], 0, 0, 0);
-          dk[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              tr_slots<HD>(Qt, d * 32, qq * 32 + 16 * s2, lane), da, dk[d], 0, 0, 0);
-        }
+      for (int d = 0; d < ND; ++d) {
+        tg[d] = tr_slots<HD>(Gt, d * 32, r0 + 16 * s2, lane);
+        tq[d] = tr_slots<HD>(Qt, d * 32, r0 + 16 * s2, lane);
       }
-      __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        dv[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tg[d], pa[s2], dv[d], 0, 0, 0);
+        dk[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq[d], da[s2], dk[d], 0, 0, 0);
+      }
     }
   };
 
-  // Per-query scalars travel through registers (one per thread of the first wave).
+  // Per-query scalars travel through registers (one per thread of the first two waves).
   float rl = 0.f, rd = 0.f;
   auto fetch = [&](int q0, int bb) {
-    dma_tile<HD>(rq, ld, h * HD, q0, Tn, Qs[bb], wave, lane);
-    dma_tile<HD>(rg, C, h * HD, q0, Tn, Gs[bb], wave, lane);
-    if (threadIdx.x < KB) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      dma_tile<HD>(rq, ld, h * HD, q0 + 64 * half, Tn, Qs[bb] + 64 * half * HD, wave, lane);
+      dma_tile<HD>(rg, C, h * HD, q0 + 64 * half, Tn, Gs[bb] + 64 * half * HD, wave, lane);
+    }
+    if (threadIdx.x < QT) {
       const int q = q0 + threadIdx.x;
       rl = q < Tn ? lrow[q] : 0.f;
       rd = q < Tn ? drow[q] : 0.f;
     }
   };
   fetch(kblk0, 0);
-  if (threadIdx.x < KB) {
+  if (threadIdx.x < QT) {
     Ls[0][threadIdx.x] = rl;
     Ds[0][threadIdx.x] = rd;
   }
   int buf = 0;
-  for (int qb0 = kblk0; qb0 <= qend; qb0 += KB, buf ^= 1) {
+  for (int qb0 = kblk0; qb0 <= qend; qb0 += QT, buf ^= 1) {
     __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's share of block qb0 landed
     __syncthreads();                     // ... and every other wave's (tiles and scalars)
-    const bool more = qb0 + KB <= qend;
-    if (more) fetch(qb0 + KB, buf ^ 1);
-    const bool skip = qb0 + KB - 1 < kw0 || (left >= 0 && qb0 > kw0 + 31 + left);
-    if (!skip) {
-      const bool full =
-          qb0 >= kw0 + 31 && qb0 + KB <= Tn && (left < 0 || qb0 + KB - 1 - kw0 <= left);
-      if (full) step(Qs[buf], Gs[buf], Ls[buf], Ds[buf], qb0, Mask<false>{});
-      else step(Qs[buf], Gs[buf], Ls[buf], Ds[buf], qb0, Mask<true>{});
+    const bool more = qb0 + QT <= qend;
+    if (more) fetch(qb0 + QT, buf ^ 1);
+    const bf16_t* Qt = Qs[buf];
+    const bf16_t* Gt = Gs[buf];
+    const float* Lt = Ls[buf];
+    const float* Dt = Ds[buf];
+    // every (query, key) pair of the workgroup visible in this tile: uniform branch
+    const bool full = qb0 >= kblk0 + 127 && qb0 + QT <= Tn &&
+                      (left < 0 || qb0 + QT - 1 - kblk0 <= left);
+    if (full) {
+      f32x16 s, dp;
+      bf16x8 qr[NS], gr[NS], pa[2], da[2];
+#pragma unroll 1
+      for (int j = 0; j < QT / 32; ++j) {
+        rows(qr, gr, Qt, Gt, 32 * j);
+        sdp(s, dp, qr, gr);
+        soft(s, dp, Lt, Dt, 32 * j, pa, da, Mask<false>{}, 0);
+        dvk(Qt, Gt, 32 * j, pa, da);
+      }
+    } else {
+#pragma unroll 1
+      for (int j = 0; j < QT / 32; ++j) {
+        const int qb = qb0 + 32 * j;
+        const bool skip = qb + 31 < kw0 || (left >= 0 && qb > kw0 + 31 + left) || qb >= Tn;
+        if (skip) continue;
+        f32x16 s, dp;
+        bf16x8 qr[NS], gr[NS], pa[2], da[2];
+        rows(qr, gr, Qt, Gt, 32 * j);
+        sdp(s, dp, qr, gr);
+        soft(s, dp, Lt, Dt, 32 * j, pa, da, Mask<true>{}, qb);
+        dvk(Qt, Gt, 32 * j, pa, da);
+      }
     }
-    if (more && threadIdx.x < KB) {
+    if (more && threadIdx.x < QT) {
       Ls[buf ^ 1][threadIdx.x] = rl;
       Ds[buf ^ 1][threadIdx.x] = rd;
     }
@@ -578,15 +641,23 @@ __global__ void __launch_bounds__(256, HD == 128 ? 1 : 2)
 }
 
 // dQ: 128 queries of one (batch, head) per workgroup, 32 per wave; the
-// workgroup walks their key blocks.
+// workgroup walks 128-key tiles of K and V (KT rows each, two LDS stages).
+// A tile whose 128 x 128 (query, key) pairs are all visible is multiplied in
+// a software pipeline over its four 32-key sub-blocks: the MFMAs of S and dP
+// for sub-block n + 1 and of dQ for sub-block n - 1 are issued between the
+// VALU instructions that rebuild P and dS for sub-block n, so the matrix unit
+// and the ALUs work at the same time within one wave.  Tiles on the diagonal,
+// at a window edge or past the sequence end take a per-sub-block masked path.
+constexpr int KT = 128;  // keys per LDS tile of the dQ kernel
+
 template <int HD>
 __global__ void __launch_bounds__(256, HD == 128 ? 1 : 2)
     attn_dq_mfma(const bf16_t* qkv, const float* lse, const bf16_t* out, const bf16_t* dout,
                  float* D, float* L2, bf16_t* dqkv, int Tn, int H, int left, float scale,
                  float scale_log2) {
   constexpr int NS = HD / 16, ND = HD / 32;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KB * HD];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][KB * HD];
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KT * HD];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][KT * HD];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5, c = lane & 31;
   const int h = blockIdx.x % H, b = blockIdx.x / H;
@@ -627,61 +698,155 @@ __global__ void __launch_bounds__(256, HD == 128 ? 1 : 2)
   for (int d = 0; d < ND; ++d) dq[d] = f32x16{};
 
   const int qlast = min(Tn - 1, qblk0 + 127);
-  const int kstart = left < 0 ? 0 : (max(0, qblk0 - left) / KB) * KB;
+  const int kstart = left < 0 ? 0 : (max(0, qblk0 - left) / KT) * KT;
 
-  auto step = [&](const bf16_t* Kt, const bf16_t* Vt, int kb0, auto mask) {
-    constexpr bool MASK = decltype(mask)::value;
+  // S^T and dP^T of the 32-key sub-block at tile row kr: s[r], dp[r] hold key
+  // kr + acc_row(r, g) for query qi.
+  auto sdp = [&](f32x16& s, f32x16& dp, const bf16_t* Kt, const bf16_t* Vt, int kr) {
+    s = f32x16{};
+    dp = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      f32x16 s{}, dp{};
-      __builtin_amdgcn_s_setprio(1);
+    for (int st = 0; st < NS; ++st) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<HD>(Kt, kr, st, lane), qf[st], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<HD>(Vt, kr, st, lane), gf[st], dp, 0, 0,
+                                                   0);
+    }
+  };
+  // P = exp2(S log2e / sqrt(hd) - L2), dS = P (dP - D), as two bf16 operands.
+  auto soft = [&](const f32x16& s, const f32x16& dp, bf16x8* da) {
+    f32x16 ds;
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<HD>(Kt, kk * 32, st, lane), qf[st], s,
-                                                    0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<HD>(Vt, kk * 32, st, lane), gf[st],
-                                                     dp, 0, 0, 0);
-      }
-      __builtin_amdgcn_s_setprio(0);
-      // s[r], dp[r]: key kb0 + kk * 32 + acc_row(r, g), query qi.
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -Lq));
+      ds[r] = p * (dp[r] - Dq);
+    }
+    da[0] = acc_slots(ds, 0);
+    da[1] = acc_slots(ds, 1);
+  };
+  // dQ^T[d][q] += K^T[d][key] dS^T[key][q] over the sub-block at tile row kr.
+  auto dqm = [&](const bf16x8* da, const bf16_t* Kt, int kr) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -Lq));
-        if constexpr (MASK) {
-          if (!visible(qi, kb0 + kk * 32 + acc_row(r, g), left, Tn)) p = 0.f;
-        }
-        dp[r] = p * (dp[r] - Dq);
-      }
-      __builtin_amdgcn_s_setprio(1);
-      // dQ^T[d][q] += K^T[d][key] dS^T[key][q]
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const bf16x8 da = acc_slots(dp, s2);
+      for (int d = 0; d < ND; ++d)
+        dq[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_slots<HD>(Kt, d * 32, kr + 16 * s2, lane),
+                                                        da[s2], dq[d], 0, 0, 0);
+  };
+  // One masked 32-key sub-block (diagonal, window edge, sequence end).
+  auto masked = [&](const bf16_t* Kt, const bf16_t* Vt, int kr, int kb) {
+    f32x16 s, dp;
+    sdp(s, dp, Kt, Vt, kr);
 #pragma unroll
-        for (int d = 0; d < ND; ++d)
-          dq[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              tr_slots<HD>(Kt, d * 32, kk * 32 + 16 * s2, lane), da, dq[d], 0, 0, 0);
-      }
-      __builtin_amdgcn_s_setprio(0);
+    for (int r = 0; r < 16; ++r) {
+      float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -Lq));
+      if (!visible(qi, kb + acc_row(r, g), left, Tn)) p = 0.f;
+      dp[r] = p * (dp[r] - Dq);
+    }
+    const bf16x8 da[2] = {acc_slots(dp, 0), acc_slots(dp, 1)};
+    dqm(da, Kt, kr);
+  };
+  // Scheduling pattern of a pipeline phase: the LDS reads first, then each
+  // MFMA followed by an equal share of the VALU work.
+  constexpr int SDP_M = 2 * NS, DQ_M = 2 * ND;       // MFMAs of sdp / dqm
+  constexpr int SDP_R = 2 * NS, DQ_R = 4 * ND;       // LDS read instructions
+  constexpr int SOFT_V = 16 * 4 + 8;                 // VALU instructions of soft
+  auto fetch = [&](int k0, int bb) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      dma_tile<HD>(rs, ld, C + h * HD, k0 + 64 * half, Tn, Ks[bb] + 64 * half * HD, wave, lane);
+      dma_tile<HD>(rs, ld, 2 * C + h * HD, k0 + 64 * half, Tn, Vs[bb] + 64 * half * HD, wave, lane);
     }
   };
 
-  dma_tile<HD>(rs, ld, C + h * HD, kstart, Tn, Ks[0], wave, lane);
-  dma_tile<HD>(rs, ld, 2 * C + h * HD, kstart, Tn, Vs[0], wave, lane);
+  fetch(kstart, 0);
   int buf = 0;
-  for (int kb0 = kstart; kb0 <= qlast; kb0 += KB, buf ^= 1) {
+  for (int kb0 = kstart; kb0 <= qlast; kb0 += KT, buf ^= 1) {
     __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's share of tile kb0 landed
     __syncthreads();                     // ... and every other wave's
-    if (kb0 + KB <= qlast) {
-      dma_tile<HD>(rs, ld, C + h * HD, kb0 + KB, Tn, Ks[buf ^ 1], wave, lane);
-      dma_tile<HD>(rs, ld, 2 * C + h * HD, kb0 + KB, Tn, Vs[buf ^ 1], wave, lane);
+    if (kb0 + KT <= qlast) fetch(kb0 + KT, buf ^ 1);
+    const bf16_t* Kt = Ks[buf];
+    const bf16_t* Vt = Vs[buf];
+    // every (query, key) pair of the workgroup visible in this tile: uniform branch
+    const bool full = kb0 + KT - 1 <= qblk0 && qblk0 + 127 < Tn &&
+                      (left < 0 || qblk0 + 127 - kb0 <= left);
+    if (full) {
+      // Fragments are read one phase ahead of the MFMAs that use them, each
+      // read issued right after the MFMA that frees its registers.
+      f32x16 s0, p0, s1, p1;
+      bf16x8 a0[2], a1[2], kr[NS], vr[NS], tf[2][ND];
+      auto rows = [&](int r0) {
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          kr[st] = row_frag<HD>(Kt, r0, st, lane);
+          vr[st] = row_frag<HD>(Vt, r0, st, lane);
+        }
+      };
+      auto trs = [&](int r0) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int d = 0; d < ND; ++d) tf[s2][d] = tr_slots<HD>(Kt, d * 32, r0 + 16 * s2, lane);
+      };
+      auto sdp_m = [&](f32x16& s, f32x16& dp) {
+        s = f32x16{};
+        dp = f32x16{};
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[st], qf[st], s, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[st], gf[st], dp, 0, 0, 0);
+        }
+      };
+      auto dqm_m = [&](const bf16x8* da) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int d = 0; d < ND; ++d)
+            dq[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[s2][d], da[s2], dq[d], 0, 0, 0);
+      };
+      rows(0);
+      __builtin_amdgcn_sched_barrier(0);
+      sdp_m(s0, p0);
+      rows(32);
+      __builtin_amdgcn_sched_barrier(0);
+      // phase 1: S, dP of sub-block 1; P, dS of 0
+      sdp_m(s1, p1);
+      trs(0);
+      rows(64);
+      soft(s0, p0, a0);
+      phase_pattern<SDP_M, SDP_R + DQ_R, SOFT_V>();
+      __builtin_amdgcn_sched_barrier(0);
+      // phase 2: dQ of 0, S, dP of 2; P, dS of 1
+      dqm_m(a0);
+      trs(32);
+      sdp_m(s0, p0);
+      rows(96);
+      soft(s1, p1, a1);
+      phase_pattern<SDP_M + DQ_M, SDP_R + DQ_R, SOFT_V>();
+      __builtin_amdgcn_sched_barrier(0);
+      // phase 3: dQ of 1, S, dP of 3; P, dS of 2
+      dqm_m(a1);
+      trs(64);
+      sdp_m(s1, p1);
+      soft(s0, p0, a0);
+      phase_pattern<SDP_M + DQ_M, DQ_R, SOFT_V>();
+      __builtin_amdgcn_sched_barrier(0);
+      // phase 4: dQ of 2; P, dS of 3
+      dqm_m(a0);
+      trs(96);
+      soft(s1, p1, a1);
+      phase_pattern<DQ_M, DQ_R, SOFT_V>();
+      __builtin_amdgcn_sched_barrier(0);
+      // phase 5: dQ of 3
+      dqm_m(a1);
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+#pragma unroll 1
+      for (int kk = 0; kk < KT / 32; ++kk) {
+        const int kb = kb0 + 32 * kk;
+        const bool skip = kb > qw0 + 31 || (left >= 0 && kb + 31 < qw0 - left);
+        if (!skip) masked(Kt, Vt, 32 * kk, kb);
+      }
     }
-    const bool skip = kb0 > qw0 + 31 || (left >= 0 && kb0 + KB - 1 < qw0 - left);
-    if (skip) continue;
-    const bool full =
-        kb0 + KB - 1 <= qw0 && qw0 + 31 < Tn && (left < 0 || qw0 + 31 - kb0 <= left);
-    if (full) step(Ks[buf], Vs[buf], kb0, Mask<false>{});
-    else step(Ks[buf], Vs[buf], kb0, Mask<true>{});
   }
   if (qi < Tn) {
     bf16_t* row = dqkv + ((long)b * Tn + qi) * ld + h * HD;

@@ -278,6 +278,9 @@ ATT = [  # B, T, H, hd, left
     (1, 260, 2, 128, 64),
     (1, 129, 3, 128, -1),
     (1, 190, 2, 32, 17),
+    (1, 600, 2, 64, 400),   # unmasked 128-row tiles inside a window, ragged end
+    (1, 700, 1, 128, 300),
+    (1, 512, 2, 32, -1),
 ]
 
 
