@@ -26,9 +26,11 @@ namespace {
 
 __global__ void __launch_bounds__(256) gen_embed_kernel(const int32_t* __restrict__ tok,
                                                         const float* __restrict__ wte,
-                                                        const float* __restrict__ wpe, int pos,
+                                                        const float* __restrict__ wpe,
+                                                        const int32_t* __restrict__ pos_ptr,
                                                         int C, int V, float* __restrict__ x) {
   const int b = blockIdx.x;
+  const int pos = *pos_ptr;
   const long t = checked_id(tok[b], V, nullptr, 0);  // out-of-range ids read row 0
   for (int c = threadIdx.x * 4; c < C; c += 256 * 4) {  // C % 64 == 0
     const float4 e = *(const float4*)(wte + t * C + c);
@@ -41,8 +43,10 @@ constexpr int AD_THREADS = 256;
 
 template <typename ActT, int HD>
 __global__ void __launch_bounds__(AD_THREADS) attn_decode_kernel(
-    const ActT* __restrict__ qkv, ActT* __restrict__ kc, ActT* __restrict__ vc, int pos,
-    int Tmax, int H, int left, float scale, ActT* __restrict__ out) {
+    const ActT* __restrict__ qkv, ActT* __restrict__ kc, ActT* __restrict__ vc,
+    const int32_t* __restrict__ pos_ptr, int Tmax, int H, int left, float scale,
+    ActT* __restrict__ out) {
+  const int pos = *pos_ptr;
   __shared__ float q[HD];
   __shared__ float red[AD_THREADS];
   __shared__ float part[AD_THREADS][33];
@@ -120,9 +124,11 @@ constexpr int AW_WAVES = 16, AW_DEPTH = 4;
 
 template <int HD>
 __global__ void __launch_bounds__(AW_WAVES * 64) attn_decode_wide_kernel(
-    const bf16_t* __restrict__ qkv, bf16_t* __restrict__ kc, bf16_t* __restrict__ vc, int pos,
-    int Tmax, int H, int left, float scale, bf16_t* __restrict__ out) {
+    const bf16_t* __restrict__ qkv, bf16_t* __restrict__ kc, bf16_t* __restrict__ vc,
+    const int32_t* __restrict__ pos_ptr, int Tmax, int H, int left, float scale,
+    bf16_t* __restrict__ out) {
   constexpr int LPK = HD / 8, KPB = 64 / LPK;
+  const int pos = *pos_ptr;
   __shared__ float wmax[AW_WAVES], wsum[AW_WAVES];
   __shared__ float wo[AW_WAVES][HD];
   const int bh = blockIdx.x, b = bh / H, h = bh - b * H;
@@ -538,11 +544,30 @@ __global__ void copy_prompt_kernel(const int32_t* __restrict__ prompt, int T0, i
   }
 }
 
+// The decode position lives in device memory, so a captured step serves
+// every position: set at a reset, advanced by the last kernel of a step.
+__global__ void gen_set_pos_kernel(int32_t* pos, int32_t v) {
+  if (threadIdx.x == 0) *pos = v;
+}
+__global__ void gen_advance_kernel(int32_t* pos) {
+  if (threadIdx.x == 0) *pos += 1;
+}
+
 }  // namespace
 
-hipError_t gen_embed(const int32_t* tok, const float* wte, const float* wpe, int pos, int B, int C,
-                     int V, float* x, hipStream_t s) {
+hipError_t gen_embed(const int32_t* tok, const float* wte, const float* wpe, const int32_t* pos,
+                     int B, int C, int V, float* x, hipStream_t s) {
   gen_embed_kernel<<<B, 256, 0, s>>>(tok, wte, wpe, pos, C, V, x);
+  return hipGetLastError();
+}
+
+hipError_t gen_set_pos(int32_t* pos, int32_t v, hipStream_t s) {
+  gen_set_pos_kernel<<<1, 64, 0, s>>>(pos, v);
+  return hipGetLastError();
+}
+
+hipError_t gen_advance(int32_t* pos, hipStream_t s) {
+  gen_advance_kernel<<<1, 64, 0, s>>>(pos);
   return hipGetLastError();
 }
 
@@ -585,8 +610,8 @@ hipError_t rows_linear(const RowsLinear& p, hipStream_t s) {
 
 bool attn_decode_supported(int hd) { return hd == 32 || hd == 64 || hd == 128; }
 
-hipError_t attn_decode(int prec, int hd, const void* qkv, void* kc, void* vc, int pos, int Tmax,
-                       int B, int H, int left, void* out, hipStream_t s) {
+hipError_t attn_decode(int prec, int hd, const void* qkv, void* kc, void* vc, const int32_t* pos,
+                       int Tmax, int B, int H, int left, void* out, hipStream_t s) {
   const float scale = 1.0f / sqrtf((float)hd);
 #define AD_(T, D)                                                                            \
   attn_decode_kernel<T, D><<<B * H, AD_THREADS, 0, s>>>((const T*)qkv, (T*)kc, (T*)vc, pos, \

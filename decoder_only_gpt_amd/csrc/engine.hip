@@ -836,7 +836,16 @@ struct gpt_gen {
   gpt_model* m;
   int B, Tmax, pos;
   char* base;
-  int64_t kc, vc, x, a, qkv, att, u, gact, mean, rstd, logits, tok, ws, ws_bytes, total;
+  int64_t kc, vc, x, a, qkv, att, u, gact, mean, rstd, logits, tok, ws, ws_bytes, posd, total;
+  // The device copy of pos (posd) is what the kernels read; pos_dirty: the
+  // host moved pos (reset) and the device copy is set before the next step.
+  bool pos_dirty = false;
+  // Decode steps after the token embedding replay one captured HIP graph
+  // (captured on `cap` at the first step that needs it).
+  bool use_graph = true;
+  hipStream_t cap = nullptr;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
 };
 
 namespace {
@@ -857,6 +866,7 @@ int64_t gen_layout(const gpt_model* m, int B, int Tmax, gpt_gen* g) {
   g->rstd = take(B * 4);
   g->logits = take(B * m->Vq * act);
   g->tok = take(B * 4);
+  g->posd = take(16);
   // split-K partials of the fp32 decode products (at most 32 splits of B x max(3C, F) floats)
   g->ws_bytes = 32 * (int64_t)B * std::max(3 * C, F) * 4;
   g->ws = take(g->ws_bytes);
@@ -927,11 +937,11 @@ hipError_t gen_linear(const gpt_gen* g, const void* a, int64_t K, int64_t w_off,
   return gpt::gemm(d, s);
 }
 
-int gen_step(gpt_gen* g, const int32_t* d_tok, hipStream_t s) {
+// Everything of a decode step after the token embedding (x already holds the
+// embedded rows): the blocks, the final LayerNorm, the lm_head and the
+// position advance.  Only kernel launches: it is captured into a graph.
+int gen_body(gpt_gen* g, hipStream_t s) {
   gpt_model* m = g->m;
-  if (g->pos >= g->Tmax) return fail(GPT_E_INVALID, "the cache is full (Tmax tokens)");
-  int rc = wait_adam(m, s, -1);
-  if (rc != GPT_OK) return rc;
   const gpt_config& c = m->cfg;
   const int prec = m->prec();
   const int B = g->B;
@@ -942,14 +952,13 @@ int gen_step(gpt_gen* g, const int32_t* d_tok, hipStream_t s) {
   float* mean = (float*)(base + g->mean);
   float* rstd = (float*)(base + g->rstd);
   const int64_t cache_layer = (int64_t)B * m->H * g->Tmax * m->hd * act;
-  HIP_TRY(gpt::gen_embed(d_tok, m->P(m->pl.wte), m->P(m->pl.wpe), g->pos, B, (int)C,
-                         m->cfg.vocab_size, x, s));
+  const int32_t* posd = (const int32_t*)(base + g->posd);
   for (int l = 0; l < c.n_layer; ++l) {
     const LayerOff& L = m->pl.layer[l];
     HIP_TRY(gen_linear(g, a, C, L.qkvw, 3 * C, L.qkvb, GPT_EPI_STORE, base + g->qkv, 3 * C,
                        nullptr, nullptr, s, x, L.ln1w, L.ln1b));
     HIP_TRY(gpt::attn_decode(prec, (int)m->hd, base + g->qkv, base + g->kc + l * cache_layer,
-                             base + g->vc + l * cache_layer, g->pos, g->Tmax, B, (int)m->H,
+                             base + g->vc + l * cache_layer, posd, g->Tmax, B, (int)m->H,
                              c.window_left[l], base + g->att, s));
     HIP_TRY(gen_linear(g, base + g->att, C, L.projw, C, L.projb, GPT_EPI_RESIDUAL, x, C, x,
                        nullptr, s));
@@ -962,6 +971,42 @@ int gen_step(gpt_gen* g, const int32_t* d_tok, hipStream_t s) {
                              mean, rstd, s));
   HIP_TRY(gen_linear(g, a, C, m->pl.lmw, m->Vp, -1, GPT_EPI_STORE, base + g->logits, m->Vq,
                      nullptr, nullptr, s));
+  HIP_TRY(gpt::gen_advance((int32_t*)(base + g->posd), s));
+  return GPT_OK;
+}
+
+int gen_step(gpt_gen* g, const int32_t* d_tok, hipStream_t s) {
+  gpt_model* m = g->m;
+  if (g->pos >= g->Tmax) return fail(GPT_E_INVALID, "the cache is full (Tmax tokens)");
+  int rc = wait_adam(m, s, -1);
+  if (rc != GPT_OK) return rc;
+  int32_t* posd = (int32_t*)(g->base + g->posd);
+  if (g->pos_dirty) {
+    HIP_TRY(gpt::gen_set_pos(posd, g->pos, s));
+    g->pos_dirty = false;
+  }
+  HIP_TRY(gpt::gen_embed(d_tok, m->P(m->pl.wte), m->P(m->pl.wpe), posd, g->B, (int)m->C,
+                         m->cfg.vocab_size, (float*)(g->base + g->x), s));
+  if (!g->use_graph) {
+    rc = gen_body(g, s);
+    if (rc != GPT_OK) return rc;
+  } else {
+    if (!g->exec) {
+      if (!g->cap) HIP_TRY(hipStreamCreateWithFlags(&g->cap, hipStreamNonBlocking));
+      HIP_TRY(hipStreamBeginCapture(g->cap, hipStreamCaptureModeThreadLocal));
+      rc = gen_body(g, g->cap);
+      hipGraph_t graph = nullptr;
+      const hipError_t ce = hipStreamEndCapture(g->cap, &graph);
+      if (rc != GPT_OK) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return rc;
+      }
+      if (ce != hipSuccess) return fail(GPT_E_HIP, std::string("capture: ") + hipGetErrorString(ce));
+      g->graph = graph;
+      HIP_TRY(hipGraphInstantiateWithFlags(&g->exec, g->graph, 0));
+    }
+    HIP_TRY(hipGraphLaunch(g->exec, s));
+  }
   g->pos += 1;
   return GPT_OK;
 }
@@ -1004,9 +1049,16 @@ int gpt_gen_init(gpt_model* m, int32_t B, int32_t Tmax, void* d_arena, int64_t a
   return GPT_OK;
 }
 
+int gpt_gen_set_graph(gpt_gen* g, int32_t enable) {
+  if (!g || (enable != 0 && enable != 1)) return fail(GPT_E_INVALID, "NULL context or bad flag");
+  g->use_graph = enable != 0;
+  return GPT_OK;
+}
+
 int gpt_gen_reset(gpt_gen* g) {
   if (!g) return fail(GPT_E_INVALID, "NULL context");
   g->pos = 0;
+  g->pos_dirty = true;
   return GPT_OK;
 }
 
@@ -1049,6 +1101,7 @@ int gpt_generate(gpt_gen* g, const int32_t* d_prompt, int32_t T0, int32_t n_new,
   const int Ltot = T0 + n_new;
   int32_t* tok = (int32_t*)(g->base + g->tok);
   g->pos = 0;
+  g->pos_dirty = true;
   HIP_TRY(gpt::copy_prompt(d_prompt, T0, Ltot, g->B, d_out, s));
   for (int t = 0; t < T0; ++t) {
     HIP_TRY(gpt::gather_column(d_out, Ltot, t, g->B, tok, s));
@@ -1068,6 +1121,11 @@ int gpt_generate(gpt_gen* g, const int32_t* d_prompt, int32_t T0, int32_t n_new,
 }
 
 int gpt_gen_destroy(gpt_gen* g) {
+  if (g) {
+    if (g->exec) (void)hipGraphExecDestroy(g->exec);
+    if (g->graph) (void)hipGraphDestroy(g->graph);
+    if (g->cap) (void)hipStreamDestroy(g->cap);
+  }
   delete g;
   return GPT_OK;
 }

@@ -114,12 +114,15 @@ hipError_t adamw_segments(const int64_t* d_seg, int nseg, int blocks, float* p, 
                           float* v, const float* g, uint16_t* shadow, AdamScalars sc,
                           Guard guard, hipStream_t s);
 
-// Generation (decode.hip).  x[b] = wte[tok[b]] + wpe[pos]; ids outside [0, V)
-// read row 0.
-hipError_t gen_embed(const int32_t* tok, const float* wte, const float* wpe, int pos, int B, int C,
-                     int V, float* x, hipStream_t s);
-// One query per (sequence b, head h) at position pos: qkv [B, 3*H*hd] (act);
-// caches [B, H, Tmax, hd] (act) of this layer; row pos of both caches is
+// Generation (decode.hip).  The position of a decode step is read from
+// device memory (*pos), so one captured step serves every position.
+// x[b] = wte[tok[b]] + wpe[*pos]; ids outside [0, V) read row 0.
+hipError_t gen_embed(const int32_t* tok, const float* wte, const float* wpe, const int32_t* pos,
+                     int B, int C, int V, float* x, hipStream_t s);
+hipError_t gen_set_pos(int32_t* pos, int32_t v, hipStream_t s);  // *pos = v
+hipError_t gen_advance(int32_t* pos, hipStream_t s);             // *pos += 1
+// One query per (sequence b, head h) at position *pos: qkv [B, 3*H*hd] (act);
+// caches [B, H, Tmax, hd] (act) of this layer; row *pos of both caches is
 // written from qkv; out [B, H*hd] (act).
 bool attn_decode_supported(int hd);
 // Few-row bf16 product of a decode step: out[b, n] = epilogue(sum_k a[b, k] W[n, k]),
@@ -145,8 +148,8 @@ struct RowsLinear {
 };
 constexpr int ROWS_LINEAR_MAX_LN_K = 1024;  // LayerNorm rows staged in LDS
 hipError_t rows_linear(const RowsLinear& p, hipStream_t s);
-hipError_t attn_decode(int prec, int hd, const void* qkv, void* kc, void* vc, int pos, int Tmax,
-                       int B, int H, int left, void* out, hipStream_t s);
+hipError_t attn_decode(int prec, int hd, const void* qkv, void* kc, void* vc, const int32_t* pos,
+                       int Tmax, int B, int H, int left, void* out, hipStream_t s);
 // Per row b of logits [B, ldz] (act): token from the first V entries with
 // u[b * u_stride]; written to tok[b] and, if seq, seq[b * seq_stride + seq_col].
 hipError_t sample(int prec, const void* logits, long ldz, int B, int V, float temperature,

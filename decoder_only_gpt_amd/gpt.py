@@ -31,6 +31,7 @@ EXPORTS = [
     "gpt_adamw_step_clipped", "gpt_muon_step",
     "gpt_get_buffer",
     "gpt_set_buffer", "gpt_destroy", "gpt_gen_plan", "gpt_gen_init", "gpt_gen_reset",
+    "gpt_gen_set_graph",
     "gpt_gen_step", "gpt_gen_logits", "gpt_gen_sample", "gpt_generate", "gpt_gen_destroy",
     "gpt_last_error", "gpt_op_gemm", "gpt_op_gemm_group", "gpt_op_gemm_group_workspace",
     "gpt_op_attention_fwd", "gpt_op_attention_bwd", "gpt_op_attention_bwd_noalloc",
@@ -144,6 +145,7 @@ def lib():
         "gpt_gen_plan": ([vp, i32, i32, ctypes.POINTER(i64)], i32),
         "gpt_gen_init": ([vp, i32, i32, vp, i64, vp, ctypes.POINTER(vp)], i32),
         "gpt_gen_reset": ([vp], i32),
+        "gpt_gen_set_graph": ([vp, i32], i32),
         "gpt_gen_step": ([vp, vp, vp], i32),
         "gpt_gen_logits": ([vp, vp, ctypes.POINTER(i64), vp], i32),
         "gpt_gen_sample": ([vp, ctypes.c_float, i32, vp, i64, vp, vp], i32),
@@ -392,7 +394,7 @@ class Generator:
     """Key/value-cache generation on a model's weights (B sequences of up to
     Tmax tokens); methods map 1:1 onto the gpt_gen_* entry points."""
 
-    def __init__(self, model: Model, B: int, Tmax: int):
+    def __init__(self, model: Model, B: int, Tmax: int, graph: bool = True):
         import torch
         self.model, self.B, self.Tmax = model, B, Tmax
         n = ctypes.c_int64()
@@ -403,6 +405,7 @@ class Generator:
                                   int(n.value), _stream(), ctypes.byref(h)))
         self.h = h
         self._keep = []
+        _check(lib().gpt_gen_set_graph(self.h, int(bool(graph))))
 
     def __del__(self):
         h = getattr(self, "h", None)

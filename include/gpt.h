@@ -307,6 +307,16 @@ int gpt_gen_init(gpt_model* m, int32_t B, int32_t Tmax, void* d_arena, int64_t a
                  void* stream, gpt_gen** out);
 /* Forget the cached tokens (next gpt_gen_step is position 0). */
 int gpt_gen_reset(gpt_gen* g);
+/* Decode steps replay one captured HIP graph (enable = 1, the default) or
+ * launch their kernels one by one (0); the results are the same bits.  The
+ * token embedding of a step is launched on its own (its token buffer is the
+ * caller's per step); the rest of the step (every block, the final LayerNorm,
+ * the lm_head) is captured at the first step that needs it, on a stream of
+ * the context, and reads the position from device memory, so the one graph
+ * serves every position (nanoGPT README "sampling / inference": sampling
+ * from a trained model; the llm.c summary notes the code is not optimised
+ * for inference).  INVALID for a NULL context or a flag other than 0 / 1. */
+int gpt_gen_set_graph(gpt_gen* g, int32_t enable);
 /* Append one token per sequence (d_tokens: device int32 [B], ids < vocab)
  * at the current position: its keys / values join the cache and the logits
  * of the next token are computed.  GPT_E_INVALID once Tmax tokens are cached. */

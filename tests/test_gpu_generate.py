@@ -196,3 +196,35 @@ def test_generation_errors():
     assert e.value.code == gpt.E_INVALID
     with pytest.raises(gpt.GptError):
         gpt.Generator(m, 1, cfg["block_size"] + 1)
+
+
+@pytest.mark.parametrize("prec", ["fp32", "bf16"])
+@pytest.mark.parametrize("name", ["gpt2_s", "chat_s"])
+def test_graph_replay_equals_eager_steps(name, prec):
+    """Decode steps replayed from the captured graph give the same logits, bit
+    for bit, as the same steps launched one kernel at a time, at every
+    position; with eager work and synchronisations between the replays, a
+    reset in the middle, and whole-sequence generation on both paths."""
+    cfg, p, m = _setup(name, prec)
+    B, T = 3, 24
+    seq, _ = synth.tokens(cfg, B=B, T=T, seed=13)
+    gg = gpt.Generator(m, B, T, graph=True)
+    ge = gpt.Generator(m, B, T, graph=False)
+    for rnd in range(2):  # the second round after a reset of both
+        for t in range(T):
+            tok = _dev(seq[:, t])
+            gg.step(tok)
+            ze = None
+            if t % 5 == 0:
+                torch.cuda.synchronize()
+            ge.step(tok)
+            zg, ze = gg.logits(), ge.logits()
+            assert np.array_equal(zg.view(np.uint32) if zg.dtype == np.float32 else zg,
+                                  ze.view(np.uint32) if ze.dtype == np.float32 else ze), (rnd, t)
+        gg.reset()
+        ge.reset()
+    prompt = _dev(seq[:, :6])
+    u = torch.from_numpy(np.random.default_rng(3).random((B, 10), dtype=np.float32)).cuda()
+    og = gg.generate(prompt, 10, 0.8, 20, u)
+    oe = ge.generate(prompt, 10, 0.8, 20, u)
+    assert torch.equal(og, oe)
