@@ -27,6 +27,7 @@
 #include <algorithm>
 #include <climits>
 #include <cstdlib>
+#include <type_traits>
 
 namespace gpt {
 
@@ -819,6 +820,45 @@ __device__ __forceinline__ void dma_tile256_w8(__amdgpu_buffer_rsrc_t rs, const 
   }
 }
 
+// The same loads for a k-tile that lies wholly inside both operands' K range:
+// the per-lane source offsets (bytes, relative to the tile's first K) are
+// computed once per tile by dma_plan256_w8, and the k-tile's own K offset goes
+// in the instruction's scalar offset, so a load costs no vector arithmetic.
+// Rows past the operand keep an offset beyond the buffer's range (zeros).
+template <int TRANS>
+__device__ __forceinline__ void dma_plan256_w8(const OpArgs& a, int r0, int kbeg, int wave,
+                                               int lane, unsigned (&voff)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int blk = wave * 4 + i;
+    int r, k;
+    if constexpr (TRANS == 0) {
+      const int row = blk * 8 + (lane >> 3), phys = lane & 7;
+      const int chunk = phys ^ (row & 7) ^ ((row >> 3) & 1);
+      r = r0 + row;
+      k = kbeg + chunk * 8;
+    } else {
+      const int kk = blk * 2 + (lane >> 5), phys = lane & 31;
+      const int chunk = phys ^ ((kk & 3) << 2);
+      k = kbeg + kk;
+      r = r0 + chunk * 8;
+    }
+    const long e = TRANS ? (long)k * a.ld + r : (long)r * a.ld + k;
+    voff[i] = r < a.rows ? (unsigned)(e * 2) : 0x80000000u;
+  }
+}
+__device__ __forceinline__ void dma_fast256_w8(__amdgpu_buffer_rsrc_t rs, const unsigned (&voff)[4],
+                                               unsigned soff, bf16_t* lds, int wave_s) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const unsigned m0v = (unsigned)(uintptr_t)(lds + (wave_s * 4 + i) * 512);
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(m0v), "v"(voff[i]), "s"(rs), "s"(soff)
+                 : "memory", "m0");
+  }
+}
+
 // One 256 x 256 output tile (tx, ty) over the K range of split tz; `smem` is
 // the kernel's 128 KB LDS block (two stages of A and B tiles, later the
 // epilogue slices).
@@ -831,9 +871,11 @@ __device__ __forceinline__ void big8_tile(const OpArgs& A, const OpArgs& B, int 
                                           const EpiArgs& e, float* partial, int tx, int ty, int tz,
                                           bf16_t* smem, float* csum = nullptr) {
   static_assert(!CSUM || AT == 1, "column sums of a K-major A tile");
+  // Stage s of A at s * 32 KB, of B at 64 KB + s * 32 KB: each operand's two
+  // stages lie within one LDS instruction offset (16 bits) of each other.
   bf16_t* const sA0 = smem;
-  bf16_t* const sB0 = smem + BIG * BK;
-  bf16_t* const sA1 = smem + 2 * BIG * BK;
+  bf16_t* const sA1 = smem + BIG * BK;
+  bf16_t* const sB0 = smem + 2 * BIG * BK;
   bf16_t* const sB1 = smem + 3 * BIG * BK;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 2, wn = wave & 3;  // rows wm * 128 .., columns wn * 64 ..
@@ -859,17 +901,29 @@ __device__ __forceinline__ void big8_tile(const OpArgs& A, const OpArgs& B, int 
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  dma_tile256_w8<AT, (AT || BT)>(ra, a, m0, kbeg, sA0, wave, lane);
-  dma_tile256_w8<BT, (AT || BT)>(rb, b, n0, kbeg, sB0, wave, lane);
-  for (int kt = 0; kt < nk; ++kt) {
+  // Full k-tiles load through the precomputed offsets; a ragged last one (and
+  // the first, if ragged) through the masked loader.
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  unsigned voa[4], vob[4];
+  dma_plan256_w8<AT>(a, m0, kbeg, wave, lane, voa);
+  dma_plan256_w8<BT>(b, n0, kbeg, wave, lane, vob);
+  const unsigned a_kstep = AT ? (unsigned)(a.ld * 2 * BK) : 2u * BK;  // bytes per k-tile
+  const unsigned b_kstep = BT ? (unsigned)(b.ld * 2 * BK) : 2u * BK;
+  auto load_stage = [&](int kt, bf16_t* sa, bf16_t* sb) {
+    const int k0 = kbeg + kt * BK;
+    if (k0 + BK <= a.kvalid) dma_fast256_w8(ra, voa, (unsigned)kt * a_kstep, sa, wave_s);
+    else dma_tile256_w8<AT, true>(ra, a, m0, k0, sa, wave, lane);
+    if (k0 + BK <= b.kvalid) dma_fast256_w8(rb, vob, (unsigned)kt * b_kstep, sb, wave_s);
+    else dma_tile256_w8<BT, true>(rb, b, n0, k0, sb, wave, lane);
+  };
+  load_stage(0, sA0, sB0);
+  // One k-tile from stage ODD; the loop runs them in pairs so each stage's LDS
+  // addresses are fixed offsets of loop-invariant registers.
+  auto ktile = [&](int kt, auto odd_c) {
+    constexpr bool odd = decltype(odd_c)::value;
     __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's loads of tile kt landed
     __syncthreads();                     // ... and every other wave's
-    const bool odd = kt & 1;
-    if (kt + 1 < nk) {
-      const int k1 = kbeg + (kt + 1) * BK;
-      dma_tile256_w8<AT, (AT || BT)>(ra, a, m0, k1, odd ? sA0 : sA1, wave, lane);
-      dma_tile256_w8<BT, (AT || BT)>(rb, b, n0, k1, odd ? sB0 : sB1, wave, lane);
-    }
+    if (kt + 1 < nk) load_stage(kt + 1, odd ? sA0 : sA1, odd ? sB0 : sB1);
     const bf16_t* as = odd ? sA1 : sA0;
     const bf16_t* bs = odd ? sB1 : sB0;
     // Fragments double-buffered across the 16-deep steps: the reads of step
@@ -925,6 +979,10 @@ __device__ __forceinline__ void big8_tile(const OpArgs& A, const OpArgs& B, int 
         }
       }
     }
+  };
+  for (int kt = 0; kt < nk; kt += 2) {
+    ktile(kt, std::false_type{});
+    if (kt + 1 < nk) ktile(kt + 1, std::true_type{});
   }
 
   // Epilogue, one 32-row block of the wave's 128 x 64 tile at a time:
@@ -1045,9 +1103,9 @@ template <int AT, int BT, int EPI>
 __global__ void __launch_bounds__(512, 1) gemm_big8w_kernel(OpArgs A, OpArgs B, int K, int kchunk,
                                                             EpiArgs e, float* partial) {
   __shared__ __attribute__((aligned(16))) bf16_t smem[4 * BIG * BK];
-  bf16_t* const sA0 = smem;
-  bf16_t* const sB0 = smem + BIG * BK;
-  bf16_t* const sA1 = smem + 2 * BIG * BK;
+  bf16_t* const sA0 = smem;  // stage layout of the 256-tile kernel
+  bf16_t* const sA1 = smem + BIG * BK;
+  bf16_t* const sB0 = smem + 2 * BIG * BK;
   bf16_t* const sB1 = smem + 3 * BIG * BK;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;  // rows wm * 64 .., columns wn * 96 ..
@@ -1078,17 +1136,26 @@ __global__ void __launch_bounds__(512, 1) gemm_big8w_kernel(OpArgs A, OpArgs B, 
 #pragma unroll
     for (int j = 0; j < 3; ++j) acc[i][j] = f32x16{};
 
-  dma_tile256_w8<AT, (AT || BT)>(ra, a, m0, kbeg, sA0, wave, lane);
-  dma_tile256_w8<BT, (AT || BT)>(rb, b, n0, kbeg, sB0, wave, lane);
-  for (int kt = 0; kt < nk; ++kt) {
+  // Full k-tiles through precomputed offsets, as in the 256-tile kernel.
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  unsigned voa[4], vob[4];
+  dma_plan256_w8<AT>(a, m0, kbeg, wave, lane, voa);
+  dma_plan256_w8<BT>(b, n0, kbeg, wave, lane, vob);
+  const unsigned a_kstep = AT ? (unsigned)(a.ld * 2 * BK) : 2u * BK;
+  const unsigned b_kstep = BT ? (unsigned)(b.ld * 2 * BK) : 2u * BK;
+  auto load_stage = [&](int kt, bf16_t* sa, bf16_t* sb) {
+    const int k0 = kbeg + kt * BK;
+    if (k0 + BK <= a.kvalid) dma_fast256_w8(ra, voa, (unsigned)kt * a_kstep, sa, wave_s);
+    else dma_tile256_w8<AT, true>(ra, a, m0, k0, sa, wave, lane);
+    if (k0 + BK <= b.kvalid) dma_fast256_w8(rb, vob, (unsigned)kt * b_kstep, sb, wave_s);
+    else dma_tile256_w8<BT, true>(rb, b, n0, k0, sb, wave, lane);
+  };
+  load_stage(0, sA0, sB0);
+  auto ktile = [&](int kt, auto odd_c) {  // k-tiles in pairs, as in the 256-tile kernel
+    constexpr bool odd = decltype(odd_c)::value;
     __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's loads of tile kt landed
     __syncthreads();                     // ... and every other wave's
-    const bool odd = kt & 1;
-    if (kt + 1 < nk) {
-      const int k1 = kbeg + (kt + 1) * BK;
-      dma_tile256_w8<AT, (AT || BT)>(ra, a, m0, k1, odd ? sA0 : sA1, wave, lane);
-      dma_tile256_w8<BT, (AT || BT)>(rb, b, n0, k1, odd ? sB0 : sB1, wave, lane);
-    }
+    if (kt + 1 < nk) load_stage(kt + 1, odd ? sA0 : sA1, odd ? sB0 : sB1);
     const bf16_t* as = odd ? sA1 : sA0;
     const bf16_t* bs = odd ? sB1 : sB0;
     // Fragments double-buffered across the 16-deep steps, as in the 256-tile kernel.
@@ -1124,6 +1191,10 @@ __global__ void __launch_bounds__(512, 1) gemm_big8w_kernel(OpArgs A, OpArgs B, 
       else __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int kt = 0; kt < nk; kt += 2) {
+    ktile(kt, std::false_type{});
+    if (kt + 1 < nk) ktile(kt + 1, std::true_type{});
   }
 
   // Epilogue, one 32-row block of the wave's 64 x 96 tile at a time (see the

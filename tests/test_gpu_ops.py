@@ -175,6 +175,67 @@ def test_gemm_long_reduction_many_tiles(epi):
     assert err < 2e-5, err
 
 
+ROUNDS_CASES = [
+    # M, N, K, b_trans, epilogue: unsplit 256-tile plans of more than one round of
+    # the 256 CUs
+    (4000, 8144, 136, 0, gpt.EPI_GELU_PAIR),   # 512 tiles, ragged M / N
+    (4000, 8144, 72, 1, gpt.EPI_MUL),          # input-gradient layout
+    (4000, 8144, 200, 0, gpt.EPI_RESIDUAL),    # float output, ragged K
+    (4000, 8144, 264, 1, gpt.EPI_DGELU),
+    (16504, 16504, 64, 0, gpt.EPI_STORE),      # 4225 tiles (no XCD renumbering), one k-tile
+]
+
+
+@pytest.mark.parametrize("M,N,K,bt,epi", ROUNDS_CASES)
+def test_gemm_many_rounds(M, N, K, bt, epi):
+    """Unsplit 256-tile products over several rounds of the CUs, ragged in M,
+    N and K; sampled rows (including the first and last of tiles), all
+    columns, against exact values."""
+    A, lda, Ax = _operand(M, K, 0, torch.bfloat16, 51)
+    B, ldb, Bx = _operand(N, K, bt, torch.bfloat16, 52)
+    bias = torch.from_numpy(synth.normal(N, 53, 0.5)).cuda()
+    resid = torch.from_numpy(synth.normal((M, N), 54, 1.0)).cuda() if epi == gpt.EPI_RESIDUAL else None
+    aux_in = to_dev(synth.normal((M, N), 55, 1.5), torch.bfloat16)
+    f32 = epi == gpt.EPI_RESIDUAL
+    out = torch.zeros((M, N), dtype=torch.float32 if f32 else torch.bfloat16, device="cuda")
+    aux = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+    d = gpt.GemmDesc(precision=gpt.BF16, M=M, N=N, K=K, A=A.data_ptr(), lda=lda, a_trans=0, a_rows=M,
+                     a_kvalid=K, B=B.data_ptr(), ldb=ldb, b_trans=bt, b_rows=N, b_kvalid=K,
+                     epilogue=epi, gelu_tanh=1, out=out.data_ptr(), ldo=N)
+    if epi in (gpt.EPI_STORE, gpt.EPI_RESIDUAL, gpt.EPI_GELU_PAIR):
+        d.bias = bias.data_ptr()
+    if epi == gpt.EPI_RESIDUAL:
+        d.resid = resid.data_ptr()
+    if epi == gpt.EPI_GELU_PAIR:
+        d.aux, d.ldaux = aux.data_ptr(), N
+    if epi in (gpt.EPI_MUL, gpt.EPI_DGELU):
+        d.aux, d.ldaux = aux_in.data_ptr(), N
+    gpt.op_gemm(d)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(56)
+    rows = np.unique(np.concatenate([rng.choice(M, 40, replace=False), [0, 255, 256, 3839, M - 1]]))
+    rows_t = torch.from_numpy(rows).cuda()
+    got = rounded(out[rows_t])
+    acc = Ax[rows] @ Bx.T
+    bx = bias.cpu().numpy().astype(np.float64)
+    if epi == gpt.EPI_STORE:
+        ref = acc + bx
+    elif epi == gpt.EPI_RESIDUAL:
+        ref = resid[rows_t].cpu().numpy().astype(np.float64) + acc + bx
+    elif epi == gpt.EPI_MUL:
+        ref = acc * rounded(aux_in[rows_t])
+    elif epi == gpt.EPI_DGELU:
+        ref = acc * oracle.gelu_grad(rounded(aux_in[rows_t]), 1)
+    else:  # GELU pair: u = acc + bias rounded to bf16; out = GELU'(u), aux = GELU(u)
+        u = oracle.bf16_round((acc + bx).astype(np.float32)).astype(np.float64)
+        ref = oracle.gelu_grad(u, 1)
+        g_ref = oracle.gelu(u, 1)
+        g_err = np.abs(rounded(aux[rows_t]) - g_ref).max() / np.abs(g_ref).max()
+        assert g_err < 1e-2, g_err
+    err = np.abs(got - ref).max() / np.abs(ref).max()
+    assert err < (2e-5 if f32 else 1e-2), err
+
+
 @pytest.mark.parametrize("prec", [gpt.FP32, gpt.BF16])
 @pytest.mark.parametrize("epi", [gpt.EPI_STORE, gpt.EPI_RESIDUAL, gpt.EPI_GELU, gpt.EPI_DGELU,
                                  gpt.EPI_F32_ACCUM, gpt.EPI_GELU_PAIR, gpt.EPI_MUL])
