@@ -667,6 +667,18 @@ __global__ void __launch_bounds__(256, HD == 128 ? 1 : 2)
   const int qblk0 = (gridDim.y - 1 - blockIdx.y) * 128;  // longest key ranges first
   const int qw0 = qblk0 + wave * 32;
   const int qi = qw0 + c;
+  const int qlast = min(Tn - 1, qblk0 + 127);
+  const int kstart = left < 0 ? 0 : (max(0, qblk0 - left) / KT) * KT;
+  auto fetch = [&](int k0, int bb) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      dma_tile<HD>(rs, ld, C + h * HD, k0 + 64 * half, Tn, Ks[bb] + 64 * half * HD, wave, lane);
+      dma_tile<HD>(rs, ld, 2 * C + h * HD, k0 + 64 * half, Tn, Vs[bb] + 64 * half * HD, wave, lane);
+    }
+  };
+  // The first key tile is requested before this wave's own rows, so the two
+  // memory latencies overlap instead of adding up.
+  fetch(kstart, 0);
 
   bf16x8 qf[NS], gf[NS];
   float dpart = 0.f;  // this lane's share of D = sum_d dO O for its query
@@ -696,9 +708,6 @@ __global__ void __launch_bounds__(256, HD == 128 ? 1 : 2)
   f32x16 dq[ND];  // dQ^T: head dim d * 32 + acc_row(r, g), query qi
 #pragma unroll
   for (int d = 0; d < ND; ++d) dq[d] = f32x16{};
-
-  const int qlast = min(Tn - 1, qblk0 + 127);
-  const int kstart = left < 0 ? 0 : (max(0, qblk0 - left) / KT) * KT;
 
   // S^T and dP^T of the 32-key sub-block at tile row kr: s[r], dp[r] hold key
   // kr + acc_row(r, g) for query qi.
@@ -750,15 +759,6 @@ __global__ void __launch_bounds__(256, HD == 128 ? 1 : 2)
   constexpr int SDP_M = 2 * NS, DQ_M = 2 * ND;       // MFMAs of sdp / dqm
   constexpr int SDP_R = 2 * NS, DQ_R = 4 * ND;       // LDS read instructions
   constexpr int SOFT_V = 16 * 4 + 8;                 // VALU instructions of soft
-  auto fetch = [&](int k0, int bb) {
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      dma_tile<HD>(rs, ld, C + h * HD, k0 + 64 * half, Tn, Ks[bb] + 64 * half * HD, wave, lane);
-      dma_tile<HD>(rs, ld, 2 * C + h * HD, k0 + 64 * half, Tn, Vs[bb] + 64 * half * HD, wave, lane);
-    }
-  };
-
-  fetch(kstart, 0);
   int buf = 0;
   for (int kb0 = kstart; kb0 <= qlast; kb0 += KT, buf ^= 1) {
     __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's share of tile kb0 landed
