@@ -79,6 +79,22 @@ ParamLayout param_layout(const gpt_config& c) {
   return p;
 }
 
+// The ranges of the flat vector whose gradients the grouped weight-gradient
+// reductions do not write (embeddings, the LayerNorm parameters of every
+// block, the final LayerNorm and an untied head): the gradient norm sums them
+// separately and takes the blocks' matrices and biases from those reductions.
+std::vector<std::pair<int64_t, int64_t>> norm_ranges(const gpt_config& c, const ParamLayout& p) {
+  std::vector<std::pair<int64_t, int64_t>> r;
+  auto add = [&](int64_t b, int64_t e) { if (e > b) r.push_back({b, e - b}); };
+  add(0, c.n_layer > 0 ? p.layer[0].ln1w : p.lnfw);
+  for (const LayerOff& L : p.layer) {
+    add(L.ln1w, L.qkvw);
+    add(L.ln2w, L.fcw);
+  }
+  add(p.lnfw, p.n);
+  return r;
+}
+
 int64_t n_matmul(const gpt_config& c) {
   const int64_t C = c.n_embd, F = c.mlp_hidden;
   return (int64_t)c.n_layer * (3 * C * C + C * C + 2 * F * C) + (int64_t)c.padded_vocab * C;
@@ -131,7 +147,7 @@ struct Arena {
   int64_t X, ln_mean, ln_rstd;
   std::vector<int64_t> a1, qkv, att, lse, a2, u, g;
   int64_t xf, logits, loss_rows, loss, gres[2], gact[NGB], dC, dC2, dF[NGB], dqkv[NGB], dvec;
-  int64_t gemm_ws, gemm_ws_bytes, cs_part, ln_part, n_part, norm2, clip, muon_ws, adam_seg;
+  int64_t gemm_ws, gemm_ws_bytes, cs_part, ln_part, n_part, n_rng, norm2, clip, muon_ws, adam_seg;
   int64_t e_counts, e_offsets, e_tile_sums, e_rank, e_perm, e_carry_first, e_carry_last, e_flags,
       e_last_tok;
   int64_t ids, id_flag;  // token ids the forward used; forward count of the last bad id
@@ -208,7 +224,13 @@ Arena plan_arena(const gpt_config& c, int B, int T) {
   a.e_last_tok = take(nch * 4);
   a.ids = take(M * 4);
   a.id_flag = take(16);
-  a.n_part = take(1024 * 8);
+  {  // norm partials: one full pass, or the blocks' reductions plus the other ranges
+    const std::vector<std::pair<int64_t, int64_t>> nr = norm_ranges(c, param_layout(c));
+    int64_t nb = L * gpt::GROUP_REDUCE_MAX_BLOCKS;
+    for (const auto& x : nr) nb += gpt::sumsq_range_blocks(x.second);
+    a.n_part = take(std::max<int64_t>(1024, nb) * 8);
+    a.n_rng = take((int64_t)nr.size() * 3 * 8 + 8);
+  }
   a.norm2 = take(16);
   a.clip = take(32);  // device clip: {norm, grad_scale} doubles, then grad_scale as float
   // Muon working set, sized for the largest kind of block matrix (one kind at a time).
@@ -264,6 +286,13 @@ struct gpt_model {
   // the final LayerNorm and untied head); the next forward waits per group.
   std::vector<hipEvent_t> ev_adam;
   bool adam_pending = false;
+  // Gradient norm from the backward's partial sums of squares (the blocks'
+  // weight-gradient reductions, then the remaining ranges): valid until the
+  // gradients are rewritten otherwise.
+  std::vector<int64_t> norm_rng;  // (begin, length, first block) per range
+  int norm_rng_blocks = 0;
+  bool norm_parts = false;
+  int64_t norm_part_count = 0;
   // The runs of the flat vector outside the Muon matrices (AdamW in the
   // Muon step): (begin, length, first block) triples, also on the device.
   std::vector<int64_t> adam_seg;
@@ -515,15 +544,22 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
     return run_gemm(m, st, dd, site);
   };
   auto gemm_group_on = [&](hipStream_t st, const gpt_gemm_desc* dd, float* const* db, int n,
-                           int site) -> int {
+                           int site, double* sq) -> int {
     double fl = 0;
     for (int i = 0; i < n; ++i) fl += 2.0 * dd[i].M * dd[i].N * dd[i].K;
     hipStream_t s = st;
     // The products and their fixed-order reduction are timed as separate sites.
     LAUNCH(GPT_K_GEMM_SPLITK, site, fl, 0, gpt::gemm_group(dd, n, s, db, 1));
-    LAUNCH(GPT_K_GEMM_SPLITK, GPT_S_BLOCK_DW_REDUCE, 0, 0, gpt::gemm_group(dd, n, s, db, 2));
+    LAUNCH(GPT_K_GEMM_SPLITK, GPT_S_BLOCK_DW_REDUCE, 0, 0, gpt::gemm_group(dd, n, s, db, 2, sq));
     return GPT_OK;
   };
+  // The gradient norm's partials: each block's grouped reduction writes its
+  // rb per-block sums of squares at n_part + l * rb (every block has the same
+  // shapes, so the same rb), the other ranges follow after the backward.
+  m->norm_parts = false;
+  double* n_part = m->at<double>(m->ar.n_part);
+  bool fold = true;
+  int rb = -1;
   auto bias_grad = [&](const char* x, int64_t n, int64_t off) -> int {
     if (off < 0) return GPT_OK;
     hipStream_t s = s2;
@@ -618,7 +654,14 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
     CHECK(add_dw(linear_dw(m, dqkv, 3 * C, 3 * C, act(m->ar.a1[l]), C, L.qkvw, 3 * C, acc), dqkv,
                  3 * C, L.qkvb));
     held[nheld++] = 2 * NGB + di;
-    CHECK(gemm_group_on(s2, dw, db, ndw, GPT_S_BLOCK_DW));
+    double* sq = nullptr;
+    if (fold) {
+      const int b = ndw == 4 ? gpt::gemm_group_reduce_blocks(dw, ndw, db) : 0;
+      if (rb < 0) rb = b;
+      fold = b > 0 && b == rb;
+      if (fold) sq = n_part + (int64_t)l * rb;
+    }
+    CHECK(gemm_group_on(s2, dw, db, ndw, GPT_S_BLOCK_DW, sq));
     for (int i = 0; i < nheld; ++i) CHECK(mark(held[i]));
     d = linear_dx(m, dqkv, 3 * C, L.qkvw, C, 3 * C, 3 * C);
     d.epilogue = GPT_EPI_STORE; d.out = dC; d.ldo = C;
@@ -650,6 +693,14 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
   if (s2 != s) {
     CHECK(hip_ok(hipEventRecord(m->ev_join, s2), "hipEventRecord"));
     CHECK(hip_ok(hipStreamWaitEvent(s, m->ev_join, 0), "hipStreamWaitEvent"));
+  }
+  if (fold && rb > 0 && !m->norm_rng.empty()) {
+    const int64_t off = (int64_t)c.n_layer * rb;
+    LAUNCH(GPT_K_NORM, GPT_S_GRAD_NORM, 0, 0,
+           gpt::sumsq_ranges(m->G(0), m->at<int64_t>(m->ar.n_rng), (int)(m->norm_rng.size() / 3),
+                             m->norm_rng_blocks, n_part + off, s));
+    m->norm_part_count = off + m->norm_rng_blocks;
+    m->norm_parts = true;
   }
 #undef CHECK
   return GPT_OK;
@@ -815,9 +866,16 @@ int gpt_init(const gpt_config* cfg, int32_t B, int32_t T, void* d_arena, int64_t
       }
       if (i < mr.size()) pos = mr[i].second;
     }
-    // After the clear on the same stream; the host vector lives as long as the model.
+    for (const auto& x : norm_ranges(m->cfg, m->pl)) {
+      m->norm_rng.insert(m->norm_rng.end(), {x.first, x.second, (int64_t)m->norm_rng_blocks});
+      m->norm_rng_blocks += gpt::sumsq_range_blocks(x.second);
+    }
+    // After the clear on the same stream; the host vectors live as long as the model.
     e = hipMemcpyAsync(m->at<int64_t>(a.adam_seg), m->adam_seg.data(), m->adam_seg.size() * 8,
                        hipMemcpyHostToDevice, s);
+    if (e == hipSuccess && !m->norm_rng.empty())
+      e = hipMemcpyAsync(m->at<int64_t>(a.n_rng), m->norm_rng.data(), m->norm_rng.size() * 8,
+                         hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) {
       gpt_destroy(m);
@@ -1188,12 +1246,26 @@ int gpt_backward(gpt_model* m, int32_t accumulate, void* stream) {
   return GPT_OK;
 }
 
+// The sum of squares of the gradient vector into norm2: from the backward's
+// partials when it left them, else one fixed-order pass over the vector.
+int grad_sumsq(gpt_model* m, hipStream_t s) {
+  double* part = m->at<double>(m->ar.n_part);
+  double* out = m->at<double>(m->ar.norm2);
+  if (m->norm_parts) {
+    LAUNCH(GPT_K_NORM, GPT_S_GRAD_NORM, 0, 8.0 * m->norm_part_count,
+           gpt::sum_partials(part, (int)m->norm_part_count, out, s));
+  } else {
+    LAUNCH(GPT_K_NORM, GPT_S_GRAD_NORM, 0, 4.0 * m->N, gpt::sumsq(m->G(0), m->N, part, out, s));
+  }
+  return GPT_OK;
+}
+
 int gpt_grad_norm(gpt_model* m, void* stream, double* h_norm) {
   if (!m || !h_norm) return fail(GPT_E_INVALID, "NULL argument");
   if (m->state != 2) return fail(GPT_E_STATE, "grad_norm needs a backward first");
   hipStream_t s = (hipStream_t)stream;
-  LAUNCH(GPT_K_NORM, GPT_S_GRAD_NORM, 0, 4.0 * m->N,
-         gpt::sumsq(m->G(0), m->N, m->at<double>(m->ar.n_part), m->at<double>(m->ar.norm2), s));
+  int rc = grad_sumsq(m, s);
+  if (rc != GPT_OK) return rc;
   double n2 = 0.0;
   int32_t flag = 0;
   HIP_TRY(hipMemcpyAsync(&n2, m->at<double>(m->ar.norm2), 8, hipMemcpyDeviceToHost, s));
@@ -1250,8 +1322,8 @@ int gpt_adamw_step_clipped(gpt_model* m, const gpt_adamw_hp* hp, int32_t n_micro
   hipStream_t s = (hipStream_t)stream;
   double* clip = m->at<double>(m->ar.clip);
   float* d_scale = (float*)(clip + 2);
-  LAUNCH(GPT_K_NORM, GPT_S_GRAD_NORM, 0, 4.0 * m->N,
-         gpt::sumsq(m->G(0), m->N, m->at<double>(m->ar.n_part), m->at<double>(m->ar.norm2), s));
+  rc = grad_sumsq(m, s);
+  if (rc != GPT_OK) return rc;
   HIP_TRY(gpt::clip_scale(m->at<double>(m->ar.norm2), n_micro, max_norm, clip, d_scale,
                           m->guard(), s));
   if (h_norm_scale)
@@ -1381,7 +1453,10 @@ int gpt_set_buffer(gpt_model* m, int32_t which, const void* src, int32_t src_on_
                          src_on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, s));
   if (which == GPT_BUF_PARAMS && m->bf16)
     HIP_TRY(gpt::to_bf16(m->P(0), m->N, m->at<uint16_t>(m->ar.shadow), s));
-  if (which == GPT_BUF_GRADS) m->state = 2;  // caller-provided gradients may be stepped
+  if (which == GPT_BUF_GRADS) {
+    m->state = 2;  // caller-provided gradients may be stepped
+    m->norm_parts = false;
+  }
   if (!src_on_device) HIP_TRY(hipStreamSynchronize(s));
   return GPT_OK;
 }

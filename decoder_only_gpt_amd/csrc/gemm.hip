@@ -1583,10 +1583,13 @@ struct GroupReduceArgs {
   int cM[GROUP_MAX];
   long c0[GROUP_MAX + 1];  // first item of each bias gradient (c0[0] = vec0[n]); c0[nc]: all
   int n, nc, S, accumulate;
+  double* sq;  // NULL, or one sum of squares of the written values per block
 };
 
 __global__ void __launch_bounds__(256) group_reduce_kernel(GroupReduceArgs r) {
+  __shared__ double red[256];
   const long total = r.c0[r.nc];
+  float ss = 0.f;  // this thread's sum of squares of what it writes (fixed order)
   for (long i = blockIdx.x * 256L + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
     if (i < r.vec0[r.n]) {
       int p = 0;
@@ -1608,14 +1611,27 @@ __global__ void __launch_bounds__(256) group_reduce_kernel(GroupReduceArgs r) {
       }
       o[0] = a;
       o[1] = b;
+      ss += ((a.x * a.x + a.y * a.y) + (a.z * a.z + a.w * a.w)) +
+            ((b.x * b.x + b.y * b.y) + (b.z * b.z + b.w * b.w));
     } else {
       int p = 0;
       while (p + 1 < r.nc && i >= r.c0[p + 1]) ++p;
       const int m = (int)(i - r.c0[p]);
       float t = r.cpart[p][m];
       for (int z = 1; z < r.S; ++z) t += r.cpart[p][(long)z * r.cM[p] + m];
-      r.db[p][m] = r.accumulate ? r.db[p][m] + t : t;
+      if (r.accumulate) t += r.db[p][m];
+      r.db[p][m] = t;
+      ss += t * t;
     }
+  }
+  if (r.sq) {  // block sum in double, in a fixed tree order
+    red[threadIdx.x] = (double)ss;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+      if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) r.sq[blockIdx.x] = red[0];
   }
 }
 }  // namespace
@@ -1659,7 +1675,8 @@ int64_t gemm_group_workspace_bytes(const int* M, const int* N, int n, int K) {
   return (int64_t)S * mn * 4;
 }
 
-hipError_t gemm_group(const gpt_gemm_desc* d, int n, hipStream_t s, float* const* db, int phase) {
+hipError_t gemm_group(const gpt_gemm_desc* d, int n, hipStream_t s, float* const* db, int phase,
+                      double* sq) {
   if (n <= 0) return hipSuccess;
   const bool run_products = phase != 2, run_reduce = phase != 1;
   if (db) {  // column sums need a bf16 K-major A
@@ -1751,9 +1768,24 @@ hipError_t gemm_group(const gpt_gemm_desc* d, int n, hipStream_t s, float* const
     ++r.nc;
   }
   r.c0[r.nc] = items;
-  const unsigned blocks = (unsigned)std::min<long>(cdiv(items, 256), 8192);
+  r.sq = sq;
+  const unsigned blocks = (unsigned)std::min<long>(cdiv(items, 256), GROUP_REDUCE_MAX_BLOCKS);
   group_reduce_kernel<<<blocks, 256, 0, s>>>(r);
   return hipGetLastError();
+}
+
+int gemm_group_reduce_blocks(const gpt_gemm_desc* d, int n, float* const* db) {
+  if (n <= 0 || !group_ok(d, n)) return 0;
+  int Ms[GROUP_MAX], Ns[GROUP_MAX];
+  long items = 0;
+  for (int i = 0; i < n; ++i) {
+    Ms[i] = d[i].M;
+    Ns[i] = d[i].N;
+    items += (long)d[i].M * d[i].N / 8 + ((db && db[i]) ? d[i].M : 0);
+  }
+  if (!d[0].workspace || d[0].workspace_bytes < gemm_group_workspace_bytes(Ms, Ns, n, d[0].K))
+    return 0;
+  return (int)std::min<long>(cdiv(items, 256), GROUP_REDUCE_MAX_BLOCKS);
 }
 
 }  // namespace gpt

@@ -21,8 +21,15 @@ int64_t gemm_workspace_bytes(int M, int N, int K, int precision);
 // bf16 K-major A_i (sum over K), stored or added as the product's epilogue.
 // phase: 0 = everything; 1 = the products (partials) only; 2 = the reduction
 // only (after phase 1 with the same arguments; nothing when not grouped).
+// sq (may be NULL): the reduction also writes, per block, the sum of squares
+// of the values it stores (products and bias gradients; double, fixed order),
+// gemm_group_reduce_blocks(d, n, db) entries.
 hipError_t gemm_group(const gpt_gemm_desc* d, int n, hipStream_t s, float* const* db = nullptr,
-                      int phase = 0);
+                      int phase = 0, double* sq = nullptr);
+constexpr int GROUP_REDUCE_MAX_BLOCKS = 8192;
+// Blocks of the grouped launch's reduction (0: the products would not be
+// grouped, so there is no reduction and no sum of squares).
+int gemm_group_reduce_blocks(const gpt_gemm_desc* d, int n, float* const* db);
 int64_t gemm_group_workspace_bytes(const int* M, const int* N, int n, int K);
 // Number of K splits gemm() will use for this descriptor (1 = single kernel).
 int gemm_split_count(const gpt_gemm_desc& d);
@@ -85,6 +92,14 @@ hipError_t mean_loss(const float* loss_rows, int M, float* out, const int32_t* f
                      hipStream_t s);
 // Sum of squares of x[n] (float) -> *out (double), fixed order.
 hipError_t sumsq(const float* x, int64_t n, double* partials, double* out, hipStream_t s);
+// Sums of squares over ranges of x: d_ranges (device) holds (begin, length,
+// first block) per range, the first blocks the running sum of
+// sumsq_range_blocks(length); one double per block into partials.
+int sumsq_range_blocks(int64_t len);
+hipError_t sumsq_ranges(const float* x, const int64_t* d_ranges, int nranges, int blocks,
+                        double* partials, hipStream_t s);
+// out = the sum of partials[0 .. n) in index order (double).
+hipError_t sum_partials(const double* partials, int n, double* out, hipStream_t s);
 hipError_t to_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t s);
 // Seeded initialisation: p[0 .. n) holds flat indices begin .. begin + n; the
 // first n_normal get (float)(stdv * z(i)), z the Philox4x32-10 / Box-Muller

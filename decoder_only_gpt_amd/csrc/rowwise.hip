@@ -751,6 +751,28 @@ __global__ void __launch_bounds__(256) sum_partials_kernel(const double* partial
   if (threadIdx.x == 0) out[0] = red[0];
 }
 
+// The same for many partials: 1024 threads, each summing every 1024th partial
+// into four accumulators in turn (independent loads in flight), combined in a
+// fixed order, then a fixed tree over the threads.
+__global__ void __launch_bounds__(1024) sum_partials_wide_kernel(const double* partials, int n,
+                                                                 double* out) {
+  __shared__ double red[1024];
+  double a[4] = {0.0, 0.0, 0.0, 0.0};
+  int i = threadIdx.x;
+  for (; i + 3 * 1024 < n; i += 4 * 1024) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[k] += partials[i + k * 1024];
+  }
+  for (int k = 0; i < n; i += 1024, ++k) a[k] += partials[i];
+  red[threadIdx.x] = (a[0] + a[1]) + (a[2] + a[3]);
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[0] = red[0];
+}
+
 __global__ void __launch_bounds__(256) to_bf16_kernel(const float* x, int64_t n, bf16_t* y) {
   int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i + 3 < n) {
@@ -913,6 +935,56 @@ hipError_t cross_entropy(int prec, void* logits, int M, int V, int ldz, const in
 hipError_t mean_loss(const float* loss_rows, int M, float* out, const int32_t* flag, int32_t gen,
                      hipStream_t s) {
   mean_kernel<<<1, 1024, 0, s>>>(loss_rows, M, out, flag, gen);
+  return hipGetLastError();
+}
+
+// Sums of squares over a table of ranges (begin, length, first block): block
+// b belongs to the last range whose first block is <= b and sums its chunk of
+// SQR_CHUNK elements of that range.
+constexpr int64_t SQR_CHUNK = 256 * 64;
+__global__ void __launch_bounds__(256) sumsq_ranges_kernel(const float* __restrict__ x,
+                                                           const int64_t* __restrict__ rg,
+                                                           int nr, double* partials) {
+  __shared__ double red[256];
+  int lo = 0, hi = nr - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (rg[3 * mid + 2] <= (int64_t)blockIdx.x) lo = mid; else hi = mid - 1;
+  }
+  const int64_t b = rg[3 * lo] + ((int64_t)blockIdx.x - rg[3 * lo + 2]) * SQR_CHUNK;
+  const int64_t e = std::min<int64_t>(rg[3 * lo] + rg[3 * lo + 1], b + SQR_CHUNK);
+  float s = 0.f;
+  if ((rg[3 * lo] & 3) == 0) {  // 16-byte vectors (chunks start on a multiple of 4)
+    const int64_t e4 = b + (e - b) / 4 * 4;
+#pragma unroll 4
+    for (int64_t i = b + threadIdx.x * 4; i < e4; i += 1024) {
+      const float4 v = *(const float4*)(x + i);
+      s += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
+    }
+    if ((int64_t)threadIdx.x < e - e4) s += x[e4 + threadIdx.x] * x[e4 + threadIdx.x];
+  } else {
+    for (int64_t i = b + threadIdx.x; i < e; i += 256) s += x[i] * x[i];
+  }
+  red[threadIdx.x] = (double)s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) partials[blockIdx.x] = red[0];
+}
+
+int sumsq_range_blocks(int64_t len) { return (int)std::max<int64_t>(1, (len + SQR_CHUNK - 1) / SQR_CHUNK); }
+
+hipError_t sumsq_ranges(const float* x, const int64_t* d_ranges, int nranges, int blocks,
+                        double* partials, hipStream_t s) {
+  if (nranges < 1 || blocks < 1) return hipErrorInvalidValue;
+  sumsq_ranges_kernel<<<(unsigned)blocks, 256, 0, s>>>(x, d_ranges, nranges, partials);
+  return hipGetLastError();
+}
+
+hipError_t sum_partials(const double* partials, int n, double* out, hipStream_t s) {
+  sum_partials_wide_kernel<<<1, 1024, 0, s>>>(partials, n, out);
   return hipGetLastError();
 }
 

@@ -252,6 +252,32 @@ def test_device_clip_matches_host_rule(prec, max_norm, n_micro):
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), which
 
 
+@pytest.mark.parametrize("name,prec", [("gpt2_s", "bf16"), ("gpt2_s", "fp32"), ("chat_s", "bf16"),
+                                       ("gpt2_rc", "bf16")])
+@pytest.mark.parametrize("n_micro", [1, 2])
+def test_grad_norm_matches_downloaded_gradients(name, prec, n_micro):
+    """The gradient norm after a backward (in bf16 taken from the partial sums
+    of squares the grouped weight-gradient reductions leave, plus one pass over
+    the remaining ranges; otherwise one pass over the vector) equals the
+    float64 norm of the downloaded gradients; after the same gradients are
+    written back with set_buffer the norm is recomputed in one pass and agrees
+    too."""
+    cfg = dict(gpu_cfgs()[name], precision=prec)
+    m = gpt.Model(cfg)
+    m.set_params(synth.init_params(cfg, seed=11, perturb=True))
+    for k in range(n_micro):
+        idx, tgt = synth.tokens(cfg, seed=40 + k)
+        m.forward(torch.from_numpy(idx.reshape(-1)).cuda(), torch.from_numpy(tgt.reshape(-1)).cuda())
+        m.backward(1 if k else 0)
+    n_step = m.grad_norm()
+    g = m.grads()
+    n_ref = float(np.sqrt(np.sum(g.astype(np.float64) ** 2)))
+    assert abs(n_step - n_ref) <= 1e-6 * n_ref, (n_step, n_ref)
+    m.set_buffer(gpt.BUF_GRADS, g)
+    n_pass = m.grad_norm()
+    assert abs(n_pass - n_ref) <= 1e-6 * n_ref, (n_pass, n_ref)
+
+
 def test_device_clip_nonfinite_skips_update():
     """A non-finite gradient norm: no parameter or moment changes, NaN scale
     reported, and Model.train_step raises."""
