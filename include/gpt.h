@@ -201,7 +201,10 @@ int gpt_backward(gpt_model* m, int32_t accumulate, void* stream);
 
 /* Global L2 norm of the gradient buffer (llm.c summary "Proceso de
  * entrenamiento": the gradient norm that clipping acts on), float32 squares
- * summed per block, blocks summed in double in a fixed order.  Synchronises.
+ * summed per workgroup, workgroups summed in double in a fixed order (in bf16
+ * the blocks' weight and bias gradients are squared by the backward's own
+ * fixed-order reductions as it stores them; gradients written with
+ * gpt_set_buffer are summed in one pass).  Synchronises.
  * Returns GPT_E_NONFINITE (with *h_norm set) if the norm is NaN or Inf;
  * STATE without a backward; INVALID (with *h_norm set) if a forward since
  * the last update met an id outside [0, vocab_size). */
