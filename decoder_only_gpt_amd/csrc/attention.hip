@@ -317,6 +317,37 @@ __device__ __forceinline__ void store_dims(bf16_t* dst, int d0, const f32x16& a,
                    pack_bf2(a[4 * i + 2] * mul, a[4 * i + 3] * mul));
 }
 
+// Store a wave's [32 rows][HD] output block, held as HD / 32 accumulators
+// (acc[d][r]: head dim d * 32 + acc_row(r, g) of row lane % 32), as bf16 rows
+// dst + i * ldr (i < nrows), each value times this lane's `mul`.  The block is
+// staged through the wave's LDS slice `st` (32 rows of HD + 8 elements, the
+// pad spreading the rows over the banks) so that every row leaves as whole
+// 16-byte chunks, HD / 8 consecutive lanes per row: the stores write full
+// cache lines instead of a 16-byte piece of 32 rows per instruction.  The
+// caller makes sure no other wave still reads `st`.
+template <int HD>
+__device__ __forceinline__ void store_rows(bf16_t* dst, long ldr, int nrows, const f32x16* acc,
+                                           float mul, bf16_t* st, int lane) {
+  constexpr int ND = HD / 32, P = HD + 8, LPR = HD / 8, RPP = 64 / LPR;
+  const int c = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int d = 0; d < ND; ++d)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *(uint2*)(st + c * P + d * 32 + 8 * i + 4 * g) =
+          make_uint2(pack_bf2(acc[d][4 * i] * mul, acc[d][4 * i + 1] * mul),
+                     pack_bf2(acc[d][4 * i + 2] * mul, acc[d][4 * i + 3] * mul));
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the slice is written
+#pragma unroll
+  for (int pass = 0; pass < 32 / RPP; ++pass) {
+    const int r = pass * RPP + lane / LPR, ch = lane % LPR;
+    const u32x4 v = *(const u32x4*)(st + r * P + ch * 8);
+    if (r < nrows) *(u32x4*)(dst + (long)r * ldr + ch * 8) = v;
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the slice is reused
+}
+template <int HD> constexpr int store_slice_elems() { return 32 * (HD + 8); }
+
 template <bool B> struct Mask { static constexpr bool value = B; };
 
 // Forward: 128 queries of one (batch, head) per workgroup, 32 per wave.
@@ -432,6 +463,7 @@ __global__ void __launch_bounds__(256, HD == 128 ? 1 : 2)
     if (full) step(Ks[buf], Vs[buf], kb0, Mask<false>{});
     else step(Ks[buf], Vs[buf], kb0, Mask<true>{});
   }
+  // (Staging these rows through LDS, as the backward kernels do, is slower here.)
   if (qi < Tn) {
     const float inv = 1.f / lrow;
     bf16_t* orow = out + ((long)b * Tn + qi) * C + h * HD;
@@ -630,13 +662,14 @@ __global__ void __launch_bounds__(256, HD == 128 ? 1 : 2)
       Ds[buf ^ 1][threadIdx.x] = rd;
     }
   }
-  if (kj < Tn) {
-    bf16_t* row = dqkv + ((long)b * Tn + kj) * ld + h * HD;
-#pragma unroll
-    for (int d = 0; d < ND; ++d) {
-      store_dims(row + C, d * 32, dk[d], scale, g);
-      store_dims(row + 2 * C, d * 32, dv[d], 1.f, g);
-    }
+  __syncthreads();  // every wave is done with the Q / dO tiles: they become output slices
+  static_assert(4 * store_slice_elems<HD>() <= 2 * QT * HD, "output slices fit the Q tiles");
+  {
+    bf16_t* const st = &Qs[0][0] + wave * store_slice_elems<HD>();
+    bf16_t* const row = dqkv + ((long)b * Tn + kw0) * ld + h * HD;
+    const int nrows = min(32, Tn - kw0);
+    store_rows<HD>(row + C, ld, nrows, dk, scale, st, lane);
+    store_rows<HD>(row + 2 * C, ld, nrows, dv, 1.f, st, lane);
   }
 }
 
@@ -848,11 +881,10 @@ __global__ void __launch_bounds__(256, HD == 128 ? 1 : 2)
       }
     }
   }
-  if (qi < Tn) {
-    bf16_t* row = dqkv + ((long)b * Tn + qi) * ld + h * HD;
-#pragma unroll
-    for (int d = 0; d < ND; ++d) store_dims(row, d * 32, dq[d], scale, g);
-  }
+  __syncthreads();  // every wave is done with the K / V tiles: they become output slices
+  static_assert(4 * store_slice_elems<HD>() <= 2 * KT * HD, "output slices fit the K tiles");
+  store_rows<HD>(dqkv + ((long)b * Tn + qw0) * ld + h * HD, ld, min(32, Tn - qw0), dq, scale,
+                 &Ks[0][0] + wave * store_slice_elems<HD>(), lane);
 }
 
 // Sequences whose packed qkv rows exceed what a 32-bit buffer offset reaches
