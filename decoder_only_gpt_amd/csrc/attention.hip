@@ -368,13 +368,7 @@ __global__ void __launch_bounds__(256, HD == 128 ? 1 : 2)
   const int qw0 = qblk0 + wave * 32;
   const int qi = qw0 + c;  // this lane's query
 
-  bf16x8 qf[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    u32x4 v{0, 0, 0, 0};
-    if (qi < Tn) v = *(const u32x4*)(base + (long)qi * ld + h * HD + 16 * s + 8 * g);
-    qf[s] = *(bf16x8*)&v;
-  }
+  bf16x8 qf[NS];  // this lane's query row qi, head dims 16 s + 8 g .. (filled below)
   f32x16 o[ND];  // O^T: head dim d * 32 + acc_row(r, g), query qi
 #pragma unroll
   for (int d = 0; d < ND; ++d) o[d] = f32x16{};
@@ -447,6 +441,16 @@ __global__ void __launch_bounds__(256, HD == 128 ? 1 : 2)
 
   dma_tile<HD>(rs, ld, C + h * HD, kstart, Tn, Ks[0], wave, lane);
   dma_tile<HD>(rs, ld, 2 * C + h * HD, kstart, Tn, Vs[0], wave, lane);
+  // The workgroup's 128 query rows pass through the second K and V stages
+  // (free until the loop first refills them) as whole-row loads; each wave
+  // then reads its 32 queries' fragments (zero rows past the sequence end).
+  dma_tile<HD>(rs, ld, h * HD, qblk0, Tn, Ks[1], wave, lane);
+  dma_tile<HD>(rs, ld, h * HD, qblk0 + 64, Tn, Vs[1], wave, lane);
+  __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's loads landed
+  __syncthreads();                     // ... and every other wave's
+#pragma unroll
+  for (int s = 0; s < NS; ++s) qf[s] = row_frag<HD>(wave < 2 ? Ks[1] : Vs[1], (wave & 1) * 32, s, lane);
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): read before the stages are refilled
   int buf = 0;
   for (int kb0 = kstart; kb0 <= qlast; kb0 += KB, buf ^= 1) {
     __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's share of tile kb0 landed
@@ -519,17 +523,7 @@ __global__ void __launch_bounds__(256, HD == 128 ? 1 : 2)
   const int kw0 = kblk0 + wave * 32;
   const int kj = kw0 + c;  // this lane's key (operand column)
 
-  bf16x8 kf[NS], vf[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    u32x4 a{0, 0, 0, 0}, v{0, 0, 0, 0};
-    if (kj < Tn) {
-      a = *(const u32x4*)(base + (long)kj * ld + C + h * HD + 16 * s + 8 * g);
-      v = *(const u32x4*)(base + (long)kj * ld + 2 * C + h * HD + 16 * s + 8 * g);
-    }
-    kf[s] = *(bf16x8*)&a;
-    vf[s] = *(bf16x8*)&v;
-  }
+  bf16x8 kf[NS], vf[NS];  // this lane's key row kj, head dims 16 s + 8 g .. (filled below)
   f32x16 dk[ND], dv[ND];  // dK^T, dV^T: head dim d * 32 + acc_row(r, g), key kj
 #pragma unroll
   for (int d = 0; d < ND; ++d) dk[d] = dv[d] = f32x16{};
@@ -616,10 +610,26 @@ __global__ void __launch_bounds__(256, HD == 128 ? 1 : 2)
     }
   };
   fetch(kblk0, 0);
+  // The workgroup's 128 K and V rows pass through the second Q / dO stage
+  // (free until the loop first refills it) as whole-row loads; each wave then
+  // reads its 32 keys' fragments (zero rows past the sequence end).
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    dma_tile<HD>(rq, ld, C + h * HD, kblk0 + 64 * half, Tn, Qs[1] + 64 * half * HD, wave, lane);
+    dma_tile<HD>(rq, ld, 2 * C + h * HD, kblk0 + 64 * half, Tn, Gs[1] + 64 * half * HD, wave, lane);
+  }
   if (threadIdx.x < QT) {
     Ls[0][threadIdx.x] = rl;
     Ds[0][threadIdx.x] = rd;
   }
+  __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's loads landed
+  __syncthreads();                     // ... and every other wave's
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    kf[s] = row_frag<HD>(Qs[1], wave * 32, s, lane);
+    vf[s] = row_frag<HD>(Gs[1], wave * 32, s, lane);
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): read before the stage is refilled
   int buf = 0;
   for (int qb0 = kblk0; qb0 <= qend; qb0 += QT, buf ^= 1) {
     __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's share of block qb0 landed
@@ -712,23 +722,35 @@ __global__ void __launch_bounds__(256, HD == 128 ? 1 : 2)
   // The first key tile is requested before this wave's own rows, so the two
   // memory latencies overlap instead of adding up.
   fetch(kstart, 0);
-
+  // The workgroup's 128 Q and dO rows pass through the second K / V stage
+  // (free until the loop first refills it) as whole-row loads; each wave then
+  // reads its 32 queries' fragments (zero rows past the sequence end).  O,
+  // needed only for D, is read straight into registers.
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(dout + (long)b * Tn * C, (long)Tn * C * 2);
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    dma_tile<HD>(rs, ld, h * HD, qblk0 + 64 * half, Tn, Ks[1] + 64 * half * HD, wave, lane);
+    dma_tile<HD>(rg, C, h * HD, qblk0 + 64 * half, Tn, Vs[1] + 64 * half * HD, wave, lane);
+  }
+  u32x4 orow[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    orow[s] = u32x4{0, 0, 0, 0};
+    if (qi < Tn) orow[s] = *(const u32x4*)(out + ((long)b * Tn + qi) * C + h * HD + 16 * s + 8 * g);
+  }
+  __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's loads landed
+  __syncthreads();                     // ... and every other wave's
   bf16x8 qf[NS], gf[NS];
   float dpart = 0.f;  // this lane's share of D = sum_d dO O for its query
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    u32x4 a{0, 0, 0, 0}, v{0, 0, 0, 0}, o{0, 0, 0, 0};
-    if (qi < Tn) {
-      const long row = ((long)b * Tn + qi) * C + h * HD + 16 * s + 8 * g;
-      a = *(const u32x4*)(base + (long)qi * ld + h * HD + 16 * s + 8 * g);
-      v = *(const u32x4*)(dout + row);
-      o = *(const u32x4*)(out + row);
-    }
+    qf[s] = row_frag<HD>(Ks[1], wave * 32, s, lane);
+    gf[s] = row_frag<HD>(Vs[1], wave * 32, s, lane);
+    const u32x4 v = *(const u32x4*)&gf[s], o = orow[s];
 #pragma unroll
     for (int k = 0; k < 4; ++k) dpart += bf_lo(o[k]) * bf_lo(v[k]) + bf_hi(o[k]) * bf_hi(v[k]);
-    qf[s] = *(bf16x8*)&a;
-    gf[s] = *(bf16x8*)&v;
   }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): read before the stage is refilled
   // Lanes c and c + 32 hold the two halves of query qi's head dims; the sum
   // and the log-sum-exp in log2 units also go to D and L2 for the dK/dV kernel.
   const long r0 = ((long)b * H + h) * Tn;
