@@ -281,6 +281,9 @@ struct gpt_model {
   // priority) and the events that order it against the main chain.
   hipStream_t side = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr, ev_lmdw = nullptr;
+  // Second half-batch chain of the forward's blocks (default priority).
+  hipStream_t fwd2 = nullptr;
+  hipEvent_t ev_ffork = nullptr, ev_fjoin = nullptr;
   hipEvent_t ev_buf[3 * NGB] = {};  // last side-stream read of gact[], dF[], dqkv[]
   // AdamW runs on the side stream in parameter groups (embeddings, each layer,
   // the final LayerNorm and untied head); the next forward waits per group.
@@ -443,41 +446,75 @@ int run_forward(gpt_model* m, const int32_t* idx, const int32_t* tgt, hipStream_
   LAUNCH(GPT_K_EMBED, GPT_S_EMBED_FWD, 0, 12.0 * M * C,
          gpt::embed_fwd(prec, idx, m->P(m->pl.wte), m->P(m->pl.wpe), (int)M, m->T, (int)C,
                         c.vocab_size, m->X(0), m->at<int32_t>(m->ar.ids), m->id_flag(), gen, s));
-  for (int l = 0; l < c.n_layer; ++l) {
+  // The blocks run as two half-batch chains (rows [0, M/2) on s, the rest on
+  // fwd2), issued layer by layer, so one chain's epilogues, LayerNorms and
+  // attention overlap the other's products; every kernel is row-independent,
+  // so the results are those of one chain.  Only for large batches (small
+  // ones would change the products' plans); timed profiles keep one stream.
+  const int nch = (!m->prof_on && m->B % 2 == 0 && M / 2 >= 2048) ? 2 : 1;
+  const int64_t Mh = M / nch;
+  const int Bh = m->B / nch;
+  const int64_t eb = m->bf16 ? 2 : 4;
+  if (nch == 2) {
+    hipError_t e = hipEventRecord(m->ev_ffork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(m->fwd2, m->ev_ffork, 0);
+    if (e != hipSuccess) return fail(GPT_E_HIP, std::string("forward fork: ") + hipGetErrorString(e));
+  }
+  auto block = [&](int l, int ch, hipStream_t s) -> int {
     const LayerOff& L = m->pl.layer[l];
-    if ((rc = wait_adam(m, s, 1 + l)) != GPT_OK) return rc;
-    LAUNCH(GPT_K_LAYERNORM, GPT_S_LN_FWD, 0, ln_fwd_bytes,
-           gpt::layernorm_fwd(prec, m->X(2 * l), m->P(L.ln1w), m->P(L.ln1b), (int)M, (int)C,
-                              c.ln_eps, act(m->ar.a1[l]), m->mean(2 * l), m->rstd(2 * l), s));
-    gpt_gemm_desc d = linear_fwd(m, act(m->ar.a1[l]), C, L.qkvw, 3 * C, 3 * C);
-    d.epilogue = GPT_EPI_STORE; d.bias = m->P(L.qkvb); d.out = act(m->ar.qkv[l]); d.ldo = 3 * C;
+    const int64_t r0 = ch * Mh;
+    auto rows = [&](int64_t off, int64_t width) { return act(off) + r0 * width * eb; };
+    int rc2 = wait_adam(m, s, 1 + l);
+    if (rc2 != GPT_OK) return rc2;
+    LAUNCH(GPT_K_LAYERNORM, GPT_S_LN_FWD, 0, ln_fwd_bytes / nch,
+           gpt::layernorm_fwd(prec, m->X(2 * l) + r0 * C, m->P(L.ln1w), m->P(L.ln1b), (int)Mh,
+                              (int)C, c.ln_eps, rows(m->ar.a1[l], C), m->mean(2 * l) + r0,
+                              m->rstd(2 * l) + r0, s));
+    gpt_gemm_desc d = linear_fwd(m, rows(m->ar.a1[l], C), C, L.qkvw, 3 * C, 3 * C);
+    d.M = d.a_rows = (int)Mh;
+    d.epilogue = GPT_EPI_STORE; d.bias = m->P(L.qkvb); d.out = rows(m->ar.qkv[l], 3 * C);
+    d.ldo = 3 * C;
     GEMM(d, GPT_S_QKV_FWD);
-    LAUNCH(GPT_K_ATTN_FWD, GPT_S_ATTN_FWD, attn_flops * attn_pairs(m->T, c.window_left[l]), 0,
-           gpt::attention_fwd(prec, m->B, m->T, (int)m->H, (int)m->hd, c.window_left[l],
-                              act(m->ar.qkv[l]), act(m->ar.att[l]), m->at<float>(m->ar.lse[l]), s));
-    d = linear_fwd(m, act(m->ar.att[l]), C, L.projw, C, C);
-    d.epilogue = GPT_EPI_RESIDUAL; d.bias = m->P(L.projb); d.resid = m->X(2 * l);
-    d.out = m->X(2 * l + 1); d.ldo = C;
+    LAUNCH(GPT_K_ATTN_FWD, GPT_S_ATTN_FWD, attn_flops / nch * attn_pairs(m->T, c.window_left[l]), 0,
+           gpt::attention_fwd(prec, Bh, m->T, (int)m->H, (int)m->hd, c.window_left[l],
+                              rows(m->ar.qkv[l], 3 * C), rows(m->ar.att[l], C),
+                              m->at<float>(m->ar.lse[l]) + (int64_t)ch * Bh * m->H * m->T, s));
+    d = linear_fwd(m, rows(m->ar.att[l], C), C, L.projw, C, C);
+    d.M = d.a_rows = (int)Mh;
+    d.epilogue = GPT_EPI_RESIDUAL; d.bias = m->P(L.projb); d.resid = m->X(2 * l) + r0 * C;
+    d.out = m->X(2 * l + 1) + r0 * C; d.ldo = C;
     GEMM(d, GPT_S_PROJ_FWD);
-    LAUNCH(GPT_K_LAYERNORM, GPT_S_LN_FWD, 0, ln_fwd_bytes,
-           gpt::layernorm_fwd(prec, m->X(2 * l + 1), m->P(L.ln2w), m->P(L.ln2b), (int)M, (int)C,
-                              c.ln_eps, act(m->ar.a2[l]), m->mean(2 * l + 1), m->rstd(2 * l + 1), s));
-    d = linear_fwd(m, act(m->ar.a2[l]), C, L.fcw, F, F);
+    LAUNCH(GPT_K_LAYERNORM, GPT_S_LN_FWD, 0, ln_fwd_bytes / nch,
+           gpt::layernorm_fwd(prec, m->X(2 * l + 1) + r0 * C, m->P(L.ln2w), m->P(L.ln2b), (int)Mh,
+                              (int)C, c.ln_eps, rows(m->ar.a2[l], C), m->mean(2 * l + 1) + r0,
+                              m->rstd(2 * l + 1) + r0, s));
+    d = linear_fwd(m, rows(m->ar.a2[l], C), C, L.fcw, F, F);
+    d.M = d.a_rows = (int)Mh;
     // Kept for the backward: u itself when GELU is recomputed there, else
     // GELU'(u) (in the u buffer) next to GELU(u).
     d.epilogue = c.recompute_gelu ? GPT_EPI_GELU : GPT_EPI_GELU_PAIR;
-    d.bias = m->P(L.fcb); d.out = act(m->ar.u[l]); d.ldo = F;
-    d.aux = c.recompute_gelu ? nullptr : act(m->ar.g[l]); d.ldaux = F;
+    d.bias = m->P(L.fcb); d.out = rows(m->ar.u[l], F); d.ldo = F;
+    d.aux = c.recompute_gelu ? nullptr : rows(m->ar.g[l], F); d.ldaux = F;
     GEMM(d, GPT_S_FC_FWD);
     if (c.recompute_gelu) {
-      d = linear_fwd(m, act(m->ar.u[l]), F, L.fcpw, C, C);
+      d = linear_fwd(m, rows(m->ar.u[l], F), F, L.fcpw, C, C);
       d.a_gelu = 1;
     } else {
-      d = linear_fwd(m, act(m->ar.g[l]), F, L.fcpw, C, C);
+      d = linear_fwd(m, rows(m->ar.g[l], F), F, L.fcpw, C, C);
     }
-    d.epilogue = GPT_EPI_RESIDUAL; d.bias = m->P(L.fcpb); d.resid = m->X(2 * l + 1);
-    d.out = m->X(2 * l + 2); d.ldo = C;
+    d.M = d.a_rows = (int)Mh;
+    d.epilogue = GPT_EPI_RESIDUAL; d.bias = m->P(L.fcpb); d.resid = m->X(2 * l + 1) + r0 * C;
+    d.out = m->X(2 * l + 2) + r0 * C; d.ldo = C;
     GEMM(d, GPT_S_FCPROJ_FWD);
+    return GPT_OK;
+  };
+  for (int l = 0; l < c.n_layer; ++l)
+    for (int ch = 0; ch < nch; ++ch)
+      if ((rc = block(l, ch, ch == 0 ? s : m->fwd2)) != GPT_OK) return rc;
+  if (nch == 2) {
+    hipError_t e = hipEventRecord(m->ev_fjoin, m->fwd2);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, m->ev_fjoin, 0);
+    if (e != hipSuccess) return fail(GPT_E_HIP, std::string("forward join: ") + hipGetErrorString(e));
   }
   const int64_t nl = 2 * c.n_layer;
   if ((rc = wait_adam(m, s, -1)) != GPT_OK) return rc;  // the last group: all are done
@@ -802,6 +839,9 @@ int gpt_init(const gpt_config* cfg, int32_t B, int32_t T, void* d_arena, int64_t
   if (se == hipSuccess) se = hipEventCreateWithFlags(&m->ev_fork, hipEventDisableTiming);
   if (se == hipSuccess) se = hipEventCreateWithFlags(&m->ev_join, hipEventDisableTiming);
   if (se == hipSuccess) se = hipEventCreateWithFlags(&m->ev_lmdw, hipEventDisableTiming);
+  if (se == hipSuccess) se = hipStreamCreateWithFlags(&m->fwd2, hipStreamNonBlocking);
+  if (se == hipSuccess) se = hipEventCreateWithFlags(&m->ev_ffork, hipEventDisableTiming);
+  if (se == hipSuccess) se = hipEventCreateWithFlags(&m->ev_fjoin, hipEventDisableTiming);
   for (int i = 0; i < 3 * NGB && se == hipSuccess; ++i)
     se = hipEventCreateWithFlags(&m->ev_buf[i], hipEventDisableTiming);
   for (int i = 0; i < cfg->n_layer + 2 && se == hipSuccess; ++i) {
@@ -1191,8 +1231,10 @@ int gpt_gen_destroy(gpt_gen* g) {
 int gpt_destroy(gpt_model* m) {
   if (m) {
     for (hipEvent_t e : m->ev_pool) (void)hipEventDestroy(e);
-    for (hipEvent_t e : {m->ev_fork, m->ev_join, m->ev_lmdw})
+    for (hipEvent_t e : {m->ev_fork, m->ev_join, m->ev_lmdw, m->ev_ffork, m->ev_fjoin})
       if (e) (void)hipEventDestroy(e);
+    if (m->fwd2) (void)hipStreamSynchronize(m->fwd2);
+    if (m->fwd2) (void)hipStreamDestroy(m->fwd2);
     for (hipEvent_t e : m->ev_buf)
       if (e) (void)hipEventDestroy(e);
     if (m->side) (void)hipStreamSynchronize(m->side);
