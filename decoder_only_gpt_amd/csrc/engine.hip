@@ -281,9 +281,11 @@ struct gpt_model {
   // priority) and the events that order it against the main chain.
   hipStream_t side = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr, ev_lmdw = nullptr;
-  // Second half-batch chain of the forward's blocks (default priority).
-  hipStream_t fwd2 = nullptr;
-  hipEvent_t ev_ffork = nullptr, ev_fjoin = nullptr;
+  // Further batch chains of the forward's blocks (default priority).  Two
+  // chains: four made the GPT-2 124M step slower (19.2 against 18.15 ms).
+  static constexpr int FWD_CHAINS = 2;
+  hipStream_t fwdc[FWD_CHAINS - 1] = {};
+  hipEvent_t ev_ffork = nullptr, ev_fjoin[FWD_CHAINS - 1] = {};
   hipEvent_t ev_buf[3 * NGB] = {};  // last side-stream read of gact[], dF[], dqkv[]
   // AdamW runs on the side stream in parameter groups (embeddings, each layer,
   // the final LayerNorm and untied head); the next forward waits per group.
@@ -446,18 +448,19 @@ int run_forward(gpt_model* m, const int32_t* idx, const int32_t* tgt, hipStream_
   LAUNCH(GPT_K_EMBED, GPT_S_EMBED_FWD, 0, 12.0 * M * C,
          gpt::embed_fwd(prec, idx, m->P(m->pl.wte), m->P(m->pl.wpe), (int)M, m->T, (int)C,
                         c.vocab_size, m->X(0), m->at<int32_t>(m->ar.ids), m->id_flag(), gen, s));
-  // The blocks run as two half-batch chains (rows [0, M/2) on s, the rest on
-  // fwd2), issued layer by layer, so one chain's epilogues, LayerNorms and
+  // The blocks run as FWD_CHAINS batch chains (rows [0, M/2) on s, the rest
+  // on fwdc[0] for two), issued layer by layer, so one chain's epilogues, LayerNorms and
   // attention overlap the other's products; every kernel is row-independent,
   // so the results are those of one chain.  Only for large batches (small
   // ones would change the products' plans); timed profiles keep one stream.
-  const int nch = (!m->prof_on && m->B % 2 == 0 && M / 2 >= 2048) ? 2 : 1;
+  const int nch = (!m->prof_on && m->B % gpt_model::FWD_CHAINS == 0 &&
+                   M / gpt_model::FWD_CHAINS >= 2048) ? gpt_model::FWD_CHAINS : 1;
   const int64_t Mh = M / nch;
   const int Bh = m->B / nch;
   const int64_t eb = m->bf16 ? 2 : 4;
-  if (nch == 2) {
+  if (nch > 1) {
     hipError_t e = hipEventRecord(m->ev_ffork, s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(m->fwd2, m->ev_ffork, 0);
+    for (int i = 0; i + 1 < nch && e == hipSuccess; ++i) e = hipStreamWaitEvent(m->fwdc[i], m->ev_ffork, 0);
     if (e != hipSuccess) return fail(GPT_E_HIP, std::string("forward fork: ") + hipGetErrorString(e));
   }
   auto block = [&](int l, int ch, hipStream_t s) -> int {
@@ -510,10 +513,10 @@ int run_forward(gpt_model* m, const int32_t* idx, const int32_t* tgt, hipStream_
   };
   for (int l = 0; l < c.n_layer; ++l)
     for (int ch = 0; ch < nch; ++ch)
-      if ((rc = block(l, ch, ch == 0 ? s : m->fwd2)) != GPT_OK) return rc;
-  if (nch == 2) {
-    hipError_t e = hipEventRecord(m->ev_fjoin, m->fwd2);
-    if (e == hipSuccess) e = hipStreamWaitEvent(s, m->ev_fjoin, 0);
+      if ((rc = block(l, ch, ch == 0 ? s : m->fwdc[ch - 1])) != GPT_OK) return rc;
+  for (int i = 0; i + 1 < nch; ++i) {
+    hipError_t e = hipEventRecord(m->ev_fjoin[i], m->fwdc[i]);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, m->ev_fjoin[i], 0);
     if (e != hipSuccess) return fail(GPT_E_HIP, std::string("forward join: ") + hipGetErrorString(e));
   }
   const int64_t nl = 2 * c.n_layer;
@@ -839,9 +842,11 @@ int gpt_init(const gpt_config* cfg, int32_t B, int32_t T, void* d_arena, int64_t
   if (se == hipSuccess) se = hipEventCreateWithFlags(&m->ev_fork, hipEventDisableTiming);
   if (se == hipSuccess) se = hipEventCreateWithFlags(&m->ev_join, hipEventDisableTiming);
   if (se == hipSuccess) se = hipEventCreateWithFlags(&m->ev_lmdw, hipEventDisableTiming);
-  if (se == hipSuccess) se = hipStreamCreateWithFlags(&m->fwd2, hipStreamNonBlocking);
   if (se == hipSuccess) se = hipEventCreateWithFlags(&m->ev_ffork, hipEventDisableTiming);
-  if (se == hipSuccess) se = hipEventCreateWithFlags(&m->ev_fjoin, hipEventDisableTiming);
+  for (int i = 0; i + 1 < gpt_model::FWD_CHAINS && se == hipSuccess; ++i) {
+    se = hipStreamCreateWithFlags(&m->fwdc[i], hipStreamNonBlocking);
+    if (se == hipSuccess) se = hipEventCreateWithFlags(&m->ev_fjoin[i], hipEventDisableTiming);
+  }
   for (int i = 0; i < 3 * NGB && se == hipSuccess; ++i)
     se = hipEventCreateWithFlags(&m->ev_buf[i], hipEventDisableTiming);
   for (int i = 0; i < cfg->n_layer + 2 && se == hipSuccess; ++i) {
@@ -1231,10 +1236,15 @@ int gpt_gen_destroy(gpt_gen* g) {
 int gpt_destroy(gpt_model* m) {
   if (m) {
     for (hipEvent_t e : m->ev_pool) (void)hipEventDestroy(e);
-    for (hipEvent_t e : {m->ev_fork, m->ev_join, m->ev_lmdw, m->ev_ffork, m->ev_fjoin})
+    for (hipEvent_t e : {m->ev_fork, m->ev_join, m->ev_lmdw, m->ev_ffork})
       if (e) (void)hipEventDestroy(e);
-    if (m->fwd2) (void)hipStreamSynchronize(m->fwd2);
-    if (m->fwd2) (void)hipStreamDestroy(m->fwd2);
+    for (hipEvent_t e : m->ev_fjoin)
+      if (e) (void)hipEventDestroy(e);
+    for (hipStream_t f : m->fwdc)
+      if (f) {
+        (void)hipStreamSynchronize(f);
+        (void)hipStreamDestroy(f);
+      }
     for (hipEvent_t e : m->ev_buf)
       if (e) (void)hipEventDestroy(e);
     if (m->side) (void)hipStreamSynchronize(m->side);
