@@ -449,7 +449,8 @@ __global__ void __launch_bounds__(256, HD == 128 ? 1 : 2)
   __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's loads landed
   __syncthreads();                     // ... and every other wave's
 #pragma unroll
-  for (int s = 0; s < NS; ++s) qf[s] = row_frag<HD>(wave < 2 ? Ks[1] : Vs[1], (wave & 1) * 32, s, lane);
+  for (int s = 0; s < NS; ++s)
+    qf[s] = row_frag<HD>(wave < 2 ? Ks[1] : Vs[1], (wave & 1) * 32, s, lane);
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): read before the stages are refilled
   int buf = 0;
   for (int kb0 = kstart; kb0 <= qlast; kb0 += KB, buf ^= 1) {

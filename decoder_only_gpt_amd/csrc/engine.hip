@@ -448,11 +448,12 @@ int run_forward(gpt_model* m, const int32_t* idx, const int32_t* tgt, hipStream_
   LAUNCH(GPT_K_EMBED, GPT_S_EMBED_FWD, 0, 12.0 * M * C,
          gpt::embed_fwd(prec, idx, m->P(m->pl.wte), m->P(m->pl.wpe), (int)M, m->T, (int)C,
                         c.vocab_size, m->X(0), m->at<int32_t>(m->ar.ids), m->id_flag(), gen, s));
-  // The blocks run as FWD_CHAINS batch chains (rows [0, M/2) on s, the rest
-  // on fwdc[0] for two), issued layer by layer, so one chain's epilogues, LayerNorms and
-  // attention overlap the other's products; every kernel is row-independent,
-  // so the results are those of one chain.  Only for large batches (small
-  // ones would change the products' plans); timed profiles keep one stream.
+  // The blocks run as FWD_CHAINS batch chains (for two: rows [0, M/2) on s,
+  // the rest on fwdc[0]), issued layer by layer, so one chain's epilogues,
+  // LayerNorms and attention overlap the other's products; every kernel is
+  // row-independent, so the results are those of one chain.  Only for large
+  // batches (small ones would change the products' plans); timed profiles
+  // keep one stream.
   const int nch = (!m->prof_on && m->B % gpt_model::FWD_CHAINS == 0 &&
                    M / gpt_model::FWD_CHAINS >= 2048) ? gpt_model::FWD_CHAINS : 1;
   const int64_t Mh = M / nch;
@@ -460,8 +461,10 @@ int run_forward(gpt_model* m, const int32_t* idx, const int32_t* tgt, hipStream_
   const int64_t eb = m->bf16 ? 2 : 4;
   if (nch > 1) {
     hipError_t e = hipEventRecord(m->ev_ffork, s);
-    for (int i = 0; i + 1 < nch && e == hipSuccess; ++i) e = hipStreamWaitEvent(m->fwdc[i], m->ev_ffork, 0);
-    if (e != hipSuccess) return fail(GPT_E_HIP, std::string("forward fork: ") + hipGetErrorString(e));
+    for (int i = 0; i + 1 < nch && e == hipSuccess; ++i)
+      e = hipStreamWaitEvent(m->fwdc[i], m->ev_ffork, 0);
+    if (e != hipSuccess)
+      return fail(GPT_E_HIP, std::string("forward fork: ") + hipGetErrorString(e));
   }
   auto block = [&](int l, int ch, hipStream_t s) -> int {
     const LayerOff& L = m->pl.layer[l];
@@ -517,7 +520,8 @@ int run_forward(gpt_model* m, const int32_t* idx, const int32_t* tgt, hipStream_
   for (int i = 0; i + 1 < nch; ++i) {
     hipError_t e = hipEventRecord(m->ev_fjoin[i], m->fwdc[i]);
     if (e == hipSuccess) e = hipStreamWaitEvent(s, m->ev_fjoin[i], 0);
-    if (e != hipSuccess) return fail(GPT_E_HIP, std::string("forward join: ") + hipGetErrorString(e));
+    if (e != hipSuccess)
+      return fail(GPT_E_HIP, std::string("forward join: ") + hipGetErrorString(e));
   }
   const int64_t nl = 2 * c.n_layer;
   if ((rc = wait_adam(m, s, -1)) != GPT_OK) return rc;  // the last group: all are done
