@@ -152,6 +152,42 @@ def test_step_is_bitwise_deterministic(prec):
     assert a["loss"] == b["loss"]
 
 
+def test_concurrent_streams_equal_one_stream():
+    """The step's stream overlap (the forward's blocks as two half-batch chains,
+    the weight gradients on a side stream, AdamW parameter groups beside the
+    next forward) changes no result: two training steps enqueued normally and
+    the same two steps with kernel timing on (every kernel on the caller's
+    stream, one at a time) give bitwise-equal parameters, moments, gradients
+    and loss rows, at a batch where the forward chains engage (4096-row
+    halves)."""
+    cfg = presets.preset("gpt2_124m", vocab_size=500, padded_vocab=512, block_size=2048,
+                         n_layer=2, n_head=2, n_embd=128, mlp_hidden=512, window_left=[-1, -1],
+                         B=4, T=2048)
+    p = synth.init_params(cfg, seed=8, perturb=True)
+    batches = [synth.tokens(cfg, seed=9 + i) for i in range(2)]
+    out = []
+    for timed in (False, True):
+        m = gpt.Model(cfg)
+        m.set_params(p)
+        if timed:
+            m.profile_begin()
+        losses = []
+        for idx, tgt in batches:
+            di = torch.from_numpy(idx.reshape(-1)).cuda()
+            dt = torch.from_numpy(tgt.reshape(-1)).cuda()
+            losses.append(m.train_step(di, dt)["loss"])
+        if timed:
+            m.profile_end()
+        out.append(dict(loss=losses, p=m.params(), m=m.get_buffer(gpt.BUF_ADAM_M),
+                        v=m.get_buffer(gpt.BUF_ADAM_V), g=m.grads(),
+                        rows=m.get_buffer(gpt.BUF_LOSS_ROWS)))
+        del m
+    a, b = out
+    assert a["loss"] == b["loss"]
+    for k in ("p", "m", "v", "g", "rows"):
+        assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k
+
+
 def test_call_order_state_machine():
     cfg = presets.preset("tiny")
     m = gpt.Model(cfg)
