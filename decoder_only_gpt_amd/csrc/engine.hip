@@ -391,15 +391,22 @@ int launch(gpt_model* m, hipStream_t s, int kind, int site, double flops, double
     if (rc_ != GPT_OK) return rc_;                                                \
   } while (0)
 
-int run_gemm(gpt_model* m, hipStream_t s, const gpt_gemm_desc& d, int site) {
-  const int kind = gpt::gemm_split_count(d) > 1 ? GPT_K_GEMM_SPLITK : GPT_K_GEMM;
-  LAUNCH(kind, site, 2.0 * d.M * d.N * d.K, 0, gpt::gemm(d, s));
+// side_by_side: launches of this shape running at the same time (batch chains).
+int run_gemm(gpt_model* m, hipStream_t s, const gpt_gemm_desc& d, int site,
+             int side_by_side = 1) {
+  const int kind = gpt::gemm_split_count(d, side_by_side) > 1 ? GPT_K_GEMM_SPLITK : GPT_K_GEMM;
+  LAUNCH(kind, site, 2.0 * d.M * d.N * d.K, 0, gpt::gemm(d, s, side_by_side));
   return GPT_OK;
 }
 
 #define GEMM(d, site)                             \
   do {                                            \
     int rc_ = run_gemm(m, s, (d), (site));        \
+    if (rc_ != GPT_OK) return rc_;                \
+  } while (0)
+#define GEMM_SIDE(d, site, n)                     \
+  do {                                            \
+    int rc_ = run_gemm(m, s, (d), (site), (n));   \
     if (rc_ != GPT_OK) return rc_;                \
   } while (0)
 
@@ -480,7 +487,7 @@ int run_forward(gpt_model* m, const int32_t* idx, const int32_t* tgt, hipStream_
     d.M = d.a_rows = (int)Mh;
     d.epilogue = GPT_EPI_STORE; d.bias = m->P(L.qkvb); d.out = rows(m->ar.qkv[l], 3 * C);
     d.ldo = 3 * C;
-    GEMM(d, GPT_S_QKV_FWD);
+    GEMM_SIDE(d, GPT_S_QKV_FWD, nch);
     LAUNCH(GPT_K_ATTN_FWD, GPT_S_ATTN_FWD, attn_flops / nch * attn_pairs(m->T, c.window_left[l]), 0,
            gpt::attention_fwd(prec, Bh, m->T, (int)m->H, (int)m->hd, c.window_left[l],
                               rows(m->ar.qkv[l], 3 * C), rows(m->ar.att[l], C),
@@ -489,7 +496,7 @@ int run_forward(gpt_model* m, const int32_t* idx, const int32_t* tgt, hipStream_
     d.M = d.a_rows = (int)Mh;
     d.epilogue = GPT_EPI_RESIDUAL; d.bias = m->P(L.projb); d.resid = m->X(2 * l) + r0 * C;
     d.out = m->X(2 * l + 1) + r0 * C; d.ldo = C;
-    GEMM(d, GPT_S_PROJ_FWD);
+    GEMM_SIDE(d, GPT_S_PROJ_FWD, nch);
     LAUNCH(GPT_K_LAYERNORM, GPT_S_LN_FWD, 0, ln_fwd_bytes / nch,
            gpt::layernorm_fwd(prec, m->X(2 * l + 1) + r0 * C, m->P(L.ln2w), m->P(L.ln2b), (int)Mh,
                               (int)C, c.ln_eps, rows(m->ar.a2[l], C), m->mean(2 * l + 1) + r0,
@@ -501,7 +508,7 @@ int run_forward(gpt_model* m, const int32_t* idx, const int32_t* tgt, hipStream_
     d.epilogue = c.recompute_gelu ? GPT_EPI_GELU : GPT_EPI_GELU_PAIR;
     d.bias = m->P(L.fcb); d.out = rows(m->ar.u[l], F); d.ldo = F;
     d.aux = c.recompute_gelu ? nullptr : rows(m->ar.g[l], F); d.ldaux = F;
-    GEMM(d, GPT_S_FC_FWD);
+    GEMM_SIDE(d, GPT_S_FC_FWD, nch);
     if (c.recompute_gelu) {
       d = linear_fwd(m, rows(m->ar.u[l], F), F, L.fcpw, C, C);
       d.a_gelu = 1;
@@ -511,7 +518,7 @@ int run_forward(gpt_model* m, const int32_t* idx, const int32_t* tgt, hipStream_
     d.M = d.a_rows = (int)Mh;
     d.epilogue = GPT_EPI_RESIDUAL; d.bias = m->P(L.fcpb); d.resid = m->X(2 * l + 1) + r0 * C;
     d.out = m->X(2 * l + 2) + r0 * C; d.ldo = C;
-    GEMM(d, GPT_S_FCPROJ_FWD);
+    GEMM_SIDE(d, GPT_S_FCPROJ_FWD, nch);
     return GPT_OK;
   };
   for (int l = 0; l < c.n_layer; ++l)

@@ -1325,7 +1325,7 @@ struct GemmPlan {
 };
 
 GemmPlan plan_gemm(int M, int N, int K, int precision, bool splittable, int64_t ws_bytes,
-                   bool big_ok, int batch = 1, bool wide_ok = false) {
+                   bool big_ok, int batch = 1, bool wide_ok = false, int side_by_side = 1) {
   GemmPlan p{false, 1, false};
   if (precision != GPT_BF16 || M <= 0 || N <= 0 || K <= 0) return p;
   if (!big_ok) {
@@ -1346,7 +1346,10 @@ GemmPlan plan_gemm(int M, int N, int K, int precision, bool splittable, int64_t 
       }
     }
   }
-  const long t256 = cdiv(M, BIG) * cdiv(N, BIG) * batch;
+  // Grids of unsplit products that run side by side (batch chains of the
+  // forward) fill the CUs together: their fill is judged on all their tiles.
+  const long cf = splittable ? 1 : std::max(1, side_by_side);
+  const long t256 = cdiv(M, BIG) * cdiv(N, BIG) * batch * cf;
   // 256 x 192 tiles where that grid fills whole rounds of the 256 CUs and the
   // square grids do not (N = 768: 256 tiles against 192 of 256 x 256 and 1.5
   // rounds of 128 x 128; QKV forward: 3 rounds).  Not for products that may be
@@ -1354,7 +1357,7 @@ GemmPlan plan_gemm(int M, int N, int K, int precision, bool splittable, int64_t 
   // 256-tiles than unsplit here).
   if (wide_ok && !splittable && batch == 1) {
     auto fill = [](long t, long slots) { return (double)t / (double)(cdiv(t, slots) * slots); };
-    const long t192 = cdiv(M, BIG) * cdiv(N, BW), t128 = cdiv(M, BM) * cdiv(N, BN);
+    const long t192 = cdiv(M, BIG) * cdiv(N, BW) * cf, t128 = cdiv(M, BM) * cdiv(N, BN) * cf;
     const double f192 = fill(t192, 256);
     if (t192 >= 256 && f192 >= 0.95 && f192 > std::max(fill(t256, 256), fill(t128, 512)) + 0.05) {
       p.wide = true;
@@ -1403,7 +1406,7 @@ GemmPlan plan_gemm(int M, int N, int K, int precision, bool splittable, int64_t 
     // (measured on the 768 x 768 projections; at full rounds, e.g. the
     // 3072-wide FC products, the 256-tiles stay faster).
     if (!splittable && t256 >= 128) {
-      const long t128 = cdiv(M, BM) * cdiv(N, BN) * batch;
+      const long t128 = cdiv(M, BM) * cdiv(N, BN) * batch * cf;
       const double f256 = (double)t256 / (256.0 * cdiv(t256, 256));
       const double f128 = (double)t128 / (512.0 * cdiv(t128, 512));
       const bool tie = f256 < f128 + 1e-9 && f256 < 1.0 - 1e-9;
@@ -1448,9 +1451,10 @@ bool wide_ok(const gpt_gemm_desc& d) {
 
 }  // namespace
 
-int gemm_split_count(const gpt_gemm_desc& d) {
+int gemm_split_count(const gpt_gemm_desc& d, int side_by_side) {
   GemmPlan p = plan_gemm(d.M, d.N, d.K, d.precision, splittable(d),
-                         d.workspace ? d.workspace_bytes : 0, big_ok(d), 1, wide_ok(d));
+                         d.workspace ? d.workspace_bytes : 0, big_ok(d), 1, wide_ok(d),
+                         side_by_side);
   return effective_splits(p, d.K);
 }
 
@@ -1461,7 +1465,7 @@ int64_t gemm_workspace_bytes(int M, int N, int K, int precision) {
   return S > 1 ? (int64_t)S * M * N * 4 : 0;
 }
 
-hipError_t gemm(const gpt_gemm_desc& d, hipStream_t s) {
+hipError_t gemm(const gpt_gemm_desc& d, hipStream_t s, int side_by_side) {
   if (d.M <= 0 || d.N <= 0) return hipSuccess;
   // Vector loads: 8 K-values (row-major operand) or 8 rows (K-major operand).
   const bool k_vectors = !d.a_trans || !d.b_trans;
@@ -1489,7 +1493,7 @@ hipError_t gemm(const gpt_gemm_desc& d, hipStream_t s) {
   }
   const GemmPlan plan = plan_gemm(d.M, d.N, d.K, d.precision, batch == 1 && splittable(d),
                                   d.workspace ? d.workspace_bytes : 0, big_ok(d), batch,
-                                  wide_ok(d));
+                                  wide_ok(d), side_by_side);
   if (plan.wide) {  // wide_ok: the kernel exists for this combination
     dim3 grid((unsigned)cdiv(d.N, BW), (unsigned)cdiv(d.M, BIG), 1);
     big8w_kernel_for(d.a_trans, d.b_trans, d.epilogue, 0, 0)<<<grid, 512, 0, s>>>(A, B, d.K, d.K,

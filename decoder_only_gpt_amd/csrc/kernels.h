@@ -11,7 +11,10 @@ namespace gpt {
 
 // Matrix products (gemm.hip).  Returns hipSuccess or the launch error;
 // hipErrorInvalidValue when the descriptor breaks the stated layout rules.
-hipError_t gemm(const gpt_gemm_desc& d, hipStream_t s);
+// side_by_side: how many launches of this shape run at the same time on
+// other streams (1 = alone); the tile plan judges how evenly a grid fills the
+// CUs on that many grids (results do not depend on it).
+hipError_t gemm(const gpt_gemm_desc& d, hipStream_t s, int side_by_side = 1);
 // Bytes of split-K workspace gemm() may use for this shape (0 = never splits).
 int64_t gemm_workspace_bytes(int M, int N, int K, int precision);
 // n (<= 4) weight-gradient products with the same K in one launch (split-K
@@ -32,7 +35,7 @@ constexpr int GROUP_REDUCE_MAX_BLOCKS = 8192;
 int gemm_group_reduce_blocks(const gpt_gemm_desc* d, int n, float* const* db);
 int64_t gemm_group_workspace_bytes(const int* M, const int* N, int n, int K);
 // Number of K splits gemm() will use for this descriptor (1 = single kernel).
-int gemm_split_count(const gpt_gemm_desc& d);
+int gemm_split_count(const gpt_gemm_desc& d, int side_by_side = 1);
 
 // Attention (attention.hip).
 hipError_t attention_fwd(int prec, int B, int T, int H, int hd, int left, const void* qkv,
