@@ -648,7 +648,11 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
     d.epilogue = c.recompute_gelu ? GPT_EPI_DGELU : GPT_EPI_MUL;
     d.aux = act(m->ar.u[l]); d.ldaux = F; d.out = dF; d.ldo = F;
     GEMM(d, GPT_S_FCPROJ_DX);
-    CHECK(fork());
+    // An event record on s costs the chain a few microseconds between its
+    // kernels, so s2 is forked only where it launches next: here for the
+    // float32 bias gradients and the recomputed-GELU weight gradient; in bf16
+    // the block's products all wait for the fork after the attention.
+    if (!m->bf16 || c.recompute_gelu) CHECK(fork());
     // The block's weight gradients share K (the tokens): they are collected
     // and issued as one grouped launch once dqkv exists, and the buffers they
     // read are released after it.  With GELU recompute the FC-projection
@@ -688,7 +692,7 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
                               m->G(L.ln2w), m->G(L.ln2b), acc, ln_part, s));
     cur ^= 1;
     // attention out: x_mid = x_in + y Wproj^T + b
-    CHECK(fork());
+    if (!m->bf16) CHECK(fork());  // the float32 bias gradient of the projection
     CHECK(add_dw(linear_dw(m, gact, C, C, act(m->ar.att[l]), C, L.projw, C, acc), gact, C,
                  L.projb));
     held[nheld++] = gi;
