@@ -286,7 +286,7 @@ struct gpt_model {
   static constexpr int FWD_CHAINS = 2;
   hipStream_t fwdc[FWD_CHAINS - 1] = {};
   hipEvent_t ev_ffork = nullptr, ev_fjoin[FWD_CHAINS - 1] = {};
-  hipEvent_t ev_buf[3 * NGB] = {};  // last side-stream read of gact[], dF[], dqkv[]
+  hipEvent_t ev_buf[3 * NGB] = {};  // block l's grouped weight gradients done (index l % 18)
   // AdamW runs on the side stream in parameter groups (embeddings, each layer,
   // the final LayerNorm and untied head); the next forward waits per group.
   std::vector<hipEvent_t> ev_adam;
@@ -568,7 +568,6 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
   // stream, overlapping the input-gradient chain on `s`.  While kernels are
   // being timed everything stays on `s`, so each kernel is timed alone.
   hipStream_t s2 = m->prof_on ? s : m->side;
-  bool live[3 * NGB] = {};
   auto hip_ok = [&](hipError_t e, const char* what) -> int {
     return e == hipSuccess ? GPT_OK : fail(GPT_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
   };
@@ -577,14 +576,21 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
     int rc = hip_ok(hipEventRecord(m->ev_fork, s), "hipEventRecord");
     return rc != GPT_OK ? rc : hip_ok(hipStreamWaitEvent(s2, m->ev_fork, 0), "hipStreamWaitEvent");
   };
-  auto mark = [&](int slot) -> int {  // s2 is done reading buffer `slot` after this point
+  // The gradients the weight-gradient branch reads live in rings: dF and dqkv
+  // one slot per block (NGB deep), gact two per block.  The slots block l
+  // writes were last read by the grouped launches of blocks l + 2 (the gact
+  // its LayerNorm 1 writes), l + 3 (LayerNorm 2's) and l + NGB (dF, dqkv);
+  // s2 runs those launches in order, so one wait per block, for block l + 2's
+  // launch, frees them all (every event operation on s costs the chain a few
+  // microseconds between its kernels).
+  static_assert(NGB == 6, "the reuse distances above are those of rings of 6");
+  auto group_done = [&](int l) -> int {  // s2 has read block l's buffers after this point
     if (s2 == s) return GPT_OK;
-    live[slot] = true;
-    return hip_ok(hipEventRecord(m->ev_buf[slot], s2), "hipEventRecord");
+    return hip_ok(hipEventRecord(m->ev_buf[l % (3 * NGB)], s2), "hipEventRecord");
   };
-  auto before_write = [&](int slot) -> int {  // s may overwrite buffer `slot`
-    if (s2 == s || !live[slot]) return GPT_OK;
-    return hip_ok(hipStreamWaitEvent(s, m->ev_buf[slot], 0), "hipStreamWaitEvent");
+  auto before_block = [&](int l) -> int {  // s may overwrite the slots block l writes
+    if (s2 == s || l + 2 >= c.n_layer) return GPT_OK;
+    return hip_ok(hipStreamWaitEvent(s, m->ev_buf[(l + 2) % (3 * NGB)], 0), "hipStreamWaitEvent");
   };
 #define CHECK(x)                    \
   do {                              \
@@ -643,7 +649,7 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
     char* dF = act(m->ar.dF[di]);
     char* dqkv = act(m->ar.dqkv[di]);
     // MLP out: x_out = x_mid + GELU(u) Wfcp^T + b
-    CHECK(before_write(NGB + di));
+    CHECK(before_block(l));
     d = linear_dx(m, gact, C, L.fcpw, F, C, C);
     d.epilogue = c.recompute_gelu ? GPT_EPI_DGELU : GPT_EPI_MUL;
     d.aux = act(m->ar.u[l]); d.ldaux = F; d.out = dF; d.ldo = F;
@@ -661,7 +667,7 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
     // launch, summed from the dY tiles it stages in LDS.
     gpt_gemm_desc dw[4];
     float* db[4];
-    int ndw = 0, held[4], nheld = 0;
+    int ndw = 0;
     auto add_dw = [&](const gpt_gemm_desc& dd, const char* dy, int64_t n, int64_t b_off) -> int {
       dw[ndw] = dd;
       db[ndw] = (m->bf16 && b_off >= 0) ? m->G(b_off) : nullptr;
@@ -676,16 +682,13 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
     } else {
       CHECK(add_dw(linear_dw(m, gact, C, C, act(m->ar.g[l]), F, L.fcpw, C, acc), gact, C, L.fcpb));
     }
-    held[nheld++] = gi;
     // MLP in: u = a2 Wfc^T + b
     CHECK(add_dw(linear_dw(m, dF, F, F, act(m->ar.a2[l]), C, L.fcw, F, acc), dF, F, L.fcb));
-    held[nheld++] = NGB + di;
     d = linear_dx(m, dF, F, L.fcw, C, F, F);
     d.epilogue = GPT_EPI_STORE; d.out = dC; d.ldo = C;
     GEMM(d, GPT_S_FC_DX);
     gi = (gi + 1) % NGB;
     gact = act(m->ar.gact[gi]);
-    CHECK(before_write(gi));
     LAUNCH(GPT_K_LAYERNORM, GPT_S_LN_BWD, 0, ln_bwd_bytes,
            gpt::layernorm_bwd(prec, dC, m->X(2 * l + 1), m->mean(2 * l + 1), m->rstd(2 * l + 1),
                               m->P(L.ln2w), gres[cur], (int)M, (int)C, gres[cur ^ 1], gact,
@@ -695,11 +698,9 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
     if (!m->bf16) CHECK(fork());  // the float32 bias gradient of the projection
     CHECK(add_dw(linear_dw(m, gact, C, C, act(m->ar.att[l]), C, L.projw, C, acc), gact, C,
                  L.projb));
-    held[nheld++] = gi;
     d = linear_dx(m, gact, C, L.projw, C, C, C);
     d.epilogue = GPT_EPI_STORE; d.out = dC2; d.ldo = C;
     GEMM(d, GPT_S_PROJ_DX);
-    CHECK(before_write(2 * NGB + di));
     LAUNCH(GPT_K_ATTN_BWD, GPT_S_ATTN_BWD, attn_flops * attn_pairs(m->T, c.window_left[l]), 0,
            gpt::attention_bwd(prec, m->B, m->T, (int)m->H, (int)m->hd, c.window_left[l],
                               act(m->ar.qkv[l]), act(m->ar.att[l]), m->at<float>(m->ar.lse[l]),
@@ -708,7 +709,6 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
     CHECK(fork());
     CHECK(add_dw(linear_dw(m, dqkv, 3 * C, 3 * C, act(m->ar.a1[l]), C, L.qkvw, 3 * C, acc), dqkv,
                  3 * C, L.qkvb));
-    held[nheld++] = 2 * NGB + di;
     double* sq = nullptr;
     if (fold) {
       const int b = ndw == 4 ? gpt::gemm_group_reduce_blocks(dw, ndw, db) : 0;
@@ -717,13 +717,12 @@ int run_backward(gpt_model* m, int acc, hipStream_t s) {
       if (fold) sq = n_part + (int64_t)l * rb;
     }
     CHECK(gemm_group_on(s2, dw, db, ndw, GPT_S_BLOCK_DW, sq));
-    for (int i = 0; i < nheld; ++i) CHECK(mark(held[i]));
+    CHECK(group_done(l));
     d = linear_dx(m, dqkv, 3 * C, L.qkvw, C, 3 * C, 3 * C);
     d.epilogue = GPT_EPI_STORE; d.out = dC; d.ldo = C;
     GEMM(d, GPT_S_QKV_DX);
     gi = (gi + 1) % NGB;
     gact = act(m->ar.gact[gi]);
-    CHECK(before_write(gi));
     LAUNCH(GPT_K_LAYERNORM, GPT_S_LN_BWD, 0, ln_bwd_bytes,
            gpt::layernorm_bwd(prec, dC, m->X(2 * l), m->mean(2 * l), m->rstd(2 * l), m->P(L.ln1w),
                               gres[cur], (int)M, (int)C, gres[cur ^ 1], gact, m->G(L.ln1w),
