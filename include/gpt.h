@@ -147,9 +147,10 @@ int gpt_plan(const gpt_config* cfg, int32_t B, int32_t T, gpt_sizes* out);
 double gpt_flops_per_token(const gpt_config* cfg, int32_t T);
 
 /* Bind a model to a caller-owned device arena of at least arena_bytes
- * (gpt_plan), 256-byte aligned, and initialise it on `stream` (BASELINE
- * workloads: "weights N(0,0.02)"; nanoGPT README "quick start": a GPT trained
- * from scratch): every matrix and embedding entry at flat index i is
+ * (gpt_plan), 256-byte aligned, and initialise it on `stream` for training
+ * from scratch (nanoGPT README, "quick start"; the pages fix no initial scale,
+ * so the usual GPT-2 scale 0.02 is taken): every matrix and embedding entry at
+ * flat index i is
  * (float)(0.02 * z(i)), z(i) a standard normal drawn from `seed` by
  * Philox4x32-10 (Salmon et al., SC 2011; block i / 4, counter (i/4 lo, i/4 hi,
  * 0, 0), key (seed lo, seed hi)) and the Box-Muller transform in double (words
