@@ -1,7 +1,7 @@
 // Causal multi-head self-attention with an optional left window, forward and
 // backward.
 //
-// What is computed (nanoGPT README: "6-layer Transformer with 6 heads";
+// What is computed (nanoGPT README, "quick start": a six-layer, six-head model;
 // nanochat "FLOPs-Berechnung im Detail": per-layer (left, right) window, the
 // effective sequence is min(window, T)): for each batch row and head,
 // S = q k^T / sqrt(hd), key j visible to query i iff i - left <= j <= i

@@ -1,7 +1,7 @@
 // Matrix products of the GPT step: C = op(A) . op(B)^T with fused epilogues.
 //
-// Every Linear layer of the model (nanoGPT README: "model.py ... a GPT model
-// definition"; nanochat "FLOPs-Berechnung im Detail": each matmul parameter
+// Every Linear layer of the model (nanoGPT README: model.py defines the GPT;
+// nanochat "FLOPs-Berechnung im Detail": each matmul parameter
 // costs 2 FLOPs forward and 4 backward) runs through here three times:
 //   forward  y  = x W^T            A = x  [M,K]            B = W [N,K]
 //   backward dx = dy W             A = dy [M,K]            B = W stored [K,N]

@@ -10,7 +10,7 @@
  * Sources (web pages, by title and section):
  *   - nanoGPT README, "quick start" / "reproducing GPT-2" / "todos": the model
  *     (6-layer, 6-head, 384-channel character model; GPT-2 124M; absolute
- *     learned position embeddings, "other embeddings" being a todo);
+ *     learned position embeddings, other schemes listed under "todos");
  *   - Panthalia "Create a Plugin", "Components of the Example Plugin": the
  *     GPTConfig fields and the flattened-tensor representation of the model
  *     that forward/backward/update act on;
@@ -168,9 +168,10 @@ int gpt_init(const gpt_config* cfg, int32_t B, int32_t T, void* d_arena, int64_t
  * "quick start": the GPT of model.py) on device token ids d_idx [B*T]
  * (int32, row-major [B][T], caller-owned and read during the enqueued work
  * only).  With d_tgt [B*T] (int32, the next-token targets: Panthalia "Create
- * a Plugin", input-target pairs) the per-token cross-entropy (NiNo "usage":
- * loss = F.cross_entropy(output, target), mean) and its gradient w.r.t. the
- * logits are computed too (required before gpt_backward); with d_tgt == NULL
+ * a Plugin", input-target pairs) the per-token cross-entropy (NiNo README,
+ * "usage": the mean cross-entropy of the output against the target) and its
+ * gradient w.r.t. the logits are computed too (required before gpt_backward);
+ * with d_tgt == NULL
  * only the logits.  Ids outside [0, vocab_size): see the conventions above.
  * Enqueue only.  INVALID on NULL model / d_idx. */
 int gpt_forward(gpt_model* m, const int32_t* d_idx, const int32_t* d_tgt, void* stream);
@@ -195,8 +196,8 @@ int gpt_loss_async(gpt_model* m, float* h_loss, void* stream);
  * loss.backward(); Panthalia "Create a Plugin": gradient computation on the
  * flattened representation): the exact gradient of the mean loss w.r.t. every
  * parameter, into the flat gradient buffer.  accumulate = 0 overwrites it,
- * 1 adds to it (gradient accumulation over micro-batches, Panthalia
- * "accumulations").  Enqueue only.  STATE without a preceding forward with
+ * 1 adds to it (gradient accumulation over micro-batches, as in the
+ * Panthalia plugin example).  Enqueue only.  STATE without a preceding forward with
  * targets; INVALID for accumulate not in {0, 1}. */
 int gpt_backward(gpt_model* m, int32_t accumulate, void* stream);
 

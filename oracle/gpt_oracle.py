@@ -12,7 +12,8 @@ What it follows (page titles and sections of the source pages):
   * Panthalia "Create a Plugin" (the `GPTConfig` example and "Components"):
     block_size / vocab_size / n_layer / n_head / n_embd / bias, the flattened
     parameter representation, input/target pairs;
-  * NiNo README ("usage"): loss = F.cross_entropy(logits, targets) (mean);
+  * NiNo README ("usage"): the loss is the mean cross-entropy of the logits
+    against the targets;
   * nanochat "Architektur im Überblick", "FLOPs-Berechnung im Detail": FLOPs
     per token = 6 * (params - excluded) + sum over layers 12*h*q*effective_seq,
     with a (left, right) window per layer; "AdamW Fused Step": decay, lerp of
@@ -74,7 +75,7 @@ def _mm(ctr, a, b):
 
 def layout(cfg):
     """(name, shape) of every parameter tensor, in the flat order of the
-    Panthalia page's "flattened tensor representation" (one contiguous vector)."""
+    Panthalia page's flat form of the model's parameters (one contiguous vector)."""
     C, F, Vp, Tb = cfg["n_embd"], cfg["mlp_hidden"], cfg["padded_vocab"], cfg["block_size"]
     bias = bool(cfg["bias"])
     out = [("wte", (Vp, C)), ("wpe", (Tb, C))]
