@@ -171,8 +171,8 @@ int gpt_init(const gpt_config* cfg, int32_t B, int32_t T, void* d_arena, int64_t
  * a Plugin", input-target pairs) the per-token cross-entropy (NiNo README,
  * "usage": the mean cross-entropy of the output against the target) and its
  * gradient w.r.t. the logits are computed too (required before gpt_backward);
- * with d_tgt == NULL
- * only the logits.  Ids outside [0, vocab_size): see the conventions above.
+ * with d_tgt == NULL only the logits.  Ids outside [0, vocab_size): see the
+ * conventions above.
  * Enqueue only.  INVALID on NULL model / d_idx. */
 int gpt_forward(gpt_model* m, const int32_t* d_idx, const int32_t* d_tgt, void* stream);
 
