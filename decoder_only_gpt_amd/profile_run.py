@@ -14,6 +14,9 @@
     python -m decoder_only_gpt_amd.profile_run summarize-mfma CSV OUT --command "..."
         rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE counter rows -> per-kernel
         fraction of SIMD cycles the matrix units were busy
+    python -m decoder_only_gpt_amd.profile_run summarize-timeline CSV OUT --command "..."
+        rocprofv3 --kernel-trace rows of concurrent steps -> per step: busy fraction,
+        fraction with two or more kernels running, idle gaps (and where they fall)
     python -m decoder_only_gpt_amd.profile_run summarize-traffic --kernel SUBSTR
         --fetch CSV --write CSV --copy-fetch CSV --copy-write CSV --copy-mib N OUT --command "..."
         per-dispatch FETCH_SIZE / WRITE_SIZE of one kernel, scaled by the same counters
@@ -171,6 +174,62 @@ def summarize_mfma(csv_path: str, out_path: str, command: str, top: int = 40):
     print("\n".join(lines))
 
 
+def _short(name: str) -> str:
+    for pre in ("void gpt::(anonymous namespace)::", "gpt::(anonymous namespace)::", "gpt::"):
+        name = name.replace(pre, "")
+    return name.split("(")[0][:44]
+
+
+def summarize_timeline(csv_path: str, out_path: str, command: str, marker: str = "embed_fwd_kernel"):
+    """Kernel trace of back-to-back training steps: a step runs from one
+    embedding lookup to the next.  Per whole step: its length, the fraction
+    of it with at least one kernel running (busy) and with two or more, and
+    the idle gaps; for the median step, every gap with the kernels around it."""
+    with open(csv_path) as f:
+        rows = list(csv.DictReader(f))
+    ev = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"])
+                for r in rows)
+    starts = [b for b, e, n in ev if marker in n]
+    steps = []
+    for a, b in zip(starts[1:-1], starts[2:]):  # whole steps only (the first may be warm-up)
+        ks = [(s, e, n) for s, e, n in ev if a <= s < b]
+        busy, gaps, cur_s, cur_e, last = 0, [], None, None, None
+        for s, e, n in ks:
+            if cur_e is not None and s > cur_e:
+                busy += cur_e - cur_s
+                gaps.append(((cur_e - a) / 1e3, (s - cur_e) / 1e3, last, n))
+                cur_s = None
+            if cur_s is None:
+                cur_s = s
+            if cur_e is None or e > cur_e:
+                cur_e, last = e, n
+        busy += cur_e - cur_s
+        pts = sorted([(s, 1) for s, e, n in ks] + [(min(e, b), -1) for s, e, n in ks])
+        two, run, prev = 0, 0, a
+        for t, d in pts:
+            if run >= 2:
+                two += t - prev
+            run += d
+            prev = t
+        steps.append(dict(ms=(b - a) / 1e6, busy=busy / (b - a), two=two / (b - a), gaps=gaps))
+    lines = ["# Kernel timeline of concurrent training steps", f"# command: {command}",
+             f"# kernel sources sha: {kernel_source_sha()}",
+             "# busy = fraction of the step with a kernel running; 2+ = with two or more", "",
+             "  step      ms   busy     2+   idle_us  gaps"]
+    for i, st in enumerate(steps):
+        idle = sum(g for _, g, _, _ in st["gaps"])
+        lines.append(f"  {i:4d} {st['ms']:7.3f}  {st['busy']:.3f}  {st['two']:.3f}  {idle:8.1f}"
+                     f"  {len(st['gaps']):4d}")
+    if steps:
+        med = sorted(steps, key=lambda x: x["ms"])[len(steps) // 2]
+        lines += ["", "gaps of the median step (offset in the step, idle time, kernels around it):"]
+        for off, g, p_, n in med["gaps"]:
+            lines.append(f"  {off:9.1f} us  {g:5.1f} us  {_short(p_):44s} -> {_short(n)}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines[:12 + len(steps)]))
+
+
 def _per_dispatch(csv_path: str, counter: str, substr: str):
     vals = []
     for r in csv.DictReader(open(csv_path)):
@@ -209,7 +268,8 @@ def main():
     p.add_argument("--config", default="gpt2_124m")
     p.add_argument("--steps", type=int, default=3)
     p.add_argument("--concurrent", action="store_true",
-                   help="weight gradients on their side stream, as in training")
+                   help="the streams of training (forward chains, weight gradients and "
+                        "AdamW groups beside the main chain) instead of one timed stream")
     p = sub.add_parser("muon")
     p.add_argument("--config", default="gpt2_124m")
     p.add_argument("--steps", type=int, default=3)
@@ -225,6 +285,10 @@ def main():
     p.add_argument("out")
     p.add_argument("--command", required=True)
     p = sub.add_parser("summarize-mfma")
+    p.add_argument("csv")
+    p.add_argument("out")
+    p.add_argument("--command", required=True)
+    p = sub.add_parser("summarize-timeline")
     p.add_argument("csv")
     p.add_argument("out")
     p.add_argument("--command", required=True)
@@ -255,6 +319,8 @@ def main():
         summarize_stats(a.csv, a.out, a.command)
     elif a.cmd == "summarize-mfma":
         summarize_mfma(a.csv, a.out, a.command)
+    elif a.cmd == "summarize-timeline":
+        summarize_timeline(a.csv, a.out, a.command)
     else:
         summarize_traffic(a)
 
