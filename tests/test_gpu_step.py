@@ -152,17 +152,18 @@ def test_step_is_bitwise_deterministic(prec):
     assert a["loss"] == b["loss"]
 
 
-def test_concurrent_streams_equal_one_stream():
+@pytest.mark.parametrize("B,T", [(4, 2048), (2, 2100)])
+def test_concurrent_streams_equal_one_stream(B, T):
     """The step's stream overlap (the forward's blocks as two half-batch chains,
     the weight gradients on a side stream, AdamW parameter groups beside the
     next forward) changes no result: two training steps enqueued normally and
     the same two steps with kernel timing on (every kernel on the caller's
     stream, one at a time) give bitwise-equal parameters, moments, gradients
-    and loss rows, at a batch where the forward chains engage (4096-row
-    halves)."""
-    cfg = presets.preset("gpt2_124m", vocab_size=500, padded_vocab=512, block_size=2048,
+    and loss rows, at batches where the forward chains engage (4096-row halves,
+    and 2100-row halves: ragged tiles and a ragged attention tail)."""
+    cfg = presets.preset("gpt2_124m", vocab_size=500, padded_vocab=512, block_size=T,
                          n_layer=2, n_head=2, n_embd=128, mlp_hidden=512, window_left=[-1, -1],
-                         B=4, T=2048)
+                         B=B, T=T)
     p = synth.init_params(cfg, seed=8, perturb=True)
     batches = [synth.tokens(cfg, seed=9 + i) for i in range(2)]
     out = []
